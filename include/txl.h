@@ -1,0 +1,188 @@
+/*
+ * txl.h -- C ABI of libtxl.so: Transformer-XL relative-position attention over
+ * segment-level memory (forward), the layer step that feeds it, and the memory
+ * update, for AMD Instinct MI355X (gfx950).
+ *
+ * Source of every operation: Dai et al., "Transformer-XL: Attentive Language
+ * Models Beyond a Fixed-Length Context" (arXiv 1901.02860v3), section 3.2
+ * (segment-level recurrence with a length-M memory), section 3.3 (relative
+ * positional encodings: the score A^rel with terms (a)-(d), the biases u and v,
+ * separate W_{k,E} and W_{k,R}, and the N-layer computational procedure), and
+ * Appendix B (distances range over 0 .. M+L-1).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are device pointers (hipMalloc'd or torch-allocated memory).
+ *     The library allocates no device memory; scratch comes from the caller's
+ *     workspace argument.
+ *   - Strides are in ELEMENTS.  Element types: TXL_FP32 = float,
+ *     TXL_BF16 = bfloat16 (stored as 16-bit words).  One call uses one dtype for
+ *     all of its tensor arguments (scores_dbg is always float).
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     No entry point synchronises; the caller owns ordering and lifetime.
+ *   - Every argument is validated before anything is enqueued, so a call that
+ *     returns an error has written nothing.  No C++ exception crosses the ABI.
+ *   - Weights are stored [out, in] row-major: y = x W^T, as the pages write
+ *     projections (h W^T).
+ */
+#ifndef TXL_H
+#define TXL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TXL_OK = 0,
+  TXL_EINVAL = -1,        /* null pointer, non-positive size, bad stride, aliasing  */
+  TXL_EUNSUPPORTED = -2,  /* valid but not supported: dtype, d_head > 128           */
+  TXL_EHIP = -3,          /* a HIP runtime call or kernel launch failed             */
+  TXL_EWORKSPACE = -4     /* workspace smaller than txl_layer_workspace_bytes()     */
+} txl_status;
+
+typedef enum { TXL_FP32 = 0, TXL_BF16 = 1 } txl_dtype;
+
+/*
+ * Relative-position attention, forward (section 3.3, the A^rel equation and the
+ * masked softmax of the N-layer procedure).  For batch row b, head h, query
+ * i in [0, L) and key j in [0, T), T = mem_len + L (keys 0 .. mem_len-1 are the
+ * memory, oldest first; keys mem_len .. T-1 are the current segment):
+ *
+ *   key j is visible to query i  iff  j <= mem_len + i      (the query sees itself)
+ *   p = mem_len + i - j                                      (relative distance)
+ *   A[i][j] = scale * ( (q_i + u_h) . k_j  +  (q_i + v_h) . r_p )
+ *           = scale * ( (a) + (c) + (b) + (d) )
+ *   out_i   = sum_j softmax_j(A[i][.]) v_j
+ *
+ * Arguments
+ *   stream            hipStream_t to enqueue on.
+ *   dtype             TXL_FP32 or TXL_BF16 (bf16 inputs: fp32 accumulation and
+ *                     fp32 softmax state; output rounded to bf16).
+ *   B, H, L           batch, heads, segment length (queries per batch row), >= 1.
+ *   mem_len           valid memory rows, >= 0.
+ *   d_head            head size, 1 .. 128.
+ *   q                 q[b][i][h][c]  at q + b*q_sb + i*q_st + h*q_sh + c.
+ *   k, v              k[b][j][h][c]  at k + b*kv_sb + j*kv_st + h*kv_sh + c
+ *                     (v uses the same strides), j in [0, T).
+ *   r                 r[p][h][c]     at r + p*r_sp + h*r_sh + c, p in [0, r_rows);
+ *                     row p is W_{k,R} R_p, the projected encoding of distance p.
+ *                     r_rows must be >= T.
+ *   u_bias, v_bias    [H][d_head] dense: the global content bias u and the
+ *                     global position bias v of section 3.3.
+ *   scale             multiplies the whole four-term score (1/sqrt(d_head) is
+ *                     the usual choice).
+ *   out               out[b][i][h][c] at out + b*o_sb + i*o_st + h*o_sh + c.
+ *                     Must not overlap any input.
+ *   scores_dbg        NULL, or float [B][H][L][T] dense: receives A (scaled), with
+ *                     -INFINITY where masked.  Debug only; it slows the call.
+ *
+ * Layouts: any strides with the innermost (c) dimension contiguous are
+ * accepted.  bf16 calls whose q/k/v/r base pointers are 16-byte aligned and
+ * whose q/k/v/r strides are multiples of 8 take the matrix-core path (d_head
+ * <= 64); other layouts take a generic path.  This is never an error.
+ * Returns TXL_OK or a txl_status.
+ */
+int txl_rel_attn_fwd(void* stream, int dtype,
+                     int64_t B, int64_t H, int64_t L, int64_t mem_len, int64_t d_head,
+                     const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                     const void* k, const void* v, int64_t kv_sb, int64_t kv_st, int64_t kv_sh,
+                     const void* r, int64_t r_sp, int64_t r_sh, int64_t r_rows,
+                     const void* u_bias, const void* v_bias, float scale,
+                     void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                     float* scores_dbg);
+
+/*
+ * The memory of one layer (section 3.2: a length-M cache of old hidden states
+ * that may span several segments), stored as a ring so that an update never
+ * moves the rows it keeps.
+ *   data      device [B][capacity][d_model], row pitch d_model elements.
+ *   capacity  M >= 1.
+ *   start     physical slot of logical row 0 (the oldest), 0 <= start < M.
+ *   len       valid rows, 0 <= len <= M (0 = empty memory).
+ * Logical row t (0 = oldest) of batch row b lives at data[b][(start + t) % M].
+ */
+typedef struct {
+  void* data;
+  int64_t capacity;
+  int64_t start;
+  int64_t len;
+} txl_ring;
+
+typedef struct {
+  int64_t B;        /* batch                               */
+  int64_t L;        /* segment length                      */
+  int64_t d_model;  /* hidden size D                       */
+  int64_t n_head;   /* H                                   */
+  int64_t d_head;   /* d, 1 .. 128                         */
+  float ln_eps;     /* LayerNorm epsilon (e.g. 1e-5)       */
+} txl_layer_dims;
+
+typedef struct {
+  const void* W_q;       /* [H*d, D]  query projection                      */
+  const void* W_kE;      /* [H*d, D]  content-key projection W_{k,E}         */
+  const void* W_v;       /* [H*d, D]  value projection                      */
+  const void* W_kR;      /* [H*d, D]  position-key projection W_{k,R}        */
+  const void* W_o;       /* [D, H*d]  output projection ("Linear")           */
+  const void* ln_gamma;  /* [D]       LayerNorm scale                        */
+  const void* ln_beta;   /* [D]       LayerNorm shift                        */
+} txl_layer_weights;
+
+/*
+ * Bytes of workspace txl_layer_step needs for these dims with a memory of
+ * capacity mem_capacity (it covers every mem->len <= mem_capacity).
+ * Returns 0 if the arguments are invalid.
+ */
+size_t txl_layer_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype);
+
+/*
+ * One Transformer-XL layer for one segment (section 3.3, the N-layer procedure,
+ * without the position-wise feed-forward; section 3.2 for the context):
+ *
+ *   ctx   = [ memory (mem->len rows, oldest first) ; h_in (L rows) ]   per batch row
+ *   q     = h_in W_q^T             k = ctx W_kE^T        v = ctx W_v^T
+ *   r     = R[0 : mem->len + L] W_kR^T        (row p <-> distance p)
+ *   a     = txl_rel_attn_fwd(q, k, v, r, u, v_bias, scale = 1/sqrt(d_head))
+ *   h_out = LayerNorm(a W_o^T + h_in) * gamma + beta   (biased variance over D)
+ *
+ *   h_in      [B][L][D] dense, the layer input of the current segment.
+ *   mem       the layer's memory, read only (the ring is gathered in place,
+ *             never copied).  mem->data must have d_model columns.
+ *   w         this layer's weights.
+ *   u_bias, v_bias  [H][d] dense.
+ *   R         [R_rows][D] dense, row p the encoding of distance p; R_rows >= mem->len + L.
+ *   h_out     [B][L][D] dense; must not alias h_in or the memory.
+ *   workspace device scratch of ws_bytes >= txl_layer_workspace_bytes(dims,
+ *             mem->capacity, dtype), 256-byte aligned.  Holds q, k, v, r, a and
+ *             the pre-LayerNorm sum between the kernels of this call.
+ *
+ * To advance the recurrence the caller then appends h_in (the layer INPUT,
+ * which is what this layer reads at the next segment) with txl_mem_update on
+ * the same stream.
+ */
+int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims,
+                   const void* h_in, const txl_ring* mem, const txl_layer_weights* w,
+                   const void* u_bias, const void* v_bias,
+                   const void* R, int64_t R_rows, void* h_out,
+                   void* workspace, size_t ws_bytes);
+
+/*
+ * Memory update (section 3.2): the memory becomes the last min(M, len + L)
+ * rows of [memory ; h_new].  Only the newest min(L, M) rows of h_new are
+ * copied (into the ring slots that follow the current content); rows that stay
+ * are not moved.  mem->start and mem->len are updated on the host before the
+ * call returns; the copy is enqueued on `stream`.
+ *   h_new  [B][L][d_model] dense, same dtype as the ring.
+ */
+int txl_mem_update(void* stream, int dtype, txl_ring* mem, int64_t B, int64_t d_model,
+                   const void* h_new, int64_t L);
+
+/* Static text for a status, followed by the calling thread's detail of its last error. */
+const char* txl_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TXL_H */

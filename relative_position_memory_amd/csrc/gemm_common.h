@@ -1,0 +1,50 @@
+// Row gather and epilogue helpers shared by the projection GEMM kernels.
+#pragma once
+#include "txl_internal.h"
+
+namespace txl {
+
+// Address of logical row m of the gathered A operand (see RowGather).
+__device__ inline const char* gather_row(const RowGather& a, int64_t m, int es) {
+  const int64_t per = a.mem_len + a.cur_rows;
+  const int64_t b = m / per, t = m - b * per;
+  if (t < a.mem_len) {
+    int64_t slot = a.mem_start + t;
+    if (slot >= a.mem_cap) slot -= a.mem_cap;
+    return (const char*)a.mem + (b * a.mem_cap + slot) * a.lda * es;
+  }
+  return (const char*)a.cur + (b * a.cur_rows + (t - a.mem_len)) * a.lda * es;
+}
+
+__device__ inline const char* weight_row(const WeightPair& w, int64_t n, int es) {
+  return n < w.n_split ? (const char*)w.W0 + n * w.ldw * es
+                       : (const char*)w.W1 + (n - w.n_split) * w.ldw * es;
+}
+
+// Destination of output element (m, n) for EPI_HEADS.
+template <typename T>
+__device__ inline T* heads_dst(const GemmArgs& g, int64_t m, int64_t n) {
+  const Epilogue& e = g.e;
+  const int64_t per = g.a.mem_len + g.a.cur_rows;
+  const int64_t b = m / per, t = m - b * per;
+  const int64_t which = n / e.HD, nn = n - which * e.HD;
+  const int64_t head = nn / e.d, c = nn - head * e.d;
+  T* base = (T*)(which ? e.dst1 : e.dst0);
+  return base + b * e.sb + head * e.sh + t * e.st + c;
+}
+
+template <typename T>
+__device__ inline void epilogue_store(const GemmArgs& g, int64_t m, int64_t n, float acc) {
+  if (g.e.mode == EPI_HEADS) {
+    Elt<T>::store(heads_dst<T>(g, m, n), acc);
+  } else {
+    const T* res = (const T*)g.e.resid + m * g.N + n;
+    g.e.y[m * g.N + n] = acc + Elt<T>::load(res);
+  }
+}
+
+hipError_t launch_gemm_generic(int dtype, const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s);
+bool gemm_mfma_supported(const GemmArgs& g);
+
+}  // namespace txl

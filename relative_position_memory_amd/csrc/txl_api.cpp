@@ -1,0 +1,335 @@
+// C ABI of libtxl.so: argument validation, workspace layout and launch plans.
+// Every check runs before the first launch, so a failing call writes nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/txl.h"
+#include "gemm_common.h"
+#include "txl_internal.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+thread_local char g_msg[640] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TXL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t elt_size(int dtype) { return dtype == TXL_FP32 ? 4 : 2; }
+
+// Byte span [lo, hi) touched by a [n0][n1][n2][d] tensor with strides s0, s1, s2.
+struct Span { uintptr_t lo, hi; };
+Span span4(const void* p, int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2, int64_t s2,
+           int64_t d, int64_t es) {
+  const int64_t last = (n0 - 1) * s0 + (n1 - 1) * s1 + (n2 - 1) * s2 + d;
+  return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)(last * es)};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool stride_ok(int64_t n, int64_t s, int64_t d) { return n <= 1 || s >= d; }
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layout of txl_layer_step (byte offsets, each 256-aligned).
+struct WsLayout {
+  int64_t dp;                      // padded head size of q/k/v/r rows
+  size_t q, k, v, r, a, y, total;  // offsets and total bytes
+};
+WsLayout ws_layout(const txl_layer_dims& dm, int64_t T, int64_t es) {
+  WsLayout w;
+  w.dp = round_up(dm.d_head, 8);
+  const int64_t B = dm.B, H = dm.n_head, L = dm.L;
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up(bytes, 256);
+    return o;
+  };
+  w.q = take(B * H * L * w.dp * es);
+  w.k = take(B * H * T * w.dp * es);
+  w.v = take(B * H * T * w.dp * es);
+  w.r = take(H * T * w.dp * es);
+  w.a = take(B * L * H * dm.d_head * es);
+  w.y = take(B * L * dm.d_model * 4);
+  w.total = off;
+  return w;
+}
+
+int check_dims(const txl_layer_dims* dm) {
+  if (!dm) return fail(TXL_EINVAL, "dims is NULL");
+  if (dm->B < 1 || dm->L < 1 || dm->d_model < 1 || dm->n_head < 1 || dm->d_head < 1)
+    return fail(TXL_EINVAL, "dims must be >= 1 (B=%lld L=%lld D=%lld H=%lld d=%lld)",
+                (long long)dm->B, (long long)dm->L, (long long)dm->d_model,
+                (long long)dm->n_head, (long long)dm->d_head);
+  if (dm->d_head > 128) return fail(TXL_EUNSUPPORTED, "d_head %lld > 128", (long long)dm->d_head);
+  if (!(dm->ln_eps >= 0.f) || !isfinite(dm->ln_eps))
+    return fail(TXL_EINVAL, "ln_eps must be finite and >= 0");
+  if (dm->n_head > 65535 || dm->B > 65535)
+    return fail(TXL_EUNSUPPORTED, "B and n_head must be <= 65535");
+  return TXL_OK;
+}
+
+int check_attn(int dtype, const txl::AttnArgs& a, int64_t r_rows) {
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  if (a.B < 1 || a.H < 1 || a.L < 1 || a.mem_len < 0)
+    return fail(TXL_EINVAL, "B, H, L must be >= 1 and mem_len >= 0");
+  if (a.d < 1) return fail(TXL_EINVAL, "d_head must be >= 1");
+  if (a.d > 128) return fail(TXL_EUNSUPPORTED, "d_head %lld > 128", (long long)a.d);
+  if (a.H > 65535 || a.B > 65535 || a.L > 0x7fffffffLL)
+    return fail(TXL_EUNSUPPORTED, "B, H must be <= 65535 and L < 2^31");
+  if (!a.q || !a.k || !a.v || !a.r || !a.u || !a.vb || !a.out)
+    return fail(TXL_EINVAL, "NULL tensor pointer");
+  const int64_t T = a.mem_len + a.L;
+  if (r_rows < T)
+    return fail(TXL_EINVAL, "r_rows %lld < mem_len + L = %lld", (long long)r_rows, (long long)T);
+  const int64_t ss[] = {a.q_sb, a.q_st, a.q_sh, a.kv_sb, a.kv_st, a.kv_sh, a.r_sp, a.r_sh,
+                        a.o_sb, a.o_st, a.o_sh};
+  for (int64_t s : ss)
+    if (s < 0) return fail(TXL_EINVAL, "negative stride");
+  if (!stride_ok(a.L, a.q_st, a.d) || !stride_ok(a.H, a.q_sh, a.d) ||
+      !stride_ok(T, a.kv_st, a.d) || !stride_ok(a.H, a.kv_sh, a.d) ||
+      !stride_ok(T, a.r_sp, a.d) || !stride_ok(a.H, a.r_sh, a.d) ||
+      !stride_ok(a.L, a.o_st, a.d) || !stride_ok(a.H, a.o_sh, a.d))
+    return fail(TXL_EINVAL, "a token/head stride is below d_head");
+  if (!isfinite(a.scale)) return fail(TXL_EINVAL, "scale is not finite");
+  const int64_t es = elt_size(dtype);
+  const Span so = span4(a.out, a.B, a.o_sb, a.L, a.o_st, a.H, a.o_sh, a.d, es);
+  const Span in[] = {span4(a.q, a.B, a.q_sb, a.L, a.q_st, a.H, a.q_sh, a.d, es),
+                     span4(a.k, a.B, a.kv_sb, T, a.kv_st, a.H, a.kv_sh, a.d, es),
+                     span4(a.v, a.B, a.kv_sb, T, a.kv_st, a.H, a.kv_sh, a.d, es),
+                     span4(a.r, 1, 0, T, a.r_sp, a.H, a.r_sh, a.d, es),
+                     span4(a.u, 1, 0, 1, 0, 1, 0, a.H * a.d, es),
+                     span4(a.vb, 1, 0, 1, 0, 1, 0, a.H * a.d, es)};
+  for (const Span& s : in)
+    if (overlap(so, s)) return fail(TXL_EINVAL, "out overlaps an input");
+  if (a.scores) {
+    const Span sd = {(uintptr_t)a.scores, (uintptr_t)(a.scores + a.B * a.H * a.L * T)};
+    if (overlap(sd, so)) return fail(TXL_EINVAL, "scores_dbg overlaps out");
+    for (const Span& s : in)
+      if (overlap(sd, s)) return fail(TXL_EINVAL, "scores_dbg overlaps an input");
+  }
+  return TXL_OK;
+}
+
+int run_attn(int dtype, const txl::AttnArgs& a, hipStream_t st) {
+  const int64_t T = a.mem_len + a.L;
+  hipError_t e;
+  if (a.scores) {
+    e = txl::launch_fill_f32(a.scores, a.B * a.H * a.L * T, -INFINITY, st);
+    if (e != hipSuccess) return hip_fail(e, "scores fill");
+  }
+  if (dtype == TXL_BF16 && txl::attn_mfma_supported(a))
+    e = txl::launch_attn_mfma(a, num_cus(), st);
+  else
+    e = txl::launch_attn_generic(dtype, a, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return TXL_OK;
+}
+
+int run_gemm(int dtype, const txl::GemmArgs& g, hipStream_t st, const char* what) {
+  if (g.M == 0 || g.N == 0) return TXL_OK;
+  hipError_t e;
+  if (dtype == TXL_BF16 && txl::gemm_mfma_supported(g))
+    e = txl::launch_gemm_mfma(g, st);
+  else
+    e = txl::launch_gemm_generic(dtype, g, st);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return TXL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* txl_status_string(int status) {
+  const char* s;
+  switch (status) {
+    case TXL_OK: s = "TXL_OK"; break;
+    case TXL_EINVAL: s = "TXL_EINVAL: invalid argument"; break;
+    case TXL_EUNSUPPORTED: s = "TXL_EUNSUPPORTED: unsupported configuration"; break;
+    case TXL_EHIP: s = "TXL_EHIP: HIP runtime error"; break;
+    case TXL_EWORKSPACE: s = "TXL_EWORKSPACE: workspace too small"; break;
+    default: s = "unknown txl status"; break;
+  }
+  if (status == TXL_OK || g_detail[0] == 0) {
+    snprintf(g_msg, sizeof(g_msg), "%s", s);
+  } else {
+    snprintf(g_msg, sizeof(g_msg), "%s (%s)", s, g_detail);
+  }
+  return g_msg;
+}
+
+int txl_rel_attn_fwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, int64_t mem_len,
+                     int64_t d_head, const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                     const void* k, const void* v, int64_t kv_sb, int64_t kv_st, int64_t kv_sh,
+                     const void* r, int64_t r_sp, int64_t r_sh, int64_t r_rows,
+                     const void* u_bias, const void* v_bias, float scale, void* out,
+                     int64_t o_sb, int64_t o_st, int64_t o_sh, float* scores_dbg) {
+  g_detail[0] = 0;
+  txl::AttnArgs a;
+  a.B = B; a.H = H; a.L = L; a.mem_len = mem_len; a.d = d_head;
+  a.q = q; a.q_sb = q_sb; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = k; a.v = v; a.kv_sb = kv_sb; a.kv_st = kv_st; a.kv_sh = kv_sh;
+  a.r = r; a.r_sp = r_sp; a.r_sh = r_sh;
+  a.u = u_bias; a.vb = v_bias; a.scale = scale;
+  a.out = out; a.o_sb = o_sb; a.o_st = o_st; a.o_sh = o_sh;
+  a.scores = scores_dbg;
+  const int rc = check_attn(dtype, a, r_rows);
+  if (rc != TXL_OK) return rc;
+  return run_attn(dtype, a, (hipStream_t)stream);
+}
+
+size_t txl_layer_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype) {
+  if (check_dims(dims) != TXL_OK || mem_capacity < 0) return 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
+  return ws_layout(*dims, mem_capacity + dims->L, elt_size(dtype)).total;
+}
+
+int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                   const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
+                   const void* v_bias, const void* R, int64_t R_rows, void* h_out,
+                   void* workspace, size_t ws_bytes) {
+  g_detail[0] = 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  int rc = check_dims(dims);
+  if (rc != TXL_OK) return rc;
+  if (!mem) return fail(TXL_EINVAL, "mem is NULL");
+  if (mem->capacity < 1 || mem->start < 0 || mem->start >= mem->capacity || mem->len < 0 ||
+      mem->len > mem->capacity)
+    return fail(TXL_EINVAL, "ring state (capacity %lld, start %lld, len %lld) is invalid",
+                (long long)mem->capacity, (long long)mem->start, (long long)mem->len);
+  if (!mem->data) return fail(TXL_EINVAL, "mem->data is NULL");
+  if (!w || !w->W_q || !w->W_kE || !w->W_v || !w->W_kR || !w->W_o || !w->ln_gamma ||
+      !w->ln_beta)
+    return fail(TXL_EINVAL, "NULL weight pointer");
+  if (!h_in || !h_out || !u_bias || !v_bias || !R) return fail(TXL_EINVAL, "NULL tensor pointer");
+  if (!workspace) return fail(TXL_EINVAL, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(TXL_EINVAL, "workspace is not 256-byte aligned");
+  const txl_layer_dims dm = *dims;
+  const int64_t B = dm.B, L = dm.L, D = dm.d_model, H = dm.n_head, d = dm.d_head;
+  const int64_t len = mem->len, T = len + L, HD = H * d;
+  if (R_rows < T)
+    return fail(TXL_EINVAL, "R_rows %lld < mem->len + L = %lld", (long long)R_rows, (long long)T);
+  const int64_t es = elt_size(dtype);
+  const size_t need = ws_layout(dm, mem->capacity + L, es).total;
+  if (ws_bytes < need)
+    return fail(TXL_EWORKSPACE, "need %zu bytes, got %zu", need, ws_bytes);
+  const Span sh_in = {(uintptr_t)h_in, (uintptr_t)h_in + (uintptr_t)(B * L * D * es)};
+  const Span sh_out = {(uintptr_t)h_out, (uintptr_t)h_out + (uintptr_t)(B * L * D * es)};
+  const Span sring = {(uintptr_t)mem->data,
+                      (uintptr_t)mem->data + (uintptr_t)(B * mem->capacity * D * es)};
+  const Span sws = {(uintptr_t)workspace, (uintptr_t)workspace + ws_bytes};
+  if (overlap(sh_out, sh_in)) return fail(TXL_EINVAL, "h_out aliases h_in");
+  if (overlap(sh_out, sring)) return fail(TXL_EINVAL, "h_out aliases the memory");
+  if (overlap(sws, sh_in) || overlap(sws, sh_out) || overlap(sws, sring))
+    return fail(TXL_EINVAL, "workspace overlaps an argument");
+
+  const WsLayout ws = ws_layout(dm, T, es);
+  char* base = (char*)workspace;
+  void* q = base + ws.q;
+  void* k = base + ws.k;
+  void* v = base + ws.v;
+  void* r = base + ws.r;
+  void* a = base + ws.a;
+  float* y = (float*)(base + ws.y);
+  const int64_t dp = ws.dp;
+  hipStream_t st = (hipStream_t)stream;
+
+  // k, v over the extended context [memory ; h] (section 3.2): the ring rows are
+  // gathered by the GEMM's row loader, never copied.
+  txl::GemmArgs g{};
+  g.M = B * T; g.N = 2 * HD; g.K = D;
+  g.a = {mem->data, mem->capacity, mem->start, len, h_in, L, D};
+  g.w = {w->W_kE, w->W_v, HD, D};
+  g.e = {txl::EPI_HEADS, k, v, HD, d, H * T * dp, T * dp, dp, nullptr, nullptr};
+  if ((rc = run_gemm(dtype, g, st, "kv projection")) != TXL_OK) return rc;
+  // q from the current rows only
+  g = {};
+  g.M = B * L; g.N = HD; g.K = D;
+  g.a = {nullptr, 1, 0, 0, h_in, L, D};
+  g.w = {w->W_q, w->W_q, HD, D};
+  g.e = {txl::EPI_HEADS, q, q, HD, d, H * L * dp, L * dp, dp, nullptr, nullptr};
+  if ((rc = run_gemm(dtype, g, st, "q projection")) != TXL_OK) return rc;
+  // r = R[0:T] W_kR^T, shared by the whole batch
+  g = {};
+  g.M = T; g.N = HD; g.K = D;
+  g.a = {nullptr, 1, 0, 0, R, T, D};
+  g.w = {w->W_kR, w->W_kR, HD, D};
+  g.e = {txl::EPI_HEADS, r, r, HD, d, 0, T * dp, dp, nullptr, nullptr};
+  if ((rc = run_gemm(dtype, g, st, "r projection")) != TXL_OK) return rc;
+  // attention; output a [B, L, H*d] token-major for the output projection
+  txl::AttnArgs at;
+  at.B = B; at.H = H; at.L = L; at.mem_len = len; at.d = d;
+  at.q = q; at.q_sb = H * L * dp; at.q_st = dp; at.q_sh = L * dp;
+  at.k = k; at.v = v; at.kv_sb = H * T * dp; at.kv_st = dp; at.kv_sh = T * dp;
+  at.r = r; at.r_sp = dp; at.r_sh = T * dp;
+  at.u = u_bias; at.vb = v_bias; at.scale = 1.0f / sqrtf((float)d);
+  at.out = a; at.o_sb = L * HD; at.o_st = HD; at.o_sh = d;
+  at.scores = nullptr;
+  if ((rc = run_attn(dtype, at, st)) != TXL_OK) return rc;
+  // y = a W_o^T + h, then LayerNorm
+  g = {};
+  g.M = B * L; g.N = D; g.K = HD;
+  g.a = {nullptr, 1, 0, 0, a, L, HD};
+  g.w = {w->W_o, w->W_o, D, HD};
+  g.e = {txl::EPI_RESID_F32, nullptr, nullptr, 0, 1, 0, 0, 0, y, h_in};
+  if ((rc = run_gemm(dtype, g, st, "output projection")) != TXL_OK) return rc;
+  hipError_t e = txl::launch_layer_norm(dtype, y, w->ln_gamma, w->ln_beta, dm.ln_eps, B * L, D,
+                                        h_out, st);
+  if (e != hipSuccess) return hip_fail(e, "layer norm");
+  return TXL_OK;
+}
+
+int txl_mem_update(void* stream, int dtype, txl_ring* mem, int64_t B, int64_t d_model,
+                   const void* h_new, int64_t L) {
+  g_detail[0] = 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  if (!mem || !mem->data || !h_new) return fail(TXL_EINVAL, "NULL pointer");
+  if (B < 1 || d_model < 1 || L < 1) return fail(TXL_EINVAL, "B, d_model, L must be >= 1");
+  if (B > 65535) return fail(TXL_EUNSUPPORTED, "B must be <= 65535");
+  const int64_t M = mem->capacity;
+  if (M < 1 || mem->start < 0 || mem->start >= M || mem->len < 0 || mem->len > M)
+    return fail(TXL_EINVAL, "ring state (capacity %lld, start %lld, len %lld) is invalid",
+                (long long)M, (long long)mem->start, (long long)mem->len);
+  const int64_t es = elt_size(dtype);
+  const Span sring = {(uintptr_t)mem->data, (uintptr_t)mem->data + (uintptr_t)(B * M * d_model * es)};
+  const Span sh = {(uintptr_t)h_new, (uintptr_t)h_new + (uintptr_t)(B * L * d_model * es)};
+  if (overlap(sring, sh)) return fail(TXL_EINVAL, "h_new overlaps the memory");
+  const int64_t n = L < M ? L : M;                 // newest rows that survive
+  const int64_t slot0 = (mem->start + mem->len + (L - n)) % M;
+  hipError_t e = txl::launch_ring_copy(dtype, mem->data, M, slot0, h_new, L, L - n, n, B,
+                                       d_model, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ring copy");
+  const int64_t tot = mem->len + L;
+  const int64_t new_len = tot < M ? tot : M;
+  mem->start = (mem->start + tot - new_len) % M;
+  mem->len = new_len;
+  return TXL_OK;
+}
+
+}  // extern "C"

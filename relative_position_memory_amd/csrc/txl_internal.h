@@ -1,0 +1,99 @@
+// Internal launch interfaces of libtxl.so (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace txl {
+
+// ---- element helpers -------------------------------------------------------------
+// bf16 is carried as its 16-bit pattern; widening is a shift, narrowing rounds
+// to nearest even (NaN stays NaN).
+__host__ __device__ inline float bf16_to_f32(uint16_t h) {
+  union { uint32_t u; float f; } x;
+  x.u = (uint32_t)h << 16;
+  return x.f;
+}
+__host__ __device__ inline uint16_t f32_to_bf16(float f) {
+  union { uint32_t u; float f; } x;
+  x.f = f;
+  if ((x.u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((x.u >> 16) | 0x40u);
+  const uint32_t bias = 0x7fffu + ((x.u >> 16) & 1u);
+  return (uint16_t)((x.u + bias) >> 16);
+}
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  __device__ static inline float load(const float* p) { return *p; }
+  __device__ static inline void store(float* p, float v) { *p = v; }
+};
+template <> struct Elt<uint16_t> {
+  __device__ static inline float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ static inline void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// ---- attention ---------------------------------------------------------------------
+struct AttnArgs {
+  int64_t B, H, L, mem_len, d;
+  const void* q; int64_t q_sb, q_st, q_sh;
+  const void* k; const void* v; int64_t kv_sb, kv_st, kv_sh;
+  const void* r; int64_t r_sp, r_sh;
+  const void* u; const void* vb;
+  float scale;
+  void* out; int64_t o_sb, o_st, o_sh;
+  float* scores;  // NULL or [B][H][L][T]
+};
+
+// Any strides, d <= 128, fp32 math.  dtype 0 = fp32, 1 = bf16.
+hipError_t launch_attn_generic(int dtype, const AttnArgs& a, hipStream_t s);
+// bf16 matrix-core path: d <= 64, 16-byte aligned q/k/v/r, strides multiple of 8.
+hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s);
+bool attn_mfma_supported(const AttnArgs& a);
+
+// ---- GEMM: C[m][n] = sum_k A[m][k] * W[n][k] ---------------------------------------
+// Row m of A is gathered: with rows_per_batch = mem_len + cur_rows,
+//   b = m / rows_per_batch, t = m % rows_per_batch,
+//   t <  mem_len: ring row  mem + (b*mem_cap + (mem_start + t) % mem_cap) * lda
+//   t >= mem_len: current   cur + (b*cur_rows + t - mem_len) * lda
+struct RowGather {
+  const void* mem; int64_t mem_cap, mem_start, mem_len;
+  const void* cur; int64_t cur_rows;
+  int64_t lda;
+};
+
+// Two weight matrices may be stacked along n: rows [0, n_split) of the output
+// use W0, rows [n_split, N) use W1 (row n - n_split).
+struct WeightPair {
+  const void* W0; const void* W1; int64_t n_split; int64_t ldw;
+};
+
+enum EpiMode { EPI_HEADS = 0, EPI_RESID_F32 = 1 };
+struct Epilogue {
+  int mode;
+  // EPI_HEADS: column n -> tensor (n / HD), head (n % HD) / d, element (n % HD) % d,
+  //   written to dst[n / HD] + b*sb + head*sh + t*st + elem, (b, t) as in RowGather.
+  void* dst0; void* dst1; int64_t HD, d, sb, sh, st;
+  // EPI_RESID_F32: y[m][n] = acc + resid[m][n]  (y fp32 [M][N], resid dtype [M][N]).
+  float* y; const void* resid;
+};
+
+struct GemmArgs {
+  int64_t M, N, K;
+  RowGather a;
+  WeightPair w;
+  Epilogue e;
+};
+
+hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
+
+// ---- row kernels -------------------------------------------------------------------
+// out[m] = LayerNorm(y[m]) * gamma + beta, biased variance over D.
+hipError_t launch_layer_norm(int dtype, const float* y, const void* gamma, const void* beta,
+                             float eps, int64_t rows, int64_t D, void* out, hipStream_t s);
+// ring[b][(slot0 + t) % cap] = src[b][row0 + t] for t < n, rows of D elements.
+hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0,
+                            const void* src, int64_t src_rows, int64_t row0, int64_t n,
+                            int64_t B, int64_t D, hipStream_t s);
+// p[0 .. n) = value
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
+
+}  // namespace txl

@@ -1,0 +1,159 @@
+"""Thin ctypes binding of libtxl.so (declared in include/txl.h).
+
+Argument marshalling only: torch supplies device memory (data_ptr), strides
+and the current HIP stream; every step of the computation runs in the
+library's HIP kernels.  Importing this module fails loudly if libtxl.so has
+not been built (there is no fallback of any kind).
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtxl.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(or python relative_position_memory_amd/build.py)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+FP32, BF16 = 0, 1
+OK, EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = 0, -1, -2, -3, -4
+
+_i64, _p, _f, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+
+
+class Ring(ctypes.Structure):
+    """txl_ring: the memory of one layer as a ring over [B, capacity, d_model]."""
+    _fields_ = [("data", _p), ("capacity", _i64), ("start", _i64), ("len", _i64)]
+
+
+class LayerDims(ctypes.Structure):
+    _fields_ = [("B", _i64), ("L", _i64), ("d_model", _i64), ("n_head", _i64),
+                ("d_head", _i64), ("ln_eps", _f)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("W_q", _p), ("W_kE", _p), ("W_v", _p), ("W_kR", _p), ("W_o", _p),
+                ("ln_gamma", _p), ("ln_beta", _p)]
+
+
+_lib.txl_rel_attn_fwd.argtypes = ([_p, ctypes.c_int] + [_i64] * 5 + [_p, _i64, _i64, _i64]
+                                  + [_p, _p, _i64, _i64, _i64] + [_p, _i64, _i64, _i64]
+                                  + [_p, _p, _f] + [_p, _i64, _i64, _i64] + [_p])
+_lib.txl_rel_attn_fwd.restype = ctypes.c_int
+_lib.txl_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int]
+_lib.txl_layer_workspace_bytes.restype = _sz
+_lib.txl_layer_step.argtypes = [_p, ctypes.c_int, ctypes.POINTER(LayerDims), _p,
+                                ctypes.POINTER(Ring), ctypes.POINTER(LayerWeights), _p, _p,
+                                _p, _i64, _p, _p, _sz]
+_lib.txl_layer_step.restype = ctypes.c_int
+_lib.txl_mem_update.argtypes = [_p, ctypes.c_int, ctypes.POINTER(Ring), _i64, _i64, _p, _i64]
+_lib.txl_mem_update.restype = ctypes.c_int
+_lib.txl_status_string.argtypes = [ctypes.c_int]
+_lib.txl_status_string.restype = ctypes.c_char_p
+
+
+class TxlError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)}")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return _lib.txl_status_string(int(status)).decode()
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return FP32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise TxlError(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def rel_attn_fwd(q, k, v, r, u, vb, mem_len, out, scale=None, scores=None, stream=None):
+    """txl_rel_attn_fwd on torch tensors.
+
+    q, out [B, L, H, d]; k, v [B, mem_len+L, H, d]; r [R_rows, H, d]; u, vb [H, d]
+    (dense).  Any strides are passed through as long as the last dimension is
+    contiguous.  scores: None or float32 [B, H, L, mem_len+L] contiguous.
+    """
+    B, L, H, d = q.shape
+    for t in (q, k, v, r, out):
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if scores is not None and (scores.dtype != torch.float32 or not scores.is_contiguous()):
+        raise ValueError("scores must be a contiguous float32 tensor")
+    rc = _lib.txl_rel_attn_fwd(
+        _stream(stream), dtype_code(q.dtype), B, H, L, int(mem_len), d,
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2),
+        _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
+        _ptr(r), r.stride(0), r.stride(1), r.shape[0],
+        _ptr(u), _ptr(vb), float(scale),
+        _ptr(out), out.stride(0), out.stride(1), out.stride(2), _ptr(scores))
+    _check(rc, "txl_rel_attn_fwd")
+    return out
+
+
+def layer_dims(B, L, d_model, n_head, d_head, ln_eps=1e-5):
+    return LayerDims(B, L, d_model, n_head, d_head, ln_eps)
+
+
+def workspace_bytes(dims: LayerDims, mem_capacity: int, dtype: torch.dtype) -> int:
+    n = _lib.txl_layer_workspace_bytes(ctypes.byref(dims), int(mem_capacity), dtype_code(dtype))
+    if n == 0:
+        raise ValueError("invalid layer dims")
+    return int(n)
+
+
+def make_ring(data, start=0, length=0) -> Ring:
+    """A Ring over a [B, capacity, d_model] device tensor (kept alive by the caller)."""
+    return Ring(data.data_ptr(), data.shape[1], int(start), int(length))
+
+
+def layer_weights(W) -> LayerWeights:
+    return LayerWeights(*[W[n].data_ptr() for n in
+                          ("W_q", "W_kE", "W_v", "W_kR", "W_o", "gamma", "beta")])
+
+
+def layer_step(dims, h_in, ring, W, u, vb, R, h_out, workspace, stream=None):
+    """txl_layer_step; W is a LayerWeights (see layer_weights) or a dict of tensors."""
+    lw = W if isinstance(W, LayerWeights) else layer_weights(W)
+    rc = _lib.txl_layer_step(_stream(stream), dtype_code(h_in.dtype), ctypes.byref(dims),
+                             _ptr(h_in), ctypes.byref(ring), ctypes.byref(lw), _ptr(u),
+                             _ptr(vb), _ptr(R), R.shape[0], _ptr(h_out), _ptr(workspace),
+                             workspace.numel() * workspace.element_size())
+    _check(rc, "txl_layer_step")
+    return h_out
+
+
+def mem_update(ring, h_new, stream=None):
+    """txl_mem_update: append the newest rows of h_new [B, L, d_model] to the ring."""
+    B, L, D = h_new.shape
+    rc = _lib.txl_mem_update(_stream(stream), dtype_code(h_new.dtype), ctypes.byref(ring),
+                             B, D, _ptr(h_new), L)
+    _check(rc, "txl_mem_update")
+    return ring

@@ -1,0 +1,77 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/txl.h declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "txl.h")
+LIB = os.path.join(ROOT, "relative_position_memory_amd", "libtxl.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(txl_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libtxl.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("txl_rel_attn_fwd", "txl_layer_step", "txl_mem_update",
+              "txl_layer_workspace_bytes", "txl_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    lib.txl_status_string.restype = ctypes.c_char_p
+    for s in (0, -1, -2, -3, -4, 7):
+        assert lib.txl_status_string(s)
+
+
+def test_argument_errors_need_no_gpu():
+    from relative_position_memory_amd import txl
+    lib = txl._lib
+    i64 = ctypes.c_int64
+    # NULL tensors -> EINVAL, before any HIP call
+    args = [None, txl.BF16, 1, 1, 4, 0, 16] + [None, 16, 16, 16] + [None, None, 16, 16, 16] \
+        + [None, 16, 16, 4] + [None, None, 0.25] + [None, 16, 16, 16] + [None]
+    assert lib.txl_rel_attn_fwd(*args) == txl.EINVAL
+    # unsupported dtype and d_head
+    bad = list(args)
+    bad[1] = 7
+    assert lib.txl_rel_attn_fwd(*bad) == txl.EUNSUPPORTED
+    bad = list(args)
+    bad[6] = 200
+    fake = ctypes.c_void_p(0x1000)
+    for idx in (7, 11, 12, 16, 20, 21, 23):
+        bad[idx] = fake
+    assert lib.txl_rel_attn_fwd(*bad) == txl.EUNSUPPORTED
+    assert "d_head" in txl.status_string(txl.EUNSUPPORTED)
+    # workspace size is a pure host computation
+    dims = txl.layer_dims(22, 512, 512, 8, 64)
+    n = txl.workspace_bytes(dims, 512, __import__("torch").bfloat16)
+    assert n >= 2 * (22 * 8 * 1024 * 64 * 2)
+    assert lib.txl_layer_workspace_bytes(ctypes.byref(txl.layer_dims(1, 1, 1, 1, 300)), 1, 1) == 0
+    # ring state errors
+    ring = txl.Ring(0x1000, 4, 5, 0)
+    assert lib.txl_mem_update(None, txl.BF16, ctypes.byref(ring), 1, 8, fake, 2) == txl.EINVAL
+    ring = txl.Ring(0x1000, 4, 0, 0)
+    assert lib.txl_mem_update(None, txl.BF16, ctypes.byref(ring), 1, 8, None, 2) == txl.EINVAL
+    # h_new overlapping the ring
+    assert lib.txl_mem_update(None, txl.BF16, ctypes.byref(ring), 1, 8,
+                              ctypes.c_void_p(0x1000 + 8), 2) == txl.EINVAL
+    assert ring.start == 0 and ring.len == 0

@@ -1,0 +1,213 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+fp32 within 1e-4 and bf16 within 2e-2 max-abs (element by element); bf16
+inputs are rounded once and both sides consume the same rounded values.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from relative_position_memory_amd import inputs as I
+from tests.gpu_util import TOL, dev, host, max_err, need_gpu, ring_logical
+
+pytestmark = pytest.mark.gpu
+
+
+def _txl():
+    need_gpu()
+    from relative_position_memory_amd import txl
+    return txl
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ---- attention entry point -------------------------------------------------------------
+
+def _attn_case(dtype, B, H, L, M, d, seed=0, sigma=1.0, layout="bthd"):
+    txl = _txl()
+    c = I.attention_inputs(B, H, L, M, d, seed=seed, sigma=sigma, sigma_uv=0.5, dtype=dtype)
+    T = M + L
+    if layout == "bthd":
+        q, k, v = dev(c["q"], dtype), dev(c["k"], dtype), dev(c["v"], dtype)
+        r = dev(c["r"], dtype)
+    else:  # head-major storage, passed as permuted views
+        q = dev(c["q"].transpose(0, 2, 1, 3), dtype).permute(0, 2, 1, 3)
+        k = dev(c["k"].transpose(0, 2, 1, 3), dtype).permute(0, 2, 1, 3)
+        v = dev(c["v"].transpose(0, 2, 1, 3), dtype).permute(0, 2, 1, 3)
+        r = dev(c["r"].transpose(1, 0, 2), dtype).permute(1, 0, 2)
+    u, vb = dev(c["u"], dtype), dev(c["vb"], dtype)
+    out = torch.empty((B, L, H, d), dtype=q.dtype, device="cuda")
+    scores = torch.empty((B, H, L, T), dtype=torch.float32, device="cuda")
+    _say(f"attn case dtype={dtype} B={B} H={H} L={L} M={M} d={d} layout={layout}")
+    txl.rel_attn_fwd(q, k, v, r, u, vb, M, out, scores=scores)
+    torch.cuda.synchronize()
+    ref, ref_s = O.rel_attn(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M, want_scores=True)
+    return host(out), scores.cpu().numpy().astype(np.float64), ref, ref_s
+
+
+def _check_scores(got_s, ref_s, tol):
+    fin = np.isfinite(ref_s)
+    assert np.array_equal(fin, np.isfinite(got_s)), "mask pattern differs"
+    assert np.all(got_s[~fin] == -np.inf)
+    assert max_err(got_s[fin], ref_s[fin]) <= tol
+
+
+def _check_argmax(got_s, ref_s):
+    """Exact argmax per query row; a row whose fp64 top-2 gap is below 1e-9 is a tie."""
+    srt = np.sort(ref_s, axis=-1)
+    gap = srt[..., -1] - srt[..., -2]
+    tie = gap < 1e-9
+    am_g, am_r = np.argmax(got_s, axis=-1), np.argmax(ref_s, axis=-1)
+    assert np.all((am_g == am_r) | tie)
+
+
+def test_attn_tiny_fp32():
+    """The tiny workload: B 1, H 2, d 16, L 16, M 16, fp32."""
+    got, got_s, ref, ref_s = _attn_case("fp32", 1, 2, 16, 16, 16)
+    assert max_err(got, ref) <= TOL["fp32"]
+    _check_scores(got_s, ref_s, TOL["fp32"])
+    _check_argmax(got_s, ref_s)
+
+
+@pytest.mark.parametrize("dtype,B,H,L,M,d,layout", [
+    ("fp32", 2, 3, 37, 20, 41, "bthd"),
+    ("fp32", 1, 1, 1, 0, 1, "bthd"),
+    ("fp32", 1, 2, 5, 0, 128, "bhtd"),
+    ("bf16", 1, 2, 16, 16, 16, "bthd"),
+    ("bf16", 2, 2, 130, 70, 64, "bthd"),
+    ("bf16", 2, 2, 130, 70, 64, "bhtd"),
+    ("bf16", 1, 3, 150, 150, 41, "bthd"),
+    ("bf16", 2, 1, 200, 0, 64, "bhtd"),
+    ("bf16", 1, 2, 1, 300, 64, "bhtd"),
+    ("bf16", 1, 2, 77, 333, 48, "bhtd"),
+])
+def test_attn_shapes(dtype, B, H, L, M, d, layout):
+    got, got_s, ref, ref_s = _attn_case(dtype, B, H, L, M, d, seed=B * 7 + L, layout=layout)
+    assert max_err(got, ref) <= TOL[dtype]
+    _check_scores(got_s, ref_s, 5 * TOL[dtype] if dtype == "bf16" else TOL[dtype])
+
+
+def test_attn_argmax_tiny_bf16():
+    got, got_s, ref, ref_s = _attn_case("bf16", 1, 2, 16, 16, 16, seed=3, layout="bhtd")
+    _check_argmax(got_s, ref_s)
+
+
+# ---- layer step and memory --------------------------------------------------------------
+
+def _layer_setup(w, seed=0, mem_len=None, start=0):
+    txl = _txl()
+    x = I.make_inputs(w, seed=seed, layers=1, segments=1)
+    dt = w.dtype
+    W = {n: dev(a, dt) for n, a in x["weights"][0].items()}
+    mem_len = w.M if mem_len is None else mem_len
+    logical = x["mem"][0][:, w.M - mem_len:] if mem_len else x["mem"][0][:, :0]
+    data = torch.zeros((w.B, w.M, w.D), dtype=W["W_q"].dtype, device="cuda")
+    # place logical row t at slot (start + t) % M
+    for t in range(mem_len):
+        data[:, (start + t) % w.M] = dev(logical[:, t], dt)
+    ring = txl.make_ring(data, start, mem_len)
+    h = dev(x["h0"][0], dt)
+    return txl, x, W, data, ring, h, logical
+
+
+def _run_layer(txl, w, W, ring, h, x, dt):
+    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
+    ws = torch.empty(txl.workspace_bytes(dims, w.M, h.dtype), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(h)
+    txl.layer_step(dims, h, ring, W, dev(x["u"], dt), dev(x["v"], dt), dev(x["R"], dt), out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,over,mem_len,start", [
+    ("tiny", {}, None, 0),
+    ("tiny", {}, 5, 13),
+    ("tiny", {}, 0, 0),
+    ("tiny", {"B": 2, "L": 37, "M": 50, "d": 12, "H": 3, "D": 40}, 45, 31),
+])
+def test_layer_step_fp32(name, over, mem_len, start):
+    w = I.workload(name, **over)
+    _say(f"layer fp32 {w} mem_len={mem_len} start={start}")
+    txl, x, W, data, ring, h, logical = _layer_setup(w, mem_len=mem_len, start=start)
+    out = _run_layer(txl, w, W, ring, h, x, "fp32")
+    ref = O.layer_step(x["h0"][0], logical, x["weights"][0], x["u"], x["v"], x["R"])
+    assert max_err(host(out), ref) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("over,mem_len,start", [
+    ({"B": 2, "L": 64, "M": 64, "D": 128, "H": 2, "d": 64}, 64, 0),
+    ({"B": 2, "L": 100, "M": 130, "D": 96, "H": 3, "d": 32}, 130, 77),
+    ({"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
+    ({"B": 1, "L": 33, "M": 200, "D": 128, "H": 2, "d": 64}, 17, 190),
+])
+def test_layer_step_bf16(over, mem_len, start):
+    w = I.workload("charlm", **over)
+    _say(f"layer bf16 {w} mem_len={mem_len} start={start}")
+    txl, x, W, data, ring, h, logical = _layer_setup(w, mem_len=mem_len, start=start)
+    out = _run_layer(txl, w, W, ring, h, x, "bf16")
+    ref = O.layer_step(x["h0"][0], logical, x["weights"][0], x["u"], x["v"], x["R"])
+    assert max_err(host(out), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ring_rotation_is_invisible(dtype):
+    """The same logical memory at different ring offsets gives bit-identical output."""
+    over = {"B": 2, "L": 40, "M": 56, "D": 64, "H": 2, "d": 32, "dtype": dtype}
+    w = I.workload("charlm", **over)
+    outs = []
+    for start in (0, 23, 55):
+        txl, x, W, data, ring, h, logical = _layer_setup(w, start=start)
+        outs.append(_run_layer(txl, w, W, ring, h, x, dtype))
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("M,Ls", [(16, [16, 16, 16]), (10, [4, 4, 7, 3, 12, 1]), (5, [9, 2, 5])])
+def test_mem_update_matches_oracle(M, Ls):
+    txl = _txl()
+    B, D = 2, 24
+    rng = np.random.default_rng(M)
+    data = torch.zeros((B, M, D), dtype=torch.bfloat16, device="cuda")
+    ring = txl.make_ring(data, 3 % M, 0)
+    ref = None
+    for L in Ls:
+        h = I.round_bf16(rng.standard_normal((B, L, D)).astype(np.float32))
+        txl.mem_update(ring, dev(h, "bf16"))
+        ref = O.mem_update(ref, h, M)
+        torch.cuda.synchronize()
+        assert ring.len == ref.shape[1]
+        np.testing.assert_array_equal(host(ring_logical(data, ring)), ref)
+
+
+def test_segments_match_oracle_recurrence():
+    """N = 2 layers x S = 4 segments with the memory update, fp32, tiny dims."""
+    txl = _txl()
+    w = I.workload("tiny", M=24, n_layers=2, n_segments=4, R_rows=40)
+    x = I.make_inputs(w, seed=5)
+    dt = "fp32"
+    Ws = [{n: dev(a, dt) for n, a in lw.items()} for lw in x["weights"]]
+    datas = [torch.zeros((w.B, w.M, w.D), device="cuda") for _ in range(2)]
+    rings = [txl.make_ring(dd, 0, 0) for dd in datas]
+    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
+    ws = torch.empty(txl.workspace_bytes(dims, w.M, torch.float32), dtype=torch.uint8,
+                     device="cuda")
+    u, vb, R = dev(x["u"], dt), dev(x["v"], dt), dev(x["R"], dt)
+    ref_mems = [None, None]
+    for s in range(w.n_segments):
+        h = dev(x["h0"][s], dt)
+        href = x["h0"][s].astype(np.float64)
+        for n in range(2):
+            out = torch.empty_like(h)
+            txl.layer_step(dims, h, rings[n], Ws[n], u, vb, R, out, ws)
+            txl.mem_update(rings[n], h)
+            ref_out = O.layer_step(href, ref_mems[n], x["weights"][n], x["u"], x["v"], x["R"])
+            ref_mems[n] = O.mem_update(ref_mems[n], href, w.M)
+            torch.cuda.synchronize()
+            assert max_err(host(out), ref_out) <= TOL["fp32"], (s, n)
+            h, href = out, ref_out
