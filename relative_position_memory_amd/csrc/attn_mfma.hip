@@ -40,7 +40,7 @@ constexpr int BK = 64;          // keys per tile
 constexpr int DP = 64;          // head size padded for the MFMA k-loop
 constexpr int KP = 72;          // Ks / Rs row pitch (bf16): 144 B, 16B-aligned, conflict-free
 constexpr int VP = 68;          // Vt row pitch (bf16): 136 B, 8B-aligned, conflict-free
-constexpr int RROWS = BQ + BK;  // staged r rows: 191 distances (+1)
+constexpr int RROWS = BQ + BK;  // staged r rows: distances dist_lo .. dist_lo+191
 constexpr int WP = 101;         // W row pitch (floats); read pitch WP-1 = 100
 constexpr int WBUF = 1 + BQW * WP + 3;  // one wave's W buffer (floats), 16B multiple
 constexpr float LOG2E = 1.4426950408889634f;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, 
   if (a.scores) srow_base = a.scores + ((b * a.H + hd) * L) * T;
 
   TileRegs tr;
-  load_tile(tr, a, kb, vbp, rb, 0, len + q0 - (BK - 1), T, tid);
+  load_tile(tr, a, kb, vbp, rb, 0, len + q0 - BK, T, tid);
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int64_t j0 = (int64_t)kt * BK;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, 
     __syncthreads();
     if (kt + 1 < n_kt) {
       const int64_t j1 = j0 + BK;
-      load_tile(tr, a, kb, vbp, rb, j1, len + q0 - j1 - (BK - 1), T, tid);
+      load_tile(tr, a, kb, vbp, rb, j1, len + q0 - j1 - BK, T, tid);
     }
     if (kt > kt_w) continue;
 
@@ -220,7 +220,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, 
       f32x16 w;
 #pragma unroll
       for (int x = 0; x < 16; ++x) w[x] = 0.f;
-      const int rrow = BQW * wave + 94 - 32 * blk - li;  // staged row of A-row li
+      // A-row li of block blk is distance Dw + 31 - 32 blk - li, staged at row
+      // dist - (len + q0 - j0 - 64), which lies in [0, 191]
+      const int rrow = BQW * wave + 95 - 32 * blk - li;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8 ar = lds_b128(&sm.Rs[rrow * KP + 16 * s + 8 * lh]);

@@ -59,13 +59,21 @@ def _check_scores(got_s, ref_s, tol):
     assert max_err(got_s[fin], ref_s[fin]) <= tol
 
 
-def _check_argmax(got_s, ref_s):
-    """Exact argmax per query row; a row whose fp64 top-2 gap is below 1e-9 is a tie."""
+def _check_argmax(got_s, ref_s, tol):
+    """Argmax of each query row's scores.
+
+    Where the oracle's top-2 gap exceeds 2*tol (the scores' error bound on both
+    sides of the comparison) the argmax is unique and must agree exactly.
+    Elsewhere several keys are valid answers: the GPU's choice must score within
+    2*tol of the oracle's maximum.
+    """
     srt = np.sort(ref_s, axis=-1)
-    gap = srt[..., -1] - srt[..., -2]
-    tie = gap < 1e-9
+    gap = srt[..., -1] - srt[..., -2] if ref_s.shape[-1] > 1 else np.full(srt.shape[:-1], np.inf)
+    unique = gap > 2 * tol
     am_g, am_r = np.argmax(got_s, axis=-1), np.argmax(ref_s, axis=-1)
-    assert np.all((am_g == am_r) | tie)
+    assert np.all((am_g == am_r) | ~unique)
+    picked = np.take_along_axis(ref_s, am_g[..., None], axis=-1)[..., 0]
+    assert np.all(srt[..., -1] - picked <= 2 * tol)
 
 
 def test_attn_tiny_fp32():
@@ -73,7 +81,7 @@ def test_attn_tiny_fp32():
     got, got_s, ref, ref_s = _attn_case("fp32", 1, 2, 16, 16, 16)
     assert max_err(got, ref) <= TOL["fp32"]
     _check_scores(got_s, ref_s, TOL["fp32"])
-    _check_argmax(got_s, ref_s)
+    _check_argmax(got_s, ref_s, TOL["fp32"])
 
 
 @pytest.mark.parametrize("dtype,B,H,L,M,d,layout", [
@@ -94,9 +102,53 @@ def test_attn_shapes(dtype, B, H, L, M, d, layout):
     _check_scores(got_s, ref_s, 5 * TOL[dtype] if dtype == "bf16" else TOL[dtype])
 
 
+def _attn_padded(dtype, B, H, L, M, d, dp, seed):
+    """Head-major storage with rows padded to dp elements, passed as [..., :d] views
+    (16-byte aligned rows: the matrix-core layout)."""
+    txl = _txl()
+    c = I.attention_inputs(B, H, L, M, d, seed=seed, sigma=1.0, sigma_uv=0.5, dtype=dtype)
+    T = M + L
+
+    def padded(x, lead_perm, back_perm):
+        y = np.zeros(x.transpose(*lead_perm).shape[:-1] + (dp,), np.float32)
+        y[..., :d] = x.transpose(*lead_perm)
+        return dev(y, dtype)[..., :d].permute(*back_perm)
+
+    q = padded(c["q"], (0, 2, 1, 3), (0, 2, 1, 3))
+    k = padded(c["k"], (0, 2, 1, 3), (0, 2, 1, 3))
+    v = padded(c["v"], (0, 2, 1, 3), (0, 2, 1, 3))
+    r = padded(c["r"], (1, 0, 2), (1, 0, 2))
+    u, vb = dev(c["u"], dtype), dev(c["vb"], dtype)
+    out = torch.empty((B, L, H, d), dtype=q.dtype, device="cuda")
+    scores = torch.empty((B, H, L, T), dtype=torch.float32, device="cuda")
+    _say(f"attn padded dtype={dtype} B={B} H={H} L={L} M={M} d={d} dp={dp}")
+    txl.rel_attn_fwd(q, k, v, r, u, vb, M, out, scores=scores)
+    torch.cuda.synchronize()
+    ref, ref_s = O.rel_attn(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M, want_scores=True)
+    return host(out), scores.cpu().numpy().astype(np.float64), ref, ref_s
+
+
+@pytest.mark.parametrize("B,H,L,M,d,dp", [
+    (1, 2, 128, 128, 64, 64),     # one query tile, full memory
+    (1, 2, 513, 511, 64, 64),     # ragged query and key tails
+    (1, 1, 128, 1600, 64, 64),    # long memory, skinny query block
+    (2, 2, 384, 384, 64, 64),
+    (1, 2, 1, 0, 64, 64),         # a single query, no memory
+    (1, 2, 1, 200, 64, 64),       # a single query over a memory
+    (1, 1, 300, 0, 32, 32),       # no memory, d 32
+    (1, 2, 200, 50, 41, 48),      # ragged head size in padded rows
+    (1, 2, 70, 130, 16, 16),
+])
+def test_attn_matrix_core_layouts(B, H, L, M, d, dp):
+    got, got_s, ref, ref_s = _attn_padded("bf16", B, H, L, M, d, dp, seed=L + M)
+    assert max_err(got, ref) <= TOL["bf16"]
+    _check_scores(got_s, ref_s, 5 * TOL["bf16"])
+    _check_argmax(got_s, ref_s, 5 * TOL["bf16"])
+
+
 def test_attn_argmax_tiny_bf16():
     got, got_s, ref, ref_s = _attn_case("bf16", 1, 2, 16, 16, 16, seed=3, layout="bhtd")
-    _check_argmax(got_s, ref_s)
+    _check_argmax(got_s, ref_s, 5 * TOL["bf16"])
 
 
 # ---- layer step and memory --------------------------------------------------------------
