@@ -9,12 +9,15 @@
 //   position term  W^T = r_win . Qp^T : a 96 x 32 MFMA product of the r rows of
 //                  the 95 distances the tile can need (reversed order) with the
 //                  wave's queries (q+v) -> written to a wave-private LDS buffer.
-//                  Row ii of W (query ii) is stored with pitch P = 101 floats;
+//                  Row ii of W (query ii) is stored with pitch P = 69 floats;
 //                  the score of (query ii, key jj) sits at window index
 //                  31 - ii + jj, i.e. at flat offset ii*(P-1) + jj + 31 : read
 //                  back with pitch P-1 the diagonal "relative shift" becomes a
 //                  plain aligned 16-byte read (the padded-reshape idea of the
 //                  shift, done in LDS addresses instead of memory copies).
+//                  Only the 64 window entries a row reads are written, so the
+//                  rows may overlap and the buffer stays small enough for two
+//                  workgroups per CU.
 //   content term   S^T = K . Qc^T  (q+u), with the position term loaded as the
 //                  MFMA accumulator, so the sum of the four terms costs no ALU op.
 //   softmax        S^T keeps one query per lane: row max and row sum are in-lane
@@ -41,9 +44,10 @@ constexpr int DP = 64;          // head size padded for the MFMA k-loop
 constexpr int KP = 72;          // Ks / Rs row pitch (bf16): 144 B, 16B-aligned, conflict-free
 constexpr int VP = 68;          // Vt row pitch (bf16): 136 B, 8B-aligned, conflict-free
 constexpr int RROWS = BQ + BK;  // staged r rows: distances dist_lo .. dist_lo+191
-constexpr int WP = 101;         // W row pitch (floats); read pitch WP-1 = 100
-constexpr int WBUF = 1 + BQW * WP + 3;  // one wave's W buffer (floats), 16B multiple
+constexpr int WP = 69;          // W row pitch (floats); read pitch WP-1 = 68 (= 4 mod 32)
+constexpr int WBUF = 2208;      // one wave's W buffer (floats): 1 + 31*69 + 94 - 31 < 2208
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int NXCD = 8;         // accelerator dies (XCDs), one L2 each
 
 struct __align__(16) Smem {
   uint16_t Ks[BK * KP];      // K tile, [key][c]
@@ -58,136 +62,182 @@ __device__ inline bf16x8 lds_2xb64(const uint16_t* p0, const uint16_t* p1) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// 8 consecutive bf16 of a head row starting at element c0 (< d); zeros past d.
-__device__ inline uint4 load_chunk(const uint16_t* row, int c0, int d, bool valid) {
-  uint4 z = {0u, 0u, 0u, 0u};
-  if (!valid || c0 >= d) return z;
-  if (c0 + 8 <= d) return *(const uint4*)(row + c0);
-  uint16_t t[8];
+// Column mask of a 16-byte chunk starting at column c0: all-ones words for
+// columns < d, zero words past d (d is not necessarily a multiple of 8).
+__device__ inline uint4 chunk_mask(int c0, int d) {
+  uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = (c0 + e < d) ? row[c0 + e] : (uint16_t)0;
-  uint4 o;
-  o.x = t[0] | ((uint32_t)t[1] << 16);
-  o.y = t[2] | ((uint32_t)t[3] << 16);
-  o.z = t[4] | ((uint32_t)t[5] << 16);
-  o.w = t[6] | ((uint32_t)t[7] << 16);
-  return o;
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = (c0 + 2 * e < d) ? 0x0000ffffu : 0u;
+    const uint32_t hi = (c0 + 2 * e + 1 < d) ? 0xffff0000u : 0u;
+    w[e] = lo | hi;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ inline uint4 and4(uint4 a, uint4 m, bool keep) {
+  const uint32_t k = keep ? 0xffffffffu : 0u;
+  return make_uint4(a.x & m.x & k, a.y & m.y & k, a.z & m.z & k, a.w & m.w & k);
 }
 
-// Registers holding one key tile on its way from HBM to LDS.
+// Registers holding one key tile on its way from HBM to LDS.  The loads are
+// unconditional (addresses clamped into the tensor); rows and columns that
+// are out of range are zeroed when the tile is written to LDS, after the wait
+// that the write needs anyway, so no load is waited for early.
 struct TileRegs {
-  uint4 k[2];     // two 16B chunks of K
-  uint4 v[2];     // V rows 2p and 2p+1, chunk cv
-  uint4 r[6];     // six 16B chunks of the r window
+  uint4 k[2];  // two 16B chunks of K
+  uint4 v[2];  // V rows 2p and 2p+1, chunk cv
+  uint4 r[6];  // six 16B chunks of the r window
 };
 
-__device__ inline void load_tile(TileRegs& tr, const AttnArgs& a, const uint16_t* kb,
-                                 const uint16_t* vbp, const uint16_t* rb, int64_t j0,
-                                 int64_t dist_lo, int64_t T, int tid) {
-  const int d = (int)a.d;
+struct TileGeom {
+  const uint16_t* kb;
+  const uint16_t* vb;
+  const uint16_t* rb;
+  int kv_st, r_sp;  // strides (elements)
+  int T;            // keys
+  int cl_max;       // last loadable chunk index (d_load / 8 - 1)
+};
+
+__device__ inline void load_tile(TileRegs& tr, const TileGeom& g, int j0, int dist_lo, int tid) {
+  const int c = tid & 7;
+  const int cl = c < g.cl_max ? c : g.cl_max;
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    const int idx = tid + 256 * x;
-    const int key = idx >> 3, c = idx & 7;
-    const int64_t j = j0 + key;
-    tr.k[x] = load_chunk(kb + j * a.kv_st, 8 * c, d, j < T);
+    const int j = j0 + (tid >> 3) + 32 * x;
+    const int jc = j < g.T ? j : g.T - 1;
+    tr.k[x] = *(const uint4*)(g.kb + (int64_t)jc * g.kv_st + 8 * cl);
   }
-  {
-    const int cv = tid & 7, p = tid >> 3;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int64_t j = j0 + 2 * p + x;
-      tr.v[x] = load_chunk(vbp + j * a.kv_st, 8 * cv, d, j < T);
-    }
+  for (int x = 0; x < 2; ++x) {
+    const int j = j0 + 2 * (tid >> 3) + x;
+    const int jc = j < g.T ? j : g.T - 1;
+    tr.v[x] = *(const uint4*)(g.vb + (int64_t)jc * g.kv_st + 8 * cl);
   }
 #pragma unroll
   for (int x = 0; x < 6; ++x) {
-    const int idx = tid + 256 * x;
-    const int row = idx >> 3, c = idx & 7;
-    const int64_t dist = dist_lo + row;
-    tr.r[x] = load_chunk(rb + dist * a.r_sp, 8 * c, d, dist >= 0 && dist < T);
+    const int dist = dist_lo + (tid >> 3) + 32 * x;
+    const int dc = dist < 0 ? 0 : (dist < g.T ? dist : g.T - 1);
+    tr.r[x] = *(const uint4*)(g.rb + (int64_t)dc * g.r_sp + 8 * cl);
   }
 }
 
-__device__ inline void store_tile(Smem& sm, const TileRegs& tr, int tid) {
+__device__ inline void store_tile(Smem& sm, const TileRegs& tr, const TileGeom& g, uint4 cmask,
+                                  bool full_cols, int j0, int dist_lo, int tid) {
+  const int c = tid & 7;
+  // interior tile with all 64 columns live: no masking at all (wave-uniform)
+  if (full_cols && j0 + BK <= g.T && dist_lo >= 0 && dist_lo + RROWS <= g.T) {
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int idx = tid + 256 * x;
-    const int key = idx >> 3, c = idx & 7;
-    *(uint4*)&sm.Ks[key * KP + 8 * c] = tr.k[x];
-  }
-  {
-    const int cv = tid & 7, p = tid >> 3;
+    for (int x = 0; x < 2; ++x)
+      *(uint4*)&sm.Ks[((tid >> 3) + 32 * x) * KP + 8 * c] = tr.k[x];
+    const int p = tid >> 3;
     const uint32_t* v0 = (const uint32_t*)&tr.v[0];
     const uint32_t* v1 = (const uint32_t*)&tr.v[1];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      *(uint32_t*)&sm.Vt[(8 * c + 2 * w) * VP + 2 * p] = (v0[w] & 0xffffu) | (v1[w] << 16);
+      *(uint32_t*)&sm.Vt[(8 * c + 2 * w + 1) * VP + 2 * p] = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int x = 0; x < 6; ++x)
+      *(uint4*)&sm.Rs[((tid >> 3) + 32 * x) * KP + 8 * c] = tr.r[x];
+    return;
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int key = (tid >> 3) + 32 * x;
+    *(uint4*)&sm.Ks[key * KP + 8 * c] = and4(tr.k[x], cmask, j0 + key < g.T);
+  }
+  {
+    const int p = tid >> 3;
+    const uint4 a0 = and4(tr.v[0], cmask, j0 + 2 * p < g.T);
+    const uint4 a1 = and4(tr.v[1], cmask, j0 + 2 * p + 1 < g.T);
+    const uint32_t* v0 = (const uint32_t*)&a0;
+    const uint32_t* v1 = (const uint32_t*)&a1;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       // elements 2w (low halves) and 2w+1 (high halves) of keys 2p and 2p+1
       const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);
       const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
-      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w) * VP + 2 * p] = lo;
-      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w + 1) * VP + 2 * p] = hi;
+      *(uint32_t*)&sm.Vt[(8 * c + 2 * w) * VP + 2 * p] = lo;
+      *(uint32_t*)&sm.Vt[(8 * c + 2 * w + 1) * VP + 2 * p] = hi;
     }
   }
 #pragma unroll
   for (int x = 0; x < 6; ++x) {
-    const int idx = tid + 256 * x;
-    const int row = idx >> 3, c = idx & 7;
-    *(uint4*)&sm.Rs[row * KP + 8 * c] = tr.r[x];
+    const int row = (tid >> 3) + 32 * x;
+    const int dist = dist_lo + row;
+    *(uint4*)&sm.Rs[row * KP + 8 * c] = and4(tr.r[x], cmask, dist >= 0 && dist < g.T);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, int groups) {
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, int groups) {
   extern __shared__ __align__(16) char smem_raw[];
   Smem& sm = *(Smem*)smem_raw;
 
-  // All query tiles of one (batch, head) are consecutive, longest first, so
-  // they run together and share K, V and r through L2.
-  const int g = blockIdx.x / nqt;
-  const int qt = nqt - 1 - (int)(blockIdx.x % nqt);
+  // Workgroups are dispatched to the 8 XCDs round-robin by id, and each XCD has
+  // its own L2.  Block id n runs on XCD n % 8 as its (n / 8)-th block; that
+  // XCD takes the (batch, head) groups g = x, x + 8, ... with their query tiles
+  // consecutive and longest first, so the tiles of a group run together on
+  // one L2 and share its K, V and r.
+  const int xcd = blockIdx.x % NXCD, k_on = blockIdx.x / NXCD;
+  const int g = (k_on / nqt) * NXCD + xcd;
+  const int qt = nqt - 1 - k_on % nqt;
   if (g >= groups) return;
   const int64_t b = g / a.H, hd = g % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, lh = lane >> 5;
   const int d = (int)a.d;
-  const int64_t L = a.L, len = a.mem_len, T = len + L;
-  const int64_t q0 = (int64_t)qt * BQ;
-  const int64_t i0w = q0 + wave * BQW;
+  const int L = (int)a.L, len = (int)a.mem_len, T = len + L;
+  const int q0 = qt * BQ;
+  const int i0w = q0 + wave * BQW;
 
-  const uint16_t* kb = (const uint16_t*)a.k + b * a.kv_sb + hd * a.kv_sh;
-  const uint16_t* vbp = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
-  const uint16_t* rb = (const uint16_t*)a.r + hd * a.r_sh;
+  TileGeom tg;
+  tg.kb = (const uint16_t*)a.k + b * a.kv_sb + hd * a.kv_sh;
+  tg.vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
+  tg.rb = (const uint16_t*)a.r + hd * a.r_sh;
+  tg.kv_st = (int)a.kv_st;
+  tg.r_sp = (int)a.r_sp;
+  tg.T = T;
+  tg.cl_max = (int)(a.d_load / 8) - 1;
+  const uint4 cmask = chunk_mask(8 * (tid & 7), d);
+  const bool full_cols = d == DP;
+
+  TileRegs tr;
+  load_tile(tr, tg, 0, len + q0 - BK, tid);
 
   // ---- this lane's query (column li of the MFMA B operand), pre-scaled ----------
   bf16x8 qc[4], qp[4];
   {
-    const int64_t i = i0w + li;
-    const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + i * a.q_st + hd * a.q_sh;
+    const int i = i0w + li;
+    const int ic = i < L ? i : L - 1;
+    const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + (int64_t)ic * a.q_st + hd * a.q_sh;
     const uint16_t* ur = (const uint16_t*)a.u + hd * d;
     const uint16_t* vr = (const uint16_t*)a.vb + hd * d;
     const float sl2 = a.scale * LOG2E;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c0 = 16 * s + 8 * lh;
-      const uint4 raw = load_chunk(qrow, c0, d, i < L);
+      const int cc = c0 / 8 < tg.cl_max ? c0 : 8 * tg.cl_max;
+      const uint4 raw = *(const uint4*)(qrow + cc);
       const uint16_t* rv = (const uint16_t*)&raw;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = c0 + e;
-        float x = bf16_to_f32(rv[e]);
-        const float uu = c < d ? bf16_to_f32(ur[c]) : 0.f;
-        const float vv = c < d ? bf16_to_f32(vr[c]) : 0.f;
-        qc[s][e] = (__bf16)(c < d ? (x + uu) * sl2 : 0.f);
-        qp[s][e] = (__bf16)(c < d ? (x + vv) * sl2 : 0.f);
+        const bool ok = c < d && i < L;
+        const float x = bf16_to_f32(rv[e]);
+        const float uu = c < d ? bf16_to_f32(ur[c < d ? c : 0]) : 0.f;
+        const float vv = c < d ? bf16_to_f32(vr[c < d ? c : 0]) : 0.f;
+        qc[s][e] = (__bf16)(ok ? (x + uu) * sl2 : 0.f);
+        qp[s][e] = (__bf16)(ok ? (x + vv) * sl2 : 0.f);
       }
     }
   }
 
-  const int64_t imax_wg = (q0 + BQ - 1 < L - 1) ? q0 + BQ - 1 : L - 1;
-  const int n_kt = (int)((len + imax_wg) / BK) + 1;
+  const int imax_wg = (q0 + BQ - 1 < L - 1) ? q0 + BQ - 1 : L - 1;
+  const int n_kt = (len + imax_wg) / BK + 1;
   const bool wave_has_rows = i0w < L;
-  const int64_t imax_w = (i0w + BQW - 1 < L - 1) ? i0w + BQW - 1 : L - 1;
-  const int kt_w = wave_has_rows ? (int)((len + imax_w) / BK) : -1;
+  const int imax_w = (i0w + BQW - 1 < L - 1) ? i0w + BQW - 1 : L - 1;
+  const int kt_w = wave_has_rows ? (len + imax_w) / BK : -1;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc[2];
@@ -196,42 +246,46 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, 
 
   float* wb = sm.Wb + wave * WBUF;
   float* srow_base = nullptr;
-  if (a.scores) srow_base = a.scores + ((b * a.H + hd) * L) * T;
-
-  TileRegs tr;
-  load_tile(tr, a, kb, vbp, rb, 0, len + q0 - BK, T, tid);
+  if (a.scores) srow_base = a.scores + ((b * a.H + hd) * a.L) * (int64_t)T;
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int64_t j0 = (int64_t)kt * BK;
+    const int j0 = kt * BK;
     __syncthreads();
-    store_tile(sm, tr, tid);
+    store_tile(sm, tr, tg, cmask, full_cols, j0, len + q0 - j0 - BK, tid);
     __syncthreads();
-    if (kt + 1 < n_kt) {
-      const int64_t j1 = j0 + BK;
-      load_tile(tr, a, kb, vbp, rb, j1, len + q0 - j1 - BK, T, tid);
-    }
+    if (kt + 1 < n_kt) load_tile(tr, tg, j0 + BK, len + q0 - j0 - 2 * BK, tid);
     if (kt > kt_w) continue;
 
-    const int64_t Dw = len + i0w - j0;  // distance of (query 0, key 0) of this wave's tile
+    const int Dw = len + i0w - j0;  // distance of (query 0, key 0) of this wave's tile
 
     // ---- position term: W^T[w''][ii] = r[Dw + 31 - w''] . qp[ii], w'' in [0, 96) ----
+    // A-row li of block blk is distance Dw + 31 - 32 blk - li, staged at row
+    // dist - (len + q0 - j0 - 64), which lies in [0, 191].
+    {
+      f32x16 w[3];
 #pragma unroll
-    for (int blk = 0; blk < 3; ++blk) {
-      f32x16 w;
+      for (int blk = 0; blk < 3; ++blk)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) w[x] = 0.f;
-      // A-row li of block blk is distance Dw + 31 - 32 blk - li, staged at row
-      // dist - (len + q0 - j0 - 64), which lies in [0, 191]
-      const int rrow = BQW * wave + 95 - 32 * blk - li;
+        for (int x = 0; x < 16; ++x) w[blk][x] = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 ar = lds_b128(&sm.Rs[rrow * KP + 16 * s + 8 * lh]);
-        w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qp[s], w, 0, 0, 0);
-      }
-      // lane (query li, half lh), reg x -> window index 32 blk + 8 (x/4) + 4 lh + x%4
+        bf16x8 ar[3];
 #pragma unroll
-      for (int x = 0; x < 16; ++x)
-        wb[1 + li * WP + 32 * blk + 8 * (x >> 2) + 4 * lh + (x & 3)] = w[x];
+        for (int blk = 0; blk < 3; ++blk)
+          ar[blk] = lds_b128(&sm.Rs[(BQW * wave + 95 - 32 * blk - li) * KP + 16 * s + 8 * lh]);
+#pragma unroll
+        for (int blk = 0; blk < 3; ++blk)
+          w[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[blk], qp[s], w[blk], 0, 0, 0);
+      }
+      // lane (query li, half lh), reg x -> window index w'' = 32 blk + 8 (x/4) + 4 lh + x%4;
+      // row li reads w'' in [31 - li, 94 - li] only, and only those are written
+#pragma unroll
+      for (int blk = 0; blk < 3; ++blk)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int wi = 32 * blk + 8 * (x >> 2) + 4 * lh + (x & 3);
+          if (wi + li >= 31 && wi + li <= 94) wb[1 + li * WP + wi] = w[blk][x];
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -240,21 +294,23 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, 
     // ---- content term with the gathered position term as accumulator ------------
     f32x16 sc[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int x4 = 0; x4 < 4; ++x4) {
         // keys jj = 32 kb2 + 8 x4 + 4 lh + t, t = 0..3 -> flat 32 + 100 li + jj
         const f32x4 sp = *(const f32x4*)&wb[32 + (WP - 1) * li + 32 * kb2 + 8 * x4 + 4 * lh];
-        sc[kb2][4 * x4 + 0] = sp[0];
-        sc[kb2][4 * x4 + 1] = sp[1];
-        sc[kb2][4 * x4 + 2] = sp[2];
-        sc[kb2][4 * x4 + 3] = sp[3];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sc[kb2][4 * x4 + t] = sp[t];
       }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 ak = lds_b128(&sm.Ks[(32 * kb2 + li) * KP + 16 * s + 8 * lh]);
-        sc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qc[s], sc[kb2], 0, 0, 0);
-      }
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 ak[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+        ak[kb2] = lds_b128(&sm.Ks[(32 * kb2 + li) * KP + 16 * s + 8 * lh]);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+        sc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kb2], qc[s], sc[kb2], 0, 0, 0);
     }
 
     // ---- causal mask (tiles that reach past the wave's first query only) --------
@@ -264,18 +320,18 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, 
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int jj = 32 * kb2 + 8 * (x >> 2) + 4 * lh + (x & 3);
-          if (jj - li > Dw) sc[kb2][x] = -INFINITY;
+          sc[kb2][x] = (jj - li > Dw) ? -INFINITY : sc[kb2][x];
         }
     }
     if (srow_base) {
-      const int64_t i = i0w + li;
+      const int i = i0w + li;
       if (i < L) {
-        float* srow = srow_base + i * T;
+        float* srow = srow_base + (int64_t)i * T;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int x = 0; x < 16; ++x) {
-            const int64_t j = j0 + 32 * kb2 + 8 * (x >> 2) + 4 * lh + (x & 3);
+            const int j = j0 + 32 * kb2 + 8 * (x >> 2) + 4 * lh + (x & 3);
             if (j < T) srow[j] = sc[kb2][x] * (1.0f / LOG2E);
           }
       }
@@ -301,10 +357,13 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, 
         psum += p;
       }
     l_run = l_run * alpha + psum;
+    // the running max rarely moves after the first tiles: rescale only if it did
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      acc[0][x] *= alpha;
-      acc[1][x] *= alpha;
+      for (int x = 0; x < 16; ++x) {
+        acc[0][x] *= alpha;
+        acc[1][x] *= alpha;
+      }
     }
 
     // ---- O^T += V^T . P^T ------------------------------------------------------------
@@ -314,35 +373,60 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a, int nqt, 
       const int kb2 = s >> 1, v0 = 8 * (s & 1);
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[kb2][v0 + e];
+      bf16x8 av[2];
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const uint16_t* vrow = &sm.Vt[(32 * db + li) * VP + 16 * s + 4 * lh];
-        const bf16x8 av = lds_2xb64(vrow, vrow + 8);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, acc[db], 0, 0, 0);
+        av[db] = lds_2xb64(vrow, vrow + 8);
       }
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[db], pb, acc[db], 0, 0, 0);
     }
   }
 
   // ---- epilogue: out[i][c] = acc / l -------------------------------------------------
   if (!wave_has_rows) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const int64_t i = i0w + li;
+  const int i = i0w + li;
   if (i >= L) return;
   const float inv = 1.f / l_tot;
-  uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + i * a.o_st + hd * a.o_sh;
+  uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
+  const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
+                   ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
+  if (vec) {
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int c = 32 * db + 8 * (x >> 2) + 4 * lh + (x & 3);
-      if (c < d) orow[c] = f32_to_bf16(acc[db][x] * inv);
-    }
+      for (int x4 = 0; x4 < 4; ++x4) {
+        const int c = 32 * db + 8 * x4 + 4 * lh;
+        if (c < d) {
+          uint2 pk;
+          pk.x = f32_to_bf16(acc[db][4 * x4] * inv) |
+                 ((uint32_t)f32_to_bf16(acc[db][4 * x4 + 1] * inv) << 16);
+          pk.y = f32_to_bf16(acc[db][4 * x4 + 2] * inv) |
+                 ((uint32_t)f32_to_bf16(acc[db][4 * x4 + 3] * inv) << 16);
+          *(uint2*)(orow + c) = pk;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int c = 32 * db + 8 * (x >> 2) + 4 * lh + (x & 3);
+        if (c < d) orow[c] = f32_to_bf16(acc[db][x] * inv);
+      }
+  }
 }
 
 }  // namespace
 
 bool attn_mfma_supported(const AttnArgs& a) {
-  if (a.d > DP) return false;
+  if (a.d > DP || a.d_load % 8 != 0 || a.d_load > DP) return false;
+  if (a.mem_len + a.L > 0x7fffffffLL - 2 * BQ) return false;
+  // 32-bit element offsets inside a (batch, head) slab
+  if ((a.mem_len + a.L) * (a.kv_st > a.r_sp ? a.kv_st : a.r_sp) > 0x7fffffffLL) return false;
   const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.r;
   if (al % 16) return false;
   const int64_t st[] = {a.q_sb, a.q_st, a.q_sh, a.kv_sb, a.kv_st, a.kv_sh, a.r_sp, a.r_sh};
@@ -355,7 +439,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
   (void)num_cus;
   const int nqt = (int)((a.L + BQ - 1) / BQ);
   const int groups = (int)(a.B * a.H);
-  const int64_t nblocks = (int64_t)nqt * groups;
+  const int64_t nblocks = (int64_t)nqt * NXCD * ((groups + NXCD - 1) / NXCD);
   const size_t smem = sizeof(Smem);
   static bool attr_set = false;
   if (!attr_set) {

@@ -199,6 +199,7 @@ int txl_rel_attn_fwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
   a.u = u_bias; a.vb = v_bias; a.scale = scale;
   a.out = out; a.o_sb = o_sb; a.o_st = o_st; a.o_sh = o_sh;
   a.scores = scores_dbg;
+  a.d_load = d_head;
   const int rc = check_attn(dtype, a, r_rows);
   if (rc != TXL_OK) return rc;
   return run_attn(dtype, a, (hipStream_t)stream);
@@ -291,6 +292,7 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
   at.u = u_bias; at.vb = v_bias; at.scale = 1.0f / sqrtf((float)d);
   at.out = a; at.o_sb = L * HD; at.o_st = HD; at.o_sh = d;
   at.scores = nullptr;
+  at.d_load = dp;  // workspace rows hold dp readable columns
   if ((rc = run_attn(dtype, at, st)) != TXL_OK) return rc;
   // y = a W_o^T + h, then LayerNorm
   g = {};

@@ -41,6 +41,10 @@ struct AttnArgs {
   float scale;
   void* out; int64_t o_sb, o_st, o_sh;
   float* scores;  // NULL or [B][H][L][T]
+  // Columns of every q/k/v/r row that may be read (>= d).  Equal to d for
+  // caller-owned tensors; the layer step's own workspace rows are padded to a
+  // multiple of 8 and may be read whole (columns >= d are ignored).
+  int64_t d_load;
 };
 
 // Any strides, d <= 128, fp32 math.  dtype 0 = fp32, 1 = bf16.
