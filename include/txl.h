@@ -168,6 +168,23 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims,
                    void* workspace, size_t ws_bytes);
 
 /*
+ * Where txl_layer_step leaves its intermediates in the workspace (section 3.3's
+ * q, k, v, the projected encodings r = R W_kR^T, and the attention output a),
+ * for a call with mem->len == mem_len.  After such a call the workspace holds,
+ * at the returned byte offsets (T = mem_len + L, d_pad = row pitch):
+ *   q [B][H][L][d_pad]   k, v [B][H][T][d_pad]   r [H][T][d_pad]   a [B][L][H*d]
+ * in the call's dtype; columns d .. d_pad-1 of q, k, v, r rows are unspecified.
+ * Returns TXL_OK, or TXL_EINVAL / TXL_EUNSUPPORTED for bad dims or dtype.
+ */
+typedef struct {
+  size_t q, k, v, r, a;  /* byte offsets into the workspace          */
+  int64_t d_pad;         /* row pitch in elements of q, k, v, r rows */
+} txl_workspace_map;
+
+int txl_layer_workspace_map(const txl_layer_dims* dims, int64_t mem_len, int dtype,
+                            txl_workspace_map* map);
+
+/*
  * Memory update (section 3.2): the memory becomes the last min(M, len + L)
  * rows of [memory ; h_new].  Only the newest min(L, M) rows of h_new are
  * copied (into the ring slots that follow the current content); rows that stay

@@ -211,6 +211,24 @@ size_t txl_layer_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacit
   return ws_layout(*dims, mem_capacity + dims->L, elt_size(dtype)).total;
 }
 
+int txl_layer_workspace_map(const txl_layer_dims* dims, int64_t mem_len, int dtype,
+                            txl_workspace_map* map) {
+  g_detail[0] = 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  const int rc = check_dims(dims);
+  if (rc != TXL_OK) return rc;
+  if (!map) return fail(TXL_EINVAL, "map is NULL");
+  if (mem_len < 0) return fail(TXL_EINVAL, "mem_len must be >= 0");
+  const WsLayout w = ws_layout(*dims, mem_len + dims->L, elt_size(dtype));
+  map->q = w.q;
+  map->k = w.k;
+  map->v = w.v;
+  map->r = w.r;
+  map->a = w.a;
+  map->d_pad = w.dp;
+  return TXL_OK;
+}
+
 int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
                    const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
                    const void* v_bias, const void* R, int64_t R_rows, void* h_out,

@@ -157,3 +157,36 @@ def mem_update(ring, h_new, stream=None):
                              B, D, _ptr(h_new), L)
     _check(rc, "txl_mem_update")
     return ring
+
+
+class WorkspaceMap(ctypes.Structure):
+    _fields_ = [("q", _sz), ("k", _sz), ("v", _sz), ("r", _sz), ("a", _sz), ("d_pad", _i64)]
+
+
+_lib.txl_layer_workspace_map.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int,
+                                         ctypes.POINTER(WorkspaceMap)]
+_lib.txl_layer_workspace_map.restype = ctypes.c_int
+
+
+def workspace_views(dims, mem_len, workspace, dtype):
+    """Views of the intermediates txl_layer_step leaves in `workspace`
+    (txl_layer_workspace_map): q [B,L,H,d], k/v [B,T,H,d], r [T,H,d], a [B,L,H,d]."""
+    mp = WorkspaceMap()
+    _check(_lib.txl_layer_workspace_map(ctypes.byref(dims), int(mem_len), dtype_code(dtype),
+                                        ctypes.byref(mp)), "txl_layer_workspace_map")
+    B, L, H, d, dp = dims.B, dims.L, dims.n_head, dims.d_head, mp.d_pad
+    T = mem_len + L
+    es = torch.tensor([], dtype=dtype).element_size()
+
+    def view(off, shape):
+        n = 1
+        for s in shape:
+            n *= s
+        return workspace[off: off + n * es].view(dtype).view(*shape)
+
+    q = view(mp.q, (B, H, L, dp))[..., :d].permute(0, 2, 1, 3)
+    k = view(mp.k, (B, H, T, dp))[..., :d].permute(0, 2, 1, 3)
+    v = view(mp.v, (B, H, T, dp))[..., :d].permute(0, 2, 1, 3)
+    r = view(mp.r, (H, T, dp))[..., :d].permute(1, 0, 2)
+    a = view(mp.a, (B, L, H, d))
+    return {"q": q, "k": k, "v": v, "r": r, "a": a}

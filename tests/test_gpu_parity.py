@@ -263,3 +263,31 @@ def test_segments_match_oracle_recurrence():
             torch.cuda.synchronize()
             assert max_err(host(out), ref_out) <= TOL["fp32"], (s, n)
             h, href = out, ref_out
+
+
+@pytest.mark.parametrize("over,mem_len,start", [
+    ({"B": 2, "L": 200, "M": 130, "D": 256, "H": 4, "d": 64}, 130, 57),
+    ({"B": 3, "L": 129, "M": 300, "D": 136, "H": 3, "d": 40}, 170, 299),
+    ({"B": 1, "L": 64, "M": 64, "D": 512, "H": 8, "d": 64}, 0, 0),
+])
+def test_layer_intermediates_bf16(over, mem_len, start):
+    """q, k, v, r (projection GEMMs with the ring gather) and a (attention) of a
+    layer step, each against the oracle's value of the same quantity."""
+    w = I.workload("charlm", **over)
+    _say(f"intermediates {w} mem_len={mem_len} start={start}")
+    txl, x, W, data, ring, h, logical = _layer_setup(w, mem_len=mem_len, start=start)
+    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
+    ws = torch.empty(txl.workspace_bytes(dims, w.M, h.dtype), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(h)
+    txl.layer_step(dims, h, ring, W, dev(x["u"], "bf16"), dev(x["v"], "bf16"), dev(x["R"], "bf16"),
+                   out, ws)
+    torch.cuda.synchronize()
+    views = txl.workspace_views(dims, mem_len, ws, torch.bfloat16)
+    ref_out, it = O.layer_step(x["h0"][0], logical, x["weights"][0], x["u"], x["v"], x["R"],
+                               want_intermediates=True)
+    for name in ("q", "k", "v", "r", "a"):
+        got, want = host(views[name]), it[name]
+        assert got.shape == want.shape, name
+        err = max_err(got, want)
+        assert err <= TOL["bf16"] and err <= 1e-2 * np.abs(want).max(), (name, err)
+    assert max_err(host(out), ref_out) <= TOL["bf16"]
