@@ -56,6 +56,9 @@ struct __align__(16) Smem {
   float Wb[NW * WBUF];       // position-term windows, one per wave
 };
 
+// fp32 -> bf16 bits with the hardware conversion (round to nearest even)
+__device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
 __device__ inline bf16x8 lds_b128(const uint16_t* p) { return *(const bf16x8*)p; }
 __device__ inline bf16x8 lds_2xb64(const uint16_t* p0, const uint16_t* p1) {
   const bf16x4 a = *(const bf16x4*)p0, b = *(const bf16x4*)p1;
@@ -107,11 +110,15 @@ __device__ inline void load_tile(TileRegs& tr, const TileGeom& g, int j0, int di
     const int jc = j < g.T ? j : g.T - 1;
     tr.k[x] = *(const uint4*)(g.kb + (int64_t)jc * g.kv_st + 8 * cl);
   }
+  // V: key pair p = tid & 31 (fastest, so the transposed LDS writes are
+  // conflict-free), chunk cv = tid >> 5
+  const int cv = tid >> 5;
+  const int cvl = cv < g.cl_max ? cv : g.cl_max;
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    const int j = j0 + 2 * (tid >> 3) + x;
+    const int j = j0 + 2 * (tid & 31) + x;
     const int jc = j < g.T ? j : g.T - 1;
-    tr.v[x] = *(const uint4*)(g.vb + (int64_t)jc * g.kv_st + 8 * cl);
+    tr.v[x] = *(const uint4*)(g.vb + (int64_t)jc * g.kv_st + 8 * cvl);
   }
 #pragma unroll
   for (int x = 0; x < 6; ++x) {
@@ -122,20 +129,20 @@ __device__ inline void load_tile(TileRegs& tr, const TileGeom& g, int j0, int di
 }
 
 __device__ inline void store_tile(Smem& sm, const TileRegs& tr, const TileGeom& g, uint4 cmask,
-                                  bool full_cols, int j0, int dist_lo, int tid) {
+                                  uint4 cmask_v, bool full_cols, int j0, int dist_lo, int tid) {
   const int c = tid & 7;
+  const int p = tid & 31, cv = tid >> 5;
   // interior tile with all 64 columns live: no masking at all (wave-uniform)
   if (full_cols && j0 + BK <= g.T && dist_lo >= 0 && dist_lo + RROWS <= g.T) {
 #pragma unroll
     for (int x = 0; x < 2; ++x)
       *(uint4*)&sm.Ks[((tid >> 3) + 32 * x) * KP + 8 * c] = tr.k[x];
-    const int p = tid >> 3;
     const uint32_t* v0 = (const uint32_t*)&tr.v[0];
     const uint32_t* v1 = (const uint32_t*)&tr.v[1];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      *(uint32_t*)&sm.Vt[(8 * c + 2 * w) * VP + 2 * p] = (v0[w] & 0xffffu) | (v1[w] << 16);
-      *(uint32_t*)&sm.Vt[(8 * c + 2 * w + 1) * VP + 2 * p] = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
+      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w) * VP + 2 * p] = (v0[w] & 0xffffu) | (v1[w] << 16);
+      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w + 1) * VP + 2 * p] = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
     }
 #pragma unroll
     for (int x = 0; x < 6; ++x)
@@ -148,9 +155,8 @@ __device__ inline void store_tile(Smem& sm, const TileRegs& tr, const TileGeom& 
     *(uint4*)&sm.Ks[key * KP + 8 * c] = and4(tr.k[x], cmask, j0 + key < g.T);
   }
   {
-    const int p = tid >> 3;
-    const uint4 a0 = and4(tr.v[0], cmask, j0 + 2 * p < g.T);
-    const uint4 a1 = and4(tr.v[1], cmask, j0 + 2 * p + 1 < g.T);
+    const uint4 a0 = and4(tr.v[0], cmask_v, j0 + 2 * p < g.T);
+    const uint4 a1 = and4(tr.v[1], cmask_v, j0 + 2 * p + 1 < g.T);
     const uint32_t* v0 = (const uint32_t*)&a0;
     const uint32_t* v1 = (const uint32_t*)&a1;
 #pragma unroll
@@ -158,8 +164,8 @@ __device__ inline void store_tile(Smem& sm, const TileRegs& tr, const TileGeom& 
       // elements 2w (low halves) and 2w+1 (high halves) of keys 2p and 2p+1
       const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);
       const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
-      *(uint32_t*)&sm.Vt[(8 * c + 2 * w) * VP + 2 * p] = lo;
-      *(uint32_t*)&sm.Vt[(8 * c + 2 * w + 1) * VP + 2 * p] = hi;
+      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w) * VP + 2 * p] = lo;
+      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w + 1) * VP + 2 * p] = hi;
     }
   }
 #pragma unroll
@@ -200,6 +206,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   tg.T = T;
   tg.cl_max = (int)(a.d_load / 8) - 1;
   const uint4 cmask = chunk_mask(8 * (tid & 7), d);
+  const uint4 cmask_v = chunk_mask(8 * (tid >> 5), d);
   const bool full_cols = d == DP;
 
   TileRegs tr;
@@ -214,21 +221,31 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
     const uint16_t* ur = (const uint16_t*)a.u + hd * d;
     const uint16_t* vr = (const uint16_t*)a.vb + hd * d;
     const float sl2 = a.scale * LOG2E;
+    // u and v rows: 16-byte loads when they are aligned, else element by element
+    const bool uv_vec = (d % 8 == 0) && ((((uintptr_t)a.u) | ((uintptr_t)a.vb)) % 16 == 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c0 = 16 * s + 8 * lh;
       const int cc = c0 / 8 < tg.cl_max ? c0 : 8 * tg.cl_max;
       const uint4 raw = *(const uint4*)(qrow + cc);
       const uint16_t* rv = (const uint16_t*)&raw;
+      uint16_t uh[8], vh[8];
+      if (uv_vec && c0 < d) {
+        *(uint4*)uh = *(const uint4*)(ur + c0);
+        *(uint4*)vh = *(const uint4*)(vr + c0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uh[e] = c0 + e < d ? ur[c0 + e] : (uint16_t)0;
+          vh[e] = c0 + e < d ? vr[c0 + e] : (uint16_t)0;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int c = c0 + e;
-        const bool ok = c < d && i < L;
+        const bool ok = c0 + e < d && i < L;
         const float x = bf16_to_f32(rv[e]);
-        const float uu = c < d ? bf16_to_f32(ur[c < d ? c : 0]) : 0.f;
-        const float vv = c < d ? bf16_to_f32(vr[c < d ? c : 0]) : 0.f;
-        qc[s][e] = (__bf16)(ok ? (x + uu) * sl2 : 0.f);
-        qp[s][e] = (__bf16)(ok ? (x + vv) * sl2 : 0.f);
+        qc[s][e] = (__bf16)(ok ? (x + bf16_to_f32(uh[e])) * sl2 : 0.f);
+        qp[s][e] = (__bf16)(ok ? (x + bf16_to_f32(vh[e])) * sl2 : 0.f);
       }
     }
   }
@@ -251,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int j0 = kt * BK;
     __syncthreads();
-    store_tile(sm, tr, tg, cmask, full_cols, j0, len + q0 - j0 - BK, tid);
+    store_tile(sm, tr, tg, cmask, cmask_v, full_cols, j0, len + q0 - j0 - BK, tid);
     __syncthreads();
     if (kt + 1 < n_kt) load_tile(tr, tg, j0 + BK, len + q0 - j0 - 2 * BK, tid);
     if (kt > kt_w) continue;
@@ -267,25 +284,34 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
       for (int blk = 0; blk < 3; ++blk)
 #pragma unroll
         for (int x = 0; x < 16; ++x) w[blk][x] = 0.f;
+      // all twelve A fragments first, so their LDS latency overlaps
+      bf16x8 ar[3][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 ar[3];
-#pragma unroll
-        for (int blk = 0; blk < 3; ++blk)
-          ar[blk] = lds_b128(&sm.Rs[(BQW * wave + 95 - 32 * blk - li) * KP + 16 * s + 8 * lh]);
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int blk = 0; blk < 3; ++blk)
-          w[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[blk], qp[s], w[blk], 0, 0, 0);
-      }
+          ar[blk][s] = lds_b128(&sm.Rs[(BQW * wave + 95 - 32 * blk - li) * KP + 16 * s + 8 * lh]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int blk = 0; blk < 3; ++blk)
+          w[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[blk][s], qp[s], w[blk], 0, 0, 0);
       // lane (query li, half lh), reg x -> window index w'' = 32 blk + 8 (x/4) + 4 lh + x%4;
-      // row li reads w'' in [31 - li, 94 - li] only, and only those are written
+      // row li reads w'' in [31 - li, 94 - li] only, and only those are written:
+      // all of block 1, the part of block 0 with w'' >= 31 - li and the part of
+      // block 2 with w'' <= 94 - li.  The other values of blocks 0 and 2 go to a
+      // per-lane dump slot (floats 0..31 of the buffer are never read), which
+      // keeps the writes branch-free.
+      float* wrow = wb + 1 + li * WP + 4 * lh;
+      float* dump = wb + li;
+      const int c_l = li + 4 * lh;
 #pragma unroll
-      for (int blk = 0; blk < 3; ++blk)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int wi = 32 * blk + 8 * (x >> 2) + 4 * lh + (x & 3);
-          if (wi + li >= 31 && wi + li <= 94) wb[1 + li * WP + wi] = w[blk][x];
-        }
+      for (int x = 0; x < 16; ++x) {
+        const int off = 8 * (x >> 2) + (x & 3);
+        wrow[32 + off] = w[1][x];
+        *(c_l + off >= 31 ? wrow + off : dump) = w[0][x];
+        *(c_l + off <= 30 ? wrow + 64 + off : dump) = w[2][x];
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -302,15 +328,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 #pragma unroll
         for (int t = 0; t < 4; ++t) sc[kb2][4 * x4 + t] = sp[t];
       }
+    {
+      bf16x8 ak[2][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 ak[2];
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-        ak[kb2] = lds_b128(&sm.Ks[(32 * kb2 + li) * KP + 16 * s + 8 * lh]);
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+          ak[kb2][s] = lds_b128(&sm.Ks[(32 * kb2 + li) * KP + 16 * s + 8 * lh]);
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-        sc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kb2], qc[s], sc[kb2], 0, 0, 0);
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+          sc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kb2][s], qc[s], sc[kb2], 0, 0, 0);
     }
 
     // ---- causal mask (tiles that reach past the wave's first query only) --------
@@ -402,10 +431,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
         const int c = 32 * db + 8 * x4 + 4 * lh;
         if (c < d) {
           uint2 pk;
-          pk.x = f32_to_bf16(acc[db][4 * x4] * inv) |
-                 ((uint32_t)f32_to_bf16(acc[db][4 * x4 + 1] * inv) << 16);
-          pk.y = f32_to_bf16(acc[db][4 * x4 + 2] * inv) |
-                 ((uint32_t)f32_to_bf16(acc[db][4 * x4 + 3] * inv) << 16);
+          pk.x = bf16_bits(acc[db][4 * x4] * inv) |
+                 ((uint32_t)bf16_bits(acc[db][4 * x4 + 1] * inv) << 16);
+          pk.y = bf16_bits(acc[db][4 * x4 + 2] * inv) |
+                 ((uint32_t)bf16_bits(acc[db][4 * x4 + 3] * inv) << 16);
           *(uint2*)(orow + c) = pk;
         }
       }
@@ -415,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int c = 32 * db + 8 * (x >> 2) + 4 * lh + (x & 3);
-        if (c < d) orow[c] = f32_to_bf16(acc[db][x] * inv);
+        if (c < d) orow[c] = bf16_bits(acc[db][x] * inv);
       }
   }
 }
