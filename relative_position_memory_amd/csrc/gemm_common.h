@@ -44,7 +44,9 @@ __device__ inline void epilogue_store(const GemmArgs& g, int64_t m, int64_t n, f
 }
 
 hipError_t launch_gemm_generic(int dtype, const GemmArgs& g, hipStream_t s);
-hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s, int num_cus);
+// Up to four independent problems in one grid (all must be gemm_mfma_supported).
+hipError_t launch_gemm_mfma_multi(const GemmArgs* g, int n, hipStream_t s, int num_cus);
 bool gemm_mfma_supported(const GemmArgs& g);
 
 }  // namespace txl

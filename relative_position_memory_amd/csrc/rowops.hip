@@ -17,27 +17,74 @@ __device__ inline float block_sum(float x, float* red) {
 
 // LayerNorm(Linear(a) + h) of the N-layer procedure (section 3.3): the input
 // y already holds a W_o^T + h in fp32.  Mean and biased variance over D.
+__device__ inline float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// One wavefront per row, four rows per block: no block-level synchronisation.
 template <typename T>
 __global__ __launch_bounds__(256) void layer_norm_kernel(const float* __restrict__ y,
                                                          const T* __restrict__ gamma,
                                                          const T* __restrict__ beta, float eps,
-                                                         int64_t D, T* __restrict__ out) {
-  __shared__ float red[4];
-  const int64_t row = blockIdx.x;
+                                                         int64_t rows, int64_t D,
+                                                         T* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
   const float* x = y + row * D;
   float s = 0.f;
-  for (int64_t c = threadIdx.x; c < D; c += blockDim.x) s += x[c];
-  const float mean = block_sum(s, red) / (float)D;
+  for (int64_t c = lane; c < D; c += 64) s += x[c];
+  const float mean = wave_sum(s) / (float)D;
   float v = 0.f;
-  for (int64_t c = threadIdx.x; c < D; c += blockDim.x) {
+  for (int64_t c = lane; c < D; c += 64) {
     const float t = x[c] - mean;
     v += t * t;
   }
-  const float var = block_sum(v, red) / (float)D;
+  const float var = wave_sum(v) / (float)D;
   const float inv = rsqrtf(var + eps);
   T* o = out + row * D;
-  for (int64_t c = threadIdx.x; c < D; c += blockDim.x)
+  for (int64_t c = lane; c < D; c += 64)
     Elt<T>::store(o + c, (x[c] - mean) * inv * Elt<T>::load(gamma + c) + Elt<T>::load(beta + c));
+}
+
+// The same LayerNorm for D = 256 NV (NV <= 8) with aligned rows: each lane keeps
+// NV float4 chunks of its row in registers (chunk lane + 64 k), one pass over y.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* __restrict__ y,
+                                                             const T* __restrict__ gamma,
+                                                             const T* __restrict__ beta,
+                                                             float eps, int64_t rows,
+                                                             T* __restrict__ out) {
+  constexpr int D = 256 * NV;
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float4* x = (const float4*)(y + row * D);
+  float4 v[NV];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    v[k] = x[lane + 64 * k];
+    s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+  }
+  const float mean = wave_sum(s) / (float)D;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    v[k].x -= mean; v[k].y -= mean; v[k].z -= mean; v[k].w -= mean;
+    q += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
+  }
+  const float inv = rsqrtf(wave_sum(q) / (float)D + eps);
+  T* o = out + row * D;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int c = 4 * (lane + 64 * k);
+    const float r[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      Elt<T>::store(o + c + e, r[e] * inv * Elt<T>::load(gamma + c + e) + Elt<T>::load(beta + c + e));
+  }
 }
 
 // One row of D elements per (t, b), copied with `V`-byte words.
@@ -65,12 +112,30 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
 hipError_t launch_layer_norm(int dtype, const float* y, const void* gamma, const void* beta,
                              float eps, int64_t rows, int64_t D, void* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  if (D % 256 == 0 && D <= 2048 && ((uintptr_t)y % 16) == 0) {
+#define TXL_LN_VEC(NV)                                                                        \
+  if (D == 256 * NV) {                                                                        \
+    if (dtype == 0)                                                                           \
+      hipLaunchKernelGGL((layer_norm_vec_kernel<float, NV>), dim3(blocks), dim3(256), 0, s, y, \
+                         (const float*)gamma, (const float*)beta, eps, rows, (float*)out);    \
+    else                                                                                      \
+      hipLaunchKernelGGL((layer_norm_vec_kernel<uint16_t, NV>), dim3(blocks), dim3(256), 0, s, \
+                         y, (const uint16_t*)gamma, (const uint16_t*)beta, eps, rows,          \
+                         (uint16_t*)out);                                                     \
+    return hipGetLastError();                                                                 \
+  }
+    TXL_LN_VEC(1) TXL_LN_VEC(2) TXL_LN_VEC(3) TXL_LN_VEC(4)
+    TXL_LN_VEC(5) TXL_LN_VEC(6) TXL_LN_VEC(7) TXL_LN_VEC(8)
+#undef TXL_LN_VEC
+  }
   if (dtype == 0)
-    hipLaunchKernelGGL(layer_norm_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s, y,
-                       (const float*)gamma, (const float*)beta, eps, D, (float*)out);
+    hipLaunchKernelGGL(layer_norm_kernel<float>, dim3(blocks), dim3(256), 0, s, y,
+                       (const float*)gamma, (const float*)beta, eps, rows, D, (float*)out);
   else
-    hipLaunchKernelGGL(layer_norm_kernel<uint16_t>, dim3((unsigned)rows), dim3(256), 0, s, y,
-                       (const uint16_t*)gamma, (const uint16_t*)beta, eps, D, (uint16_t*)out);
+    hipLaunchKernelGGL(layer_norm_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, y,
+                       (const uint16_t*)gamma, (const uint16_t*)beta, eps, rows, D,
+                       (uint16_t*)out);
   return hipGetLastError();
 }
 

@@ -155,7 +155,7 @@ int run_gemm(int dtype, const txl::GemmArgs& g, hipStream_t st, const char* what
   if (g.M == 0 || g.N == 0) return TXL_OK;
   hipError_t e;
   if (dtype == TXL_BF16 && txl::gemm_mfma_supported(g))
-    e = txl::launch_gemm_mfma(g, st);
+    e = txl::launch_gemm_mfma(g, st, num_cus());
   else
     e = txl::launch_gemm_generic(dtype, g, st);
   if (e != hipSuccess) return hip_fail(e, what);
@@ -281,26 +281,35 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
 
   // k, v over the extended context [memory ; h] (section 3.2): the ring rows are
   // gathered by the GEMM's row loader, never copied.
-  txl::GemmArgs g{};
-  g.M = B * T; g.N = 2 * HD; g.K = D;
-  g.a = {mem->data, mem->capacity, mem->start, len, h_in, L, D};
-  g.w = {w->W_kE, w->W_v, HD, D};
-  g.e = {txl::EPI_HEADS, k, v, HD, d, H * T * dp, T * dp, dp, nullptr, nullptr};
-  if ((rc = run_gemm(dtype, g, st, "kv projection")) != TXL_OK) return rc;
+  txl::GemmArgs proj[3] = {};
+  txl::GemmArgs& gkv = proj[0];
+  gkv.M = B * T; gkv.N = 2 * HD; gkv.K = D;
+  gkv.a = {mem->data, mem->capacity, mem->start, len, h_in, L, D};
+  gkv.w = {w->W_kE, w->W_v, HD, D};
+  gkv.e = {txl::EPI_HEADS, k, v, HD, d, H * T * dp, T * dp, dp, nullptr, nullptr};
   // q from the current rows only
-  g = {};
-  g.M = B * L; g.N = HD; g.K = D;
-  g.a = {nullptr, 1, 0, 0, h_in, L, D};
-  g.w = {w->W_q, w->W_q, HD, D};
-  g.e = {txl::EPI_HEADS, q, q, HD, d, H * L * dp, L * dp, dp, nullptr, nullptr};
-  if ((rc = run_gemm(dtype, g, st, "q projection")) != TXL_OK) return rc;
+  txl::GemmArgs& gq = proj[1];
+  gq.M = B * L; gq.N = HD; gq.K = D;
+  gq.a = {nullptr, 1, 0, 0, h_in, L, D};
+  gq.w = {w->W_q, w->W_q, HD, D};
+  gq.e = {txl::EPI_HEADS, q, q, HD, d, H * L * dp, L * dp, dp, nullptr, nullptr};
   // r = R[0:T] W_kR^T, shared by the whole batch
-  g = {};
-  g.M = T; g.N = HD; g.K = D;
-  g.a = {nullptr, 1, 0, 0, R, T, D};
-  g.w = {w->W_kR, w->W_kR, HD, D};
-  g.e = {txl::EPI_HEADS, r, r, HD, d, 0, T * dp, dp, nullptr, nullptr};
-  if ((rc = run_gemm(dtype, g, st, "r projection")) != TXL_OK) return rc;
+  txl::GemmArgs& gr = proj[2];
+  gr.M = T; gr.N = HD; gr.K = D;
+  gr.a = {nullptr, 1, 0, 0, R, T, D};
+  gr.w = {w->W_kR, w->W_kR, HD, D};
+  gr.e = {txl::EPI_HEADS, r, r, HD, d, 0, T * dp, dp, nullptr, nullptr};
+  if (dtype == TXL_BF16 && txl::gemm_mfma_supported(gkv) && txl::gemm_mfma_supported(gq) &&
+      txl::gemm_mfma_supported(gr)) {
+    // the three projections share K and run as one grid
+    const hipError_t e = txl::launch_gemm_mfma_multi(proj, 3, st, num_cus());
+    if (e != hipSuccess) return hip_fail(e, "q/kv/r projections");
+  } else {
+    if ((rc = run_gemm(dtype, gkv, st, "kv projection")) != TXL_OK) return rc;
+    if ((rc = run_gemm(dtype, gq, st, "q projection")) != TXL_OK) return rc;
+    if ((rc = run_gemm(dtype, gr, st, "r projection")) != TXL_OK) return rc;
+  }
+  txl::GemmArgs g{};
   // attention; output a [B, L, H*d] token-major for the output projection
   txl::AttnArgs at;
   at.B = B; at.H = H; at.L = L; at.mem_len = len; at.d = d;
