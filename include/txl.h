@@ -77,6 +77,15 @@ typedef enum { TXL_FP32 = 0, TXL_BF16 = 1 } txl_dtype;
  *                     Must not overlap any input.
  *   scores_dbg        NULL, or float [B][H][L][T] dense: receives A (scaled), with
  *                     -INFINITY where masked.  Debug only; it slows the call.
+ *   workspace, ws_bytes  NULL/0, or device scratch of at least
+ *                     txl_rel_attn_workspace_bytes() bytes (it must not overlap
+ *                     any tensor argument).  When the query tiles alone cannot
+ *                     fill the GPU (few batch rows and heads, short segments over
+ *                     a long memory), the matrix-core path splits the keys among
+ *                     several workgroups, keeps their partial softmax states
+ *                     here and merges them with a log-sum-exp.  Without enough
+ *                     workspace it does not split; the result is the same up
+ *                     to rounding.
  *
  * Layouts: any strides with the innermost (c) dimension contiguous are
  * accepted.  bf16 calls whose q/k/v/r base pointers are 16-byte aligned and
@@ -91,7 +100,14 @@ int txl_rel_attn_fwd(void* stream, int dtype,
                      const void* r, int64_t r_sp, int64_t r_sh, int64_t r_rows,
                      const void* u_bias, const void* v_bias, float scale,
                      void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
-                     float* scores_dbg);
+                     float* scores_dbg, void* workspace, size_t ws_bytes);
+
+/*
+ * Scratch bytes txl_rel_attn_fwd can use for a key split at these sizes on the
+ * current device (0: it would not split).  Returns 0 for invalid arguments too.
+ */
+size_t txl_rel_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L,
+                                    int64_t mem_len, int64_t d_head);
 
 /*
  * The memory of one layer (section 3.2: a length-M cache of old hidden states

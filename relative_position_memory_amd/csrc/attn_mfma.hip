@@ -184,10 +184,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   // its own L2.  Block id n runs on XCD n % 8 as its (n / 8)-th block; that
   // XCD takes the (batch, head) groups g = x, x + 8, ... with their query tiles
   // consecutive and longest first, so the tiles of a group run together on
-  // one L2 and share its K, V and r.
+  // one L2 and share its K, V and r.  With a key split, the nsplit workgroups
+  // of one query tile are consecutive as well.
+  const int nsplit = a.nsplit;
+  const int nper = nqt * nsplit;
   const int xcd = blockIdx.x % NXCD, k_on = blockIdx.x / NXCD;
-  const int g = (k_on / nqt) * NXCD + xcd;
-  const int qt = nqt - 1 - k_on % nqt;
+  const int g = (k_on / nper) * NXCD + xcd;
+  const int qt = nqt - 1 - (k_on % nper) / nsplit;
+  const int split = (k_on % nper) % nsplit;
   if (g >= groups) return;
   const int64_t b = g / a.H, hd = g % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -209,8 +213,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const uint4 cmask_v = chunk_mask(8 * (tid >> 5), d);
   const bool full_cols = d == DP;
 
+  // key tiles of this workgroup: all tiles up to the last query's last key,
+  // or this split's share of them
+  const int imax_wg = (q0 + BQ - 1 < L - 1) ? q0 + BQ - 1 : L - 1;
+  const int n_kt = (len + imax_wg) / BK + 1;
+  const int kt_lo = (split * n_kt) / nsplit, kt_hi = ((split + 1) * n_kt) / nsplit;
+  const bool wave_has_rows = i0w < L;
+  const int imax_w = (i0w + BQW - 1 < L - 1) ? i0w + BQW - 1 : L - 1;
+  const int kt_w = wave_has_rows ? (len + imax_w) / BK : -1;
+
   TileRegs tr;
-  load_tile(tr, tg, 0, len + q0 - BK, tid);
+  if (kt_lo < kt_hi) load_tile(tr, tg, kt_lo * BK, len + q0 - kt_lo * BK - BK, tid);
 
   // ---- this lane's query (column li of the MFMA B operand), pre-scaled ----------
   bf16x8 qc[4], qp[4];
@@ -250,12 +263,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
     }
   }
 
-  const int imax_wg = (q0 + BQ - 1 < L - 1) ? q0 + BQ - 1 : L - 1;
-  const int n_kt = (len + imax_wg) / BK + 1;
-  const bool wave_has_rows = i0w < L;
-  const int imax_w = (i0w + BQW - 1 < L - 1) ? i0w + BQW - 1 : L - 1;
-  const int kt_w = wave_has_rows ? (len + imax_w) / BK : -1;
-
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc[2];
 #pragma unroll
@@ -265,12 +272,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   float* srow_base = nullptr;
   if (a.scores) srow_base = a.scores + ((b * a.H + hd) * a.L) * (int64_t)T;
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
     const int j0 = kt * BK;
     __syncthreads();
     store_tile(sm, tr, tg, cmask, cmask_v, full_cols, j0, len + q0 - j0 - BK, tid);
     __syncthreads();
-    if (kt + 1 < n_kt) load_tile(tr, tg, j0 + BK, len + q0 - j0 - 2 * BK, tid);
+    if (kt + 1 < kt_hi) load_tile(tr, tg, j0 + BK, len + q0 - j0 - 2 * BK, tid);
     if (kt > kt_w) continue;
 
     const int Dw = len + i0w - j0;  // distance of (query 0, key 0) of this wave's tile
@@ -374,14 +381,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
       for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sc[kb2][x]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // a split's tiles can hide every key of a query so far: keep the max at
+    // -inf then, with zero weights and no NaN from (-inf) - (-inf)
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const float p = __builtin_amdgcn_exp2f(sc[kb2][x] - m_new);
+        const float p = __builtin_amdgcn_exp2f(sc[kb2][x] - m_use);
         sc[kb2][x] = p;
         psum += p;
       }
@@ -419,6 +429,24 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const int i = i0w + li;
   if (i >= L) return;
+  if (nsplit > 1) {
+    // unnormalised partial of this split: acc (all 64 columns), max and sum
+    const int64_t row = ((int64_t)split * groups + g) * a.L + i;
+    float* pa = a.part_acc + row * DP;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int x4 = 0; x4 < 4; ++x4) {
+        const int c = 32 * db + 8 * x4 + 4 * lh;
+        *(f32x4*)(pa + c) = {acc[db][4 * x4], acc[db][4 * x4 + 1], acc[db][4 * x4 + 2],
+                             acc[db][4 * x4 + 3]};
+      }
+    if (lh == 0) {
+      a.part_ml[2 * row] = m_run;
+      a.part_ml[2 * row + 1] = l_tot;
+    }
+    return;
+  }
   const float inv = 1.f / l_tot;
   uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
   const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
@@ -449,7 +477,51 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   }
 }
 
+// Log-sum-exp merge of the key splits of one (query, batch*head) per wavefront:
+//   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+// Split 0 holds key 0, visible to every query, so M is finite.
+__global__ __launch_bounds__(64) void attn_split_merge_kernel(AttnArgs a) {
+  const int64_t i = blockIdx.x, g = blockIdx.y;
+  const int c = threadIdx.x;
+  const int64_t G = a.B * a.H;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * ((s * G + g) * a.L + i)]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const int64_t row = (s * G + g) * a.L + i;
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * row] - M);
+    den += w * a.part_ml[2 * row + 1];
+    num += w * a.part_acc[row * DP + c];
+  }
+  if (c < a.d) {
+    const int64_t b = g / a.H, hd = g % a.H;
+    uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + i * a.o_st + hd * a.o_sh;
+    orow[c] = bf16_bits(num / den);
+  }
+}
+
 }  // namespace
+
+int attn_mfma_plan_splits(const AttnArgs& a, int num_cus) {
+  // split the keys only when the query tiles cannot give every CU two workgroups
+  const int64_t nqt = (a.L + BQ - 1) / BQ;
+  const int64_t base = nqt * a.B * a.H;
+  if (base >= 2LL * num_cus) return 1;
+  const int64_t imax0 = (BQ - 1 < a.L - 1) ? BQ - 1 : a.L - 1;
+  const int64_t tiles0 = (a.mem_len + imax0) / BK + 1;  // fewest tiles of any query tile
+  int64_t ns = (2LL * num_cus + base - 1) / base;
+  // at least two key tiles per split: with one, each workgroup's fixed start-up
+  // (q, u, v and the first tile) outweighs its work
+  if (ns > tiles0 / 2) ns = tiles0 / 2;
+  if (ns > 16) ns = 16;
+  return ns < 2 ? 1 : (int)ns;
+}
+
+size_t attn_split_bytes(const AttnArgs& a, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t rows = (size_t)nsplit * (size_t)(a.B * a.H) * (size_t)a.L;
+  return rows * DP * sizeof(float) + rows * 2 * sizeof(float) + 256;
+}
 
 bool attn_mfma_supported(const AttnArgs& a) {
   if (a.d > DP || a.d_load % 8 != 0 || a.d_load > DP) return false;
@@ -468,7 +540,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
   (void)num_cus;
   const int nqt = (int)((a.L + BQ - 1) / BQ);
   const int groups = (int)(a.B * a.H);
-  const int64_t nblocks = (int64_t)nqt * NXCD * ((groups + NXCD - 1) / NXCD);
+  const int nsplit = a.nsplit > 1 ? a.nsplit : 1;
+  const int64_t nblocks = (int64_t)nqt * nsplit * NXCD * ((groups + NXCD - 1) / NXCD);
   const size_t smem = sizeof(Smem);
   static bool attr_set = false;
   if (!attr_set) {
@@ -477,8 +550,14 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(attn_mfma_kernel, dim3((unsigned)nblocks), dim3(256), smem, s, a, nqt,
+  AttnArgs aa = a;
+  aa.nsplit = nsplit;
+  hipLaunchKernelGGL(attn_mfma_kernel, dim3((unsigned)nblocks), dim3(256), smem, s, aa, nqt,
                      groups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  hipLaunchKernelGGL(attn_split_merge_kernel, dim3((unsigned)a.L, (unsigned)groups), dim3(64),
+                     0, s, aa);
   return hipGetLastError();
 }
 

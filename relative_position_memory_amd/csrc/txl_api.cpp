@@ -58,9 +58,10 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // Workspace layout of txl_layer_step (byte offsets, each 256-aligned).
 struct WsLayout {
   int64_t dp;                      // padded head size of q/k/v/r rows
-  size_t q, k, v, r, a, y, total;  // offsets and total bytes
+  size_t q, k, v, r, a, y, part, total;  // offsets and total bytes
 };
-WsLayout ws_layout(const txl_layer_dims& dm, int64_t T, int64_t es) {
+// part_bytes: room for the attention's key-split partials (0 when it does not split)
+WsLayout ws_layout(const txl_layer_dims& dm, int64_t T, int64_t es, size_t part_bytes = 0) {
   WsLayout w;
   w.dp = round_up(dm.d_head, 8);
   const int64_t B = dm.B, H = dm.n_head, L = dm.L;
@@ -76,6 +77,7 @@ WsLayout ws_layout(const txl_layer_dims& dm, int64_t T, int64_t es) {
   w.r = take(H * T * w.dp * es);
   w.a = take(B * L * H * dm.d_head * es);
   w.y = take(B * L * dm.d_model * 4);
+  w.part = take((int64_t)part_bytes);
   w.total = off;
   return w;
 }
@@ -136,17 +138,50 @@ int check_attn(int dtype, const txl::AttnArgs& a, int64_t r_rows) {
   return TXL_OK;
 }
 
-int run_attn(int dtype, const txl::AttnArgs& a, hipStream_t st) {
+// Splits of the key axis the matrix-core attention would use (1 = none).
+int attn_plan(int dtype, const txl::AttnArgs& a) {
+  if (dtype != TXL_BF16 || !txl::attn_mfma_supported(a)) return 1;
+  return txl::attn_mfma_plan_splits(a, num_cus());
+}
+
+// Bytes of key-split partials the layer step's attention needs at this memory length.
+size_t layer_part_bytes(const txl_layer_dims& dm, int64_t mem_len, int dtype) {
+  txl::AttnArgs a{};
+  const int64_t dp = round_up(dm.d_head, 8), T = mem_len + dm.L;
+  a.B = dm.B; a.H = dm.n_head; a.L = dm.L; a.mem_len = mem_len; a.d = dm.d_head;
+  a.d_load = dp;
+  a.q = a.k = a.v = a.r = (const void*)(uintptr_t)256;  // workspace regions are aligned
+  a.q_sb = dm.n_head * dm.L * dp; a.q_st = dp; a.q_sh = dm.L * dp;
+  a.kv_sb = dm.n_head * T * dp; a.kv_st = dp; a.kv_sh = T * dp;
+  a.r_sp = dp; a.r_sh = T * dp;
+  return txl::attn_split_bytes(a, attn_plan(dtype, a));
+}
+
+// Runs the attention; scratch (may be NULL) holds the key-split partials when
+// the plan splits the keys and scratch_bytes covers them, else no split.
+int run_attn(int dtype, txl::AttnArgs a, void* scratch, size_t scratch_bytes, hipStream_t st) {
   const int64_t T = a.mem_len + a.L;
   hipError_t e;
   if (a.scores) {
     e = txl::launch_fill_f32(a.scores, a.B * a.H * a.L * T, -INFINITY, st);
     if (e != hipSuccess) return hip_fail(e, "scores fill");
   }
-  if (dtype == TXL_BF16 && txl::attn_mfma_supported(a))
+  a.nsplit = 1;
+  a.part_acc = nullptr;
+  a.part_ml = nullptr;
+  if (dtype == TXL_BF16 && txl::attn_mfma_supported(a)) {
+    const int ns = attn_plan(dtype, a);
+    if (ns > 1 && scratch && scratch_bytes >= txl::attn_split_bytes(a, ns)) {
+      const size_t rows = (size_t)ns * (size_t)(a.B * a.H) * (size_t)a.L;
+      char* base = (char*)(((uintptr_t)scratch + 255) & ~(uintptr_t)255);
+      a.nsplit = ns;
+      a.part_acc = (float*)base;
+      a.part_ml = (float*)(base + rows * 64 * sizeof(float));
+    }
     e = txl::launch_attn_mfma(a, num_cus(), st);
-  else
+  } else {
     e = txl::launch_attn_generic(dtype, a, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return TXL_OK;
 }
@@ -189,9 +224,10 @@ int txl_rel_attn_fwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
                      const void* k, const void* v, int64_t kv_sb, int64_t kv_st, int64_t kv_sh,
                      const void* r, int64_t r_sp, int64_t r_sh, int64_t r_rows,
                      const void* u_bias, const void* v_bias, float scale, void* out,
-                     int64_t o_sb, int64_t o_st, int64_t o_sh, float* scores_dbg) {
+                     int64_t o_sb, int64_t o_st, int64_t o_sh, float* scores_dbg,
+                     void* workspace, size_t ws_bytes) {
   g_detail[0] = 0;
-  txl::AttnArgs a;
+  txl::AttnArgs a{};
   a.B = B; a.H = H; a.L = L; a.mem_len = mem_len; a.d = d_head;
   a.q = q; a.q_sb = q_sb; a.q_st = q_st; a.q_sh = q_sh;
   a.k = k; a.v = v; a.kv_sb = kv_sb; a.kv_st = kv_st; a.kv_sh = kv_sh;
@@ -200,15 +236,44 @@ int txl_rel_attn_fwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
   a.out = out; a.o_sb = o_sb; a.o_st = o_st; a.o_sh = o_sh;
   a.scores = scores_dbg;
   a.d_load = d_head;
+  a.nsplit = 1;
   const int rc = check_attn(dtype, a, r_rows);
   if (rc != TXL_OK) return rc;
-  return run_attn(dtype, a, (hipStream_t)stream);
+  if (workspace) {
+    const int64_t T = mem_len + L;
+    const Span sw = {(uintptr_t)workspace, (uintptr_t)workspace + ws_bytes};
+    const int64_t es = elt_size(dtype);
+    const Span io[] = {span4(a.out, B, o_sb, L, o_st, H, o_sh, d_head, es),
+                       span4(a.q, B, q_sb, L, q_st, H, q_sh, d_head, es),
+                       span4(a.k, B, kv_sb, T, kv_st, H, kv_sh, d_head, es),
+                       span4(a.v, B, kv_sb, T, kv_st, H, kv_sh, d_head, es),
+                       span4(a.r, 1, 0, T, r_sp, H, r_sh, d_head, es)};
+    for (const Span& s : io)
+      if (overlap(sw, s)) return fail(TXL_EINVAL, "workspace overlaps a tensor argument");
+  }
+  return run_attn(dtype, a, workspace, ws_bytes, (hipStream_t)stream);
+}
+
+size_t txl_rel_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L, int64_t mem_len,
+                                    int64_t d_head) {
+  if ((dtype != TXL_FP32 && dtype != TXL_BF16) || B < 1 || H < 1 || L < 1 || mem_len < 0 ||
+      d_head < 1 || d_head > 128)
+    return 0;
+  txl::AttnArgs a{};
+  a.B = B; a.H = H; a.L = L; a.mem_len = mem_len; a.d = d_head; a.d_load = d_head;
+  // the plan depends only on the shapes; layouts are taken as aligned head-major
+  a.q = a.k = a.v = a.r = (const void*)(uintptr_t)256;
+  a.q_sb = a.q_st = a.q_sh = a.kv_sb = a.kv_st = a.kv_sh = a.r_sp = a.r_sh = 64;
+  const int ns = attn_plan(dtype, a);
+  return txl::attn_split_bytes(a, ns);
 }
 
 size_t txl_layer_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype) {
   if (check_dims(dims) != TXL_OK || mem_capacity < 0) return 0;
   if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
-  return ws_layout(*dims, mem_capacity + dims->L, elt_size(dtype)).total;
+  return ws_layout(*dims, mem_capacity + dims->L, elt_size(dtype),
+                   layer_part_bytes(*dims, mem_capacity, dtype))
+      .total;
 }
 
 int txl_layer_workspace_map(const txl_layer_dims* dims, int64_t mem_len, int dtype,
@@ -255,7 +320,8 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
   if (R_rows < T)
     return fail(TXL_EINVAL, "R_rows %lld < mem->len + L = %lld", (long long)R_rows, (long long)T);
   const int64_t es = elt_size(dtype);
-  const size_t need = ws_layout(dm, mem->capacity + L, es).total;
+  const size_t need =
+      ws_layout(dm, mem->capacity + L, es, layer_part_bytes(dm, mem->capacity, dtype)).total;
   if (ws_bytes < need)
     return fail(TXL_EWORKSPACE, "need %zu bytes, got %zu", need, ws_bytes);
   const Span sh_in = {(uintptr_t)h_in, (uintptr_t)h_in + (uintptr_t)(B * L * D * es)};
@@ -311,7 +377,7 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
   }
   txl::GemmArgs g{};
   // attention; output a [B, L, H*d] token-major for the output projection
-  txl::AttnArgs at;
+  txl::AttnArgs at{};
   at.B = B; at.H = H; at.L = L; at.mem_len = len; at.d = d;
   at.q = q; at.q_sb = H * L * dp; at.q_st = dp; at.q_sh = L * dp;
   at.k = k; at.v = v; at.kv_sb = H * T * dp; at.kv_st = dp; at.kv_sh = T * dp;
@@ -320,7 +386,7 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
   at.out = a; at.o_sb = L * HD; at.o_st = HD; at.o_sh = d;
   at.scores = nullptr;
   at.d_load = dp;  // workspace rows hold dp readable columns
-  if ((rc = run_attn(dtype, at, st)) != TXL_OK) return rc;
+  if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
   // y = a W_o^T + h, then LayerNorm
   g = {};
   g.M = B * L; g.N = D; g.K = HD;

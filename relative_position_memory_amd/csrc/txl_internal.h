@@ -45,7 +45,20 @@ struct AttnArgs {
   // caller-owned tensors; the layer step's own workspace rows are padded to a
   // multiple of 8 and may be read whole (columns >= d are ignored).
   int64_t d_load;
+  // Split over keys (matrix-core path only): 1 = off.  With nsplit > 1 each
+  // query tile's key tiles are divided among nsplit workgroups that write
+  // unnormalised partials, merged afterwards:
+  //   part_acc [nsplit][B*H][L][64] fp32, part_ml [nsplit][B*H][L][2] fp32 (max in
+  //   the exp2 domain, sum of exponentials).
+  int nsplit;
+  float* part_acc;
+  float* part_ml;
 };
+
+// Number of key splits the matrix-core attention would use for these shapes on
+// a device with num_cus CUs (1 = no split), and the partials' bytes it needs.
+int attn_mfma_plan_splits(const AttnArgs& a, int num_cus);
+size_t attn_split_bytes(const AttnArgs& a, int nsplit);
 
 // Any strides, d <= 128, fp32 math.  dtype 0 = fp32, 1 = bf16.
 hipError_t launch_attn_generic(int dtype, const AttnArgs& a, hipStream_t s);

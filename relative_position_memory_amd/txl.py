@@ -41,8 +41,10 @@ class LayerWeights(ctypes.Structure):
 
 _lib.txl_rel_attn_fwd.argtypes = ([_p, ctypes.c_int] + [_i64] * 5 + [_p, _i64, _i64, _i64]
                                   + [_p, _p, _i64, _i64, _i64] + [_p, _i64, _i64, _i64]
-                                  + [_p, _p, _f] + [_p, _i64, _i64, _i64] + [_p])
+                                  + [_p, _p, _f] + [_p, _i64, _i64, _i64] + [_p, _p, _sz])
 _lib.txl_rel_attn_fwd.restype = ctypes.c_int
+_lib.txl_rel_attn_workspace_bytes.argtypes = [ctypes.c_int] + [_i64] * 5
+_lib.txl_rel_attn_workspace_bytes.restype = _sz
 _lib.txl_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int]
 _lib.txl_layer_workspace_bytes.restype = _sz
 _lib.txl_layer_step.argtypes = [_p, ctypes.c_int, ctypes.POINTER(LayerDims), _p,
@@ -90,12 +92,19 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def rel_attn_fwd(q, k, v, r, u, vb, mem_len, out, scale=None, scores=None, stream=None):
+def rel_attn_workspace_bytes(dtype, B, H, L, mem_len, d):
+    """txl_rel_attn_workspace_bytes: scratch the key split can use (0 = no split)."""
+    return int(_lib.txl_rel_attn_workspace_bytes(dtype_code(dtype), B, H, L, int(mem_len), d))
+
+
+def rel_attn_fwd(q, k, v, r, u, vb, mem_len, out, scale=None, scores=None, stream=None,
+                 workspace=None):
     """txl_rel_attn_fwd on torch tensors.
 
     q, out [B, L, H, d]; k, v [B, mem_len+L, H, d]; r [R_rows, H, d]; u, vb [H, d]
     (dense).  Any strides are passed through as long as the last dimension is
     contiguous.  scores: None or float32 [B, H, L, mem_len+L] contiguous.
+    workspace: None or a uint8 device tensor of rel_attn_workspace_bytes() bytes.
     """
     B, L, H, d = q.shape
     for t in (q, k, v, r, out):
@@ -113,7 +122,8 @@ def rel_attn_fwd(q, k, v, r, u, vb, mem_len, out, scale=None, scores=None, strea
         _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
         _ptr(r), r.stride(0), r.stride(1), r.shape[0],
         _ptr(u), _ptr(vb), float(scale),
-        _ptr(out), out.stride(0), out.stride(1), out.stride(2), _ptr(scores))
+        _ptr(out), out.stride(0), out.stride(1), out.stride(2), _ptr(scores),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size())
     _check(rc, "txl_rel_attn_fwd")
     return out
 

@@ -48,7 +48,7 @@ def test_argument_errors_need_no_gpu():
     i64 = ctypes.c_int64
     # NULL tensors -> EINVAL, before any HIP call
     args = [None, txl.BF16, 1, 1, 4, 0, 16] + [None, 16, 16, 16] + [None, None, 16, 16, 16] \
-        + [None, 16, 16, 4] + [None, None, 0.25] + [None, 16, 16, 16] + [None]
+        + [None, 16, 16, 4] + [None, None, 0.25] + [None, 16, 16, 16] + [None, None, 0]
     assert lib.txl_rel_attn_fwd(*args) == txl.EINVAL
     # unsupported dtype and d_head
     bad = list(args)

@@ -146,6 +146,38 @@ def test_attn_matrix_core_layouts(B, H, L, M, d, dp):
     _check_argmax(got_s, ref_s, 5 * TOL["bf16"])
 
 
+@pytest.mark.parametrize("B,H,L,M,d", [
+    (1, 2, 128, 1600, 64),   # the long-memory evaluation shape, fewer heads
+    (1, 1, 130, 900, 64),    # ragged query tail
+    (2, 2, 64, 700, 32),
+    (1, 1, 1, 1000, 64),     # one query over a long memory
+    (1, 3, 200, 333, 48),
+])
+def test_attn_key_split(B, H, L, M, d):
+    """Few (batch, head) pairs over a long memory: the keys are split among
+    workgroups and merged (log-sum-exp) when a workspace is given."""
+    txl = _txl()
+    c = I.attention_inputs(B, H, L, M, d, seed=L + 3 * M, sigma=1.0, sigma_uv=0.5, dtype="bf16")
+    T = M + L
+    hm = lambda x: dev(x.transpose(0, 2, 1, 3), "bf16").permute(0, 2, 1, 3)
+    q, k, v = hm(c["q"]), hm(c["k"]), hm(c["v"])
+    r = dev(c["r"].transpose(1, 0, 2), "bf16").permute(1, 0, 2)
+    nbytes = txl.rel_attn_workspace_bytes(torch.bfloat16, B, H, L, M, d)
+    assert nbytes > 0, "this shape should take the key-split path"
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device="cuda")
+    scores = torch.empty((B, H, L, T), dtype=torch.float32, device="cuda")
+    _say(f"key split B={B} H={H} L={L} M={M} d={d} workspace={nbytes}")
+    txl.rel_attn_fwd(q, k, v, r, dev(c["u"], "bf16"), dev(c["vb"], "bf16"), M, out,
+                     scores=scores, workspace=ws)
+    torch.cuda.synchronize()
+    ref, ref_s = O.rel_attn(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M, want_scores=True)
+    assert max_err(host(out), ref) <= TOL["bf16"]
+    got_s = scores.cpu().numpy().astype(np.float64)
+    _check_scores(got_s, ref_s, 5 * TOL["bf16"])
+    _check_argmax(got_s, ref_s, 5 * TOL["bf16"])
+
+
 def test_attn_argmax_tiny_bf16():
     got, got_s, ref, ref_s = _attn_case("bf16", 1, 2, 16, 16, 16, seed=3, layout="bhtd")
     _check_argmax(got_s, ref_s, 5 * TOL["bf16"])
