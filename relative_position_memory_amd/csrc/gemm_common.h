@@ -49,4 +49,19 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s, int num_cus);
 hipError_t launch_gemm_mfma_multi(const GemmArgs* g, int n, hipStream_t s, int num_cus);
 bool gemm_mfma_supported(const GemmArgs& g);
 
+// h_out = LayerNorm(a W^T + resid) * gamma + beta for bf16 rows of width D
+// (D % 64 == 0, D <= 512, K % 32 == 0, 16-byte aligned tensors).
+struct LnArgs {
+  int64_t M, D, K;        // rows, width, inner size
+  const void* a;          // [M][K]
+  const void* W;          // [D][K]
+  const void* resid;      // [M][D]
+  const void* gamma;      // [D]
+  const void* beta;       // [D]
+  float eps;
+  void* out;              // [M][D]
+};
+bool gemm_ln_supported(const LnArgs& p);
+hipError_t launch_gemm_ln(const LnArgs& p, hipStream_t s);
+
 }  // namespace txl

@@ -3,16 +3,27 @@
 // A's rows are gathered (memory ring rows, then the current rows: the extended
 // context [SG(m) o h] of Transformer-XL section 3.2 is never materialised).
 //
-// (64 MI) x 128 output tile per workgroup of 4 waves (2 x 2), each wave
-// (32 MI) x 64 = MI x 2 blocks of v_mfma_f32_32x32x16_bf16 (MI = 2 for large
-// grids, 1 when 128-row tiles would leave CUs idle).  K is walked 64 at a time
-// through double-buffered LDS (row pitch 72 bf16: 16-byte reads without bank
-// conflicts).  Global loads run two K-steps ahead in two register sets, so a
-// step's tiles have a whole step of compute to arrive before they are staged.
-// Both operands are K-contiguous, so every MFMA fragment is one 16-byte LDS read.
+// Sizing for gfx950.  A CU reads LDS at ~256 B/clk (16-byte reads) but writes
+// it at ~100 B/clk, and global-load latency under load exceeds one K step of
+// matrix work, so:
+//  * The large tile is 256 x 256 per workgroup of 8 waves (2 along m, 4 along
+//    n), each wave 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16; per
+//    16-deep k slice a wave reads 6 KB of LDS for 8 MFMAs.  A 128 x 128 tile
+//    (4 waves of 64 x 64) serves grids that would leave CUs idle.
+//  * When K is a multiple of 32 the tiles travel from global memory straight
+//    into LDS (global_load_lds_dwordx4, no register staging) through a ring of
+//    four 32-deep stages, loads running three stages ahead of the MFMAs.
+//    Rows are 64 bytes; 16-byte chunk c of row r sits in slot
+//    c ^ swz(r), which keeps every fragment read conflict-free.
+//  * Otherwise a register-staged, double-buffered 64-deep pipeline is used.
+//  * Workgroups are persistent: each walks tiles blockIdx.x, + gridDim.x, ...
 //
-// One launch may carry up to four independent problems (the layer step's q,
-// k/v and r projections share K and run as one grid).
+// The product is formed transposed, C^T = W A^T: W supplies the MFMA's A
+// operand and the gathered rows its B operand, so each lane owns one output
+// row m; W rows are fed in a permuted order so that each lane holds 16
+// consecutive output columns.  The epilogue stages the tile in LDS and writes
+// whole 16-byte chunks.  One launch may carry up to four independent problems
+// (the layer step's q, k/v and r projections share K and run as one grid).
 #include "gemm_common.h"
 
 namespace txl {
@@ -21,20 +32,13 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int GBN = 128, GBK = 64, GKP = 72;
 constexpr int NXCD = 8;
 constexpr int MAXP = 4;
-
-template <int MI>
-struct __align__(16) GSmem {
-  uint16_t A[2][64 * MI * GKP];
-  uint16_t W[2][GBN * GKP];
-};
 
 struct GemmBatch {
   GemmArgs g[MAXP];
   int ntm[MAXP], ntn[MAXP];
-  int block_end[MAXP];  // inclusive prefix sums of the problems' block counts
+  int block_end[MAXP];  // inclusive prefix sums of the problems' tile counts
   int n;
 };
 
@@ -43,190 +47,699 @@ __device__ inline uint4 keep_if(uint4 v, bool keep) {
   return make_uint4(v.x & k, v.y & k, v.z & k, v.w & k);
 }
 
-// 16-byte chunk c = tid % 8 of A rows (tid / 8) + 32 x, x < 2 MI, and of
-// W rows (tid / 8) + 32 x, x < 4.
-template <int MI>
-struct Regs {
-  uint4 a[2 * MI], w[4];
-};
-
-template <int MI>
-struct Loader {
-  const uint16_t* arow[2 * MI];
-  const uint16_t* wrow[4];
-  bool aval[2 * MI], wval[4];
-  int c, K, tid;
-
-  __device__ void load(Regs<MI>& r, int k0) const {
-    const int kc = k0 + 8 * c;
-    const int kk = kc < K ? kc : K - 8;  // clamped into the row; masked at store
-#pragma unroll
-    for (int x = 0; x < 2 * MI; ++x) r.a[x] = *(const uint4*)(arow[x] + kk);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) r.w[x] = *(const uint4*)(wrow[x] + kk);
-  }
-  __device__ void store(GSmem<MI>& sm, int buf, const Regs<MI>& r, int k0) const {
-    const bool kin = k0 + 8 * c < K;
-#pragma unroll
-    for (int x = 0; x < 2 * MI; ++x)
-      *(uint4*)&sm.A[buf][((tid >> 3) + 32 * x) * GKP + 8 * c] = keep_if(r.a[x], kin && aval[x]);
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      *(uint4*)&sm.W[buf][((tid >> 3) + 32 * x) * GKP + 8 * c] = keep_if(r.w[x], kin && wval[x]);
-  }
-};
-
-template <int MI>
-__device__ inline void mma_step(const GSmem<MI>& sm, int buf, int wm, int wn, int li, int lh,
-                                f32x16 (&acc)[MI][2]) {
-#pragma unroll
-  for (int s = 0; s < GBK / 16; ++s) {
-    bf16x8 af[MI], wf[2];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      af[i] = *(const bf16x8*)&sm.A[buf][(wm * 32 * MI + 32 * i + li) * GKP + 16 * s + 8 * lh];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      wf[j] = *(const bf16x8*)&sm.W[buf][(wn * 64 + 32 * j + li) * GKP + 16 * s + 8 * lh];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
-  }
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-template <int MI>
-__global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmBatch bt) {
-  constexpr int BM = 64 * MI;
-  extern __shared__ __align__(16) char smem_raw[];
-  GSmem<MI>& sm = *(GSmem<MI>*)smem_raw;
+// Output row rho = 8 q + 4 h + t of a 32 x 32 MFMA block (q = register group,
+// h = lane half, t = register in the group) is fed W row wrow_perm(rho) =
+// 16 h + 4 q + t, so lane half h ends up holding the 16 consecutive columns
+// 16 h .. 16 h + 15 of the block in registers 0 .. 15.
+__device__ inline int wrow_perm(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
 
-  int p = 0;
-  while (p + 1 < bt.n && (int)blockIdx.x >= bt.block_end[p]) ++p;
-  const GemmArgs& g = bt.g[p];
-  const int ntm = bt.ntm[p], ntn = bt.ntn[p];
-  const int bid = (int)blockIdx.x - (p ? bt.block_end[p - 1] : 0);
-  // Row tiles of A are spread over the XCDs (block n runs on XCD n % 8; every
-  // problem's block range starts at a multiple of 8); the column tiles of one
-  // row tile run consecutively on the same XCD, whose L2 then serves the A tile
-  // to all of them.
+// Tile geometry: BM x BN outputs, WM x WN waves of (BM/WM) x (BN/WN).
+template <int BM_, int BN_, int WM_, int WN_, int OCC_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int OCC = OCC_;                // workgroups per CU
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = 64 * NW;             // threads
+  static constexpr int TI = BM / WM / 32;        // 32-row blocks of m per wave
+  static constexpr int TJ = BN / WN / 32;        // 32-column blocks of n per wave
+  // register-staged pipeline: 64-deep K steps, rows padded to 72 bf16
+  static constexpr int RBK = 64, RKP = 72;
+  static constexpr int RPP = NT / 8;             // rows per load pass (8 x 16 B per row)
+  static constexpr int PA = BM / RPP, PW = BN / RPP;
+  static constexpr size_t RSMEM = (size_t)2 * (BM + BN) * RKP * sizeof(uint16_t);
+  // LDS-direct pipeline: 32-deep K steps (64-byte rows), NS stages
+  static constexpr int DBK = 32, NS = 4;
+  static constexpr int STAGE = (BM + BN) * DBK;  // bf16 elements per stage
+  static constexpr int QA = BM / 16 / NW, QW = BN / 16 / NW;  // 1 KB loads per wave and stage
+  static constexpr size_t DSMEM = (size_t)NS * STAGE * sizeof(uint16_t);
+  // epilogue staging
+  static constexpr size_t ESMEM_BF16 = (size_t)BM * (BN + 8) * sizeof(uint16_t);
+  static constexpr size_t ESMEM_F32 = (size_t)BM * (BN + 4) * sizeof(float);
+};
+using Big = Cfg<256, 256, 2, 4, 1>;
+using Small = Cfg<128, 128, 2, 2, 2>;
+
+enum { EPI_SCALAR = 0, EPI_STAGE_BF16 = 1, EPI_STAGE_F32 = 2 };
+
+template <class C, int EPI>
+constexpr size_t epi_smem() {
+  return EPI == EPI_STAGE_BF16 ? C::ESMEM_BF16 : EPI == EPI_STAGE_F32 ? C::ESMEM_F32 : 0;
+}
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+// Address of logical row m of the gathered A operand, 32-bit index arithmetic
+// (the launch checks that every row and offset fits).
+__device__ inline const uint16_t* gather_row32(const RowGather& a, int m) {
+  const int per = (int)(a.mem_len + a.cur_rows), len = (int)a.mem_len;
+  const int b = m / per, t = m - b * per;
+  if (t < len) {
+    int slot = (int)a.mem_start + t;
+    if (slot >= (int)a.mem_cap) slot -= (int)a.mem_cap;
+    return (const uint16_t*)a.mem + ((int64_t)b * a.mem_cap + slot) * a.lda;
+  }
+  return (const uint16_t*)a.cur + ((int64_t)b * a.cur_rows + (t - len)) * a.lda;
+}
+
+struct TileId {
+  int p, m0, n0;
+  bool valid;
+};
+
+// Tile n of the batch.  Row tiles of A are spread over the XCDs (workgroup w
+// runs on XCD w % 8, the grid is a multiple of 8 and every problem's tile
+// range starts at a multiple of 8, so tile n is always computed on XCD n % 8);
+// the column tiles of one row tile run consecutively on the same XCD, whose L2
+// then serves the A tile to all of them.
+template <class C>
+__device__ inline TileId tile_id(const GemmBatch& bt, int tile) {
+  TileId t;
+  t.p = 0;
+  while (t.p + 1 < bt.n && tile >= bt.block_end[t.p]) ++t.p;
+  const int ntm = bt.ntm[t.p], ntn = bt.ntn[t.p];
+  const int bid = tile - (t.p ? bt.block_end[t.p - 1] : 0);
   const int xcd = bid % NXCD, k_on = bid / NXCD;
   const int tm = (k_on / ntn) * NXCD + xcd;
-  const int tn = k_on % ntn;
-  if (tm >= ntm) return;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * GBN;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int li = lane & 31, lh = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  t.valid = tm < ntm;
+  t.m0 = tm * C::BM;
+  t.n0 = (k_on % ntn) * C::BN;
+  return t;
+}
 
-  Loader<MI> ld;
-  ld.c = tid & 7;
-  ld.K = (int)g.K;
-  ld.tid = tid;
+template <class C>
+__device__ inline void zero_acc(f32x16 (&acc)[C::TJ][C::TI]) {
 #pragma unroll
-  for (int x = 0; x < 2 * MI; ++x) {
-    const int64_t m = m0 + (tid >> 3) + 32 * x;
-    ld.aval[x] = m < g.M;
-    ld.arow[x] = (const uint16_t*)gather_row(g.a, ld.aval[x] ? m : g.M - 1, 2);
-  }
+  for (int j = 0; j < C::TJ; ++j)
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int64_t n = n0 + (tid >> 3) + 32 * x;
-    ld.wval[x] = n < g.N;
-    ld.wrow[x] = (const uint16_t*)weight_row(g.w, ld.wval[x] ? n : g.N - 1, 2);
-  }
+    for (int i = 0; i < C::TI; ++i)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[j][i][x] = 0.f;
+}
 
-  f32x16 acc[MI][2];
+// ---- epilogue -----------------------------------------------------------------------
+// Lane (li, h) of block (j, i) holds row m0 + wm*32*TI + 32 i + li, columns
+// n0 + wn*32*TJ + 32 j + 16 h + [0, 16) in registers 0..15.  The staged forms
+// write the tile to LDS (whose K-loop contents are dead: the caller has passed
+// a barrier after the last fragment read), then store 16-byte chunks: every
+// row's columns are contiguous in the destination, so each store instruction
+// covers whole cache lines.  Ends with a barrier (the next tile reuses LDS).
+template <class C, int EPI>
+__device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
+                                const f32x16 (&acc)[C::TJ][C::TI], int tid, int wm, int wn,
+                                int li, int lh) {
+  if (EPI == EPI_STAGE_BF16) {
+    constexpr int EP = C::BN + 8;  // row pitch (bf16): 16-byte aligned, conflict-free
+    uint16_t* es = (uint16_t*)smem;
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < C::TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < C::TJ; ++j) {
+        uint32_t pk[8];
 #pragma unroll
-      for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.f;
-
-  // Invariant at the top of step kt: LDS buffer kt%2 holds tile kt, register
-  // set (kt+1)%2 holds (or is receiving) tile kt+1, set kt%2 is free.
-  const int nk = (ld.K + GBK - 1) / GBK;
-  Regs<MI> r0, r1;
-  ld.load(r0, 0);
-  if (nk > 1) ld.load(r1, GBK);
-  ld.store(sm, 0, r0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) ld.load(r0, (kt + 2) * GBK);
-    mma_step<MI>(sm, 0, wm, wn, li, lh, acc);
-    if (kt + 1 < nk) ld.store(sm, 1, r1, (kt + 1) * GBK);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) ld.load(r1, (kt + 3) * GBK);
-    mma_step<MI>(sm, 1, wm, wn, li, lh, acc);
-    if (kt + 2 < nk) ld.store(sm, 0, r0, (kt + 2) * GBK);
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane (column li of block j, half lh), reg x -> row 8 (x/4) + 4 lh + x%4
-  const int64_t per = g.a.mem_len + g.a.cur_rows;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = n0 + wn * 64 + 32 * j + li;
-    if (n >= g.N) continue;
-    uint16_t* hcol = nullptr;  // EPI_HEADS: destination of (b = 0, t = 0) for column n
-    if (g.e.mode == EPI_HEADS) {
-      const int64_t which = n / g.e.HD, nn = n - which * g.e.HD;
-      const int64_t head = nn / g.e.d, cc = nn - head * g.e.d;
-      hcol = (uint16_t*)(which ? g.e.dst1 : g.e.dst0) + head * g.e.sh + cc;
-    }
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) {
-        const int64_t mb = m0 + wm * 32 * MI + 32 * i + 8 * x4 + 4 * lh;
-        int64_t b = mb / per, t = mb - b * per;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t m = mb + e;
-          if (m < g.M) {
-            const float v = acc[i][j][4 * x4 + e];
-            if (g.e.mode == EPI_HEADS) {
-              hcol[b * g.e.sb + t * g.e.st] = __builtin_bit_cast(uint16_t, (__bf16)v);
-            } else {
-              const uint16_t* res = (const uint16_t*)g.e.resid + m * g.N + n;
-              g.e.y[m * g.N + n] = v + bf16_to_f32(*res);
-            }
-          }
-          if (++t == per) { t = 0; ++b; }
-        }
+        for (int e = 0; e < 8; ++e) pk[e] = pack_bf16x2(acc[j][i][2 * e], acc[j][i][2 * e + 1]);
+        uint16_t* dst = es + (wm * 32 * C::TI + 32 * i + li) * EP + wn * 32 * C::TJ + 32 * j + 16 * lh;
+        *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        *(uint4*)(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
       }
+    __syncthreads();
+    constexpr int CPR = C::BN / 8;     // 16-byte chunks per row
+    constexpr int STEP = C::NT / CPR;  // rows between a thread's chunks
+    const int per = (int)(g.a.mem_len + g.a.cur_rows);
+    const int HD = (int)g.e.HD, d = (int)g.e.d;
+    const int c = tid % CPR;
+    const int n = n0 + 8 * c;
+    const int which = n >= HD, nn = n - which * HD;
+    const int head = nn / d, cc = nn - head * d;
+    uint16_t* colbase = (uint16_t*)(which ? g.e.dst1 : g.e.dst0) + (int64_t)head * g.e.sh + cc;
+    const int row0 = tid / CPR;
+    int b = (m0 + row0) / per, t = m0 + row0 - b * per;
+    for (int row = row0; row < C::BM; row += STEP) {
+      if (m0 + row >= g.M) break;
+      if (n < g.N)
+        *(uint4*)(colbase + b * g.e.sb + t * g.e.st) = *(const uint4*)(es + row * EP + 8 * c);
+      t += STEP;
+      while (t >= per) { t -= per; ++b; }
+    }
+    __syncthreads();
+  } else if (EPI == EPI_STAGE_F32) {
+    constexpr int EP = C::BN + 4;  // row pitch (fp32)
+    float* es = (float*)smem;
+#pragma unroll
+    for (int i = 0; i < C::TI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TJ; ++j) {
+        float* dst = es + (wm * 32 * C::TI + 32 * i + li) * EP + wn * 32 * C::TJ + 32 * j + 16 * lh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *(float4*)(dst + 4 * e) = make_float4(acc[j][i][4 * e], acc[j][i][4 * e + 1],
+                                                acc[j][i][4 * e + 2], acc[j][i][4 * e + 3]);
+      }
+    __syncthreads();
+    constexpr int CPR = C::BN / 4;
+    const int c = tid % CPR;
+    const int n = n0 + 4 * c;
+    for (int row = tid / CPR; row < C::BM; row += C::NT / CPR) {
+      const int64_t m = (int64_t)m0 + row;
+      if (m >= g.M || n >= g.N) continue;
+      const uint2 rr = *(const uint2*)((const uint16_t*)g.e.resid + m * g.N + n);
+      const float4 a4 = *(const float4*)(es + row * EP + 4 * c);
+      float4 o;
+      o.x = a4.x + bf16_to_f32((uint16_t)(rr.x & 0xffffu));
+      o.y = a4.y + bf16_to_f32((uint16_t)(rr.x >> 16));
+      o.z = a4.z + bf16_to_f32((uint16_t)(rr.y & 0xffffu));
+      o.w = a4.w + bf16_to_f32((uint16_t)(rr.y >> 16));
+      *(float4*)(g.e.y + m * g.N + n) = o;
+    }
+    __syncthreads();
+  } else {
+    // element by element (any layout)
+#pragma unroll
+    for (int i = 0; i < C::TI; ++i) {
+      const int64_t m = (int64_t)m0 + wm * 32 * C::TI + 32 * i + li;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < C::TJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t n = (int64_t)n0 + wn * 32 * C::TJ + 32 * j + 16 * lh + e;
+          if (n >= g.N) continue;
+          const float v = acc[j][i][e];
+          if (g.e.mode == EPI_HEADS) {
+            *heads_dst<uint16_t>(g, m, n) = __builtin_bit_cast(uint16_t, (__bf16)v);
+          } else {
+            g.e.y[m * g.N + n] = v + bf16_to_f32(((const uint16_t*)g.e.resid)[m * g.N + n]);
+          }
+        }
+    }
+    __syncthreads();
   }
 }
 
-template <int MI>
-hipError_t launch_mi(const GemmArgs* gs, int n, hipStream_t s) {
-  constexpr int BM = 64 * MI;
-  GemmBatch bt{};
-  int64_t total = 0;
-  for (int p = 0; p < n; ++p) {
-    bt.g[p] = gs[p];
-    bt.ntm[p] = (int)((gs[p].M + BM - 1) / BM);
-    bt.ntn[p] = (int)((gs[p].N + GBN - 1) / GBN);
-    total += (int64_t)NXCD * ((bt.ntm[p] + NXCD - 1) / NXCD) * bt.ntn[p];
-    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    bt.block_end[p] = (int)total;
+// ---- LDS-direct pipeline (K % 32 == 0) ----------------------------------------------
+
+// Swizzle of a 64-byte row: chunk c of row r lives in slot c ^ swz(r).  Sixteen
+// lanes reading one chunk of rows {0-3, 16-19, 4-7, 20-23} (W, permuted) or of
+// 16 consecutive rows (A) hit 16 distinct (r mod 4, slot) bank groups.
+__device__ inline int swz(int r) { return ((r >> 2) + 2 * (r >> 4)) & 3; }
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left alone (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// wait until at most `later` stages of PER loads each are still in flight
+template <int PER>
+__device__ inline void wait_stages(int later) {
+  if (later >= 2) wait_vm<2 * PER>();
+  else if (later == 1) wait_vm<PER>();
+  else wait_vm<0>();
+}
+
+// Barrier that orders LDS accesses for the compiler without waiting for the
+// in-flight LDS-direct loads (each wave waits for its own loads first).
+__device__ inline void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <class C, int EPI>
+__global__ __launch_bounds__(C::NT, C::OCC) void gemm_dma_kernel(GemmBatch bt) {
+  extern __shared__ __align__(16) char smem_raw[];
+  uint16_t* ring = (uint16_t*)smem_raw;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 31, lh = lane >> 5;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int wli = wrow_perm(li);
+  // fragment rows (within the stage's A / W blocks)
+  int arow_f[C::TI], wrow_f[C::TJ];
+#pragma unroll
+  for (int i = 0; i < C::TI; ++i) arow_f[i] = wm * 32 * C::TI + 32 * i + li;
+#pragma unroll
+  for (int j = 0; j < C::TJ; ++j) wrow_f[j] = wn * 32 * C::TJ + 32 * j + wli;
+
+  for (int tile = blockIdx.x; tile < bt.block_end[bt.n - 1]; tile += gridDim.x) {
+    const TileId tl = tile_id<C>(bt, tile);
+    if (!tl.valid) continue;
+    const GemmArgs& g = bt.g[tl.p];
+    const int m0 = tl.m0, n0 = tl.n0;
+
+    // This lane's source rows: load q of the wave covers stage rows 16 q' + lane/4
+    // (q' = wave * Q + q), 16-byte slot lane % 4, i.e. chunk slot ^ swz(row).
+    const uint16_t* asrc[C::QA];
+    const uint16_t* wsrc[C::QW];
+#pragma unroll
+    for (int q = 0; q < C::QA; ++q) {
+      const int r = 16 * (wave * C::QA + q) + (lane >> 2);
+      const int m = m0 + r < g.M ? m0 + r : (int)g.M - 1;  // rows past M: never stored
+      asrc[q] = gather_row32(g.a, m) + 8 * ((lane & 3) ^ swz(r));
+    }
+#pragma unroll
+    for (int q = 0; q < C::QW; ++q) {
+      const int r = 16 * (wave * C::QW + q) + (lane >> 2);
+      const int n = n0 + r < g.N ? n0 + r : (int)g.N - 1;  // columns past N: never stored
+      wsrc[q] = (const uint16_t*)weight_row(g.w, n, 2) + 8 * ((lane & 3) ^ swz(r));
+    }
+    const int nk = (int)(g.K / C::DBK);
+    auto issue = [&](int kt) {
+      uint16_t* st = ring + (kt % C::NS) * C::STAGE;
+#pragma unroll
+      for (int q = 0; q < C::QA; ++q)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(asrc[q] + kt * C::DBK),
+            (void __attribute__((address_space(3)))*)(st + (wave * C::QA + q) * 16 * C::DBK), 16,
+            0, 0);
+#pragma unroll
+      for (int q = 0; q < C::QW; ++q)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(wsrc[q] + kt * C::DBK),
+            (void __attribute__((address_space(3)))*)(st + C::BM * C::DBK +
+                                                      (wave * C::QW + q) * 16 * C::DBK),
+            16, 0, 0);
+    };
+    constexpr int PER_STAGE = C::QA + C::QW;  // loads per wave and stage
+    static_assert(C::NS == 4, "wait_stages covers up to two later stages");
+
+    f32x16 acc[C::TJ][C::TI];
+    zero_acc<C>(acc);
+#pragma unroll
+    for (int s = 0; s < C::NS - 1; ++s)
+      if (s < nk) issue(s);
+    for (int kt = 0; kt < nk; ++kt) {
+      // this wave's loads of stage kt have landed; the barrier makes every
+      // wave's visible and retires the reads of stage kt - 1, whose buffer
+      // (kt + 3) % 4 the next loads overwrite
+      const int later = nk - 1 - kt < C::NS - 2 ? nk - 1 - kt : C::NS - 2;
+      wait_stages<PER_STAGE>(later);
+      lds_barrier();
+      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1);
+      const uint16_t* sa = ring + (kt % C::NS) * C::STAGE;
+      const uint16_t* sw = sa + C::BM * C::DBK;
+#pragma unroll
+      for (int s = 0; s < C::DBK / 16; ++s) {
+        const int kc = 2 * s + lh;  // this lane's 16-byte chunk of the 32-deep step
+        bf16x8 wf[C::TJ], af[C::TI];
+#pragma unroll
+        for (int j = 0; j < C::TJ; ++j)
+          wf[j] = *(const bf16x8*)&sw[wrow_f[j] * C::DBK + 8 * (kc ^ swz(wrow_f[j]))];
+#pragma unroll
+        for (int i = 0; i < C::TI; ++i)
+          af[i] = *(const bf16x8*)&sa[arow_f[i] * C::DBK + 8 * (kc ^ swz(arow_f[i]))];
+#pragma unroll
+        for (int j = 0; j < C::TJ; ++j)
+#pragma unroll
+          for (int i = 0; i < C::TI; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // all fragment reads done before the epilogue reuses LDS
+    epilogue<C, EPI>(g, m0, n0, smem_raw, acc, tid, wm, wn, li, lh);
   }
-  bt.n = n;
-  if (total == 0) return hipSuccess;
+}
+
+// ---- register-staged pipeline (any K % 8 == 0) ---------------------------------------
+
+// Thread t stages 16-byte chunk (t % 8) of A rows t/8 + RPP x and W rows t/8 + RPP x.
+template <class C>
+struct Loader {
+  const uint16_t* arow[C::PA];
+  const uint16_t* wrow[C::PW];
+  uint32_t aval, wval;  // bit x: row x is inside the problem
+  int c, K, tid;
+
+  __device__ void load(uint4 (&ra)[C::PA], uint4 (&rw)[C::PW], int k0) const {
+    const int kc = k0 + 8 * c;
+    const int kk = kc < K ? kc : K - 8;  // clamped into the row; zeroed at store
+#pragma unroll
+    for (int x = 0; x < C::PA; ++x) ra[x] = *(const uint4*)(arow[x] + kk);
+#pragma unroll
+    for (int x = 0; x < C::PW; ++x) rw[x] = *(const uint4*)(wrow[x] + kk);
+  }
+  __device__ void store(uint16_t* sa, uint16_t* sw, const uint4 (&ra)[C::PA],
+                        const uint4 (&rw)[C::PW], int k0) const {
+    const bool kin = k0 + 8 * c < K;
+#pragma unroll
+    for (int x = 0; x < C::PA; ++x)
+      *(uint4*)&sa[((tid >> 3) + C::RPP * x) * C::RKP + 8 * c] =
+          keep_if(ra[x], kin && ((aval >> x) & 1));
+#pragma unroll
+    for (int x = 0; x < C::PW; ++x)
+      *(uint4*)&sw[((tid >> 3) + C::RPP * x) * C::RKP + 8 * c] =
+          keep_if(rw[x], kin && ((wval >> x) & 1));
+  }
+};
+
+template <class C, int EPI>
+__global__ __launch_bounds__(C::NT, C::OCC) void gemm_reg_kernel(GemmBatch bt) {
+  extern __shared__ __align__(16) char smem_raw[];
+  uint16_t* lds = (uint16_t*)smem_raw;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 31, lh = lane >> 5;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int wli = wrow_perm(li);
+
+  for (int tile = blockIdx.x; tile < bt.block_end[bt.n - 1]; tile += gridDim.x) {
+    const TileId tl = tile_id<C>(bt, tile);
+    if (!tl.valid) continue;
+    const GemmArgs& g = bt.g[tl.p];
+    const int m0 = tl.m0, n0 = tl.n0;
+
+    Loader<C> ld;
+    ld.c = tid & 7;
+    ld.K = (int)g.K;
+    ld.tid = tid;
+    ld.aval = 0;
+    ld.wval = 0;
+#pragma unroll
+    for (int x = 0; x < C::PA; ++x) {
+      const int m = m0 + (tid >> 3) + C::RPP * x;
+      const bool ok = m < g.M;
+      ld.aval |= (uint32_t)ok << x;
+      ld.arow[x] = gather_row32(g.a, ok ? m : (int)g.M - 1);
+    }
+#pragma unroll
+    for (int x = 0; x < C::PW; ++x) {
+      const int n = n0 + (tid >> 3) + C::RPP * x;
+      const bool ok = n < g.N;
+      ld.wval |= (uint32_t)ok << x;
+      ld.wrow[x] = (const uint16_t*)weight_row(g.w, ok ? n : g.N - 1, 2);
+    }
+
+    f32x16 acc[C::TJ][C::TI];
+    zero_acc<C>(acc);
+    // At the top of step kt LDS buffer kt % 2 holds tile kt and the registers
+    // hold (or are receiving) tile kt + 1; buffer (kt + 1) % 2 was last read in
+    // step kt - 1, which every wave finished before the barrier that ended it.
+    auto sa = [&](int buf) { return lds + buf * (C::BM + C::BN) * C::RKP; };
+    auto sw = [&](int buf) { return lds + buf * (C::BM + C::BN) * C::RKP + C::BM * C::RKP; };
+    const int nk = (ld.K + C::RBK - 1) / C::RBK;
+    uint4 ra[C::PA], rw[C::PW];
+    ld.load(ra, rw, 0);
+    ld.store(sa(0), sw(0), ra, rw, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) ld.load(ra, rw, (kt + 1) * C::RBK);
+      const uint16_t* A = sa(kt & 1);
+      const uint16_t* W = sw(kt & 1);
+#pragma unroll
+      for (int s = 0; s < C::RBK / 16; ++s) {
+        bf16x8 wf[C::TJ], af[C::TI];
+#pragma unroll
+        for (int j = 0; j < C::TJ; ++j)
+          wf[j] = *(const bf16x8*)&W[(wn * 32 * C::TJ + 32 * j + wli) * C::RKP + 16 * s + 8 * lh];
+#pragma unroll
+        for (int i = 0; i < C::TI; ++i)
+          af[i] = *(const bf16x8*)&A[(wm * 32 * C::TI + 32 * i + li) * C::RKP + 16 * s + 8 * lh];
+#pragma unroll
+        for (int j = 0; j < C::TJ; ++j)
+#pragma unroll
+          for (int i = 0; i < C::TI; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+      }
+      if (more) ld.store(sa((kt + 1) & 1), sw((kt + 1) & 1), ra, rw, (kt + 1) * C::RBK);
+      __syncthreads();
+    }
+    epilogue<C, EPI>(g, m0, n0, smem_raw, acc, tid, wm, wn, li, lh);
+  }
+}
+
+// ---- launch ----------------------------------------------------------------------------
+
+// Staged epilogues write 16-byte chunks: eight bf16 columns of one head (or
+// four fp32 columns of y) that are contiguous and 16-byte aligned in memory.
+template <class C>
+int epi_kind(const GemmArgs& g) {
+  if (g.e.mode == EPI_HEADS) {
+    const bool ok = g.e.d % 8 == 0 && g.e.HD % 8 == 0 && g.N % 8 == 0 && g.N <= 2 * g.e.HD &&
+                    g.e.sb % 8 == 0 && g.e.sh % 8 == 0 && g.e.st % 8 == 0 &&
+                    (uintptr_t)g.e.dst0 % 16 == 0 && (uintptr_t)g.e.dst1 % 16 == 0;
+    return ok ? EPI_STAGE_BF16 : EPI_SCALAR;
+  }
+  const bool ok = C::ESMEM_F32 <= 160 * 1024 / C::OCC && g.N % 4 == 0 &&
+                  (uintptr_t)g.e.y % 16 == 0 && (uintptr_t)g.e.resid % 8 == 0;
+  return ok ? EPI_STAGE_F32 : EPI_SCALAR;
+}
+
+template <class C, int EPI, bool DMA>
+hipError_t launch_cfg(const GemmBatch& bt, int total, int num_cus, hipStream_t s) {
+  constexpr size_t smem = cmax(DMA ? C::DSMEM : C::RSMEM, epi_smem<C, EPI>());
+  const void* fn = DMA ? (const void*)gemm_dma_kernel<C, EPI> : (const void*)gemm_reg_kernel<C, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_mfma_kernel<MI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(GSmem<MI>));
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(gemm_mfma_kernel<MI>, dim3((unsigned)total), dim3(256), sizeof(GSmem<MI>),
-                     s, bt);
+  // a multiple of 8 workgroups (one XCD each in turn), at most one round
+  const int slots = (num_cus * C::OCC) / NXCD * NXCD;
+  const int grid = total < slots ? total : (slots > 0 ? slots : NXCD);
+  if (DMA)
+    hipLaunchKernelGGL((gemm_dma_kernel<C, EPI>), dim3((unsigned)grid), dim3(C::NT), smem, s, bt);
+  else
+    hipLaunchKernelGGL((gemm_reg_kernel<C, EPI>), dim3((unsigned)grid), dim3(C::NT), smem, s, bt);
   return hipGetLastError();
+}
+
+template <class C, bool DMA>
+hipError_t launch_epi(const GemmBatch& bt, int epi, int total, int num_cus, hipStream_t s) {
+  if (epi == EPI_STAGE_BF16) return launch_cfg<C, EPI_STAGE_BF16, DMA>(bt, total, num_cus, s);
+  if (epi == EPI_STAGE_F32) return launch_cfg<C, EPI_STAGE_F32, DMA>(bt, total, num_cus, s);
+  return launch_cfg<C, EPI_SCALAR, DMA>(bt, total, num_cus, s);
+}
+
+// LDS-direct loads move whole 32-deep K steps (no tail masking).
+bool dma_ok(const GemmArgs& g) { return g.K % 32 == 0; }
+
+template <class C>
+hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s) {
+  GemmBatch bt{};
+  int64_t total = 0;
+  int epi = -1;
+  bool dma = true;
+  for (int p = 0; p < n; ++p) {
+    bt.g[p] = gs[p];
+    bt.ntm[p] = (int)((gs[p].M + C::BM - 1) / C::BM);
+    bt.ntn[p] = (int)((gs[p].N + C::BN - 1) / C::BN);
+    total += (int64_t)NXCD * ((bt.ntm[p] + NXCD - 1) / NXCD) * bt.ntn[p];
+    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+    bt.block_end[p] = (int)total;
+    const int k = epi_kind<C>(gs[p]);
+    epi = (epi < 0 || epi == k) ? k : EPI_SCALAR;
+    dma = dma && dma_ok(gs[p]);
+  }
+  bt.n = n;
+  if (total == 0) return hipSuccess;
+  return dma ? launch_epi<C, true>(bt, epi, (int)total, num_cus, s)
+             : launch_epi<C, false>(bt, epi, (int)total, num_cus, s);
+}
+
+
+// ---- output projection + residual + LayerNorm ------------------------------------------
+// h_out[m] = LayerNorm(a[m] W_o^T + h[m]) * gamma + beta (section 3.3: post-norm,
+// mean and biased variance over D).  One workgroup owns 64 whole rows, so the
+// row statistics never leave the CU and y never goes to memory.  Eight waves;
+// wave w owns output columns 64 w .. 64 w + 63 (2 x 2 blocks of 32 x 32 over the
+// 64 rows), so D <= 512.  K streams through the same LDS-direct ring as above:
+// per 32-deep stage 4 KB of a and D x 64 B of W_o.
+constexpr int LBM = 64, LNW = 8, LNT = 64 * LNW, LBK = 32, LNS = 4, LDMAX = 512;
+
+__global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  uint16_t* ring = (uint16_t*)smem_raw;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 31, lh = lane >> 5;
+  const int D = (int)p.D, K = (int)p.K, M = (int)p.M;
+  const int m0 = blockIdx.x * LBM;
+  const int stage = (LBM + D) * LBK;         // bf16 elements per stage
+  const bool active = wave * 64 < D;         // this wave owns columns
+  const int wli = wrow_perm(li);
+
+  // DMA sources: a-block loads 0..3 by waves 0..3, W loads q = wave + 8 x
+  const int qa = wave < LBM / 16 ? 1 : 0;
+  const int qw = (D / 16 - wave + LNW - 1) / LNW;  // W loads of this wave (<= 4)
+  const uint16_t* asrc = nullptr;
+  if (qa) {
+    const int r = 16 * wave + (lane >> 2);
+    const int m = m0 + r < M ? m0 + r : M - 1;  // rows past M: never stored
+    asrc = (const uint16_t*)p.a + (int64_t)m * K + 8 * ((lane & 3) ^ swz(r));
+  }
+  const uint16_t* wsrc[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int r = 16 * (wave + LNW * x) + (lane >> 2);
+    const int n = r < D ? r : D - 1;
+    wsrc[x] = (const uint16_t*)p.W + (int64_t)n * K + 8 * ((lane & 3) ^ swz(r));
+  }
+  const int nk = K / LBK;
+  auto issue = [&](int kt) {
+    uint16_t* st = ring + (kt % LNS) * stage;
+    if (qa)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(asrc + kt * LBK),
+          (void __attribute__((address_space(3)))*)(st + wave * 16 * LBK), 16, 0, 0);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      if (x < qw)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(wsrc[x] + kt * LBK),
+            (void __attribute__((address_space(3)))*)(st + LBM * LBK + (wave + LNW * x) * 16 * LBK),
+            16, 0, 0);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[j][i][x] = 0.f;
+  for (int s = 0; s < LNS - 1; ++s)
+    if (s < nk) issue(s);
+  const int per = qa + qw;  // loads per stage issued by this wave (wave-uniform)
+  for (int kt = 0; kt < nk; ++kt) {
+    const int later = nk - 1 - kt < LNS - 2 ? nk - 1 - kt : LNS - 2;
+    if (per == 5) wait_stages<5>(later);
+    else if (per == 4) wait_stages<4>(later);
+    else if (per == 3) wait_stages<3>(later);
+    else if (per == 2) wait_stages<2>(later);
+    else if (per == 1) wait_stages<1>(later);
+    lds_barrier();
+    if (kt + LNS - 1 < nk) issue(kt + LNS - 1);
+    if (active) {
+      const uint16_t* sa = ring + (kt % LNS) * stage;
+      const uint16_t* sw = sa + LBM * LBK;
+#pragma unroll
+      for (int s = 0; s < LBK / 16; ++s) {
+        const int kc = 2 * s + lh;
+        bf16x8 wf[2], af[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = wave * 64 + 32 * j + wli;
+          wf[j] = *(const bf16x8*)&sw[r * LBK + 8 * (kc ^ swz(r))];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 32 * i + li;
+          af[i] = *(const bf16x8*)&sa[r * LBK + 8 * (kc ^ swz(r))];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // ring dead from here on
+
+  // ---- epilogue: lane (li, h) of block (j, i) holds row 32 i + li, columns
+  //      64 w + 32 j + 16 h + [0, 16).  y = acc + h, then the row statistics.
+  constexpr int EP = LDMAX + 8;
+  uint16_t* es = (uint16_t*)smem_raw;                        // [64][EP] bf16 output
+  float* red = (float*)(smem_raw + LBM * EP * sizeof(uint16_t));  // [LNW][64]
+  float rs[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + 32 * i + li;
+    const int mc = m < M ? m : M - 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wave * 64 + 32 * j + 16 * lh;
+      if (!active) continue;
+      const uint4* rp = (const uint4*)((const uint16_t*)p.resid + (int64_t)mc * D + n);
+      const uint4 r0 = rp[0], r1 = rp[1];
+      const uint32_t rw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[j][i][2 * e] += bf16_to_f32((uint16_t)(rw[e] & 0xffffu));
+        acc[j][i][2 * e + 1] += bf16_to_f32((uint16_t)(rw[e] >> 16));
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rs[i] += acc[j][i][e];
+    }
+  }
+  // row sums: lane halves, then waves
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    rs[i] += __shfl_xor(rs[i], 32, 64);
+    if (lh == 0) red[wave * 64 + 32 * i + li] = rs[i];
+  }
+  __syncthreads();
+  float mean[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < LNW; ++w) t += red[w * 64 + 32 * i + li];
+    mean[i] = t / (float)D;
+  }
+  __syncthreads();
+  float rq[2] = {0.f, 0.f};
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float t = acc[j][i][e] - mean[i];
+          rq[i] += t * t;
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    rq[i] += __shfl_xor(rq[i], 32, 64);
+    if (lh == 0) red[wave * 64 + 32 * i + li] = rq[i];
+  }
+  __syncthreads();
+  float rstd[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < LNW; ++w) t += red[w * 64 + 32 * i + li];
+    rstd[i] = rsqrtf(t / (float)D + p.eps);
+  }
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wave * 64 + 32 * j + 16 * lh;
+      const uint4* gp = (const uint4*)((const uint16_t*)p.gamma + n);
+      const uint4* bp = (const uint4*)((const uint16_t*)p.beta + n);
+      const uint4 g0 = gp[0], g1 = gp[1], b0 = bp[0], b1 = bp[1];
+      const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint32_t pk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lo = (acc[j][i][2 * e] - mean[i]) * rstd[i] *
+                               bf16_to_f32((uint16_t)(gw[e] & 0xffffu)) +
+                           bf16_to_f32((uint16_t)(bw[e] & 0xffffu));
+          const float hi = (acc[j][i][2 * e + 1] - mean[i]) * rstd[i] *
+                               bf16_to_f32((uint16_t)(gw[e] >> 16)) +
+                           bf16_to_f32((uint16_t)(bw[e] >> 16));
+          pk[e] = pack_bf16x2(lo, hi);
+        }
+        uint16_t* dst = es + (32 * i + li) * EP + n;
+        *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        *(uint4*)(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      }
+    }
+  }
+  __syncthreads();
+  // 16-byte chunks: D / 8 per row, rows contiguous in h_out
+  const int cpr = D / 8;
+  for (int q = tid; q < LBM * cpr; q += LNT) {
+    const int row = q / cpr, c = q - row * cpr;
+    const int m = m0 + row;
+    if (m < M)
+      *(uint4*)((uint16_t*)p.out + (int64_t)m * D + 8 * c) = *(const uint4*)(es + row * EP + 8 * c);
+  }
 }
 
 }  // namespace
@@ -236,21 +749,55 @@ bool gemm_mfma_supported(const GemmArgs& g) {
   const uintptr_t al = (uintptr_t)g.a.cur | (uintptr_t)g.w.W0 | (uintptr_t)g.w.W1 |
                        (g.a.mem_len ? (uintptr_t)g.a.mem : 0);
   if (al % 16) return false;
-  if (g.K > 0x7fffffffLL) return false;
+  // 32-bit row/column/offset arithmetic in the kernel
+  if (g.K > 0x7fffffffLL || g.M > 0x7fffffffLL - 256 || g.N > 0x7fffffffLL - 256) return false;
+  if (g.e.mode == EPI_HEADS) {
+    const int64_t per = g.a.mem_len + g.a.cur_rows;
+    const int64_t nb = (g.M + per - 1) / per;
+    const int64_t span = nb * g.e.sb + (g.N / (g.e.d > 0 ? g.e.d : 1) + 1) * g.e.sh + per * g.e.st;
+    if (span > 0x7fffffffLL) return false;
+  }
   return true;
 }
 
 hipError_t launch_gemm_mfma_multi(const GemmArgs* gs, int n, hipStream_t s, int num_cus) {
   if (n < 1 || n > MAXP) return hipErrorInvalidValue;
-  // 128-row tiles when they still give every CU two workgroups, else 64-row tiles
-  int64_t tiles128 = 0;
-  for (int p = 0; p < n; ++p) tiles128 += ((gs[p].M + 127) / 128) * ((gs[p].N + GBN - 1) / GBN);
-  if (tiles128 >= 2LL * num_cus) return launch_mi<2>(gs, n, s);
-  return launch_mi<1>(gs, n, s);
+  // 256 x 256 tiles when they give most CUs a workgroup, else 128 x 128
+  int64_t big = 0;
+  for (int p = 0; p < n; ++p)
+    big += ((gs[p].M + Big::BM - 1) / Big::BM) * ((gs[p].N + Big::BN - 1) / Big::BN);
+  if (big >= (int64_t)num_cus * 3 / 4) return launch_tiles<Big>(gs, n, num_cus, s);
+  return launch_tiles<Small>(gs, n, num_cus, s);
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s, int num_cus) {
   return launch_gemm_mfma_multi(&g, 1, s, num_cus);
+}
+
+bool gemm_ln_supported(const LnArgs& p) {
+  if (p.D % 64 != 0 || p.D > LDMAX || p.D < 64 || p.K % LBK != 0 || p.K < LBK) return false;
+  if (p.M < 1 || p.M > 0x7fffffffLL - LBM || p.M * p.K > 0x7fffffffLL || p.M * p.D > 0x7fffffffLL)
+    return false;
+  const uintptr_t al = (uintptr_t)p.a | (uintptr_t)p.W | (uintptr_t)p.resid |
+                       (uintptr_t)p.gamma | (uintptr_t)p.beta | (uintptr_t)p.out;
+  return al % 16 == 0;
+}
+
+hipError_t launch_gemm_ln(const LnArgs& p, hipStream_t s) {
+  const size_t ring = (size_t)LNS * (LBM + p.D) * LBK * sizeof(uint16_t);
+  const size_t epi = (size_t)LBM * (LDMAX + 8) * sizeof(uint16_t) + LNW * 64 * sizeof(float);
+  const size_t smem = cmax(ring, epi);
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t most = cmax((size_t)LNS * (LBM + LDMAX) * LBK * sizeof(uint16_t), epi);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_ln_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned blocks = (unsigned)((p.M + LBM - 1) / LBM);
+  hipLaunchKernelGGL(gemm_ln_kernel, dim3(blocks), dim3(LNT), smem, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace txl

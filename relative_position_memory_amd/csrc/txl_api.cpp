@@ -387,6 +387,13 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
   at.scores = nullptr;
   at.d_load = dp;  // workspace rows hold dp readable columns
   if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
+  // h_out = LayerNorm(a W_o^T + h): one fused kernel when the rows fit it
+  txl::LnArgs ln{B * L, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
+  if (dtype == TXL_BF16 && txl::gemm_ln_supported(ln)) {
+    const hipError_t e = txl::launch_gemm_ln(ln, st);
+    if (e != hipSuccess) return hip_fail(e, "output projection + LayerNorm");
+    return TXL_OK;
+  }
   // y = a W_o^T + h, then LayerNorm
   g = {};
   g.M = B * L; g.N = D; g.K = HD;
