@@ -3,26 +3,32 @@
 // Appendix B: distances 0 .. M+L-1, key j of query i at distance mem_len+i-j).
 //
 // One workgroup = 4 waves = 128 queries of one (batch row, head); each wave owns
-// 32 queries and walks the key tiles (64 keys) up to its last visible key with
-// an online softmax in the exp2 domain.  Per key tile and wave:
+// 32 queries as two groups of 16 and walks the 64-key tiles up to its last
+// visible key with an online softmax in the exp2 domain.  All products are
+// v_mfma_f32_16x16x32_bf16.  Per key tile and 16-query group:
 //
-//   position term  W^T = r_win . Qp^T : a 96 x 32 MFMA product of the r rows of
-//                  the 95 distances the tile can need (reversed order) with the
-//                  wave's queries (q+v) -> written to a wave-private LDS buffer.
-//                  Row ii of W (query ii) is stored with pitch P = 69 floats;
-//                  the score of (query ii, key jj) sits at window index
-//                  31 - ii + jj, i.e. at flat offset ii*(P-1) + jj + 31 : read
-//                  back with pitch P-1 the diagonal "relative shift" becomes a
-//                  plain aligned 16-byte read (the padded-reshape idea of the
-//                  shift, done in LDS addresses instead of memory copies).
-//                  Only the 64 window entries a row reads are written, so the
-//                  rows may overlap and the buffer stays small enough for two
-//                  workgroups per CU.
-//   content term   S^T = K . Qc^T  (q+u), with the position term loaded as the
-//                  MFMA accumulator, so the sum of the four terms costs no ALU op.
-//   softmax        S^T keeps one query per lane: row max and row sum are in-lane
-//                  (plus one exchange between the two lane halves).
-//   P.V            O^T = V^T . P^T, V staged transposed in LDS.
+//   position term  W^T = r_win . Qp^T: the 80 r rows of the distances the tile
+//                  can need (16 + 64 - 1, rounded up) against the group's
+//                  (q+v).  Lane (g, n) holds four consecutive window rows of
+//                  query n; they are written to a per-group LDS buffer with one
+//                  16-byte store (row pitch 68 floats; only the chunks the query
+//                  reads are stored, so rows may interleave).  Query n reads key
+//                  jj at window row 15 - n + jj: the diagonal "relative shift"
+//                  is a per-lane address offset on the read side.
+//   content term   S^T = K . Qc^T (q+u), accumulated onto the gathered
+//                  position term, so the four terms add inside the MFMA.
+//   softmax        lane (g, n) holds 16 of query n's 64 scores; row max and the
+//                  running sum are kept per lane and combined over the four
+//                  lanes of a query (lane xor 16, 32).
+//   P.V            O^T = V^T . P^T.  V stays row-major in LDS and its fragments
+//                  are read with ds_read_b64_tr_b16 (a transposing LDS read).
+//
+// K, V and the r rows reach LDS straight from global memory (global_load_lds,
+// no register staging).  r lives in a ring of three 64-distance blocks indexed
+// by (distance - mem_len) mod 192: successive key tiles move the window by one
+// block, so each tile loads only 64 new r rows.  Every 128-byte row stores its
+// 16-byte chunk c in slot c ^ ((row >> 1) & 7), which keeps the fragment reads
+// free of bank conflicts.
 //
 // The scale 1/sqrt(d) and log2(e) are folded into (q+u) and (q+v) before they
 // are rounded to bf16, so the softmax is exp2(S - max) with no extra multiply.
@@ -32,148 +38,73 @@ namespace txl {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int NW = 4;           // waves per workgroup
-constexpr int BQW = 32;         // queries per wave
+constexpr int BQW = 32;         // queries per wave (two groups of 16)
 constexpr int BQ = NW * BQW;    // queries per workgroup
 constexpr int BK = 64;          // keys per tile
 constexpr int DP = 64;          // head size padded for the MFMA k-loop
-constexpr int KP = 72;          // Ks / Rs row pitch (bf16): 144 B, 16B-aligned, conflict-free
-constexpr int VP = 68;          // Vt row pitch (bf16): 136 B, 8B-aligned, conflict-free
-constexpr int RROWS = BQ + BK;  // staged r rows: distances dist_lo .. dist_lo+191
-constexpr int WP = 69;          // W row pitch (floats); read pitch WP-1 = 68 (= 4 mod 32)
-constexpr int WBUF = 2208;      // one wave's W buffer (floats): 1 + 31*69 + 94 - 31 < 2208
+constexpr int RRING = 3 * BK;   // r ring rows (three 64-distance blocks)
+constexpr int WP = 68;          // W row pitch (floats): 16-byte aligned, conflict-free
+constexpr int WGF = 1088;       // one group's W buffer (floats): 15*68 + 76 + pad
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int NXCD = 8;         // accelerator dies (XCDs), one L2 each
 
 struct __align__(16) Smem {
-  uint16_t Ks[BK * KP];      // K tile, [key][c]
-  uint16_t Vt[DP * VP];      // V tile transposed, [c][key]
-  uint16_t Rs[RROWS * KP];   // r rows of the window union, [row][c], natural order
-  float Wb[NW * WBUF];       // position-term windows, one per wave
+  uint16_t K[BK * DP];       // key tile, [key][c], swizzled 16-byte chunks
+  uint16_t V[BK * DP];       // value tile, [key][c], swizzled
+  uint16_t R[RRING * DP];    // r ring, row (distance - mem_len) mod 192, swizzled
+  float W[NW][2][WGF];       // position-term windows, per wave and query group
 };
 
 // fp32 -> bf16 bits with the hardware conversion (round to nearest even)
 __device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ inline uint32_t pack2(float lo, float hi) {
+  return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+}
+
+// 16-byte slot of chunk c in row r: c ^ swz(r)
+__device__ inline int swz(int r) { return (r >> 1) & 7; }
+
+__device__ inline void dma16(const uint16_t* src, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
+}
+__device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
+// Workgroup barrier for LDS written by this workgroup's waves and for the
+// LDS-direct loads each wave has already waited for.
+__device__ inline void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory"); }
 
 __device__ inline bf16x8 lds_b128(const uint16_t* p) { return *(const bf16x8*)p; }
-__device__ inline bf16x8 lds_2xb64(const uint16_t* p0, const uint16_t* p1) {
-  const bf16x4 a = *(const bf16x4*)p0, b = *(const bf16x4*)p1;
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+__device__ inline bf16x8 lds_tr2(const uint16_t* p0, const uint16_t* p1) {
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
+  const v4s ab[2] = {a, b};
+  return *(const bf16x8*)ab;
 }
-
-// Column mask of a 16-byte chunk starting at column c0: all-ones words for
-// columns < d, zero words past d (d is not necessarily a multiple of 8).
-__device__ inline uint4 chunk_mask(int c0, int d) {
-  uint32_t w[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t lo = (c0 + 2 * e < d) ? 0x0000ffffu : 0u;
-    const uint32_t hi = (c0 + 2 * e + 1 < d) ? 0xffff0000u : 0u;
-    w[e] = lo | hi;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+// Reductions over the lanes n, n + 16, n + 32, n + 48 (one query of a 16 x 16
+// block) with the gfx950 lane-swap instructions: permlane16_swap(v, v) yields the
+// value of lane ^ 16 in one of its two results, permlane32_swap that of lane ^ 32.
+__device__ inline float max4(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  const uint32_t w = __builtin_bit_cast(uint32_t, x);
+  auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)q[0]), __builtin_bit_cast(float, (uint32_t)q[1]));
 }
-__device__ inline uint4 and4(uint4 a, uint4 m, bool keep) {
-  const uint32_t k = keep ? 0xffffffffu : 0u;
-  return make_uint4(a.x & m.x & k, a.y & m.y & k, a.z & m.z & k, a.w & m.w & k);
+__device__ inline float sum4(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+  const uint32_t w = __builtin_bit_cast(uint32_t, x);
+  auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __builtin_bit_cast(float, (uint32_t)q[0]) + __builtin_bit_cast(float, (uint32_t)q[1]);
 }
-
-// Registers holding one key tile on its way from HBM to LDS.  The loads are
-// unconditional (addresses clamped into the tensor); rows and columns that
-// are out of range are zeroed when the tile is written to LDS, after the wait
-// that the write needs anyway, so no load is waited for early.
-struct TileRegs {
-  uint4 k[2];  // two 16B chunks of K
-  uint4 v[2];  // V rows 2p and 2p+1, chunk cv
-  uint4 r[6];  // six 16B chunks of the r window
-};
-
-struct TileGeom {
-  const uint16_t* kb;
-  const uint16_t* vb;
-  const uint16_t* rb;
-  int kv_st, r_sp;  // strides (elements)
-  int T;            // keys
-  int cl_max;       // last loadable chunk index (d_load / 8 - 1)
-};
-
-__device__ inline void load_tile(TileRegs& tr, const TileGeom& g, int j0, int dist_lo, int tid) {
-  const int c = tid & 7;
-  const int cl = c < g.cl_max ? c : g.cl_max;
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int j = j0 + (tid >> 3) + 32 * x;
-    const int jc = j < g.T ? j : g.T - 1;
-    tr.k[x] = *(const uint4*)(g.kb + (int64_t)jc * g.kv_st + 8 * cl);
-  }
-  // V: key pair p = tid & 31 (fastest, so the transposed LDS writes are
-  // conflict-free), chunk cv = tid >> 5
-  const int cv = tid >> 5;
-  const int cvl = cv < g.cl_max ? cv : g.cl_max;
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int j = j0 + 2 * (tid & 31) + x;
-    const int jc = j < g.T ? j : g.T - 1;
-    tr.v[x] = *(const uint4*)(g.vb + (int64_t)jc * g.kv_st + 8 * cvl);
-  }
-#pragma unroll
-  for (int x = 0; x < 6; ++x) {
-    const int dist = dist_lo + (tid >> 3) + 32 * x;
-    const int dc = dist < 0 ? 0 : (dist < g.T ? dist : g.T - 1);
-    tr.r[x] = *(const uint4*)(g.rb + (int64_t)dc * g.r_sp + 8 * cl);
-  }
-}
-
-__device__ inline void store_tile(Smem& sm, const TileRegs& tr, const TileGeom& g, uint4 cmask,
-                                  uint4 cmask_v, bool full_cols, int j0, int dist_lo, int tid) {
-  const int c = tid & 7;
-  const int p = tid & 31, cv = tid >> 5;
-  // interior tile with all 64 columns live: no masking at all (wave-uniform)
-  if (full_cols && j0 + BK <= g.T && dist_lo >= 0 && dist_lo + RROWS <= g.T) {
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-      *(uint4*)&sm.Ks[((tid >> 3) + 32 * x) * KP + 8 * c] = tr.k[x];
-    const uint32_t* v0 = (const uint32_t*)&tr.v[0];
-    const uint32_t* v1 = (const uint32_t*)&tr.v[1];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w) * VP + 2 * p] = (v0[w] & 0xffffu) | (v1[w] << 16);
-      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w + 1) * VP + 2 * p] = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
-    }
-#pragma unroll
-    for (int x = 0; x < 6; ++x)
-      *(uint4*)&sm.Rs[((tid >> 3) + 32 * x) * KP + 8 * c] = tr.r[x];
-    return;
-  }
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int key = (tid >> 3) + 32 * x;
-    *(uint4*)&sm.Ks[key * KP + 8 * c] = and4(tr.k[x], cmask, j0 + key < g.T);
-  }
-  {
-    const uint4 a0 = and4(tr.v[0], cmask_v, j0 + 2 * p < g.T);
-    const uint4 a1 = and4(tr.v[1], cmask_v, j0 + 2 * p + 1 < g.T);
-    const uint32_t* v0 = (const uint32_t*)&a0;
-    const uint32_t* v1 = (const uint32_t*)&a1;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // elements 2w (low halves) and 2w+1 (high halves) of keys 2p and 2p+1
-      const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);
-      const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
-      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w) * VP + 2 * p] = lo;
-      *(uint32_t*)&sm.Vt[(8 * cv + 2 * w + 1) * VP + 2 * p] = hi;
-    }
-  }
-#pragma unroll
-  for (int x = 0; x < 6; ++x) {
-    const int row = (tid >> 3) + 32 * x;
-    const int dist = dist_lo + row;
-    *(uint4*)&sm.Rs[row * KP + 8 * c] = and4(tr.r[x], cmask, dist >= 0 && dist < g.T);
-  }
+__device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, int groups) {
@@ -195,23 +126,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   if (g >= groups) return;
   const int64_t b = g / a.H, hd = g % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int li = lane & 31, lh = lane >> 5;
+  const int g4 = lane >> 4, n16 = lane & 15;  // 16x16 MFMA lane coordinates
   const int d = (int)a.d;
   const int L = (int)a.L, len = (int)a.mem_len, T = len + L;
   const int q0 = qt * BQ;
   const int i0w = q0 + wave * BQW;
-
-  TileGeom tg;
-  tg.kb = (const uint16_t*)a.k + b * a.kv_sb + hd * a.kv_sh;
-  tg.vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
-  tg.rb = (const uint16_t*)a.r + hd * a.r_sh;
-  tg.kv_st = (int)a.kv_st;
-  tg.r_sp = (int)a.r_sp;
-  tg.T = T;
-  tg.cl_max = (int)(a.d_load / 8) - 1;
-  const uint4 cmask = chunk_mask(8 * (tid & 7), d);
-  const uint4 cmask_v = chunk_mask(8 * (tid >> 5), d);
-  const bool full_cols = d == DP;
+  const int cl_max = (int)(a.d_load / 8) - 1;  // last readable 16-byte chunk of a row
 
   // key tiles of this workgroup: all tiles up to the last query's last key,
   // or this split's share of them
@@ -222,258 +142,329 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const int imax_w = (i0w + BQW - 1 < L - 1) ? i0w + BQW - 1 : L - 1;
   const int kt_w = wave_has_rows ? (len + imax_w) / BK : -1;
 
-  TileRegs tr;
-  if (kt_lo < kt_hi) load_tile(tr, tg, kt_lo * BK, len + q0 - kt_lo * BK - BK, tid);
+  // ---- LDS-direct loads: instruction x (0, 1) of this wave fills tile rows
+  //      16 wave + 8 x .. + 7; lane -> row + lane / 8, slot lane % 8 (chunk slot ^ swz)
+  const uint16_t* kb = (const uint16_t*)a.k + b * a.kv_sb + hd * a.kv_sh;
+  const uint16_t* vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
+  const uint16_t* rb = (const uint16_t*)a.r + hd * a.r_sh;
+  const int kv_st = (int)a.kv_st, r_sp = (int)a.r_sp;
+  int drow[2], dch[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    drow[x] = 16 * wave + 8 * x + (lane >> 3);
+    const int c = (lane & 7) ^ swz(drow[x]);
+    dch[x] = 8 * (c < cl_max ? c : cl_max);  // chunks past d_load repeat a real one (times q = 0)
+  }
+  auto load_kv = [&](const uint16_t* base, uint16_t* lds, int j0) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;  // keys past T are masked
+      dma16(base + j * kv_st + dch[x], lds + (16 * wave + 8 * x) * DP);
+    }
+  };
+  // r rows of relative distances e0 .. e0 + 63 (e = distance - mem_len, e0 % 64 == 0)
+  auto load_r = [&](int e0) {
+    const int ring0 = ((e0 % RRING) + RRING) % RRING;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      int dist = len + e0 + drow[x];
+      dist = dist < 0 ? 0 : (dist < T ? dist : T - 1);  // out-of-range distances feed masked scores only
+      dma16(rb + dist * r_sp + dch[x], sm.R + (ring0 + 16 * wave + 8 * x) * DP);
+    }
+  };
 
-  // ---- this lane's query (column li of the MFMA B operand), pre-scaled ----------
-  bf16x8 qc[4], qp[4];
+  // ---- fragment offsets (elements / floats), fixed for the whole walk -----------------
+  // K (16x16x32 A operand): row 16 kb + n16, chunk 4 s + g4
+  int koff[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) koff[s] = n16 * DP + 8 * ((4 * s + g4) ^ swz(n16));
+  // V^T through transposing reads: lane (g4, n16) of a 16-lane group reads key row
+  // 4 g4 + n16 / 4 (+ 32 h + 16 kb'), columns 16 dblk + 4 (n16 % 4) .. + 3
+  int voff[4];
   {
-    const int i = i0w + li;
-    const int ic = i < L ? i : L - 1;
-    const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + (int64_t)ic * a.q_st + hd * a.q_sh;
+    const int vrow = 4 * g4 + (n16 >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int piece = 4 * db + (n16 & 3);  // 8-byte piece of the row
+      voff[db] = vrow * DP + 8 * ((piece >> 1) ^ swz(vrow)) + 4 * (piece & 1);
+    }
+  }
+  // W: lane (g4, n16) writes rows 16 b + 4 g4 .. + 3 of query n16 and reads key
+  // jj = 16 kb + 4 g4 + i at window row 15 - n16 + jj.
+  float* wbuf[2] = {sm.W[wave][0], sm.W[wave][1]};
+  const int wwoff = n16 * WP + 4 * g4;
+  const int wroff = n16 * (WP - 1) + 15 + 4 * g4;
+  // only the window rows a query reads are stored (block 0 and 4 partly)
+  const bool wr0 = 4 * g4 + 3 >= 15 - n16;
+  const bool wr4 = 64 + 4 * g4 <= 78 - n16;
+  // r fragments: union block u (0..5) of the wave's 96 window rows, row rho =
+  // n16 is relative distance i0w - j0 + 31 - 16 u - n16, stored at ring row
+  // (that) mod 192; roff[u] is its s = 0 offset, s = 1 is roff[u] ^ 32.
+  int roff[6];
+
+  // ---- this lane's queries, pre-scaled: group gm holds query i0w + 16 gm + n16,
+  //      k-step s columns 32 s + 8 g4 .. + 7 ---------------------------------------------
+  bf16x8 qc[2][2], qp[2][2];
+  {
     const uint16_t* ur = (const uint16_t*)a.u + hd * d;
     const uint16_t* vr = (const uint16_t*)a.vb + hd * d;
     const float sl2 = a.scale * LOG2E;
-    // u and v rows: 16-byte loads when they are aligned, else element by element
     const bool uv_vec = (d % 8 == 0) && ((((uintptr_t)a.u) | ((uintptr_t)a.vb)) % 16 == 0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c0 = 16 * s + 8 * lh;
-      const int cc = c0 / 8 < tg.cl_max ? c0 : 8 * tg.cl_max;
-      const uint4 raw = *(const uint4*)(qrow + cc);
-      const uint16_t* rv = (const uint16_t*)&raw;
-      uint16_t uh[8], vh[8];
-      if (uv_vec && c0 < d) {
-        *(uint4*)uh = *(const uint4*)(ur + c0);
-        *(uint4*)vh = *(const uint4*)(vr + c0);
-      } else {
+    for (int gm = 0; gm < 2; ++gm) {
+      const int i = i0w + 16 * gm + n16;
+      const int ic = i < L ? i : L - 1;
+      const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + (int64_t)ic * a.q_st + hd * a.q_sh;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c0 = 32 * s + 8 * g4;
+        const int cc = c0 / 8 < cl_max ? c0 : 8 * cl_max;
+        const uint4 raw = *(const uint4*)(qrow + cc);
+        const uint16_t* rv = (const uint16_t*)&raw;
+        uint16_t uh[8], vh[8];
+        if (uv_vec && c0 < d) {
+          *(uint4*)uh = *(const uint4*)(ur + c0);
+          *(uint4*)vh = *(const uint4*)(vr + c0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uh[e] = c0 + e < d ? ur[c0 + e] : (uint16_t)0;
+            vh[e] = c0 + e < d ? vr[c0 + e] : (uint16_t)0;
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          uh[e] = c0 + e < d ? ur[c0 + e] : (uint16_t)0;
-          vh[e] = c0 + e < d ? vr[c0 + e] : (uint16_t)0;
+          const bool ok = c0 + e < d && i < L;
+          const float x = bf16_to_f32(rv[e]);
+          qc[gm][s][e] = (__bf16)(ok ? (x + bf16_to_f32(uh[e])) * sl2 : 0.f);
+          qp[gm][s][e] = (__bf16)(ok ? (x + bf16_to_f32(vh[e])) * sl2 : 0.f);
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool ok = c0 + e < d && i < L;
-        const float x = bf16_to_f32(rv[e]);
-        qc[s][e] = (__bf16)(ok ? (x + bf16_to_f32(uh[e])) * sl2 : 0.f);
-        qp[s][e] = (__bf16)(ok ? (x + bf16_to_f32(vh[e])) * sl2 : 0.f);
       }
     }
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 acc[2];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 acc[2][4];
 #pragma unroll
-  for (int x = 0; x < 16; ++x) { acc[0][x] = 0.f; acc[1][x] = 0.f; }
+  for (int gm = 0; gm < 2; ++gm)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[gm][db] = {0.f, 0.f, 0.f, 0.f};
 
-  float* wb = sm.Wb + wave * WBUF;
   float* srow_base = nullptr;
   if (a.scores) srow_base = a.scores + ((b * a.H + hd) * a.L) * (int64_t)T;
 
+  // ---- first tile: K, V and the three r blocks of its window -----------------------------
+  if (kt_lo < kt_hi) {
+    const int j0 = kt_lo * BK;
+    load_kv(kb, sm.K, j0);
+    load_kv(vb, sm.V, j0);
+#pragma unroll
+    for (int blk = 0; blk < 3; ++blk) load_r(q0 - j0 - BK + BK * blk);
+    // ring offsets of the union blocks for this tile
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int e = i0w - j0 + 31 - 16 * u - n16;
+      const int rr = ((e % RRING) + RRING) % RRING;
+      roff[u] = rr * DP + 8 * (g4 ^ swz(rr));
+    }
+  }
+
+  // Per tile: [own loads of K, r landed] barrier A -> load V -> position, content
+  //   -> [V landed] barrier B -> load next K and r block -> softmax, P.V.
+  // K is overwritten only after barrier B (every wave is past its content
+  // product), the r block the next tile drops likewise, V only after the next
+  // barrier A (every wave is past its P.V).
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     const int j0 = kt * BK;
-    __syncthreads();
-    store_tile(sm, tr, tg, cmask, cmask_v, full_cols, j0, len + q0 - j0 - BK, tid);
-    __syncthreads();
-    if (kt + 1 < kt_hi) load_tile(tr, tg, j0 + BK, len + q0 - j0 - 2 * BK, tid);
-    if (kt > kt_w) continue;
-
-    const int Dw = len + i0w - j0;  // distance of (query 0, key 0) of this wave's tile
-
-    // ---- position term: W^T[w''][ii] = r[Dw + 31 - w''] . qp[ii], w'' in [0, 96) ----
-    // A-row li of block blk is distance Dw + 31 - 32 blk - li, staged at row
-    // dist - (len + q0 - j0 - 64), which lies in [0, 191].
-    {
-      f32x16 w[3];
+    wait_dma();
+    barrier();
+    if (kt != kt_lo) load_kv(vb, sm.V, j0);
+    const bool work = kt <= kt_w;
+    const int Dw = len + i0w - j0;  // distance of (query i0w, key j0)
+    f32x4 sc[2][4];
+    if (work) {
+      // ---- position term: W^T[gm] block bw = union block bw + 1 - gm.  All r
+      //      and K fragments are read first, so their LDS latency overlaps.
+      bf16x8 rf[6][2], kf[4][2];
 #pragma unroll
-      for (int blk = 0; blk < 3; ++blk)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) w[blk][x] = 0.f;
-      // all twelve A fragments first, so their LDS latency overlaps
-      bf16x8 ar[3][4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int blk = 0; blk < 3; ++blk)
-          ar[blk][s] = lds_b128(&sm.Rs[(BQW * wave + 95 - 32 * blk - li) * KP + 16 * s + 8 * lh]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int blk = 0; blk < 3; ++blk)
-          w[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[blk][s], qp[s], w[blk], 0, 0, 0);
-      // lane (query li, half lh), reg x -> window index w'' = 32 blk + 8 (x/4) + 4 lh + x%4;
-      // row li reads w'' in [31 - li, 94 - li] only, and only those are written:
-      // all of block 1, the part of block 0 with w'' >= 31 - li and the part of
-      // block 2 with w'' <= 94 - li.  The other values of blocks 0 and 2 go to a
-      // per-lane dump slot (floats 0..31 of the buffer are never read), which
-      // keeps the writes branch-free.
-      float* wrow = wb + 1 + li * WP + 4 * lh;
-      float* dump = wb + li;
-      const int c_l = li + 4 * lh;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int off = 8 * (x >> 2) + (x & 3);
-        wrow[32 + off] = w[1][x];
-        *(c_l + off >= 31 ? wrow + off : dump) = w[0][x];
-        *(c_l + off <= 30 ? wrow + 64 + off : dump) = w[2][x];
+      for (int u = 0; u < 6; ++u) {
+        rf[u][0] = lds_b128(sm.R + roff[u]);
+        rf[u][1] = lds_b128(sm.R + (roff[u] ^ 32));
       }
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) kf[kbk][s] = lds_b128(sm.K + kbk * 16 * DP + koff[s]);
+      f32x4 wv[2][5];
+#pragma unroll
+      for (int bw = 0; bw < 5; ++bw)
+#pragma unroll
+        for (int gm = 0; gm < 2; ++gm) {
+          const int u = bw + 1 - gm;
+          f32x4 w = {0.f, 0.f, 0.f, 0.f};
+          w = mfma(rf[u][0], qp[gm][0], w);
+          wv[gm][bw] = mfma(rf[u][1], qp[gm][1], w);
+        }
+#pragma unroll
+      for (int bw = 0; bw < 5; ++bw)
+#pragma unroll
+        for (int gm = 0; gm < 2; ++gm) {
+          const bool keep = bw == 0 ? wr0 : (bw == 4 ? wr4 : true);
+          if (keep) *(f32x4*)(wbuf[gm] + wwoff + 16 * bw) = wv[gm][bw];
+        }
+      // the window reads below are this wave's own stores
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // ---- content term on top of the gathered position term --------------------------
+#pragma unroll
+      for (int gm = 0; gm < 2; ++gm)
+#pragma unroll
+        for (int kbk = 0; kbk < 4; ++kbk) {
+          const float* wr = wbuf[gm] + wroff + 16 * kbk;
+          f32x4 c = {wr[0], wr[1], wr[2], wr[3]};
+          c = mfma(kf[kbk][0], qc[gm][0], c);
+          c = mfma(kf[kbk][1], qc[gm][1], c);
+          sc[gm][kbk] = c;
+        }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- content term with the gathered position term as accumulator ------------
-    f32x16 sc[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) {
-        // keys jj = 32 kb2 + 8 x4 + 4 lh + t, t = 0..3 -> flat 32 + 100 li + jj
-        const f32x4 sp = *(const f32x4*)&wb[32 + (WP - 1) * li + 32 * kb2 + 8 * x4 + 4 * lh];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) sc[kb2][4 * x4 + t] = sp[t];
-      }
-    {
-      bf16x8 ak[2][4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-          ak[kb2][s] = lds_b128(&sm.Ks[(32 * kb2 + li) * KP + 16 * s + 8 * lh]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-          sc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kb2][s], qc[s], sc[kb2], 0, 0, 0);
+    wait_dma();
+    barrier();
+    if (kt + 1 < kt_hi) {
+      load_kv(kb, sm.K, j0 + BK);
+      load_r(q0 - j0 - 2 * BK);  // the block the next tile adds
     }
+    // the next tile's union blocks sit one ring block lower
+#pragma unroll
+    for (int u = 0; u < 6; ++u) roff[u] = roff[u] >= BK * DP ? roff[u] - BK * DP : roff[u] + 2 * BK * DP;
+    if (!work) continue;
 
-    // ---- causal mask (tiles that reach past the wave's first query only) --------
+    // ---- causal mask (tiles that reach past the wave's first query only) --------------
     if (j0 + BK - 1 > len + i0w) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int gm = 0; gm < 2; ++gm)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int jj = 32 * kb2 + 8 * (x >> 2) + 4 * lh + (x & 3);
-          sc[kb2][x] = (jj - li > Dw) ? -INFINITY : sc[kb2][x];
-        }
+        for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jj = 16 * kbk + 4 * g4 + e;
+            sc[gm][kbk][e] = (jj - n16 > Dw + 16 * gm) ? -INFINITY : sc[gm][kbk][e];
+          }
     }
     if (srow_base) {
-      const int i = i0w + li;
-      if (i < L) {
-        float* srow = srow_base + (int64_t)i * T;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int gm = 0; gm < 2; ++gm) {
+        const int i = i0w + 16 * gm + n16;
+        if (i < L) {
+          float* srow = srow_base + (int64_t)i * T;
 #pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int j = j0 + 32 * kb2 + 8 * (x >> 2) + 4 * lh + (x & 3);
-            if (j < T) srow[j] = sc[kb2][x] * (1.0f / LOG2E);
-          }
-      }
-    }
-
-    // ---- online softmax (exp2 domain), one query per lane --------------------------
-    float tmax = -INFINITY;
+          for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sc[kb2][x]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    // a split's tiles can hide every key of a query so far: keep the max at
-    // -inf then, with zero weights and no NaN from (-inf) - (-inf)
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float p = __builtin_amdgcn_exp2f(sc[kb2][x] - m_use);
-        sc[kb2][x] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-    // the running max rarely moves after the first tiles: rescale only if it did
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        acc[0][x] *= alpha;
-        acc[1][x] *= alpha;
-      }
-    }
-
-    // ---- O^T += V^T . P^T ------------------------------------------------------------
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 pb;
-      const int kb2 = s >> 1, v0 = 8 * (s & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[kb2][v0 + e];
-      bf16x8 av[2];
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const uint16_t* vrow = &sm.Vt[(32 * db + li) * VP + 16 * s + 4 * lh];
-        av[db] = lds_2xb64(vrow, vrow + 8);
-      }
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[db], pb, acc[db], 0, 0, 0);
-    }
-  }
-
-  // ---- epilogue: out[i][c] = acc / l -------------------------------------------------
-  if (!wave_has_rows) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const int i = i0w + li;
-  if (i >= L) return;
-  if (nsplit > 1) {
-    // unnormalised partial of this split: acc (all 64 columns), max and sum
-    const int64_t row = ((int64_t)split * groups + g) * a.L + i;
-    float* pa = a.part_acc + row * DP;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) {
-        const int c = 32 * db + 8 * x4 + 4 * lh;
-        *(f32x4*)(pa + c) = {acc[db][4 * x4], acc[db][4 * x4 + 1], acc[db][4 * x4 + 2],
-                             acc[db][4 * x4 + 3]};
-      }
-    if (lh == 0) {
-      a.part_ml[2 * row] = m_run;
-      a.part_ml[2 * row + 1] = l_tot;
-    }
-    return;
-  }
-  const float inv = 1.f / l_tot;
-  uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
-  const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
-                   ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
-  if (vec) {
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) {
-        const int c = 32 * db + 8 * x4 + 4 * lh;
-        if (c < d) {
-          uint2 pk;
-          pk.x = bf16_bits(acc[db][4 * x4] * inv) |
-                 ((uint32_t)bf16_bits(acc[db][4 * x4 + 1] * inv) << 16);
-          pk.y = bf16_bits(acc[db][4 * x4 + 2] * inv) |
-                 ((uint32_t)bf16_bits(acc[db][4 * x4 + 3] * inv) << 16);
-          *(uint2*)(orow + c) = pk;
+            for (int e = 0; e < 4; ++e) {
+              const int j = j0 + 16 * kbk + 4 * g4 + e;
+              if (j < T) srow[j] = sc[gm][kbk][e] * (1.0f / LOG2E);
+            }
         }
       }
-  } else {
+    }
+
+    // ---- online softmax (exp2 domain); query n16 of group gm lives in lanes
+    //      n16 + 16 g4, g4 = 0..3 ------------------------------------------------------
+    bf16x8 pb[2][2];
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int gm = 0; gm < 2; ++gm) {
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int c = 32 * db + 8 * (x >> 2) + 4 * lh + (x & 3);
-        if (c < d) orow[c] = bf16_bits(acc[db][x] * inv);
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[gm][kbk][e]);
+      tmax = max4(tmax);
+      const float m_new = fmaxf(m_run[gm], tmax);
+      // a split's tiles can hide every key of a query so far: keep the max at
+      // -inf then, with zero weights and no NaN from (-inf) - (-inf)
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[gm] - m_use);
+      m_run[gm] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(sc[gm][kbk][e] - m_use);
+          sc[gm][kbk][e] = p;
+          psum += p;
+        }
+      l_run[gm] = l_run[gm] * alpha + psum;
+      // the running max rarely moves after the first tiles: rescale only if it did
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[gm][db][e] *= alpha;
       }
+      // P^T operand of key half h: k index 8 g4 + 4 kb' + e <-> key 32 h + 16 kb' + 4 g4 + e
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w0 = pack2(sc[gm][2 * h][0], sc[gm][2 * h][1]);
+        const uint32_t w1 = pack2(sc[gm][2 * h][2], sc[gm][2 * h][3]);
+        const uint32_t w2 = pack2(sc[gm][2 * h + 1][0], sc[gm][2 * h + 1][1]);
+        const uint32_t w3 = pack2(sc[gm][2 * h + 1][2], sc[gm][2 * h + 1][3]);
+        const uint4 pk = make_uint4(w0, w1, w2, w3);
+        pb[gm][h] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+
+    // ---- O^T += V^T . P^T --------------------------------------------------------------
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 vf[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        vf[db] = lds_tr2(sm.V + (32 * h) * DP + voff[db], sm.V + (32 * h + 16) * DP + voff[db]);
+#pragma unroll
+      for (int gm = 0; gm < 2; ++gm)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[gm][db] = mfma(vf[db], pb[gm][h], acc[gm][db]);
+    }
+  }
+
+  // ---- epilogue: out[i][c] = acc / l, lane (g4, n16) of block db holds query
+  //      i0w + 16 gm + n16, columns 16 db + 4 g4 .. + 3 -------------------------------------
+  if (!wave_has_rows) return;
+#pragma unroll
+  for (int gm = 0; gm < 2; ++gm) {
+    const float l_tot = sum4(l_run[gm]);
+    const int i = i0w + 16 * gm + n16;
+    if (i >= L) continue;
+    if (nsplit > 1) {
+      // unnormalised partial of this split: acc (all 64 columns), max and sum
+      const int64_t row = ((int64_t)split * groups + g) * a.L + i;
+      float* pa = a.part_acc + row * DP;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) *(f32x4*)(pa + 16 * db + 4 * g4) = acc[gm][db];
+      if (g4 == 0) {
+        a.part_ml[2 * row] = m_run[gm];
+        a.part_ml[2 * row + 1] = l_tot;
+      }
+      continue;
+    }
+    const float inv = 1.f / l_tot;
+    uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
+    const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
+                     ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int c = 16 * db + 4 * g4;
+      if (vec) {
+        if (c < d)
+          *(uint2*)(orow + c) = make_uint2(pack2(acc[gm][db][0] * inv, acc[gm][db][1] * inv),
+                                           pack2(acc[gm][db][2] * inv, acc[gm][db][3] * inv));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < d) orow[c + e] = bf16_bits(acc[gm][db][e] * inv);
+      }
+    }
   }
 }
 
