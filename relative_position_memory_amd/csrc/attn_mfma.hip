@@ -112,17 +112,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   Smem& sm = *(Smem*)smem_raw;
 
   // Workgroups are dispatched to the 8 XCDs round-robin by id, and each XCD has
-  // its own L2.  Block id n runs on XCD n % 8 as its (n / 8)-th block; that
-  // XCD takes the (batch, head) groups g = x, x + 8, ... with their query tiles
-  // consecutive and longest first, so the tiles of a group run together on
-  // one L2 and share its K, V and r.  With a key split, the nsplit workgroups
-  // of one query tile are consecutive as well.
+  // its own L2.  Block id n runs on XCD n % 8 as its (n / 8)-th block; XCD x
+  // owns the (batch, head) groups g = x, x + 8, ..., so their K, V and r stay in
+  // one L2.  Each XCD first issues the last query tile (the most key tiles) of
+  // all its groups, then the one before, and so on: the long workgroups start
+  // first and the short ones fill the tail.  With a key split, the nsplit
+  // workgroups of one query tile are consecutive.
   const int nsplit = a.nsplit;
-  const int nper = nqt * nsplit;
+  const int gpx = (groups + NXCD - 1) / NXCD;  // groups per XCD
   const int xcd = blockIdx.x % NXCD, k_on = blockIdx.x / NXCD;
-  const int g = (k_on / nper) * NXCD + xcd;
-  const int qt = nqt - 1 - (k_on % nper) / nsplit;
-  const int split = (k_on % nper) % nsplit;
+  const int slot = k_on / nsplit;
+  const int g = (slot % gpx) * NXCD + xcd;
+  const int qt = nqt - 1 - slot / gpx;
+  const int split = k_on % nsplit;
   if (g >= groups) return;
   const int64_t b = g / a.H, hd = g % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
