@@ -10,11 +10,11 @@
 //   position term  W^T = r_win . Qp^T: the 80 r rows of the distances the tile
 //                  can need (16 + 64 - 1, rounded up) against the group's
 //                  (q+v).  Lane (g, n) holds four consecutive window rows of
-//                  query n; they are written to a per-group LDS buffer with one
-//                  16-byte store (row pitch 68 floats; only the chunks the query
-//                  reads are stored, so rows may interleave).  Query n reads key
-//                  jj at window row 15 - n + jj: the diagonal "relative shift"
-//                  is a per-lane address offset on the read side.
+//                  query n; window row rho of query n is the distance of key
+//                  jj = rho - 15 + n, so each value is stored in key jj's slot
+//                  of a [query][key] LDS buffer (row pitch 68 floats): the
+//                  diagonal "relative shift" is a per-lane address offset on
+//                  the store side and the reads are aligned 16-byte loads.
 //   content term   S^T = K . Qc^T (q+u), accumulated onto the gathered
 //                  position term, so the four terms add inside the MFMA.
 //   softmax        lane (g, n) holds 16 of query n's 64 scores; row max and the
@@ -47,8 +47,8 @@ constexpr int BQ = NW * BQW;    // queries per workgroup
 constexpr int BK = 64;          // keys per tile
 constexpr int DP = 64;          // head size padded for the MFMA k-loop
 constexpr int RRING = 3 * BK;   // r ring rows (three 64-distance blocks)
-constexpr int WP = 68;          // W row pitch (floats): 16-byte aligned, conflict-free
-constexpr int WGF = 1088;       // one group's W buffer (floats): 15*68 + 76 + pad
+constexpr int WP = 68;          // S_p row pitch (floats): 16-byte aligned, conflict-free reads
+constexpr int WGF = 1088;       // one group's S_p buffer (floats): 16 rows of WP
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int NXCD = 8;         // accelerator dies (XCDs), one L2 each
 
@@ -191,14 +191,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
       voff[db] = vrow * DP + 8 * ((piece >> 1) ^ swz(vrow)) + 4 * (piece & 1);
     }
   }
-  // W: lane (g4, n16) writes rows 16 b + 4 g4 .. + 3 of query n16 and reads key
-  // jj = 16 kb + 4 g4 + i at window row 15 - n16 + jj.
+  // Gathered position term S_p[query n][key jj] at wbuf[gm][n * WP + jj]: lane
+  // (g4, n16) holds window rows 16 bw + 4 g4 + e of query n16 (row rho = distance
+  // offset 15 - n16 + jj) and stores them at skoff + 16 bw + e.
   float* wbuf[2] = {sm.W[wave][0], sm.W[wave][1]};
-  const int wwoff = n16 * WP + 4 * g4;
-  const int wroff = n16 * (WP - 1) + 15 + 4 * g4;
-  // only the window rows a query reads are stored (block 0 and 4 partly)
-  const bool wr0 = 4 * g4 + 3 >= 15 - n16;
-  const bool wr4 = 64 + 4 * g4 <= 78 - n16;
+  const int skoff = n16 * (WP + 1) + 4 * g4 - 15;
   // r fragments: union block u (0..5) of the wave's 96 window rows, row rho =
   // n16 is relative distance i0w - j0 + 31 - 16 u - n16, stored at ring row
   // (that) mod 192; roff[u] is its s = 0 offset, s = 1 is roff[u] ^ 32.
@@ -307,13 +304,20 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
           w = mfma(rf[u][0], qp[gm][0], w);
           wv[gm][bw] = mfma(rf[u][1], qp[gm][1], w);
         }
+      // The diagonal shift happens at the store: value (gm, bw, e) of lane (g4, n16)
+      // is window row 16 bw + 4 g4 + e of query n16, the distance of key
+      // 16 bw + 4 g4 + e - 15 + n16, and is stored in that key's slot of row n16
+      // (rows of keys 0..63 only), so the reads below are aligned 16-byte loads.
 #pragma unroll
       for (int bw = 0; bw < 5; ++bw)
 #pragma unroll
-        for (int gm = 0; gm < 2; ++gm) {
-          const bool keep = bw == 0 ? wr0 : (bw == 4 ? wr4 : true);
-          if (keep) *(f32x4*)(wbuf[gm] + wwoff + 16 * bw) = wv[gm][bw];
-        }
+        for (int gm = 0; gm < 2; ++gm)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool keep = bw == 0 ? (4 * g4 + e >= 15 - n16)
+                                      : (bw == 4 ? (64 + 4 * g4 + e <= 78 - n16) : true);
+            if (keep) wbuf[gm][skoff + 16 * bw + e] = wv[gm][bw][e];
+          }
       // the window reads below are this wave's own stores
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -323,8 +327,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
       for (int gm = 0; gm < 2; ++gm)
 #pragma unroll
         for (int kbk = 0; kbk < 4; ++kbk) {
-          const float* wr = wbuf[gm] + wroff + 16 * kbk;
-          f32x4 c = {wr[0], wr[1], wr[2], wr[3]};
+          f32x4 c = *(const f32x4*)(wbuf[gm] + n16 * WP + 16 * kbk + 4 * g4);
           c = mfma(kf[kbk][0], qc[gm][0], c);
           c = mfma(kf[kbk][1], qc[gm][1], c);
           sc[gm][kbk] = c;
@@ -416,7 +419,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
       }
     }
 
-    // ---- O^T += V^T . P^T --------------------------------------------------------------
+    // ---- O^T += V^T . P^T (raised issue priority: while this wave feeds the
+    //      matrix core, the other waves' vector work waits) ------------------------------
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 vf[4];
@@ -428,6 +433,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc[gm][db] = mfma(vf[db], pb[gm][h], acc[gm][db]);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- epilogue: out[i][c] = acc / l, lane (g4, n16) of block db holds query
