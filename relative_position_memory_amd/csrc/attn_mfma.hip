@@ -24,8 +24,8 @@
 //                  are read with ds_read_b64_tr_b16 (a transposing LDS read).
 //
 // K, V and the r rows reach LDS straight from global memory (global_load_lds,
-// no register staging).  r lives in a ring of three 64-distance blocks indexed
-// by (distance - mem_len) mod 192: successive key tiles move the window by one
+// no register staging).  r lives in a ring of four 64-distance blocks indexed
+// by (distance - mem_len) mod 256: successive key tiles move the window by one
 // block, so each tile loads only 64 new r rows.  Every 128-byte row stores its
 // 16-byte chunk c in slot c ^ ((row >> 1) & 7), which keeps the fragment reads
 // free of bank conflicts.
@@ -46,23 +46,26 @@ constexpr int BQW = 32;         // queries per wave (two groups of 16)
 constexpr int BQ = NW * BQW;    // queries per workgroup
 constexpr int BK = 64;          // keys per tile
 constexpr int DP = 64;          // head size padded for the MFMA k-loop
-constexpr int RRING = 3 * BK;   // r ring rows (three 64-distance blocks)
-constexpr int WP = 68;          // S_p row pitch (floats): 16-byte aligned, conflict-free reads
-constexpr int WGF = 1088;       // one group's S_p buffer (floats): 16 rows of WP
+constexpr int RRING = 4 * BK;   // r ring rows (four 64-distance blocks)
+constexpr int WGF = 16 * 64;    // a wave's S_p buffer (floats): 16 queries x 64 keys
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int NXCD = 8;         // accelerator dies (XCDs), one L2 each
 
+// 80 KB: two workgroups fill a CU's 160 KB.
 struct __align__(16) Smem {
-  uint16_t K[BK * DP];       // key tile, [key][c], swizzled 16-byte chunks
-  uint16_t V[BK * DP];       // value tile, [key][c], swizzled
-  uint16_t R[RRING * DP];    // r ring, row (distance - mem_len) mod 192, swizzled
-  float W[NW][2][WGF];       // position-term windows, per wave and query group
+  uint16_t K[2][BK * DP];    // key tiles (double-buffered), [key][c], swizzled 16-byte chunks
+  uint16_t V[2][BK * DP];    // value tiles (double-buffered), [key][c], swizzled
+  uint16_t R[RRING * DP];    // r ring, row (distance - mem_len) mod 256, swizzled
+  float W[NW][WGF];          // gathered position term of one 16-query group, per wave
 };
 
 // fp32 -> bf16 bits with the hardware conversion (round to nearest even)
 __device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+// two floats -> packed bf16 pair (low half = lo), one v_cvt_pk_bf16_f32
 __device__ inline uint32_t pack2(float lo, float hi) {
-  return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // 16-byte slot of chunk c in row r: c ^ swz(r)
@@ -127,7 +130,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const int split = k_on % nsplit;
   if (g >= groups) return;
   const int64_t b = g / a.H, hd = g % a.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address math
   const int g4 = lane >> 4, n16 = lane & 15;  // 16x16 MFMA lane coordinates
   const int d = (int)a.d;
   const int L = (int)a.L, len = (int)a.mem_len, T = len + L;
@@ -150,28 +154,45 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const uint16_t* vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
   const uint16_t* rb = (const uint16_t*)a.r + hd * a.r_sh;
   const int kv_st = (int)a.kv_st, r_sp = (int)a.r_sp;
-  int drow[2], dch[2];
+  int drow[2], dch[2], kvo[2], ro[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     drow[x] = 16 * wave + 8 * x + (lane >> 3);
     const int c = (lane & 7) ^ swz(drow[x]);
     dch[x] = 8 * (c < cl_max ? c : cl_max);  // chunks past d_load repeat a real one (times q = 0)
+    kvo[x] = drow[x] * kv_st + dch[x];       // this lane's element offset within a tile
+    ro[x] = drow[x] * r_sp + dch[x];
   }
+  // Interior tiles address from a uniform tile base plus the lane's fixed offset;
+  // rows past the ends are clamped (they feed masked scores only).
   auto load_kv = [&](const uint16_t* base, uint16_t* lds, int j0) {
+    if (j0 + BK <= T) {
+      const uint16_t* tb = base + j0 * kv_st;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;  // keys past T are masked
-      dma16(base + j * kv_st + dch[x], lds + (16 * wave + 8 * x) * DP);
+      for (int x = 0; x < 2; ++x) dma16(tb + kvo[x], lds + (16 * wave + 8 * x) * DP);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;
+        dma16(base + j * kv_st + dch[x], lds + (16 * wave + 8 * x) * DP);
+      }
     }
   };
   // r rows of relative distances e0 .. e0 + 63 (e = distance - mem_len, e0 % 64 == 0)
   auto load_r = [&](int e0) {
-    const int ring0 = ((e0 % RRING) + RRING) % RRING;
+    uint16_t* dst = sm.R + ((e0 & (RRING - 1)) + 16 * wave) * DP;
+    const int dist0 = len + e0;
+    if (dist0 >= 0 && dist0 + BK <= T) {
+      const uint16_t* tb = rb + dist0 * r_sp;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      int dist = len + e0 + drow[x];
-      dist = dist < 0 ? 0 : (dist < T ? dist : T - 1);  // out-of-range distances feed masked scores only
-      dma16(rb + dist * r_sp + dch[x], sm.R + (ring0 + 16 * wave + 8 * x) * DP);
+      for (int x = 0; x < 2; ++x) dma16(tb + ro[x], dst + 8 * x * DP);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        int dist = dist0 + drow[x];
+        dist = dist < 0 ? 0 : (dist < T ? dist : T - 1);
+        dma16(rb + dist * r_sp + dch[x], dst + 8 * x * DP);
+      }
     }
   };
 
@@ -191,14 +212,16 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
       voff[db] = vrow * DP + 8 * ((piece >> 1) ^ swz(vrow)) + 4 * (piece & 1);
     }
   }
-  // Gathered position term S_p[query n][key jj] at wbuf[gm][n * WP + jj]: lane
-  // (g4, n16) holds window rows 16 bw + 4 g4 + e of query n16 (row rho = distance
-  // offset 15 - n16 + jj) and stores them at skoff + 16 bw + e.
-  float* wbuf[2] = {sm.W[wave][0], sm.W[wave][1]};
-  const int skoff = n16 * (WP + 1) + 4 * g4 - 15;
+  // Gathered position term S_p[query n][key jj] of one 16-query group: row n of
+  // 64 floats, 16-byte chunk c of it in slot c ^ (n % 8) (conflict-free 16-byte
+  // reads).  Lane (g4, n16) holds window rows 16 bw + 4 g4 + e of query n16,
+  // window row rho being the distance of key jj = rho - 15 + n16.
+  float* const wbuf = sm.W[wave];
+  const int wsw = n16 & 7;
+  auto sp_slot = [&](int jj) { return n16 * 64 + (((jj >> 2) ^ wsw) << 2) + (jj & 3); };
   // r fragments: union block u (0..5) of the wave's 96 window rows, row rho =
   // n16 is relative distance i0w - j0 + 31 - 16 u - n16, stored at ring row
-  // (that) mod 192; roff[u] is its s = 0 offset, s = 1 is roff[u] ^ 32.
+  // (that) mod 256; roff[u] is its s = 0 offset, s = 1 is roff[u] ^ 32.
   int roff[6];
 
   // ---- this lane's queries, pre-scaled: group gm holds query i0w + 16 gm + n16,
@@ -242,12 +265,23 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
     }
   }
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  f32x4 acc[2][4];
+  // Softmax state per query: the reference s_off that the position product
+  // subtracts from every score through its accumulator's initial value (so the
+  // scores arrive as S - s_off and P = exp2 of them), and lim, how far above
+  // s_off a score may go before the reference moves: -inf until the query has
+  // seen a key, then TAU.  The reference is a maximum of the scores seen when it
+  // was set, so P stays below 2^TAU and moves are rare.  acc_l accumulates the
+  // row sums of P with the matrix core (a ones operand).
+  constexpr float TAU = 8.f;
+  float s_off[2] = {0.f, 0.f}, lim[2] = {-INFINITY, -INFINITY};
+  f32x4 acc[2][4], acc_l[2];
 #pragma unroll
-  for (int gm = 0; gm < 2; ++gm)
+  for (int gm = 0; gm < 2; ++gm) {
+    acc_l[gm] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[gm][db] = {0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
   float* srow_base = nullptr;
   if (a.scores) srow_base = a.scores + ((b * a.H + hd) * a.L) * (int64_t)T;
@@ -255,35 +289,40 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   // ---- first tile: K, V and the three r blocks of its window -----------------------------
   if (kt_lo < kt_hi) {
     const int j0 = kt_lo * BK;
-    load_kv(kb, sm.K, j0);
-    load_kv(vb, sm.V, j0);
+    load_kv(kb, sm.K[kt_lo & 1], j0);
+    load_kv(vb, sm.V[kt_lo & 1], j0);
 #pragma unroll
     for (int blk = 0; blk < 3; ++blk) load_r(q0 - j0 - BK + BK * blk);
     // ring offsets of the union blocks for this tile
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
       const int e = i0w - j0 + 31 - 16 * u - n16;
-      const int rr = ((e % RRING) + RRING) % RRING;
+      const int rr = e & (RRING - 1);
       roff[u] = rr * DP + 8 * (g4 ^ swz(rr));
     }
   }
 
-  // Per tile: [own loads of K, r landed] barrier A -> load V -> position, content
-  //   -> [V landed] barrier B -> load next K and r block -> softmax, P.V.
-  // K is overwritten only after barrier B (every wave is past its content
-  // product), the r block the next tile drops likewise, V only after the next
-  // barrier A (every wave is past its P.V).
+  // One barrier per tile.  At the top of tile kt every wave has waited for its
+  // own loads of tile kt, and the barrier makes them visible and retires tile
+  // kt - 1 in every wave; then tile kt + 1's K and V go to the other buffers and
+  // its new r block to the ring slot only tile kt - 1 used, so the loads run a
+  // whole tile ahead of their use.
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     const int j0 = kt * BK;
     wait_dma();
     barrier();
-    if (kt != kt_lo) load_kv(vb, sm.V, j0);
+    if (kt + 1 < kt_hi) {
+      load_kv(kb, sm.K[(kt + 1) & 1], j0 + BK);
+      load_kv(vb, sm.V[(kt + 1) & 1], j0 + BK);
+      load_r(q0 - j0 - 2 * BK);  // the block the next tile adds
+    }
+    const uint16_t* Kt = sm.K[kt & 1];
+    const uint16_t* Vt = sm.V[kt & 1];
     const bool work = kt <= kt_w;
     const int Dw = len + i0w - j0;  // distance of (query i0w, key j0)
     f32x4 sc[2][4];
     if (work) {
-      // ---- position term: W^T[gm] block bw = union block bw + 1 - gm.  All r
-      //      and K fragments are read first, so their LDS latency overlaps.
+      // ---- r and K fragments first, so their LDS latency overlaps ---------------------
       bf16x8 rf[6][2], kf[4][2];
 #pragma unroll
       for (int u = 0; u < 6; ++u) {
@@ -293,55 +332,44 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 #pragma unroll
       for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) kf[kbk][s] = lds_b128(sm.K + kbk * 16 * DP + koff[s]);
-      f32x4 wv[2][5];
+        for (int s = 0; s < 2; ++s) kf[kbk][s] = lds_b128(Kt + kbk * 16 * DP + koff[s]);
 #pragma unroll
-      for (int bw = 0; bw < 5; ++bw)
+      for (int gm = 0; gm < 2; ++gm) {
+        // ---- position term: W^T[gm] block bw = union block bw + 1 - gm ------------------
+        f32x4 wv[5];
 #pragma unroll
-        for (int gm = 0; gm < 2; ++gm) {
+        for (int bw = 0; bw < 5; ++bw) {
           const int u = bw + 1 - gm;
-          f32x4 w = {0.f, 0.f, 0.f, 0.f};
+          f32x4 w = {-s_off[gm], -s_off[gm], -s_off[gm], -s_off[gm]};
           w = mfma(rf[u][0], qp[gm][0], w);
-          wv[gm][bw] = mfma(rf[u][1], qp[gm][1], w);
+          wv[bw] = mfma(rf[u][1], qp[gm][1], w);
         }
-      // The diagonal shift happens at the store: value (gm, bw, e) of lane (g4, n16)
-      // is window row 16 bw + 4 g4 + e of query n16, the distance of key
-      // 16 bw + 4 g4 + e - 15 + n16, and is stored in that key's slot of row n16
-      // (rows of keys 0..63 only), so the reads below are aligned 16-byte loads.
+        // The diagonal shift happens at the store: value (bw, e) is window row
+        // 16 bw + 4 g4 + e of query n16 and goes to key 16 bw + 4 g4 + e - 15 + n16
+        // (keys 0..63 only).  The buffer is reused by the next group: LDS
+        // operations of one wave complete in order, so this group's stores follow
+        // the previous group's reads.
 #pragma unroll
-      for (int bw = 0; bw < 5; ++bw)
-#pragma unroll
-        for (int gm = 0; gm < 2; ++gm)
+        for (int bw = 0; bw < 5; ++bw)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool keep = bw == 0 ? (4 * g4 + e >= 15 - n16)
                                       : (bw == 4 ? (64 + 4 * g4 + e <= 78 - n16) : true);
-            if (keep) wbuf[gm][skoff + 16 * bw + e] = wv[gm][bw][e];
+            if (keep) wbuf[sp_slot(16 * bw + 4 * g4 + e - 15 + n16)] = wv[bw][e];
           }
-      // the window reads below are this wave's own stores
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // ---- content term on top of the gathered position term --------------------------
-#pragma unroll
-      for (int gm = 0; gm < 2; ++gm)
+        // ---- content term on top of the gathered position term ------------------------
 #pragma unroll
         for (int kbk = 0; kbk < 4; ++kbk) {
-          f32x4 c = *(const f32x4*)(wbuf[gm] + n16 * WP + 16 * kbk + 4 * g4);
+          f32x4 c = *(const f32x4*)(wbuf + n16 * 64 + (((4 * kbk + g4) ^ wsw) << 2));
           c = mfma(kf[kbk][0], qc[gm][0], c);
           c = mfma(kf[kbk][1], qc[gm][1], c);
           sc[gm][kbk] = c;
         }
-    }
-    wait_dma();
-    barrier();
-    if (kt + 1 < kt_hi) {
-      load_kv(kb, sm.K, j0 + BK);
-      load_r(q0 - j0 - 2 * BK);  // the block the next tile adds
+      }
     }
     // the next tile's union blocks sit one ring block lower
 #pragma unroll
-    for (int u = 0; u < 6; ++u) roff[u] = roff[u] >= BK * DP ? roff[u] - BK * DP : roff[u] + 2 * BK * DP;
+    for (int u = 0; u < 6; ++u) roff[u] = (roff[u] - BK * DP) & (RRING * DP - 1);
     if (!work) continue;
 
     // ---- causal mask (tiles that reach past the wave's first query only) --------------
@@ -367,46 +395,56 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int j = j0 + 16 * kbk + 4 * g4 + e;
-              if (j < T) srow[j] = sc[gm][kbk][e] * (1.0f / LOG2E);
+              if (j < T) srow[j] = (sc[gm][kbk][e] + s_off[gm]) * (1.0f / LOG2E);
             }
         }
       }
     }
 
     // ---- online softmax (exp2 domain); query n16 of group gm lives in lanes
-    //      n16 + 16 g4, g4 = 0..3 ------------------------------------------------------
+    //      n16 + 16 g4, g4 = 0..3.  The scores are S - s_off.  While none exceeds
+    //      its query's limit (the common case after the first tile) P = exp2 of
+    //      them as they are; otherwise the queries over their limit move s_off to
+    //      their new maximum and rescale what they have accumulated. ---------------
+    float lmax[2];
+#pragma unroll
+    for (int gm = 0; gm < 2; ++gm) {
+      lmax[gm] = -INFINITY;
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lmax[gm] = fmaxf(lmax[gm], sc[gm][kbk][e]);
+    }
+    if (__any(lmax[0] > lim[0] || lmax[1] > lim[1])) {
+#pragma unroll
+      for (int gm = 0; gm < 2; ++gm) {
+        const float tmax = max4(lmax[gm]);  // this query's largest S - s_off in the tile
+        const bool move = tmax > lim[gm];
+        const float delta = move ? tmax : 0.f;
+        // rescale by 2^(old reference - new one); nothing is accumulated yet
+        // while lim is -inf, and the factor is finite either way
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+        for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[gm][kbk][e] -= delta;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc_l[gm][e] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) acc[gm][db][e] *= alpha;
+        }
+        s_off[gm] += delta;
+        if (move) lim[gm] = TAU;
+      }
+    }
     bf16x8 pb[2][2];
 #pragma unroll
     for (int gm = 0; gm < 2; ++gm) {
-      float tmax = -INFINITY;
 #pragma unroll
       for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[gm][kbk][e]);
-      tmax = max4(tmax);
-      const float m_new = fmaxf(m_run[gm], tmax);
-      // a split's tiles can hide every key of a query so far: keep the max at
-      // -inf then, with zero weights and no NaN from (-inf) - (-inf)
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[gm] - m_use);
-      m_run[gm] = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int kbk = 0; kbk < 4; ++kbk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sc[gm][kbk][e] - m_use);
-          sc[gm][kbk][e] = p;
-          psum += p;
-        }
-      l_run[gm] = l_run[gm] * alpha + psum;
-      // the running max rarely moves after the first tiles: rescale only if it did
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[gm][db][e] *= alpha;
-      }
+        for (int e = 0; e < 4; ++e) sc[gm][kbk][e] = __builtin_amdgcn_exp2f(sc[gm][kbk][e]);
       // P^T operand of key half h: k index 8 g4 + 4 kb' + e <-> key 32 h + 16 kb' + 4 g4 + e
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -427,11 +465,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
       bf16x8 vf[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        vf[db] = lds_tr2(sm.V + (32 * h) * DP + voff[db], sm.V + (32 * h + 16) * DP + voff[db]);
+        vf[db] = lds_tr2(Vt + (32 * h) * DP + voff[db], Vt + (32 * h + 16) * DP + voff[db]);
 #pragma unroll
-      for (int gm = 0; gm < 2; ++gm)
+      for (int gm = 0; gm < 2; ++gm) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc[gm][db] = mfma(vf[db], pb[gm][h], acc[gm][db]);
+        acc_l[gm] = mfma(ones, pb[gm][h], acc_l[gm]);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   }
@@ -441,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   if (!wave_has_rows) return;
 #pragma unroll
   for (int gm = 0; gm < 2; ++gm) {
-    const float l_tot = sum4(l_run[gm]);
+    const float l_tot = acc_l[gm][0];
     const int i = i0w + 16 * gm + n16;
     if (i >= L) continue;
     if (nsplit > 1) {
@@ -451,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 #pragma unroll
       for (int db = 0; db < 4; ++db) *(f32x4*)(pa + 16 * db + 4 * g4) = acc[gm][db];
       if (g4 == 0) {
-        a.part_ml[2 * row] = m_run[gm];
+        a.part_ml[2 * row] = lim[gm] == -INFINITY ? -INFINITY : s_off[gm];
         a.part_ml[2 * row + 1] = l_tot;
       }
       continue;

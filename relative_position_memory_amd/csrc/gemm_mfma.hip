@@ -47,9 +47,11 @@ __device__ inline uint4 keep_if(uint4 v, bool keep) {
   return make_uint4(v.x & k, v.y & k, v.z & k, v.w & k);
 }
 
+// two floats -> packed bf16 pair (low half = lo), one v_cvt_pk_bf16_f32
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Output row rho = 8 q + 4 h + t of a 32 x 32 MFMA block (q = register group,
