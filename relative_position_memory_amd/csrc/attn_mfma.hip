@@ -27,8 +27,8 @@
 // no register staging).  r lives in a ring of four 64-distance blocks indexed
 // by (distance - mem_len) mod 256: successive key tiles move the window by one
 // block, so each tile loads only 64 new r rows.  Every 128-byte row stores its
-// 16-byte chunk c in slot c ^ ((row >> 1) & 7), which keeps the fragment reads
-// free of bank conflicts.
+// 16-byte chunk c in slot c ^ ((row >> 1) & 7) (V: c ^ (row & 6)), which keeps
+// the fragment reads free of bank conflicts.
 //
 // The scale 1/sqrt(d) and log2(e) are folded into (q+u) and (q+v) before they
 // are rounded to bf16, so the softmax is exp2(S - max) with no extra multiply.
@@ -68,8 +68,14 @@ __device__ inline uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// 16-byte slot of chunk c in row r: c ^ swz(r)
+// The LDS has 64 banks of 4 bytes; a 128-byte row covers half of them.
+// 16-byte slot of chunk c in row r of K and r: c ^ swz(r) (16 consecutive rows
+// read at one chunk hit 16 distinct 16-byte bank groups).
 __device__ inline int swz(int r) { return (r >> 1) & 7; }
+// V: c ^ swzv(r).  A transposing read of 8 rows x 4 eight-byte pieces (two
+// chunks) is conflict-free when the rows of one parity use four different
+// chunk pairs.
+__device__ inline int swzv(int r) { return r & 6; }
 
 __device__ inline void dma16(const uint16_t* src, uint16_t* lds) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -154,27 +160,31 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const uint16_t* vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
   const uint16_t* rb = (const uint16_t*)a.r + hd * a.r_sh;
   const int kv_st = (int)a.kv_st, r_sp = (int)a.r_sp;
-  int drow[2], dch[2], kvo[2], ro[2];
+  int drow[2], dch[2], dchv[2], ko[2], vo[2], ro[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     drow[x] = 16 * wave + 8 * x + (lane >> 3);
-    const int c = (lane & 7) ^ swz(drow[x]);
-    dch[x] = 8 * (c < cl_max ? c : cl_max);  // chunks past d_load repeat a real one (times q = 0)
-    kvo[x] = drow[x] * kv_st + dch[x];       // this lane's element offset within a tile
+    // chunks past d_load repeat a real one (times q = 0)
+    const int c = (lane & 7) ^ swz(drow[x]), cv = (lane & 7) ^ swzv(drow[x]);
+    dch[x] = 8 * (c < cl_max ? c : cl_max);
+    dchv[x] = 8 * (cv < cl_max ? cv : cl_max);
+    ko[x] = drow[x] * kv_st + dch[x];  // this lane's element offsets within a tile
+    vo[x] = drow[x] * kv_st + dchv[x];
     ro[x] = drow[x] * r_sp + dch[x];
   }
   // Interior tiles address from a uniform tile base plus the lane's fixed offset;
   // rows past the ends are clamped (they feed masked scores only).
-  auto load_kv = [&](const uint16_t* base, uint16_t* lds, int j0) {
+  auto load_kv = [&](const uint16_t* base, uint16_t* lds, int j0, const int (&off)[2],
+                     const int (&ch)[2]) {
     if (j0 + BK <= T) {
       const uint16_t* tb = base + j0 * kv_st;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) dma16(tb + kvo[x], lds + (16 * wave + 8 * x) * DP);
+      for (int x = 0; x < 2; ++x) dma16(tb + off[x], lds + (16 * wave + 8 * x) * DP);
     } else {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;
-        dma16(base + j * kv_st + dch[x], lds + (16 * wave + 8 * x) * DP);
+        dma16(base + j * kv_st + ch[x], lds + (16 * wave + 8 * x) * DP);
       }
     }
   };
@@ -209,16 +219,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int piece = 4 * db + (n16 & 3);  // 8-byte piece of the row
-      voff[db] = vrow * DP + 8 * ((piece >> 1) ^ swz(vrow)) + 4 * (piece & 1);
+      voff[db] = vrow * DP + 8 * ((piece >> 1) ^ swzv(vrow)) + 4 * (piece & 1);
     }
   }
   // Gathered position term S_p[query n][key jj] of one 16-query group: row n of
-  // 64 floats, 16-byte chunk c of it in slot c ^ (n % 8) (conflict-free 16-byte
-  // reads).  Lane (g4, n16) holds window rows 16 bw + 4 g4 + e of query n16,
-  // window row rho being the distance of key jj = rho - 15 + n16.
+  // 64 floats, 16-byte chunk c of it in slot (c + 4 n + 3 (n / 4)) % 16.  Both
+  // the 16-byte reads (16 queries at one chunk) and the 4-byte stores (64 lanes,
+  // 64 distinct banks for every (bw, e)) are then free of bank conflicts.  Lane
+  // (g4, n16) holds window rows 16 bw + 4 g4 + e of query n16, window row rho
+  // being the distance of key jj = rho - 15 + n16.
   float* const wbuf = sm.W[wave];
-  const int wsw = n16 & 7;
-  auto sp_slot = [&](int jj) { return n16 * 64 + (((jj >> 2) ^ wsw) << 2) + (jj & 3); };
+  const int sprot = 4 * n16 + 3 * (n16 >> 2);
+  auto sp_slot = [&](int jj) { return n16 * 64 + ((((jj >> 2) + sprot) & 15) << 2) + (jj & 3); };
   // r fragments: union block u (0..5) of the wave's 96 window rows, row rho =
   // n16 is relative distance i0w - j0 + 31 - 16 u - n16, stored at ring row
   // (that) mod 256; roff[u] is its s = 0 offset, s = 1 is roff[u] ^ 32.
@@ -289,8 +301,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   // ---- first tile: K, V and the three r blocks of its window -----------------------------
   if (kt_lo < kt_hi) {
     const int j0 = kt_lo * BK;
-    load_kv(kb, sm.K[kt_lo & 1], j0);
-    load_kv(vb, sm.V[kt_lo & 1], j0);
+    load_kv(kb, sm.K[kt_lo & 1], j0, ko, dch);
+    load_kv(vb, sm.V[kt_lo & 1], j0, vo, dchv);
 #pragma unroll
     for (int blk = 0; blk < 3; ++blk) load_r(q0 - j0 - BK + BK * blk);
     // ring offsets of the union blocks for this tile
@@ -312,8 +324,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
     wait_dma();
     barrier();
     if (kt + 1 < kt_hi) {
-      load_kv(kb, sm.K[(kt + 1) & 1], j0 + BK);
-      load_kv(vb, sm.V[(kt + 1) & 1], j0 + BK);
+      load_kv(kb, sm.K[(kt + 1) & 1], j0 + BK, ko, dch);
+      load_kv(vb, sm.V[(kt + 1) & 1], j0 + BK, vo, dchv);
       load_r(q0 - j0 - 2 * BK);  // the block the next tile adds
     }
     const uint16_t* Kt = sm.K[kt & 1];
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
         // ---- content term on top of the gathered position term ------------------------
 #pragma unroll
         for (int kbk = 0; kbk < 4; ++kbk) {
-          f32x4 c = *(const f32x4*)(wbuf + n16 * 64 + (((4 * kbk + g4) ^ wsw) << 2));
+          f32x4 c = *(const f32x4*)(wbuf + n16 * 64 + (((4 * kbk + g4 + sprot) & 15) << 2));
           c = mfma(kf[kbk][0], qc[gm][0], c);
           c = mfma(kf[kbk][1], qc[gm][1], c);
           sc[gm][kbk] = c;
