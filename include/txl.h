@@ -211,6 +211,71 @@ int txl_layer_workspace_map(const txl_layer_dims* dims, int64_t mem_len, int dty
 int txl_mem_update(void* stream, int dtype, txl_ring* mem, int64_t B, int64_t d_model,
                    const void* h_new, int64_t L);
 
+/*
+ * ---- Evaluation with cached keys and values ---------------------------------------------
+ * At evaluation the weights are fixed, so the projected keys and values of a
+ * memory row (section 3.2's cached hidden states, projected by W_kE and W_v as in
+ * section 3.3) and the projected encodings r = R W_kR^T do not change once
+ * computed.  This path keeps the projected k and v of the memory rows in a ring
+ * per layer and projects only the L new rows of each segment; r is projected
+ * once (txl_pos_proj).  The result equals txl_layer_step over the hidden-state
+ * memory up to rounding.  L = 1 is the per-token (decode) shape.
+ *
+ * A layer's key/value ring:
+ *   k, v       device [B][H][capacity][d_pad] each, d_pad = d_head rounded up to 8;
+ *              txl_kv_ring_bytes() bytes each.  Memory row t (0 = oldest) of batch
+ *              row b, head h sits at row (start + t) % capacity.  Contents need no
+ *              initialisation (rows are written before they are read).
+ *   capacity   >= mem_max + L of every call (the new rows are appended behind the
+ *              memory before the oldest ones are dropped).
+ *   start      0 <= start < capacity.
+ *   len        memory rows, 0 <= len <= mem_max (0 = empty memory).
+ *   mem_max    M: after a step the memory keeps the newest min(M, len + L) rows.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t capacity;
+  int64_t start;
+  int64_t len;
+  int64_t mem_max;
+} txl_kv_ring;
+
+/* Bytes of one of k, v of a ring of this capacity (0 for invalid arguments). */
+size_t txl_kv_ring_bytes(const txl_layer_dims* dims, int64_t capacity, int dtype);
+
+/*
+ * r = R[0 : R_rows] W_kR^T (section 3.3's W_{k,R} R_{i-j}; row p <-> distance p)
+ * into r_out [H][R_rows][d_pad] (padding columns written as zeros), dims->d_model
+ * columns of R and of W_kR.  Enqueued on `stream`.  r_out must not overlap R or
+ * W_kR.
+ */
+int txl_pos_proj(void* stream, int dtype, const txl_layer_dims* dims, const void* R,
+                 int64_t R_rows, const void* W_kR, void* r_out);
+
+/* Workspace bytes of txl_layer_step_kv for rings of this mem_max (0 if invalid). */
+size_t txl_layer_kv_workspace_bytes(const txl_layer_dims* dims, int64_t mem_max, int dtype);
+
+/*
+ * One layer for one segment with cached keys and values:
+ *   k, v of the L rows of h_in are projected into the ring behind its len memory
+ *   rows; q = h_in W_q^T; a = attention of q over the len + L keys (relative
+ *   distances through r); h_out = LayerNorm(a W_o^T + h_in) * gamma + beta.
+ *   Then the ring keeps the newest min(mem_max, len + L) rows: kv->start and
+ *   kv->len are updated on the host before the call returns (no data moves).
+ *   h_in     [B][L][D] dense.      h_out  [B][L][D] dense, must not alias h_in.
+ *   kv       this layer's ring (see above); w->W_kR is not used.
+ *   r        txl_pos_proj output [H][r_rows][d_pad]; r_rows >= kv->len + L.
+ *   workspace  >= txl_layer_kv_workspace_bytes(dims, kv->mem_max, dtype) bytes,
+ *            256-byte aligned.
+ * Errors as txl_layer_step; a failing call changes nothing.  Calls that share a
+ * ring or a workspace must be ordered (one stream).
+ */
+int txl_layer_step_kv(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                      txl_kv_ring* kv, const txl_layer_weights* w, const void* u_bias,
+                      const void* v_bias, const void* r, int64_t r_rows, void* h_out,
+                      void* workspace, size_t ws_bytes);
+
 /* Static text for a status, followed by the calling thread's detail of its last error. */
 const char* txl_status_string(int status);
 

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
     const int64_t j = j0 + lane;
     float s = -INFINITY;
     if (j < nvis) {
-      const T* kj = kb + j * a.kv_st;
+      const T* kj = kb + kv_row(a, j) * a.kv_st;
       const T* rp = rb + (a.mem_len + i - j) * a.r_sp;
       float acc = 0.f;
       for (int64_t c = 0; c < d; ++c)
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
     acc1 *= alpha;
     const int64_t nk = nvis - j0 < 64 ? nvis - j0 : 64;
     for (int64_t jj = 0; jj < nk; ++jj) {
-      const T* vj = vbase + (j0 + jj) * a.kv_st;
+      const T* vj = vbase + kv_row(a, j0 + jj) * a.kv_st;
       const float pj = pw[jj];
       if (lane < d) acc0 += pj * Elt<T>::load(vj + lane);
       if (lane + 64 < d) acc1 += pj * Elt<T>::load(vj + lane + 64);

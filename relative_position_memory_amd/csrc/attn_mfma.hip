@@ -174,17 +174,25 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   }
   // Interior tiles address from a uniform tile base plus the lane's fixed offset;
   // rows past the ends are clamped (they feed masked scores only).
+  // Keys may sit in a ring (row (kv_start + j) % kv_cap); without one the cap is
+  // past every key, so the row is j.
+  const int kvs = a.kv_cap > 0 ? (int)a.kv_start : 0;
+  const int kvc = a.kv_cap > 0 ? (int)a.kv_cap : 0x7fffffff - BK;
   auto load_kv = [&](const uint16_t* base, uint16_t* lds, int j0, const int (&off)[2],
                      const int (&ch)[2]) {
-    if (j0 + BK <= T) {
-      const uint16_t* tb = base + j0 * kv_st;
+    int p0 = kvs + j0;
+    p0 = p0 >= kvc ? p0 - kvc : p0;
+    if (j0 + BK <= T && p0 + BK <= kvc) {
+      const uint16_t* tb = base + p0 * kv_st;
 #pragma unroll
       for (int x = 0; x < 2; ++x) dma16(tb + off[x], lds + (16 * wave + 8 * x) * DP);
     } else {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;
-        dma16(base + j * kv_st + ch[x], lds + (16 * wave + 8 * x) * DP);
+        int p = kvs + j;
+        p = p >= kvc ? p - kvc : p;
+        dma16(base + p * kv_st + ch[x], lds + (16 * wave + 8 * x) * DP);
       }
     }
   };
@@ -578,7 +586,9 @@ bool attn_mfma_supported(const AttnArgs& a) {
   if (a.d > DP || a.d_load % 8 != 0 || a.d_load > DP) return false;
   if (a.mem_len + a.L > 0x7fffffffLL - 2 * BQ) return false;
   // 32-bit element offsets inside a (batch, head) slab
-  if ((a.mem_len + a.L) * (a.kv_st > a.r_sp ? a.kv_st : a.r_sp) > 0x7fffffffLL) return false;
+  const int64_t krows = a.kv_cap > 0 ? a.kv_cap : a.mem_len + a.L;
+  if (krows * a.kv_st > 0x7fffffffLL || (a.mem_len + a.L) * a.r_sp > 0x7fffffffLL) return false;
+  if (a.kv_cap > 0x7fffffffLL - 2 * BK) return false;
   const uintptr_t al = (uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.r;
   if (al % 16) return false;
   const int64_t st[] = {a.q_sb, a.q_st, a.q_sh, a.kv_sb, a.kv_st, a.kv_sh, a.r_sp, a.r_sh};

@@ -30,13 +30,23 @@ __device__ inline T* heads_dst(const GemmArgs& g, int64_t m, int64_t n) {
   const int64_t which = n / e.HD, nn = n - which * e.HD;
   const int64_t head = nn / e.d, c = nn - head * e.d;
   T* base = (T*)(which ? e.dst1 : e.dst0);
-  return base + b * e.sb + head * e.sh + t * e.st + c;
+  return base + b * e.sb + head * e.sh + ring_t(e, t) * e.st + c;
+}
+
+// Stores element (m, n) of a head-major output; the store of a head's last
+// element also clears the row's padding.
+template <typename T>
+__device__ inline void heads_store(const GemmArgs& g, int64_t m, int64_t n, float acc) {
+  T* p = heads_dst<T>(g, m, n);
+  Elt<T>::store(p, acc);
+  if (g.e.pad > g.e.d && (n % g.e.HD) % g.e.d == g.e.d - 1)
+    for (int64_t c = 1; c < g.e.pad - g.e.d + 1; ++c) Elt<T>::store(p + c, 0.f);
 }
 
 template <typename T>
 __device__ inline void epilogue_store(const GemmArgs& g, int64_t m, int64_t n, float acc) {
   if (g.e.mode == EPI_HEADS) {
-    Elt<T>::store(heads_dst<T>(g, m, n), acc);
+    heads_store<T>(g, m, n, acc);
   } else {
     const T* res = (const T*)g.e.resid + m * g.N + n;
     g.e.y[m * g.N + n] = acc + Elt<T>::load(res);

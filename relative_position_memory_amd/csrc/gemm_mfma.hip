@@ -182,7 +182,8 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
     for (int row = row0; row < C::BM; row += STEP) {
       if (m0 + row >= g.M) break;
       if (n < g.N)
-        *(uint4*)(colbase + b * g.e.sb + t * g.e.st) = *(const uint4*)(es + row * EP + 8 * c);
+        *(uint4*)(colbase + b * g.e.sb + ring_t(g.e, t) * g.e.st) =
+            *(const uint4*)(es + row * EP + 8 * c);
       t += STEP;
       while (t >= per) { t -= per; ++b; }
     }
@@ -231,7 +232,7 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
           if (n >= g.N) continue;
           const float v = acc[j][i][e];
           if (g.e.mode == EPI_HEADS) {
-            *heads_dst<uint16_t>(g, m, n) = __builtin_bit_cast(uint16_t, (__bf16)v);
+            heads_store<uint16_t>(g, m, n, v);
           } else {
             g.e.y[m * g.N + n] = v + bf16_to_f32(((const uint16_t*)g.e.resid)[m * g.N + n]);
           }

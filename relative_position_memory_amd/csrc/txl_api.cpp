@@ -186,6 +186,34 @@ int run_attn(int dtype, txl::AttnArgs a, void* scratch, size_t scratch_bytes, hi
   return TXL_OK;
 }
 
+int run_gemm(int dtype, const txl::GemmArgs& g, hipStream_t st, const char* what);
+
+// h_out = LayerNorm(a W_o^T + h_in) * gamma + beta (section 3.3), a [B*L][H*d]
+// token-major; y: fp32 [B*L][D] scratch for the unfused form.
+int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
+               const void* h_in, void* h_out, float* y, hipStream_t st) {
+  const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
+  // one fused kernel when the rows fit it
+  txl::LnArgs ln{BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
+  if (dtype == TXL_BF16 && txl::gemm_ln_supported(ln)) {
+    const hipError_t e = txl::launch_gemm_ln(ln, st);
+    if (e != hipSuccess) return hip_fail(e, "output projection + LayerNorm");
+    return TXL_OK;
+  }
+  // y = a W_o^T + h, then LayerNorm
+  txl::GemmArgs g{};
+  g.M = BL; g.N = D; g.K = HD;
+  g.a = {nullptr, 1, 0, 0, a, BL, HD};
+  g.w = {w->W_o, w->W_o, D, HD};
+  g.e = {txl::EPI_RESID_F32, nullptr, nullptr, 0, 1, 0, 0, 0, y, h_in};
+  int rc;
+  if ((rc = run_gemm(dtype, g, st, "output projection")) != TXL_OK) return rc;
+  const hipError_t e =
+      txl::launch_layer_norm(dtype, y, w->ln_gamma, w->ln_beta, dm.ln_eps, BL, D, h_out, st);
+  if (e != hipSuccess) return hip_fail(e, "layer norm");
+  return TXL_OK;
+}
+
 int run_gemm(int dtype, const txl::GemmArgs& g, hipStream_t st, const char* what) {
   if (g.M == 0 || g.N == 0) return TXL_OK;
   hipError_t e;
@@ -195,6 +223,26 @@ int run_gemm(int dtype, const txl::GemmArgs& g, hipStream_t st, const char* what
     e = txl::launch_gemm_generic(dtype, g, st);
   if (e != hipSuccess) return hip_fail(e, what);
   return TXL_OK;
+}
+
+// Workspace of txl_layer_step_kv: q [B][H][L][dp], a [B][L][H*d], y fp32
+// [B][L][D], then the attention's scratch.
+struct KvWs { size_t q, a, y, part, total; int64_t dp; };
+KvWs kv_ws_layout(const txl_layer_dims& dm, int64_t es, size_t part_bytes) {
+  KvWs w;
+  w.dp = round_up(dm.d_head, 8);
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up(bytes, 256);
+    return o;
+  };
+  w.q = take(dm.B * dm.n_head * dm.L * w.dp * es);
+  w.a = take(dm.B * dm.L * dm.n_head * dm.d_head * es);
+  w.y = take(dm.B * dm.L * dm.d_model * 4);
+  w.part = take((int64_t)part_bytes);
+  w.total = off;
+  return w;
 }
 
 }  // namespace
@@ -352,19 +400,19 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
   gkv.M = B * T; gkv.N = 2 * HD; gkv.K = D;
   gkv.a = {mem->data, mem->capacity, mem->start, len, h_in, L, D};
   gkv.w = {w->W_kE, w->W_v, HD, D};
-  gkv.e = {txl::EPI_HEADS, k, v, HD, d, H * T * dp, T * dp, dp, nullptr, nullptr};
+  gkv.e = {txl::EPI_HEADS, k, v, HD, d, H * T * dp, T * dp, dp, nullptr, nullptr, 0, 0, dp};
   // q from the current rows only
   txl::GemmArgs& gq = proj[1];
   gq.M = B * L; gq.N = HD; gq.K = D;
   gq.a = {nullptr, 1, 0, 0, h_in, L, D};
   gq.w = {w->W_q, w->W_q, HD, D};
-  gq.e = {txl::EPI_HEADS, q, q, HD, d, H * L * dp, L * dp, dp, nullptr, nullptr};
+  gq.e = {txl::EPI_HEADS, q, q, HD, d, H * L * dp, L * dp, dp, nullptr, nullptr, 0, 0, dp};
   // r = R[0:T] W_kR^T, shared by the whole batch
   txl::GemmArgs& gr = proj[2];
   gr.M = T; gr.N = HD; gr.K = D;
   gr.a = {nullptr, 1, 0, 0, R, T, D};
   gr.w = {w->W_kR, w->W_kR, HD, D};
-  gr.e = {txl::EPI_HEADS, r, r, HD, d, 0, T * dp, dp, nullptr, nullptr};
+  gr.e = {txl::EPI_HEADS, r, r, HD, d, 0, T * dp, dp, nullptr, nullptr, 0, 0, dp};
   if (dtype == TXL_BF16 && txl::gemm_mfma_supported(gkv) && txl::gemm_mfma_supported(gq) &&
       txl::gemm_mfma_supported(gr)) {
     // the three projections share K and run as one grid
@@ -375,7 +423,6 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
     if ((rc = run_gemm(dtype, gq, st, "q projection")) != TXL_OK) return rc;
     if ((rc = run_gemm(dtype, gr, st, "r projection")) != TXL_OK) return rc;
   }
-  txl::GemmArgs g{};
   // attention; output a [B, L, H*d] token-major for the output projection
   txl::AttnArgs at{};
   at.B = B; at.H = H; at.L = L; at.mem_len = len; at.d = d;
@@ -387,24 +434,7 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
   at.scores = nullptr;
   at.d_load = dp;  // workspace rows hold dp readable columns
   if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
-  // h_out = LayerNorm(a W_o^T + h): one fused kernel when the rows fit it
-  txl::LnArgs ln{B * L, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
-  if (dtype == TXL_BF16 && txl::gemm_ln_supported(ln)) {
-    const hipError_t e = txl::launch_gemm_ln(ln, st);
-    if (e != hipSuccess) return hip_fail(e, "output projection + LayerNorm");
-    return TXL_OK;
-  }
-  // y = a W_o^T + h, then LayerNorm
-  g = {};
-  g.M = B * L; g.N = D; g.K = HD;
-  g.a = {nullptr, 1, 0, 0, a, L, HD};
-  g.w = {w->W_o, w->W_o, D, HD};
-  g.e = {txl::EPI_RESID_F32, nullptr, nullptr, 0, 1, 0, 0, 0, y, h_in};
-  if ((rc = run_gemm(dtype, g, st, "output projection")) != TXL_OK) return rc;
-  hipError_t e = txl::launch_layer_norm(dtype, y, w->ln_gamma, w->ln_beta, dm.ln_eps, B * L, D,
-                                        h_out, st);
-  if (e != hipSuccess) return hip_fail(e, "layer norm");
-  return TXL_OK;
+  return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st);
 }
 
 int txl_mem_update(void* stream, int dtype, txl_ring* mem, int64_t B, int64_t d_model,
@@ -434,4 +464,136 @@ int txl_mem_update(void* stream, int dtype, txl_ring* mem, int64_t B, int64_t d_
   return TXL_OK;
 }
 
+// ---- evaluation with cached keys and values -----------------------------------------
+
+size_t txl_kv_ring_bytes(const txl_layer_dims* dims, int64_t capacity, int dtype) {
+  if (check_dims(dims) != TXL_OK || capacity < 1) return 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
+  return (size_t)(dims->B * dims->n_head * capacity * round_up(dims->d_head, 8) * elt_size(dtype));
+}
+
+int txl_pos_proj(void* stream, int dtype, const txl_layer_dims* dims, const void* R,
+                 int64_t R_rows, const void* W_kR, void* r_out) {
+  g_detail[0] = 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  const int rc = check_dims(dims);
+  if (rc != TXL_OK) return rc;
+  if (!R || !W_kR || !r_out) return fail(TXL_EINVAL, "NULL pointer");
+  if (R_rows < 1 || R_rows > 0x7fffffffLL) return fail(TXL_EINVAL, "R_rows must be in 1 .. 2^31-1");
+  const int64_t D = dims->d_model, H = dims->n_head, d = dims->d_head, HD = H * d;
+  const int64_t dp = round_up(d, 8), es = elt_size(dtype);
+  const Span so = {(uintptr_t)r_out, (uintptr_t)r_out + (uintptr_t)(H * R_rows * dp * es)};
+  const Span sR = {(uintptr_t)R, (uintptr_t)R + (uintptr_t)(R_rows * D * es)};
+  const Span sW = {(uintptr_t)W_kR, (uintptr_t)W_kR + (uintptr_t)(HD * D * es)};
+  if (overlap(so, sR) || overlap(so, sW)) return fail(TXL_EINVAL, "r_out overlaps an input");
+  txl::GemmArgs gr{};
+  gr.M = R_rows; gr.N = HD; gr.K = D;
+  gr.a = {nullptr, 1, 0, 0, R, R_rows, D};
+  gr.w = {W_kR, W_kR, HD, D};
+  gr.e = {txl::EPI_HEADS, r_out, r_out, HD, d, 0, R_rows * dp, dp, nullptr, nullptr, 0, 0, dp};
+  return run_gemm(dtype, gr, (hipStream_t)stream, "position projection");
+}
+
+
+size_t txl_layer_kv_workspace_bytes(const txl_layer_dims* dims, int64_t mem_max, int dtype) {
+  if (check_dims(dims) != TXL_OK || mem_max < 0) return 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
+  return kv_ws_layout(*dims, elt_size(dtype), layer_part_bytes(*dims, mem_max, dtype)).total;
+}
+
+int txl_layer_step_kv(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                      txl_kv_ring* kv, const txl_layer_weights* w, const void* u_bias,
+                      const void* v_bias, const void* r, int64_t r_rows, void* h_out,
+                      void* workspace, size_t ws_bytes) {
+  g_detail[0] = 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  int rc = check_dims(dims);
+  if (rc != TXL_OK) return rc;
+  if (!kv || !kv->k || !kv->v) return fail(TXL_EINVAL, "kv ring or its k / v is NULL");
+  const txl_layer_dims dm = *dims;
+  const int64_t B = dm.B, L = dm.L, D = dm.d_model, H = dm.n_head, d = dm.d_head, HD = H * d;
+  const int64_t C = kv->capacity, M = kv->mem_max, len = kv->len, T = len + L;
+  if (M < 0 || C < M + L || C > 0x7fffffffLL || kv->start < 0 || kv->start >= C || len < 0 ||
+      len > M)
+    return fail(TXL_EINVAL,
+                "kv ring state (capacity %lld, mem_max %lld, start %lld, len %lld) is invalid "
+                "for L = %lld (needs capacity >= mem_max + L, len <= mem_max)",
+                (long long)C, (long long)M, (long long)kv->start, (long long)len, (long long)L);
+  if (!w || !w->W_q || !w->W_kE || !w->W_v || !w->W_o || !w->ln_gamma || !w->ln_beta)
+    return fail(TXL_EINVAL, "NULL weight pointer");
+  if (!h_in || !h_out || !u_bias || !v_bias || !r) return fail(TXL_EINVAL, "NULL tensor pointer");
+  if (r_rows < T)
+    return fail(TXL_EINVAL, "r_rows %lld < kv->len + L = %lld", (long long)r_rows, (long long)T);
+  if (!workspace) return fail(TXL_EINVAL, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(TXL_EINVAL, "workspace is not 256-byte aligned");
+  const int64_t es = elt_size(dtype);
+  const KvWs ws = kv_ws_layout(dm, es, layer_part_bytes(dm, M, dtype));
+  if (ws_bytes < ws.total)
+    return fail(TXL_EWORKSPACE, "need %zu bytes, got %zu", ws.total, ws_bytes);
+  const int64_t dp = ws.dp;
+  const size_t ring_bytes = (size_t)(B * H * C * dp * es);
+  const Span sh_in = {(uintptr_t)h_in, (uintptr_t)h_in + (uintptr_t)(B * L * D * es)};
+  const Span sh_out = {(uintptr_t)h_out, (uintptr_t)h_out + (uintptr_t)(B * L * D * es)};
+  const Span sk = {(uintptr_t)kv->k, (uintptr_t)kv->k + ring_bytes};
+  const Span sv = {(uintptr_t)kv->v, (uintptr_t)kv->v + ring_bytes};
+  const Span sr = {(uintptr_t)r, (uintptr_t)r + (uintptr_t)(H * r_rows * dp * es)};
+  const Span sws = {(uintptr_t)workspace, (uintptr_t)workspace + ws_bytes};
+  if (overlap(sh_out, sh_in)) return fail(TXL_EINVAL, "h_out aliases h_in");
+  if (overlap(sk, sv)) return fail(TXL_EINVAL, "kv->k and kv->v overlap");
+  const Span outs[] = {sh_out, sk, sv, sws};
+  const Span ins[] = {sh_in, sr};
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (overlap(o, i)) return fail(TXL_EINVAL, "an output (h_out, k, v, workspace) overlaps an input");
+  if (overlap(sws, sh_out) || overlap(sws, sk) || overlap(sws, sv) || overlap(sh_out, sk) ||
+      overlap(sh_out, sv))
+    return fail(TXL_EINVAL, "h_out, the ring and the workspace must not overlap");
+
+  char* base = (char*)workspace;
+  void* q = base + ws.q;
+  void* a = base + ws.a;
+  float* y = (float*)(base + ws.y);
+  hipStream_t st = (hipStream_t)stream;
+
+  // k, v of the L new rows straight into the ring, after the len memory rows
+  txl::GemmArgs proj[2] = {};
+  txl::GemmArgs& gkv = proj[0];
+  gkv.M = B * L; gkv.N = 2 * HD; gkv.K = D;
+  gkv.a = {nullptr, 1, 0, 0, h_in, L, D};
+  gkv.w = {w->W_kE, w->W_v, HD, D};
+  gkv.e = {txl::EPI_HEADS, kv->k, kv->v, HD, d, H * C * dp, C * dp, dp, nullptr, nullptr,
+           (kv->start + len) % C, C, dp};
+  txl::GemmArgs& gq = proj[1];
+  gq.M = B * L; gq.N = HD; gq.K = D;
+  gq.a = {nullptr, 1, 0, 0, h_in, L, D};
+  gq.w = {w->W_q, w->W_q, HD, D};
+  gq.e = {txl::EPI_HEADS, q, q, HD, d, H * L * dp, L * dp, dp, nullptr, nullptr, 0, 0, dp};
+  if (dtype == TXL_BF16 && txl::gemm_mfma_supported(gkv) && txl::gemm_mfma_supported(gq)) {
+    const hipError_t e = txl::launch_gemm_mfma_multi(proj, 2, st, num_cus());
+    if (e != hipSuccess) return hip_fail(e, "q/kv projections");
+  } else {
+    if ((rc = run_gemm(dtype, gkv, st, "kv projection")) != TXL_OK) return rc;
+    if ((rc = run_gemm(dtype, gq, st, "q projection")) != TXL_OK) return rc;
+  }
+  // attention over the len memory keys and the L new ones, all in the ring
+  txl::AttnArgs at{};
+  at.B = B; at.H = H; at.L = L; at.mem_len = len; at.d = d;
+  at.q = q; at.q_sb = H * L * dp; at.q_st = dp; at.q_sh = L * dp;
+  at.k = kv->k; at.v = kv->v; at.kv_sb = H * C * dp; at.kv_st = dp; at.kv_sh = C * dp;
+  at.kv_start = kv->start; at.kv_cap = C;
+  at.r = r; at.r_sp = dp; at.r_sh = r_rows * dp;
+  at.u = u_bias; at.vb = v_bias; at.scale = 1.0f / sqrtf((float)d);
+  at.out = a; at.o_sb = L * HD; at.o_st = HD; at.o_sh = d;
+  at.scores = nullptr;
+  at.d_load = dp;  // ring, q and r rows hold dp readable columns (padding zeroed)
+  if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
+  if ((rc = run_out_ln(dtype, dm, a, w, h_in, h_out, y, st)) != TXL_OK) return rc;
+  // the memory keeps the newest min(M, len + L) rows: only the ring state moves
+  const int64_t new_len = T < M ? T : M;
+  kv->start = (kv->start + T - new_len) % C;
+  kv->len = new_len;
+  return TXL_OK;
+}
+
 }  // extern "C"
+

@@ -53,7 +53,17 @@ struct AttnArgs {
   int nsplit;
   float* part_acc;
   float* part_ml;
+  // Keys as a ring: when kv_cap > 0, key j (0 <= j < mem_len + L <= kv_cap) is
+  // row (kv_start + j) % kv_cap of k and v (0 <= kv_start < kv_cap).
+  int64_t kv_start, kv_cap;
 };
+
+// Row of key j in k / v (see AttnArgs::kv_start).
+__host__ __device__ inline int64_t kv_row(const AttnArgs& a, int64_t j) {
+  if (a.kv_cap <= 0) return j;
+  const int64_t p = a.kv_start + j;
+  return p >= a.kv_cap ? p - a.kv_cap : p;
+}
 
 // Number of key splits the matrix-core attention would use for these shapes on
 // a device with num_cus CUs (1 = no split), and the partials' bytes it needs.
@@ -91,7 +101,19 @@ struct Epilogue {
   void* dst0; void* dst1; int64_t HD, d, sb, sh, st;
   // EPI_RESID_F32: y[m][n] = acc + resid[m][n]  (y fp32 [M][N], resid dtype [M][N]).
   float* y; const void* resid;
+  // EPI_HEADS into a ring: when t_mod > 0, row t is stored at (t_off + t) % t_mod
+  // (0 <= t_off < t_mod, t < t_mod).
+  int64_t t_off, t_mod;
+  // EPI_HEADS rows padded past d: when pad > d, elements d .. pad-1 of every
+  // head row are written as zeros (readers may load whole padded rows).
+  int64_t pad;
 };
+
+__host__ __device__ inline int64_t ring_t(const Epilogue& e, int64_t t) {
+  if (e.t_mod <= 0) return t;
+  const int64_t p = e.t_off + t;
+  return p >= e.t_mod ? p - e.t_mod : p;
+}
 
 struct GemmArgs {
   int64_t M, N, K;

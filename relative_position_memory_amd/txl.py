@@ -200,3 +200,69 @@ def workspace_views(dims, mem_len, workspace, dtype):
     r = view(mp.r, (H, T, dp))[..., :d].permute(1, 0, 2)
     a = view(mp.a, (B, L, H, d))
     return {"q": q, "k": k, "v": v, "r": r, "a": a}
+
+
+# ---- evaluation with cached keys and values ----------------------------------------------
+
+class KVRing(ctypes.Structure):
+    """txl_kv_ring: projected k and v of the memory rows, [B, H, capacity, d_pad] each."""
+    _fields_ = [("k", _p), ("v", _p), ("capacity", _i64), ("start", _i64), ("len", _i64),
+                ("mem_max", _i64)]
+
+
+_lib.txl_kv_ring_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int]
+_lib.txl_kv_ring_bytes.restype = _sz
+_lib.txl_pos_proj.argtypes = [_p, ctypes.c_int, ctypes.POINTER(LayerDims), _p, _i64, _p, _p]
+_lib.txl_pos_proj.restype = ctypes.c_int
+_lib.txl_layer_kv_workspace_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int]
+_lib.txl_layer_kv_workspace_bytes.restype = _sz
+_lib.txl_layer_step_kv.argtypes = [_p, ctypes.c_int, ctypes.POINTER(LayerDims), _p,
+                                   ctypes.POINTER(KVRing), ctypes.POINTER(LayerWeights), _p, _p,
+                                   _p, _i64, _p, _p, _sz]
+_lib.txl_layer_step_kv.restype = ctypes.c_int
+
+
+def d_pad(d_head: int) -> int:
+    return (int(d_head) + 7) // 8 * 8
+
+
+def make_kv_ring(dims, mem_max, dtype, capacity=None, device="cuda"):
+    """Allocates k, v [B, H, capacity, d_pad] (capacity defaults to mem_max + L) and
+    returns (KVRing, k, v); the caller keeps k and v alive."""
+    cap = int(mem_max + dims.L if capacity is None else capacity)
+    if _lib.txl_kv_ring_bytes(ctypes.byref(dims), cap, dtype_code(dtype)) == 0:
+        raise ValueError("invalid layer dims or capacity")
+    shape = (dims.B, dims.n_head, cap, d_pad(dims.d_head))
+    k = torch.empty(shape, dtype=dtype, device=device)
+    v = torch.empty(shape, dtype=dtype, device=device)
+    return KVRing(k.data_ptr(), v.data_ptr(), cap, 0, 0, int(mem_max)), k, v
+
+
+def pos_proj(dims, R, W_kR, r_out=None, stream=None):
+    """txl_pos_proj: r = R W_kR^T as [H, R_rows, d_pad]."""
+    rows = R.shape[0]
+    if r_out is None:
+        r_out = torch.empty((dims.n_head, rows, d_pad(dims.d_head)), dtype=R.dtype,
+                            device=R.device)
+    rc = _lib.txl_pos_proj(_stream(stream), dtype_code(R.dtype), ctypes.byref(dims), _ptr(R),
+                           rows, _ptr(W_kR), _ptr(r_out))
+    _check(rc, "txl_pos_proj")
+    return r_out
+
+
+def kv_workspace_bytes(dims, mem_max, dtype) -> int:
+    n = _lib.txl_layer_kv_workspace_bytes(ctypes.byref(dims), int(mem_max), dtype_code(dtype))
+    if n == 0:
+        raise ValueError("invalid layer dims")
+    return int(n)
+
+
+def layer_step_kv(dims, h_in, kv, W, u, vb, r, h_out, workspace, stream=None):
+    """txl_layer_step_kv; r from pos_proj ([H, r_rows, d_pad]); kv is a KVRing."""
+    lw = W if isinstance(W, LayerWeights) else layer_weights(W)
+    rc = _lib.txl_layer_step_kv(_stream(stream), dtype_code(h_in.dtype), ctypes.byref(dims),
+                                _ptr(h_in), ctypes.byref(kv), ctypes.byref(lw), _ptr(u), _ptr(vb),
+                                _ptr(r), r.shape[1], _ptr(h_out), _ptr(workspace),
+                                workspace.numel() * workspace.element_size())
+    _check(rc, "txl_layer_step_kv")
+    return h_out

@@ -75,3 +75,36 @@ def test_argument_errors_need_no_gpu():
     assert lib.txl_mem_update(None, txl.BF16, ctypes.byref(ring), 1, 8,
                               ctypes.c_void_p(0x1000 + 8), 2) == txl.EINVAL
     assert ring.start == 0 and ring.len == 0
+
+
+def test_kv_path_argument_errors_need_no_gpu():
+    from relative_position_memory_amd import txl
+    lib = txl._lib
+    dims = txl.layer_dims(2, 16, 64, 2, 32)
+    assert lib.txl_kv_ring_bytes(ctypes.byref(dims), 40, txl.BF16) == 2 * 2 * 40 * 32 * 2
+    assert lib.txl_kv_ring_bytes(ctypes.byref(dims), 0, txl.BF16) == 0
+    assert lib.txl_layer_kv_workspace_bytes(ctypes.byref(dims), 24, txl.FP32) > 0
+    fake = ctypes.c_void_p(0x100000)
+    W = txl.LayerWeights(*([fake] * 7))
+    good = dict(k=fake, v=ctypes.c_void_p(0x200000), capacity=40, start=0, len=0, mem_max=24)
+
+    def call(**ring_over):
+        kv = txl.KVRing(**{**good, **ring_over})
+        return lib.txl_layer_step_kv(None, txl.BF16, ctypes.byref(dims), fake, ctypes.byref(kv),
+                                     ctypes.byref(W), fake, fake, fake, 64, fake,
+                                     ctypes.c_void_p(0x400000), 1 << 20)
+    assert call(capacity=39) == txl.EINVAL        # capacity < mem_max + L
+    assert call(len=25) == txl.EINVAL             # len > mem_max
+    assert call(start=40) == txl.EINVAL           # start outside the ring
+    assert call(k=None) == txl.EINVAL
+    # a failing call leaves the ring state alone
+    kv = txl.KVRing(**{**good, "len": 25})
+    lib.txl_layer_step_kv(None, txl.BF16, ctypes.byref(dims), fake, ctypes.byref(kv),
+                          ctypes.byref(W), fake, fake, fake, 64, fake, fake, 1 << 20)
+    assert (kv.start, kv.len) == (0, 25)
+    # r too short for len + L
+    kv = txl.KVRing(**{**good, "len": 20})
+    assert lib.txl_layer_step_kv(None, txl.BF16, ctypes.byref(dims), fake, ctypes.byref(kv),
+                                 ctypes.byref(W), fake, fake, fake, 35, fake,
+                                 ctypes.c_void_p(0x400000), 1 << 20) == txl.EINVAL
+    assert lib.txl_pos_proj(None, txl.BF16, ctypes.byref(dims), None, 64, fake, fake) == txl.EINVAL
