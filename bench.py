@@ -41,6 +41,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--eval-speed", action="store_true",
+                   help="instead of the throughput line, print the per-token evaluation time "
+                        "with memory against the vanilla recompute of the window (the pages' "
+                        "Table 9 comparison) at attention lengths 800 .. 3800")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (reads 256 MiB, writes 256 MiB) "
                         "so that a counter run can calibrate FETCH_SIZE / WRITE_SIZE")
@@ -108,6 +112,162 @@ def cpu_baseline(w, x, target_s):
     }
 
 
+def kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, steps, warmup, stream):
+    """ms per step of the stack run with txl_layer_step_kv."""
+    import torch
+    from relative_position_memory_amd import txl
+    tdt = h0.dtype
+    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
+    dims_m = txl.layer_dims(w.B, w.M, w.D, w.H, w.d)
+    rs = [txl.pos_proj(dims, R, Wl["W_kR"], stream=stream) for Wl in Ws]
+    rings = []
+    ws = torch.empty(max(txl.kv_workspace_bytes(dims, w.M, tdt),
+                         txl.kv_workspace_bytes(dims_m, w.M, tdt)), dtype=torch.uint8,
+                     device="cuda")
+    for n, Wl in enumerate(Ws):
+        kv, kb, vbuf = txl.make_kv_ring(dims, w.M, tdt, capacity=w.M + max(w.L, w.M))
+        kv.mem_max = w.M
+        m = torch.from_numpy(x["mem"][n]).to(tdt).cuda()
+        # prefill: the initial memory rows as one segment over an empty memory
+        txl.layer_step_kv(dims_m, m, kv, Wl, u, vb, rs[n], torch.empty_like(m), ws,
+                          stream=stream)
+        rings.append((kv, kb, vbuf))
+    bufs = [torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(2)]
+
+    def step():
+        for s_ in range(w.n_segments):
+            h = h0[s_]
+            for n in range(w.n_layers):
+                out = bufs[n % 2]
+                txl.layer_step_kv(dims, h, rings[n][0], lws[n], u, vb, rs[n], out, ws,
+                                  stream=stream)
+                h = out
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def eval_speed(args):
+    """Per-token evaluation time with memory against the vanilla model that
+    recomputes the whole window for every prediction ([XL] section 4.5, Table 9):
+    the long-memory evaluation shape (d_model 1024, 16 heads of 64, 18 layers),
+    one sequence, attention lengths 800 .. 3800.  Three ways per length:
+      vanilla      txl_layer_step over the attn_len tokens of the window with an
+                   empty memory, every layer: the cost of one prediction;
+      state reuse  one new token (L = 1) over a memory of attn_len - 1 cached
+                   hidden states, re-projected every step (txl_layer_step), plus
+                   the memory update;
+      kv cache     one new token over cached keys and values (txl_layer_step_kv)."""
+    import numpy as np
+    import torch
+    from relative_position_memory_amd import inputs as I
+    from relative_position_memory_amd import txl
+
+    w = I.workload("large_eval")
+    lens = [800, 1800, 2800, 3800]
+    rng = np.random.default_rng(0)
+    tdt = torch.bfloat16
+    HD = w.H * w.d
+
+    def normal(shape, std):
+        return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(
+            tdt).cuda()
+
+    Ws = [{"W_q": normal((HD, w.D), 0.02), "W_kE": normal((HD, w.D), 0.02),
+           "W_v": normal((HD, w.D), 0.02), "W_kR": normal((HD, w.D), 0.02),
+           "W_o": normal((w.D, HD), 0.02), "gamma": torch.ones(w.D, dtype=tdt).cuda(),
+           "beta": torch.zeros(w.D, dtype=tdt).cuda()} for _ in range(w.n_layers)]
+    lws = [txl.layer_weights(Wl) for Wl in Ws]
+    u, vb = normal((w.H, w.d), 0.02), normal((w.H, w.d), 0.02)
+    R = torch.from_numpy(I.sinusoid_table(max(lens), w.D)).to(tdt).cuda()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    rows = []
+    for n_att in lens:
+        M = n_att - 1
+        # vanilla: the whole window, empty memory
+        dv = txl.layer_dims(1, n_att, w.D, w.H, w.d)
+        wsv = torch.empty(txl.workspace_bytes(dv, 1, tdt), dtype=torch.uint8, device="cuda")
+        hv = normal((1, n_att, w.D), 1.0)
+        ov = [torch.empty_like(hv) for _ in range(2)]
+        empty = txl.make_ring(torch.zeros((1, 1, w.D), dtype=tdt, device="cuda"), 0, 0)
+
+        def vanilla():
+            h = hv
+            for n in range(w.n_layers):
+                txl.layer_step(dv, h, empty, lws[n], u, vb, R, ov[n % 2], wsv, stream=stream)
+                h = ov[n % 2]
+        t_van = timed(vanilla, 3)
+        # state reuse: L = 1 over attn_len - 1 cached hidden states per layer
+        d1 = txl.layer_dims(1, 1, w.D, w.H, w.d)
+        ws1 = torch.empty(txl.workspace_bytes(d1, M, tdt), dtype=torch.uint8, device="cuda")
+        mems = [normal((1, M, w.D), 1.0) for _ in range(w.n_layers)]
+        rings = [txl.make_ring(m, 0, M) for m in mems]
+        h1 = normal((1, 1, w.D), 1.0)
+        o1 = [torch.empty_like(h1) for _ in range(2)]
+
+        def reuse():
+            h = h1
+            for n in range(w.n_layers):
+                txl.layer_step(d1, h, rings[n], lws[n], u, vb, R, o1[n % 2], ws1, stream=stream)
+                txl.mem_update(rings[n], h, stream=stream)
+                h = o1[n % 2]
+        t_reuse = timed(reuse, 20)
+        # cached keys and values
+        rs = [txl.pos_proj(d1, R[:n_att], Wl["W_kR"], stream=stream) for Wl in Ws]
+        kvs = []
+        for _ in range(w.n_layers):
+            kv, kb, vbuf = txl.make_kv_ring(d1, M, tdt)
+            kb.zero_()
+            vbuf.zero_()
+            kv.len = M
+            kvs.append((kv, kb, vbuf))
+        wsk = torch.empty(txl.kv_workspace_bytes(d1, M, tdt), dtype=torch.uint8, device="cuda")
+
+        def kvstep():
+            h = h1
+            for n in range(w.n_layers):
+                txl.layer_step_kv(d1, h, kvs[n][0], lws[n], u, vb, rs[n], o1[n % 2], wsk,
+                                  stream=stream)
+                h = o1[n % 2]
+        t_kv = timed(kvstep, 20)
+        rows.append({"attn_len": n_att, "vanilla_ms_per_token": t_van,
+                     "state_reuse_ms_per_token": t_reuse, "kv_cache_ms_per_token": t_kv,
+                     "speedup_state_reuse": t_van / t_reuse, "speedup_kv_cache": t_van / t_kv})
+        print(f"# attn_len {n_att}: vanilla {t_van:.3f} ms, state reuse {t_reuse:.3f} ms, "
+              f"kv cache {t_kv:.3f} ms per token", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "evaluation time per token: memory vs vanilla window recompute",
+        "unit": "ms per token", "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic, random-init weights",
+        "config": {"workload": "long-memory evaluation shape without feed-forward",
+                   "batch": 1, "d_model": w.D, "n_head": w.H, "d_head": w.d,
+                   "n_layers": w.n_layers},
+        "rows": rows,
+        "pages_table9_speedup": {"3800": 1874, "2800": 1409, "1800": 773, "800": 363},
+        "note": "the pages' speed-ups are ratios on their own hardware and full models; "
+                "context, not a target"}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -115,6 +275,10 @@ def main():
         print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); no multi-GPU path is built", file=sys.stderr, flush=True)
         sys.exit(2)
+
+    if args.eval_speed:
+        eval_speed(args)
+        return
 
     import torch
     from relative_position_memory_amd import inputs as I
@@ -177,6 +341,10 @@ def main():
     af = attn_flops(w)
     attn_tflops = af / attn_s / 1e12
 
+    # the same stack with cached keys and values (txl_layer_step_kv): each layer's
+    # ring is filled from its initial memory first (untimed), then the segments run
+    kv_ms = kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, args.steps, args.warmup, stream)
+
     tokens = w.B * w.L * w.n_segments
     step_flops = layer_flops(w) * w.n_layers * w.n_segments
     res = {
@@ -201,6 +369,11 @@ def main():
                      "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic(),
                      "launch_us": attn_s * 1e6, "flop_per_launch": af},
         "step_tflops": step_flops / (ms / 1e3) / 1e12,
+        "eval_kv_cache": {
+            "value": tokens / (kv_ms / 1e3), "unit": "query tokens/s", "ms_per_step": kv_ms,
+            "note": "same stack and inputs with cached keys/values (txl_layer_step_kv): only "
+                    "the L new rows are projected per segment, r is projected once; outputs "
+                    "equal the step above up to rounding"},
     }
     if args.calib_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
