@@ -41,6 +41,8 @@ def _lib():
         lib.txo_layer_step_rows.restype = ctypes.c_int
         lib.txo_mem_update.argtypes = [_i64] * 3 + [_p, _i64, _p, _i64, _p]
         lib.txo_mem_update.restype = _i64
+        lib.txo_pos_ff.argtypes = [_i64] * 3 + [_p] * 7 + [_dbl, _p]
+        lib.txo_pos_ff.restype = ctypes.c_int
         lib.txo_num_threads.argtypes = []
         lib.txo_num_threads.restype = ctypes.c_int
         _LIB = lib
@@ -89,6 +91,24 @@ def linear(x, W):
     y = np.zeros((x2.shape[0], W.shape[0]))
     _lib().txo_linear(x2.shape[0], W.shape[0], W.shape[1], _ptr(x2), _ptr(W), _ptr(y))
     return y.reshape(*lead, W.shape[0])
+
+
+def pos_ff(x, W1, b1, W2, b2, gamma, beta, eps=1e-5):
+    """Position-wise feed-forward (section 3.3's h = Positionwise-Feed-Forward(o)),
+    read as LayerNorm(x + relu(x W1^T + b1) W2^T + b2) over the last axis of x.
+    W1 [Di, D], b1 [Di], W2 [D, Di], b2 / gamma / beta [D]."""
+    x = _f64(x)
+    W1, b1, W2, b2 = _f64(W1), _f64(b1), _f64(W2), _f64(b2)
+    gamma, beta = _f64(gamma), _f64(beta)
+    D, Di = x.shape[-1], W1.shape[0]
+    assert W1.shape == (Di, D) and W2.shape == (D, Di) and b1.shape == (Di,)
+    x2 = x.reshape(-1, D)
+    out = np.zeros_like(x2)
+    rc = _lib().txo_pos_ff(x2.shape[0], D, Di, _ptr(x2), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                           _ptr(gamma), _ptr(beta), float(eps), _ptr(out))
+    if rc != 0:
+        raise MemoryError("oracle pos_ff: allocation failed")
+    return out.reshape(x.shape)
 
 
 def layer_norm(x, gamma, beta, eps=1e-5):

@@ -25,7 +25,10 @@
  *   - queries come from the current rows only, keys/values from [mem ; h];
  *   - multi-head: head hd uses rows hd*d .. hd*d+d-1 of every projection;
  *   - LayerNorm is post-norm, biased variance, eps given, gamma/beta given;
- *   - no bias terms in the projections; the feed-forward is not part of it;
+ *   - no bias terms in the attention projections;
+ *   - the position-wise feed-forward (section 3.3 names it, leaves its inside
+ *     open) is the two-layer ReLU network with biases and a post-norm
+ *     residual: LayerNorm(x + relu(x W1^T + b1) W2^T + b2);
  *   - the new memory is the last min(M, len+L) rows of [old memory ; h].
  */
 #include <math.h>
@@ -144,6 +147,39 @@ void txo_layer_norm(int64_t rows, int64_t D, const double* x, const double* gamm
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < rows; ++m)
         layer_norm_row(D, x + m * D, gamma, beta, eps, y + m * D);
+}
+
+/*
+ * Position-wise feed-forward of the N-layer procedure (section 3.3, the step
+ * h = Positionwise-Feed-Forward(o) after the attention sublayer), per row:
+ *   f   = relu(x W1^T + b1)          W1 [Di, D], b1 [Di]
+ *   out = LayerNorm(x + f W2^T + b2)  W2 [D, Di], b2 [D], biased variance, eps
+ *   x, out [rows, D]
+ * Returns 0, or -1 if scratch allocation fails.
+ */
+int txo_pos_ff(int64_t rows, int64_t D, int64_t Di, const double* x, const double* W1,
+               const double* b1, const double* W2, const double* b2, const double* gamma,
+               const double* beta, double eps, double* out) {
+    double* f = (double*)malloc(sizeof(double) * (size_t)(rows * Di));
+    double* y = (double*)malloc(sizeof(double) * (size_t)(rows * D));
+    if (!f || !y) {
+        free(f);
+        free(y);
+        return -1;
+    }
+    txo_linear(rows, Di, D, x, W1, f);
+    for (int64_t m = 0; m < rows; ++m)
+        for (int64_t c = 0; c < Di; ++c) {
+            const double t = f[m * Di + c] + b1[c];
+            f[m * Di + c] = t > 0.0 ? t : 0.0;
+        }
+    txo_linear(rows, D, Di, f, W2, y);
+    for (int64_t m = 0; m < rows; ++m)
+        for (int64_t c = 0; c < D; ++c) y[m * D + c] += b2[c] + x[m * D + c];
+    txo_layer_norm(rows, D, y, gamma, beta, eps, out);
+    free(f);
+    free(y);
+    return 0;
 }
 
 /*

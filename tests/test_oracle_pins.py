@@ -328,3 +328,44 @@ def test_first_layer_with_eviction_is_a_sliding_window(oracle):
         lo = max(0, s * L - M)
         direct = oracle.layer_step(h0[s], full[:, lo:s * L], W, u, vb, R)
         np.testing.assert_allclose(outs[s][0], direct, rtol=0, atol=1e-12)
+
+
+# --- position-wise feed-forward (section 3.3: h = Positionwise-Feed-Forward(o)) -------------
+
+def test_pos_ff_worked_example(oracle):
+    """A case small enough to do by hand.  x = [1, 0, -1];
+    x W1^T = [1, 1], + b1 = [1, -1], relu -> [1, 0];
+    . W2^T = [1, 2, 0], + b2 = [1, 2, 1], + x = [2, 2, 0];
+    mean 4/3, deviations [2/3, 2/3, -4/3], biased variance 8/9, so with eps = 0 the
+    normalised row is [1/sqrt(2), 1/sqrt(2), -sqrt(2)]."""
+    x = np.array([[1.0, 0.0, -1.0]])
+    W1 = np.array([[1.0, 2.0, 0.0], [0.0, 1.0, -1.0]])
+    b1 = np.array([0.0, -2.0])
+    W2 = np.array([[1.0, 0.0], [2.0, 1.0], [0.0, 3.0]])
+    b2 = np.array([0.0, 0.0, 1.0])
+    out = oracle.pos_ff(x, W1, b1, W2, b2, np.ones(3), np.zeros(3), 0.0)
+    s = np.sqrt(2.0)
+    np.testing.assert_allclose(out, [[1 / s, 1 / s, -s]], rtol=0, atol=1e-12)
+    g, b = np.array([2.0, -1.0, 0.5]), np.array([0.1, 0.2, 0.3])
+    np.testing.assert_allclose(oracle.pos_ff(x, W1, b1, W2, b2, g, b, 0.0),
+                               [[2 / s + 0.1, -1 / s + 0.2, -0.5 * s + 0.3]], rtol=0, atol=1e-12)
+
+
+def test_pos_ff_without_second_layer_is_layer_norm(oracle):
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((4, 5, 6))
+    W1, b1 = rng.standard_normal((9, 6)), rng.standard_normal(9)
+    g, b = rng.standard_normal(6), rng.standard_normal(6)
+    out = oracle.pos_ff(x, W1, b1, np.zeros((6, 9)), np.zeros(6), g, b, 1e-5)
+    np.testing.assert_allclose(out, oracle.layer_norm(x, g, b, 1e-5), rtol=0, atol=1e-12)
+
+
+def test_pos_ff_closed_gate_adds_only_the_output_bias(oracle):
+    """With every hidden unit below zero the ReLU passes nothing: LN(x + b2)."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((3, 7))
+    W1, W2 = rng.standard_normal((11, 7)), rng.standard_normal((7, 11))
+    b2 = rng.standard_normal(7)
+    out = oracle.pos_ff(x, W1, np.full(11, -1e6), W2, b2, np.ones(7), np.zeros(7), 1e-5)
+    np.testing.assert_allclose(out, oracle.layer_norm(x + b2, np.ones(7), np.zeros(7), 1e-5),
+                               rtol=0, atol=1e-12)
