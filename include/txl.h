@@ -276,6 +276,25 @@ int txl_layer_step_kv(void* stream, int dtype, const txl_layer_dims* dims, const
                       const void* v_bias, const void* r, int64_t r_rows, void* h_out,
                       void* workspace, size_t ws_bytes);
 
+/*
+ * Position-wise feed-forward of the N-layer procedure (section 3.3: after the
+ * attention sublayer, h = Positionwise-Feed-Forward(o); the pages leave its
+ * inside open).  Read as the two-layer ReLU network with biases and a post-norm
+ * residual, per row:
+ *   out = LayerNorm(x + relu(x W1^T + b1) W2^T + b2) * gamma + beta   (biased variance)
+ *   x, out   [rows][d_model] dense (out must not overlap any input)
+ *   W1 [d_inner][d_model], b1 [d_inner], W2 [d_model][d_inner], b2, ln_gamma, ln_beta [d_model]
+ *   workspace  >= txl_pos_ff_workspace_bytes() bytes, 256-byte aligned (holds the
+ *            hidden activations).
+ * A layer of the full stack is txl_layer_step (or txl_layer_step_kv) followed by
+ * this on its output; the memory still caches the layer INPUT.
+ */
+size_t txl_pos_ff_workspace_bytes(int64_t rows, int64_t d_model, int64_t d_inner, int dtype);
+int txl_pos_ff(void* stream, int dtype, int64_t rows, int64_t d_model, int64_t d_inner,
+               const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
+               const void* ln_gamma, const void* ln_beta, float ln_eps, void* out,
+               void* workspace, size_t ws_bytes);
+
 /* Static text for a status, followed by the calling thread's detail of its last error. */
 const char* txl_status_string(int status);
 

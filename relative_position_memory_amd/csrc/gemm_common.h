@@ -33,6 +33,14 @@ __device__ inline T* heads_dst(const GemmArgs& g, int64_t m, int64_t n) {
   return base + b * e.sb + head * e.sh + ring_t(e, t) * e.st + c;
 }
 
+// acc + bias[n], then the activation (EPI_HEADS) -- see Epilogue::bias.
+template <typename T>
+__device__ inline float epi_value(const Epilogue& e, int64_t n, float acc) {
+  if (e.bias) acc += Elt<T>::load((const T*)e.bias + n);
+  if (e.mode == EPI_HEADS && e.act == ACT_RELU) acc = acc > 0.f ? acc : 0.f;
+  return acc;
+}
+
 // Stores element (m, n) of a head-major output; the store of a head's last
 // element also clears the row's padding.
 template <typename T>
@@ -45,6 +53,7 @@ __device__ inline void heads_store(const GemmArgs& g, int64_t m, int64_t n, floa
 
 template <typename T>
 __device__ inline void epilogue_store(const GemmArgs& g, int64_t m, int64_t n, float acc) {
+  acc = epi_value<T>(g.e, n, acc);
   if (g.e.mode == EPI_HEADS) {
     heads_store<T>(g, m, n, acc);
   } else {
@@ -59,7 +68,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s, int num_cus);
 hipError_t launch_gemm_mfma_multi(const GemmArgs* g, int n, hipStream_t s, int num_cus);
 bool gemm_mfma_supported(const GemmArgs& g);
 
-// h_out = LayerNorm(a W^T + resid) * gamma + beta for bf16 rows of width D
+// h_out = LayerNorm(a W^T + bias + resid) * gamma + beta for bf16 rows of width D
 // (D % 64 == 0, D <= 512, K % 32 == 0, 16-byte aligned tensors).
 struct LnArgs {
   int64_t M, D, K;        // rows, width, inner size
@@ -70,6 +79,7 @@ struct LnArgs {
   const void* beta;       // [D]
   float eps;
   void* out;              // [M][D]
+  const void* bias;       // [D] added before the residual, or NULL
 };
 bool gemm_ln_supported(const LnArgs& p);
 hipError_t launch_gemm_ln(const LnArgs& p, hipStream_t s);

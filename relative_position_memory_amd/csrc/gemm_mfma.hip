@@ -156,13 +156,24 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
   if (EPI == EPI_STAGE_BF16) {
     constexpr int EP = C::BN + 8;  // row pitch (bf16): 16-byte aligned, conflict-free
     uint16_t* es = (uint16_t*)smem;
+    // bias and activation (wave-uniform: only the feed-forward's first layer has them)
+    const bool post = g.e.bias != nullptr || g.e.act != ACT_NONE;
 #pragma unroll
     for (int i = 0; i < C::TI; ++i)
 #pragma unroll
       for (int j = 0; j < C::TJ; ++j) {
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = acc[j][i][e];
+        if (post) {
+          const int nb = n0 + wn * 32 * C::TJ + 32 * j + 16 * lh;
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            v[e] = nb + e < g.N ? epi_value<uint16_t>(g.e, nb + e, v[e]) : v[e];
+        }
         uint32_t pk[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = pack_bf16x2(acc[j][i][2 * e], acc[j][i][2 * e + 1]);
+        for (int e = 0; e < 8; ++e) pk[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
         uint16_t* dst = es + (wm * 32 * C::TI + 32 * i + li) * EP + wn * 32 * C::TJ + 32 * j + 16 * lh;
         *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         *(uint4*)(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
@@ -211,10 +222,10 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
       const uint2 rr = *(const uint2*)((const uint16_t*)g.e.resid + m * g.N + n);
       const float4 a4 = *(const float4*)(es + row * EP + 4 * c);
       float4 o;
-      o.x = a4.x + bf16_to_f32((uint16_t)(rr.x & 0xffffu));
-      o.y = a4.y + bf16_to_f32((uint16_t)(rr.x >> 16));
-      o.z = a4.z + bf16_to_f32((uint16_t)(rr.y & 0xffffu));
-      o.w = a4.w + bf16_to_f32((uint16_t)(rr.y >> 16));
+      o.x = epi_value<uint16_t>(g.e, n, a4.x) + bf16_to_f32((uint16_t)(rr.x & 0xffffu));
+      o.y = epi_value<uint16_t>(g.e, n + 1, a4.y) + bf16_to_f32((uint16_t)(rr.x >> 16));
+      o.z = epi_value<uint16_t>(g.e, n + 2, a4.z) + bf16_to_f32((uint16_t)(rr.y & 0xffffu));
+      o.w = epi_value<uint16_t>(g.e, n + 3, a4.w) + bf16_to_f32((uint16_t)(rr.y >> 16));
       *(float4*)(g.e.y + m * g.N + n) = o;
     }
     __syncthreads();
@@ -230,7 +241,7 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
         for (int e = 0; e < 16; ++e) {
           const int64_t n = (int64_t)n0 + wn * 32 * C::TJ + 32 * j + 16 * lh + e;
           if (n >= g.N) continue;
-          const float v = acc[j][i][e];
+          const float v = epi_value<uint16_t>(g.e, n, acc[j][i][e]);
           if (g.e.mode == EPI_HEADS) {
             heads_store<uint16_t>(g, m, n, v);
           } else {
@@ -541,7 +552,7 @@ hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s) {
 
 
 // ---- output projection + residual + LayerNorm ------------------------------------------
-// h_out[m] = LayerNorm(a[m] W_o^T + h[m]) * gamma + beta (section 3.3: post-norm,
+// h_out[m] = LayerNorm(a[m] W_o^T (+ bias) + h[m]) * gamma + beta (section 3.3: post-norm,
 // mean and biased variance over D).  One workgroup owns 64 whole rows, so the
 // row statistics never leave the CU and y never goes to memory.  Eight waves;
 // wave w owns output columns 64 w .. 64 w + 63 (2 x 2 blocks of 32 x 32 over the
@@ -659,6 +670,16 @@ __global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
       for (int e = 0; e < 8; ++e) {
         acc[j][i][2 * e] += bf16_to_f32((uint16_t)(rw[e] & 0xffffu));
         acc[j][i][2 * e + 1] += bf16_to_f32((uint16_t)(rw[e] >> 16));
+      }
+      if (p.bias) {
+        const uint4* bp = (const uint4*)((const uint16_t*)p.bias + n);
+        const uint4 b0 = bp[0], b1 = bp[1];
+        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[j][i][2 * e] += bf16_to_f32((uint16_t)(bw[e] & 0xffffu));
+          acc[j][i][2 * e + 1] += bf16_to_f32((uint16_t)(bw[e] >> 16));
+        }
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) rs[i] += acc[j][i][e];
@@ -782,7 +803,8 @@ bool gemm_ln_supported(const LnArgs& p) {
   if (p.M < 1 || p.M > 0x7fffffffLL - LBM || p.M * p.K > 0x7fffffffLL || p.M * p.D > 0x7fffffffLL)
     return false;
   const uintptr_t al = (uintptr_t)p.a | (uintptr_t)p.W | (uintptr_t)p.resid |
-                       (uintptr_t)p.gamma | (uintptr_t)p.beta | (uintptr_t)p.out;
+                       (uintptr_t)p.gamma | (uintptr_t)p.beta | (uintptr_t)p.out |
+                       (uintptr_t)p.bias;
   return al % 16 == 0;
 }
 

@@ -595,5 +595,75 @@ int txl_layer_step_kv(void* stream, int dtype, const txl_layer_dims* dims, const
   return TXL_OK;
 }
 
+// ---- position-wise feed-forward ---------------------------------------------------------
+
+size_t txl_pos_ff_workspace_bytes(int64_t rows, int64_t d_model, int64_t d_inner, int dtype) {
+  if ((dtype != TXL_FP32 && dtype != TXL_BF16) || rows < 1 || d_model < 1 || d_inner < 1)
+    return 0;
+  return (size_t)(round_up(rows * d_inner * elt_size(dtype), 256) + round_up(rows * d_model * 4, 256));
+}
+
+int txl_pos_ff(void* stream, int dtype, int64_t rows, int64_t d_model, int64_t d_inner,
+               const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
+               const void* ln_gamma, const void* ln_beta, float ln_eps, void* out,
+               void* workspace, size_t ws_bytes) {
+  g_detail[0] = 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  if (rows < 1 || d_model < 1 || d_inner < 1)
+    return fail(TXL_EINVAL, "rows, d_model, d_inner must be >= 1");
+  if (rows > 0x7fffffffLL || d_model > 65535 || d_inner > 0x7fffffffLL / 8)
+    return fail(TXL_EUNSUPPORTED, "sizes out of range");
+  if (!x || !W1 || !b1 || !W2 || !b2 || !ln_gamma || !ln_beta || !out)
+    return fail(TXL_EINVAL, "NULL tensor pointer");
+  if (!(ln_eps >= 0.f) || !isfinite(ln_eps)) return fail(TXL_EINVAL, "ln_eps must be finite and >= 0");
+  if (!workspace) return fail(TXL_EINVAL, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(TXL_EINVAL, "workspace is not 256-byte aligned");
+  const size_t need = txl_pos_ff_workspace_bytes(rows, d_model, d_inner, dtype);
+  if (ws_bytes < need) return fail(TXL_EWORKSPACE, "need %zu bytes, got %zu", need, ws_bytes);
+  const int64_t es = elt_size(dtype), D = d_model, Di = d_inner;
+  const Span sx = {(uintptr_t)x, (uintptr_t)x + (uintptr_t)(rows * D * es)};
+  const Span so = {(uintptr_t)out, (uintptr_t)out + (uintptr_t)(rows * D * es)};
+  const Span sws = {(uintptr_t)workspace, (uintptr_t)workspace + ws_bytes};
+  const Span sw[] = {{(uintptr_t)W1, (uintptr_t)W1 + (uintptr_t)(Di * D * es)},
+                     {(uintptr_t)W2, (uintptr_t)W2 + (uintptr_t)(D * Di * es)},
+                     {(uintptr_t)b1, (uintptr_t)b1 + (uintptr_t)(Di * es)},
+                     {(uintptr_t)b2, (uintptr_t)b2 + (uintptr_t)(D * es)},
+                     {(uintptr_t)ln_gamma, (uintptr_t)ln_gamma + (uintptr_t)(D * es)},
+                     {(uintptr_t)ln_beta, (uintptr_t)ln_beta + (uintptr_t)(D * es)}, sx};
+  for (const Span& s : sw)
+    if (overlap(so, s) || overlap(sws, s)) return fail(TXL_EINVAL, "out or workspace overlaps an input");
+  if (overlap(so, sws)) return fail(TXL_EINVAL, "out overlaps the workspace");
+
+  char* base = (char*)workspace;
+  void* f = base;  // relu(x W1^T + b1), [rows][Di]
+  float* y = (float*)(base + round_up(rows * Di * es, 256));
+  hipStream_t st = (hipStream_t)stream;
+  txl::GemmArgs g1{};
+  g1.M = rows; g1.N = Di; g1.K = D;
+  g1.a = {nullptr, 1, 0, 0, x, rows, D};
+  g1.w = {W1, W1, Di, D};
+  // row-major [rows][Di] as a single "head" of width Di
+  g1.e = {txl::EPI_HEADS, f, f, Di, Di, 0, 0, Di, nullptr, nullptr, 0, 0, 0, b1, txl::ACT_RELU};
+  int rc = run_gemm(dtype, g1, st, "feed-forward first layer");
+  if (rc != TXL_OK) return rc;
+  txl::LnArgs ln{rows, D, Di, f, W2, x, ln_gamma, ln_beta, ln_eps, out, b2};
+  if (dtype == TXL_BF16 && txl::gemm_ln_supported(ln)) {
+    const hipError_t e = txl::launch_gemm_ln(ln, st);
+    if (e != hipSuccess) return hip_fail(e, "feed-forward second layer + LayerNorm");
+    return TXL_OK;
+  }
+  txl::GemmArgs g2{};
+  g2.M = rows; g2.N = D; g2.K = Di;
+  g2.a = {nullptr, 1, 0, 0, f, rows, Di};
+  g2.w = {W2, W2, D, Di};
+  g2.e = {txl::EPI_RESID_F32, nullptr, nullptr, 0, 1, 0, 0, 0, y, x, 0, 0, 0, b2, txl::ACT_NONE};
+  if ((rc = run_gemm(dtype, g2, st, "feed-forward second layer")) != TXL_OK) return rc;
+  const hipError_t e =
+      txl::launch_layer_norm(dtype, y, ln_gamma, ln_beta, ln_eps, rows, D, out, st);
+  if (e != hipSuccess) return hip_fail(e, "layer norm");
+  return TXL_OK;
+}
+
 }  // extern "C"
+
 

@@ -107,7 +107,12 @@ struct Epilogue {
   // EPI_HEADS rows padded past d: when pad > d, elements d .. pad-1 of every
   // head row are written as zeros (readers may load whole padded rows).
   int64_t pad;
+  // Optional per-column bias (dtype [N], NULL = none) added to acc, then for
+  // EPI_HEADS the activation act (ACT_NONE or ACT_RELU).
+  const void* bias;
+  int act;
 };
+enum ActMode { ACT_NONE = 0, ACT_RELU = 1 };
 
 __host__ __device__ inline int64_t ring_t(const Epilogue& e, int64_t t) {
   if (e.t_mod <= 0) return t;

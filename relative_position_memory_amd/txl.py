@@ -266,3 +266,34 @@ def layer_step_kv(dims, h_in, kv, W, u, vb, r, h_out, workspace, stream=None):
                                 workspace.numel() * workspace.element_size())
     _check(rc, "txl_layer_step_kv")
     return h_out
+
+
+# ---- position-wise feed-forward ----------------------------------------------------------
+
+_lib.txl_pos_ff_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int]
+_lib.txl_pos_ff_workspace_bytes.restype = _sz
+_lib.txl_pos_ff.argtypes = ([_p, ctypes.c_int, _i64, _i64, _i64] + [_p] * 7
+                            + [ctypes.c_float, _p, _p, _sz])
+_lib.txl_pos_ff.restype = ctypes.c_int
+
+
+def pos_ff_workspace_bytes(rows, d_model, d_inner, dtype) -> int:
+    n = _lib.txl_pos_ff_workspace_bytes(int(rows), int(d_model), int(d_inner), dtype_code(dtype))
+    if n == 0:
+        raise ValueError("invalid feed-forward sizes")
+    return int(n)
+
+
+def pos_ff(x, W1, b1, W2, b2, gamma, beta, out, workspace=None, eps=1e-5, stream=None):
+    """txl_pos_ff over the rows of x [..., d_model]."""
+    D = x.shape[-1]
+    rows = x.numel() // D
+    Di = W1.shape[0]
+    if workspace is None:
+        workspace = torch.empty(pos_ff_workspace_bytes(rows, D, Di, x.dtype), dtype=torch.uint8,
+                                device=x.device)
+    rc = _lib.txl_pos_ff(_stream(stream), dtype_code(x.dtype), rows, D, Di, _ptr(x), _ptr(W1),
+                         _ptr(b1), _ptr(W2), _ptr(b2), _ptr(gamma), _ptr(beta), float(eps),
+                         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size())
+    _check(rc, "txl_pos_ff")
+    return out

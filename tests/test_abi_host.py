@@ -108,3 +108,26 @@ def test_kv_path_argument_errors_need_no_gpu():
                                  ctypes.byref(W), fake, fake, fake, 35, fake,
                                  ctypes.c_void_p(0x400000), 1 << 20) == txl.EINVAL
     assert lib.txl_pos_proj(None, txl.BF16, ctypes.byref(dims), None, 64, fake, fake) == txl.EINVAL
+
+
+def test_pos_ff_argument_errors_need_no_gpu():
+    from relative_position_memory_amd import txl
+    lib = txl._lib
+    # hidden activations (bf16) + the fp32 pre-LayerNorm rows, each rounded up to 256 bytes
+    assert lib.txl_pos_ff_workspace_bytes(10, 64, 256, txl.BF16) == 5120 + 2560
+    assert lib.txl_pos_ff_workspace_bytes(0, 64, 256, txl.BF16) == 0
+    fake = ctypes.c_void_p(0x100000)
+    args = [None, txl.BF16, 10, 64, 256] + [fake] * 7 + [ctypes.c_float(1e-5), ctypes.c_void_p(0x900000),
+                                                         ctypes.c_void_p(0xa00000), 1 << 20]
+    bad = list(args)
+    bad[5] = None                      # x
+    assert lib.txl_pos_ff(*bad) == txl.EINVAL
+    bad = list(args)
+    bad[2] = 0                         # rows
+    assert lib.txl_pos_ff(*bad) == txl.EINVAL
+    bad = list(args)
+    bad[1] = 5                         # dtype
+    assert lib.txl_pos_ff(*bad) == txl.EUNSUPPORTED
+    bad = list(args)
+    bad[-1] = 16                       # workspace too small
+    assert lib.txl_pos_ff(*bad) == txl.EWORKSPACE
