@@ -551,6 +551,97 @@ hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s) {
 }
 
 
+// ---- skinny GEMM: at most 32 rows (decode steps) -----------------------------------------
+// C = A W^T with M <= 32: the large tiles would leave almost every CU idle and
+// read the weights through 256-row tiles of mostly absent rows.  Here a
+// workgroup owns 32 output columns for all M rows and its 8 waves split K in
+// eighths; each wave keeps 16 accumulators of v_mfma_f32_32x32x16_bf16 (W rows
+// as the A operand, the gathered rows of A, zero past M, as B), so lane l holds
+// row l % 32.  Operands come straight from global memory, four 16-deep k steps
+// per batch with the next batch's loads issued before the current batch's
+// products, so every wave keeps 8 loads in flight; the weights are read once and
+// A (a few KB) is shared through L2.  The eighths are summed through LDS and the
+// usual epilogue stores each output.
+constexpr int SK_BN = 32, SK_NW = 8, SK_CH = 4;
+
+struct SkinnyBatch {
+  GemmArgs g[MAXP];
+  int block_end[MAXP];  // inclusive prefix sums of the problems' column tiles
+  int n;
+};
+
+__global__ __launch_bounds__(64 * SK_NW) void gemm_skinny_kernel(SkinnyBatch bt) {
+  __shared__ float red[SK_NW][64][16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int p = 0;
+  while (p + 1 < bt.n && (int)blockIdx.x >= bt.block_end[p]) ++p;
+  const GemmArgs& g = bt.g[p];
+  const int n0 = ((int)blockIdx.x - (p ? bt.block_end[p - 1] : 0)) * SK_BN;
+  const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+  const int r32 = lane & 31, kc = 8 * (lane >> 5);  // operand row, 8-element k chunk
+  const uint16_t* arow = r32 < M ? gather_row32(g.a, r32) : nullptr;
+  const uint16_t* wrow = (const uint16_t*)weight_row(g.w, n0 + r32 < N ? n0 + r32 : N - 1, 2);
+  const int kq = K / SK_NW, k_lo = wave * kq + kc, nit = kq / 16;
+  const bf16x8 zero8 = {};
+  bf16x8 wa[2][SK_CH], xb[2][SK_CH];
+  auto load = [&](bf16x8 (&w)[SK_CH], bf16x8 (&x)[SK_CH], int it0) {
+#pragma unroll
+    for (int c = 0; c < SK_CH; ++c) {
+      if (it0 + c >= nit) break;
+      const int k = k_lo + 16 * (it0 + c);
+      w[c] = *(const bf16x8*)(wrow + k);
+      x[c] = arow ? *(const bf16x8*)(arow + k) : zero8;
+    }
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) acc[x] = 0.f;
+  auto mult = [&](const bf16x8 (&w)[SK_CH], const bf16x8 (&x)[SK_CH], int it0) {
+#pragma unroll
+    for (int c = 0; c < SK_CH; ++c) {
+      if (it0 + c >= nit) break;
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[c], x[c], acc, 0, 0, 0);
+    }
+  };
+  load(wa[0], xb[0], 0);
+  for (int it0 = 0; it0 < nit; it0 += 2 * SK_CH) {
+    load(wa[1], xb[1], it0 + SK_CH);
+    mult(wa[0], xb[0], it0);
+    load(wa[0], xb[0], it0 + 2 * SK_CH);
+    mult(wa[1], xb[1], it0 + SK_CH);
+  }
+#pragma unroll
+  for (int x = 0; x < 16; ++x) red[wave][lane][x] = acc[x];
+  __syncthreads();
+  // C[n][m]: lane l, register x is column n0 + 8 (x / 4) + 4 (l / 32) + x % 4, row l % 32
+  for (int v = tid; v < 64 * 16; v += 64 * SK_NW) {
+    const int l = v >> 4, x = v & 15;
+    const int m = l & 31, n = n0 + 8 * (x >> 2) + 4 * (l >> 5) + (x & 3);
+    if (m >= M || n >= N) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < SK_NW; ++w) sum += red[w][l][x];
+    epilogue_store<uint16_t>(g, m, n, sum);
+  }
+}
+
+bool skinny_ok(const GemmArgs& g) { return g.M <= 32 && g.K % (16 * SK_NW) == 0; }
+
+hipError_t launch_skinny(const GemmArgs* gs, int n, hipStream_t s) {
+  SkinnyBatch bt{};
+  int64_t total = 0;
+  for (int p = 0; p < n; ++p) {
+    bt.g[p] = gs[p];
+    total += (gs[p].N + SK_BN - 1) / SK_BN;
+    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+    bt.block_end[p] = (int)total;
+  }
+  bt.n = n;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)total), dim3(64 * SK_NW), 0, s, bt);
+  return hipGetLastError();
+}
+
 // ---- output projection + residual + LayerNorm ------------------------------------------
 // h_out[m] = LayerNorm(a[m] W_o^T (+ bias) + h[m]) * gamma + beta (section 3.3: post-norm,
 // mean and biased variance over D).  One workgroup owns 64 whole rows, so the
@@ -786,6 +877,9 @@ bool gemm_mfma_supported(const GemmArgs& g) {
 
 hipError_t launch_gemm_mfma_multi(const GemmArgs* gs, int n, hipStream_t s, int num_cus) {
   if (n < 1 || n > MAXP) return hipErrorInvalidValue;
+  bool skinny = true;
+  for (int p = 0; p < n; ++p) skinny = skinny && skinny_ok(gs[p]);
+  if (skinny) return launch_skinny(gs, n, s);
   // 256 x 256 tiles when they give most CUs a workgroup, else 128 x 128
   int64_t big = 0;
   for (int p = 0; p < n; ++p)

@@ -195,7 +195,8 @@ int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_lay
   const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
   // one fused kernel when the rows fit it
   txl::LnArgs ln{BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
-  if (dtype == TXL_BF16 && txl::gemm_ln_supported(ln)) {
+  // (a few rows, as in a decode step, go to the skinny GEMM and the row kernel)
+  if (dtype == TXL_BF16 && BL > 32 && txl::gemm_ln_supported(ln)) {
     const hipError_t e = txl::launch_gemm_ln(ln, st);
     if (e != hipSuccess) return hip_fail(e, "output projection + LayerNorm");
     return TXL_OK;
@@ -647,7 +648,7 @@ int txl_pos_ff(void* stream, int dtype, int64_t rows, int64_t d_model, int64_t d
   int rc = run_gemm(dtype, g1, st, "feed-forward first layer");
   if (rc != TXL_OK) return rc;
   txl::LnArgs ln{rows, D, Di, f, W2, x, ln_gamma, ln_beta, ln_eps, out, b2};
-  if (dtype == TXL_BF16 && txl::gemm_ln_supported(ln)) {
+  if (dtype == TXL_BF16 && rows > 32 && txl::gemm_ln_supported(ln)) {
     const hipError_t e = txl::launch_gemm_ln(ln, st);
     if (e != hipSuccess) return hip_fail(e, "feed-forward second layer + LayerNorm");
     return TXL_OK;

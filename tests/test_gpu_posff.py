@@ -35,6 +35,7 @@ def _ff_weights(rng, D, Di, dtype):
     ("bf16", 300, 512, 2048),   # matrix cores, fused second layer + LayerNorm
     ("bf16", 77, 96, 200),      # ragged rows, unfused LayerNorm (D % 64 != 0)
     ("bf16", 100, 1024, 4096),  # D > 512: unfused LayerNorm
+    ("bf16", 3, 512, 2048),     # a decode step's rows: skinny GEMMs
 ])
 def test_pos_ff_matches_oracle(dtype, rows, D, Di):
     from relative_position_memory_amd import txl
