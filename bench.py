@@ -112,6 +112,38 @@ def cpu_baseline(w, x, target_s):
     }
 
 
+def pos_ff_time(w, reps, stream):
+    """txl_pos_ff over the B*L rows of a segment (d_inner = 4 d_model), HIP events."""
+    import numpy as np
+    import torch
+    from relative_position_memory_amd import txl
+    rows, D, Di = w.B * w.L, w.D, 4 * w.D
+    rng = np.random.default_rng(3)
+    t = lambda shape, std: torch.from_numpy(
+        (rng.standard_normal(shape) * std).astype(np.float32)).to(torch.bfloat16).cuda()
+    x = t((rows, D), 1.0)
+    W1, b1, W2, b2 = t((Di, D), D ** -0.5), t((Di,), 0.1), t((D, Di), Di ** -0.5), t((D,), 0.1)
+    g, b = torch.ones(D, dtype=torch.bfloat16).cuda(), torch.zeros(D, dtype=torch.bfloat16).cuda()
+    out = torch.empty_like(x)
+    ws = torch.empty(txl.pos_ff_workspace_bytes(rows, D, Di, x.dtype), dtype=torch.uint8,
+                     device="cuda")
+    run = lambda: txl.pos_ff(x, W1, b1, W2, b2, g, b, out, ws, stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    flop = 2.0 * 2 * rows * D * Di
+    return {"rows": rows, "d_model": D, "d_inner": Di, "launch_us": us,
+            "achieved": flop / (us * 1e-6) / 1e12, "unit": "TFLOP/s",
+            "frac": flop / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, steps, warmup, stream):
     """ms per step of the stack run with txl_layer_step_kv."""
     import torch
@@ -345,6 +377,10 @@ def main():
     # ring is filled from its initial memory first (untimed), then the segments run
     kv_ms = kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, args.steps, args.warmup, stream)
 
+    # the position-wise feed-forward (not part of the step above) at the same rows,
+    # d_inner = 4 d_model
+    ff = pos_ff_time(w, args.attn_reps, stream)
+
     tokens = w.B * w.L * w.n_segments
     step_flops = layer_flops(w) * w.n_layers * w.n_segments
     res = {
@@ -369,6 +405,7 @@ def main():
                      "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic(),
                      "launch_us": attn_s * 1e6, "flop_per_launch": af},
         "step_tflops": step_flops / (ms / 1e3) / 1e12,
+        "pos_ff": ff,
         "eval_kv_cache": {
             "value": tokens / (kv_ms / 1e3), "unit": "query tokens/s", "ms_per_step": kv_ms,
             "note": "same stack and inputs with cached keys/values (txl_layer_step_kv): only "

@@ -47,8 +47,12 @@ template <typename T>
 __device__ inline void heads_store(const GemmArgs& g, int64_t m, int64_t n, float acc) {
   T* p = heads_dst<T>(g, m, n);
   Elt<T>::store(p, acc);
-  if (g.e.pad > g.e.d && (n % g.e.HD) % g.e.d == g.e.d - 1)
-    for (int64_t c = 1; c < g.e.pad - g.e.d + 1; ++c) Elt<T>::store(p + c, 0.f);
+  // (padding is less than 8 elements: a fixed-trip loop)
+  if (g.e.pad > g.e.d && (n % g.e.HD) % g.e.d == g.e.d - 1) {
+#pragma unroll
+    for (int c = 1; c < 8; ++c)
+      if (c <= g.e.pad - g.e.d) Elt<T>::store(p + c, 0.f);
+  }
 }
 
 template <typename T>

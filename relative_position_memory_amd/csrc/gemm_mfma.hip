@@ -82,6 +82,7 @@ struct Cfg {
   // epilogue staging
   static constexpr size_t ESMEM_BF16 = (size_t)BM * (BN + 8) * sizeof(uint16_t);
   static constexpr size_t ESMEM_F32 = (size_t)BM * (BN + 4) * sizeof(float);
+  static constexpr size_t ESMEM_SCALAR = (size_t)NW * 32 * (32 * TJ + 1) * sizeof(float);
 };
 using Big = Cfg<256, 256, 2, 4, 1>;
 using Small = Cfg<128, 128, 2, 2, 2>;
@@ -90,7 +91,9 @@ enum { EPI_SCALAR = 0, EPI_STAGE_BF16 = 1, EPI_STAGE_F32 = 2 };
 
 template <class C, int EPI>
 constexpr size_t epi_smem() {
-  return EPI == EPI_STAGE_BF16 ? C::ESMEM_BF16 : EPI == EPI_STAGE_F32 ? C::ESMEM_F32 : 0;
+  return EPI == EPI_STAGE_BF16 ? C::ESMEM_BF16
+       : EPI == EPI_STAGE_F32  ? C::ESMEM_F32
+                               : C::ESMEM_SCALAR;
 }
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
@@ -230,26 +233,36 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
     }
     __syncthreads();
   } else {
-    // element by element (any layout)
+    // element by element (any layout): each wave passes one 32-row block at a
+    // time through its own LDS slice, then its lanes walk the block row-major
+    // (consecutive lanes take consecutive columns).
+    constexpr int WC = 32 * C::TJ, EPW = WC + 1;
+    float* ws = (float*)smem + (wm * C::WN + wn) * 32 * EPW;
+    const int lane = tid & 63;
+    const bool heads = g.e.mode == EPI_HEADS;
 #pragma unroll
     for (int i = 0; i < C::TI; ++i) {
-      const int64_t m = (int64_t)m0 + wm * 32 * C::TI + 32 * i + li;
-      if (m >= g.M) continue;
 #pragma unroll
       for (int j = 0; j < C::TJ; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t n = (int64_t)n0 + wn * 32 * C::TJ + 32 * j + 16 * lh + e;
-          if (n >= g.N) continue;
-          const float v = epi_value<uint16_t>(g.e, n, acc[j][i][e]);
-          if (g.e.mode == EPI_HEADS) {
-            heads_store<uint16_t>(g, m, n, v);
-          } else {
-            g.e.y[m * g.N + n] = v + bf16_to_f32(((const uint16_t*)g.e.resid)[m * g.N + n]);
-          }
+        for (int e = 0; e < 16; ++e) ws[li * EPW + 32 * j + 16 * lh + e] = acc[j][i][e];
+      __syncthreads();
+      const int64_t mb = (int64_t)m0 + wm * 32 * C::TI + 32 * i;
+      const int64_t nb = (int64_t)n0 + wn * WC;
+#pragma unroll 2
+      for (int idx = lane; idx < 32 * WC; idx += 64) {
+        const int r = idx / WC, c = idx - r * WC;
+        const int64_t m = mb + r, n = nb + c;
+        if (m >= g.M || n >= g.N) continue;
+        const float v = epi_value<uint16_t>(g.e, n, ws[r * EPW + c]);
+        if (heads) {
+          heads_store<uint16_t>(g, m, n, v);
+        } else {
+          g.e.y[m * g.N + n] = v + bf16_to_f32(((const uint16_t*)g.e.resid)[m * g.N + n]);
         }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
