@@ -366,17 +366,20 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
         }
         // The diagonal shift happens at the store: value (bw, e) is window row
         // 16 bw + 4 g4 + e of query n16 and goes to key 16 bw + 4 g4 + e - 15 + n16
-        // (keys 0..63 only).  The buffer is reused by the next group: LDS
+        // (keys 0..63 only).  Blocks 0 and 4 hold keys jj and jj + 64 for the same
+        // (lane, e), and exactly one of the two is in range, so they share one
+        // unconditional store.  The buffer is reused by the next group: LDS
         // operations of one wave complete in order, so this group's stores follow
         // the previous group's reads.
 #pragma unroll
-        for (int bw = 0; bw < 5; ++bw)
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 4 * g4 + e - 15 + n16;  // key of block 0, in -15 .. 15
+          wbuf[sp_slot(jj & (BK - 1))] = jj >= 0 ? wv[0][e] : wv[4][e];
+        }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool keep = bw == 0 ? (4 * g4 + e >= 15 - n16)
-                                      : (bw == 4 ? (64 + 4 * g4 + e <= 78 - n16) : true);
-            if (keep) wbuf[sp_slot(16 * bw + 4 * g4 + e - 15 + n16)] = wv[bw][e];
-          }
+        for (int bw = 1; bw < 4; ++bw)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wbuf[sp_slot(16 * bw + 4 * g4 + e - 15 + n16)] = wv[bw][e];
         // ---- content term on top of the gathered position term ------------------------
 #pragma unroll
         for (int kbk = 0; kbk < 4; ++kbk) {
