@@ -34,6 +34,11 @@
 // are rounded to bf16, so the softmax is exp2(S - max) with no extra multiply.
 #include "txl_internal.h"
 
+#include <algorithm>
+#include <functional>
+#include <mutex>
+#include <vector>
+
 namespace txl {
 namespace {
 
@@ -50,6 +55,9 @@ constexpr int RRING = 4 * BK;   // r ring rows (four 64-distance blocks)
 constexpr int WGF = 16 * 64;    // a wave's S_p buffer (floats): 16 queries x 64 keys
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int NXCD = 8;         // accelerator dies (XCDs), one L2 each
+#ifndef TXL_ATTN_SCHED
+#define TXL_ATTN_SCHED 1
+#endif
 
 // 80 KB: two workgroups fill a CU's 160 KB.
 struct __align__(16) Smem {
@@ -85,6 +93,26 @@ __device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vm
 // Workgroup barrier for LDS written by this workgroup's waves and for the
 // LDS-direct loads each wave has already waited for.
 __device__ inline void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory"); }
+
+// Device-scope (agent) relaxed atomic accesses for the in-kernel merge: coherent
+// across the XCDs' L2s without cache-wide write-back or invalidation.  Pairs of
+// floats go as one 8-byte access, so a wave's 64 lanes cover 512 contiguous
+// bytes (whole lines).
+__device__ inline void st2_coherent(float* p, float x, float y) {
+  const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, x) |
+                     ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float2 ld2_coherent(const float* p) {
+  const uint64_t v = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__builtin_bit_cast(float, (uint32_t)v), __builtin_bit_cast(float, (uint32_t)(v >> 32)));
+}
+__device__ inline void st_coherent_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int atomic_add_coherent(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ inline bf16x8 lds_b128(const uint16_t* p) { return *(const bf16x8*)p; }
 __device__ inline bf16x8 lds_tr2(const uint16_t* p0, const uint16_t* p1) {
@@ -123,17 +151,16 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   // Workgroups are dispatched to the 8 XCDs round-robin by id, and each XCD has
   // its own L2.  Block id n runs on XCD n % 8 as its (n / 8)-th block; XCD x
   // owns the (batch, head) groups g = x, x + 8, ..., so their K, V and r stay in
-  // one L2.  Each XCD first issues the last query tile (the most key tiles) of
-  // all its groups, then the one before, and so on: the long workgroups start
-  // first and the short ones fill the tail.  With a key split, the nsplit
-  // workgroups of one query tile are consecutive.
-  const int nsplit = a.nsplit;
+  // one L2.  Each XCD issues the plan's work classes in order (all its groups of
+  // one class, then the next): the longest parts start first and the short ones
+  // fill the tail.
   const int gpx = (groups + NXCD - 1) / NXCD;  // groups per XCD
   const int xcd = blockIdx.x % NXCD, k_on = blockIdx.x / NXCD;
-  const int slot = k_on / nsplit;
-  const int g = (slot % gpx) * NXCD + xcd;
-  const int qt = nqt - 1 - slot / gpx;
-  const int split = k_on % nsplit;
+  const int cls = k_on / gpx;
+  const int g = (k_on % gpx) * NXCD + xcd;
+  const int qt = a.plan.ncls > 0 ? a.plan.cls_qt[cls] : nqt - 1 - cls;
+  const int part = a.plan.ncls > 0 ? a.plan.cls_part[cls] : 0;
+  const int nparts = a.plan.ncls > 0 ? a.plan.nparts[qt] : 1;
   if (g >= groups) return;
   const int64_t b = g / a.H, hd = g % a.H;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -146,10 +173,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const int cl_max = (int)(a.d_load / 8) - 1;  // last readable 16-byte chunk of a row
 
   // key tiles of this workgroup: all tiles up to the last query's last key,
-  // or this split's share of them
+  // or this part's share of them
   const int imax_wg = (q0 + BQ - 1 < L - 1) ? q0 + BQ - 1 : L - 1;
   const int n_kt = (len + imax_wg) / BK + 1;
-  const int kt_lo = (split * n_kt) / nsplit, kt_hi = ((split + 1) * n_kt) / nsplit;
+  const int kt_lo = (part * n_kt) / nparts, kt_hi = ((part + 1) * n_kt) / nparts;
   const bool wave_has_rows = i0w < L;
   const int imax_w = (i0w + BQW - 1 < L - 1) ? i0w + BQW - 1 : L - 1;
   const int kt_w = wave_has_rows ? (len + imax_w) / BK : -1;
@@ -244,6 +271,23 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   // (that) mod 256; roff[u] is its s = 0 offset, s = 1 is roff[u] ^ 32.
   int roff[6];
 
+  // ---- first tile: K, V and the three r blocks of its window (issued before the
+  //      query loads, so the two global round trips overlap) -----------------------
+  if (kt_lo < kt_hi) {
+    const int j0 = kt_lo * BK;
+    load_kv(kb, sm.K[kt_lo & 1], j0, ko, dch);
+    load_kv(vb, sm.V[kt_lo & 1], j0, vo, dchv);
+#pragma unroll
+    for (int blk = 0; blk < 3; ++blk) load_r(q0 - j0 - BK + BK * blk);
+    // ring offsets of the union blocks for this tile
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int e = i0w - j0 + 31 - 16 * u - n16;
+      const int rr = e & (RRING - 1);
+      roff[u] = rr * DP + 8 * (g4 ^ swz(rr));
+    }
+  }
+
   // ---- this lane's queries, pre-scaled: group gm holds query i0w + 16 gm + n16,
   //      k-step s columns 32 s + 8 g4 .. + 7 ---------------------------------------------
   bf16x8 qc[2][2], qp[2][2];
@@ -305,22 +349,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 
   float* srow_base = nullptr;
   if (a.scores) srow_base = a.scores + ((b * a.H + hd) * a.L) * (int64_t)T;
-
-  // ---- first tile: K, V and the three r blocks of its window -----------------------------
-  if (kt_lo < kt_hi) {
-    const int j0 = kt_lo * BK;
-    load_kv(kb, sm.K[kt_lo & 1], j0, ko, dch);
-    load_kv(vb, sm.V[kt_lo & 1], j0, vo, dchv);
-#pragma unroll
-    for (int blk = 0; blk < 3; ++blk) load_r(q0 - j0 - BK + BK * blk);
-    // ring offsets of the union blocks for this tile
-#pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int e = i0w - j0 + 31 - 16 * u - n16;
-      const int rr = e & (RRING - 1);
-      roff[u] = rr * DP + 8 * (g4 ^ swz(rr));
-    }
-  }
 
   // One barrier per tile.  At the top of tile kt every wave has waited for its
   // own loads of tile kt, and the barrier makes them visible and retires tile
@@ -461,9 +489,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
         if (move) lim[gm] = TAU;
       }
     }
-    bf16x8 pb[2][2];
+    // ---- P = exp2(S - s_off) packed to bf16, and O^T += V^T . P^T.  The V^T
+    //      fragments do not depend on P, so their reads go out before the
+    //      exponentials; group 1's exponentials are interleaved with group 0's
+    //      products (the hints below), so the vector unit and the matrix core
+    //      work at the same time within this wave.  Raised issue priority while
+    //      this wave feeds the matrix core. ---------------------------------------------
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8 vf[2][4];
 #pragma unroll
-    for (int gm = 0; gm < 2; ++gm) {
+    for (int db = 0; db < 4; ++db) vf[0][db] = lds_tr2(Vt + voff[db], Vt + 16 * DP + voff[db]);
+    bf16x8 pb[2][2];
+    auto exp_pack = [&](int gm) {
 #pragma unroll
       for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
@@ -478,25 +515,126 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
         const uint4 pk = make_uint4(w0, w1, w2, w3);
         pb[gm][h] = __builtin_bit_cast(bf16x8, pk);
       }
-    }
-
-    // ---- O^T += V^T . P^T (raised issue priority: while this wave feeds the
-    //      matrix core, the other waves' vector work waits) ------------------------------
-    __builtin_amdgcn_s_setprio(1);
+    };
+    exp_pack(0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 vf[4];
+    for (int db = 0; db < 4; ++db)
+      vf[1][db] = lds_tr2(Vt + 32 * DP + voff[db], Vt + 48 * DP + voff[db]);
+    exp_pack(1);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        vf[db] = lds_tr2(Vt + (32 * h) * DP + voff[db], Vt + (32 * h + 16) * DP + voff[db]);
+    for (int gm = 0; gm < 2; ++gm)
 #pragma unroll
-      for (int gm = 0; gm < 2; ++gm) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) acc[gm][db] = mfma(vf[db], pb[gm][h], acc[gm][db]);
+        for (int db = 0; db < 4; ++db) acc[gm][db] = mfma(vf[h][db], pb[gm][h], acc[gm][db]);
         acc_l[gm] = mfma(ones, pb[gm][h], acc_l[gm]);
       }
+#if TXL_ATTN_SCHED
+    // schedule: group 0's exponentials and packing, then each of group 0's ten
+    // products followed by up to three of group 1's vector instructions, then
+    // group 1's products
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // V reads, half 0
+    __builtin_amdgcn_sched_group_barrier(0x402, 24, 0);   // exp + pack, group 0
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // V reads, half 1
+#pragma unroll
+    for (int x = 0; x < 10; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+#endif
     __builtin_amdgcn_s_setprio(0);
+  }
+
+  // ---- a part of a split query tile writes its unnormalised state (acc, its
+  //      reference and row sum) in one block per (slot, group), laid out by lane
+  //      so that each access covers whole lines:
+  //        acc  [wave][gm][db][pair][lane] x 2 floats (pair 0: elements 0, 1)
+  //        m, l [wave][gm][n16] x 2 floats
+  //      With plan.ext_merge, attn_part_merge_kernel merges the parts.  Otherwise
+  //      the stores are device-coherent (they bypass the XCDs' separate L2s);
+  //      once they have completed (vmcnt 0) the workgroup counts itself in, and
+  //      the part that arrives last reads the others back with device-coherent
+  //      loads and merges them into its own state before the normal epilogue:
+  //        acc = sum_p 2^(m_p - M) acc_p,  l = sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+  //      The part that holds key 0 has a finite reference for every query. ---------
+  float l_tot[2] = {acc_l[0][0], acc_l[1][0]};
+  if (nparts > 1) {
+    const int64_t slot0 = a.plan.slot0[qt];
+    auto pacc = [&](int p) { return a.part_acc + ((slot0 + p) * groups + g) * (BQ * DP); };
+    auto pml = [&](int p) { return a.part_ml + ((slot0 + p) * groups + g) * (BQ * 2); };
+    auto aidx = [&](int gm, int db, int pr) {
+      return ((((wave * 2 + gm) * 4 + db) * 2 + pr) * 64 + lane) * 2;
+    };
+    auto midx = [&](int gm) { return ((wave * 2 + gm) * 16 + n16) * 2; };
+    const bool ext = a.plan.ext_merge != 0;
+#pragma unroll
+    for (int gm = 0; gm < 2; ++gm) {
+      s_off[gm] = lim[gm] == -INFINITY ? -INFINITY : s_off[gm];
+      if (!wave_has_rows || i0w + 16 * gm + n16 >= L) continue;
+      float* pa = pacc(part);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          if (ext)
+            *(float2*)(pa + aidx(gm, db, pr)) = make_float2(acc[gm][db][2 * pr], acc[gm][db][2 * pr + 1]);
+          else
+            st2_coherent(pa + aidx(gm, db, pr), acc[gm][db][2 * pr], acc[gm][db][2 * pr + 1]);
+        }
+      if (g4 == 0) {
+        if (ext)
+          *(float2*)(pml(part) + midx(gm)) = make_float2(s_off[gm], l_tot[gm]);
+        else
+          st2_coherent(pml(part) + midx(gm), s_off[gm], l_tot[gm]);
+      }
+    }
+    if (ext) return;
+    wait_dma();
+    barrier();  // (every wave is past its last tile: the S_p buffers are free)
+    volatile int* flag = (volatile int*)&sm.W[0][0];
+    if (tid == 0) *flag = atomic_add_coherent(a.part_cnt + (int64_t)g * nqt + qt, 1);
+    barrier();
+    if (*flag != nparts - 1) return;
+    if (tid == 0) st_coherent_i(a.part_cnt + (int64_t)g * nqt + qt, 0);
+#pragma unroll
+    for (int gm = 0; gm < 2; ++gm) {
+      if (!wave_has_rows || i0w + 16 * gm + n16 >= L) continue;
+      // four parts per batch: all their loads are in flight before the first use
+      for (int p0 = 0; p0 < nparts; p0 += 4) {
+        float2 ml[4], av[4][4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int p = p0 + j;
+          if (p >= nparts || p == part) continue;
+          const float* pa = pacc(p);
+          // (m, l) sit in the lanes with g4 == 0; every lane of a query reads them
+          ml[j] = ld2_coherent(pml(p) + midx(gm));
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) av[j][db][pr] = ld2_coherent(pa + aidx(gm, db, pr));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int p = p0 + j;
+          if (p >= nparts || p == part) continue;
+          const float M = fmaxf(s_off[gm], ml[j].x);
+          const float Mu = M == -INFINITY ? 0.f : M;
+          const float a_own = __builtin_amdgcn_exp2f(s_off[gm] - Mu);
+          const float a_p = __builtin_amdgcn_exp2f(ml[j].x - Mu);
+          l_tot[gm] = l_tot[gm] * a_own + ml[j].y * a_p;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+              acc[gm][db][2 * pr] = acc[gm][db][2 * pr] * a_own + av[j][db][pr].x * a_p;
+              acc[gm][db][2 * pr + 1] = acc[gm][db][2 * pr + 1] * a_own + av[j][db][pr].y * a_p;
+            }
+          s_off[gm] = M;
+        }
+      }
+    }
   }
 
   // ---- epilogue: out[i][c] = acc / l, lane (g4, n16) of block db holds query
@@ -504,22 +642,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   if (!wave_has_rows) return;
 #pragma unroll
   for (int gm = 0; gm < 2; ++gm) {
-    const float l_tot = acc_l[gm][0];
     const int i = i0w + 16 * gm + n16;
     if (i >= L) continue;
-    if (nsplit > 1) {
-      // unnormalised partial of this split: acc (all 64 columns), max and sum
-      const int64_t row = ((int64_t)split * groups + g) * a.L + i;
-      float* pa = a.part_acc + row * DP;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) *(f32x4*)(pa + 16 * db + 4 * g4) = acc[gm][db];
-      if (g4 == 0) {
-        a.part_ml[2 * row] = lim[gm] == -INFINITY ? -INFINITY : s_off[gm];
-        a.part_ml[2 * row + 1] = l_tot;
-      }
-      continue;
-    }
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / l_tot[gm];
     uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
     const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
                      ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
@@ -539,50 +664,292 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   }
 }
 
-// Log-sum-exp merge of the key splits of one (query, batch*head) per wavefront:
-//   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
-// Split 0 holds key 0, visible to every query, so M is finite.
-__global__ __launch_bounds__(64) void attn_split_merge_kernel(AttnArgs a) {
-  const int64_t i = blockIdx.x, g = blockIdx.y;
-  const int c = threadIdx.x;
-  const int64_t G = a.B * a.H;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * ((s * G + g) * a.L + i)]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t row = (s * G + g) * a.L + i;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * row] - M);
-    den += w * a.part_ml[2 * row + 1];
-    num += w * a.part_acc[row * DP + c];
+// Merge of the parts of a split query tile: one workgroup per (query tile,
+// group) whose 256 threads take the writing lanes' places (wave w, lane (g4,
+// n16) holds query 32 w + 16 gm + n16, columns 16 db + 4 g4 .. + 3), so every
+// load covers whole lines:
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// The part that holds key 0 has a finite reference for every query.
+__global__ __launch_bounds__(256) void attn_part_merge_kernel(AttnArgs a) {
+  const int qt = blockIdx.x, g = blockIdx.y;
+  const int np = a.plan.nparts[qt];
+  if (np <= 1) return;
+  const int64_t groups = a.B * a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int d = (int)a.d, L = (int)a.L;
+  const int64_t b = g / a.H, hd = g % a.H;
+  const int64_t blk0 = (int64_t)a.plan.slot0[qt] * groups + g;
+#pragma unroll 1
+  for (int gm = 0; gm < 2; ++gm) {
+    const int i = qt * BQ + wave * BQW + 16 * gm + n16;
+    if (i >= L) continue;
+    const int moff = ((wave * 2 + gm) * 16 + n16) * 2;
+    // references and sums of every part (at most 16), one round trip
+    float2 ml[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+      ml[p] = p < np ? *(const float2*)(a.part_ml + (blk0 + p * groups) * (BQ * 2) + moff)
+                     : make_float2(-INFINITY, 0.f);
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) M = fmaxf(M, ml[p].x);
+    float wgt[16], den = 0.f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      wgt[p] = p < np ? __builtin_amdgcn_exp2f(ml[p].x - M) : 0.f;
+      den += wgt[p] * ml[p].y;
+    }
+    float o[4][4] = {};
+#pragma unroll
+    for (int p0 = 0; p0 < 16; p0 += 8) {
+      if (p0 >= np) break;
+      float2 av[8][4][2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int p = p0 + j;
+        const float* pa = a.part_acc + (blk0 + (int64_t)p * groups) * (BQ * DP);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+            av[j][db][pr] = p < np ? *(const float2*)(pa + ((((wave * 2 + gm) * 4 + db) * 2 + pr) * 64 + lane) * 2)
+                                   : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            o[db][2 * pr] += wgt[p0 + j] * av[j][db][pr].x;
+            o[db][2 * pr + 1] += wgt[p0 + j] * av[j][db][pr].y;
+          }
+    }
+    const float inv = 1.f / den;
+    uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
+    const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
+                     ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int c = 16 * db + 4 * g4;
+      if (vec) {
+        if (c < d)
+          *(uint2*)(orow + c) = make_uint2(pack2(o[db][0] * inv, o[db][1] * inv),
+                                           pack2(o[db][2] * inv, o[db][3] * inv));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < d) orow[c + e] = bf16_bits(o[db][e] * inv);
+      }
+    }
   }
-  if (c < a.d) {
-    const int64_t b = g / a.H, hd = g % a.H;
-    uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + i * a.o_st + hd * a.o_sh;
-    orow[c] = bf16_bits(num / den);
-  }
+}
+
+// Clears the in-kernel merge's counters before a launch (a kernel, not a memset,
+// so the launch sequence may be captured in a graph).
+__global__ __launch_bounds__(256) void attn_cnt_clear_kernel(int* cnt, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) cnt[i] = 0;
 }
 
 }  // namespace
 
-int attn_mfma_plan_splits(const AttnArgs& a, int num_cus) {
-  // split the keys only when the query tiles cannot give every CU two workgroups
-  const int64_t nqt = (a.L + BQ - 1) / BQ;
-  const int64_t base = nqt * a.B * a.H;
-  if (base >= 2LL * num_cus) return 1;
-  const int64_t imax0 = (BQ - 1 < a.L - 1) ? BQ - 1 : a.L - 1;
-  const int64_t tiles0 = (a.mem_len + imax0) / BK + 1;  // fewest tiles of any query tile
-  int64_t ns = (2LL * num_cus + base - 1) / base;
-  // at least two key tiles per split: with one, each workgroup's fixed start-up
-  // (q, u, v and the first tile) outweighs its work
-  if (ns > tiles0 / 2) ns = tiles0 / 2;
-  if (ns > 16) ns = 16;
-  return ns < 2 ? 1 : (int)ns;
+// ---- work plan ---------------------------------------------------------------------------
+// Workgroups of one XCD run on its CUs two at a time and start in id order, so
+// the kernel's time is the longest chain of work one workgroup slot receives.
+// The plan splits the key axis of some query tiles into parts (each part costs
+// a fixed start-up, the partial write and the merge, PART_COST tiles) so that
+// a greedy list schedule of the parts, longest first, over the XCD's slots ends
+// early.  The planner starts from no split and keeps taking the single change
+// (one more part for one query tile) that shortens the simulated schedule most.
+namespace {
+
+#ifndef TXL_PART_COST
+#define TXL_PART_COST 2.0
+#endif
+constexpr double PART_COST = TXL_PART_COST;
+
+struct PlanShape {
+  int nqt, gpx, slots;
+  int n_kt[ATTN_MAXQT];
+};
+
+double plan_makespan(const PlanShape& sh, const int* k, std::vector<double>& sizes,
+                     std::vector<double>& heap) {
+  sizes.clear();
+  for (int t = 0; t < sh.nqt; ++t)
+    for (int p = 0; p < k[t]; ++p) {
+      const int lo = p * sh.n_kt[t] / k[t], hi = (p + 1) * sh.n_kt[t] / k[t];
+      sizes.push_back((hi - lo) + (k[t] > 1 ? PART_COST : 0.0));
+    }
+  std::sort(sizes.begin(), sizes.end(), [](double x, double y) { return x > y; });
+  heap.assign(sh.slots, 0.0);  // min-heap of slot finish times
+  for (double sz : sizes)
+    for (int gi = 0; gi < sh.gpx; ++gi) {
+      std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+      heap.back() += sz;
+      std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+    }
+  return *std::max_element(heap.begin(), heap.end());
 }
 
-size_t attn_split_bytes(const AttnArgs& a, int nsplit) {
-  if (nsplit <= 1) return 0;
-  const size_t rows = (size_t)nsplit * (size_t)(a.B * a.H) * (size_t)a.L;
-  return rows * DP * sizeof(float) + rows * 2 * sizeof(float) + 256;
+}  // namespace
+
+AttnPlan plan_uncached(const AttnArgs& a, int num_cus, size_t budget);
+
+// Plans are cached per shape (the search costs far more than a launch).
+AttnPlan attn_mfma_plan(const AttnArgs& a, int num_cus, size_t budget) {
+  struct Entry { int64_t groups, L, mem_len; int cus; size_t budget; AttnPlan plan; };
+  static std::mutex mu;
+  static Entry cache[16];
+  static int n_cached = 0, next = 0;
+  const int64_t groups = a.B * a.H;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cached; ++i) {
+      const Entry& e = cache[i];
+      if (e.groups == groups && e.L == a.L && e.mem_len == a.mem_len && e.cus == num_cus &&
+          e.budget == budget)
+        return e.plan;
+    }
+  }
+  const AttnPlan p = plan_uncached(a, num_cus, budget);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[next] = {groups, a.L, a.mem_len, num_cus, budget, p};
+  next = (next + 1) % 16;
+  if (n_cached < 16) ++n_cached;
+  return p;
+}
+
+AttnPlan plan_uncached(const AttnArgs& a, int num_cus, size_t budget) {
+  AttnPlan p{};
+  const int64_t nqt = (a.L + BQ - 1) / BQ;
+  const int64_t groups = a.B * a.H;
+  if (nqt > ATTN_MAXQT || groups <= 0) return p;  // default order, no split
+  PlanShape sh{};
+  sh.nqt = (int)nqt;
+  sh.gpx = (int)((groups + NXCD - 1) / NXCD);
+  sh.slots = num_cus * 2 / NXCD > 0 ? num_cus * 2 / NXCD : 1;
+  for (int t = 0; t < sh.nqt; ++t) {
+    const int64_t imax = (int64_t)t * BQ + BQ - 1 < a.L - 1 ? (int64_t)t * BQ + BQ - 1 : a.L - 1;
+    sh.n_kt[t] = (int)((a.mem_len + imax) / BK + 1);
+  }
+  int k[ATTN_MAXQT];
+  for (int t = 0; t < sh.nqt; ++t) k[t] = 1;
+  auto bytes_of = [&](const int* kk) {
+    int slots = 0, ncls = 0;
+    for (int t = 0; t < sh.nqt; ++t) {
+      ncls += kk[t];
+      if (kk[t] > 1) slots += kk[t];
+    }
+    if (ncls > ATTN_MAXCLS || slots > 255) return (size_t)-1;
+    const size_t rows = (size_t)slots * (size_t)groups * BQ;
+    return slots ? rows * (DP + 2) * sizeof(float) + (size_t)groups * nqt * sizeof(int) + 768
+                 : (size_t)0;
+  };
+  // Descent: each step takes the change (one more part for one query tile) that
+  // shortens the simulated schedule most, or, when none does, splits the tile
+  // with the longest parts further (the schedule may need several tiles split
+  // before it shortens).  The best plan met on the way wins; a plan replaces a
+  // smaller one only for a clear gain.
+  std::vector<double> sizes, heap;
+  double cur = plan_makespan(sh, k, sizes, heap), best = cur;
+  int best_k[ATTN_MAXQT];
+  for (int t = 0; t < sh.nqt; ++t) best_k[t] = k[t];
+  auto can_split = [&](int t, int kk) {
+    if (kk > 16 || kk > sh.n_kt[t] / 2) return false;
+    const int keep = k[t];
+    k[t] = kk;
+    const bool ok = bytes_of(k) <= budget;
+    k[t] = keep;
+    return ok;
+  };
+  for (int step = 0; step < ATTN_MAXCLS; ++step) {
+    int bt = -1;
+    double bm = cur;
+    for (int t = 0; t < sh.nqt; ++t) {
+      if (!can_split(t, k[t] + 1)) continue;
+      ++k[t];
+      const double m = plan_makespan(sh, k, sizes, heap);
+      --k[t];
+      if (m < bm) {
+        bm = m;
+        bt = t;
+      }
+    }
+    if (bt < 0) {  // no single change helps: split the longest parts further
+      int longest = 0;
+      for (int t = 0; t < sh.nqt; ++t) {
+        const int part = (sh.n_kt[t] + k[t] - 1) / k[t];
+        if (can_split(t, k[t] + 1) && part > longest) {
+          longest = part;
+          bt = t;
+        }
+      }
+      if (bt < 0) break;
+      ++k[bt];
+      bm = plan_makespan(sh, k, sizes, heap);
+    } else {
+      ++k[bt];
+    }
+    cur = bm;
+    if (cur < best * 0.99) {
+      best = cur;
+      for (int t = 0; t < sh.nqt; ++t) best_k[t] = k[t];
+    }
+  }
+  for (int t = 0; t < sh.nqt; ++t) k[t] = best_k[t];
+  // class list: parts longest first (ties: later query tile first), slots of split tiles
+  struct Cls { int sz, qt, part; };
+  std::vector<Cls> cl;
+  int slot = 0;
+  for (int t = 0; t < sh.nqt; ++t) {
+    p.nparts[t] = (uint8_t)k[t];
+    p.slot0[t] = (uint8_t)(k[t] > 1 ? slot : 0);
+    if (k[t] > 1) slot += k[t];
+    for (int q = 0; q < k[t]; ++q) {
+      const int lo = q * sh.n_kt[t] / k[t], hi = (q + 1) * sh.n_kt[t] / k[t];
+      cl.push_back({hi - lo, t, q});
+    }
+  }
+  std::stable_sort(cl.begin(), cl.end(), [](const Cls& x, const Cls& y) {
+    return x.sz != y.sz ? x.sz > y.sz : x.qt > y.qt;
+  });
+  p.ncls = slot > 0 ? (int)cl.size() : 0;  // no split: the kernel's own order, same list
+  p.slots = slot;
+  // Many parts per tile: the last part would merge them one batch after another
+  // at the end of its own work; a second kernel reads them all at once.
+  int kmax = 1;
+  for (int t = 0; t < sh.nqt; ++t) kmax = k[t] > kmax ? k[t] : kmax;
+  p.ext_merge = kmax > 4 ? 1 : 0;
+  for (int c = 0; c < p.ncls; ++c) {
+    p.cls_qt[c] = (uint8_t)cl[c].qt;
+    p.cls_part[c] = (uint8_t)cl[c].part;
+  }
+  return p;
+}
+
+size_t attn_plan_bytes(const AttnArgs& a, const AttnPlan& p) {
+  if (p.slots <= 0) return 0;
+  const size_t groups = (size_t)(a.B * a.H), nqt = (size_t)((a.L + BQ - 1) / BQ);
+  const size_t rows = (size_t)p.slots * groups * BQ;
+  return rows * (DP + 2) * sizeof(float) + groups * nqt * sizeof(int) + 768;
+}
+
+void attn_plan_bind(AttnArgs& a, const AttnPlan& p, void* scratch) {
+  a.plan = p;
+  a.part_acc = nullptr;
+  a.part_ml = nullptr;
+  a.part_cnt = nullptr;
+  if (p.slots <= 0) return;
+  const size_t groups = (size_t)(a.B * a.H);
+  const size_t rows = (size_t)p.slots * groups * BQ;
+  char* base = (char*)(((uintptr_t)scratch + 255) & ~(uintptr_t)255);
+  a.part_acc = (float*)base;
+  base += (rows * DP * sizeof(float) + 255) & ~(size_t)255;
+  a.part_ml = (float*)base;
+  base += (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
+  a.part_cnt = (int*)base;
 }
 
 bool attn_mfma_supported(const AttnArgs& a) {
@@ -604,8 +971,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
   (void)num_cus;
   const int nqt = (int)((a.L + BQ - 1) / BQ);
   const int groups = (int)(a.B * a.H);
-  const int nsplit = a.nsplit > 1 ? a.nsplit : 1;
-  const int64_t nblocks = (int64_t)nqt * nsplit * NXCD * ((groups + NXCD - 1) / NXCD);
+  const int ncls = a.plan.ncls > 0 ? a.plan.ncls : nqt;
+  const int64_t nblocks = (int64_t)ncls * NXCD * ((groups + NXCD - 1) / NXCD);
   const size_t smem = sizeof(Smem);
   static bool attr_set = false;
   if (!attr_set) {
@@ -614,14 +981,22 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  AttnArgs aa = a;
-  aa.nsplit = nsplit;
-  hipLaunchKernelGGL(attn_mfma_kernel, dim3((unsigned)nblocks), dim3(256), smem, s, aa, nqt,
+  if (a.plan.slots > 0) {
+    if (!a.part_acc || !a.part_ml || !a.part_cnt) return hipErrorInvalidValue;
+    if (!a.plan.ext_merge) {
+      const int n = groups * nqt;
+      const int nb = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+      hipLaunchKernelGGL(attn_cnt_clear_kernel, dim3((unsigned)nb), dim3(256), 0, s, a.part_cnt, n);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL(attn_mfma_kernel, dim3((unsigned)nblocks), dim3(256), smem, s, a, nqt,
                      groups);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_split_merge_kernel, dim3((unsigned)a.L, (unsigned)groups), dim3(64),
-                     0, s, aa);
+  if (e != hipSuccess || a.plan.slots == 0 || !a.plan.ext_merge) return e;
+  hipLaunchKernelGGL(attn_part_merge_kernel, dim3((unsigned)nqt, (unsigned)groups), dim3(256), 0,
+                     s, a);
   return hipGetLastError();
 }
 

@@ -138,10 +138,10 @@ int check_attn(int dtype, const txl::AttnArgs& a, int64_t r_rows) {
   return TXL_OK;
 }
 
-// Splits of the key axis the matrix-core attention would use (1 = none).
-int attn_plan(int dtype, const txl::AttnArgs& a) {
-  if (dtype != TXL_BF16 || !txl::attn_mfma_supported(a)) return 1;
-  return txl::attn_mfma_plan_splits(a, num_cus());
+// Bytes of key-split partials the matrix-core attention's plan needs (0 = none).
+size_t attn_plan_bytes(int dtype, const txl::AttnArgs& a) {
+  if (dtype != TXL_BF16 || !txl::attn_mfma_supported(a)) return 0;
+  return txl::attn_plan_bytes(a, txl::attn_mfma_plan(a, num_cus(), (size_t)-1));
 }
 
 // Bytes of key-split partials the layer step's attention needs at this memory length.
@@ -154,7 +154,7 @@ size_t layer_part_bytes(const txl_layer_dims& dm, int64_t mem_len, int dtype) {
   a.q_sb = dm.n_head * dm.L * dp; a.q_st = dp; a.q_sh = dm.L * dp;
   a.kv_sb = dm.n_head * T * dp; a.kv_st = dp; a.kv_sh = T * dp;
   a.r_sp = dp; a.r_sh = T * dp;
-  return txl::attn_split_bytes(a, attn_plan(dtype, a));
+  return attn_plan_bytes(dtype, a);
 }
 
 // Runs the attention; scratch (may be NULL) holds the key-split partials when
@@ -166,18 +166,10 @@ int run_attn(int dtype, txl::AttnArgs a, void* scratch, size_t scratch_bytes, hi
     e = txl::launch_fill_f32(a.scores, a.B * a.H * a.L * T, -INFINITY, st);
     if (e != hipSuccess) return hip_fail(e, "scores fill");
   }
-  a.nsplit = 1;
-  a.part_acc = nullptr;
-  a.part_ml = nullptr;
   if (dtype == TXL_BF16 && txl::attn_mfma_supported(a)) {
-    const int ns = attn_plan(dtype, a);
-    if (ns > 1 && scratch && scratch_bytes >= txl::attn_split_bytes(a, ns)) {
-      const size_t rows = (size_t)ns * (size_t)(a.B * a.H) * (size_t)a.L;
-      char* base = (char*)(((uintptr_t)scratch + 255) & ~(uintptr_t)255);
-      a.nsplit = ns;
-      a.part_acc = (float*)base;
-      a.part_ml = (float*)(base + rows * 64 * sizeof(float));
-    }
+    // the best plan whose partials fit the scratch (none: no split)
+    const txl::AttnPlan plan = txl::attn_mfma_plan(a, num_cus(), scratch ? scratch_bytes : 0);
+    txl::attn_plan_bind(a, plan, scratch);
     e = txl::launch_attn_mfma(a, num_cus(), st);
   } else {
     e = txl::launch_attn_generic(dtype, a, st);
@@ -285,7 +277,6 @@ int txl_rel_attn_fwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
   a.out = out; a.o_sb = o_sb; a.o_st = o_st; a.o_sh = o_sh;
   a.scores = scores_dbg;
   a.d_load = d_head;
-  a.nsplit = 1;
   const int rc = check_attn(dtype, a, r_rows);
   if (rc != TXL_OK) return rc;
   if (workspace) {
@@ -313,8 +304,7 @@ size_t txl_rel_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L, 
   // the plan depends only on the shapes; layouts are taken as aligned head-major
   a.q = a.k = a.v = a.r = (const void*)(uintptr_t)256;
   a.q_sb = a.q_st = a.q_sh = a.kv_sb = a.kv_st = a.kv_sh = a.r_sp = a.r_sh = 64;
-  const int ns = attn_plan(dtype, a);
-  return txl::attn_split_bytes(a, ns);
+  return attn_plan_bytes(dtype, a);
 }
 
 size_t txl_layer_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype) {

@@ -32,6 +32,21 @@ template <> struct Elt<uint16_t> {
 };
 
 // ---- attention ---------------------------------------------------------------------
+// Work plan of the matrix-core attention.  Query tile t (128 queries) of every
+// (batch, head) group has its key tiles divided among nparts[t] workgroups.  The
+// work classes (query tile cls_qt[c], part cls_part[c]) are issued in list order
+// (longest first) for all groups of an XCD before the next class.  ncls == 0
+// means one part per query tile, last tile first.
+constexpr int ATTN_MAXQT = 64, ATTN_MAXCLS = 192;
+struct AttnPlan {
+  int ncls;
+  int slots;                       // partial slots (sum of nparts over split tiles)
+  int ext_merge;                   // 1: a second kernel merges the parts, 0: the last part
+  uint8_t cls_qt[ATTN_MAXCLS], cls_part[ATTN_MAXCLS];
+  uint8_t nparts[ATTN_MAXQT];
+  uint8_t slot0[ATTN_MAXQT];       // first partial slot of a split tile's parts
+};
+
 struct AttnArgs {
   int64_t B, H, L, mem_len, d;
   const void* q; int64_t q_sb, q_st, q_sh;
@@ -45,14 +60,17 @@ struct AttnArgs {
   // caller-owned tensors; the layer step's own workspace rows are padded to a
   // multiple of 8 and may be read whole (columns >= d are ignored).
   int64_t d_load;
-  // Split over keys (matrix-core path only): 1 = off.  With nsplit > 1 each
-  // query tile's key tiles are divided among nsplit workgroups that write
-  // unnormalised partials, merged afterwards:
-  //   part_acc [nsplit][B*H][L][64] fp32, part_ml [nsplit][B*H][L][2] fp32 (max in
-  //   the exp2 domain, sum of exponentials).
-  int nsplit;
+  // Split of the key axis (matrix-core path only), see AttnPlan.  Parts of a
+  // split query tile write unnormalised partials; a second kernel merges them
+  // (plan.ext_merge), or the part that finishes last, counted in part_cnt.
+  // Slot s of the plan holds, per (batch, head) group, a block of
+  //   part_acc: 128 queries x 64 fp32, part_ml: 128 x 2 fp32 (max in the exp2
+  //   domain, sum of exponentials), in the writing lanes' order.
+  // part_cnt [B*H][query tiles] is cleared before the launch and left zero.
+  AttnPlan plan;
   float* part_acc;
   float* part_ml;
+  int* part_cnt;
   // Keys as a ring: when kv_cap > 0, key j (0 <= j < mem_len + L <= kv_cap) is
   // row (kv_start + j) % kv_cap of k and v (0 <= kv_start < kv_cap).
   int64_t kv_start, kv_cap;
@@ -65,10 +83,13 @@ __host__ __device__ inline int64_t kv_row(const AttnArgs& a, int64_t j) {
   return p >= a.kv_cap ? p - a.kv_cap : p;
 }
 
-// Number of key splits the matrix-core attention would use for these shapes on
-// a device with num_cus CUs (1 = no split), and the partials' bytes it needs.
-int attn_mfma_plan_splits(const AttnArgs& a, int num_cus);
-size_t attn_split_bytes(const AttnArgs& a, int nsplit);
+// Work plan of the matrix-core attention for these shapes on a device with
+// num_cus CUs whose partials (and counters) fit in budget bytes, and the bytes a
+// plan needs (0 when it splits nothing).
+AttnPlan attn_mfma_plan(const AttnArgs& a, int num_cus, size_t budget);
+size_t attn_plan_bytes(const AttnArgs& a, const AttnPlan& p);
+// Points a's partial buffers into scratch (256-byte aligned inside it).
+void attn_plan_bind(AttnArgs& a, const AttnPlan& p, void* scratch);
 
 // Any strides, d <= 128, fp32 math.  dtype 0 = fp32, 1 = bf16.
 hipError_t launch_attn_generic(int dtype, const AttnArgs& a, hipStream_t s);
