@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--workload", default="charlm")
     p.add_argument("--attn-reps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--main-only", action="store_true",
+                   help="skip the cached-K/V stack and the feed-forward timing (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--eval-speed", action="store_true",
@@ -375,11 +377,12 @@ def main():
 
     # the same stack with cached keys and values (txl_layer_step_kv): each layer's
     # ring is filled from its initial memory first (untimed), then the segments run
-    kv_ms = kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, args.steps, args.warmup, stream)
+    kv_ms = None if args.main_only else kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, args.steps,
+                                                    args.warmup, stream)
 
     # the position-wise feed-forward (not part of the step above) at the same rows,
     # d_inner = 4 d_model
-    ff = pos_ff_time(w, args.attn_reps, stream)
+    ff = None if args.main_only else pos_ff_time(w, args.attn_reps, stream)
 
     tokens = w.B * w.L * w.n_segments
     step_flops = layer_flops(w) * w.n_layers * w.n_segments
@@ -405,13 +408,14 @@ def main():
                      "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic(),
                      "launch_us": attn_s * 1e6, "flop_per_launch": af},
         "step_tflops": step_flops / (ms / 1e3) / 1e12,
-        "pos_ff": ff,
-        "eval_kv_cache": {
+    }
+    if not args.main_only:
+        res["pos_ff"] = ff
+        res["eval_kv_cache"] = {
             "value": tokens / (kv_ms / 1e3), "unit": "query tokens/s", "ms_per_step": kv_ms,
             "note": "same stack and inputs with cached keys/values (txl_layer_step_kv): only "
                     "the L new rows are projected per segment, r is projected once; outputs "
-                    "equal the step above up to rounding"},
-    }
+                    "equal the step above up to rounding"}
     if args.calib_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

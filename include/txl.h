@@ -79,13 +79,15 @@ typedef enum { TXL_FP32 = 0, TXL_BF16 = 1 } txl_dtype;
  *                     -INFINITY where masked.  Debug only; it slows the call.
  *   workspace, ws_bytes  NULL/0, or device scratch of at least
  *                     txl_rel_attn_workspace_bytes() bytes (it must not overlap
- *                     any tensor argument).  When the query tiles alone cannot
- *                     fill the GPU (few batch rows and heads, short segments over
- *                     a long memory), the matrix-core path splits the keys among
- *                     several workgroups, keeps their partial softmax states
- *                     here and merges them with a log-sum-exp.  Without enough
- *                     workspace it does not split; the result is the same up
- *                     to rounding.
+ *                     any tensor argument).  When the query tiles alone would
+ *                     leave the GPU unevenly loaded (few batch rows and heads,
+ *                     short segments over a long memory), the matrix-core path
+ *                     splits the keys of some query tiles among several
+ *                     workgroups, keeps their partial softmax states (and
+ *                     arrival counters) here and merges them with a
+ *                     log-sum-exp.  With less workspace it takes the best split
+ *                     that fits, or none; the result is the same up to
+ *                     rounding.  Calls that share a workspace must not overlap.
  *
  * Layouts: any strides with the innermost (c) dimension contiguous are
  * accepted.  bf16 calls whose q/k/v/r base pointers are 16-byte aligned and

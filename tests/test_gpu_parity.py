@@ -178,6 +178,30 @@ def test_attn_key_split(B, H, L, M, d):
     _check_argmax(got_s, ref_s, 5 * TOL["bf16"])
 
 
+@pytest.mark.parametrize("B,H,L,M,d,frac", [
+    (1, 3, 200, 333, 48, 2),     # parts merged by the last part
+    (1, 2, 128, 1600, 64, 3),    # parts merged by the merge kernel
+    (1, 2, 128, 1600, 64, 1000), # too small for any split: one part per tile
+])
+def test_attn_key_split_small_workspace(B, H, L, M, d, frac):
+    """A workspace smaller than the shape's query asks for: the plan shrinks to
+    what fits (fewer parts, or none) and the result is unchanged."""
+    txl = _txl()
+    c = I.attention_inputs(B, H, L, M, d, seed=7 * L + M, sigma=1.0, sigma_uv=0.5, dtype="bf16")
+    hm = lambda x: dev(x.transpose(0, 2, 1, 3), "bf16").permute(0, 2, 1, 3)
+    q, k, v = hm(c["q"]), hm(c["k"]), hm(c["v"])
+    r = dev(c["r"].transpose(1, 0, 2), "bf16").permute(1, 0, 2)
+    nbytes = txl.rel_attn_workspace_bytes(torch.bfloat16, B, H, L, M, d)
+    assert nbytes > 0
+    ws = torch.empty(max(nbytes // frac, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device="cuda")
+    _say(f"key split, workspace {ws.numel()} of {nbytes}: B={B} H={H} L={L} M={M} d={d}")
+    txl.rel_attn_fwd(q, k, v, r, dev(c["u"], "bf16"), dev(c["vb"], "bf16"), M, out, workspace=ws)
+    torch.cuda.synchronize()
+    ref = O.rel_attn(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M)
+    assert max_err(host(out), ref) <= TOL["bf16"]
+
+
 def test_attn_argmax_tiny_bf16():
     got, got_s, ref, ref_s = _attn_case("bf16", 1, 2, 16, 16, 16, seed=3, layout="bhtd")
     _check_argmax(got_s, ref_s, 5 * TOL["bf16"])
