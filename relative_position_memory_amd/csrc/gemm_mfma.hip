@@ -291,6 +291,10 @@ __device__ inline void wait_stages(int later) {
 // Barrier that orders LDS accesses for the compiler without waiting for the
 // in-flight LDS-direct loads (each wave waits for its own loads first).
 __device__ inline void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// The same after this wave's own LDS reads have completed.
+__device__ inline void lds_read_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
+}
 
 template <class C, int EPI>
 __global__ __launch_bounds__(C::NT, C::OCC) void gemm_dma_kernel(GemmBatch bt) {
@@ -351,35 +355,49 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_dma_kernel(GemmBatch bt) {
 
     f32x16 acc[C::TJ][C::TI];
     zero_acc<C>(acc);
+    // Fragments of 16-deep half s of stage kt (lane's chunk kc of the 32-deep step).
+    auto frags = [&](int kt, int s, bf16x8 (&wf)[C::TJ], bf16x8 (&af)[C::TI]) {
+      const uint16_t* sa = ring + (kt % C::NS) * C::STAGE;
+      const uint16_t* sw = sa + C::BM * C::DBK;
+      const int kc = 2 * s + lh;
+#pragma unroll
+      for (int j = 0; j < C::TJ; ++j)
+        wf[j] = *(const bf16x8*)&sw[wrow_f[j] * C::DBK + 8 * (kc ^ swz(wrow_f[j]))];
+#pragma unroll
+      for (int i = 0; i < C::TI; ++i)
+        af[i] = *(const bf16x8*)&sa[arow_f[i] * C::DBK + 8 * (kc ^ swz(arow_f[i]))];
+    };
+    auto mfmas = [&](const bf16x8 (&wf)[C::TJ], const bf16x8 (&af)[C::TI]) {
+#pragma unroll
+      for (int j = 0; j < C::TJ; ++j)
+#pragma unroll
+        for (int i = 0; i < C::TI; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+    };
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
       if (s < nk) issue(s);
+    // Every fragment read goes out one half-step ahead of its products, so its
+    // LDS latency hides behind the previous half's MFMAs.  Stage kt + 1 is
+    // waited for and made visible by the barrier in the middle of step kt; the
+    // barrier also retires this wave's reads of stage kt (lgkmcnt 0), whose
+    // buffer the loads of stage kt + 4 then reuse.
+    wait_stages<PER_STAGE>(nk - 1 < C::NS - 2 ? nk - 1 : C::NS - 2);
+    lds_barrier();
+    if (C::NS - 1 < nk) issue(C::NS - 1);
+    bf16x8 wf0[C::TJ], af0[C::TI], wf1[C::TJ], af1[C::TI];
+    frags(0, 0, wf0, af0);
     for (int kt = 0; kt < nk; ++kt) {
-      // this wave's loads of stage kt have landed; the barrier makes every
-      // wave's visible and retires the reads of stage kt - 1, whose buffer
-      // (kt + 3) % 4 the next loads overwrite
-      const int later = nk - 1 - kt < C::NS - 2 ? nk - 1 - kt : C::NS - 2;
-      wait_stages<PER_STAGE>(later);
-      lds_barrier();
-      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1);
-      const uint16_t* sa = ring + (kt % C::NS) * C::STAGE;
-      const uint16_t* sw = sa + C::BM * C::DBK;
-#pragma unroll
-      for (int s = 0; s < C::DBK / 16; ++s) {
-        const int kc = 2 * s + lh;  // this lane's 16-byte chunk of the 32-deep step
-        bf16x8 wf[C::TJ], af[C::TI];
-#pragma unroll
-        for (int j = 0; j < C::TJ; ++j)
-          wf[j] = *(const bf16x8*)&sw[wrow_f[j] * C::DBK + 8 * (kc ^ swz(wrow_f[j]))];
-#pragma unroll
-        for (int i = 0; i < C::TI; ++i)
-          af[i] = *(const bf16x8*)&sa[arow_f[i] * C::DBK + 8 * (kc ^ swz(arow_f[i]))];
-#pragma unroll
-        for (int j = 0; j < C::TJ; ++j)
-#pragma unroll
-          for (int i = 0; i < C::TI; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[j][i], 0, 0, 0);
+      frags(kt, 1, wf1, af1);
+      mfmas(wf0, af0);
+      if (kt + 1 < nk) {
+        const int later = nk - 2 - kt < C::NS - 2 ? nk - 2 - kt : C::NS - 2;
+        wait_stages<PER_STAGE>(later);
+        lds_read_barrier();
+        if (kt + C::NS < nk) issue(kt + C::NS);
+        frags(kt + 1, 0, wf0, af0);
       }
+      mfmas(wf1, af1);
     }
     __syncthreads();  // all fragment reads done before the epilogue reuses LDS
     epilogue<C, EPI>(g, m0, n0, smem_raw, acc, tid, wm, wn, li, lh);
