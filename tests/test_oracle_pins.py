@@ -369,3 +369,108 @@ def test_pos_ff_closed_gate_adds_only_the_output_bias(oracle):
     out = oracle.pos_ff(x, W1, np.full(11, -1e6), W2, b2, np.ones(7), np.zeros(7), 1e-5)
     np.testing.assert_allclose(out, oracle.layer_norm(x + b2, np.ones(7), np.zeros(7), 1e-5),
                                rtol=0, atol=1e-12)
+
+
+# --- backward (training step with a stop-gradient memory) ---------------------------
+# Pins of oracle_bwd: central finite differences of the forward oracle along
+# random directions (brute force, fp64), a closed form for the value gradient,
+# and the memory's stopped gradient.
+
+def _fd(f, x, direction, eps=1e-5):
+    return (f(x + eps * direction) - f(x - eps * direction)) / (2 * eps)
+
+
+@pytest.mark.parametrize("B,H,L,M,d", [(2, 2, 3, 2, 4), (1, 3, 4, 0, 5), (1, 1, 5, 6, 3)])
+def test_bwd_attention_matches_finite_differences(oracle, B, H, L, M, d):
+    from oracle import oracle_bwd as OB
+    c = _attn_case(11 * L + M, B, H, L, M, d)
+    rng = np.random.default_rng(7 + d)
+    G = _rand(rng, B, L, H, d)
+    g = OB.rel_attn_bwd(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M, G)
+    names = {"q": "dq", "k": "dk", "v": "dv", "r": "dr", "u": "du", "vb": "dvb"}
+    for x, gx in names.items():
+        V = _rand(rng, *c[x].shape)
+
+        def loss(val, x=x):
+            args = dict(c)
+            args[x] = val
+            out = oracle.rel_attn(args["q"], args["k"], args["v"], args["r"], args["u"],
+                                  args["vb"], M)
+            return float(np.sum(out * G))
+
+        fd = _fd(loss, c[x], V)
+        an = float(np.sum(g[gx] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (x, fd, an)
+
+
+def test_bwd_value_gradient_sums_to_the_output_gradient(oracle):
+    """The softmax rows sum to one, so the value gradients of one (batch, head)
+    sum to the sum of the output gradients over its queries."""
+    from oracle import oracle_bwd as OB
+    B, H, L, M, d = 2, 2, 4, 3, 5
+    c = _attn_case(5, B, H, L, M, d)
+    G = _rand(np.random.default_rng(3), B, L, H, d)
+    g = OB.rel_attn_bwd(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M, G)
+    np.testing.assert_allclose(g["dv"].sum(axis=1), G.sum(axis=1), rtol=1e-12, atol=1e-12)
+
+
+def _layer_case(seed, B, L, M, D, H, d):
+    rng = np.random.default_rng(seed)
+    W = {"W_q": _rand(rng, H * d, D, s=0.3), "W_kE": _rand(rng, H * d, D, s=0.3),
+         "W_v": _rand(rng, H * d, D, s=0.3), "W_kR": _rand(rng, H * d, D, s=0.3),
+         "W_o": _rand(rng, D, H * d, s=0.3), "gamma": 1.0 + _rand(rng, D, s=0.2),
+         "beta": _rand(rng, D, s=0.2)}
+    return dict(h=_rand(rng, B, L, D), mem=_rand(rng, B, M, D), W=W,
+                u=_rand(rng, H, d, s=0.3), vb=_rand(rng, H, d, s=0.3), R=_rand(rng, M + L, D))
+
+
+@pytest.mark.parametrize("B,L,M,D,H,d", [(1, 3, 2, 8, 2, 4), (2, 2, 0, 6, 1, 3)])
+def test_bwd_layer_step_matches_finite_differences(oracle, B, L, M, D, H, d):
+    from oracle import oracle_bwd as OB
+    c = _layer_case(B + 10 * L + M, B, L, M, D, H, d)
+    rng = np.random.default_rng(17)
+    G = _rand(rng, B, L, D)
+    g = OB.layer_step_bwd(c["h"], c["mem"], c["W"], c["u"], c["vb"], c["R"], G)
+
+    def loss(h=None, W=None, u=None, vb=None):
+        out = oracle.layer_step(c["h"] if h is None else h, c["mem"], c["W"] if W is None else W,
+                                c["u"] if u is None else u, c["vb"] if vb is None else vb,
+                                c["R"])
+        return float(np.sum(out * G))
+
+    V = _rand(rng, *c["h"].shape)
+    fd = _fd(lambda x: loss(h=x), c["h"], V)
+    assert abs(fd - np.sum(g["dh"] * V)) <= 1e-6 * max(1.0, abs(fd))
+    for name, gname in [("W_q", "dW_q"), ("W_kE", "dW_kE"), ("W_v", "dW_v"), ("W_kR", "dW_kR"),
+                        ("W_o", "dW_o"), ("gamma", "dgamma"), ("beta", "dbeta")]:
+        V = _rand(rng, *c["W"][name].shape)
+
+        def lw(x, name=name):
+            W = dict(c["W"])
+            W[name] = x
+            return loss(W=W)
+
+        fd = _fd(lw, c["W"][name], V)
+        an = float(np.sum(g[gname] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+    for name, gname in [("u", "du"), ("vb", "dvb")]:
+        V = _rand(rng, *c[name].shape)
+        fd = _fd(lambda x, name=name: loss(**{name: x}), c[name], V)
+        an = float(np.sum(g[gname] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_bwd_layer_step_memory_gradient_is_stopped(oracle):
+    """The output depends on the memory, but its gradient is stopped: dh is the
+    derivative with the memory held fixed, i.e. a perturbation of h alone (the
+    memory rows are a separate input that gets no gradient)."""
+    from oracle import oracle_bwd as OB
+    B, L, M, D, H, d = 1, 3, 3, 6, 2, 3
+    c = _layer_case(23, B, L, M, D, H, d)
+    G = _rand(np.random.default_rng(2), B, L, D)
+    g = OB.layer_step_bwd(c["h"], c["mem"], c["W"], c["u"], c["vb"], c["R"], G)
+    assert set(g) == {"dh", "dW_q", "dW_kE", "dW_v", "dW_kR", "dW_o", "du", "dvb", "dgamma",
+                      "dbeta"}
+    V = _rand(np.random.default_rng(4), B, M, D)
+    f = lambda m: float(np.sum(oracle.layer_step(c["h"], m, c["W"], c["u"], c["vb"], c["R"]) * G))
+    assert abs(_fd(f, c["mem"], V)) > 1e-3  # the forward does depend on the memory
