@@ -414,7 +414,7 @@ def test_bwd_value_gradient_sums_to_the_output_gradient(oracle):
     np.testing.assert_allclose(g["dv"].sum(axis=1), G.sum(axis=1), rtol=1e-12, atol=1e-12)
 
 
-def _layer_case(seed, B, L, M, D, H, d):
+def _bwd_layer_case(seed, B, L, M, D, H, d):
     rng = np.random.default_rng(seed)
     W = {"W_q": _rand(rng, H * d, D, s=0.3), "W_kE": _rand(rng, H * d, D, s=0.3),
          "W_v": _rand(rng, H * d, D, s=0.3), "W_kR": _rand(rng, H * d, D, s=0.3),
@@ -427,7 +427,7 @@ def _layer_case(seed, B, L, M, D, H, d):
 @pytest.mark.parametrize("B,L,M,D,H,d", [(1, 3, 2, 8, 2, 4), (2, 2, 0, 6, 1, 3)])
 def test_bwd_layer_step_matches_finite_differences(oracle, B, L, M, D, H, d):
     from oracle import oracle_bwd as OB
-    c = _layer_case(B + 10 * L + M, B, L, M, D, H, d)
+    c = _bwd_layer_case(B + 10 * L + M, B, L, M, D, H, d)
     rng = np.random.default_rng(17)
     G = _rand(rng, B, L, D)
     g = OB.layer_step_bwd(c["h"], c["mem"], c["W"], c["u"], c["vb"], c["R"], G)
@@ -466,7 +466,7 @@ def test_bwd_layer_step_memory_gradient_is_stopped(oracle):
     memory rows are a separate input that gets no gradient)."""
     from oracle import oracle_bwd as OB
     B, L, M, D, H, d = 1, 3, 3, 6, 2, 3
-    c = _layer_case(23, B, L, M, D, H, d)
+    c = _bwd_layer_case(23, B, L, M, D, H, d)
     G = _rand(np.random.default_rng(2), B, L, D)
     g = OB.layer_step_bwd(c["h"], c["mem"], c["W"], c["u"], c["vb"], c["R"], G)
     assert set(g) == {"dh", "dW_q", "dW_kE", "dW_v", "dW_kR", "dW_o", "du", "dvb", "dgamma",
