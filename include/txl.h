@@ -112,6 +112,42 @@ size_t txl_rel_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L,
                                     int64_t mem_len, int64_t d_head);
 
 /*
+ * Backward pass of txl_rel_attn_fwd (training with a stop-gradient memory:
+ * Transformer-XL section 3.2 stops the gradient at the cached memory, so the
+ * keys and values of the memory rows still get gradients here, but nothing
+ * below them does; section 3.3 defines the score whose chain rule this is).
+ * With P the attention weights, dP_ij = dout_i . v_j and
+ * dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij'):
+ *   dq_i = scale sum_j dS_ij (k_j + r_{mem_len+i-j})
+ *   dk_j = scale sum_i dS_ij (q_i + u),   dv_j = sum_i P_ij dout_i
+ *   dr_p = scale sum of dS_ij (q_i + v) over the pairs at distance p
+ *   du   = scale sum_ij dS_ij k_j,        dv_bias = scale sum_ij dS_ij r_{mem_len+i-j}
+ *
+ * Arguments as in txl_rel_attn_fwd (same layouts and strides for q, k, v, r,
+ * u_bias, v_bias and scale; dout takes out's place and layout), d_head <= 64
+ * (else TXL_EUNSUPPORTED).  The forward's output is not needed: the softmax
+ * statistics are recomputed.  Gradients are fp32, dense and written whole:
+ *   dq [B][L][H][d]  dk, dv [B][T][H][d]  dr [T][H][d]  du, dvb [H][d]
+ * workspace (required): device scratch of txl_rel_attn_bwd_workspace_bytes()
+ * bytes; it holds P and dS [B][H][L][T] in fp32.  Gradients, workspace and
+ * inputs must not overlap.  Returns TXL_OK or a txl_status.
+ */
+int txl_rel_attn_bwd(void* stream, int dtype,
+                     int64_t B, int64_t H, int64_t L, int64_t mem_len, int64_t d_head,
+                     const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                     const void* k, const void* v, int64_t kv_sb, int64_t kv_st, int64_t kv_sh,
+                     const void* r, int64_t r_sp, int64_t r_sh, int64_t r_rows,
+                     const void* u_bias, const void* v_bias, float scale,
+                     const void* dout, int64_t do_sb, int64_t do_st, int64_t do_sh,
+                     float* dq, float* dk, float* dv, float* dr, float* du, float* dvb,
+                     void* workspace, size_t ws_bytes);
+
+/* Scratch bytes txl_rel_attn_bwd needs at these sizes (0 for invalid or
+ * unsupported arguments). */
+size_t txl_rel_attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L,
+                                        int64_t mem_len, int64_t d_head);
+
+/*
  * The memory of one layer (section 3.2: a length-M cache of old hidden states
  * that may span several segments), stored as a ring so that an update never
  * moves the rows it keeps.

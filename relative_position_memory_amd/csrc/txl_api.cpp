@@ -655,6 +655,77 @@ int txl_pos_ff(void* stream, int dtype, int64_t rows, int64_t d_model, int64_t d
   return TXL_OK;
 }
 
+
+
+
+// ---- attention backward -----------------------------------------------------------------
+
+size_t txl_rel_attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L,
+                                        int64_t mem_len, int64_t d_head) {
+  if ((dtype != TXL_FP32 && dtype != TXL_BF16) || B < 1 || H < 1 || L < 1 || mem_len < 0 ||
+      d_head < 1 || d_head > 64)
+    return 0;
+  return txl::attn_bwd_scratch_bytes(B, H, L, mem_len);
+}
+
+int txl_rel_attn_bwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, int64_t mem_len,
+                     int64_t d_head, const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                     const void* k, const void* v, int64_t kv_sb, int64_t kv_st, int64_t kv_sh,
+                     const void* r, int64_t r_sp, int64_t r_sh, int64_t r_rows,
+                     const void* u_bias, const void* v_bias, float scale, const void* dout,
+                     int64_t do_sb, int64_t do_st, int64_t do_sh, float* dq, float* dk, float* dv,
+                     float* dr, float* du, float* dvb, void* workspace, size_t ws_bytes) {
+  g_detail[0] = 0;
+  // the forward's checks cover q, k, v, r, u, v and dout (in out's place)
+  txl::AttnArgs f{};
+  f.B = B; f.H = H; f.L = L; f.mem_len = mem_len; f.d = d_head;
+  f.q = q; f.q_sb = q_sb; f.q_st = q_st; f.q_sh = q_sh;
+  f.k = k; f.v = v; f.kv_sb = kv_sb; f.kv_st = kv_st; f.kv_sh = kv_sh;
+  f.r = r; f.r_sp = r_sp; f.r_sh = r_sh;
+  f.u = u_bias; f.vb = v_bias; f.scale = scale;
+  f.out = (void*)dout; f.o_sb = do_sb; f.o_st = do_st; f.o_sh = do_sh;
+  f.d_load = d_head;
+  int rc = check_attn(dtype, f, r_rows);
+  if (rc != TXL_OK) return rc;
+  if (d_head > 64) return fail(TXL_EUNSUPPORTED, "backward: d_head %lld > 64", (long long)d_head);
+  if (!dq || !dk || !dv || !dr || !du || !dvb) return fail(TXL_EINVAL, "NULL gradient pointer");
+  const size_t need = txl::attn_bwd_scratch_bytes(B, H, L, mem_len);
+  if (!workspace || ws_bytes < need)
+    return fail(TXL_EINVAL, "workspace of %zu bytes < %zu", ws_bytes, need);
+  const int64_t T = mem_len + L, es = elt_size(dtype);
+  const Span outs[] = {{(uintptr_t)dq, (uintptr_t)(dq + B * L * H * d_head)},
+                       {(uintptr_t)dk, (uintptr_t)(dk + B * T * H * d_head)},
+                       {(uintptr_t)dv, (uintptr_t)(dv + B * T * H * d_head)},
+                       {(uintptr_t)dr, (uintptr_t)(dr + T * H * d_head)},
+                       {(uintptr_t)du, (uintptr_t)(du + H * d_head)},
+                       {(uintptr_t)dvb, (uintptr_t)(dvb + H * d_head)},
+                       {(uintptr_t)workspace, (uintptr_t)workspace + ws_bytes}};
+  const Span ins[] = {span4(q, B, q_sb, L, q_st, H, q_sh, d_head, es),
+                      span4(k, B, kv_sb, T, kv_st, H, kv_sh, d_head, es),
+                      span4(v, B, kv_sb, T, kv_st, H, kv_sh, d_head, es),
+                      span4(r, 1, 0, T, r_sp, H, r_sh, d_head, es),
+                      span4(u_bias, 1, 0, 1, 0, 1, 0, H * d_head, es),
+                      span4(v_bias, 1, 0, 1, 0, 1, 0, H * d_head, es),
+                      span4(dout, B, do_sb, L, do_st, H, do_sh, d_head, es)};
+  const int n_out = sizeof(outs) / sizeof(outs[0]);
+  for (int x = 0; x < n_out; ++x) {
+    for (const Span& s : ins)
+      if (overlap(outs[x], s)) return fail(TXL_EINVAL, "a gradient or the workspace overlaps an input");
+    for (int y = x + 1; y < n_out; ++y)
+      if (overlap(outs[x], outs[y])) return fail(TXL_EINVAL, "gradients / workspace overlap");
+  }
+  txl::AttnBwdArgs a{};
+  a.B = B; a.H = H; a.L = L; a.mem_len = mem_len; a.d = d_head;
+  a.q = q; a.q_sb = q_sb; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = k; a.v = v; a.kv_sb = kv_sb; a.kv_st = kv_st; a.kv_sh = kv_sh;
+  a.r = r; a.r_sp = r_sp; a.r_sh = r_sh;
+  a.u = u_bias; a.vb = v_bias; a.scale = scale;
+  a.dout = dout; a.do_sb = do_sb; a.do_st = do_st; a.do_sh = do_sh;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dr = dr; a.du = du; a.dvb = dvb;
+  txl::attn_bwd_bind(a, workspace);
+  const hipError_t e = txl::launch_attn_bwd(dtype == TXL_BF16 ? 1 : 0, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return TXL_OK;
+}
+
 }  // extern "C"
-
-

@@ -91,6 +91,45 @@ size_t attn_plan_bytes(const AttnArgs& a, const AttnPlan& p);
 // Points a's partial buffers into scratch (256-byte aligned inside it).
 void attn_plan_bind(AttnArgs& a, const AttnPlan& p, void* scratch);
 
+// ---- attention backward ------------------------------------------------------------
+// Gradients of the relative attention for an upstream gradient dout (same layout
+// as the forward's out), d <= 64.  Inputs keep the forward's strides; every
+// gradient is fp32 and dense: dq [B][L][H][d], dk, dv [B][T][H][d], dr [T][H][d],
+// du, dvb [H][d].  Scratch (fp32): P and dS [B][H][L][T], qc = q + u and
+// qp = q + v [B][H][L][64].
+struct AttnBwdArgs {
+  int64_t B, H, L, mem_len, d;
+  const void* q; int64_t q_sb, q_st, q_sh;
+  const void* k; const void* v; int64_t kv_sb, kv_st, kv_sh;
+  const void* r; int64_t r_sp, r_sh;
+  const void* u; const void* vb;
+  float scale;
+  const void* dout; int64_t do_sb, do_st, do_sh;
+  float* dq; float* dk; float* dv; float* dr; float* du; float* dvb;
+  float* P; float* dS; float* qc; float* qp;
+};
+size_t attn_bwd_scratch_bytes(int64_t B, int64_t H, int64_t L, int64_t mem_len);
+// Points P, dS, qc and qp into scratch (256-byte aligned inside it).
+void attn_bwd_bind(AttnBwdArgs& a, void* scratch);
+hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s);
+
+// C[z] = alpha A[z] B[z] (+ C[z] when accumulate), fp32 accumulation and output,
+// any element strides.  Operand X's element (i, j) of batch z sits at
+// X + (z / zdiv) * s1 + (z % zdiv) * s2 + i * si + j * sj.  dtype of A and B:
+// 0 = fp32, 1 = bf16.
+struct StridedOperand {
+  const void* p; int64_t s1, s2, si, sj;
+};
+struct StridedGemm {
+  int64_t M, N, K, batch, zdiv;
+  StridedOperand A, B;   // A (m, k), B (k, n)
+  float* C; int64_t c1, c2, cm, cn;
+  float alpha;
+  int accumulate;
+  int a_dtype, b_dtype;
+};
+hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s);
+
 // Any strides, d <= 128, fp32 math.  dtype 0 = fp32, 1 = bf16.
 hipError_t launch_attn_generic(int dtype, const AttnArgs& a, hipStream_t s);
 // bf16 matrix-core path: d <= 64, 16-byte aligned q/k/v/r, strides multiple of 8.

@@ -44,6 +44,13 @@ _lib.txl_rel_attn_fwd.argtypes = ([_p, ctypes.c_int] + [_i64] * 5 + [_p, _i64, _
                                   + [_p, _p, _f] + [_p, _i64, _i64, _i64] + [_p, _p, _sz])
 _lib.txl_rel_attn_fwd.restype = ctypes.c_int
 _lib.txl_rel_attn_workspace_bytes.argtypes = [ctypes.c_int] + [_i64] * 5
+_lib.txl_rel_attn_bwd.argtypes = ([_p, ctypes.c_int] + [_i64] * 5 + [_p, _i64, _i64, _i64]
+                                  + [_p, _p, _i64, _i64, _i64] + [_p, _i64, _i64, _i64]
+                                  + [_p, _p, ctypes.c_float] + [_p, _i64, _i64, _i64]
+                                  + [_p] * 6 + [_p, ctypes.c_size_t])
+_lib.txl_rel_attn_bwd.restype = ctypes.c_int
+_lib.txl_rel_attn_bwd_workspace_bytes.argtypes = [ctypes.c_int] + [_i64] * 5
+_lib.txl_rel_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.txl_rel_attn_workspace_bytes.restype = _sz
 _lib.txl_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int]
 _lib.txl_layer_workspace_bytes.restype = _sz
@@ -126,6 +133,51 @@ def rel_attn_fwd(q, k, v, r, u, vb, mem_len, out, scale=None, scores=None, strea
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size())
     _check(rc, "txl_rel_attn_fwd")
     return out
+
+
+def rel_attn_bwd_workspace_bytes(dtype, B, H, L, mem_len, d):
+    """txl_rel_attn_bwd_workspace_bytes."""
+    return int(_lib.txl_rel_attn_bwd_workspace_bytes(dtype_code(dtype), B, H, L, int(mem_len), d))
+
+
+def rel_attn_bwd(q, k, v, r, u, vb, mem_len, dout, scale=None, stream=None, workspace=None):
+    """txl_rel_attn_bwd on torch tensors (layouts as rel_attn_fwd; dout like out).
+
+    Returns a dict of fp32 gradients dq [B,L,H,d], dk, dv [B,T,H,d], dr [T,H,d],
+    du, dvb [H,d].  workspace: None (allocated here) or a uint8 device tensor of
+    at least rel_attn_bwd_workspace_bytes() bytes.
+    """
+    B, L, H, d = q.shape
+    T = int(mem_len) + L
+    for t in (q, k, v, r, dout):
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = q.device
+    f32 = torch.float32
+    g = {"dq": torch.empty((B, L, H, d), dtype=f32, device=dev),
+         "dk": torch.empty((B, T, H, d), dtype=f32, device=dev),
+         "dv": torch.empty((B, T, H, d), dtype=f32, device=dev),
+         "dr": torch.empty((T, H, d), dtype=f32, device=dev),
+         "du": torch.empty((H, d), dtype=f32, device=dev),
+         "dvb": torch.empty((H, d), dtype=f32, device=dev)}
+    if workspace is None:
+        nb = rel_attn_bwd_workspace_bytes(q.dtype, B, H, L, mem_len, d)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    rc = _lib.txl_rel_attn_bwd(
+        _stream(stream), dtype_code(q.dtype), B, H, L, int(mem_len), d,
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2),
+        _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
+        _ptr(r), r.stride(0), r.stride(1), r.shape[0],
+        _ptr(u), _ptr(vb), float(scale),
+        _ptr(dout), dout.stride(0), dout.stride(1), dout.stride(2),
+        _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dr"]), _ptr(g["du"]), _ptr(g["dvb"]),
+        _ptr(workspace), workspace.numel() * workspace.element_size())
+    _check(rc, "txl_rel_attn_bwd")
+    return g
 
 
 def layer_dims(B, L, d_model, n_head, d_head, ln_eps=1e-5):

@@ -1,0 +1,107 @@
+"""Parity of the attention backward (txl_rel_attn_bwd, through the C ABI) with
+the fp64 backward oracle.
+
+Both sides consume the same inputs (bf16 cases: values rounded to bf16 once);
+the HIP path computes in fp32, so every gradient must agree within 2e-3 of its
+largest magnitude (fp32 sums over at most a few thousand keys and the
+exponential's rounding stay near 1e-5 relative; a dropped or misplaced term is
+O(1)).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle_bwd as OB
+from relative_position_memory_amd import inputs as I
+from tests.gpu_util import dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 2e-3
+
+
+def _txl():
+    need_gpu()
+    from relative_position_memory_amd import txl
+    return txl
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dout(B, L, H, d, seed, dtype):
+    g = np.random.default_rng(seed).standard_normal((B, L, H, d)).astype(np.float32)
+    if dtype == "bf16":
+        g = torch.from_numpy(g).bfloat16().float().numpy()
+    return g
+
+
+def _close(name, got, ref):
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert err <= GRAD_TOL * scale, f"{name}: max err {err:.3e} (scale {scale:.3e})"
+
+
+def _run(c, dout, M, dtype, layout="bthd"):
+    txl = _txl()
+    if layout == "bthd":
+        q, k, v, r = (dev(c[n], dtype) for n in ("q", "k", "v", "r"))
+        g = dev(dout, dtype)
+    else:  # head-major storage passed as permuted views
+        hm = lambda x: dev(x.transpose(0, 2, 1, 3), dtype).permute(0, 2, 1, 3)
+        q, k, v, g = hm(c["q"]), hm(c["k"]), hm(c["v"]), hm(dout)
+        r = dev(c["r"].transpose(1, 0, 2), dtype).permute(1, 0, 2)
+    out = txl.rel_attn_bwd(q, k, v, r, dev(c["u"], dtype), dev(c["vb"], dtype), M, g)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy().astype(np.float64) for n, t in out.items()}
+
+
+@pytest.mark.parametrize("dtype,B,H,L,M,d,layout", [
+    ("fp32", 1, 2, 16, 16, 16, "bthd"),     # the tiny workload's shape
+    ("bf16", 2, 2, 37, 50, 64, "bhtd"),     # ragged tiles, head-major
+    ("bf16", 1, 3, 130, 70, 41, "bthd"),    # d = 41, ragged query tail
+    ("fp32", 2, 1, 65, 0, 32, "bthd"),      # no memory
+    ("bf16", 1, 2, 1, 100, 64, "bthd"),     # one query over a memory
+    ("fp32", 1, 1, 200, 333, 48, "bhtd"),   # memory longer than the segment
+])
+def test_attn_bwd_matches_oracle(dtype, B, H, L, M, d, layout):
+    c = I.attention_inputs(B, H, L, M, d, seed=3 * L + M + d, sigma=1.0, sigma_uv=0.5,
+                           dtype=dtype)
+    dout = _dout(B, L, H, d, seed=L + d, dtype=dtype)
+    _say(f"attn bwd dtype={dtype} B={B} H={H} L={L} M={M} d={d} layout={layout}")
+    got = _run(c, dout, M, dtype, layout)
+    ref = OB.rel_attn_bwd(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M, dout)
+    for n in ("dq", "dk", "dv", "dr", "du", "dvb"):
+        _close(n, got[n], ref[n])
+
+
+def test_attn_bwd_large_train_shape_batch_row():
+    """Large train-shape (B 8, H 16, L = M = 384, d 64, bf16): the query- and key-side
+    gradients of one batch row depend only on that row, so batch row 0 is checked
+    against the oracle run on it alone."""
+    B, H, L, M, d = 8, 16, 384, 384, 64
+    c = I.attention_inputs(B, H, L, M, d, seed=5, sigma=1.0, sigma_uv=0.5, dtype="bf16")
+    dout = _dout(B, L, H, d, seed=9, dtype="bf16")
+    _say("attn bwd large train shape")
+    got = _run(c, dout, M, "bf16", "bhtd")
+    c0 = {n: (c[n][:1] if n in ("q", "k", "v") else c[n]) for n in c}
+    ref = OB.rel_attn_bwd(c0["q"], c0["k"], c0["v"], c0["r"], c0["u"], c0["vb"], M, dout[:1])
+    for n in ("dq", "dk", "dv"):
+        _close(n, got[n][:1], ref[n])
+
+
+def test_attn_bwd_rejects_bad_arguments():
+    txl = _txl()
+    B, H, L, M, d = 1, 1, 8, 8, 80
+    x = torch.zeros((B, L, H, d), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((B, M + L, H, d), dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros((M + L, H, d), dtype=torch.bfloat16, device="cuda")
+    u = torch.zeros((H, d), dtype=torch.bfloat16, device="cuda")
+    assert txl.rel_attn_bwd_workspace_bytes(torch.bfloat16, B, H, L, M, d) == 0
+    with pytest.raises(txl.TxlError):
+        txl.rel_attn_bwd(x, kv, kv, r, u, u, M, x,
+                         workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
