@@ -222,6 +222,52 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims,
                    void* workspace, size_t ws_bytes);
 
 /*
+ * Gradients of one layer step (fp32, dense), see txl_layer_step_bwd.
+ */
+typedef struct {
+  float* dh;        /* [B][L][D]  gradient of h_in (current rows; the memory gets none) */
+  float* dW_q;      /* [H*d][D]                                                        */
+  float* dW_kE;     /* [H*d][D]   over the memory rows and the current rows             */
+  float* dW_v;      /* [H*d][D]                                                        */
+  float* dW_kR;     /* [H*d][D]                                                        */
+  float* dW_o;      /* [D][H*d]                                                        */
+  float* du;        /* [H][d]     content bias u                                       */
+  float* dv_bias;   /* [H][d]     position bias v                                      */
+  float* dgamma;    /* [D]                                                             */
+  float* dbeta;     /* [D]                                                             */
+} txl_layer_grads;
+
+/* Bytes of workspace txl_layer_step_bwd needs (memory capacity mem_capacity);
+ * 0 for invalid or unsupported arguments. */
+size_t txl_layer_bwd_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype);
+
+/*
+ * Backward pass of txl_layer_step for the upstream gradient dh_out [B][L][D]
+ * (same dtype as h_in): the training step with a stop-gradient memory of
+ * Transformer-XL section 3.2 (the cached hidden states get no gradient, while
+ * the weights collect the memory rows' contributions through k and v) over the
+ * procedure of section 3.3 (projections, relative attention, output projection,
+ * residual, LayerNorm with biased variance).  All arguments but dh_out, g and
+ * the workspace are txl_layer_step's (same meaning and checks); d_head <= 64.
+ * The call recomputes the forward in its workspace, then:
+ *   dy  = LayerNorm backward of dh_out          (also dgamma, dbeta)
+ *   dW_o = dy^T a,   da = dy W_o,   (dq, dk, dv, dr, du, dv_bias) = txl_rel_attn_bwd(da)
+ *   dW_q = dq^T h_in,  dW_kE = dk^T ctx,  dW_v = dv^T ctx,  dW_kR = dr^T R[0:T]
+ *   dh  = dy + dq W_q + (dk W_kE + dv W_v) restricted to the current rows
+ * with ctx = [memory ; h_in].  Every gradient is written whole (not accumulated).
+ *   g          gradient pointers (all required; they must not overlap each other,
+ *              the inputs or the workspace).
+ *   workspace  device scratch of ws_bytes >= txl_layer_bwd_workspace_bytes(dims,
+ *              mem->capacity, dtype), 256-byte aligned.
+ * Returns TXL_OK or a txl_status.
+ */
+int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims,
+                       const void* h_in, const txl_ring* mem, const txl_layer_weights* w,
+                       const void* u_bias, const void* v_bias, const void* R, int64_t R_rows,
+                       const void* dh_out, const txl_layer_grads* g,
+                       void* workspace, size_t ws_bytes);
+
+/*
  * Where txl_layer_step leaves its intermediates in the workspace (section 3.3's
  * q, k, v, the projected encodings r = R W_kR^T, and the attention output a),
  * for a call with mem->len == mem_len.  After such a call the workspace holds,

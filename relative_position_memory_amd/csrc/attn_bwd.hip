@@ -56,7 +56,8 @@ __global__ __launch_bounds__(256) void attn_bwd_rows_kernel(AttnBwdArgs a) {
     float qv = 0.f, g = 0.f, qc = 0.f, qp = 0.f;
     if (i < L && c < d) {
       qv = ldE<E>(a.q, (int64_t)b * a.q_sb + (int64_t)i * a.q_st + (int64_t)h * a.q_sh + c);
-      g = ldE<E>(a.dout, (int64_t)b * a.do_sb + (int64_t)i * a.do_st + (int64_t)h * a.do_sh + c);
+      const int64_t go = (int64_t)b * a.do_sb + (int64_t)i * a.do_st + (int64_t)h * a.do_sh + c;
+      g = a.dout_f32 ? ((const float*)a.dout)[go] : ldE<E>(a.dout, go);
       qc = qv + ldE<E>(a.u, (int64_t)h * d + c);
       qp = qv + ldE<E>(a.vb, (int64_t)h * d + c);
     }
@@ -379,7 +380,7 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s) {
   g.A = {a.P, H * a.L * T, a.L * T, 1, T};
   g.B = {a.dout, a.do_sb, a.do_sh, a.do_st, 1};
   g.C = a.dv; g.c1 = T * H * d; g.c2 = d; g.cm = H * d; g.cn = 1;
-  g.alpha = 1.f; g.accumulate = 0; g.a_dtype = 0; g.b_dtype = dtype == 1 ? 1 : 0;
+  g.alpha = 1.f; g.accumulate = 0; g.a_dtype = 0; g.b_dtype = (dtype == 1 && !a.dout_f32) ? 1 : 0;
   if ((e = launch_gemm_strided(g, s)) != hipSuccess) return e;
   g.A.p = a.dS;
   g.B = {a.qc, H * a.L * DP, a.L * DP, DP, 1};

@@ -728,4 +728,172 @@ int txl_rel_attn_bwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
   return TXL_OK;
 }
 
+
+// ---- layer step backward --------------------------------------------------------------
+namespace {
+
+struct BwdWs {
+  size_t fwd, hout, y, dy, mean, rstd, da, dq, dk, dv, dr, ctx, attn, total;
+};
+
+BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
+  BwdWs w{};
+  const int64_t B = dm.B, L = dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
+  const int64_t T = cap + L, es = elt_size(dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  w.fwd = take(txl_layer_workspace_bytes(&dm, cap, dtype));
+  w.hout = take((size_t)(B * L * D * es));
+  w.y = take((size_t)(B * L * D) * 4);
+  w.dy = take((size_t)(B * L * D) * 4);
+  w.mean = take((size_t)(B * L) * 4);
+  w.rstd = take((size_t)(B * L) * 4);
+  w.da = take((size_t)(B * L * HD) * 4);
+  w.dq = take((size_t)(B * L * HD) * 4);
+  w.dk = take((size_t)(B * T * HD) * 4);
+  w.dv = take((size_t)(B * T * HD) * 4);
+  w.dr = take((size_t)(T * HD) * 4);
+  w.ctx = take((size_t)(B * T * D * es));
+  w.attn = take(txl::attn_bwd_scratch_bytes(B, dm.n_head, L, cap));
+  w.total = off;
+  return w;
+}
+
+// C = alpha A B (+ C), A (m, k) at a + m*am + k*ak, B (k, n) at b + k*bk + n*bn, C row-major
+// with row pitch ldc; batch z offsets a_z, b_z, c_z.
+hipError_t sgemm(hipStream_t st, int64_t M, int64_t N, int64_t K, const void* a, int adt,
+                 int64_t am, int64_t ak, const void* b, int bdt, int64_t bk, int64_t bn, float* c,
+                 int64_t ldc, bool acc, int64_t batch = 1, int64_t a_z = 0, int64_t b_z = 0,
+                 int64_t c_z = 0) {
+  txl::StridedGemm g{};
+  g.M = M; g.N = N; g.K = K; g.batch = batch; g.zdiv = 1;
+  g.A = {a, a_z, 0, am, ak};
+  g.B = {b, b_z, 0, bk, bn};
+  g.C = c; g.c1 = c_z; g.c2 = 0; g.cm = ldc; g.cn = 1;
+  g.alpha = 1.f; g.accumulate = acc ? 1 : 0;
+  g.a_dtype = adt; g.b_dtype = bdt;
+  return txl::launch_gemm_strided(g, st);
+}
+
+}  // namespace
+
+size_t txl_layer_bwd_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype) {
+  if (check_dims(dims) != TXL_OK || mem_capacity < 0 || dims->d_head > 64) return 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
+  return bwd_ws_layout(*dims, mem_capacity, dtype).total;
+}
+
+int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                       const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
+                       const void* v_bias, const void* R, int64_t R_rows, const void* dh_out,
+                       const txl_layer_grads* g, void* workspace, size_t ws_bytes) {
+  g_detail[0] = 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  int rc = check_dims(dims);
+  if (rc != TXL_OK) return rc;
+  if (dims->d_head > 64)
+    return fail(TXL_EUNSUPPORTED, "backward: d_head %lld > 64", (long long)dims->d_head);
+  if (!mem || !g || !dh_out) return fail(TXL_EINVAL, "NULL argument");
+  if (!g->dh || !g->dW_q || !g->dW_kE || !g->dW_v || !g->dW_kR || !g->dW_o || !g->du ||
+      !g->dv_bias || !g->dgamma || !g->dbeta)
+    return fail(TXL_EINVAL, "NULL gradient pointer");
+  if (!workspace || (uintptr_t)workspace % 256) return fail(TXL_EINVAL, "workspace is NULL or unaligned");
+  const txl_layer_dims dm = *dims;
+  const int64_t B = dm.B, L = dm.L, D = dm.d_model, H = dm.n_head, d = dm.d_head, HD = H * d;
+  if (mem->capacity < 1 || mem->len < 0 || mem->len > mem->capacity)
+    return fail(TXL_EINVAL, "ring state is invalid");
+  const BwdWs bw = bwd_ws_layout(dm, mem->capacity, dtype);
+  if (ws_bytes < bw.total) return fail(TXL_EWORKSPACE, "need %zu bytes, got %zu", bw.total, ws_bytes);
+  const int64_t len = mem->len, T = len + L, es = elt_size(dtype);
+  const int dt = dtype == TXL_BF16 ? 1 : 0;
+  // gradients must not overlap each other, the inputs or the workspace
+  const Span outs[] = {{(uintptr_t)g->dh, (uintptr_t)(g->dh + B * L * D)},
+                       {(uintptr_t)g->dW_q, (uintptr_t)(g->dW_q + HD * D)},
+                       {(uintptr_t)g->dW_kE, (uintptr_t)(g->dW_kE + HD * D)},
+                       {(uintptr_t)g->dW_v, (uintptr_t)(g->dW_v + HD * D)},
+                       {(uintptr_t)g->dW_kR, (uintptr_t)(g->dW_kR + HD * D)},
+                       {(uintptr_t)g->dW_o, (uintptr_t)(g->dW_o + D * HD)},
+                       {(uintptr_t)g->du, (uintptr_t)(g->du + HD)},
+                       {(uintptr_t)g->dv_bias, (uintptr_t)(g->dv_bias + HD)},
+                       {(uintptr_t)g->dgamma, (uintptr_t)(g->dgamma + D)},
+                       {(uintptr_t)g->dbeta, (uintptr_t)(g->dbeta + D)},
+                       {(uintptr_t)workspace, (uintptr_t)workspace + ws_bytes}};
+  const Span ins[] = {{(uintptr_t)h_in, (uintptr_t)h_in + (uintptr_t)(B * L * D * es)},
+                      {(uintptr_t)dh_out, (uintptr_t)dh_out + (uintptr_t)(B * L * D * es)},
+                      {(uintptr_t)mem->data,
+                       (uintptr_t)mem->data + (uintptr_t)(B * mem->capacity * D * es)}};
+  const int n_out = sizeof(outs) / sizeof(outs[0]);
+  for (int x = 0; x < n_out; ++x) {
+    for (const Span& sp : ins)
+      if (overlap(outs[x], sp)) return fail(TXL_EINVAL, "a gradient or the workspace overlaps an input");
+    for (int y = x + 1; y < n_out; ++y)
+      if (overlap(outs[x], outs[y])) return fail(TXL_EINVAL, "gradients / workspace overlap");
+  }
+  char* base = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  // the forward again, for q, k, v, r and a (it also checks the remaining arguments)
+  rc = txl_layer_step(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows,
+                      base + bw.hout, base + bw.fwd, bw.hout - bw.fwd);
+  if (rc != TXL_OK) return rc;
+  const WsLayout fl = ws_layout(dm, T, es);
+  char* fb = base + bw.fwd;
+  const void* q = fb + fl.q;
+  const void* k = fb + fl.k;
+  const void* v = fb + fl.v;
+  const void* r = fb + fl.r;
+  const void* a = fb + fl.a;
+  const int64_t dp = fl.dp;
+  float* y = (float*)(base + bw.y);
+  float* dy = (float*)(base + bw.dy);
+  float* da = (float*)(base + bw.da);
+  float* dq = (float*)(base + bw.dq);
+  float* dk = (float*)(base + bw.dk);
+  float* dv = (float*)(base + bw.dv);
+  float* dr = (float*)(base + bw.dr);
+  void* ctx = base + bw.ctx;
+  const int64_t BL = B * L;
+  hipError_t e;
+#define TXL_TRY(x, what) do { if ((e = (x)) != hipSuccess) return hip_fail(e, what); } while (0)
+  // y = a W_o^T + h_in (the LayerNorm input), then the LayerNorm backward
+  TXL_TRY(txl::launch_to_f32(dt, h_in, y, BL * D, st), "copy");
+  TXL_TRY(sgemm(st, BL, D, HD, a, dt, HD, 1, w->W_o, dt, 1, HD, y, D, true), "y");
+  TXL_TRY(txl::launch_ln_bwd(dt, y, w->ln_gamma, dh_out, BL, D, dm.ln_eps, dy,
+                             (float*)(base + bw.mean), (float*)(base + bw.rstd), g->dgamma,
+                             g->dbeta, st), "layernorm backward");
+  // dW_o = dy^T a, da = dy W_o
+  TXL_TRY(sgemm(st, D, HD, BL, dy, 0, 1, D, a, dt, HD, 1, g->dW_o, HD, false), "dW_o");
+  TXL_TRY(sgemm(st, BL, HD, D, dy, 0, D, 1, w->W_o, dt, HD, 1, da, HD, false), "da");
+  // attention backward on the forward's head-major q, k, v, r
+  txl::AttnBwdArgs ab{};
+  ab.B = B; ab.H = H; ab.L = L; ab.mem_len = len; ab.d = d;
+  ab.q = q; ab.q_sb = H * L * dp; ab.q_st = dp; ab.q_sh = L * dp;
+  ab.k = k; ab.v = v; ab.kv_sb = H * T * dp; ab.kv_st = dp; ab.kv_sh = T * dp;
+  ab.r = r; ab.r_sp = dp; ab.r_sh = T * dp;
+  ab.u = u_bias; ab.vb = v_bias; ab.scale = 1.0f / sqrtf((float)d);
+  ab.dout = da; ab.do_sb = L * HD; ab.do_st = HD; ab.do_sh = d; ab.dout_f32 = 1;
+  ab.dq = dq; ab.dk = dk; ab.dv = dv; ab.dr = dr; ab.du = g->du; ab.dvb = g->dv_bias;
+  txl::attn_bwd_bind(ab, base + bw.attn);
+  TXL_TRY(txl::launch_attn_bwd(dt, ab, st), "attention backward");
+  // projection weights: dW_q = dq^T h_in, dW_kE = dk^T ctx, dW_v = dv^T ctx, dW_kR = dr^T R
+  TXL_TRY(txl::launch_gather_ctx(dt, mem->data, mem->capacity, mem->start, len, h_in, B, L, D, ctx,
+                                 st), "context gather");
+  TXL_TRY(sgemm(st, HD, D, BL, dq, 0, 1, HD, h_in, dt, D, 1, g->dW_q, D, false), "dW_q");
+  TXL_TRY(sgemm(st, HD, D, B * T, dk, 0, 1, HD, ctx, dt, D, 1, g->dW_kE, D, false), "dW_kE");
+  TXL_TRY(sgemm(st, HD, D, B * T, dv, 0, 1, HD, ctx, dt, D, 1, g->dW_v, D, false), "dW_v");
+  TXL_TRY(sgemm(st, HD, D, T, dr, 0, 1, HD, R, dt, D, 1, g->dW_kR, D, false), "dW_kR");
+  // dh = dy + dq W_q + (dk W_kE + dv W_v) on the current rows (the memory's gradient is stopped)
+  TXL_TRY(txl::launch_to_f32(0, dy, g->dh, BL * D, st), "copy");
+  TXL_TRY(sgemm(st, BL, D, HD, dq, 0, HD, 1, w->W_q, dt, D, 1, g->dh, D, true), "dh q");
+  TXL_TRY(sgemm(st, L, D, HD, dk + len * HD, 0, HD, 1, w->W_kE, dt, D, 1, g->dh, D, true, B,
+                T * HD, 0, L * D), "dh k");
+  TXL_TRY(sgemm(st, L, D, HD, dv + len * HD, 0, HD, 1, w->W_v, dt, D, 1, g->dh, D, true, B,
+                T * HD, 0, L * D), "dh v");
+#undef TXL_TRY
+  return TXL_OK;
+}
+
 }  // extern "C"

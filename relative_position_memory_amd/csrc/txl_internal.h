@@ -105,6 +105,7 @@ struct AttnBwdArgs {
   const void* u; const void* vb;
   float scale;
   const void* dout; int64_t do_sb, do_st, do_sh;
+  int dout_f32;   // dout is fp32 whatever the inputs' dtype
   float* dq; float* dk; float* dv; float* dr; float* du; float* dvb;
   float* P; float* dS; float* qc; float* qp;
 };
@@ -129,6 +130,18 @@ struct StridedGemm {
   int a_dtype, b_dtype;
 };
 hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s);
+
+// Layer-step backward helpers: dtype 0 = fp32, 1 = bf16 for the non-fp32 operands.
+hipError_t launch_to_f32(int dtype, const void* src, float* dst, int64_t n, hipStream_t s);
+// dy of h_out = LayerNorm(y) gamma + beta for dh_out (rows of D), the rows' mean
+// and 1/sigma, and dgamma, dbeta (overwritten).
+hipError_t launch_ln_bwd(int dtype, const float* y, const void* gamma, const void* dh_out,
+                         int64_t M, int64_t D, float eps, float* dy, float* mean, float* rstd,
+                         float* dgamma, float* dbeta, hipStream_t s);
+// ctx [B][len + L][D] = [ring rows (oldest first) ; h]
+hipError_t launch_gather_ctx(int dtype, const void* ring, int64_t cap, int64_t start, int64_t len,
+                             const void* h, int64_t B, int64_t L, int64_t D, void* ctx,
+                             hipStream_t s);
 
 // Any strides, d <= 128, fp32 math.  dtype 0 = fp32, 1 = bf16.
 hipError_t launch_attn_generic(int dtype, const AttnArgs& a, hipStream_t s);

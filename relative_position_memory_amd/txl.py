@@ -230,6 +230,53 @@ _lib.txl_layer_workspace_map.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes
 _lib.txl_layer_workspace_map.restype = ctypes.c_int
 
 
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dh", "dW_q", "dW_kE", "dW_v", "dW_kR", "dW_o", "du", "dv_bias", "dgamma",
+                 "dbeta")]
+
+
+_lib.txl_layer_bwd_workspace_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int]
+_lib.txl_layer_bwd_workspace_bytes.restype = _sz
+_lib.txl_layer_step_bwd.argtypes = [_p, ctypes.c_int, ctypes.POINTER(LayerDims), _p,
+                                    ctypes.POINTER(Ring), ctypes.POINTER(LayerWeights), _p, _p,
+                                    _p, _i64, _p, ctypes.POINTER(LayerGrads), _p, _sz]
+_lib.txl_layer_step_bwd.restype = ctypes.c_int
+
+
+def layer_bwd_workspace_bytes(dims: LayerDims, mem_capacity: int, dtype: torch.dtype) -> int:
+    """txl_layer_bwd_workspace_bytes."""
+    return int(_lib.txl_layer_bwd_workspace_bytes(ctypes.byref(dims), int(mem_capacity),
+                                                  dtype_code(dtype)))
+
+
+def layer_step_bwd(dims, h, ring, W, u, vb, R, dh_out, workspace, grads=None, stream=None):
+    """txl_layer_step_bwd.  grads: None (fp32 tensors allocated here) or a dict
+    with the keys of LayerGrads.  Returns the dict of gradient tensors."""
+    dev = h.device
+    D, H, d = dims.d_model, dims.n_head, dims.d_head
+    f32 = torch.float32
+    if grads is None:
+        grads = {"dh": torch.empty((dims.B, dims.L, D), dtype=f32, device=dev),
+                 "dW_q": torch.empty((H * d, D), dtype=f32, device=dev),
+                 "dW_kE": torch.empty((H * d, D), dtype=f32, device=dev),
+                 "dW_v": torch.empty((H * d, D), dtype=f32, device=dev),
+                 "dW_kR": torch.empty((H * d, D), dtype=f32, device=dev),
+                 "dW_o": torch.empty((D, H * d), dtype=f32, device=dev),
+                 "du": torch.empty((H, d), dtype=f32, device=dev),
+                 "dv_bias": torch.empty((H, d), dtype=f32, device=dev),
+                 "dgamma": torch.empty((D,), dtype=f32, device=dev),
+                 "dbeta": torch.empty((D,), dtype=f32, device=dev)}
+    gs = LayerGrads(**{n: _ptr(t) for n, t in grads.items()})
+    lw = W if isinstance(W, LayerWeights) else layer_weights(W)
+    rc = _lib.txl_layer_step_bwd(_stream(stream), dtype_code(h.dtype), ctypes.byref(dims),
+                                 _ptr(h), ctypes.byref(ring), ctypes.byref(lw), _ptr(u), _ptr(vb),
+                                 _ptr(R), R.shape[0], _ptr(dh_out), ctypes.byref(gs),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size())
+    _check(rc, "txl_layer_step_bwd")
+    return grads
+
+
 def workspace_views(dims, mem_len, workspace, dtype):
     """Views of the intermediates txl_layer_step leaves in `workspace`
     (txl_layer_workspace_map): q [B,L,H,d], k/v [B,T,H,d], r [T,H,d], a [B,L,H,d]."""

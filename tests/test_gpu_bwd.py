@@ -105,3 +105,46 @@ def test_attn_bwd_rejects_bad_arguments():
     with pytest.raises(txl.TxlError):
         txl.rel_attn_bwd(x, kv, kv, r, u, u, M, x,
                          workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
+
+
+# ---- layer step backward -----------------------------------------------------------------
+
+# fp32: the HIP path's intermediates are fp32, so the gradients agree like the
+# attention's.  bf16: q, k, v, r and a are rounded to bf16 between the kernels
+# (relative 2^-9) and the scores, LayerNorm input and products that follow carry
+# that rounding; 3e-2 of the largest magnitude bounds it with margin.
+LAYER_TOL = {"fp32": GRAD_TOL, "bf16": 3e-2}
+GRAD_NAMES = [("dh", "dh"), ("dW_q", "dW_q"), ("dW_kE", "dW_kE"), ("dW_v", "dW_v"),
+              ("dW_kR", "dW_kR"), ("dW_o", "dW_o"), ("du", "du"), ("dv_bias", "dvb"),
+              ("dgamma", "dgamma"), ("dbeta", "dbeta")]
+
+
+@pytest.mark.parametrize("dtype,name,over,mem_len,start", [
+    ("fp32", "tiny", {}, None, 0),
+    ("fp32", "tiny", {}, 0, 0),                                                  # empty memory
+    ("fp32", "tiny", {"B": 2, "L": 37, "M": 50, "d": 12, "H": 3, "D": 40}, 45, 31),  # ring wrap
+    ("bf16", "charlm", {"B": 2, "L": 64, "M": 64, "D": 128, "H": 2, "d": 64}, 64, 0),
+    ("bf16", "charlm", {"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
+])
+def test_layer_step_bwd_matches_oracle(dtype, name, over, mem_len, start):
+    from tests.test_gpu_parity import _layer_setup
+    w = I.workload(name, **over)
+    _say(f"layer bwd {dtype} {w} mem_len={mem_len} start={start}")
+    txl, x, W, data, ring, h, logical = _layer_setup(w, mem_len=mem_len, start=start)
+    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
+    nb = txl.layer_bwd_workspace_bytes(dims, w.M, h.dtype)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    g_out = np.random.default_rng(w.L + w.D).standard_normal((w.B, w.L, w.D)).astype(np.float32)
+    if dtype == "bf16":
+        g_out = torch.from_numpy(g_out).bfloat16().float().numpy()
+    got = txl.layer_step_bwd(dims, h, ring, W, dev(x["u"], dtype), dev(x["v"], dtype),
+                             dev(x["R"], dtype), dev(g_out, dtype), ws)
+    torch.cuda.synchronize()
+    ref = OB.layer_step_bwd(x["h0"][0], logical, x["weights"][0], x["u"], x["v"], x["R"], g_out)
+    for gn, rn in GRAD_NAMES:
+        g = got[gn].cpu().numpy().astype(np.float64)
+        r = ref[rn]
+        scale = max(1.0, float(np.max(np.abs(r))))
+        err = float(np.max(np.abs(g - r)))
+        assert err <= LAYER_TOL[dtype] * scale, f"{gn}: max err {err:.3e} (scale {scale:.3e})"
