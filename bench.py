@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--workload", default="charlm")
     p.add_argument("--attn-reps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--train", action="store_true",
+                   help="time a training step (forward + backward, stop-gradient memory) at the "
+                        "Large train-shape instead")
     p.add_argument("--main-only", action="store_true",
                    help="skip the cached-K/V stack and the feed-forward timing (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -189,6 +192,93 @@ def kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def train_step(args):
+    """Training step with a stop-gradient memory ([XL] section 3.2) at the Large
+    train-shape (batch 8, d_model 1024, 16 heads of 64, L = M = 384, 18 layers,
+    4 segments, bf16).  Per segment: the forward through every layer
+    (txl_layer_step, keeping each layer's input), then the backward from the top
+    (txl_layer_step_bwd, which recomputes its layer's forward; the upstream
+    gradient of the top layer is a fixed synthetic tensor, the gradient of each
+    layer's input feeds the layer below), then the memory updates.  The weight
+    gradients are written per layer (no optimizer update is part of the step).
+    value = B * L * segments / step time."""
+    import numpy as np
+    import torch
+    from relative_position_memory_amd import inputs as I
+    from relative_position_memory_amd import txl
+
+    w = I.workload("large_train")
+    x = I.make_inputs(w, seed=0)
+    tdt = torch.bfloat16
+    dev = lambda a: torch.from_numpy(a).to(tdt).cuda()
+    Ws = [{k: dev(v) for k, v in lw.items()} for lw in x["weights"]]
+    lws = [txl.layer_weights(Wl) for Wl in Ws]
+    u, vb, R = dev(x["u"]), dev(x["v"]), dev(x["R"])
+    ring_data = [dev(m) for m in x["mem"]]
+    rings = [txl.make_ring(dd, 0, w.M) for dd in ring_data]
+    h0 = dev(x["h0"])
+    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
+    ws = torch.empty(txl.workspace_bytes(dims, w.M, tdt), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(txl.layer_bwd_workspace_bytes(dims, w.M, tdt), dtype=torch.uint8,
+                      device="cuda")
+    hs = [torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(w.n_layers + 1)]
+    rng = np.random.default_rng(1)
+    g_top = dev(rng.standard_normal((w.B, w.L, w.D)).astype(np.float32))
+    g_cur = torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda")
+    grads = None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        nonlocal grads
+        for s in range(w.n_segments):
+            hs[0].copy_(h0[s])
+            for n in range(w.n_layers):
+                txl.layer_step(dims, hs[n], rings[n], lws[n], u, vb, R, hs[n + 1], ws,
+                               stream=stream)
+            g = g_top
+            for n in reversed(range(w.n_layers)):
+                grads = txl.layer_step_bwd(dims, hs[n], rings[n], lws[n], u, vb, R, g, bws,
+                                           grads=grads, stream=stream)
+                g_cur.copy_(grads["dh"])  # the next layer down takes dh in the layers' dtype
+                g = g_cur
+            for n in range(w.n_layers):
+                txl.mem_update(rings[n], hs[n], stream=stream)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 3))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # one layer's backward alone (HIP events on the same stream)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for _ in range(5):
+        txl.layer_step_bwd(dims, hs[0], rings[0], lws[0], u, vb, R, g_top, bws, grads=grads,
+                           stream=stream)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = b0.elapsed_time(b1) / 5
+    tokens = w.B * w.L * w.n_segments
+    print(json.dumps({
+        "metric": "training step (forward + backward, stop-gradient memory): query tokens/s",
+        "value": tokens / (ms / 1e3), "unit": "query tokens/s", "n_gpus": 1, "steps": steps,
+        "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "large_train: 18 layers x 4 segments, forward + backward",
+                   "batch": w.B, "d_model": w.D, "n_head": w.H, "d_head": w.d,
+                   "segment_len": w.L, "mem_len": w.M, "n_layers": w.n_layers,
+                   "n_segments": w.n_segments},
+        "layer_bwd_ms": bwd_ms,
+        "note": "backward = txl_layer_step_bwd per layer (recomputes the layer's forward); "
+                "the upstream gradient of the top layer is synthetic; no optimizer update"}),
+          flush=True)
+
+
 def eval_speed(args):
     """Per-token evaluation time with memory against the vanilla model that
     recomputes the whole window for every prediction ([XL] section 4.5, Table 9):
@@ -312,6 +402,9 @@ def main():
 
     if args.eval_speed:
         eval_speed(args)
+        return
+    if args.train:
+        train_step(args)
         return
 
     import torch
