@@ -776,6 +776,7 @@ hipError_t sgemm(hipStream_t st, int64_t M, int64_t N, int64_t K, const void* a,
   g.C = c; g.c1 = c_z; g.c2 = 0; g.cm = ldc; g.cn = 1;
   g.alpha = 1.f; g.accumulate = acc ? 1 : 0;
   g.a_dtype = adt; g.b_dtype = bdt;
+  g.bf16_mfma = (adt == 1 || bdt == 1) ? 1 : 0;  // a bf16 layer: bf16 products, fp32 sums
   return txl::launch_gemm_strided(g, st);
 }
 

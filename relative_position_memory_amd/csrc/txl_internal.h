@@ -128,6 +128,9 @@ struct StridedGemm {
   float alpha;
   int accumulate;
   int a_dtype, b_dtype;
+  // 1: the products may run on the bf16 matrix cores (operands rounded to bf16
+  // as they are staged, fp32 accumulation); 0: fp32 throughout.
+  int bf16_mfma;
 };
 hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s);
 

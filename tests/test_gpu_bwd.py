@@ -1,11 +1,15 @@
 """Parity of the attention backward (txl_rel_attn_bwd, through the C ABI) with
 the fp64 backward oracle.
 
-Both sides consume the same inputs (bf16 cases: values rounded to bf16 once);
-the HIP path computes in fp32, so every gradient must agree within 2e-3 of its
-largest magnitude (fp32 sums over at most a few thousand keys and the
-exponential's rounding stay near 1e-5 relative; a dropped or misplaced term is
-O(1)).
+Both sides consume the same inputs (bf16 cases: values rounded to bf16 once).
+fp32 inputs: the HIP path computes in fp32, so every gradient must agree within
+2e-3 of its largest magnitude (fp32 sums over at most a few thousand keys and
+the exponential's rounding stay near 1e-5 relative; a dropped or misplaced term
+is O(1)).  bf16 inputs: the key-side products dv = P^T dO and dk = dS^T (q + u)
+run on the bf16 matrix cores, so P, dS and q + u enter them rounded to bf16
+(relative 2^-9 each, as P enters the forward's P V); an fp64 emulation of that
+rounding at these shapes stays below 4e-3 of the largest magnitude, and the bar
+is 1e-2.
 """
 import sys
 
@@ -20,6 +24,7 @@ from tests.gpu_util import dev, need_gpu
 pytestmark = pytest.mark.gpu
 
 GRAD_TOL = 2e-3
+TOL = {"fp32": GRAD_TOL, "bf16": 1e-2}
 
 
 def _txl():
@@ -40,10 +45,10 @@ def _dout(B, L, H, d, seed, dtype):
     return g
 
 
-def _close(name, got, ref):
+def _close(name, got, ref, tol):
     scale = max(1.0, float(np.max(np.abs(ref))))
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
-    assert err <= GRAD_TOL * scale, f"{name}: max err {err:.3e} (scale {scale:.3e})"
+    assert err <= tol * scale, f"{name}: max err {err:.3e} (scale {scale:.3e})"
 
 
 def _run(c, dout, M, dtype, layout="bthd"):
@@ -76,7 +81,7 @@ def test_attn_bwd_matches_oracle(dtype, B, H, L, M, d, layout):
     got = _run(c, dout, M, dtype, layout)
     ref = OB.rel_attn_bwd(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M, dout)
     for n in ("dq", "dk", "dv", "dr", "du", "dvb"):
-        _close(n, got[n], ref[n])
+        _close(n, got[n], ref[n], TOL[dtype])
 
 
 def test_attn_bwd_large_train_shape_batch_row():
@@ -91,7 +96,7 @@ def test_attn_bwd_large_train_shape_batch_row():
     c0 = {n: (c[n][:1] if n in ("q", "k", "v") else c[n]) for n in c}
     ref = OB.rel_attn_bwd(c0["q"], c0["k"], c0["v"], c0["r"], c0["u"], c0["vb"], M, dout[:1])
     for n in ("dq", "dk", "dv"):
-        _close(n, got[n][:1], ref[n])
+        _close(n, got[n][:1], ref[n], TOL["bf16"])
 
 
 def test_attn_bwd_rejects_bad_arguments():
@@ -111,8 +116,9 @@ def test_attn_bwd_rejects_bad_arguments():
 
 # fp32: the HIP path's intermediates are fp32, so the gradients agree like the
 # attention's.  bf16: q, k, v, r and a are rounded to bf16 between the kernels
-# (relative 2^-9) and the scores, LayerNorm input and products that follow carry
-# that rounding; 3e-2 of the largest magnitude bounds it with margin.
+# (relative 2^-9), the backward's products take their operands rounded to bf16
+# (matrix cores, fp32 sums), and the scores, LayerNorm input and products that
+# follow carry that rounding; 3e-2 of the largest magnitude bounds it with margin.
 LAYER_TOL = {"fp32": GRAD_TOL, "bf16": 3e-2}
 GRAD_NAMES = [("dh", "dh"), ("dW_q", "dW_q"), ("dW_kE", "dW_kE"), ("dW_v", "dW_v"),
               ("dW_kR", "dW_kR"), ("dW_o", "dW_o"), ("du", "du"), ("dv_bias", "dvb"),
