@@ -358,22 +358,22 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s) {
   if (a.B * a.H > 65535 || (a.L + BQ - 1) / BQ > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(1), dim3(256), 0, s, a.du, H * d);
   hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(1), dim3(256), 0, s, a.dvb, H * d);
-  const size_t smem = sizeof(BwdSmem);
-  static bool attr_set[2] = {false, false};
-  const void* fn = dtype == 1 ? (const void*)attn_bwd_rows_kernel<uint16_t>
-                              : (const void*)attn_bwd_rows_kernel<float>;
-  if (!attr_set[dtype == 1]) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set[dtype == 1] = true;
-  }
-  const dim3 grid((unsigned)((a.L + BQ - 1) / BQ), (unsigned)(a.B * a.H));
-  if (dtype == 1)
-    hipLaunchKernelGGL(attn_bwd_rows_kernel<uint16_t>, grid, dim3(256), smem, s, a);
-  else
+  hipError_t e;
+  if (dtype == 1) {
+    if ((e = launch_attn_bwd_rows_mfma(a, s)) != hipSuccess) return e;
+  } else {
+    const size_t smem = sizeof(BwdSmem);
+    static bool attr_set = false;
+    if (!attr_set) {
+      e = hipFuncSetAttribute((const void*)attn_bwd_rows_kernel<float>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    const dim3 grid((unsigned)((a.L + BQ - 1) / BQ), (unsigned)(a.B * a.H));
     hipLaunchKernelGGL(attn_bwd_rows_kernel<float>, grid, dim3(256), smem, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // dv = P^T dO and dk = scale dS^T (q + u), per (batch, head): m = key, k = query
   StridedGemm g{};
   g.M = T; g.N = d; g.K = a.L; g.batch = a.B * a.H; g.zdiv = H;

@@ -113,6 +113,9 @@ size_t attn_bwd_scratch_bytes(int64_t B, int64_t H, int64_t L, int64_t mem_len);
 // Points P, dS, qc and qp into scratch (256-byte aligned inside it).
 void attn_bwd_bind(AttnBwdArgs& a, void* scratch);
 hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s);
+// The per-query part of the backward (P, dS, dq, du, dv) on the bf16 matrix cores
+// (bf16 q, k, v, r, u, v; d <= 64).
+hipError_t launch_attn_bwd_rows_mfma(const AttnBwdArgs& a, hipStream_t s);
 
 // C[z] = alpha A[z] B[z] (+ C[z] when accumulate), fp32 accumulation and output,
 // any element strides.  Operand X's element (i, j) of batch z sits at
