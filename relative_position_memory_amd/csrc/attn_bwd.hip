@@ -389,6 +389,7 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s) {
   g.C = a.dk;
   g.alpha = a.scale;
   if ((e = launch_gemm_strided(g, s)) != hipSuccess) return e;
+  if (dtype == 1) return launch_attn_bwd_dr_mfma(a, s);
   hipLaunchKernelGGL(attn_bwd_dr_kernel, dim3((unsigned)((T + 63) / 64), (unsigned)H), dim3(256), 0,
                      s, a);
   return hipGetLastError();

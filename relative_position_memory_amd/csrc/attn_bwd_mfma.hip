@@ -353,7 +353,113 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
   }
 }
 
+// dr_p = scale sum over (b, i) of dS[b][h][i][len + i - p] (q_i + v): the pairs at
+// distance p lie on a diagonal of dS.  Workgroup (distance block, head, split)
+// takes the (batch, 64-query block) items split, split + nsplit, ...: per item
+// it gathers the diagonals into a [distance][query] tile and (q + v) into a
+// [column][query] tile (bf16 in LDS), and wave w multiplies distances 16 w ..
+// 16 w + 15 by all 64 columns.  With nsplit > 1 the partial sums are added
+// atomically into dr (cleared before).
+constexpr int DGP = 64 + 8;  // bf16 pitch of both tiles
+
+__global__ __launch_bounds__(256) void attn_bwd_dr_mfma_kernel(AttnBwdArgs a, int nsplit) {
+  __shared__ __align__(16) uint16_t DG[64 * DGP];
+  __shared__ __align__(16) uint16_t QT[64 * DGP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int H = (int)a.H, L = (int)a.L, len = (int)a.mem_len, d = (int)a.d;
+  const int T = len + L;
+  const int p0 = blockIdx.x * 64, h = blockIdx.y, split = blockIdx.z;
+  const int nqb = (L + 63) / 64, items = (int)a.B * nqb;
+  f32x4 acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = {0.f, 0.f, 0.f, 0.f};
+  for (int it = split; it < items; it += nsplit) {
+    const int b = it / nqb, i0 = (it % nqb) * 64;
+    const int ilast = i0 + 63 < L - 1 ? i0 + 63 : L - 1;
+    if (p0 > len + ilast) continue;  // no pair of this block at these distances
+    const int64_t z = (int64_t)b * H + h;
+    __syncthreads();  // the previous item's tiles are read
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      // unit u: distances / columns 4 (u % 16) .. + 3 of queries 2 (u / 16), + 1
+      const int u = tid + 256 * x;
+      const int f4 = 4 * (u & 15), ii = 2 * (u >> 4);
+      float v[2][4], w[2][4];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = i0 + ii + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = p0 + f4 + e, j = len + i - p;
+          v[r][e] = (i < L && p < T && j >= 0) ? a.dS[(z * L + i) * T + j] : 0.f;
+        }
+        if (i < L) {
+          const float4 f = *(const float4*)(a.qp + (z * L + i) * DP + f4);
+          w[r][0] = f.x; w[r][1] = f.y; w[r][2] = f.z; w[r][3] = f.w;
+        } else {
+          w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *(uint32_t*)(DG + (f4 + e) * DGP + ii) = pack2(v[0][e], v[1][e]);
+        *(uint32_t*)(QT + (f4 + e) * DGP + ii) = pack2(w[0][e], w[1][e]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 af = *(const bf16x8*)(DG + (16 * wave + n16) * DGP + 32 * s + 8 * g4);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        acc[cb] = mfma(af, *(const bf16x8*)(QT + (16 * cb + n16) * DGP + 32 * s + 8 * g4), acc[cb]);
+    }
+  }
+  // lane (g4, n16) of block cb: distance p0 + 16 wave + 4 g4 + e, column 16 cb + n16
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = p0 + 16 * wave + 4 * g4 + e, c = 16 * cb + n16;
+      if (p < T && c < d) {
+        float* o = a.dr + ((int64_t)p * H + h) * d + c;
+        const float v = a.scale * acc[cb][e];
+        if (nsplit > 1)
+          atomicAdd(o, v);
+        else
+          *o = v;
+      }
+    }
+}
+
+__global__ void zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
 }  // namespace
+
+hipError_t launch_attn_bwd_dr_mfma(const AttnBwdArgs& a, hipStream_t s) {
+  const int64_t T = a.mem_len + a.L, nqb = (a.L + 63) / 64, items = a.B * nqb;
+  const int64_t blocks = ((T + 63) / 64) * a.H;
+  if (blocks > 0x7fffffffLL || a.H > 65535) return hipErrorInvalidValue;
+  // enough workgroups for the GPU (about four per CU), each with several items
+  int64_t nsplit = (1024 + blocks - 1) / blocks;
+  nsplit = nsplit < items ? nsplit : items;
+  nsplit = nsplit < 1 ? 1 : (nsplit > 65535 ? 65535 : nsplit);
+  if (nsplit > 1) {
+    const int64_t n = T * a.H * a.d;
+    const int64_t zb = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, s, a.dr, n);
+  }
+  hipLaunchKernelGGL(attn_bwd_dr_mfma_kernel, dim3((unsigned)((T + 63) / 64), (unsigned)a.H,
+                                                   (unsigned)nsplit),
+                     dim3(256), 0, s, a, (int)nsplit);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bwd_rows_mfma(const AttnBwdArgs& a, hipStream_t s) {
   const size_t smem = sizeof(BwdMfmaSmem);

@@ -116,6 +116,8 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s);
 // The per-query part of the backward (P, dS, dq, du, dv) on the bf16 matrix cores
 // (bf16 q, k, v, r, u, v; d <= 64).
 hipError_t launch_attn_bwd_rows_mfma(const AttnBwdArgs& a, hipStream_t s);
+// dr from the stored dS and q + v on the bf16 matrix cores.
+hipError_t launch_attn_bwd_dr_mfma(const AttnBwdArgs& a, hipStream_t s);
 
 // C[z] = alpha A[z] B[z] (+ C[z] when accumulate), fp32 accumulation and output,
 // any element strides.  Operand X's element (i, j) of batch z sits at
