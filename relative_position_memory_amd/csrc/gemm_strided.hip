@@ -5,7 +5,7 @@
 //  * fp32: 256 threads, each a 4 x 4 block, K in steps of 16 staged through LDS
 //    (operands widened to fp32 on the way in);
 //  * bf16 matrix cores (StridedGemm::bf16_mfma): 4 waves, each one 32 x 32
-//    block of v_mfma_f32_32x32x16_bf16, K in steps of 32.  Each operand is read
+//    block of v_mfma_f32_32x32x16_bf16, K in steps of 128.  Each operand is read
 //    along whichever of its axes is contiguous (8 consecutive k of one row, or
 //    4 consecutive rows at 2 k), rounded to bf16 in registers and written to LDS
 //    k-contiguous, so the fragment reads are 16-byte rows.  The next step's
@@ -16,7 +16,7 @@ namespace txl {
 namespace {
 
 constexpr int TM = 64, TN = 64, TK = 16;
-constexpr int MK = 32, KP = MK + 8;  // matrix-core K step; LDS row pitch in bf16
+constexpr int MK = 128;  // matrix-core K step (measured: 128 beats 32 and 64)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -136,93 +136,106 @@ __device__ inline void ld_vec<uint16_t, 4>(const void* p, int64_t off, float* v)
 // aligned (checked on the host).
 constexpr int ST_ROWS = 1, ST_VEC = 2;
 
-// One thread's share of a 64 x 32 block of X(row, k) = p[base + row sr + k sk]
-// (rows r0.., k k0..; zero outside R rows and kend), as 4 packed bf16 pairs.
-template <typename T>
+// One thread's share of a 64 x KS block of X(row, k) = p[base + row sr + k sk]
+// (rows r0.., k k0..; zero outside R rows and kend), as KS / 32 units of 4
+// packed bf16 pairs.  Unit u = tid + 256 x.
+template <typename T, int KS>
 __device__ inline void stage_load(const void* p, int64_t base, int64_t sr, int64_t sk, int64_t R,
                                   int64_t r0, int64_t k0, int64_t kend, int flags, int tid,
-                                  uint32_t (&w)[4]) {
-  if (!(flags & ST_ROWS)) {  // row r0 + tid / 4, k = k0 + 8 (tid % 4) + e
-    const int64_t r = r0 + (tid >> 2), k = k0 + 8 * (tid & 3);
-    float v[8];
-    if ((flags & ST_VEC) && r < R && k + 8 <= kend) {
-      ld_vec<T, 8>(p, base + r * sr + k, v);
-    } else {
+                                  uint32_t (&w)[KS / 32][4]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = (r < R && k + e < kend) ? ld<T>(p, base + r * sr + (k + e) * sk) : 0.f;
-    }
+  for (int x = 0; x < KS / 32; ++x) {
+    const int u = tid + 256 * x;
+    if (!(flags & ST_ROWS)) {  // row r0 + u / (KS / 8), k = k0 + 8 (u % (KS / 8)) + e
+      const int64_t r = r0 + u / (KS / 8), k = k0 + 8 * (u % (KS / 8));
+      float v[8];
+      if ((flags & ST_VEC) && r < R && k + 8 <= kend) {
+        ld_vec<T, 8>(p, base + r * sr + k, v);
+      } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = pack_bf16_pair(v[2 * e], v[2 * e + 1]);
-  } else {  // rows r0 + 4 (tid % 16) + i, k = k0 + 2 (tid / 16) + {0, 1}
-    const int64_t r = r0 + 4 * (tid & 15), k = k0 + 2 * (tid >> 4);
-    float v0[4], v1[4];
-    if ((flags & ST_VEC) && r + 4 <= R) {
-      if (k < kend) ld_vec<T, 4>(p, base + r + k * sk, v0);
-      else v0[0] = v0[1] = v0[2] = v0[3] = 0.f;
-      if (k + 1 < kend) ld_vec<T, 4>(p, base + r + (k + 1) * sk, v1);
-      else v1[0] = v1[1] = v1[2] = v1[3] = 0.f;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v0[i] = (r + i < R && k < kend) ? ld<T>(p, base + (r + i) * sr + k * sk) : 0.f;
-        v1[i] = (r + i < R && k + 1 < kend) ? ld<T>(p, base + (r + i) * sr + (k + 1) * sk) : 0.f;
+        for (int e = 0; e < 8; ++e)
+          v[e] = (r < R && k + e < kend) ? ld<T>(p, base + r * sr + (k + e) * sk) : 0.f;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[x][e] = pack_bf16_pair(v[2 * e], v[2 * e + 1]);
+    } else {  // rows r0 + 4 (u % 16) + i, k = k0 + 2 (u / 16) + {0, 1}
+      const int64_t r = r0 + 4 * (u & 15), k = k0 + 2 * (u >> 4);
+      float v0[4], v1[4];
+      if ((flags & ST_VEC) && r + 4 <= R) {
+        if (k < kend) ld_vec<T, 4>(p, base + r + k * sk, v0);
+        else v0[0] = v0[1] = v0[2] = v0[3] = 0.f;
+        if (k + 1 < kend) ld_vec<T, 4>(p, base + r + (k + 1) * sk, v1);
+        else v1[0] = v1[1] = v1[2] = v1[3] = 0.f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v0[i] = (r + i < R && k < kend) ? ld<T>(p, base + (r + i) * sr + k * sk) : 0.f;
+          v1[i] = (r + i < R && k + 1 < kend) ? ld<T>(p, base + (r + i) * sr + (k + 1) * sk) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[x][i] = pack_bf16_pair(v0[i], v1[i]);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_bf16_pair(v0[i], v1[i]);
   }
 }
 
-// LDS block [64][KP], k contiguous
-__device__ inline void stage_store(uint16_t* Xs, int flags, int tid, const uint32_t (&w)[4]) {
-  if (!(flags & ST_ROWS)) {
-    *(uint4*)(Xs + (tid >> 2) * KP + 8 * (tid & 3)) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-    const int r = 4 * (tid & 15), k = 2 * (tid >> 4);
+// LDS block [64][KS + 8], k contiguous
+template <int KS>
+__device__ inline void stage_store(uint16_t* Xs, int flags, int tid, const uint32_t (&w)[KS / 32][4]) {
+  constexpr int P = KS + 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(uint32_t*)(Xs + (r + i) * KP + k) = w[i];
+  for (int x = 0; x < KS / 32; ++x) {
+    const int u = tid + 256 * x;
+    if (!(flags & ST_ROWS)) {
+      *(uint4*)(Xs + (u / (KS / 8)) * P + 8 * (u % (KS / 8))) =
+          make_uint4(w[x][0], w[x][1], w[x][2], w[x][3]);
+    } else {
+      const int r = 4 * (u & 15), k = 2 * (u >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(uint32_t*)(Xs + (r + i) * P + k) = w[x][i];
+    }
   }
 }
 
-template <typename TA, typename TB>
+template <typename TA, typename TB, int KS>
 __global__ __launch_bounds__(256) void gemm_strided_mfma_kernel(StridedGemm g, int ksplit, int fa,
                                                                 int fb) {
-  __shared__ __align__(16) uint16_t As[TM * KP];
-  __shared__ __align__(16) uint16_t Bs[TN * KP];
+  constexpr int P = KS + 8;
+  __shared__ __align__(16) uint16_t As[TM * P];
+  __shared__ __align__(16) uint16_t Bs[TN * P];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t z = blockIdx.z / ksplit;
   const int split = blockIdx.z % ksplit;
-  const int64_t kchunk = ((g.K + ksplit - 1) / ksplit + MK - 1) / MK * MK;
+  const int64_t kchunk = ((g.K + ksplit - 1) / ksplit + KS - 1) / KS * KS;
   const int64_t kbeg = split * kchunk, kend = kbeg + kchunk < g.K ? kbeg + kchunk : g.K;
   const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
   const int64_t zq = z / g.zdiv, zr = z % g.zdiv;
   const int64_t abase = zq * g.A.s1 + zr * g.A.s2;
   const int64_t bbase = zq * g.B.s1 + zr * g.B.s2;
   // A is staged as X(row m, k), B as X(row n, k)
-  uint32_t wa[4], wb[4];
+  uint32_t wa[KS / 32][4], wb[KS / 32][4];
   if (kbeg < kend) {
-    stage_load<TA>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, kbeg, kend, fa, tid, wa);
-    stage_load<TB>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, kbeg, kend, fb, tid, wb);
+    stage_load<TA, KS>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, kbeg, kend, fa, tid, wa);
+    stage_load<TB, KS>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, kbeg, kend, fb, tid, wb);
   }
   const int wm = wave >> 1, wn = wave & 1;
   // fragment rows: lane l supplies row l % 32 of its wave's block, k 8 (l / 32) .. + 8
-  const uint16_t* af = As + (32 * wm + (lane & 31)) * KP + 8 * (lane >> 5);
-  const uint16_t* bfp = Bs + (32 * wn + (lane & 31)) * KP + 8 * (lane >> 5);
+  const uint16_t* af = As + (32 * wm + (lane & 31)) * P + 8 * (lane >> 5);
+  const uint16_t* bfp = Bs + (32 * wn + (lane & 31)) * P + 8 * (lane >> 5);
   f32x16 acc;
 #pragma unroll
   for (int x = 0; x < 16; ++x) acc[x] = 0.f;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += MK) {
+  for (int64_t k0 = kbeg; k0 < kend; k0 += KS) {
     __syncthreads();  // the previous step's fragment reads are done
-    stage_store(As, fa, tid, wa);
-    stage_store(Bs, fb, tid, wb);
+    stage_store<KS>(As, fa, tid, wa);
+    stage_store<KS>(Bs, fb, tid, wb);
     __syncthreads();
-    if (k0 + MK < kend) {
-      stage_load<TA>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, k0 + MK, kend, fa, tid, wa);
-      stage_load<TB>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, k0 + MK, kend, fb, tid, wb);
+    if (k0 + KS < kend) {
+      stage_load<TA, KS>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, k0 + KS, kend, fa, tid, wa);
+      stage_load<TB, KS>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, k0 + KS, kend, fb, tid, wb);
     }
 #pragma unroll
-    for (int s = 0; s < MK / 16; ++s) {
+    for (int s = 0; s < KS / 16; ++s) {
       const bf16x8 a = *(const bf16x8*)(af + 16 * s);
       const bf16x8 b = *(const bf16x8*)(bfp + 16 * s);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
@@ -274,15 +287,33 @@ int stage_flags(const StridedOperand& o, int64_t sr, int64_t sk, int dtype) {
   return 0;  // neither axis contiguous: element loads
 }
 
+template <int KS>
+void launch_mfma_variant(const StridedGemm& g, dim3 grid, int k, int fa, int fb, hipStream_t s) {
+  if (g.a_dtype == 0 && g.b_dtype == 0)
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, float, KS>), grid, dim3(256), 0, s, g, k, fa,
+                       fb);
+  else if (g.a_dtype == 0 && g.b_dtype == 1)
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, uint16_t, KS>), grid, dim3(256), 0, s, g, k,
+                       fa, fb);
+  else if (g.a_dtype == 1 && g.b_dtype == 0)
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, float, KS>), grid, dim3(256), 0, s, g, k,
+                       fa, fb);
+  else
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, uint16_t, KS>), grid, dim3(256), 0, s, g,
+                       k, fa, fb);
+}
+
 hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   if (g.zdiv <= 0 || g.batch > 65535 || (g.N + TN - 1) / TN > 0x7fffffff ||
       (g.M + TM - 1) / TM > 65535)
     return hipErrorInvalidValue;
-  // Split K when the tiles alone leave the GPU short of workgroups (about four
-  // per CU wanted), each split at least 256 deep; the splits add atomically.
+  // Split K when the tiles alone leave the GPU short of workgroups (about two per
+  // CU for the matrix-core kernel, four for the fp32 one), each split at least 256
+  // deep; the splits add atomically.
+  const int64_t wg_target = g.bf16_mfma ? 512 : 1024;
   const int64_t tiles = ((g.N + TN - 1) / TN) * ((g.M + TM - 1) / TM) * g.batch;
-  int64_t ks = (1024 + tiles - 1) / tiles;
+  int64_t ks = (wg_target + tiles - 1) / tiles;
   if (ks > g.K / 256) ks = g.K / 256;
   if (ks > 16) ks = 16;
   if (ks < 1 || g.batch * ks > 65535) ks = 1;
@@ -297,17 +328,7 @@ hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s) {
   if (g.bf16_mfma) {
     const int fa = stage_flags(g.A, g.A.si, g.A.sj, g.a_dtype);
     const int fb = stage_flags(g.B, g.B.sj, g.B.si, g.b_dtype);
-    if (g.a_dtype == 0 && g.b_dtype == 0)
-      hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, float>), grid, dim3(256), 0, s, g, k, fa, fb);
-    else if (g.a_dtype == 0 && g.b_dtype == 1)
-      hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, uint16_t>), grid, dim3(256), 0, s, g, k, fa,
-                         fb);
-    else if (g.a_dtype == 1 && g.b_dtype == 0)
-      hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, float>), grid, dim3(256), 0, s, g, k, fa,
-                         fb);
-    else
-      hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s, g, k,
-                         fa, fb);
+    launch_mfma_variant<MK>(g, grid, k, fa, fb, s);
     return hipGetLastError();
   }
   if (g.a_dtype == 0 && g.b_dtype == 0)

@@ -131,6 +131,8 @@ GRAD_NAMES = [("dh", "dh"), ("dW_q", "dW_q"), ("dW_kE", "dW_kE"), ("dW_v", "dW_v
     ("fp32", "tiny", {"B": 2, "L": 37, "M": 50, "d": 12, "H": 3, "D": 40}, 45, 31),  # ring wrap
     ("bf16", "charlm", {"B": 2, "L": 64, "M": 64, "D": 128, "H": 2, "d": 64}, 64, 0),
     ("bf16", "charlm", {"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
+    # 128-wide product tiles with a ragged half tile, K split across workgroups
+    ("bf16", "charlm", {"B": 2, "L": 96, "M": 160, "D": 192, "H": 3, "d": 64}, 160, 37),
 ])
 def test_layer_step_bwd_matches_oracle(dtype, name, over, mem_len, start):
     from tests.test_gpu_parity import _layer_setup
