@@ -71,26 +71,38 @@ __device__ inline float sum4(float x) {
   return x + __shfl_xor(x, 32, 64);
 }
 
-// Copy rows [row0, row0 + nrows) of a bf16 [row][c] operand (row stride rs) into
-// LDS rows of KPI elements, columns 0..63 (zero past d and outside [0, rmax)).
-__device__ inline void stage_rows(uint16_t* dst, const uint16_t* src, int64_t rs, int row0,
-                                  int nrows, int rmax, int d, bool vec, int tid) {
-  for (int q = tid; q < nrows * 8; q += 256) {
+// Rows [row0, row0 + NR) of a bf16 [row][c] operand (row stride rs), columns
+// 0..63 in 16-byte chunks (zero past d and outside [0, rmax)): chunk q = tid +
+// 256 x is row q / 8, columns 8 (q % 8) ..  fetch_rows loads this thread's
+// chunks into registers, store_rows writes them to LDS rows of KPI elements.
+template <int NR>
+__device__ inline void fetch_rows(const uint16_t* src, int64_t rs, int row0, int rmax, int d,
+                                  bool vec, int tid, uint4 (&v)[(NR * 8 + 255) / 256]) {
+#pragma unroll
+  for (int x = 0; x < (NR * 8 + 255) / 256; ++x) {
+    const int q = tid + 256 * x;
     const int rr = q >> 3, c0 = 8 * (q & 7), row = row0 + rr;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row >= 0 && row < rmax && c0 < d) {
+    v[x] = make_uint4(0u, 0u, 0u, 0u);
+    if (q < NR * 8 && row >= 0 && row < rmax && c0 < d) {
       const uint16_t* p = src + (int64_t)row * rs + c0;
       if (vec && c0 + 8 <= d) {
-        v = *(const uint4*)p;
+        v[x] = *(const uint4*)p;
       } else {
         uint16_t t[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) t[e] = c0 + e < d ? p[e] : (uint16_t)0;
-        v = make_uint4(t[0] | ((uint32_t)t[1] << 16), t[2] | ((uint32_t)t[3] << 16),
-                       t[4] | ((uint32_t)t[5] << 16), t[6] | ((uint32_t)t[7] << 16));
+        v[x] = make_uint4(t[0] | ((uint32_t)t[1] << 16), t[2] | ((uint32_t)t[3] << 16),
+                          t[4] | ((uint32_t)t[5] << 16), t[6] | ((uint32_t)t[7] << 16));
       }
     }
-    *(uint4*)(dst + rr * KPI + c0) = v;
+  }
+}
+template <int NR>
+__device__ inline void store_rows(uint16_t* dst, int tid, const uint4 (&v)[(NR * 8 + 255) / 256]) {
+#pragma unroll
+  for (int x = 0; x < (NR * 8 + 255) / 256; ++x) {
+    const int q = tid + 256 * x;
+    if (q < NR * 8) *(uint4*)(dst + (q >> 3) * KPI + 8 * (q & 7)) = v[x];
   }
 }
 
@@ -155,10 +167,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
 #pragma unroll
   for (int db = 0; db < 4; ++db) toff[db] = (4 * g4 + (n16 >> 2)) * KPI + 4 * (4 * db + (n16 & 3));
 
-  auto stage = [&](int j0) {
-    stage_rows(sm.K, kbase, a.kv_st, j0, BK, T, d, vec & 1, tid);
-    stage_rows(sm.V, vbase, a.kv_st, j0, BK, T, d, vec & 1, tid);
-    stage_rows(sm.RW, rbase, a.r_sp, len + i0 - j0 - (BK - 1), RWR, T, d, (vec & 2) != 0, tid);
+  // Tile j0's K, V and r rows: fetched into registers one tile ahead (the loads
+  // run during the previous tile's products), then written to LDS.
+  uint4 fk[(BK * 8 + 255) / 256], fv[(BK * 8 + 255) / 256], fr[(RWR * 8 + 255) / 256];
+  auto fetch = [&](int j0) {
+    fetch_rows<BK>(kbase, a.kv_st, j0, T, d, vec & 1, tid, fk);
+    fetch_rows<BK>(vbase, a.kv_st, j0, T, d, vec & 1, tid, fv);
+    fetch_rows<RWR>(rbase, a.r_sp, len + i0 - j0 - (BK - 1), T, d, (vec & 2) != 0, tid, fr);
+  };
+  auto commit = [&]() {
+    store_rows<BK>(sm.K, tid, fk);
+    store_rows<BK>(sm.V, tid, fv);
+    store_rows<RWR>(sm.RW, tid, fr);
   };
   // S^T (exp2 domain, masked to -inf) and dP^T of key tile j0: block kb, register e
   // = key j0 + 16 kb + 4 g4 + e of query i
@@ -204,11 +224,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
 
   // ---- walk 1: running max m, sum l of exp2(S - m), and sum of exp2(S - m) dP ----------
   float m = -INFINITY, l = 0.f, dn = 0.f;  // l, dn: this lane's partial sums
+  fetch(0);
   for (int kb0 = 0; kb0 < nkb; ++kb0) {
     const int j0 = kb0 * BK;
     __syncthreads();
-    stage(j0);
+    commit();
     __syncthreads();
+    fetch(kb0 + 1 < nkb ? j0 + BK : 0);  // walk 2 starts again at tile 0
     f32x4 S[4], dP[4];
     scores(j0, S, dP);
     float tmax = -INFINITY;
@@ -245,8 +267,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
   for (int kb0 = 0; kb0 < nkb; ++kb0) {
     const int j0 = kb0 * BK;
     __syncthreads();
-    stage(j0);
+    commit();
     __syncthreads();
+    if (kb0 + 1 < nkb) fetch(j0 + BK);
     f32x4 S[4], dP[4];
     scores(j0, S, dP);
     f32x4 dS[4];
