@@ -129,7 +129,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
 
   // ---- this lane's query fragments: columns 32 s + 8 g4 + e --------------------------
   bf16x8 qcf[2], qpf[2], gf[2];
+  float dot_go = 0.f;  // this lane's share of dO . o (with the forward's statistics)
   {
+    const uint16_t* orow = a.o ? (const uint16_t*)a.o + b * a.o_sb + (int64_t)(qok ? i : 0) * a.o_st +
+                                     h * a.o_sh
+                               : nullptr;
     const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + (int64_t)(qok ? i : 0) * a.q_st +
                            h * a.q_sh;
     const int64_t go = b * a.do_sb + (int64_t)(qok ? i : 0) * a.do_st + h * a.do_sh;
@@ -148,6 +152,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
         qcf[s][e] = (__bf16)(qc * sl2);
         qpf[s][e] = (__bf16)(qp * sl2);
         gf[s][e] = (__bf16)g;
+        if (orow && ok) dot_go += g * bf16_to_f32(orow[c]);
         if (qok) {  // unscaled q + u, q + v for the key-side products and dr
           a.qc[((int64_t)z * L + i) * DP + c] = qc;
           a.qp[((int64_t)z * L + i) * DP + c] = qp;
@@ -223,9 +228,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
   };
 
   // ---- walk 1: running max m, sum l of exp2(S - m), and sum of exp2(S - m) dP ----------
+  //      (skipped when the forward's log-sum-exp is given: then D = dO . o)
   float m = -INFINITY, l = 0.f, dn = 0.f;  // l, dn: this lane's partial sums
   fetch(0);
-  for (int kb0 = 0; kb0 < nkb; ++kb0) {
+  const bool fwd_stats = a.lse != nullptr;
+  for (int kb0 = 0; kb0 < (fwd_stats ? 0 : nkb); ++kb0) {
     const int j0 = kb0 * BK;
     __syncthreads();
     commit();
@@ -257,8 +264,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
   }
   l = sum4(l);
   dn = sum4(dn);
-  const float lse = l > 0.f ? m + __log2f(l) : 0.f;
-  const float Dd = l > 0.f ? dn / l : 0.f;
+  dot_go = sum4(dot_go);
+  const float lse = fwd_stats ? (qok ? a.lse[(int64_t)z * L + i] : 0.f) : (l > 0.f ? m + __log2f(l) : 0.f);
+  const float Dd = fwd_stats ? dot_go : (l > 0.f ? dn / l : 0.f);
 
   // ---- walk 2: P, dS (to scratch), dq = scale (K^T dS^T + RW^T dSw^T) -------------------
   f32x4 dqc[4], dqp[4];  // rows = columns 16 db + 4 g4 + e, lane = query n16

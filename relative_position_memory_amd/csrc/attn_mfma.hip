@@ -645,6 +645,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
     const int i = i0w + 16 * gm + n16;
     if (i >= L) continue;
     const float inv = 1.f / l_tot[gm];
+    if (a.lse && g4 == 0) a.lse[(int64_t)g * L + i] = s_off[gm] + __log2f(l_tot[gm]);
     uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
     const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
                      ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
@@ -727,6 +728,7 @@ __global__ __launch_bounds__(256) void attn_part_merge_kernel(AttnArgs a) {
           }
     }
     const float inv = 1.f / den;
+    if (a.lse && g4 == 0) a.lse[(int64_t)g * L + i] = M + __log2f(den);
     uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
     const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
                      ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);

@@ -333,11 +333,14 @@ int txl_layer_workspace_map(const txl_layer_dims* dims, int64_t mem_len, int dty
   return TXL_OK;
 }
 
-int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
-                   const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
-                   const void* v_bias, const void* R, int64_t R_rows, void* h_out,
-                   void* workspace, size_t ws_bytes) {
+// The layer step; with lse != NULL the matrix-core attention also writes each
+// query's log-sum-exp there ([B][H][L]) and *lse_written says whether it did.
+static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                          const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
+                          const void* v_bias, const void* R, int64_t R_rows, void* h_out,
+                          void* workspace, size_t ws_bytes, float* lse, bool* lse_written) {
   g_detail[0] = 0;
+  if (lse_written) *lse_written = false;
   if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
   int rc = check_dims(dims);
   if (rc != TXL_OK) return rc;
@@ -424,8 +427,20 @@ int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const vo
   at.out = a; at.o_sb = L * HD; at.o_st = HD; at.o_sh = d;
   at.scores = nullptr;
   at.d_load = dp;  // workspace rows hold dp readable columns
+  if (lse && dtype == TXL_BF16 && txl::attn_mfma_supported(at)) {
+    at.lse = lse;
+    *lse_written = true;
+  }
   if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
   return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st);
+}
+
+int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                   const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
+                   const void* v_bias, const void* R, int64_t R_rows, void* h_out,
+                   void* workspace, size_t ws_bytes) {
+  return layer_step_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows, h_out,
+                        workspace, ws_bytes, nullptr, nullptr);
 }
 
 int txl_mem_update(void* stream, int dtype, txl_ring* mem, int64_t B, int64_t d_model,
@@ -733,7 +748,7 @@ int txl_rel_attn_bwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
 namespace {
 
 struct BwdWs {
-  size_t fwd, hout, y, dy, mean, rstd, da, dq, dk, dv, dr, ctx, attn, total;
+  size_t fwd, hout, y, dy, mean, rstd, da, dq, dk, dv, dr, ctx, lse, attn, total;
 };
 
 BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
@@ -758,6 +773,7 @@ BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
   w.dv = take((size_t)(B * T * HD) * 4);
   w.dr = take((size_t)(T * HD) * 4);
   w.ctx = take((size_t)(B * T * D * es));
+  w.lse = take((size_t)(B * dm.n_head * L) * 4);
   w.attn = take(txl::attn_bwd_scratch_bytes(B, dm.n_head, L, cap));
   w.total = off;
   return w;
@@ -837,8 +853,10 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
   char* base = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   // the forward again, for q, k, v, r and a (it also checks the remaining arguments)
-  rc = txl_layer_step(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows,
-                      base + bw.hout, base + bw.fwd, bw.hout - bw.fwd);
+  bool have_lse = false;
+  rc = layer_step_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows,
+                      base + bw.hout, base + bw.fwd, bw.hout - bw.fwd, (float*)(base + bw.lse),
+                      &have_lse);
   if (rc != TXL_OK) return rc;
   const WsLayout fl = ws_layout(dm, T, es);
   char* fb = base + bw.fwd;
@@ -877,6 +895,10 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
   ab.u = u_bias; ab.vb = v_bias; ab.scale = 1.0f / sqrtf((float)d);
   ab.dout = da; ab.do_sb = L * HD; ab.do_st = HD; ab.do_sh = d; ab.dout_f32 = 1;
   ab.dq = dq; ab.dk = dk; ab.dv = dv; ab.dr = dr; ab.du = g->du; ab.dvb = g->dv_bias;
+  if (have_lse) {  // the forward's softmax statistics and output
+    ab.lse = (const float*)(base + bw.lse);
+    ab.o = a; ab.o_sb = L * HD; ab.o_st = HD; ab.o_sh = d;
+  }
   txl::attn_bwd_bind(ab, base + bw.attn);
   TXL_TRY(txl::launch_attn_bwd(dt, ab, st), "attention backward");
   // projection weights: dW_q = dq^T h_in, dW_kE = dk^T ctx, dW_v = dv^T ctx, dW_kR = dr^T R

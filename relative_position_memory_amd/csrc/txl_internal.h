@@ -56,6 +56,9 @@ struct AttnArgs {
   float scale;
   void* out; int64_t o_sb, o_st, o_sh;
   float* scores;  // NULL or [B][H][L][T]
+  // NULL, or [B][H][L]: each query's log-sum-exp of its scaled scores in the
+  // exp2 domain (log2 sum_j 2^(s_ij log2 e)), for the backward (matrix-core path).
+  float* lse;
   // Columns of every q/k/v/r row that may be read (>= d).  Equal to d for
   // caller-owned tensors; the layer step's own workspace rows are padded to a
   // multiple of 8 and may be read whole (columns >= d are ignored).
@@ -108,6 +111,11 @@ struct AttnBwdArgs {
   int dout_f32;   // dout is fp32 whatever the inputs' dtype
   float* dq; float* dk; float* dv; float* dr; float* du; float* dvb;
   float* P; float* dS; float* qc; float* qp;
+  // Optional (matrix-core path): the forward's exp2-domain log-sum-exp per query
+  // ([B][H][L], AttnArgs::lse) and its output o (bf16, strides like dout); with
+  // them the softmax statistics are not recomputed and sum_j P dP = dO . o.
+  const float* lse;
+  const void* o; int64_t o_sb, o_st, o_sh;
 };
 size_t attn_bwd_scratch_bytes(int64_t B, int64_t H, int64_t L, int64_t mem_len);
 // Points P, dS, qc and qp into scratch (256-byte aligned inside it).
