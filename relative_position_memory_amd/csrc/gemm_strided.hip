@@ -1,25 +1,30 @@
 // Batched GEMM with arbitrary element strides, fp32 accumulation and output.
 // It serves the backward pass, whose products take operands transposed and
-// strided in every way (P^T dO, dS^T qc, dY^T X, dY W).  Two kernels over the
-// same 64 x 64 output tiles and K split:
-//  * fp32: 256 threads, each a 4 x 4 block, K in steps of 16 staged through LDS
-//    (operands widened to fp32 on the way in);
-//  * bf16 matrix cores (StridedGemm::bf16_mfma): 4 waves, each one 32 x 32
-//    block of v_mfma_f32_32x32x16_bf16, K in steps of 128.  Each operand is read
-//    along whichever of its axes is contiguous (8 consecutive k of one row, or
-//    4 consecutive rows at 2 k), rounded to bf16 in registers and written to LDS
-//    k-contiguous, so the fragment reads are 16-byte rows.  The next step's
-//    global loads are in flight during the current step's products.
+// strided in every way (P^T dO, dS^T qc, dY^T X, dY W).  Two kernels:
+//  * fp32: 64 x 64 output tiles, 256 threads, each a 4 x 4 block, K in steps of
+//    16 staged through LDS (operands widened to fp32 on the way in);
+//  * bf16 matrix cores (StridedGemm::bf16_mfma): 64 x 64 or 128 x 128 tiles, 4
+//    waves of v_mfma_f32_16x16x32_bf16, K in steps of 64.  Each operand is read
+//    in 16-byte pieces along whichever of its axes is contiguous (8 consecutive
+//    k of one row, or 8 consecutive rows at one k), rounded to bf16 and stored
+//    to LDS as read: [row][k] or [k][row].  The fragments of a [k][row] tile
+//    come through transposing LDS reads (ds_read_b64_tr_b16), those of a
+//    [row][k] tile through two 8-byte reads in the same k order, so no layout
+//    is transposed on the way in.  The next step's global loads are in flight
+//    during the current step's products.
+// Both split K across workgroups (atomic fp32 sums) when the tiles alone leave
+// the GPU short of workgroups.
 #include "txl_internal.h"
 
 namespace txl {
 namespace {
 
 constexpr int TM = 64, TN = 64, TK = 16;
-constexpr int MK = 128;  // matrix-core K step (measured: 128 beats 32 and 64)
+constexpr int KS = 64;  // matrix-core K step
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ inline float ld(const void* p, int64_t off) {
@@ -131,130 +136,158 @@ __device__ inline void ld_vec<uint16_t, 4>(const void* p, int64_t off, float* v)
   v[3] = bf16_to_f32((uint16_t)(a.y >> 16));
 }
 
-// Operand staging flags: bit 0 = read 4 consecutive rows at 2 k (the row axis is
-// contiguous), else 8 consecutive k of one row; bit 1 = the vector loads are
-// aligned (checked on the host).
+// Operand staging flags: bit 0 = the row axis is contiguous (pieces of 8 rows at
+// one k, tile [k][row]), else pieces of 8 k of one row (tile [row][k]); bit 1 =
+// the 16-byte (bf16) or 2 x 16-byte (fp32) loads are aligned (checked on the host).
 constexpr int ST_ROWS = 1, ST_VEC = 2;
 
-// One thread's share of a 64 x KS block of X(row, k) = p[base + row sr + k sk]
-// (rows r0.., k k0..; zero outside R rows and kend), as KS / 32 units of 4
-// packed bf16 pairs.  Unit u = tid + 256 x.
-template <typename T, int KS>
-__device__ inline void stage_load(const void* p, int64_t base, int64_t sr, int64_t sk, int64_t R,
+// LDS tile of an R-row operand: [R][KS + 8] or [KS][R + 8] bf16
+template <int R>
+constexpr int tile_elems() {
+  return R * (KS + 8) > KS * (R + 8) ? R * (KS + 8) : KS * (R + 8);
+}
+
+// This thread's pieces of the R x KS block of X(row, k) = p[base + row sr + k sk]
+// (rows r0.., k k0..; zero outside Rmax rows and kend), 8 bf16 each.  Piece
+// q = tid + 256 x: rows-contiguous: k q / (R / 8), rows 8 (q % (R / 8)) ..;
+// else row q / (KS / 8), k 8 (q % (KS / 8)) ..
+template <typename T, int R>
+__device__ inline void stage_load(const void* p, int64_t base, int64_t sr, int64_t sk, int64_t Rmax,
                                   int64_t r0, int64_t k0, int64_t kend, int flags, int tid,
-                                  uint32_t (&w)[KS / 32][4]) {
+                                  uint4 (&w)[R * KS / 2048]) {
 #pragma unroll
-  for (int x = 0; x < KS / 32; ++x) {
-    const int u = tid + 256 * x;
-    if (!(flags & ST_ROWS)) {  // row r0 + u / (KS / 8), k = k0 + 8 (u % (KS / 8)) + e
-      const int64_t r = r0 + u / (KS / 8), k = k0 + 8 * (u % (KS / 8));
-      float v[8];
-      if ((flags & ST_VEC) && r < R && k + 8 <= kend) {
+  for (int x = 0; x < R * KS / 2048; ++x) {
+    const int q = tid + 256 * x;
+    float v[8];
+    if (flags & ST_ROWS) {
+      const int64_t k = k0 + q / (R / 8), r = r0 + 8 * (q % (R / 8));
+      if ((flags & ST_VEC) && k < kend && r + 8 <= Rmax) {
+        ld_vec<T, 8>(p, base + r + k * sk, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v[e] = (k < kend && r + e < Rmax) ? ld<T>(p, base + (r + e) * sr + k * sk) : 0.f;
+      }
+    } else {
+      const int64_t r = r0 + q / (KS / 8), k = k0 + 8 * (q % (KS / 8));
+      if ((flags & ST_VEC) && r < Rmax && k + 8 <= kend) {
         ld_vec<T, 8>(p, base + r * sr + k, v);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          v[e] = (r < R && k + e < kend) ? ld<T>(p, base + r * sr + (k + e) * sk) : 0.f;
+          v[e] = (r < Rmax && k + e < kend) ? ld<T>(p, base + r * sr + (k + e) * sk) : 0.f;
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[x][e] = pack_bf16_pair(v[2 * e], v[2 * e + 1]);
-    } else {  // rows r0 + 4 (u % 16) + i, k = k0 + 2 (u / 16) + {0, 1}
-      const int64_t r = r0 + 4 * (u & 15), k = k0 + 2 * (u >> 4);
-      float v0[4], v1[4];
-      if ((flags & ST_VEC) && r + 4 <= R) {
-        if (k < kend) ld_vec<T, 4>(p, base + r + k * sk, v0);
-        else v0[0] = v0[1] = v0[2] = v0[3] = 0.f;
-        if (k + 1 < kend) ld_vec<T, 4>(p, base + r + (k + 1) * sk, v1);
-        else v1[0] = v1[1] = v1[2] = v1[3] = 0.f;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v0[i] = (r + i < R && k < kend) ? ld<T>(p, base + (r + i) * sr + k * sk) : 0.f;
-          v1[i] = (r + i < R && k + 1 < kend) ? ld<T>(p, base + (r + i) * sr + (k + 1) * sk) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[x][i] = pack_bf16_pair(v0[i], v1[i]);
     }
+    w[x] = make_uint4(pack_bf16_pair(v[0], v[1]), pack_bf16_pair(v[2], v[3]),
+                      pack_bf16_pair(v[4], v[5]), pack_bf16_pair(v[6], v[7]));
   }
 }
 
-// LDS block [64][KS + 8], k contiguous
-template <int KS>
-__device__ inline void stage_store(uint16_t* Xs, int flags, int tid, const uint32_t (&w)[KS / 32][4]) {
+template <int R>
+__device__ inline void stage_store(uint16_t* Xs, int flags, int tid, const uint4 (&w)[R * KS / 2048]) {
+#pragma unroll
+  for (int x = 0; x < R * KS / 2048; ++x) {
+    const int q = tid + 256 * x;
+    if (flags & ST_ROWS)
+      *(uint4*)(Xs + (q / (R / 8)) * (R + 8) + 8 * (q % (R / 8))) = w[x];
+    else
+      *(uint4*)(Xs + (q / (KS / 8)) * (KS + 8) + 8 * (q % (KS / 8))) = w[x];
+  }
+}
+
+// 16x16x32 operand fragment of rows rb .. rb + 15 and k 32 s .. 32 s + 31 of a
+// staged tile: lane (g, n) gets row rb + n at k index 8 g + 4 h + e <-> k
+// 32 s + 16 h + 4 g + e (h, e < 2, 4), the order the transposing reads produce.
+template <int R>
+__device__ inline bf16x8 frag(const uint16_t* Xs, int flags, int rb, int s, int g4, int n16) {
+  if (flags & ST_ROWS) {
+    constexpr int P = R + 8;
+    const uint16_t* p = Xs + (32 * s + 4 * g4 + (n16 >> 2)) * P + rb + 4 * (n16 & 3);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+    const v4s hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p + 16 * P));
+    const v4s both[2] = {lo, hi};
+    return *(const bf16x8*)both;
+  }
   constexpr int P = KS + 8;
-#pragma unroll
-  for (int x = 0; x < KS / 32; ++x) {
-    const int u = tid + 256 * x;
-    if (!(flags & ST_ROWS)) {
-      *(uint4*)(Xs + (u / (KS / 8)) * P + 8 * (u % (KS / 8))) =
-          make_uint4(w[x][0], w[x][1], w[x][2], w[x][3]);
-    } else {
-      const int r = 4 * (u & 15), k = 2 * (u >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *(uint32_t*)(Xs + (r + i) * P + k) = w[x][i];
-    }
-  }
+  const uint16_t* p = Xs + (rb + n16) * P + 32 * s + 4 * g4;
+  const uint2 lo = *(const uint2*)p, hi = *(const uint2*)(p + 16);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-template <typename TA, typename TB, int KS>
-__global__ __launch_bounds__(256) void gemm_strided_mfma_kernel(StridedGemm g, int ksplit, int fa,
+// Output tile RM x RN; wave (wm, wn) of the 2 x 2 waves owns (RM / 32) x (RN / 32)
+// blocks of 16 x 16 at rows RM / 2 wm + 16 x, columns RN / 2 wn + 16 y.
+template <typename TA, typename TB, int RM, int RN>
+__global__ __launch_bounds__(256, RM == 64 ? 2 : 1) void gemm_strided_mfma_kernel(StridedGemm g, int ksplit, int fa,
                                                                 int fb) {
-  constexpr int P = KS + 8;
-  __shared__ __align__(16) uint16_t As[TM * P];
-  __shared__ __align__(16) uint16_t Bs[TN * P];
+  constexpr int XM = RM / 32, XN = RN / 32;
+  __shared__ __align__(16) uint16_t As[tile_elems<RM>()];
+  __shared__ __align__(16) uint16_t Bs[tile_elems<RN>()];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, n16 = lane & 15;
   const int64_t z = blockIdx.z / ksplit;
   const int split = blockIdx.z % ksplit;
   const int64_t kchunk = ((g.K + ksplit - 1) / ksplit + KS - 1) / KS * KS;
   const int64_t kbeg = split * kchunk, kend = kbeg + kchunk < g.K ? kbeg + kchunk : g.K;
-  const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
+  const int64_t m0 = (int64_t)blockIdx.y * RM, n0 = (int64_t)blockIdx.x * RN;
   const int64_t zq = z / g.zdiv, zr = z % g.zdiv;
   const int64_t abase = zq * g.A.s1 + zr * g.A.s2;
   const int64_t bbase = zq * g.B.s1 + zr * g.B.s2;
   // A is staged as X(row m, k), B as X(row n, k)
-  uint32_t wa[KS / 32][4], wb[KS / 32][4];
+  uint4 wa[RM * KS / 2048], wb[RN * KS / 2048];
   if (kbeg < kend) {
-    stage_load<TA, KS>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, kbeg, kend, fa, tid, wa);
-    stage_load<TB, KS>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, kbeg, kend, fb, tid, wb);
+    stage_load<TA, RM>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, kbeg, kend, fa, tid, wa);
+    stage_load<TB, RN>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, kbeg, kend, fb, tid, wb);
   }
   const int wm = wave >> 1, wn = wave & 1;
-  // fragment rows: lane l supplies row l % 32 of its wave's block, k 8 (l / 32) .. + 8
-  const uint16_t* af = As + (32 * wm + (lane & 31)) * P + 8 * (lane >> 5);
-  const uint16_t* bfp = Bs + (32 * wn + (lane & 31)) * P + 8 * (lane >> 5);
-  f32x16 acc;
+  f32x4 acc[XM][XN];
 #pragma unroll
-  for (int x = 0; x < 16; ++x) acc[x] = 0.f;
+  for (int x = 0; x < XM; ++x)
+#pragma unroll
+    for (int y = 0; y < XN; ++y) acc[x][y] = {0.f, 0.f, 0.f, 0.f};
   for (int64_t k0 = kbeg; k0 < kend; k0 += KS) {
     __syncthreads();  // the previous step's fragment reads are done
-    stage_store<KS>(As, fa, tid, wa);
-    stage_store<KS>(Bs, fb, tid, wb);
+    stage_store<RM>(As, fa, tid, wa);
+    stage_store<RN>(Bs, fb, tid, wb);
     __syncthreads();
     if (k0 + KS < kend) {
-      stage_load<TA, KS>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, k0 + KS, kend, fa, tid, wa);
-      stage_load<TB, KS>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, k0 + KS, kend, fb, tid, wb);
+      stage_load<TA, RM>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, k0 + KS, kend, fa, tid, wa);
+      stage_load<TB, RN>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, k0 + KS, kend, fb, tid, wb);
     }
 #pragma unroll
-    for (int s = 0; s < KS / 16; ++s) {
-      const bf16x8 a = *(const bf16x8*)(af + 16 * s);
-      const bf16x8 b = *(const bf16x8*)(bfp + 16 * s);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    for (int s = 0; s < KS / 32; ++s) {
+      bf16x8 af[XM], bfr[XN];
+#pragma unroll
+      for (int x = 0; x < XM; ++x) af[x] = frag<RM>(As, fa, RM / 2 * wm + 16 * x, s, g4, n16);
+#pragma unroll
+      for (int y = 0; y < XN; ++y) bfr[y] = frag<RN>(Bs, fb, RN / 2 * wn + 16 * y, s, g4, n16);
+#pragma unroll
+      for (int x = 0; x < XM; ++x)
+#pragma unroll
+        for (int y = 0; y < XN; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[x], bfr[y], acc[x][y], 0, 0, 0);
     }
   }
-  // lane l, register x: row 32 wm + 8 (x / 4) + 4 (l / 32) + x % 4, column 32 wn + l % 32
-  const int64_t n = n0 + 32 * wn + (lane & 31);
-  if (n >= g.N) return;
+  // lane (g4, n16), register e of block (x, y): row RM / 2 wm + 16 x + 4 g4 + e,
+  // column RN / 2 wn + 16 y + n16
   const int64_t cbase = zq * g.c1 + zr * g.c2;
 #pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    const int64_t m = m0 + 32 * wm + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
-    if (m >= g.M) continue;
-    float* c = g.C + cbase + m * g.cm + n * g.cn;
-    const float v = g.alpha * acc[x];
-    if (ksplit > 1)
-      atomicAdd(c, v);
-    else
-      *c = g.accumulate ? *c + v : v;
+  for (int y = 0; y < XN; ++y) {
+    const int64_t n = n0 + RN / 2 * wn + 16 * y + n16;
+    if (n >= g.N) continue;
+#pragma unroll
+    for (int x = 0; x < XM; ++x)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = m0 + RM / 2 * wm + 16 * x + 4 * g4 + e;
+        if (m >= g.M) continue;
+        float* c = g.C + cbase + m * g.cm + n * g.cn;
+        const float v = g.alpha * acc[x][y][e];
+        if (ksplit > 1)
+          atomicAdd(c, v);
+        else
+          *c = g.accumulate ? *c + v : v;
+      }
   }
 }
 
@@ -274,45 +307,46 @@ __global__ void zero_c_kernel(StridedGemm g) {
 // Staging flags of an operand read as X(row, k) = p[... + row sr + k sk] (see stage_load).
 int stage_flags(const StridedOperand& o, int64_t sr, int64_t sk, int dtype) {
   const uintptr_t p = (uintptr_t)o.p;
-  if (sk == 1) {  // 8 consecutive k: 16-byte loads at offsets that are multiples of 4 / 8
-    const int64_t q = dtype == 0 ? 4 : 8;
+  const int64_t q = dtype == 0 ? 4 : 8;  // elements per aligned 16-byte load
+  if (sk == 1) {  // 8 consecutive k: offsets row sr + k (k % 8 == 0)
     const bool vec = p % 16 == 0 && sr % q == 0 && o.s1 % q == 0 && o.s2 % q == 0;
     return vec ? ST_VEC : 0;
   }
-  if (sr == 1) {  // 4 consecutive rows: 16 (fp32) or 8 (bf16) bytes at multiples of 4
-    const bool vec = p % (dtype == 0 ? 16 : 8) == 0 && sk % 4 == 0 && o.s1 % 4 == 0 &&
-                     o.s2 % 4 == 0;
+  if (sr == 1) {  // 8 consecutive rows: offsets row + k sk (row % 8 == 0)
+    const bool vec = p % 16 == 0 && sk % q == 0 && o.s1 % q == 0 && o.s2 % q == 0;
     return ST_ROWS | (vec ? ST_VEC : 0);
   }
   return 0;  // neither axis contiguous: element loads
 }
 
-template <int KS>
+template <int RM, int RN>
 void launch_mfma_variant(const StridedGemm& g, dim3 grid, int k, int fa, int fb, hipStream_t s) {
   if (g.a_dtype == 0 && g.b_dtype == 0)
-    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, float, KS>), grid, dim3(256), 0, s, g, k, fa,
-                       fb);
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, float, RM, RN>), grid, dim3(256), 0, s, g, k,
+                       fa, fb);
   else if (g.a_dtype == 0 && g.b_dtype == 1)
-    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, uint16_t, KS>), grid, dim3(256), 0, s, g, k,
-                       fa, fb);
-  else if (g.a_dtype == 1 && g.b_dtype == 0)
-    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, float, KS>), grid, dim3(256), 0, s, g, k,
-                       fa, fb);
-  else
-    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, uint16_t, KS>), grid, dim3(256), 0, s, g,
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, uint16_t, RM, RN>), grid, dim3(256), 0, s, g,
                        k, fa, fb);
+  else if (g.a_dtype == 1 && g.b_dtype == 0)
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, float, RM, RN>), grid, dim3(256), 0, s, g,
+                       k, fa, fb);
+  else
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, uint16_t, RM, RN>), grid, dim3(256), 0, s,
+                       g, k, fa, fb);
 }
 
 hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  if (g.zdiv <= 0 || g.batch > 65535 || (g.N + TN - 1) / TN > 0x7fffffff ||
-      (g.M + TM - 1) / TM > 65535)
-    return hipErrorInvalidValue;
-  // Split K when the tiles alone leave the GPU short of workgroups (about two per
-  // CU for the matrix-core kernel, four for the fp32 one), each split at least 256
-  // deep; the splits add atomically.
-  const int64_t wg_target = g.bf16_mfma ? 512 : 1024;
-  const int64_t tiles = ((g.N + TN - 1) / TN) * ((g.M + TM - 1) / TM) * g.batch;
+  if (g.zdiv <= 0 || g.batch > 65535) return hipErrorInvalidValue;
+  // matrix cores: 128 x 128 tiles when both output sides reach 128
+  const bool big = g.bf16_mfma && g.M >= 128 && g.N >= 128;
+  const int64_t tm = big ? 128 : 64, tn = big ? 128 : 64;
+  if ((g.N + tn - 1) / tn > 0x7fffffff || (g.M + tm - 1) / tm > 65535) return hipErrorInvalidValue;
+  // Split K when the tiles alone leave the GPU short of workgroups (about one per
+  // CU for the matrix-core kernel, four for the fp32 one; measured), each split at
+  // least 256 deep; the splits add atomically.
+  const int64_t wg_target = g.bf16_mfma ? 256 : 1024;
+  const int64_t tiles = ((g.N + tn - 1) / tn) * ((g.M + tm - 1) / tm) * g.batch;
   int64_t ks = (wg_target + tiles - 1) / tiles;
   if (ks > g.K / 256) ks = g.K / 256;
   if (ks > 16) ks = 16;
@@ -322,13 +356,16 @@ hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((unsigned)((g.N + TN - 1) / TN), (unsigned)((g.M + TM - 1) / TM),
+  const dim3 grid((unsigned)((g.N + tn - 1) / tn), (unsigned)((g.M + tm - 1) / tm),
                   (unsigned)(g.batch * ks));
   const int k = (int)ks;
   if (g.bf16_mfma) {
     const int fa = stage_flags(g.A, g.A.si, g.A.sj, g.a_dtype);
     const int fb = stage_flags(g.B, g.B.sj, g.B.si, g.b_dtype);
-    launch_mfma_variant<MK>(g, grid, k, fa, fb, s);
+    if (big)
+      launch_mfma_variant<128, 128>(g, grid, k, fa, fb, s);
+    else
+      launch_mfma_variant<64, 64>(g, grid, k, fa, fb, s);
     return hipGetLastError();
   }
   if (g.a_dtype == 0 && g.b_dtype == 0)
