@@ -71,6 +71,53 @@ def layer_flops(w):
     return gemm + attn_flops(w)
 
 
+def layer_bwd_flops(w):
+    """Algorithmic FLOPs of one layer's backward (txl_layer_step_bwd) with its
+    forward recompute: the forward (layer_flops), then per projection y = x W^T
+    the two products dX = dY W and dW = dY^T X (dX only for the current rows: the
+    memory's gradient is stopped; none for R), and the attention backward at 16 d
+    per causal pair (scores' content and position terms, dP, dV, dq's two terms,
+    dk, dr)."""
+    T = w.M + w.L
+    HD = w.H * w.d
+    BL = w.B * w.L
+    dW = 2 * (BL * HD * w.D + 2 * w.B * T * HD * w.D + T * HD * w.D + BL * w.D * HD)
+    dX = 2 * (BL * HD * w.D + 2 * BL * HD * w.D + BL * w.D * HD)
+    P = w.L * w.M + w.L * (w.L + 1) // 2
+    return layer_flops(w) + dW + dX + 16 * w.d * P * w.B * w.H
+
+
+def cpu_baseline_train(w, x, target_s):
+    """The backward oracle, as it stands, on the host cores: one layer's forward +
+    backward (oracle_bwd.layer_step_bwd) on a sample of the batch rows, scaled to
+    query tokens/s of the training step (every layer once per segment)."""
+    import numpy as np
+    from oracle import oracle as O
+    from oracle import oracle_bwd as OB
+    g = np.random.default_rng(1).standard_normal((w.B, w.L, w.D))
+
+    def run(b, n):
+        t0 = time.perf_counter()
+        for r in range(n):
+            Wl = x["weights"][r % len(x["weights"])]
+            OB.layer_step_bwd(x["h0"][0][:b], x["mem"][0][:b], Wl, x["u"], x["v"], x["R"],
+                              g[:b])
+        return time.perf_counter() - t0
+
+    t1 = run(1, 1)
+    n = max(1, int(round(target_s / max(t1, 1e-3))))
+    t = run(1, n) if n > 1 else t1
+    return {
+        "value": n * w.L / (t * w.n_layers),
+        "unit": "query tokens/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{n} fp64 layer forward + backward passes (oracle_bwd.layer_step_bwd) over "
+                   f"1 of the {w.B} batch rows at full memory ({w.M} rows), {t:.1f} s in all; "
+                   f"rate scaled by 1/{w.n_layers} layers to match the stack"),
+    }
+
+
 def read_traffic():
     """HBM bytes per attention launch from the committed rocprofv3 counter summary,
     or None when the kernel source changed since the counters were taken."""
@@ -264,8 +311,9 @@ def train_step(args):
     b1.record(stream)
     torch.cuda.synchronize()
     bwd_ms = b0.elapsed_time(b1) / 5
+    bwd_tflops = layer_bwd_flops(w) / (bwd_ms / 1e3) / 1e12
     tokens = w.B * w.L * w.n_segments
-    print(json.dumps({
+    res = {
         "metric": "training step (forward + backward, stop-gradient memory): query tokens/s",
         "value": tokens / (ms / 1e3), "unit": "query tokens/s", "n_gpus": 1, "steps": steps,
         "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
@@ -274,9 +322,15 @@ def train_step(args):
                    "segment_len": w.L, "mem_len": w.M, "n_layers": w.n_layers,
                    "n_segments": w.n_segments},
         "layer_bwd_ms": bwd_ms,
+        "roofline": {"bound": "mfma", "kernel": "txl_layer_step_bwd (one layer, all kernels)",
+                     "achieved": bwd_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": bwd_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flop_per_call": layer_bwd_flops(w)},
         "note": "backward = txl_layer_step_bwd per layer (recomputes the layer's forward); "
-                "the upstream gradient of the top layer is synthetic; no optimizer update"}),
-          flush=True)
+                "the upstream gradient of the top layer is synthetic; no optimizer update"}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_train(w, x, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
 
 
 def eval_speed(args):
