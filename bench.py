@@ -50,6 +50,10 @@ def parse():
                    help="instead of the throughput line, print the per-token evaluation time "
                         "with memory against the vanilla recompute of the window (the pages' "
                         "Table 9 comparison) at attention lengths 800 .. 3800")
+    p.add_argument("--vendor-sdpa", action="store_true",
+                   help="instead of the throughput line, time this library's attention and "
+                        "torch's fused scaled-dot-product attention (no position term) on the "
+                        "same causal-over-memory pairs of the workload's shape")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (reads 256 MiB, writes 256 MiB) "
                         "so that a counter run can calibrate FETCH_SIZE / WRITE_SIZE")
@@ -333,6 +337,66 @@ def train_step(args):
     print(json.dumps(res), flush=True)
 
 
+def vendor_sdpa(args):
+    """Context for the attention kernel: torch's fused attention (the vendor
+    stack's flash / memory-efficient kernels, selected explicitly so that no
+    unfused fallback runs) on the same (query, key) pairs -- L queries over
+    M + L keys, query i seeing keys 0 .. M + i -- but without the position term,
+    against txl_rel_attn_fwd with it, both bf16 with HIP events.  Rates are given
+    per causal pair, since the two compute different amounts per pair."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    from torch.nn.attention.bias import causal_lower_right
+    from relative_position_memory_amd import inputs as I
+    from relative_position_memory_amd import txl
+
+    w = I.workload(args.workload)
+    B, H, L, M, d = w.B, w.H, w.L, w.M, w.d
+    T = M + L
+    pairs = (L * M + L * (L + 1) // 2) * B * H
+    rng = np.random.default_rng(0)
+    bf = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    q, k, v, r = bf(B, L, H, d), bf(B, T, H, d), bf(B, T, H, d), bf(T, H, d)
+    u, vb = bf(H, d) * 0.1, bf(H, d) * 0.1
+    out = torch.empty_like(q)
+    nws = txl.rel_attn_workspace_bytes(torch.bfloat16, B, H, L, M, d)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
+    qh, kh, vh = (x.transpose(1, 2).contiguous() for x in (q, k, v))  # [B, H, rows, d]
+    mask = causal_lower_right(L, T)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    res = {"workload": w.name, "batch": B, "n_head": H, "d_head": d, "segment_len": L,
+           "mem_len": M, "causal_pairs": pairs}
+    us = timed(lambda: txl.rel_attn_fwd(q, k, v, r, u, vb, M, out, workspace=ws), args.attn_reps)
+    res["txl_rel_attn_fwd"] = {"us": us, "Gpairs_per_s": pairs / us / 1e3,
+                               "note": "content and position terms, bf16 MFMA"}
+    for name, be in (("sdpa_flash", SDPBackend.FLASH_ATTENTION),
+                     ("sdpa_efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([be]):
+                us = timed(lambda: F.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask),
+                           args.attn_reps)
+            res[name] = {"us": us, "Gpairs_per_s": pairs / us / 1e3,
+                         "note": "content term only (no position term, no biases)"}
+        except RuntimeError as ex:  # backend not built for this shape or device
+            res[name] = {"unavailable": str(ex)[:200]}
+    print(json.dumps(res), flush=True)
+
+
 def eval_speed(args):
     """Per-token evaluation time with memory against the vanilla model that
     recomputes the whole window for every prediction ([XL] section 4.5, Table 9):
@@ -456,6 +520,9 @@ def main():
 
     if args.eval_speed:
         eval_speed(args)
+        return
+    if args.vendor_sdpa:
+        vendor_sdpa(args)
         return
     if args.train:
         train_step(args)

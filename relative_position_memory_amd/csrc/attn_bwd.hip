@@ -382,8 +382,9 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s) {
   g.C = a.dv; g.c1 = T * H * d; g.c2 = d; g.cm = H * d; g.cn = 1;
   g.alpha = 1.f; g.accumulate = 0; g.a_dtype = 0; g.b_dtype = (dtype == 1 && !a.dout_f32) ? 1 : 0;
   g.bf16_mfma = dtype == 1 ? 1 : 0;  // bf16 inputs: P and dS enter the products as bf16
+  g.a_dtype = dtype == 1 ? 1 : 0;     // and the matrix-core rows kernel stores them so
   if ((e = launch_gemm_strided(g, s)) != hipSuccess) return e;
-  g.A.p = a.dS;
+  g.A.p = a.dS;  // (bf16 path: P and dS are stored as bf16)
   g.B = {a.qc, H * a.L * DP, a.L * DP, DP, 1};
   g.b_dtype = 0;
   g.C = a.dk;

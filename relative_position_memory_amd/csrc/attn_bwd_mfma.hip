@@ -2,8 +2,9 @@
 // (Transformer-XL, section 3.3: score with content and position terms and the
 // global biases u and v; Appendix B: key j of query i at distance mem_len+i-j).
 // It replaces the fp32 rows kernel for bf16 inputs and writes the same things:
-// P and dS of every pair (fp32 scratch for the key-side products), dq, and this
-// block's shares of du and dv; the gradients sum in fp32.
+// P and dS of every pair (here as bf16 scratch, the precision in which the
+// key-side products take them), dq, and this block's shares of du and dv; the
+// gradients sum in fp32.
 //
 // One workgroup = 4 waves = 64 queries of one (batch, head); wave w owns queries
 // 16 w .. 16 w + 15 of the block.  All products are v_mfma_f32_16x16x32_bf16 and
@@ -289,17 +290,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
         dS[kb][e] = p * (dP[kb][e] - Dd);
         S[kb][e] = p;
       }
-    if (qok) {
+    if (qok) {  // bf16 rows of P and dS (they enter the key-side products as bf16)
+      uint16_t* prow_p = (uint16_t*)a.P + prow;
+      uint16_t* prow_s = (uint16_t*)a.dS + prow;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = j0 + 16 * kb + 4 * g4 + e;
+      for (int kb = 0; kb < 4; ++kb) {
+        const int j = j0 + 16 * kb + 4 * g4;  // 4 consecutive keys j .. j + 3
+        if ((T & 3) == 0) {  // 8-byte aligned
           if (j < T) {
-            a.P[prow + j] = S[kb][e];
-            a.dS[prow + j] = dS[kb][e];
+            *(uint2*)(prow_p + j) = make_uint2(pack2(S[kb][0], S[kb][1]), pack2(S[kb][2], S[kb][3]));
+            *(uint2*)(prow_s + j) =
+                make_uint2(pack2(dS[kb][0], dS[kb][1]), pack2(dS[kb][2], dS[kb][3]));
           }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < T) {
+              prow_p[j + e] = __builtin_bit_cast(uint16_t, (__bf16)S[kb][e]);
+              prow_s[j + e] = __builtin_bit_cast(uint16_t, (__bf16)dS[kb][e]);
+            }
         }
+      }
     }
     // dS by distance row: key jj of query n16 is row n16 + 63 - jj
 #pragma unroll
@@ -339,8 +350,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
     const int span = T - nkb * BK;
     const int ii = e / span, j = nkb * BK + e % span, iq = i0 + ii;
     if (iq < L) {
-      a.P[((int64_t)z * L + iq) * T + j] = 0.f;
-      a.dS[((int64_t)z * L + iq) * T + j] = 0.f;
+      ((uint16_t*)a.P)[((int64_t)z * L + iq) * T + j] = 0;
+      ((uint16_t*)a.dS)[((int64_t)z * L + iq) * T + j] = 0;
     }
   }
   // dq, and this block's shares of du and dv
@@ -424,7 +435,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dr_mfma_kernel(AttnBwdArgs a, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int p = p0 + f4 + e, j = len + i - p;
-          v[r][e] = (i < L && p < T && j >= 0) ? a.dS[(z * L + i) * T + j] : 0.f;
+          v[r][e] = (i < L && p < T && j >= 0)
+                        ? bf16_to_f32(((const uint16_t*)a.dS)[(z * L + i) * T + j])
+                        : 0.f;
         }
         if (i < L) {
           const float4 f = *(const float4*)(a.qp + (z * L + i) * DP + f4);
