@@ -144,6 +144,9 @@ __device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// LSE: also write each query's log-sum-exp (AttnArgs::lse).  A separate
+// instantiation, so the plain forward's code is untouched by it.
+template <bool LSE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, int groups) {
   extern __shared__ __align__(16) char smem_raw[];
   Smem& sm = *(Smem*)smem_raw;
@@ -645,7 +648,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
     const int i = i0w + 16 * gm + n16;
     if (i >= L) continue;
     const float inv = 1.f / l_tot[gm];
-    if (a.lse && g4 == 0) a.lse[(int64_t)g * L + i] = s_off[gm] + __log2f(l_tot[gm]);
+    if constexpr (LSE) {
+      if (g4 == 0) a.lse[(int64_t)g * L + i] = s_off[gm] + __log2f(l_tot[gm]);
+    }
     uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
     const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
                      ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
@@ -978,8 +983,11 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
   const size_t smem = sizeof(Smem);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)attn_mfma_kernel<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -993,8 +1001,12 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(attn_mfma_kernel, dim3((unsigned)nblocks), dim3(256), smem, s, a, nqt,
-                     groups);
+  if (a.lse)
+    hipLaunchKernelGGL(attn_mfma_kernel<true>, dim3((unsigned)nblocks), dim3(256), smem, s, a, nqt,
+                       groups);
+  else
+    hipLaunchKernelGGL(attn_mfma_kernel<false>, dim3((unsigned)nblocks), dim3(256), smem, s, a, nqt,
+                       groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.slots == 0 || !a.plan.ext_merge) return e;
   hipLaunchKernelGGL(attn_part_merge_kernel, dim3((unsigned)nqt, (unsigned)groups), dim3(256), 0,
