@@ -128,9 +128,13 @@ size_t txl_rel_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L,
  * (else TXL_EUNSUPPORTED).  The forward's output is not needed: the softmax
  * statistics are recomputed.  Gradients are fp32, dense and written whole:
  *   dq [B][L][H][d]  dk, dv [B][T][H][d]  dr [T][H][d]  du, dvb [H][d]
+ * Precision: fp32 inputs are differentiated in fp32 throughout; bf16 inputs on
+ * the bf16 matrix cores with fp32 sums, where P, dS, dout, q + u and q + v
+ * enter the products rounded to bf16 (as P enters the forward's P V).
  * workspace (required): device scratch of txl_rel_attn_bwd_workspace_bytes()
- * bytes; it holds P and dS [B][H][L][T] in fp32.  Gradients, workspace and
- * inputs must not overlap.  Returns TXL_OK or a txl_status.
+ * bytes; it holds P and dS [B][H][L][T] (fp32, or bf16 for bf16 inputs).
+ * Gradients, workspace and inputs must not overlap.  Returns TXL_OK or a
+ * txl_status.
  */
 int txl_rel_attn_bwd(void* stream, int dtype,
                      int64_t B, int64_t H, int64_t L, int64_t mem_len, int64_t d_head,
@@ -255,6 +259,9 @@ size_t txl_layer_bwd_workspace_bytes(const txl_layer_dims* dims, int64_t mem_cap
  *   dW_q = dq^T h_in,  dW_kE = dk^T ctx,  dW_v = dv^T ctx,  dW_kR = dr^T R[0:T]
  *   dh  = dy + dq W_q + (dk W_kE + dv W_v) restricted to the current rows
  * with ctx = [memory ; h_in].  Every gradient is written whole (not accumulated).
+ * bf16 layers run every product on the bf16 matrix cores (operands rounded to
+ * bf16, fp32 sums) and take the attention's softmax statistics from the
+ * recomputed forward; fp32 layers stay in fp32 throughout.
  *   g          gradient pointers (all required; they must not overlap each other,
  *              the inputs or the workspace).
  *   workspace  device scratch of ws_bytes >= txl_layer_bwd_workspace_bytes(dims,
