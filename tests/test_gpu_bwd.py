@@ -72,6 +72,8 @@ def _run(c, dout, M, dtype, layout="bthd"):
     ("fp32", 2, 1, 65, 0, 32, "bthd"),      # no memory
     ("bf16", 1, 2, 1, 100, 64, "bthd"),     # one query over a memory
     ("fp32", 1, 1, 200, 333, 48, "bhtd"),   # memory longer than the segment
+    ("bf16", 2, 1, 65, 0, 32, "bthd"),      # no memory, matrix-core path
+    ("bf16", 1, 2, 200, 333, 64, "bhtd"),   # long memory, matrix-core path, T % 4 = 1
 ])
 def test_attn_bwd_matches_oracle(dtype, B, H, L, M, d, layout):
     c = I.attention_inputs(B, H, L, M, d, seed=3 * L + M + d, sigma=1.0, sigma_uv=0.5,
@@ -131,6 +133,7 @@ GRAD_NAMES = [("dh", "dh"), ("dW_q", "dW_q"), ("dW_kE", "dW_kE"), ("dW_v", "dW_v
     ("fp32", "tiny", {"B": 2, "L": 37, "M": 50, "d": 12, "H": 3, "D": 40}, 45, 31),  # ring wrap
     ("bf16", "charlm", {"B": 2, "L": 64, "M": 64, "D": 128, "H": 2, "d": 64}, 64, 0),
     ("bf16", "charlm", {"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
+    ("bf16", "charlm", {"B": 2, "L": 64, "M": 64, "D": 128, "H": 2, "d": 64}, 0, 0),  # empty memory
     # 128-wide product tiles with a ragged half tile, K split across workgroups
     ("bf16", "charlm", {"B": 2, "L": 96, "M": 160, "D": 192, "H": 3, "d": 64}, 160, 37),
 ])
