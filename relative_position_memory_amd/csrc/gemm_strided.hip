@@ -352,7 +352,7 @@ hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s) {
   if (ks > 16) ks = 16;
   if (ks < 1 || g.batch * ks > 65535) ks = 1;
   if (ks > 1 && !g.accumulate) {
-    hipLaunchKernelGGL(zero_c_kernel, dim3(256), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(zero_c_kernel, dim3(1024), dim3(256), 0, s, g);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

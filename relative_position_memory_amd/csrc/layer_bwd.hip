@@ -5,6 +5,8 @@
 // LayerNorm backward, the copies and the gather of [memory ; h_in].
 #include "txl_internal.h"
 
+#include <type_traits>
+
 namespace txl {
 namespace {
 
@@ -93,18 +95,21 @@ __global__ __launch_bounds__(256) void ln_bwd_cols_kernel(const float* y, const 
   atomicAdd(dbeta + c, sb);
 }
 
-// ctx[b][t] = t < len ? ring[b][(start + t) % cap] : h[b][t - len]   (rows of D elements)
-template <typename E>
+// ctx[b][t] = t < len ? ring[b][(start + t) % cap] : h[b][t - len]   (rows of D elements),
+// in groups of G consecutive elements of a row (16-byte copies when D % G == 0 and
+// the three buffers are 16-byte aligned, else G = 1).
+template <typename E, int G>
 __global__ void gather_ctx_kernel(const void* ring, int64_t cap, int64_t start, int64_t len,
                                   const void* h, int64_t B, int64_t L, int64_t D, void* ctx) {
-  const int64_t T = len + L, n = B * T * D;
+  typedef typename std::conditional<G == 1, E, uint4>::type V;
+  const int64_t T = len + L, DG = D / G, n = B * T * DG;
   for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
        x += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t c = x % D, bt = x / D, t = bt % T, b = bt / T;
+    const int64_t c = x % DG, bt = x / DG, t = bt % T, b = bt / T;
     int64_t slot = start + t;
     slot = slot >= cap ? slot - cap : slot;
-    ((E*)ctx)[x] = t < len ? ((const E*)ring)[(b * cap + slot) * D + c]
-                           : ((const E*)h)[(b * L + (t - len)) * D + c];
+    ((V*)ctx)[x] = t < len ? ((const V*)ring)[(b * cap + slot) * DG + c]
+                           : ((const V*)h)[(b * L + (t - len)) * DG + c];
   }
 }
 
@@ -129,7 +134,7 @@ hipError_t launch_ln_bwd(int dtype, const float* y, const void* gamma, const voi
   hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(D)), dim3(256), 0, s, dgamma, D);
   hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(D)), dim3(256), 0, s, dbeta, D);
   if (M > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int64_t rows = 128;
+  const int64_t rows = 16;  // enough row chunks to fill the GPU
   const dim3 gc((unsigned)((D + 255) / 256), (unsigned)((M + rows - 1) / rows));
   if (dtype == 1) {
     hipLaunchKernelGGL(ln_bwd_rows_kernel<uint16_t>, dim3((unsigned)M), dim3(256), 0, s, y, gamma,
@@ -149,12 +154,21 @@ hipError_t launch_gather_ctx(int dtype, const void* ring, int64_t cap, int64_t s
                              const void* h, int64_t B, int64_t L, int64_t D, void* ctx,
                              hipStream_t s) {
   const int64_t n = B * (len + L) * D;
-  if (dtype == 1)
-    hipLaunchKernelGGL(gather_ctx_kernel<uint16_t>, dim3(grid_for(n)), dim3(256), 0, s, ring, cap,
-                       start, len, h, B, L, D, ctx);
+  const int64_t per16 = dtype == 1 ? 8 : 4;  // elements per 16 bytes
+  const bool vec = D % per16 == 0 &&
+                   (((uintptr_t)ring | (uintptr_t)h | (uintptr_t)ctx) % 16) == 0;
+  if (vec && dtype == 1)
+    hipLaunchKernelGGL((gather_ctx_kernel<uint16_t, 8>), dim3(grid_for(n / 8)), dim3(256), 0, s,
+                       ring, cap, start, len, h, B, L, D, ctx);
+  else if (vec)
+    hipLaunchKernelGGL((gather_ctx_kernel<float, 4>), dim3(grid_for(n / 4)), dim3(256), 0, s, ring,
+                       cap, start, len, h, B, L, D, ctx);
+  else if (dtype == 1)
+    hipLaunchKernelGGL((gather_ctx_kernel<uint16_t, 1>), dim3(grid_for(n)), dim3(256), 0, s, ring,
+                       cap, start, len, h, B, L, D, ctx);
   else
-    hipLaunchKernelGGL(gather_ctx_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, ring, cap,
-                       start, len, h, B, L, D, ctx);
+    hipLaunchKernelGGL((gather_ctx_kernel<float, 1>), dim3(grid_for(n)), dim3(256), 0, s, ring,
+                       cap, start, len, h, B, L, D, ctx);
   return hipGetLastError();
 }
 
