@@ -182,13 +182,22 @@ int run_gemm(int dtype, const txl::GemmArgs& g, hipStream_t st, const char* what
 
 // h_out = LayerNorm(a W_o^T + h_in) * gamma + beta (section 3.3), a [B*L][H*d]
 // token-major; y: fp32 [B*L][D] scratch for the unfused form.
+// Whether run_out_ln takes the fused kernel (else it writes y = a W_o^T + h_in,
+// fp32, before the LayerNorm).
+bool out_ln_fused(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
+                  const void* h_in, void* h_out) {
+  const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
+  txl::LnArgs ln{BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
+  // (a few rows, as in a decode step, go to the skinny GEMM and the row kernel)
+  return dtype == TXL_BF16 && BL > 32 && txl::gemm_ln_supported(ln);
+}
+
 int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
                const void* h_in, void* h_out, float* y, hipStream_t st) {
   const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
   // one fused kernel when the rows fit it
   txl::LnArgs ln{BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
-  // (a few rows, as in a decode step, go to the skinny GEMM and the row kernel)
-  if (dtype == TXL_BF16 && BL > 32 && txl::gemm_ln_supported(ln)) {
+  if (out_ln_fused(dtype, dm, a, w, h_in, h_out)) {
     const hipError_t e = txl::launch_gemm_ln(ln, st);
     if (e != hipSuccess) return hip_fail(e, "output projection + LayerNorm");
     return TXL_OK;
@@ -334,13 +343,16 @@ int txl_layer_workspace_map(const txl_layer_dims* dims, int64_t mem_len, int dty
 }
 
 // The layer step; with lse != NULL the matrix-core attention also writes each
-// query's log-sum-exp there ([B][H][L]) and *lse_written says whether it did.
+// query's log-sum-exp there ([B][H][L]) and *lse_written says whether it did;
+// *y_written (if given) says whether the workspace holds y = a W_o^T + h_in.
 static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
                           const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
                           const void* v_bias, const void* R, int64_t R_rows, void* h_out,
-                          void* workspace, size_t ws_bytes, float* lse, bool* lse_written) {
+                          void* workspace, size_t ws_bytes, float* lse, bool* lse_written,
+                          bool* y_written = nullptr) {
   g_detail[0] = 0;
   if (lse_written) *lse_written = false;
+  if (y_written) *y_written = false;
   if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
   int rc = check_dims(dims);
   if (rc != TXL_OK) return rc;
@@ -432,6 +444,7 @@ static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, c
     *lse_written = true;
   }
   if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
+  if (y_written) *y_written = !out_ln_fused(dtype, dm, a, w, h_in, h_out);
   return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st);
 }
 
@@ -853,10 +866,10 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
   char* base = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   // the forward again, for q, k, v, r and a (it also checks the remaining arguments)
-  bool have_lse = false;
+  bool have_lse = false, have_y = false;
   rc = layer_step_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows,
                       base + bw.hout, base + bw.fwd, bw.hout - bw.fwd, (float*)(base + bw.lse),
-                      &have_lse);
+                      &have_lse, &have_y);
   if (rc != TXL_OK) return rc;
   const WsLayout fl = ws_layout(dm, T, es);
   char* fb = base + bw.fwd;
@@ -866,7 +879,9 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
   const void* r = fb + fl.r;
   const void* a = fb + fl.a;
   const int64_t dp = fl.dp;
-  float* y = (float*)(base + bw.y);
+  // y = a W_o^T + h_in: the forward's own when it wrote one (the unfused output
+  // projection), else recomputed below
+  float* y = have_y ? (float*)(fb + fl.y) : (float*)(base + bw.y);
   float* dy = (float*)(base + bw.dy);
   float* da = (float*)(base + bw.da);
   float* dq = (float*)(base + bw.dq);
@@ -878,8 +893,10 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
   hipError_t e;
 #define TXL_TRY(x, what) do { if ((e = (x)) != hipSuccess) return hip_fail(e, what); } while (0)
   // y = a W_o^T + h_in (the LayerNorm input), then the LayerNorm backward
-  TXL_TRY(txl::launch_to_f32(dt, h_in, y, BL * D, st), "copy");
-  TXL_TRY(sgemm(st, BL, D, HD, a, dt, HD, 1, w->W_o, dt, 1, HD, y, D, true), "y");
+  if (!have_y) {
+    TXL_TRY(txl::launch_to_f32(dt, h_in, y, BL * D, st), "copy");
+    TXL_TRY(sgemm(st, BL, D, HD, a, dt, HD, 1, w->W_o, dt, 1, HD, y, D, true), "y");
+  }
   TXL_TRY(txl::launch_ln_bwd(dt, y, w->ln_gamma, dh_out, BL, D, dm.ln_eps, dy,
                              (float*)(base + bw.mean), (float*)(base + bw.rstd), g->dgamma,
                              g->dbeta, st), "layernorm backward");
