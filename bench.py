@@ -247,8 +247,8 @@ def train_step(args):
     """Training step with a stop-gradient memory ([XL] section 3.2) at the Large
     train-shape (batch 8, d_model 1024, 16 heads of 64, L = M = 384, 18 layers,
     4 segments, bf16).  Per segment: the forward through every layer
-    (txl_layer_step, keeping each layer's input), then the backward from the top
-    (txl_layer_step_bwd, which recomputes its layer's forward; the upstream
+    (txl_layer_step_save, keeping each layer's input and what its backward needs),
+    then the backward from the top (txl_layer_step_bwd_saved; the upstream
     gradient of the top layer is a fixed synthetic tensor, the gradient of each
     layer's input feeds the layer below), then the memory updates.  The weight
     gradients are written per layer (no optimizer update is part of the step).
@@ -269,9 +269,11 @@ def train_step(args):
     rings = [txl.make_ring(dd, 0, w.M) for dd in ring_data]
     h0 = dev(x["h0"])
     dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
-    ws = torch.empty(txl.workspace_bytes(dims, w.M, tdt), dtype=torch.uint8, device="cuda")
     bws = torch.empty(txl.layer_bwd_workspace_bytes(dims, w.M, tdt), dtype=torch.uint8,
                       device="cuda")
+    nsv = txl.layer_saved_bytes(dims, w.M, tdt)
+    sbufs = [torch.empty(nsv, dtype=torch.uint8, device="cuda") for _ in range(w.n_layers)]
+    saved = [None] * w.n_layers
     hs = [torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(w.n_layers + 1)]
     rng = np.random.default_rng(1)
     g_top = dev(rng.standard_normal((w.B, w.L, w.D)).astype(np.float32))
@@ -284,12 +286,12 @@ def train_step(args):
         for s in range(w.n_segments):
             hs[0].copy_(h0[s])
             for n in range(w.n_layers):
-                txl.layer_step(dims, hs[n], rings[n], lws[n], u, vb, R, hs[n + 1], ws,
-                               stream=stream)
+                saved[n] = txl.layer_step_save(dims, hs[n], rings[n], lws[n], u, vb, R,
+                                               hs[n + 1], sbufs[n], stream=stream)
             g = g_top
             for n in reversed(range(w.n_layers)):
                 grads = txl.layer_step_bwd(dims, hs[n], rings[n], lws[n], u, vb, R, g, bws,
-                                           grads=grads, stream=stream)
+                                           grads=grads, stream=stream, saved=saved[n])
                 g_cur.copy_(grads["dh"])  # the next layer down takes dh in the layers' dtype
                 g = g_cur
             for n in range(w.n_layers):
@@ -306,7 +308,8 @@ def train_step(args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    # one layer's backward alone (HIP events on the same stream)
+    # one layer's backward alone, with its forward recomputed (txl_layer_step_bwd),
+    # HIP events on the same stream
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for _ in range(5):
@@ -330,8 +333,10 @@ def train_step(args):
                      "achieved": bwd_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": bwd_tflops / PEAK_BF16_TFLOPS, "traffic": None,
                      "flop_per_call": layer_bwd_flops(w)},
-        "note": "backward = txl_layer_step_bwd per layer (recomputes the layer's forward); "
-                "the upstream gradient of the top layer is synthetic; no optimizer update"}
+        "note": "forward = txl_layer_step_save, backward = txl_layer_step_bwd_saved per layer "
+                "(no recompute); layer_bwd_ms and the roofline time txl_layer_step_bwd, which "
+                "recomputes the layer's forward; the upstream gradient of the top layer is "
+                "synthetic; no optimizer update"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_train(w, x, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -275,6 +275,40 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims,
                        void* workspace, size_t ws_bytes);
 
 /*
+ * Training without the forward recompute.  txl_layer_step_save is
+ * txl_layer_step that keeps, in caller-owned device memory, what
+ * txl_layer_step_bwd would otherwise recompute (q, k, v, r, the attention output
+ * and, where the forward has them, its softmax statistics and LayerNorm input);
+ * txl_layer_step_bwd_saved is txl_layer_step_bwd that takes them from there.
+ * The arguments of the two calls must be the same (and the memory unchanged in
+ * between), as in a training step: forward through the stack, then backward.
+ *   saved->data   device memory of saved->bytes >= txl_layer_saved_bytes(dims,
+ *                 mem->capacity, dtype), 256-byte aligned, not overlapping any
+ *                 other argument; owned by the caller, alive until the backward.
+ *   saved->has_lse, saved->has_y   written by txl_layer_step_save (host side),
+ *                 read by txl_layer_step_bwd_saved.
+ * The backward's workspace and results are txl_layer_step_bwd's.  Returns TXL_OK
+ * or a txl_status.
+ */
+typedef struct {
+  void*  data;
+  size_t bytes;
+  int    has_lse;  /* the softmax statistics are in data */
+  int    has_y;    /* the fp32 LayerNorm input is in data */
+} txl_layer_saved;
+
+size_t txl_layer_saved_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype);
+int txl_layer_step_save(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                        const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
+                        const void* v_bias, const void* R, int64_t R_rows, void* h_out,
+                        txl_layer_saved* saved);
+int txl_layer_step_bwd_saved(void* stream, int dtype, const txl_layer_dims* dims,
+                             const void* h_in, const txl_ring* mem, const txl_layer_weights* w,
+                             const void* u_bias, const void* v_bias, const void* R,
+                             int64_t R_rows, const void* dh_out, const txl_layer_saved* saved,
+                             const txl_layer_grads* g, void* workspace, size_t ws_bytes);
+
+/*
  * Where txl_layer_step leaves its intermediates in the workspace (section 3.3's
  * q, k, v, the projected encodings r = R W_kR^T, and the attention output a),
  * for a call with mem->len == mem_len.  After such a call the workspace holds,

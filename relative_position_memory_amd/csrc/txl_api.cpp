@@ -817,10 +817,54 @@ size_t txl_layer_bwd_workspace_bytes(const txl_layer_dims* dims, int64_t mem_cap
   return bwd_ws_layout(*dims, mem_capacity, dtype).total;
 }
 
-int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
-                       const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
-                       const void* v_bias, const void* R, int64_t R_rows, const void* dh_out,
-                       const txl_layer_grads* g, void* workspace, size_t ws_bytes) {
+// Saved state of a training forward: the layer step's workspace, then the
+// attention's log-sum-exp [B][H][L].
+struct SavedLayout {
+  size_t fwd, lse, total;
+};
+static SavedLayout saved_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
+  SavedLayout sl{};
+  sl.fwd = 0;
+  sl.lse = (txl_layer_workspace_bytes(&dm, cap, dtype) + 255) & ~(size_t)255;
+  sl.total = sl.lse + (((size_t)(dm.B * dm.n_head * dm.L) * 4 + 255) & ~(size_t)255);
+  return sl;
+}
+
+size_t txl_layer_saved_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype) {
+  if (check_dims(dims) != TXL_OK || mem_capacity < 1) return 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
+  if (txl_layer_workspace_bytes(dims, mem_capacity, dtype) == 0) return 0;
+  return saved_layout(*dims, mem_capacity, dtype).total;
+}
+
+int txl_layer_step_save(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                        const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
+                        const void* v_bias, const void* R, int64_t R_rows, void* h_out,
+                        txl_layer_saved* saved) {
+  g_detail[0] = 0;
+  if (!saved || !saved->data || (uintptr_t)saved->data % 256)
+    return fail(TXL_EINVAL, "saved state is NULL or unaligned");
+  int rc = check_dims(dims);
+  if (rc != TXL_OK) return rc;
+  if (!mem || mem->capacity < 1) return fail(TXL_EINVAL, "ring state is invalid");
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  const SavedLayout sl = saved_layout(*dims, mem->capacity, dtype);
+  if (saved->bytes < sl.total)
+    return fail(TXL_EWORKSPACE, "saved state: need %zu bytes, got %zu", sl.total, saved->bytes);
+  char* base = (char*)saved->data;
+  bool has_lse = false, has_y = false;
+  rc = layer_step_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows, h_out,
+                      base + sl.fwd, sl.lse - sl.fwd, (float*)(base + sl.lse), &has_lse, &has_y);
+  saved->has_lse = has_lse ? 1 : 0;
+  saved->has_y = has_y ? 1 : 0;
+  return rc;
+}
+
+static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                         const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
+                         const void* v_bias, const void* R, int64_t R_rows, const void* dh_out,
+                         const txl_layer_saved* saved, const txl_layer_grads* g, void* workspace,
+                         size_t ws_bytes) {
   g_detail[0] = 0;
   if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
   int rc = check_dims(dims);
@@ -852,6 +896,18 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
                        {(uintptr_t)g->dgamma, (uintptr_t)(g->dgamma + D)},
                        {(uintptr_t)g->dbeta, (uintptr_t)(g->dbeta + D)},
                        {(uintptr_t)workspace, (uintptr_t)workspace + ws_bytes}};
+  SavedLayout sl{};
+  if (saved) {
+    sl = saved_layout(dm, mem->capacity, dtype);
+    if (!saved->data || (uintptr_t)saved->data % 256 || saved->bytes < sl.total)
+      return fail(TXL_EINVAL, "saved state is NULL, unaligned or short");
+    if (!w || !w->W_q || !w->W_kE || !w->W_v || !w->W_kR || !w->W_o || !w->ln_gamma ||
+        !w->ln_beta || !h_in || !u_bias || !v_bias || !R || !mem->data)
+      return fail(TXL_EINVAL, "NULL argument");
+    if (R_rows < mem->len + L) return fail(TXL_EINVAL, "R_rows < mem->len + L");
+  }
+  const Span ssaved = {(uintptr_t)(saved ? saved->data : nullptr),
+                       (uintptr_t)(saved ? (char*)saved->data + saved->bytes : nullptr)};
   const Span ins[] = {{(uintptr_t)h_in, (uintptr_t)h_in + (uintptr_t)(B * L * D * es)},
                       {(uintptr_t)dh_out, (uintptr_t)dh_out + (uintptr_t)(B * L * D * es)},
                       {(uintptr_t)mem->data,
@@ -862,17 +918,27 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
       if (overlap(outs[x], sp)) return fail(TXL_EINVAL, "a gradient or the workspace overlaps an input");
     for (int y = x + 1; y < n_out; ++y)
       if (overlap(outs[x], outs[y])) return fail(TXL_EINVAL, "gradients / workspace overlap");
+    if (saved && overlap(outs[x], ssaved))
+      return fail(TXL_EINVAL, "a gradient or the workspace overlaps the saved state");
   }
   char* base = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
-  // the forward again, for q, k, v, r and a (it also checks the remaining arguments)
+  // q, k, v, r and a: the saved forward's, or the forward again (which also
+  // checks the remaining arguments)
   bool have_lse = false, have_y = false;
-  rc = layer_step_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows,
-                      base + bw.hout, base + bw.fwd, bw.hout - bw.fwd, (float*)(base + bw.lse),
-                      &have_lse, &have_y);
-  if (rc != TXL_OK) return rc;
-  const WsLayout fl = ws_layout(dm, T, es);
   char* fb = base + bw.fwd;
+  float* lse = (float*)(base + bw.lse);
+  if (saved) {
+    fb = (char*)saved->data + sl.fwd;
+    lse = (float*)((char*)saved->data + sl.lse);
+    have_lse = saved->has_lse != 0;
+    have_y = saved->has_y != 0;
+  } else {
+    rc = layer_step_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows,
+                        base + bw.hout, fb, bw.hout - bw.fwd, lse, &have_lse, &have_y);
+    if (rc != TXL_OK) return rc;
+  }
+  const WsLayout fl = ws_layout(dm, T, es);
   const void* q = fb + fl.q;
   const void* k = fb + fl.k;
   const void* v = fb + fl.v;
@@ -913,7 +979,7 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
   ab.dout = da; ab.do_sb = L * HD; ab.do_st = HD; ab.do_sh = d; ab.dout_f32 = 1;
   ab.dq = dq; ab.dk = dk; ab.dv = dv; ab.dr = dr; ab.du = g->du; ab.dvb = g->dv_bias;
   if (have_lse) {  // the forward's softmax statistics and output
-    ab.lse = (const float*)(base + bw.lse);
+    ab.lse = lse;
     ab.o = a; ab.o_sb = L * HD; ab.o_st = HD; ab.o_sh = d;
   }
   txl::attn_bwd_bind(ab, base + bw.attn);
@@ -934,6 +1000,24 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, cons
                 T * HD, 0, L * D), "dh v");
 #undef TXL_TRY
   return TXL_OK;
+}
+
+int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
+                       const txl_ring* mem, const txl_layer_weights* w, const void* u_bias,
+                       const void* v_bias, const void* R, int64_t R_rows, const void* dh_out,
+                       const txl_layer_grads* g, void* workspace, size_t ws_bytes) {
+  return layer_bwd_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows, dh_out,
+                       nullptr, g, workspace, ws_bytes);
+}
+
+int txl_layer_step_bwd_saved(void* stream, int dtype, const txl_layer_dims* dims,
+                             const void* h_in, const txl_ring* mem, const txl_layer_weights* w,
+                             const void* u_bias, const void* v_bias, const void* R,
+                             int64_t R_rows, const void* dh_out, const txl_layer_saved* saved,
+                             const txl_layer_grads* g, void* workspace, size_t ws_bytes) {
+  if (!saved) return fail(TXL_EINVAL, "saved state is NULL");
+  return layer_bwd_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows, dh_out,
+                       saved, g, workspace, ws_bytes);
 }
 
 }  // extern "C"

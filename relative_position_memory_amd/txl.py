@@ -244,15 +244,53 @@ _lib.txl_layer_step_bwd.argtypes = [_p, ctypes.c_int, ctypes.POINTER(LayerDims),
 _lib.txl_layer_step_bwd.restype = ctypes.c_int
 
 
+class LayerSaved(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("bytes", _sz), ("has_lse", ctypes.c_int),
+                ("has_y", ctypes.c_int)]
+
+
+_lib.txl_layer_saved_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int]
+_lib.txl_layer_saved_bytes.restype = _sz
+_lib.txl_layer_step_save.argtypes = [_p, ctypes.c_int, ctypes.POINTER(LayerDims), _p,
+                                     ctypes.POINTER(Ring), ctypes.POINTER(LayerWeights), _p, _p,
+                                     _p, _i64, _p, ctypes.POINTER(LayerSaved)]
+_lib.txl_layer_step_save.restype = ctypes.c_int
+_lib.txl_layer_step_bwd_saved.argtypes = [_p, ctypes.c_int, ctypes.POINTER(LayerDims), _p,
+                                          ctypes.POINTER(Ring), ctypes.POINTER(LayerWeights), _p,
+                                          _p, _p, _i64, _p, ctypes.POINTER(LayerSaved),
+                                          ctypes.POINTER(LayerGrads), _p, _sz]
+_lib.txl_layer_step_bwd_saved.restype = ctypes.c_int
+
+
+def layer_saved_bytes(dims: LayerDims, mem_capacity: int, dtype: torch.dtype) -> int:
+    """txl_layer_saved_bytes."""
+    return int(_lib.txl_layer_saved_bytes(ctypes.byref(dims), int(mem_capacity),
+                                          dtype_code(dtype)))
+
+
+def layer_step_save(dims, h_in, ring, W, u, vb, R, h_out, saved_buf, stream=None):
+    """txl_layer_step_save into the device buffer saved_buf (uint8, 256-byte
+    aligned); returns the LayerSaved to hand to layer_step_bwd(saved=...)."""
+    lw = W if isinstance(W, LayerWeights) else layer_weights(W)
+    sv = LayerSaved(_ptr(saved_buf), saved_buf.numel() * saved_buf.element_size(), 0, 0)
+    rc = _lib.txl_layer_step_save(_stream(stream), dtype_code(h_in.dtype), ctypes.byref(dims),
+                                  _ptr(h_in), ctypes.byref(ring), ctypes.byref(lw), _ptr(u),
+                                  _ptr(vb), _ptr(R), R.shape[0], _ptr(h_out), ctypes.byref(sv))
+    _check(rc, "txl_layer_step_save")
+    return sv
+
+
 def layer_bwd_workspace_bytes(dims: LayerDims, mem_capacity: int, dtype: torch.dtype) -> int:
     """txl_layer_bwd_workspace_bytes."""
     return int(_lib.txl_layer_bwd_workspace_bytes(ctypes.byref(dims), int(mem_capacity),
                                                   dtype_code(dtype)))
 
 
-def layer_step_bwd(dims, h, ring, W, u, vb, R, dh_out, workspace, grads=None, stream=None):
-    """txl_layer_step_bwd.  grads: None (fp32 tensors allocated here) or a dict
-    with the keys of LayerGrads.  Returns the dict of gradient tensors."""
+def layer_step_bwd(dims, h, ring, W, u, vb, R, dh_out, workspace, grads=None, stream=None,
+                   saved=None):
+    """txl_layer_step_bwd, or txl_layer_step_bwd_saved when saved (a LayerSaved from
+    layer_step_save) is given.  grads: None (fp32 tensors allocated here) or a
+    dict with the keys of LayerGrads.  Returns the dict of gradient tensors."""
     dev = h.device
     D, H, d = dims.d_model, dims.n_head, dims.d_head
     f32 = torch.float32
@@ -269,11 +307,20 @@ def layer_step_bwd(dims, h, ring, W, u, vb, R, dh_out, workspace, grads=None, st
                  "dbeta": torch.empty((D,), dtype=f32, device=dev)}
     gs = LayerGrads(**{n: _ptr(t) for n, t in grads.items()})
     lw = W if isinstance(W, LayerWeights) else layer_weights(W)
-    rc = _lib.txl_layer_step_bwd(_stream(stream), dtype_code(h.dtype), ctypes.byref(dims),
-                                 _ptr(h), ctypes.byref(ring), ctypes.byref(lw), _ptr(u), _ptr(vb),
-                                 _ptr(R), R.shape[0], _ptr(dh_out), ctypes.byref(gs),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size())
-    _check(rc, "txl_layer_step_bwd")
+    nbytes = workspace.numel() * workspace.element_size()
+    if saved is None:
+        rc = _lib.txl_layer_step_bwd(_stream(stream), dtype_code(h.dtype), ctypes.byref(dims),
+                                     _ptr(h), ctypes.byref(ring), ctypes.byref(lw), _ptr(u),
+                                     _ptr(vb), _ptr(R), R.shape[0], _ptr(dh_out),
+                                     ctypes.byref(gs), _ptr(workspace), nbytes)
+        _check(rc, "txl_layer_step_bwd")
+    else:
+        rc = _lib.txl_layer_step_bwd_saved(_stream(stream), dtype_code(h.dtype),
+                                           ctypes.byref(dims), _ptr(h), ctypes.byref(ring),
+                                           ctypes.byref(lw), _ptr(u), _ptr(vb), _ptr(R),
+                                           R.shape[0], _ptr(dh_out), ctypes.byref(saved),
+                                           ctypes.byref(gs), _ptr(workspace), nbytes)
+        _check(rc, "txl_layer_step_bwd_saved")
     return grads
 
 

@@ -159,3 +159,49 @@ def test_layer_step_bwd_matches_oracle(dtype, name, over, mem_len, start):
         scale = max(1.0, float(np.max(np.abs(r))))
         err = float(np.max(np.abs(g - r)))
         assert err <= LAYER_TOL[dtype] * scale, f"{gn}: max err {err:.3e} (scale {scale:.3e})"
+
+
+@pytest.mark.parametrize("dtype,name,over,mem_len,start", [
+    ("fp32", "tiny", {"B": 2, "L": 37, "M": 50, "d": 12, "H": 3, "D": 40}, 45, 31),
+    ("bf16", "charlm", {"B": 2, "L": 96, "M": 160, "D": 192, "H": 3, "d": 64}, 160, 37),
+    ("bf16", "charlm", {"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
+])
+def test_layer_step_bwd_saved_matches_recompute(dtype, name, over, mem_len, start):
+    """txl_layer_step_save + txl_layer_step_bwd_saved: the forward output equals
+    txl_layer_step's and the gradients equal txl_layer_step_bwd's (same kernels on
+    the same values; only the order of atomic sums may differ) and the oracle's."""
+    from tests.test_gpu_parity import _layer_setup
+    w = I.workload(name, **over)
+    _say(f"layer bwd saved {dtype} {w} mem_len={mem_len} start={start}")
+    txl, x, W, data, ring, h, logical = _layer_setup(w, mem_len=mem_len, start=start)
+    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
+    ws = torch.empty(txl.layer_bwd_workspace_bytes(dims, w.M, h.dtype), dtype=torch.uint8,
+                     device="cuda")
+    fws = torch.empty(txl.workspace_bytes(dims, w.M, h.dtype), dtype=torch.uint8, device="cuda")
+    nsv = txl.layer_saved_bytes(dims, w.M, h.dtype)
+    assert nsv > 0
+    sbuf = torch.empty(nsv, dtype=torch.uint8, device="cuda")
+    u, vb, R = dev(x["u"], dtype), dev(x["v"], dtype), dev(x["R"], dtype)
+    g_out = np.random.default_rng(w.L + w.D).standard_normal((w.B, w.L, w.D)).astype(np.float32)
+    if dtype == "bf16":
+        g_out = torch.from_numpy(g_out).bfloat16().float().numpy()
+    g_dev = dev(g_out, dtype)
+    out_ref = torch.empty_like(h)
+    txl.layer_step(dims, h, ring, W, u, vb, R, out_ref, fws)
+    out_sv = torch.empty_like(h)
+    sv = txl.layer_step_save(dims, h, ring, W, u, vb, R, out_sv, sbuf)
+    torch.cuda.synchronize()
+    assert torch.equal(out_sv, out_ref)
+    got = txl.layer_step_bwd(dims, h, ring, W, u, vb, R, g_dev, ws, saved=sv)
+    got = {n: t.clone() for n, t in got.items()}
+    rec = txl.layer_step_bwd(dims, h, ring, W, u, vb, R, g_dev, ws)
+    torch.cuda.synchronize()
+    ref = OB.layer_step_bwd(x["h0"][0], logical, x["weights"][0], x["u"], x["v"], x["R"], g_out)
+    for gn, rn in GRAD_NAMES:
+        a, b = got[gn].cpu().double(), rec[gn].cpu().double()
+        scale = max(1.0, float(b.abs().max()))
+        assert float((a - b).abs().max()) <= 1e-5 * scale, gn
+        r = ref[rn]
+        scale = max(1.0, float(np.max(np.abs(r))))
+        err = float(np.max(np.abs(a.numpy() - r)))
+        assert err <= LAYER_TOL[dtype] * scale, f"{gn}: max err {err:.3e} (scale {scale:.3e})"
