@@ -851,6 +851,18 @@ int txl_layer_step_save(void* stream, int dtype, const txl_layer_dims* dims, con
   const SavedLayout sl = saved_layout(*dims, mem->capacity, dtype);
   if (saved->bytes < sl.total)
     return fail(TXL_EWORKSPACE, "saved state: need %zu bytes, got %zu", sl.total, saved->bytes);
+  // the saved state must not overlap the layer's input, output or memory
+  // (the workspace part of it is checked again by the step itself)
+  {
+    const int64_t es = elt_size(dtype), B = dims->B, L = dims->L, D = dims->d_model;
+    const Span ssv = {(uintptr_t)saved->data, (uintptr_t)saved->data + saved->bytes};
+    const Span others[] = {{(uintptr_t)h_in, (uintptr_t)h_in + (uintptr_t)(B * L * D * es)},
+                           {(uintptr_t)h_out, (uintptr_t)h_out + (uintptr_t)(B * L * D * es)},
+                           {(uintptr_t)mem->data,
+                            (uintptr_t)mem->data + (uintptr_t)(B * mem->capacity * D * es)}};
+    for (const Span& o : others)
+      if (o.lo && overlap(ssv, o)) return fail(TXL_EINVAL, "the saved state overlaps an argument");
+  }
   char* base = (char*)saved->data;
   bool has_lse = false, has_y = false;
   rc = layer_step_run(stream, dtype, dims, h_in, mem, w, u_bias, v_bias, R, R_rows, h_out,

@@ -131,3 +131,34 @@ def test_pos_ff_argument_errors_need_no_gpu():
     bad = list(args)
     bad[-1] = 16                       # workspace too small
     assert lib.txl_pos_ff(*bad) == txl.EWORKSPACE
+
+
+def test_saved_state_argument_errors_need_no_gpu():
+    """txl_layer_step_save / txl_layer_step_bwd_saved reject a missing, unaligned,
+    short or overlapping saved state before any HIP call."""
+    from relative_position_memory_amd import txl
+    lib = txl._lib
+    dims = txl.layer_dims(2, 16, 64, 2, 32)
+    nsv = lib.txl_layer_saved_bytes(ctypes.byref(dims), 16, txl.BF16)
+    assert nsv >= lib.txl_layer_workspace_bytes(ctypes.byref(dims), 16, txl.BF16) + 2 * 2 * 16 * 4
+    assert lib.txl_layer_saved_bytes(ctypes.byref(txl.layer_dims(0, 16, 64, 2, 32)), 16,
+                                     txl.BF16) == 0
+    fake = ctypes.c_void_p(0x100000)
+    W = txl.LayerWeights(*([fake] * 7))
+    ring = txl.Ring(0x200000, 16, 0, 16)
+    h_in, h_out = ctypes.c_void_p(0x300000), ctypes.c_void_p(0x400000)
+
+    def save(sv):
+        return lib.txl_layer_step_save(None, txl.BF16, ctypes.byref(dims), h_in,
+                                       ctypes.byref(ring), ctypes.byref(W), fake, fake, fake, 64,
+                                       h_out, ctypes.byref(sv) if sv is not None else None)
+
+    assert save(None) == txl.EINVAL
+    assert save(txl.LayerSaved(0x10000010, nsv, 0, 0)) == txl.EINVAL          # unaligned
+    assert save(txl.LayerSaved(0x10000000, nsv - 256, 0, 0)) == txl.EWORKSPACE  # short
+    assert save(txl.LayerSaved(0x300000 - 256, nsv, 0, 0)) == txl.EINVAL        # over h_in
+    grads = txl.LayerGrads(*([ctypes.c_void_p(0x500000 + 0x10000 * i) for i in range(10)]))
+    assert lib.txl_layer_step_bwd_saved(None, txl.BF16, ctypes.byref(dims), h_in,
+                                        ctypes.byref(ring), ctypes.byref(W), fake, fake, fake,
+                                        64, fake, None, ctypes.byref(grads),
+                                        ctypes.c_void_p(0x20000000), 1 << 30) == txl.EINVAL
