@@ -356,8 +356,10 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const int64_t T = a.mem_len + a.L, H = a.H, d = a.d;
   if (a.B * a.H > 65535 || (a.L + BQ - 1) / BQ > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(1), dim3(256), 0, s, a.du, H * d);
-  hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(1), dim3(256), 0, s, a.dvb, H * d);
+  if (!a.zeroed) {
+    hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(1), dim3(256), 0, s, a.du, H * d);
+    hipLaunchKernelGGL(attn_bwd_zero_kernel, dim3(1), dim3(256), 0, s, a.dvb, H * d);
+  }
   hipError_t e;
   if (dtype == 1) {
     if ((e = launch_attn_bwd_rows_mfma(a, s)) != hipSuccess) return e;

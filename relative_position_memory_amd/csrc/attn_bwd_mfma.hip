@@ -494,7 +494,7 @@ hipError_t launch_attn_bwd_dr_mfma(const AttnBwdArgs& a, hipStream_t s) {
   int64_t nsplit = (1024 + blocks - 1) / blocks;
   nsplit = nsplit < items ? nsplit : items;
   nsplit = nsplit < 1 ? 1 : (nsplit > 65535 ? 65535 : nsplit);
-  if (nsplit > 1) {
+  if (nsplit > 1 && !a.zeroed) {
     const int64_t n = T * a.H * a.d;
     const int64_t zb = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, s, a.dr, n);

@@ -113,12 +113,45 @@ __global__ void gather_ctx_kernel(const void* ring, int64_t cap, int64_t start, 
   }
 }
 
+struct ZeroList {
+  float* p[16];
+  int64_t end[16];  // running element counts
+  int n;
+};
+
+// Grid-stride over the concatenation of the buffers.
+__global__ void zero_many_kernel(ZeroList z) {
+  const int64_t total = z.end[z.n - 1];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int b = 0;
+    while (i >= z.end[b]) ++b;
+    z.p[b][i - (b ? z.end[b - 1] : 0)] = 0.f;
+  }
+}
+
 unsigned grid_for(int64_t n) {
   const int64_t g = (n + 255) / 256;
   return (unsigned)(g < 4096 ? (g > 0 ? g : 1) : 4096);
 }
 
 }  // namespace
+
+hipError_t launch_zero_many(float* const* p, const int64_t* count, int n, hipStream_t s) {
+  if (n < 1 || n > 16) return hipErrorInvalidValue;
+  ZeroList z{};
+  int64_t acc = 0;
+  for (int b = 0; b < n; ++b) {
+    if (count[b] < 0) return hipErrorInvalidValue;
+    z.p[b] = p[b];
+    acc += count[b];
+    z.end[b] = acc;
+  }
+  z.n = n;
+  if (acc == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_many_kernel, dim3(grid_for(acc)), dim3(256), 0, s, z);
+  return hipGetLastError();
+}
 
 hipError_t launch_to_f32(int dtype, const void* src, float* dst, int64_t n, hipStream_t s) {
   if (dtype == 1)
@@ -130,9 +163,11 @@ hipError_t launch_to_f32(int dtype, const void* src, float* dst, int64_t n, hipS
 
 hipError_t launch_ln_bwd(int dtype, const float* y, const void* gamma, const void* dh_out,
                          int64_t M, int64_t D, float eps, float* dy, float* mean, float* rstd,
-                         float* dgamma, float* dbeta, hipStream_t s) {
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(D)), dim3(256), 0, s, dgamma, D);
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(D)), dim3(256), 0, s, dbeta, D);
+                         float* dgamma, float* dbeta, hipStream_t s, bool zeroed) {
+  if (!zeroed) {
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(D)), dim3(256), 0, s, dgamma, D);
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(D)), dim3(256), 0, s, dbeta, D);
+  }
   if (M > 0x7fffffffLL) return hipErrorInvalidValue;
   const int64_t rows = 16;  // enough row chunks to fill the GPU
   const dim3 gc((unsigned)((D + 255) / 256), (unsigned)((M + rows - 1) / rows));

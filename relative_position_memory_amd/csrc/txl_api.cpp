@@ -970,6 +970,14 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
   const int64_t BL = B * L;
   hipError_t e;
 #define TXL_TRY(x, what) do { if ((e = (x)) != hipSuccess) return hip_fail(e, what); } while (0)
+  // every output that is summed into (atomically or by accumulating products),
+  // cleared in one launch
+  {
+    float* zp[] = {g->dgamma, g->dbeta, g->du, g->dv_bias, dr, g->dW_o, g->dW_q, g->dW_kE,
+                   g->dW_v, g->dW_kR, da};
+    const int64_t zn[] = {D, D, HD, HD, T * HD, D * HD, HD * D, HD * D, HD * D, HD * D, BL * HD};
+    TXL_TRY(txl::launch_zero_many(zp, zn, 11, st), "clear");
+  }
   // y = a W_o^T + h_in (the LayerNorm input), then the LayerNorm backward
   if (!have_y) {
     TXL_TRY(txl::launch_to_f32(dt, h_in, y, BL * D, st), "copy");
@@ -977,10 +985,10 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
   }
   TXL_TRY(txl::launch_ln_bwd(dt, y, w->ln_gamma, dh_out, BL, D, dm.ln_eps, dy,
                              (float*)(base + bw.mean), (float*)(base + bw.rstd), g->dgamma,
-                             g->dbeta, st), "layernorm backward");
+                             g->dbeta, st, true), "layernorm backward");
   // dW_o = dy^T a, da = dy W_o
-  TXL_TRY(sgemm(st, D, HD, BL, dy, 0, 1, D, a, dt, HD, 1, g->dW_o, HD, false), "dW_o");
-  TXL_TRY(sgemm(st, BL, HD, D, dy, 0, D, 1, w->W_o, dt, HD, 1, da, HD, false), "da");
+  TXL_TRY(sgemm(st, D, HD, BL, dy, 0, 1, D, a, dt, HD, 1, g->dW_o, HD, true), "dW_o");
+  TXL_TRY(sgemm(st, BL, HD, D, dy, 0, D, 1, w->W_o, dt, HD, 1, da, HD, true), "da");
   // attention backward on the forward's head-major q, k, v, r
   txl::AttnBwdArgs ab{};
   ab.B = B; ab.H = H; ab.L = L; ab.mem_len = len; ab.d = d;
@@ -990,6 +998,7 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
   ab.u = u_bias; ab.vb = v_bias; ab.scale = 1.0f / sqrtf((float)d);
   ab.dout = da; ab.do_sb = L * HD; ab.do_st = HD; ab.do_sh = d; ab.dout_f32 = 1;
   ab.dq = dq; ab.dk = dk; ab.dv = dv; ab.dr = dr; ab.du = g->du; ab.dvb = g->dv_bias;
+  ab.zeroed = 1;  // du, dv_bias and dr were cleared above
   if (have_lse) {  // the forward's softmax statistics and output
     ab.lse = lse;
     ab.o = a; ab.o_sb = L * HD; ab.o_st = HD; ab.o_sh = d;
@@ -999,10 +1008,10 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
   // projection weights: dW_q = dq^T h_in, dW_kE = dk^T ctx, dW_v = dv^T ctx, dW_kR = dr^T R
   TXL_TRY(txl::launch_gather_ctx(dt, mem->data, mem->capacity, mem->start, len, h_in, B, L, D, ctx,
                                  st), "context gather");
-  TXL_TRY(sgemm(st, HD, D, BL, dq, 0, 1, HD, h_in, dt, D, 1, g->dW_q, D, false), "dW_q");
-  TXL_TRY(sgemm(st, HD, D, B * T, dk, 0, 1, HD, ctx, dt, D, 1, g->dW_kE, D, false), "dW_kE");
-  TXL_TRY(sgemm(st, HD, D, B * T, dv, 0, 1, HD, ctx, dt, D, 1, g->dW_v, D, false), "dW_v");
-  TXL_TRY(sgemm(st, HD, D, T, dr, 0, 1, HD, R, dt, D, 1, g->dW_kR, D, false), "dW_kR");
+  TXL_TRY(sgemm(st, HD, D, BL, dq, 0, 1, HD, h_in, dt, D, 1, g->dW_q, D, true), "dW_q");
+  TXL_TRY(sgemm(st, HD, D, B * T, dk, 0, 1, HD, ctx, dt, D, 1, g->dW_kE, D, true), "dW_kE");
+  TXL_TRY(sgemm(st, HD, D, B * T, dv, 0, 1, HD, ctx, dt, D, 1, g->dW_v, D, true), "dW_v");
+  TXL_TRY(sgemm(st, HD, D, T, dr, 0, 1, HD, R, dt, D, 1, g->dW_kR, D, true), "dW_kR");
   // dh = dy + dq W_q + (dk W_kE + dv W_v) on the current rows (the memory's gradient is stopped)
   TXL_TRY(txl::launch_to_f32(0, dy, g->dh, BL * D, st), "copy");
   TXL_TRY(sgemm(st, BL, D, HD, dq, 0, HD, 1, w->W_q, dt, D, 1, g->dh, D, true), "dh q");

@@ -109,6 +109,7 @@ struct AttnBwdArgs {
   float scale;
   const void* dout; int64_t do_sb, do_st, do_sh;
   int dout_f32;   // dout is fp32 whatever the inputs' dtype
+  int zeroed;     // du, dvb and dr are already zero (the caller cleared them)
   float* dq; float* dk; float* dv; float* dr; float* du; float* dvb;
   float* P; float* dS; float* qc; float* qp;
   // Optional (matrix-core path): the forward's exp2-domain log-sum-exp per query
@@ -151,9 +152,12 @@ hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s);
 hipError_t launch_to_f32(int dtype, const void* src, float* dst, int64_t n, hipStream_t s);
 // dy of h_out = LayerNorm(y) gamma + beta for dh_out (rows of D), the rows' mean
 // and 1/sigma, and dgamma, dbeta (overwritten).
+// Sets n fp32 buffers (at most 16) to zero in one launch.
+hipError_t launch_zero_many(float* const* p, const int64_t* count, int n, hipStream_t s);
+// (dgamma and dbeta are cleared first unless zeroed)
 hipError_t launch_ln_bwd(int dtype, const float* y, const void* gamma, const void* dh_out,
                          int64_t M, int64_t D, float eps, float* dy, float* mean, float* rstd,
-                         float* dgamma, float* dbeta, hipStream_t s);
+                         float* dgamma, float* dbeta, hipStream_t s, bool zeroed = false);
 // ctx [B][len + L][D] = [ring rows (oldest first) ; h]
 hipError_t launch_gather_ctx(int dtype, const void* ring, int64_t cap, int64_t start, int64_t len,
                              const void* h, int64_t B, int64_t L, int64_t D, void* ctx,
