@@ -115,8 +115,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
   const int g4 = lane >> 4, n16 = lane & 15;
   const int H = (int)a.H, L = (int)a.L, len = (int)a.mem_len, d = (int)a.d;
   const int T = len + L;
-  const int z = blockIdx.y, b = z / H, h = z % H;
-  const int i0 = blockIdx.x * BQ;
+  // one-dimensional grid, the last query blocks (the most key tiles) first
+  const int nz = (int)(a.B * a.H), nqb = (L + BQ - 1) / BQ;
+  const int z = (int)(blockIdx.x % nz), b = z / H, h = z % H;
+  const int i0 = (nqb - 1 - (int)(blockIdx.x / nz)) * BQ;
   const int i = i0 + 16 * wave + n16;  // this lane's query
   const bool qok = i < L;
   const int imax = i0 + BQ - 1 < L - 1 ? i0 + BQ - 1 : L - 1;
@@ -518,7 +520,9 @@ hipError_t launch_attn_bwd_rows_mfma(const AttnBwdArgs& a, hipStream_t s) {
   const uintptr_t kv = (uintptr_t)a.k | (uintptr_t)a.v;
   const bool kv_vec = kv % 16 == 0 && a.kv_sb % 8 == 0 && a.kv_st % 8 == 0 && a.kv_sh % 8 == 0;
   const bool r_vec = (uintptr_t)a.r % 16 == 0 && a.r_sp % 8 == 0 && a.r_sh % 8 == 0;
-  const dim3 grid((unsigned)((a.L + BQ - 1) / BQ), (unsigned)(a.B * a.H));
+  const int64_t nblk = ((a.L + BQ - 1) / BQ) * a.B * a.H;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nblk);
   hipLaunchKernelGGL(attn_bwd_mfma_kernel, grid, dim3(256), smem, s, a,
                      (kv_vec ? 1 : 0) | (r_vec ? 2 : 0));
   return hipGetLastError();
