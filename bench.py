@@ -519,7 +519,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}, "
+        print(f"bench.py: this benchmark runs on exactly one GPU (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); no multi-GPU path is built", file=sys.stderr, flush=True)
         sys.exit(2)
 
