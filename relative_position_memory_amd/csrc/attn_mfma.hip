@@ -94,26 +94,6 @@ __device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vm
 // LDS-direct loads each wave has already waited for.
 __device__ inline void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory"); }
 
-// Device-scope (agent) relaxed atomic accesses for the in-kernel merge: coherent
-// across the XCDs' L2s without cache-wide write-back or invalidation.  Pairs of
-// floats go as one 8-byte access, so a wave's 64 lanes cover 512 contiguous
-// bytes (whole lines).
-__device__ inline void st2_coherent(float* p, float x, float y) {
-  const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, x) |
-                     ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32);
-  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float2 ld2_coherent(const float* p) {
-  const uint64_t v = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__builtin_bit_cast(float, (uint32_t)v), __builtin_bit_cast(float, (uint32_t)(v >> 32)));
-}
-__device__ inline void st_coherent_i(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline int atomic_add_coherent(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ inline bf16x8 lds_b128(const uint16_t* p) { return *(const bf16x8*)p; }
 __device__ inline bf16x8 lds_tr2(const uint16_t* p0, const uint16_t* p1) {
   const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
@@ -554,90 +534,29 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   //      so that each access covers whole lines:
   //        acc  [wave][gm][db][pair][lane] x 2 floats (pair 0: elements 0, 1)
   //        m, l [wave][gm][n16] x 2 floats
-  //      With plan.ext_merge, attn_part_merge_kernel merges the parts.  Otherwise
-  //      the stores are device-coherent (they bypass the XCDs' separate L2s);
-  //      once they have completed (vmcnt 0) the workgroup counts itself in, and
-  //      the part that arrives last reads the others back with device-coherent
-  //      loads and merges them into its own state before the normal epilogue:
-  //        acc = sum_p 2^(m_p - M) acc_p,  l = sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-  //      The part that holds key 0 has a finite reference for every query. ---------
+  //      and attn_part_merge_kernel, launched after this kernel on the same
+  //      stream, merges the parts (the kernel boundary orders the partials'
+  //      stores before its loads).  The part that holds key 0 has a finite
+  //      reference for every query. ---------------------------------------------------
   float l_tot[2] = {acc_l[0][0], acc_l[1][0]};
   if (nparts > 1) {
     const int64_t slot0 = a.plan.slot0[qt];
-    auto pacc = [&](int p) { return a.part_acc + ((slot0 + p) * groups + g) * (BQ * DP); };
-    auto pml = [&](int p) { return a.part_ml + ((slot0 + p) * groups + g) * (BQ * 2); };
-    auto aidx = [&](int gm, int db, int pr) {
-      return ((((wave * 2 + gm) * 4 + db) * 2 + pr) * 64 + lane) * 2;
-    };
-    auto midx = [&](int gm) { return ((wave * 2 + gm) * 16 + n16) * 2; };
-    const bool ext = a.plan.ext_merge != 0;
+    float* pa = a.part_acc + ((slot0 + part) * groups + g) * (BQ * DP);
+    float* pm = a.part_ml + ((slot0 + part) * groups + g) * (BQ * 2);
 #pragma unroll
     for (int gm = 0; gm < 2; ++gm) {
-      s_off[gm] = lim[gm] == -INFINITY ? -INFINITY : s_off[gm];
       if (!wave_has_rows || i0w + 16 * gm + n16 >= L) continue;
-      float* pa = pacc(part);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          if (ext)
-            *(float2*)(pa + aidx(gm, db, pr)) = make_float2(acc[gm][db][2 * pr], acc[gm][db][2 * pr + 1]);
-          else
-            st2_coherent(pa + aidx(gm, db, pr), acc[gm][db][2 * pr], acc[gm][db][2 * pr + 1]);
-        }
-      if (g4 == 0) {
-        if (ext)
-          *(float2*)(pml(part) + midx(gm)) = make_float2(s_off[gm], l_tot[gm]);
-        else
-          st2_coherent(pml(part) + midx(gm), s_off[gm], l_tot[gm]);
-      }
+        for (int pr = 0; pr < 2; ++pr)
+          *(float2*)(pa + ((((wave * 2 + gm) * 4 + db) * 2 + pr) * 64 + lane) * 2) =
+              make_float2(acc[gm][db][2 * pr], acc[gm][db][2 * pr + 1]);
+      if (g4 == 0)
+        *(float2*)(pm + ((wave * 2 + gm) * 16 + n16) * 2) =
+            make_float2(lim[gm] == -INFINITY ? -INFINITY : s_off[gm], l_tot[gm]);
     }
-    if (ext) return;
-    wait_dma();
-    barrier();  // (every wave is past its last tile: the S_p buffers are free)
-    volatile int* flag = (volatile int*)&sm.W[0][0];
-    if (tid == 0) *flag = atomic_add_coherent(a.part_cnt + (int64_t)g * nqt + qt, 1);
-    barrier();
-    if (*flag != nparts - 1) return;
-    if (tid == 0) st_coherent_i(a.part_cnt + (int64_t)g * nqt + qt, 0);
-#pragma unroll
-    for (int gm = 0; gm < 2; ++gm) {
-      if (!wave_has_rows || i0w + 16 * gm + n16 >= L) continue;
-      // four parts per batch: all their loads are in flight before the first use
-      for (int p0 = 0; p0 < nparts; p0 += 4) {
-        float2 ml[4], av[4][4][2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int p = p0 + j;
-          if (p >= nparts || p == part) continue;
-          const float* pa = pacc(p);
-          // (m, l) sit in the lanes with g4 == 0; every lane of a query reads them
-          ml[j] = ld2_coherent(pml(p) + midx(gm));
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) av[j][db][pr] = ld2_coherent(pa + aidx(gm, db, pr));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int p = p0 + j;
-          if (p >= nparts || p == part) continue;
-          const float M = fmaxf(s_off[gm], ml[j].x);
-          const float Mu = M == -INFINITY ? 0.f : M;
-          const float a_own = __builtin_amdgcn_exp2f(s_off[gm] - Mu);
-          const float a_p = __builtin_amdgcn_exp2f(ml[j].x - Mu);
-          l_tot[gm] = l_tot[gm] * a_own + ml[j].y * a_p;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-              acc[gm][db][2 * pr] = acc[gm][db][2 * pr] * a_own + av[j][db][pr].x * a_p;
-              acc[gm][db][2 * pr + 1] = acc[gm][db][2 * pr + 1] * a_own + av[j][db][pr].y * a_p;
-            }
-          s_off[gm] = M;
-        }
-      }
-    }
+    return;
   }
 
   // ---- epilogue: out[i][c] = acc / l, lane (g4, n16) of block db holds query
@@ -753,12 +672,6 @@ __global__ __launch_bounds__(256) void attn_part_merge_kernel(AttnArgs a) {
   }
 }
 
-// Clears the in-kernel merge's counters before a launch (a kernel, not a memset,
-// so the launch sequence may be captured in a graph).
-__global__ __launch_bounds__(256) void attn_cnt_clear_kernel(int* cnt, int n) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) cnt[i] = 0;
-}
-
 }  // namespace
 
 // ---- work plan ---------------------------------------------------------------------------
@@ -851,8 +764,7 @@ AttnPlan plan_uncached(const AttnArgs& a, int num_cus, size_t budget) {
     }
     if (ncls > ATTN_MAXCLS || slots > 255) return (size_t)-1;
     const size_t rows = (size_t)slots * (size_t)groups * BQ;
-    return slots ? rows * (DP + 2) * sizeof(float) + (size_t)groups * nqt * sizeof(int) + 768
-                 : (size_t)0;
+    return slots ? rows * (DP + 2) * sizeof(float) + 512 : (size_t)0;
   };
   // Descent: each step takes the change (one more part for one query tile) that
   // shortens the simulated schedule most, or, when none does, splits the tile
@@ -924,11 +836,6 @@ AttnPlan plan_uncached(const AttnArgs& a, int num_cus, size_t budget) {
   });
   p.ncls = slot > 0 ? (int)cl.size() : 0;  // no split: the kernel's own order, same list
   p.slots = slot;
-  // Many parts per tile: the last part would merge them one batch after another
-  // at the end of its own work; a second kernel reads them all at once.
-  int kmax = 1;
-  for (int t = 0; t < sh.nqt; ++t) kmax = k[t] > kmax ? k[t] : kmax;
-  p.ext_merge = kmax > 4 ? 1 : 0;
   for (int c = 0; c < p.ncls; ++c) {
     p.cls_qt[c] = (uint8_t)cl[c].qt;
     p.cls_part[c] = (uint8_t)cl[c].part;
@@ -940,14 +847,13 @@ size_t attn_plan_bytes(const AttnArgs& a, const AttnPlan& p) {
   if (p.slots <= 0) return 0;
   const size_t groups = (size_t)(a.B * a.H), nqt = (size_t)((a.L + BQ - 1) / BQ);
   const size_t rows = (size_t)p.slots * groups * BQ;
-  return rows * (DP + 2) * sizeof(float) + groups * nqt * sizeof(int) + 768;
+  return rows * (DP + 2) * sizeof(float) + 512;
 }
 
 void attn_plan_bind(AttnArgs& a, const AttnPlan& p, void* scratch) {
   a.plan = p;
   a.part_acc = nullptr;
   a.part_ml = nullptr;
-  a.part_cnt = nullptr;
   if (p.slots <= 0) return;
   const size_t groups = (size_t)(a.B * a.H);
   const size_t rows = (size_t)p.slots * groups * BQ;
@@ -955,8 +861,6 @@ void attn_plan_bind(AttnArgs& a, const AttnPlan& p, void* scratch) {
   a.part_acc = (float*)base;
   base += (rows * DP * sizeof(float) + 255) & ~(size_t)255;
   a.part_ml = (float*)base;
-  base += (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
-  a.part_cnt = (int*)base;
 }
 
 bool attn_mfma_supported(const AttnArgs& a) {
@@ -991,16 +895,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  if (a.plan.slots > 0) {
-    if (!a.part_acc || !a.part_ml || !a.part_cnt) return hipErrorInvalidValue;
-    if (!a.plan.ext_merge) {
-      const int n = groups * nqt;
-      const int nb = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
-      hipLaunchKernelGGL(attn_cnt_clear_kernel, dim3((unsigned)nb), dim3(256), 0, s, a.part_cnt, n);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
+  if (a.plan.slots > 0 && (!a.part_acc || !a.part_ml)) return hipErrorInvalidValue;
   if (a.lse)
     hipLaunchKernelGGL(attn_mfma_kernel<true>, dim3((unsigned)nblocks), dim3(256), smem, s, a, nqt,
                        groups);
@@ -1008,7 +903,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
     hipLaunchKernelGGL(attn_mfma_kernel<false>, dim3((unsigned)nblocks), dim3(256), smem, s, a, nqt,
                        groups);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.plan.slots == 0 || !a.plan.ext_merge) return e;
+  if (e != hipSuccess || a.plan.slots == 0) return e;
   hipLaunchKernelGGL(attn_part_merge_kernel, dim3((unsigned)nqt, (unsigned)groups), dim3(256), 0,
                      s, a);
   return hipGetLastError();

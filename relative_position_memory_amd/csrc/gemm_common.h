@@ -17,8 +17,13 @@ __device__ inline const char* gather_row(const RowGather& a, int64_t m, int es) 
 }
 
 __device__ inline const char* weight_row(const WeightPair& w, int64_t n, int es) {
-  return n < w.n_split ? (const char*)w.W0 + n * w.ldw * es
-                       : (const char*)w.W1 + (n - w.n_split) * w.ldw * es;
+  const bool second = n >= w.n_split;
+  if (second) n -= w.n_split;
+  if (w.hd_pad > w.hd_in && w.hd_in > 0) {
+    const int64_t head = n / w.hd_pad, c = n - head * w.hd_pad;
+    n = head * w.hd_in + (c < w.hd_in ? c : w.hd_in - 1);
+  }
+  return (const char*)(second ? w.W1 : w.W0) + n * w.ldw * es;
 }
 
 // Destination of output element (m, n) for EPI_HEADS.
@@ -41,11 +46,13 @@ __device__ inline float epi_value(const Epilogue& e, int64_t n, float acc) {
   return acc;
 }
 
-// Stores element (m, n) of a head-major output; the store of a head's last
-// element also clears the row's padding.
+// Stores element (m, n) of a head-major output (a padding element of a
+// head-padded column as zero); the store of a head's last element also clears
+// the row's padding past d when pad > d.
 template <typename T>
 __device__ inline void heads_store(const GemmArgs& g, int64_t m, int64_t n, float acc) {
   T* p = heads_dst<T>(g, m, n);
+  if (g.e.d_valid > 0 && (n % g.e.HD) % g.e.d >= g.e.d_valid) acc = 0.f;
   Elt<T>::store(p, acc);
   // (padding is less than 8 elements: a fixed-trip loop)
   if (g.e.pad > g.e.d && (n % g.e.HD) % g.e.d == g.e.d - 1) {

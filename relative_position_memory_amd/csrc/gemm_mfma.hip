@@ -191,13 +191,23 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
     const int which = n >= HD, nn = n - which * HD;
     const int head = nn / d, cc = nn - head * d;
     uint16_t* colbase = (uint16_t*)(which ? g.e.dst1 : g.e.dst0) + (int64_t)head * g.e.sh + cc;
+    // head-padded columns: this thread's 8 elements past d_valid are stored as zeros
+    uint32_t keep[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool lo = g.e.d_valid <= 0 || cc + 2 * q < g.e.d_valid;
+      const bool hi = g.e.d_valid <= 0 || cc + 2 * q + 1 < g.e.d_valid;
+      keep[q] = (lo ? 0x0000ffffu : 0u) | (hi ? 0xffff0000u : 0u);
+    }
     const int row0 = tid / CPR;
     int b = (m0 + row0) / per, t = m0 + row0 - b * per;
     for (int row = row0; row < C::BM; row += STEP) {
       if (m0 + row >= g.M) break;
-      if (n < g.N)
+      if (n < g.N) {
+        const uint4 v = *(const uint4*)(es + row * EP + 8 * c);
         *(uint4*)(colbase + b * g.e.sb + ring_t(g.e, t) * g.e.st) =
-            *(const uint4*)(es + row * EP + 8 * c);
+            make_uint4(v.x & keep[0], v.y & keep[1], v.z & keep[2], v.w & keep[3]);
+      }
       t += STEP;
       while (t >= per) { t -= per; ++b; }
     }
@@ -404,18 +414,35 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_dma_kernel(GemmBatch bt) {
   }
 }
 
-// ---- register-staged pipeline (any K % 8 == 0) ---------------------------------------
+// ---- register-staged pipeline (any K % 8 == 0; NARROW: any even K) --------------------
 
-// Thread t stages 16-byte chunk (t % 8) of A rows t/8 + RPP x and W rows t/8 + RPP x.
-template <class C>
+// Thread t stages 8-element piece (t % 8) of A rows t/8 + RPP x and W rows
+// t/8 + RPP x.  Rows whose pitch is a multiple of 8 elements (16-byte aligned)
+// load each piece as one 16-byte access; NARROW rows are only 4-byte aligned
+// (even K and pitches, as with d_model 410): four 4-byte accesses per piece,
+// each taken only below K, so the K tail is zero-filled pair by pair.
+template <class C, bool NARROW>
 struct Loader {
   const uint16_t* arow[C::PA];
   const uint16_t* wrow[C::PW];
   uint32_t aval, wval;  // bit x: row x is inside the problem
   int c, K, tid;
 
+  __device__ static uint4 piece(const uint16_t* row, int kc, int K) {
+    uint32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = kc + 2 * e < K ? *(const uint32_t*)(row + kc + 2 * e) : 0u;
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
   __device__ void load(uint4 (&ra)[C::PA], uint4 (&rw)[C::PW], int k0) const {
     const int kc = k0 + 8 * c;
+    if (NARROW) {
+#pragma unroll
+      for (int x = 0; x < C::PA; ++x) ra[x] = piece(arow[x], kc, K);
+#pragma unroll
+      for (int x = 0; x < C::PW; ++x) rw[x] = piece(wrow[x], kc, K);
+      return;
+    }
     const int kk = kc < K ? kc : K - 8;  // clamped into the row; zeroed at store
 #pragma unroll
     for (int x = 0; x < C::PA; ++x) ra[x] = *(const uint4*)(arow[x] + kk);
@@ -424,7 +451,7 @@ struct Loader {
   }
   __device__ void store(uint16_t* sa, uint16_t* sw, const uint4 (&ra)[C::PA],
                         const uint4 (&rw)[C::PW], int k0) const {
-    const bool kin = k0 + 8 * c < K;
+    const bool kin = NARROW || k0 + 8 * c < K;
 #pragma unroll
     for (int x = 0; x < C::PA; ++x)
       *(uint4*)&sa[((tid >> 3) + C::RPP * x) * C::RKP + 8 * c] =
@@ -436,7 +463,7 @@ struct Loader {
   }
 };
 
-template <class C, int EPI>
+template <class C, int EPI, bool NARROW>
 __global__ __launch_bounds__(C::NT, C::OCC) void gemm_reg_kernel(GemmBatch bt) {
   extern __shared__ __align__(16) char smem_raw[];
   uint16_t* lds = (uint16_t*)smem_raw;
@@ -451,7 +478,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_reg_kernel(GemmBatch bt) {
     const GemmArgs& g = bt.g[tl.p];
     const int m0 = tl.m0, n0 = tl.n0;
 
-    Loader<C> ld;
+    Loader<C, NARROW> ld;
     ld.c = tid & 7;
     ld.K = (int)g.K;
     ld.tid = tid;
@@ -528,10 +555,16 @@ int epi_kind(const GemmArgs& g) {
   return ok ? EPI_STAGE_F32 : EPI_SCALAR;
 }
 
-template <class C, int EPI, bool DMA>
+// Operand loads: LDS-direct (K % 32 == 0, 16-byte rows), register-staged 16-byte
+// pieces (K % 8 == 0), or register-staged 4-byte pairs (even K, 4-byte rows).
+enum { LOAD_DMA = 0, LOAD_REG = 1, LOAD_NARROW = 2 };
+
+template <class C, int EPI, int LOAD>
 hipError_t launch_cfg(const GemmBatch& bt, int total, int num_cus, hipStream_t s) {
+  constexpr bool DMA = LOAD == LOAD_DMA;
   constexpr size_t smem = cmax(DMA ? C::DSMEM : C::RSMEM, epi_smem<C, EPI>());
-  const void* fn = DMA ? (const void*)gemm_dma_kernel<C, EPI> : (const void*)gemm_reg_kernel<C, EPI>;
+  const void* fn = DMA ? (const void*)gemm_dma_kernel<C, EPI>
+                       : (const void*)gemm_reg_kernel<C, EPI, LOAD == LOAD_NARROW>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -544,26 +577,33 @@ hipError_t launch_cfg(const GemmBatch& bt, int total, int num_cus, hipStream_t s
   if (DMA)
     hipLaunchKernelGGL((gemm_dma_kernel<C, EPI>), dim3((unsigned)grid), dim3(C::NT), smem, s, bt);
   else
-    hipLaunchKernelGGL((gemm_reg_kernel<C, EPI>), dim3((unsigned)grid), dim3(C::NT), smem, s, bt);
+    hipLaunchKernelGGL((gemm_reg_kernel<C, EPI, LOAD == LOAD_NARROW>), dim3((unsigned)grid),
+                       dim3(C::NT), smem, s, bt);
   return hipGetLastError();
 }
 
-template <class C, bool DMA>
+template <class C, int LOAD>
 hipError_t launch_epi(const GemmBatch& bt, int epi, int total, int num_cus, hipStream_t s) {
-  if (epi == EPI_STAGE_BF16) return launch_cfg<C, EPI_STAGE_BF16, DMA>(bt, total, num_cus, s);
-  if (epi == EPI_STAGE_F32) return launch_cfg<C, EPI_STAGE_F32, DMA>(bt, total, num_cus, s);
-  return launch_cfg<C, EPI_SCALAR, DMA>(bt, total, num_cus, s);
+  if (epi == EPI_STAGE_BF16) return launch_cfg<C, EPI_STAGE_BF16, LOAD>(bt, total, num_cus, s);
+  if (epi == EPI_STAGE_F32) return launch_cfg<C, EPI_STAGE_F32, LOAD>(bt, total, num_cus, s);
+  return launch_cfg<C, EPI_SCALAR, LOAD>(bt, total, num_cus, s);
 }
 
+// 16-byte operand rows: K, both row pitches a multiple of 8 and 16-byte bases.
+bool wide_rows(const GemmArgs& g) {
+  const uintptr_t al = (uintptr_t)g.a.cur | (uintptr_t)g.w.W0 | (uintptr_t)g.w.W1 |
+                       (g.a.mem_len ? (uintptr_t)g.a.mem : 0);
+  return g.K % 8 == 0 && g.a.lda % 8 == 0 && g.w.ldw % 8 == 0 && al % 16 == 0;
+}
 // LDS-direct loads move whole 32-deep K steps (no tail masking).
-bool dma_ok(const GemmArgs& g) { return g.K % 32 == 0; }
+bool dma_ok(const GemmArgs& g) { return g.K % 32 == 0 && wide_rows(g); }
 
 template <class C>
 hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s) {
   GemmBatch bt{};
   int64_t total = 0;
   int epi = -1;
-  bool dma = true;
+  bool dma = true, wide = true;
   for (int p = 0; p < n; ++p) {
     bt.g[p] = gs[p];
     bt.ntm[p] = (int)((gs[p].M + C::BM - 1) / C::BM);
@@ -574,11 +614,13 @@ hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s) {
     const int k = epi_kind<C>(gs[p]);
     epi = (epi < 0 || epi == k) ? k : EPI_SCALAR;
     dma = dma && dma_ok(gs[p]);
+    wide = wide && wide_rows(gs[p]);
   }
   bt.n = n;
   if (total == 0) return hipSuccess;
-  return dma ? launch_epi<C, true>(bt, epi, (int)total, num_cus, s)
-             : launch_epi<C, false>(bt, epi, (int)total, num_cus, s);
+  if (dma) return launch_epi<C, LOAD_DMA>(bt, epi, (int)total, num_cus, s);
+  if (wide) return launch_epi<C, LOAD_REG>(bt, epi, (int)total, num_cus, s);
+  return launch_epi<C, LOAD_NARROW>(bt, epi, (int)total, num_cus, s);
 }
 
 
@@ -656,7 +698,9 @@ __global__ __launch_bounds__(64 * SK_NW) void gemm_skinny_kernel(SkinnyBatch bt)
   }
 }
 
-bool skinny_ok(const GemmArgs& g) { return g.M <= 32 && g.K % (16 * SK_NW) == 0; }
+bool skinny_ok(const GemmArgs& g) {
+  return g.M <= 32 && g.K % (16 * SK_NW) == 0 && wide_rows(g);
+}
 
 hipError_t launch_skinny(const GemmArgs* gs, int n, hipStream_t s) {
   SkinnyBatch bt{};
@@ -891,10 +935,11 @@ __global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
 }  // namespace
 
 bool gemm_mfma_supported(const GemmArgs& g) {
-  if (g.K % 8 != 0 || g.K < 8 || g.a.lda % 8 != 0 || g.w.ldw % 8 != 0) return false;
+  // even K and row pitches, 4-byte aligned rows (16-byte rows take wider loads)
+  if (g.K % 2 != 0 || g.K < 8 || g.a.lda % 2 != 0 || g.w.ldw % 2 != 0) return false;
   const uintptr_t al = (uintptr_t)g.a.cur | (uintptr_t)g.w.W0 | (uintptr_t)g.w.W1 |
                        (g.a.mem_len ? (uintptr_t)g.a.mem : 0);
-  if (al % 16) return false;
+  if (al % 4) return false;
   // 32-bit row/column/offset arithmetic in the kernel
   if (g.K > 0x7fffffffLL || g.M > 0x7fffffffLL - 256 || g.N > 0x7fffffffLL - 256) return false;
   if (g.e.mode == EPI_HEADS) {

@@ -180,6 +180,21 @@ int run_attn(int dtype, txl::AttnArgs a, void* scratch, size_t scratch_bytes, hi
 
 int run_gemm(int dtype, const txl::GemmArgs& g, hipStream_t st, const char* what);
 
+// Columns of a head-major projection over nw stacked weights of H heads of d
+// rows each, stored with rows padded to dp: the GEMM produces dp columns per
+// head (the ones past d from a repeated weight row, stored as zeros), so that
+// every output row is whole 16-byte pieces of the workspace layout.
+void head_padded_cols(txl::GemmArgs& g, int64_t nw, int64_t H, int64_t d, int64_t dp) {
+  g.N = nw * H * dp;
+  g.w.n_split = H * dp;
+  g.w.hd_in = d;
+  g.w.hd_pad = dp;
+  g.e.HD = H * dp;
+  g.e.d = dp;
+  g.e.pad = 0;
+  g.e.d_valid = d;
+}
+
 // h_out = LayerNorm(a W_o^T + h_in) * gamma + beta (section 3.3), a [B*L][H*d]
 // token-major; y: fp32 [B*L][D] scratch for the unfused form.
 // Whether run_out_ln takes the fused kernel (else it writes y = a W_o^T + h_in,
@@ -419,6 +434,9 @@ static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, c
   gr.a = {nullptr, 1, 0, 0, R, T, D};
   gr.w = {w->W_kR, w->W_kR, HD, D};
   gr.e = {txl::EPI_HEADS, r, r, HD, d, 0, T * dp, dp, nullptr, nullptr, 0, 0, dp};
+  head_padded_cols(gkv, 2, H, d, dp);
+  head_padded_cols(gq, 1, H, d, dp);
+  head_padded_cols(gr, 1, H, d, dp);
   if (dtype == TXL_BF16 && txl::gemm_mfma_supported(gkv) && txl::gemm_mfma_supported(gq) &&
       txl::gemm_mfma_supported(gr)) {
     // the three projections share K and run as one grid
@@ -510,6 +528,7 @@ int txl_pos_proj(void* stream, int dtype, const txl_layer_dims* dims, const void
   gr.a = {nullptr, 1, 0, 0, R, R_rows, D};
   gr.w = {W_kR, W_kR, HD, D};
   gr.e = {txl::EPI_HEADS, r_out, r_out, HD, d, 0, R_rows * dp, dp, nullptr, nullptr, 0, 0, dp};
+  head_padded_cols(gr, 1, H, d, dp);
   return run_gemm(dtype, gr, (hipStream_t)stream, "position projection");
 }
 
@@ -587,6 +606,8 @@ int txl_layer_step_kv(void* stream, int dtype, const txl_layer_dims* dims, const
   gq.a = {nullptr, 1, 0, 0, h_in, L, D};
   gq.w = {w->W_q, w->W_q, HD, D};
   gq.e = {txl::EPI_HEADS, q, q, HD, d, H * L * dp, L * dp, dp, nullptr, nullptr, 0, 0, dp};
+  head_padded_cols(gkv, 2, H, d, dp);
+  head_padded_cols(gq, 1, H, d, dp);
   if (dtype == TXL_BF16 && txl::gemm_mfma_supported(gkv) && txl::gemm_mfma_supported(gq)) {
     const hipError_t e = txl::launch_gemm_mfma_multi(proj, 2, st, num_cus());
     if (e != hipSuccess) return hip_fail(e, "q/kv projections");

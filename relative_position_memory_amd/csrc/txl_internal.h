@@ -41,7 +41,6 @@ constexpr int ATTN_MAXQT = 64, ATTN_MAXCLS = 192;
 struct AttnPlan {
   int ncls;
   int slots;                       // partial slots (sum of nparts over split tiles)
-  int ext_merge;                   // 1: a second kernel merges the parts, 0: the last part
   uint8_t cls_qt[ATTN_MAXCLS], cls_part[ATTN_MAXCLS];
   uint8_t nparts[ATTN_MAXQT];
   uint8_t slot0[ATTN_MAXQT];       // first partial slot of a split tile's parts
@@ -64,16 +63,14 @@ struct AttnArgs {
   // multiple of 8 and may be read whole (columns >= d are ignored).
   int64_t d_load;
   // Split of the key axis (matrix-core path only), see AttnPlan.  Parts of a
-  // split query tile write unnormalised partials; a second kernel merges them
-  // (plan.ext_merge), or the part that finishes last, counted in part_cnt.
+  // split query tile write unnormalised partials; a second kernel, launched
+  // after the attention on the same stream, merges them.
   // Slot s of the plan holds, per (batch, head) group, a block of
   //   part_acc: 128 queries x 64 fp32, part_ml: 128 x 2 fp32 (max in the exp2
   //   domain, sum of exponentials), in the writing lanes' order.
-  // part_cnt [B*H][query tiles] is cleared before the launch and left zero.
   AttnPlan plan;
   float* part_acc;
   float* part_ml;
-  int* part_cnt;
   // Keys as a ring: when kv_cap > 0, key j (0 <= j < mem_len + L <= kv_cap) is
   // row (kv_start + j) % kv_cap of k and v (0 <= kv_start < kv_cap).
   int64_t kv_start, kv_cap;
@@ -182,8 +179,13 @@ struct RowGather {
 
 // Two weight matrices may be stacked along n: rows [0, n_split) of the output
 // use W0, rows [n_split, N) use W1 (row n - n_split).
+// Head-padded columns: when hd_pad > hd_in > 0, output column n of a weight is
+// element n % hd_pad of head n / hd_pad, computed from weight row
+// (n / hd_pad) * hd_in + min(n % hd_pad, hd_in - 1); the columns past hd_in
+// duplicate a real one and the epilogue stores them as zeros (Epilogue::d_valid).
 struct WeightPair {
   const void* W0; const void* W1; int64_t n_split; int64_t ldw;
+  int64_t hd_in, hd_pad;
 };
 
 enum EpiMode { EPI_HEADS = 0, EPI_RESID_F32 = 1 };
@@ -204,6 +206,9 @@ struct Epilogue {
   // EPI_HEADS the activation act (ACT_NONE or ACT_RELU).
   const void* bias;
   int act;
+  // EPI_HEADS with head-padded columns: elements d_valid .. d-1 of every head
+  // row are stored as zeros (0 = every element is valid).
+  int64_t d_valid;
 };
 enum ActMode { ACT_NONE = 0, ACT_RELU = 1 };
 

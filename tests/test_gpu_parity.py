@@ -179,8 +179,8 @@ def test_attn_key_split(B, H, L, M, d):
 
 
 @pytest.mark.parametrize("B,H,L,M,d,frac", [
-    (1, 3, 200, 333, 48, 2),     # parts merged by the last part
-    (1, 2, 128, 1600, 64, 3),    # parts merged by the merge kernel
+    (1, 3, 200, 333, 48, 2),     # half the workspace: fewer parts
+    (1, 2, 128, 1600, 64, 3),    # a third of the workspace
     (1, 2, 128, 1600, 64, 1000), # too small for any split: one part per tile
 ])
 def test_attn_key_split_small_workspace(B, H, L, M, d, frac):
