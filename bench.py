@@ -27,8 +27,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "rel-pos memory attention fwd: query tokens/s + TFLOP/s vs bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "relative_position_memory_amd", "csrc", "attn_mfma.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_charlm_traffic.txt")
+WORKLOAD_NAMES = ("charlm", "wordlm", "large_eval", "large_train")
 
 
 def parse():
@@ -36,7 +37,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="charlm")
+    p.add_argument("--workload", default="charlm", choices=WORKLOAD_NAMES + ("tiny",))
     p.add_argument("--attn-reps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--train", action="store_true",
@@ -57,6 +58,11 @@ def parse():
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (reads 256 MiB, writes 256 MiB) "
                         "so that a counter run can calibrate FETCH_SIZE / WRITE_SIZE")
+    p.add_argument("--no-drift", action="store_true",
+                   help="skip the deep-stack bf16 drift report (batch row 0 against the oracle)")
+    p.add_argument("--pmc-summary", nargs="+", metavar="CSV",
+                   help="no GPU work: summarise rocprofv3 --pmc counter CSVs (per kernel: "
+                        "MFMA busy fraction, bf16 MFMA FLOPs, HBM bytes) and exit")
     return p.parse_args()
 
 
@@ -65,6 +71,21 @@ def attn_flops(w):
     (q.k, (q+v).r and p.v), P = L*M + L(L+1)/2 pairs per (batch, head)."""
     P = w.L * w.M + w.L * (w.L + 1) // 2
     return 6 * w.d * P * w.B * w.H
+
+
+def attn_bytes(w):
+    """Algorithmic HBM bytes of one attention call: q, out, k, v and r once each."""
+    es = 2 if w.dtype == "bf16" else 4
+    T = w.M + w.L
+    return es * (2 * w.B * w.L * w.H * w.d + 2 * w.B * T * w.H * w.d + T * w.H * w.d)
+
+
+def attn_bound(w):
+    """The roofline that bounds the attention at this shape: whichever ideal time
+    (FLOPs at the bf16 MFMA peak, bytes at the HBM peak) is longer."""
+    t_mfma = attn_flops(w) / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = attn_bytes(w) / (PEAK_HBM_GBS * 1e9)
+    return "mfma" if t_mfma >= t_hbm else "hbm"
 
 
 def layer_flops(w):
@@ -122,12 +143,17 @@ def cpu_baseline_train(w, x, target_s):
     }
 
 
-def read_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
-    or None when the kernel source changed since the counters were taken."""
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"attn_mfma_{workload}_traffic.txt")
+
+
+def read_traffic(workload):
+    """HBM bytes per attention launch at this workload from the committed rocprofv3
+    counter summary, or None when there is none or the kernel source changed since
+    the counters were taken."""
     try:
         kv = {}
-        for ln in open(TRAFFIC_FILE):
+        for ln in open(traffic_file(workload)):
             if ":" in ln and not ln.startswith("#"):
                 k, v = ln.split(":", 1)
                 kv[k.strip()] = v.strip()
@@ -139,11 +165,33 @@ def read_traffic():
         return None
 
 
+def cpu_info():
+    """CPU model and core counts of the host that runs the oracle."""
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(w, x, target_s):
     """The oracle, as it stands, on the host cores: one layer step on a sample of
-    the batch rows, scaled to query tokens/s through the N-layer stack."""
+    the batch rows, scaled to query tokens/s through the N-layer stack (all
+    threads, the headline), then the same on one thread, then the attention
+    alone (oracle rel_attn at the workload's shape) on all threads.  The oracle
+    is compiled with -O3 -march=native on this host first."""
     from oracle import oracle as O
-    W0 = x["weights"][0]
+    from relative_position_memory_amd import inputs as I
+    flags = O.use_native_build()
+    threads = O.num_threads()
 
     def run(b, n):
         t0 = time.perf_counter()
@@ -152,20 +200,51 @@ def cpu_baseline(w, x, target_s):
             O.layer_step(x["h0"][0][:b], x["mem"][0][:b], Wl, x["u"], x["v"], x["R"])
         return time.perf_counter() - t0
 
-    t1 = run(1, 1)
-    b = max(1, min(w.B, int(target_s / max(t1, 1e-3))))
-    tb = run(b, 1) if b > 1 else t1
-    n = max(1, int(round(target_s / max(tb, 1e-3))))
-    t = run(b, n) if n > 1 else tb
-    return {
+    def sample(budget, b_max):
+        t1 = run(1, 1)
+        b = max(1, min(b_max, int(budget / max(t1, 1e-3))))
+        tb = run(b, 1) if b > 1 else t1
+        n = max(1, int(round(budget / max(tb, 1e-3))))
+        t = run(b, n) if n > 1 else tb
+        return b, n, t
+
+    b, n, t = sample(target_s * 0.6, w.B)
+    res = {
         "value": n * b * w.L / (t * w.n_layers),
         "unit": "query tokens/s",
-        "cores": O.num_threads(),
+        "cores": threads,
         "kind": "oracle",
         "sample": (f"{n} fp64 layer steps (projections, attention, LayerNorm) over {b} of the "
-                   f"{w.B} batch rows at full memory ({w.M} rows), {t:.1f} s in all; rate scaled "
-                   f"by 1/{w.n_layers} layers to match the stack"),
+                   f"{w.B} batch rows at full memory ({w.M} rows), {t:.1f} s in all on {threads} "
+                   f"threads; rate scaled by 1/{w.n_layers} layers to match the stack"),
+        "build": f"gcc {flags}",
     }
+    res.update(cpu_info())
+    O.set_num_threads(1)
+    try:
+        b1, n1, t1 = sample(target_s * 0.2, w.B)
+    finally:
+        O.set_num_threads(threads)
+    res["single_thread"] = {"value": n1 * b1 * w.L / (t1 * w.n_layers), "unit": "query tokens/s",
+                            "sample": f"{n1} layer steps over {b1} batch rows, {t1:.1f} s, 1 thread"}
+    # attention alone: the oracle's rel_attn over batch rows of the workload's shape
+    c = I.attention_inputs(1, w.H, w.L, w.M, w.d, seed=0, sigma=1.0, sigma_uv=0.1)
+    t0 = time.perf_counter()
+    O.rel_attn(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], w.M)
+    ta = time.perf_counter() - t0
+    na = max(1, int(round(target_s * 0.2 / max(ta, 1e-3))))
+    if na > 1:
+        t0 = time.perf_counter()
+        for _ in range(na):
+            O.rel_attn(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], w.M)
+        ta = (time.perf_counter() - t0) / na
+    row_flops = attn_flops(w) / w.B
+    res["attention_alone"] = {
+        "query_tokens_per_s": w.L / ta, "gflops": row_flops / ta / 1e9,
+        "ms_per_call_full_batch": ta * w.B * 1e3,
+        "sample": f"{na} oracle rel_attn calls on 1 batch row ({w.H} heads, L {w.L}, memory "
+                  f"{w.M}), {ta * 1e3:.1f} ms each on {threads} threads; full batch = x{w.B}"}
+    return res
 
 
 def pos_ff_time(w, reps, stream):
@@ -515,8 +594,94 @@ def eval_speed(args):
                 "context, not a target"}), flush=True)
 
 
+def hip_time_us(fn, reps, stream):
+    """Average time of fn() in us over reps back-to-back calls, HIP events on stream."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def stack_drift(w, x, lws, u, vb, R, dims, ws, tdt, stream, segments):
+    """Deep-stack bf16 drift, reported and not gated: the stack (every layer, the
+    first `segments` segments, memory updates) from the initial memory on the
+    GPU, and the oracle's fp64 recurrence on batch row 0 (batch rows are
+    independent).  Max-abs difference of the top layer's output per segment."""
+    import numpy as np
+    import torch
+    from oracle import oracle as O
+    from relative_position_memory_amd import txl
+    dev = lambda a: torch.from_numpy(a).to(tdt).cuda()
+    datas = [dev(m) for m in x["mem"]]
+    rings = [txl.make_ring(dd, 0, w.M) for dd in datas]
+    bufs = [torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(2)]
+    gpu_top = []
+    for s_ in range(segments):
+        h = dev(x["h0"][s_])
+        for n in range(w.n_layers):
+            out = bufs[n % 2]
+            txl.layer_step(dims, h, rings[n], lws[n], u, vb, R, out, ws, stream=stream)
+            txl.mem_update(rings[n], h, stream=stream)
+            h = out
+        gpu_top.append(h[:1].float().cpu().numpy().astype(np.float64))
+    mems = [m[:1] for m in x["mem"]]
+    per_seg = []
+    t0 = time.perf_counter()
+    for s_ in range(segments):
+        h = x["h0"][s_][:1].astype(np.float64)
+        for n in range(w.n_layers):
+            out = O.layer_step(h, mems[n], x["weights"][n], x["u"], x["v"], x["R"])
+            mems[n] = O.mem_update(mems[n], h, w.M)
+            h = out
+        per_seg.append(float(np.abs(gpu_top[s_] - h).max()))
+    return {"max_abs_per_segment": per_seg, "layers": w.n_layers, "segments": segments,
+            "rows": f"batch row 0, all {w.L} positions, top layer output",
+            "oracle_s": time.perf_counter() - t0,
+            "note": "reported, not gated: the oracle runs fp64 throughout, the GPU stores every "
+                    "layer's output and memory in bf16 (half an ulp of |x| in [4, 8) is 0.0156)"}
+
+
+def pmc_summary(paths):
+    """Per-kernel summary of rocprofv3 --pmc CSVs (kernel-serialised counters, one
+    row per dispatch and counter).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES summed over
+    the GPU / (GRBM_GUI_ACTIVE x 1024 SIMDs), the form of the tool's MfmaUtil; bf16
+    MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; FETCH_SIZE / WRITE_SIZE in KiB."""
+    import collections
+    import csv
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        per_dispatch = collections.defaultdict(dict)
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"], r["Grid_Size"])
+            per_dispatch[(key, r.get("Dispatch_Id", r.get("Correlation_Id", "")))][
+                r["Counter_Name"]] = float(r["Counter_Value"])
+        for (key, _), cs in per_dispatch.items():
+            for c, v in cs.items():
+                agg[key][c].append(v)
+    print(f"{'kernel':58s} {'grid':>9s} {'n':>4s}  counters (mean per dispatch)")
+    for (name, grid), cs in sorted(agg.items(), key=lambda kv: -len(kv[1])):
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        parts = [f"{c}={m:.4g}" for c, m in sorted(mean.items())]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE"):
+            parts.append(f"MFMA_busy={mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (mean['GRBM_GUI_ACTIVE'] * 1024):.3f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
+            parts.append(f"bf16_MFMA_GFLOP={mean['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.3f}")
+        print(f"{name[:58]:58s} {grid:>9s} {n:4d}  " + "  ".join(parts))
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this benchmark runs on exactly one GPU (asked for --gpus {args.gpus}, "
@@ -540,6 +705,7 @@ def main():
     w = I.workload(args.workload)
     x = I.make_inputs(w, seed=0)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    es = 2 if w.dtype == "bf16" else 4
     dev = lambda a: torch.from_numpy(a).to(tdt).cuda()
     Ws = [{k: dev(v) for k, v in lw.items()} for lw in x["weights"]]
     lws = [txl.layer_weights(Wl) for Wl in Ws]
@@ -572,27 +738,49 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
-    # the attention kernel alone, on the last layer step's q, k, v, r (HIP events, same stream)
-    views = txl.workspace_views(dims, w.M, ws, tdt)
-    out_a = torch.empty((w.B, w.L, w.H, w.d), dtype=tdt, device="cuda")
-    nws = txl.rel_attn_workspace_bytes(tdt, w.B, w.H, w.L, w.M, w.d)
+    # the attention kernel alone, on the last layer step's q, k, v, r (HIP events, same
+    # stream); with the memory full (every ring holds M rows after the first segment)
+    # A head size that is not a multiple of 8 (the word model's 41): the layer step's
+    # attention reads its head rows padded to d_pad with zeros, and this times that
+    # same launch -- d_pad-wide views, u and v zero-padded, scale 1/sqrt(d).
+    dpad = txl.d_pad(w.d)
+    views = txl.workspace_views(dims, w.M, ws, tdt, padded=True)
+    ua = torch.zeros((w.H, dpad), dtype=tdt, device="cuda")
+    va = torch.zeros((w.H, dpad), dtype=tdt, device="cuda")
+    ua[:, :w.d], va[:, :w.d] = u, vb
+    out_a = torch.empty((w.B, w.L, w.H, dpad), dtype=tdt, device="cuda")
+    nws = txl.rel_attn_workspace_bytes(tdt, w.B, w.H, w.L, w.M, dpad)
     aws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
 
     def attn():
-        txl.rel_attn_fwd(views["q"], views["k"], views["v"], views["r"], u, vb, w.M, out_a,
-                         stream=stream, workspace=aws)
+        txl.rel_attn_fwd(views["q"], views["k"], views["v"], views["r"], ua, va, w.M, out_a,
+                         scale=1.0 / math.sqrt(w.d), stream=stream, workspace=aws)
 
-    for _ in range(3):
-        attn()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for _ in range(args.attn_reps):
-        attn()
-    a1.record(stream)
-    torch.cuda.synchronize()
-    attn_s = a0.elapsed_time(a1) / args.attn_reps / 1e3
-    af = attn_flops(w)
+    attn_s = hip_time_us(attn, args.attn_reps, stream) / 1e6
+    af, ab = attn_flops(w), attn_bytes(w)
     attn_tflops = af / attn_s / 1e12
+    attn_gbs = ab / attn_s / 1e9
+    bound = attn_bound(w)
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                "hbm_frac": attn_gbs / PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": attn_gbs / PEAK_HBM_GBS, "mfma_frac": attn_tflops / PEAK_BF16_TFLOPS}
+    roof.update({"traffic": read_traffic(w.name),
+                 "kernel": "attn_mfma_kernel" + (" + key-split merge" if nws else ""),
+                 "launch_us": attn_s * 1e6, "flop_per_launch": af, "bytes_per_launch": ab})
+
+    # one layer step alone (full memory; projections, attention, output projection +
+    # LayerNorm), and one memory update alone on a scratch ring
+    ls_us = hip_time_us(lambda: txl.layer_step(dims, h0[0], rings[0], lws[0], u, vb, R, bufs[0],
+                                               ws, stream=stream), 20, stream)
+    lf = layer_flops(w)
+    scratch = torch.empty_like(ring_data[0])
+    sring = txl.make_ring(scratch, 0, w.M)
+    mu_us = hip_time_us(lambda: txl.mem_update(sring, h0[0], stream=stream), 20, stream)
+    mu_bytes = 2 * w.B * min(w.L, w.M) * w.D * es
 
     # the same stack with cached keys and values (txl_layer_step_kv): each layer's
     # ring is filled from its initial memory first (untimed), then the segments run
@@ -622,10 +810,13 @@ def main():
                                f"with memory update", "batch": w.B, "d_model": w.D,
                    "n_head": w.H, "d_head": w.d, "segment_len": w.L, "mem_len": w.M,
                    "n_layers": w.n_layers, "n_segments": w.n_segments},
-        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel",
-                     "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic(),
-                     "launch_us": attn_s * 1e6, "flop_per_launch": af},
+        "roofline": roof,
+        "layer_step": {"us": ls_us, "flop": lf, "achieved": lf / (ls_us * 1e-6) / 1e12,
+                       "unit": "TFLOP/s", "frac": lf / (ls_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                       "bound": "mfma"},
+        "mem_update": {"us": mu_us, "bytes": mu_bytes, "achieved": mu_bytes / (mu_us * 1e-6) / 1e9,
+                       "unit": "GB/s", "frac": mu_bytes / (mu_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                       "bound": "hbm", "kernel": "ring_copy_kernel"},
         "step_tflops": step_flops / (ms / 1e3) / 1e12,
     }
     if not args.main_only:
@@ -641,6 +832,9 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+    if not args.no_drift and not args.main_only:
+        res["stack_drift"] = stack_drift(w, x, lws, u, vb, R, dims, ws, tdt, stream,
+                                         min(w.n_segments, 4))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -17,6 +17,7 @@ import numpy as np
 from . import build as _build
 
 _LIB = None
+_LIB_PATH = _build.LIB
 _i64 = ctypes.c_int64
 _dbl = ctypes.c_double
 _p = ctypes.c_void_p
@@ -25,9 +26,9 @@ _p = ctypes.c_void_p
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
+        if not os.path.exists(_LIB_PATH):
             _build.build()
-        lib = ctypes.CDLL(_build.LIB)
+        lib = ctypes.CDLL(_LIB_PATH)
         lib.txo_rel_attn.argtypes = [_i64] * 5 + [_p] * 6 + [_dbl, _p, _p]
         lib.txo_rel_attn.restype = None
         lib.txo_linear.argtypes = [_i64] * 3 + [_p] * 3
@@ -45,8 +46,27 @@ def _lib():
         lib.txo_pos_ff.restype = ctypes.c_int
         lib.txo_num_threads.argtypes = []
         lib.txo_num_threads.restype = ctypes.c_int
+        lib.txo_set_num_threads.argtypes = [ctypes.c_int]
+        lib.txo_set_num_threads.restype = None
         _LIB = lib
     return _LIB
+
+
+def use_native_build() -> str:
+    """Switch this process to the oracle compiled with -march=native for the
+    host it runs on (built now, before the first call); returns its flags.
+    Only the benchmark's CPU-baseline leg does this; results are the same."""
+    global _LIB, _LIB_PATH
+    if _LIB is not None and _LIB_PATH != _build.LIB:
+        return _build.flags(native=True)
+    _LIB_PATH = _build.build(native=True)
+    _LIB = None
+    _lib()
+    return _build.flags(native=True)
+
+
+def set_num_threads(n: int) -> None:
+    _lib().txo_set_num_threads(int(n))
 
 
 def _f64(x):

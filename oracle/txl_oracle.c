@@ -47,6 +47,15 @@ int txo_num_threads(void) {
 #endif
 }
 
+/* Threads of the parallel regions that follow (the benchmark's 1-thread run). */
+void txo_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 static double dot(const double* a, const double* b, int64_t n) {
     double s = 0.0;
     for (int64_t c = 0; c < n; ++c) s += a[c] * b[c];

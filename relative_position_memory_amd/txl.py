@@ -324,15 +324,18 @@ def layer_step_bwd(dims, h, ring, W, u, vb, R, dh_out, workspace, grads=None, st
     return grads
 
 
-def workspace_views(dims, mem_len, workspace, dtype):
+def workspace_views(dims, mem_len, workspace, dtype, padded=False):
     """Views of the intermediates txl_layer_step leaves in `workspace`
-    (txl_layer_workspace_map): q [B,L,H,d], k/v [B,T,H,d], r [T,H,d], a [B,L,H,d]."""
+    (txl_layer_workspace_map): q [B,L,H,d], k/v [B,T,H,d], r [T,H,d], a [B,L,H,d].
+    padded=True gives q, k, v, r with their whole d_pad-wide rows (the columns
+    past d hold zeros)."""
     mp = WorkspaceMap()
     _check(_lib.txl_layer_workspace_map(ctypes.byref(dims), int(mem_len), dtype_code(dtype),
                                         ctypes.byref(mp)), "txl_layer_workspace_map")
     B, L, H, d, dp = dims.B, dims.L, dims.n_head, dims.d_head, mp.d_pad
     T = mem_len + L
     es = torch.tensor([], dtype=dtype).element_size()
+    dq = dp if padded else d
 
     def view(off, shape):
         n = 1
@@ -340,10 +343,10 @@ def workspace_views(dims, mem_len, workspace, dtype):
             n *= s
         return workspace[off: off + n * es].view(dtype).view(*shape)
 
-    q = view(mp.q, (B, H, L, dp))[..., :d].permute(0, 2, 1, 3)
-    k = view(mp.k, (B, H, T, dp))[..., :d].permute(0, 2, 1, 3)
-    v = view(mp.v, (B, H, T, dp))[..., :d].permute(0, 2, 1, 3)
-    r = view(mp.r, (H, T, dp))[..., :d].permute(1, 0, 2)
+    q = view(mp.q, (B, H, L, dp))[..., :dq].permute(0, 2, 1, 3)
+    k = view(mp.k, (B, H, T, dp))[..., :dq].permute(0, 2, 1, 3)
+    v = view(mp.v, (B, H, T, dp))[..., :dq].permute(0, 2, 1, 3)
+    r = view(mp.r, (H, T, dp))[..., :dq].permute(1, 0, 2)
     a = view(mp.a, (B, L, H, d))
     return {"q": q, "k": k, "v": v, "r": r, "a": a}
 
