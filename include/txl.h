@@ -13,7 +13,8 @@
  * Conventions shared by every entry point
  *   - All tensors are device pointers (hipMalloc'd or torch-allocated memory).
  *     The library allocates no device memory; scratch comes from the caller's
- *     workspace argument.
+ *     workspace argument (txl_rel_attn_fwd_noalloc alone uses a fixed static
+ *     device array instead).
  *   - Strides are in ELEMENTS.  Element types: TXL_FP32 = float,
  *     TXL_BF16 = bfloat16 (stored as 16-bit words).  One call uses one dtype for
  *     all of its tensor arguments (scores_dbg is always float).
@@ -110,6 +111,36 @@ int txl_rel_attn_fwd(void* stream, int dtype,
  */
 size_t txl_rel_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L,
                                     int64_t mem_len, int64_t d_head);
+
+/*
+ * txl_rel_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments, layouts and results, without the workspace.
+ * The key-split partials go to the library's static device scratch instead, a
+ * file-scope array of txl_rel_attn_noalloc_max_scratch_bytes() bytes (16 MiB)
+ * that every device the library runs on holds from the library's load until the
+ * process ends.  The call allocates nothing and calls no allocating routine.
+ *   - A shape whose split plan needs more scratch than that returns
+ *     TXL_EWORKSPACE (txl_rel_attn_workspace_bytes() gives the need) and
+ *     writes nothing; use txl_rel_attn_fwd with a workspace there.
+ *   - Nothing in the scratch needs to start at zero: every partial is written
+ *     before the same call reads it; the last call's contents stay behind.
+ *   - All calls on one GPU share that GPU's scratch: calls that may overlap in
+ *     time on one GPU (several streams, several host threads) race and must be
+ *     ordered by the caller.
+ * Returns TXL_OK or a txl_status.
+ */
+int txl_rel_attn_fwd_noalloc(void* stream, int dtype,
+                             int64_t B, int64_t H, int64_t L, int64_t mem_len, int64_t d_head,
+                             const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                             const void* k, const void* v, int64_t kv_sb, int64_t kv_st,
+                             int64_t kv_sh, const void* r, int64_t r_sp, int64_t r_sh,
+                             int64_t r_rows, const void* u_bias, const void* v_bias, float scale,
+                             void* out, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                             float* scores_dbg);
+
+/* Bytes of the static scratch txl_rel_attn_fwd_noalloc uses (its maximum). */
+size_t txl_rel_attn_noalloc_max_scratch_bytes(void);
 
 /*
  * Backward pass of txl_rel_attn_fwd (training with a stop-gradient memory:

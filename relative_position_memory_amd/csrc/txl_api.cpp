@@ -318,6 +318,42 @@ int txl_rel_attn_fwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
   return run_attn(dtype, a, workspace, ws_bytes, (hipStream_t)stream);
 }
 
+int txl_rel_attn_fwd_noalloc(void* stream, int dtype, int64_t B, int64_t H, int64_t L,
+                             int64_t mem_len, int64_t d_head, const void* q, int64_t q_sb,
+                             int64_t q_st, int64_t q_sh, const void* k, const void* v,
+                             int64_t kv_sb, int64_t kv_st, int64_t kv_sh, const void* r,
+                             int64_t r_sp, int64_t r_sh, int64_t r_rows, const void* u_bias,
+                             const void* v_bias, float scale, void* out, int64_t o_sb,
+                             int64_t o_st, int64_t o_sh, float* scores_dbg) {
+  g_detail[0] = 0;
+  txl::AttnArgs a{};
+  a.B = B; a.H = H; a.L = L; a.mem_len = mem_len; a.d = d_head;
+  a.q = q; a.q_sb = q_sb; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = k; a.v = v; a.kv_sb = kv_sb; a.kv_st = kv_st; a.kv_sh = kv_sh;
+  a.r = r; a.r_sp = r_sp; a.r_sh = r_sh;
+  a.u = u_bias; a.vb = v_bias; a.scale = scale;
+  a.out = out; a.o_sb = o_sb; a.o_st = o_st; a.o_sh = o_sh;
+  a.scores = scores_dbg;
+  a.d_load = d_head;
+  const int rc = check_attn(dtype, a, r_rows);
+  if (rc != TXL_OK) return rc;
+  // the whole split plan of this shape must fit the static scratch
+  const size_t need = attn_plan_bytes(dtype, a);
+  if (need > txl::STATIC_SCRATCH_BYTES)
+    return fail(TXL_EWORKSPACE,
+                "the key split of this shape needs %zu bytes of scratch; the static scratch "
+                "holds %zu (use txl_rel_attn_fwd with a workspace)",
+                need, (size_t)txl::STATIC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = txl::static_scratch_ptr(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  }
+  return run_attn(dtype, a, scratch, need, (hipStream_t)stream);
+}
+
+size_t txl_rel_attn_noalloc_max_scratch_bytes(void) { return txl::STATIC_SCRATCH_BYTES; }
+
 size_t txl_rel_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L, int64_t mem_len,
                                     int64_t d_head) {
   if ((dtype != TXL_FP32 && dtype != TXL_BF16) || B < 1 || H < 1 || L < 1 || mem_len < 0 ||

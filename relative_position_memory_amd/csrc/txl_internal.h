@@ -238,4 +238,9 @@ hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0,
 // p[0 .. n) = value
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 
+// Static device scratch of txl_rel_attn_fwd_noalloc (static_scratch.hip): its
+// size, and its address on the current device (looked up once per device).
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)16 << 20;
+hipError_t static_scratch_ptr(void** out);
+
 }  // namespace txl

@@ -135,6 +135,40 @@ def rel_attn_fwd(q, k, v, r, u, vb, mem_len, out, scale=None, scores=None, strea
     return out
 
 
+_lib.txl_rel_attn_fwd_noalloc.argtypes = _lib.txl_rel_attn_fwd.argtypes[:-2]
+_lib.txl_rel_attn_fwd_noalloc.restype = ctypes.c_int
+_lib.txl_rel_attn_noalloc_max_scratch_bytes.argtypes = []
+_lib.txl_rel_attn_noalloc_max_scratch_bytes.restype = _sz
+
+
+def rel_attn_noalloc_max_scratch_bytes() -> int:
+    return int(_lib.txl_rel_attn_noalloc_max_scratch_bytes())
+
+
+def rel_attn_fwd_noalloc(q, k, v, r, u, vb, mem_len, out, scale=None, scores=None, stream=None):
+    """txl_rel_attn_fwd_noalloc: rel_attn_fwd without a workspace (the library's
+    static device scratch holds the key-split partials)."""
+    B, L, H, d = q.shape
+    for t in (q, k, v, r, out):
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if scores is not None and (scores.dtype != torch.float32 or not scores.is_contiguous()):
+        raise ValueError("scores must be a contiguous float32 tensor")
+    rc = _lib.txl_rel_attn_fwd_noalloc(
+        _stream(stream), dtype_code(q.dtype), B, H, L, int(mem_len), d,
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2),
+        _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
+        _ptr(r), r.stride(0), r.stride(1), r.shape[0],
+        _ptr(u), _ptr(vb), float(scale),
+        _ptr(out), out.stride(0), out.stride(1), out.stride(2), _ptr(scores))
+    _check(rc, "txl_rel_attn_fwd_noalloc")
+    return out
+
+
 def rel_attn_bwd_workspace_bytes(dtype, B, H, L, mem_len, d):
     """txl_rel_attn_bwd_workspace_bytes."""
     return int(_lib.txl_rel_attn_bwd_workspace_bytes(dtype_code(dtype), B, H, L, int(mem_len), d))

@@ -162,3 +162,30 @@ def test_saved_state_argument_errors_need_no_gpu():
                                         ctypes.byref(ring), ctypes.byref(W), fake, fake, fake,
                                         64, fake, None, ctypes.byref(grads),
                                         ctypes.c_void_p(0x20000000), 1 << 30) == txl.EINVAL
+
+
+def test_noalloc_entry_point_checks_need_no_gpu():
+    """txl_rel_attn_fwd_noalloc: bad arguments and a split larger than the static
+    scratch are rejected on the host, before any HIP call."""
+    from relative_position_memory_amd import txl
+    lib = txl._lib
+    assert txl.rel_attn_noalloc_max_scratch_bytes() == 16 << 20
+    args = [None, txl.BF16, 1, 1, 4, 0, 16] + [None, 16, 16, 16] + [None, None, 16, 16, 16] \
+        + [None, 16, 16, 4] + [None, None, 0.25] + [None, 16, 16, 16] + [None]
+    assert lib.txl_rel_attn_fwd_noalloc(*args) == txl.EINVAL
+    # B 1, H 16, L = M = 1600, d 64, head-major bf16: the split plan needs more
+    # than 16 MiB of partials
+    B, H, L, M, d = 1, 16, 1600, 1600, 64
+    T = M + L
+    gb = 1 << 30
+    base = lambda i: ctypes.c_void_p((i + 1) * gb)
+    need = lib.txl_rel_attn_workspace_bytes(txl.BF16, B, H, L, M, d)
+    assert need > 16 << 20
+    args = [None, txl.BF16, B, H, L, M, d,
+            base(0), H * L * d, d, L * d,
+            base(1), base(2), H * T * d, d, T * d,
+            base(3), d, T * d, T,
+            base(4), base(5), 0.125,
+            base(6), L * H * d, H * d, d, None]
+    assert lib.txl_rel_attn_fwd_noalloc(*args) == txl.EWORKSPACE
+    assert "static scratch" in txl.status_string(txl.EWORKSPACE)
