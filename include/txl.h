@@ -312,7 +312,8 @@ int txl_layer_step_bwd(void* stream, int dtype, const txl_layer_dims* dims,
  * and, where the forward has them, its softmax statistics and LayerNorm input);
  * txl_layer_step_bwd_saved is txl_layer_step_bwd that takes them from there.
  * The arguments of the two calls must be the same (and the memory unchanged in
- * between), as in a training step: forward through the stack, then backward.
+ * between), as in a training step: forward through the stack, then backward;
+ * the backward checks the memory, h_in, dims and dtype against the save.
  *   saved->data   device memory of saved->bytes >= txl_layer_saved_bytes(dims,
  *                 mem->capacity, dtype), 256-byte aligned, not overlapping any
  *                 other argument; owned by the caller, alive until the backward.
@@ -326,6 +327,16 @@ typedef struct {
   size_t bytes;
   int    has_lse;  /* the softmax statistics are in data */
   int    has_y;    /* the fp32 LayerNorm input is in data */
+  /* Written by txl_layer_step_save: the call the state belongs to.  The backward
+   * re-gathers the context [memory ; h_in] from the ring, so it returns
+   * TXL_EINVAL, writing nothing, when the ring (data, capacity, start, len),
+   * h_in, the dims or the dtype differ -- e.g. after a txl_mem_update of that
+   * ring between the two calls. */
+  const void* mem_data;
+  int64_t mem_capacity, mem_start, mem_len;
+  const void* h_in;
+  int64_t B, L, d_model, n_head, d_head;
+  int     dtype;
 } txl_layer_saved;
 
 size_t txl_layer_saved_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype);

@@ -926,6 +926,18 @@ int txl_layer_step_save(void* stream, int dtype, const txl_layer_dims* dims, con
                       base + sl.fwd, sl.lse - sl.fwd, (float*)(base + sl.lse), &has_lse, &has_y);
   saved->has_lse = has_lse ? 1 : 0;
   saved->has_y = has_y ? 1 : 0;
+  // what the state belongs to (the backward checks it)
+  saved->mem_data = mem->data;
+  saved->mem_capacity = mem->capacity;
+  saved->mem_start = mem->start;
+  saved->mem_len = mem->len;
+  saved->h_in = h_in;
+  saved->B = dims->B;
+  saved->L = dims->L;
+  saved->d_model = dims->d_model;
+  saved->n_head = dims->n_head;
+  saved->d_head = dims->d_head;
+  saved->dtype = dtype;
   return rc;
 }
 
@@ -974,6 +986,16 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
         !w->ln_beta || !h_in || !u_bias || !v_bias || !R || !mem->data)
       return fail(TXL_EINVAL, "NULL argument");
     if (R_rows < mem->len + L) return fail(TXL_EINVAL, "R_rows < mem->len + L");
+    if (saved->mem_data != mem->data || saved->mem_capacity != mem->capacity ||
+        saved->mem_start != mem->start || saved->mem_len != mem->len)
+      return fail(TXL_EINVAL,
+                  "the memory differs from the one the state was saved with (ring start %lld "
+                  "len %lld then, %lld %lld now): run the backward before the memory update",
+                  (long long)saved->mem_start, (long long)saved->mem_len, (long long)mem->start,
+                  (long long)mem->len);
+    if (saved->h_in != h_in || saved->dtype != dtype || saved->B != dm.B || saved->L != dm.L ||
+        saved->d_model != dm.d_model || saved->n_head != dm.n_head || saved->d_head != dm.d_head)
+      return fail(TXL_EINVAL, "h_in, the dims or the dtype differ from the saved forward's");
   }
   const Span ssaved = {(uintptr_t)(saved ? saved->data : nullptr),
                        (uintptr_t)(saved ? (char*)saved->data + saved->bytes : nullptr)};

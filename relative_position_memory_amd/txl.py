@@ -279,8 +279,12 @@ _lib.txl_layer_step_bwd.restype = ctypes.c_int
 
 
 class LayerSaved(ctypes.Structure):
+    """txl_layer_saved: the buffer, what it holds, and the call it belongs to."""
     _fields_ = [("data", ctypes.c_void_p), ("bytes", _sz), ("has_lse", ctypes.c_int),
-                ("has_y", ctypes.c_int)]
+                ("has_y", ctypes.c_int), ("mem_data", ctypes.c_void_p),
+                ("mem_capacity", _i64), ("mem_start", _i64), ("mem_len", _i64),
+                ("h_in", ctypes.c_void_p), ("B", _i64), ("L", _i64), ("d_model", _i64),
+                ("n_head", _i64), ("d_head", _i64), ("dtype", ctypes.c_int)]
 
 
 _lib.txl_layer_saved_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int]
@@ -306,7 +310,7 @@ def layer_step_save(dims, h_in, ring, W, u, vb, R, h_out, saved_buf, stream=None
     """txl_layer_step_save into the device buffer saved_buf (uint8, 256-byte
     aligned); returns the LayerSaved to hand to layer_step_bwd(saved=...)."""
     lw = W if isinstance(W, LayerWeights) else layer_weights(W)
-    sv = LayerSaved(_ptr(saved_buf), saved_buf.numel() * saved_buf.element_size(), 0, 0)
+    sv = LayerSaved(data=_ptr(saved_buf), bytes=saved_buf.numel() * saved_buf.element_size())
     rc = _lib.txl_layer_step_save(_stream(stream), dtype_code(h_in.dtype), ctypes.byref(dims),
                                   _ptr(h_in), ctypes.byref(ring), ctypes.byref(lw), _ptr(u),
                                   _ptr(vb), _ptr(R), R.shape[0], _ptr(h_out), ctypes.byref(sv))

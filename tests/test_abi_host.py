@@ -163,6 +163,28 @@ def test_saved_state_argument_errors_need_no_gpu():
                                         64, fake, None, ctypes.byref(grads),
                                         ctypes.c_void_p(0x20000000), 1 << 30) == txl.EINVAL
 
+    # a state saved with the ring at (start 0, len 16): the backward refuses the
+    # same ring after a memory update (start 5) and a different h_in
+    def saved_as(**over):
+        f = dict(data=0x10000000, bytes=nsv, has_lse=1, has_y=0, mem_data=0x200000,
+                 mem_capacity=16, mem_start=0, mem_len=16, h_in=0x300000, B=2, L=16,
+                 d_model=64, n_head=2, d_head=32, dtype=txl.BF16)
+        f.update(over)
+        return txl.LayerSaved(**f)
+
+    def bwd(sv, rg):
+        return lib.txl_layer_step_bwd_saved(None, txl.BF16, ctypes.byref(dims), h_in,
+                                            ctypes.byref(rg), ctypes.byref(W), fake, fake, fake,
+                                            64, fake, ctypes.byref(sv), ctypes.byref(grads),
+                                            ctypes.c_void_p(0x20000000), 1 << 30)
+
+    moved = txl.Ring(0x200000, 16, 5, 16)
+    assert bwd(saved_as(), moved) == txl.EINVAL
+    assert "memory differs" in txl.status_string(txl.EINVAL)
+    assert bwd(saved_as(h_in=0x310000), ring) == txl.EINVAL
+    assert "h_in" in txl.status_string(txl.EINVAL)
+    assert bwd(saved_as(d_model=128), ring) == txl.EINVAL
+
 
 def test_noalloc_entry_point_checks_need_no_gpu():
     """txl_rel_attn_fwd_noalloc: bad arguments and a split larger than the static
