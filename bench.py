@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "rel-pos memory attention fwd: query tokens/s + TFLOP/s vs bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+MI355X_XCDS, MI355X_SIMDS = 8, 1024   # accelerator dies; 256 CUs x 4 SIMDs
 ATTN_SRC = os.path.join(ROOT, "relative_position_memory_amd", "csrc", "attn_mfma.hip")
 WORKLOAD_NAMES = ("charlm", "wordlm", "large_eval", "large_train")
 
@@ -650,9 +651,12 @@ def stack_drift(w, x, lws, u, vb, R, dims, ws, tdt, stream, segments):
 
 def pmc_summary(paths):
     """Per-kernel summary of rocprofv3 --pmc CSVs (kernel-serialised counters, one
-    row per dispatch and counter).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES summed over
-    the GPU / (GRBM_GUI_ACTIVE x 1024 SIMDs), the form of the tool's MfmaUtil; bf16
-    MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; FETCH_SIZE / WRITE_SIZE in KiB."""
+    row per dispatch and counter, each the sum over the counter's hardware
+    instances).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (matrix-core cycles summed over
+    all SIMDs: 16 per 16x16x32 and 32 per 32x32x16 bf16 instruction) / (the kernel's
+    busy cycles x 1024 SIMDs), the kernel's busy cycles being GRBM_GUI_ACTIVE / 8
+    (one instance per XCD); bf16 MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512;
+    FETCH_SIZE / WRITE_SIZE in KiB."""
     import collections
     import csv
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
@@ -671,7 +675,9 @@ def pmc_summary(paths):
         n = max(len(v) for v in cs.values())
         parts = [f"{c}={m:.4g}" for c, m in sorted(mean.items())]
         if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE"):
-            parts.append(f"MFMA_busy={mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (mean['GRBM_GUI_ACTIVE'] * 1024):.3f}")
+            busy = mean["GRBM_GUI_ACTIVE"] / MI355X_XCDS
+            parts.append(f"busy_us={busy / 2.4e3:.1f}")
+            parts.append(f"MFMA_busy={mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (busy * MI355X_SIMDS):.3f}")
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
             parts.append(f"bf16_MFMA_GFLOP={mean['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.3f}")
         print(f"{name[:58]:58s} {grid:>9s} {n:4d}  " + "  ".join(parts))
