@@ -34,6 +34,9 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int NXCD = 8;
 constexpr int MAXP = 4;
+#ifndef TXL_GEMV
+#define TXL_GEMV 1
+#endif
 
 struct GemmBatch {
   GemmArgs g[MAXP];
@@ -698,6 +701,108 @@ __global__ __launch_bounds__(64 * SK_NW) void gemm_skinny_kernel(SkinnyBatch bt)
   }
 }
 
+// ---- matrix-vector products: at most 4 rows (one-token decode steps) -----------------
+// C = A W^T with M <= 4: the products are weight-streaming, so the weights are
+// read once with 16-byte coalesced loads and summed on the vector ALU.  A
+// workgroup of 4 waves covers GV_COLS consecutive output columns; each wave
+// takes GV_WCOLS of them (weight rows n), its 64 lanes reading consecutive
+// 8-element pieces of each row (K % 8 == 0), then reduces each (row m, column
+// n) sum across the lanes.  The usual element epilogue stores the results.
+constexpr int GV_WAVES = 4, GV_WCOLS = 4, GV_COLS = GV_WAVES * GV_WCOLS, GV_MAXM = 4;
+
+__global__ __launch_bounds__(64 * GV_WAVES) void gemm_gemv_kernel(SkinnyBatch bt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int p = 0;
+  while (p + 1 < bt.n && (int)blockIdx.x >= bt.block_end[p]) ++p;
+  const GemmArgs& g = bt.g[p];
+  const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+  const int n0 = ((int)blockIdx.x - (p ? bt.block_end[p - 1] : 0)) * GV_COLS + wave * GV_WCOLS;
+  float acc[GV_MAXM][GV_WCOLS];
+#pragma unroll
+  for (int m = 0; m < GV_MAXM; ++m)
+#pragma unroll
+    for (int c = 0; c < GV_WCOLS; ++c) acc[m][c] = 0.f;
+  const uint16_t* wrow[GV_WCOLS];
+#pragma unroll
+  for (int c = 0; c < GV_WCOLS; ++c)
+    wrow[c] = (const uint16_t*)weight_row(g.w, n0 + c < N ? n0 + c : N - 1, 2);
+  const uint16_t* arow[GV_MAXM];
+#pragma unroll
+  for (int m = 0; m < GV_MAXM; ++m) arow[m] = gather_row32(g.a, m < M ? m : M - 1);
+  // two 8-element pieces per lane in flight at a time (K = 1024 in one round trip)
+  for (int k0 = 8 * lane; k0 < K; k0 += 2 * 8 * 64) {
+    uint4 wv[2][GV_WCOLS], av[2][GV_MAXM];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + h * 8 * 64;
+      if (k >= K) continue;
+#pragma unroll
+      for (int c = 0; c < GV_WCOLS; ++c) wv[h][c] = *(const uint4*)(wrow[c] + k);
+#pragma unroll
+      for (int m = 0; m < GV_MAXM; ++m)
+        if (m < M) av[h][m] = *(const uint4*)(arow[m] + k);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (k0 + h * 8 * 64 >= K) continue;
+#pragma unroll
+      for (int m = 0; m < GV_MAXM; ++m) {
+        if (m >= M) continue;
+        const uint32_t aw[4] = {av[h][m].x, av[h][m].y, av[h][m].z, av[h][m].w};
+#pragma unroll
+        for (int c = 0; c < GV_WCOLS; ++c) {
+          const uint32_t ww[4] = {wv[h][c].x, wv[h][c].y, wv[h][c].z, wv[h][c].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[m][c] += __builtin_bit_cast(float, aw[e] << 16) *
+                         __builtin_bit_cast(float, ww[e] << 16);
+            acc[m][c] += __builtin_bit_cast(float, aw[e] & 0xffff0000u) *
+                         __builtin_bit_cast(float, ww[e] & 0xffff0000u);
+          }
+        }
+      }
+    }
+  }
+  // sums across the wave's 64 lanes
+#pragma unroll
+  for (int m = 0; m < GV_MAXM; ++m)
+#pragma unroll
+    for (int c = 0; c < GV_WCOLS; ++c) {
+      float v = acc[m][c];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+      acc[m][c] = v;
+    }
+  if (lane < GV_MAXM * GV_WCOLS) {
+    const int m = lane / GV_WCOLS, c = lane % GV_WCOLS;
+    float v = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < GV_MAXM; ++mm)
+#pragma unroll
+      for (int cc = 0; cc < GV_WCOLS; ++cc) v = (mm == m && cc == c) ? acc[mm][cc] : v;
+    if (m < M && n0 + c < N) epilogue_store<uint16_t>(g, m, n0 + c, v);
+  }
+}
+
+bool gemv_ok(const GemmArgs& g) {
+  return g.M <= GV_MAXM && g.K % 8 == 0 && wide_rows(g);
+}
+
+hipError_t launch_gemv(const GemmArgs* gs, int n, hipStream_t s) {
+  SkinnyBatch bt{};
+  int64_t total = 0;
+  for (int p = 0; p < n; ++p) {
+    bt.g[p] = gs[p];
+    total += (gs[p].N + GV_COLS - 1) / GV_COLS;
+    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+    bt.block_end[p] = (int)total;
+  }
+  bt.n = n;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_gemv_kernel, dim3((unsigned)total), dim3(64 * GV_WAVES), 0, s, bt);
+  return hipGetLastError();
+}
+
 bool skinny_ok(const GemmArgs& g) {
   return g.M <= 32 && g.K % (16 * SK_NW) == 0 && wide_rows(g);
 }
@@ -953,8 +1058,12 @@ bool gemm_mfma_supported(const GemmArgs& g) {
 
 hipError_t launch_gemm_mfma_multi(const GemmArgs* gs, int n, hipStream_t s, int num_cus) {
   if (n < 1 || n > MAXP) return hipErrorInvalidValue;
-  bool skinny = true;
-  for (int p = 0; p < n; ++p) skinny = skinny && skinny_ok(gs[p]);
+  bool gemv = true, skinny = true;
+  for (int p = 0; p < n; ++p) {
+    gemv = gemv && gemv_ok(gs[p]);
+    skinny = skinny && skinny_ok(gs[p]);
+  }
+  if (gemv && TXL_GEMV) return launch_gemv(gs, n, s);
   if (skinny) return launch_skinny(gs, n, s);
   // 256 x 256 tiles when they give most CUs a workgroup, else 128 x 128
   int64_t big = 0;

@@ -75,11 +75,16 @@ def test_kv_stream_matches_oracle(name, over, segments, extra):
     _stream_case(w, segments, extra)
 
 
-def test_kv_decode_one_token_at_a_time():
+@pytest.mark.parametrize("over,segments", [
+    ({"B": 2, "L": 1, "M": 100, "D": 128, "H": 2, "d": 64, "R_rows": 101}, 12),
+    # the long-memory evaluation model's width: matrix-vector products over K = 1024
+    ({"B": 1, "L": 1, "M": 300, "D": 1024, "H": 16, "d": 64, "R_rows": 301}, 6),
+])
+def test_kv_decode_one_token_at_a_time(over, segments):
     """L = 1: a memory of up to M tokens, one new token per step."""
-    w = I.workload("charlm", B=2, L=1, M=100, D=128, H=2, d=64, R_rows=101)
+    w = I.workload("charlm", **over)
     _say(f"kv decode {w}")
-    _stream_case(w, segments=12, capacity_extra=5, seed=4)
+    _stream_case(w, segments=segments, capacity_extra=5, seed=4)
 
 
 @pytest.mark.parametrize("dtype,over", [

@@ -35,7 +35,10 @@ def _ff_weights(rng, D, Di, dtype):
     ("bf16", 300, 512, 2048),   # matrix cores, fused second layer + LayerNorm
     ("bf16", 77, 96, 200),      # ragged rows, unfused LayerNorm (D % 64 != 0)
     ("bf16", 100, 1024, 4096),  # D > 512: unfused LayerNorm
-    ("bf16", 3, 512, 2048),     # a decode step's rows: skinny GEMMs
+    ("bf16", 3, 512, 2048),     # a decode step's rows: matrix-vector products
+    ("bf16", 1, 1024, 4096),    # one token of the long-memory evaluation shape
+    ("bf16", 4, 136, 200),      # 4 rows, column counts that end mid-workgroup
+    ("bf16", 5, 512, 2048),     # 5 rows: the skinny matrix-core path
 ])
 def test_pos_ff_matches_oracle(dtype, rows, D, Di):
     from relative_position_memory_amd import txl
