@@ -703,89 +703,124 @@ __global__ __launch_bounds__(64 * SK_NW) void gemm_skinny_kernel(SkinnyBatch bt)
 
 // ---- matrix-vector products: at most 4 rows (one-token decode steps) -----------------
 // C = A W^T with M <= 4: the products are weight-streaming, so the weights are
-// read once with 16-byte coalesced loads and summed on the vector ALU.  A
-// workgroup of 4 waves covers GV_COLS consecutive output columns; each wave
-// takes GV_WCOLS of them (weight rows n), its 64 lanes reading consecutive
-// 8-element pieces of each row (K % 8 == 0), then reduces each (row m, column
-// n) sum across the lanes.  The usual element epilogue stores the results.
-constexpr int GV_WAVES = 4, GV_WCOLS = 4, GV_COLS = GV_WAVES * GV_WCOLS, GV_MAXM = 4;
+// read once with 16-byte coalesced loads and summed on the vector ALU.  Each
+// wave computes one output column n (weight row n): its 64 lanes read
+// consecutive 8-element pieces of the row (K % 8 == 0), two pieces each in
+// flight (K = 1024 in one round trip), and multiply them with the matching
+// pieces of the MM rows of A by bf16 pair dot products (v_dot2, fp32
+// accumulation); the MM sums are then reduced across the lanes.  The wave's
+// column is uniform, so its weight row is found on the scalar unit; index
+// arithmetic is 32-bit (gemv_ok bounds the sizes).
+constexpr int GV_WAVES = 4, GV_COLS = GV_WAVES, GV_MAXM = 4;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Weight row of output column n (see WeightPair), 32-bit.
+__device__ inline const uint16_t* weight_row32(const WeightPair& w, int n) {
+  const bool second = n >= (int)w.n_split;
+  if (second) n -= (int)w.n_split;
+  const int hp = (int)w.hd_pad, hi = (int)w.hd_in;
+  if (hp > hi && hi > 0) {
+    const int head = n / hp, c = n - head * hp;
+    n = head * hi + (c < hi ? c : hi - 1);
+  }
+  return (const uint16_t*)(second ? w.W1 : w.W0) + (int64_t)n * w.ldw;
+}
+
+// epilogue_store with 32-bit index arithmetic (bf16 inputs).
+__device__ inline void gemv_store(const GemmArgs& g, int m, int n, float acc) {
+  const Epilogue& e = g.e;
+  acc = epi_value<uint16_t>(e, n, acc);
+  if (e.mode != EPI_HEADS) {
+    const int64_t i = (int64_t)m * g.N + n;
+    e.y[i] = acc + Elt<uint16_t>::load((const uint16_t*)e.resid + i);
+    return;
+  }
+  const int per = (int)(g.a.mem_len + g.a.cur_rows), HD = (int)e.HD, d = (int)e.d;
+  const int b = m / per, t = m - b * per;
+  const int which = n / HD, nn = n - which * HD;
+  const int head = nn / d, c = nn - head * d;
+  int tr = t;
+  if (e.t_mod > 0) {
+    tr = (int)e.t_off + t;
+    tr = tr >= (int)e.t_mod ? tr - (int)e.t_mod : tr;
+  }
+  uint16_t* p = (uint16_t*)(which ? e.dst1 : e.dst0) + b * e.sb + head * e.sh + tr * e.st + c;
+  if (e.d_valid > 0 && c >= (int)e.d_valid) acc = 0.f;
+  Elt<uint16_t>::store(p, acc);
+  if (e.pad > e.d && c == d - 1) {
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+      if (i <= (int)(e.pad - e.d)) Elt<uint16_t>::store(p + i, 0.f);
+  }
+}
+
+template <int MM>
 __global__ __launch_bounds__(64 * GV_WAVES) void gemm_gemv_kernel(SkinnyBatch bt) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int p = 0;
   while (p + 1 < bt.n && (int)blockIdx.x >= bt.block_end[p]) ++p;
+  p = __builtin_amdgcn_readfirstlane(p);
   const GemmArgs& g = bt.g[p];
-  const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
-  const int n0 = ((int)blockIdx.x - (p ? bt.block_end[p - 1] : 0)) * GV_COLS + wave * GV_WCOLS;
-  float acc[GV_MAXM][GV_WCOLS];
+  const int N = (int)g.N, K = (int)g.K;
+  const int n = ((int)blockIdx.x - (p ? bt.block_end[p - 1] : 0)) * GV_COLS + wave;
+  const uint16_t* wrow = weight_row32(g.w, n < N ? n : N - 1);
+  const uint16_t* arow[MM];
 #pragma unroll
-  for (int m = 0; m < GV_MAXM; ++m)
+  for (int m = 0; m < MM; ++m) arow[m] = gather_row32(g.a, m);
+  float acc[MM];
 #pragma unroll
-    for (int c = 0; c < GV_WCOLS; ++c) acc[m][c] = 0.f;
-  const uint16_t* wrow[GV_WCOLS];
-#pragma unroll
-  for (int c = 0; c < GV_WCOLS; ++c)
-    wrow[c] = (const uint16_t*)weight_row(g.w, n0 + c < N ? n0 + c : N - 1, 2);
-  const uint16_t* arow[GV_MAXM];
-#pragma unroll
-  for (int m = 0; m < GV_MAXM; ++m) arow[m] = gather_row32(g.a, m < M ? m : M - 1);
-  // two 8-element pieces per lane in flight at a time (K = 1024 in one round trip)
+  for (int m = 0; m < MM; ++m) acc[m] = 0.f;
+  // a second piece past K is read at the first one's k, with A zeroed
   for (int k0 = 8 * lane; k0 < K; k0 += 2 * 8 * 64) {
-    uint4 wv[2][GV_WCOLS], av[2][GV_MAXM];
+    const bool has1 = k0 + 8 * 64 < K;
+    const int k1 = has1 ? k0 + 8 * 64 : k0;
+    const uint4 w0 = *(const uint4*)(wrow + k0), w1 = *(const uint4*)(wrow + k1);
+    uint4 a0[MM], a1[MM];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = k0 + h * 8 * 64;
-      if (k >= K) continue;
-#pragma unroll
-      for (int c = 0; c < GV_WCOLS; ++c) wv[h][c] = *(const uint4*)(wrow[c] + k);
-#pragma unroll
-      for (int m = 0; m < GV_MAXM; ++m)
-        if (m < M) av[h][m] = *(const uint4*)(arow[m] + k);
+    for (int m = 0; m < MM; ++m) {
+      a0[m] = *(const uint4*)(arow[m] + k0);
+      const uint4 x = *(const uint4*)(arow[m] + k1);
+      a1[m] = has1 ? x : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (k0 + h * 8 * 64 >= K) continue;
-#pragma unroll
-      for (int m = 0; m < GV_MAXM; ++m) {
-        if (m >= M) continue;
-        const uint32_t aw[4] = {av[h][m].x, av[h][m].y, av[h][m].z, av[h][m].w};
-#pragma unroll
-        for (int c = 0; c < GV_WCOLS; ++c) {
-          const uint32_t ww[4] = {wv[h][c].x, wv[h][c].y, wv[h][c].z, wv[h][c].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[m][c] += __builtin_bit_cast(float, aw[e] << 16) *
-                         __builtin_bit_cast(float, ww[e] << 16);
-            acc[m][c] += __builtin_bit_cast(float, aw[e] & 0xffff0000u) *
-                         __builtin_bit_cast(float, ww[e] & 0xffff0000u);
-          }
-        }
-      }
+    for (int m = 0; m < MM; ++m) {
+      float t = acc[m];
+      t = dot2_bf16(a0[m].x, w0.x, t);
+      t = dot2_bf16(a0[m].y, w0.y, t);
+      t = dot2_bf16(a0[m].z, w0.z, t);
+      t = dot2_bf16(a0[m].w, w0.w, t);
+      t = dot2_bf16(a1[m].x, w1.x, t);
+      t = dot2_bf16(a1[m].y, w1.y, t);
+      t = dot2_bf16(a1[m].z, w1.z, t);
+      t = dot2_bf16(a1[m].w, w1.w, t);
+      acc[m] = t;
     }
   }
   // sums across the wave's 64 lanes
 #pragma unroll
-  for (int m = 0; m < GV_MAXM; ++m)
+  for (int m = 0; m < MM; ++m) acc[m] = wave_allsum(acc[m]);
+  if (lane < MM && n < N) {
+    float v = acc[0];
 #pragma unroll
-    for (int c = 0; c < GV_WCOLS; ++c) {
-      float v = acc[m][c];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      acc[m][c] = v;
-    }
-  if (lane < GV_MAXM * GV_WCOLS) {
-    const int m = lane / GV_WCOLS, c = lane % GV_WCOLS;
-    float v = 0.f;
-#pragma unroll
-    for (int mm = 0; mm < GV_MAXM; ++mm)
-#pragma unroll
-      for (int cc = 0; cc < GV_WCOLS; ++cc) v = (mm == m && cc == c) ? acc[mm][cc] : v;
-    if (m < M && n0 + c < N) epilogue_store<uint16_t>(g, m, n0 + c, v);
+    for (int m = 1; m < MM; ++m) v = lane == m ? acc[m] : v;
+    gemv_store(g, lane, n, v);
   }
 }
 
+// Sizes the 32-bit index arithmetic of the matrix-vector kernel covers.
 bool gemv_ok(const GemmArgs& g) {
-  return g.M <= GV_MAXM && g.K % 8 == 0 && wide_rows(g);
+  const int64_t lim = 0x7fffffffLL;
+  if (g.M > GV_MAXM || g.K % 8 != 0 || !wide_rows(g)) return false;
+  if (g.N > lim || g.K > lim || g.w.n_split > lim || g.a.mem_len + g.a.cur_rows > lim) return false;
+  if (g.e.mode == EPI_HEADS && (g.e.HD > lim || g.e.d > lim || g.e.t_mod > lim)) return false;
+  if (g.a.mem_cap > lim) return false;
+  return true;
 }
 
 hipError_t launch_gemv(const GemmArgs* gs, int n, hipStream_t s) {
@@ -799,7 +834,19 @@ hipError_t launch_gemv(const GemmArgs* gs, int n, hipStream_t s) {
   }
   bt.n = n;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_gemv_kernel, dim3((unsigned)total), dim3(64 * GV_WAVES), 0, s, bt);
+  int M = 0;
+  for (int p = 0; p < n; ++p) M = gs[p].M > M ? (int)gs[p].M : M;
+  for (int p = 0; p < n; ++p)
+    if (gs[p].M != M) return hipErrorInvalidValue;  // one row count per launch
+  if (M == 0) return hipSuccess;
+  const dim3 grid((unsigned)total), block(64 * GV_WAVES);
+  switch (M) {
+    case 1: hipLaunchKernelGGL(gemm_gemv_kernel<1>, grid, block, 0, s, bt); break;
+    case 2: hipLaunchKernelGGL(gemm_gemv_kernel<2>, grid, block, 0, s, bt); break;
+    case 3: hipLaunchKernelGGL(gemm_gemv_kernel<3>, grid, block, 0, s, bt); break;
+    case 4: hipLaunchKernelGGL(gemm_gemv_kernel<4>, grid, block, 0, s, bt); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1060,7 +1107,7 @@ hipError_t launch_gemm_mfma_multi(const GemmArgs* gs, int n, hipStream_t s, int 
   if (n < 1 || n > MAXP) return hipErrorInvalidValue;
   bool gemv = true, skinny = true;
   for (int p = 0; p < n; ++p) {
-    gemv = gemv && gemv_ok(gs[p]);
+    gemv = gemv && gemv_ok(gs[p]) && gs[p].M == gs[0].M;
     skinny = skinny && skinny_ok(gs[p]);
   }
   if (gemv && TXL_GEMV) return launch_gemv(gs, n, s);

@@ -48,8 +48,27 @@ __global__ __launch_bounds__(256) void layer_norm_kernel(const float* __restrict
     Elt<T>::store(o + c, (x[c] - mean) * inv * Elt<T>::load(gamma + c) + Elt<T>::load(beta + c));
 }
 
+// Four consecutive elements as floats / from floats (16-byte aligned fp32,
+// 8-byte aligned bf16).
+__device__ inline float4 load4(const float* p) { return *(const float4*)p; }
+__device__ inline float4 load4(const uint16_t* p) {
+  const uint2 w = *(const uint2*)p;
+  return make_float4(__builtin_bit_cast(float, w.x << 16),
+                     __builtin_bit_cast(float, w.x & 0xffff0000u),
+                     __builtin_bit_cast(float, w.y << 16),
+                     __builtin_bit_cast(float, w.y & 0xffff0000u));
+}
+__device__ inline void store4(float* p, float4 v) { *(float4*)p = v; }
+__device__ inline void store4(uint16_t* p, float4 v) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+  *(uint2*)p = make_uint2(lo, hi);
+}
+
 // The same LayerNorm for D = 256 NV (NV <= 8) with aligned rows: each lane keeps
-// NV float4 chunks of its row in registers (chunk lane + 64 k), one pass over y.
+// NV 4-element chunks (chunk lane + 64 k) of its row, and of gamma and beta, in
+// registers; every load is issued before the two reductions, so one memory
+// round trip serves the row.
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* __restrict__ y,
                                                              const T* __restrict__ gamma,
@@ -60,14 +79,18 @@ __global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* __rest
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const float4* x = (const float4*)(y + row * D);
-  float4 v[NV];
-  float s = 0.f;
+  const float* x = y + row * D;
+  float4 v[NV], ga[NV], be[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    v[k] = x[lane + 64 * k];
-    s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+    const int c = 4 * (lane + 64 * k);
+    v[k] = load4(x + c);
+    ga[k] = load4(gamma + c);
+    be[k] = load4(beta + c);
   }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
   const float mean = wave_sum(s) / (float)D;
   float q = 0.f;
 #pragma unroll
@@ -79,11 +102,9 @@ __global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* __rest
   T* o = out + row * D;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int c = 4 * (lane + 64 * k);
-    const float r[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      Elt<T>::store(o + c + e, r[e] * inv * Elt<T>::load(gamma + c + e) + Elt<T>::load(beta + c + e));
+    const float4 r = make_float4(v[k].x * inv * ga[k].x + be[k].x, v[k].y * inv * ga[k].y + be[k].y,
+                                 v[k].z * inv * ga[k].z + be[k].z, v[k].w * inv * ga[k].w + be[k].w);
+    store4(o + 4 * (lane + 64 * k), r);
   }
 }
 
@@ -113,7 +134,8 @@ hipError_t launch_layer_norm(int dtype, const float* y, const void* gamma, const
                              float eps, int64_t rows, int64_t D, void* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (D % 256 == 0 && D <= 2048 && ((uintptr_t)y % 16) == 0) {
+  const uintptr_t al = (uintptr_t)gamma | (uintptr_t)beta | (uintptr_t)out;
+  if (D % 256 == 0 && D <= 2048 && ((uintptr_t)y % 16) == 0 && al % (dtype == 0 ? 16 : 8) == 0) {
 #define TXL_LN_VEC(NV)                                                                        \
   if (D == 256 * NV) {                                                                        \
     if (dtype == 0)                                                                           \

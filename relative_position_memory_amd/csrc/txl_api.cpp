@@ -138,9 +138,14 @@ int check_attn(int dtype, const txl::AttnArgs& a, int64_t r_rows) {
   return TXL_OK;
 }
 
-// Bytes of key-split partials the matrix-core attention's plan needs (0 = none).
+// Bytes of key-split partials the attention's plan needs (0 = none): the
+// single-query kernel's parts for one query per (batch, head), else the
+// matrix-core plan's.
 size_t attn_plan_bytes(int dtype, const txl::AttnArgs& a) {
-  if (dtype != TXL_BF16 || !txl::attn_mfma_supported(a)) return 0;
+  if (dtype != TXL_BF16) return 0;
+  if (txl::attn_decode_supported(a))
+    return txl::attn_decode_bytes(a, txl::attn_decode_parts(a, num_cus(), (size_t)-1));
+  if (!txl::attn_mfma_supported(a)) return 0;
   return txl::attn_plan_bytes(a, txl::attn_mfma_plan(a, num_cus(), (size_t)-1));
 }
 
@@ -166,7 +171,12 @@ int run_attn(int dtype, txl::AttnArgs a, void* scratch, size_t scratch_bytes, hi
     e = txl::launch_fill_f32(a.scores, a.B * a.H * a.L * T, -INFINITY, st);
     if (e != hipSuccess) return hip_fail(e, "scores fill");
   }
-  if (dtype == TXL_BF16 && txl::attn_mfma_supported(a)) {
+  const int dec_parts = dtype == TXL_BF16 && txl::attn_decode_supported(a)
+                            ? txl::attn_decode_parts(a, num_cus(), scratch ? scratch_bytes : 0)
+                            : 0;
+  if (dec_parts > 0) {
+    e = txl::launch_attn_decode(a, dec_parts, scratch, st);
+  } else if (dtype == TXL_BF16 && txl::attn_mfma_supported(a)) {
     // the best plan whose partials fit the scratch (none: no split)
     const txl::AttnPlan plan = txl::attn_mfma_plan(a, num_cus(), scratch ? scratch_bytes : 0);
     txl::attn_plan_bind(a, plan, scratch);

@@ -21,6 +21,36 @@ __host__ __device__ inline uint16_t f32_to_bf16(float f) {
   return (uint16_t)((x.u + bias) >> 16);
 }
 
+// ---- wave reductions ---------------------------------------------------------------
+// Sum / maximum over the 64 lanes of a wave with DPP row operations (swap within
+// pairs and quads, mirror within half-rows and rows of 16, then broadcast lane 15
+// of a row into the next row and lane 31 into the upper half), the total read
+// from lane 63 into every lane.  Every lane of the wave must be active.
+template <int CTRL, int ROWS>
+__device__ inline float dpp_f32(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROWS, 0xf, false));
+}
+__device__ inline float wave_allsum(float v) {
+  v += dpp_f32<0xB1, 0xf>(0.f, v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E, 0xf>(0.f, v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141, 0xf>(0.f, v);  // row_half_mirror
+  v += dpp_f32<0x140, 0xf>(0.f, v);  // row_mirror
+  v += dpp_f32<0x142, 0xa>(0.f, v);  // row_bcast:15 into rows 1, 3
+  v += dpp_f32<0x143, 0xc>(0.f, v);  // row_bcast:31 into rows 2, 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ inline float wave_allmax(float v) {
+  v = fmaxf(v, dpp_f32<0xB1, 0xf>(v, v));
+  v = fmaxf(v, dpp_f32<0x4E, 0xf>(v, v));
+  v = fmaxf(v, dpp_f32<0x141, 0xf>(v, v));
+  v = fmaxf(v, dpp_f32<0x140, 0xf>(v, v));
+  v = fmaxf(v, dpp_f32<0x142, 0xa>(v, v));
+  v = fmaxf(v, dpp_f32<0x143, 0xc>(v, v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 template <typename T> struct Elt;
 template <> struct Elt<float> {
   __device__ static inline float load(const float* p) { return *p; }
@@ -165,6 +195,15 @@ hipError_t launch_attn_generic(int dtype, const AttnArgs& a, hipStream_t s);
 // bf16 matrix-core path: d <= 64, 16-byte aligned q/k/v/r, strides multiple of 8.
 hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s);
 bool attn_mfma_supported(const AttnArgs& a);
+// One query per (batch, head) (L == 1, no scores or lse output), bf16, d <= 64,
+// 16-byte aligned k/v/r with strides a multiple of 8: keys split into parts, one
+// workgroup each.  attn_decode_parts gives the parts for a device with num_cus
+// CUs whose partials fit scratch_bytes (0: none fits, take another path);
+// attn_decode_bytes the scratch they need (0 for one part).
+bool attn_decode_supported(const AttnArgs& a);
+int attn_decode_parts(const AttnArgs& a, int num_cus, size_t scratch_bytes);
+size_t attn_decode_bytes(const AttnArgs& a, int nparts);
+hipError_t launch_attn_decode(const AttnArgs& a, int nparts, void* scratch, hipStream_t s);
 
 // ---- GEMM: C[m][n] = sum_k A[m][k] * W[n][k] ---------------------------------------
 // Row m of A is gathered: with rows_per_batch = mem_len + cur_rows,

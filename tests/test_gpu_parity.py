@@ -347,3 +347,40 @@ def test_layer_intermediates_bf16(over, mem_len, start):
         err = max_err(got, want)
         assert err <= TOL["bf16"] and err <= 1e-2 * np.abs(want).max(), (name, err)
     assert max_err(host(out), ref_out) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,H,M,d,layout,ws_div", [
+    (1, 2, 0, 64, "bhtd", 1),       # one key: the query itself
+    (1, 2, 300, 64, "bhtd", 0),     # one part, no workspace
+    (1, 16, 3799, 64, "bhtd", 1),   # one token over the long evaluation memory
+    (2, 3, 1000, 48, "bthd", 1),    # token-major rows, d 48
+    (1, 1, 5000, 64, "bhtd", 1),    # many parts per (batch, head)
+    (1, 2, 2000, 64, "bhtd", 3),    # a third of the workspace: fewer parts
+    (1, 2, 2000, 64, "bhtd", 0),    # keys beyond one part, no workspace: matrix-core path
+    (3, 2, 511, 32, "bthd", 1),     # T = 512, d 32
+])
+def test_attn_single_query(B, H, M, d, layout, ws_div):
+    """One query per (batch, head) without a scores output (the decode step):
+    the keys are split into parts whose (max, sum, output) partials are merged."""
+    txl = _txl()
+    L = 1
+    c = I.attention_inputs(B, H, L, M, d, seed=11 * M + H, sigma=1.0, sigma_uv=0.5, dtype="bf16")
+    if layout == "bthd":
+        q, k, v, r = (dev(c[n], "bf16") for n in ("q", "k", "v", "r"))
+    else:
+        hm = lambda x: dev(x.transpose(0, 2, 1, 3), "bf16").permute(0, 2, 1, 3)
+        q, k, v = hm(c["q"]), hm(c["k"]), hm(c["v"])
+        r = dev(c["r"].transpose(1, 0, 2), "bf16").permute(1, 0, 2)
+    ws = None
+    nbytes = txl.rel_attn_workspace_bytes(torch.bfloat16, B, H, L, M, d)
+    if ws_div:
+        assert M < 64 or nbytes > 0, "this shape should split its keys"
+        ws = torch.empty(max(nbytes // ws_div, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device="cuda")
+    _say(f"single query B={B} H={H} M={M} d={d} {layout} workspace="
+         f"{None if ws is None else ws.numel()} of {nbytes}")
+    txl.rel_attn_fwd(q, k, v, r, dev(c["u"], "bf16"), dev(c["vb"], "bf16"), M, out, workspace=ws)
+    torch.cuda.synchronize()
+    ref = O.rel_attn(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], M)
+    ref = ref[0] if isinstance(ref, tuple) else ref
+    assert max_err(host(out), ref) <= TOL["bf16"]
