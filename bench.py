@@ -61,6 +61,11 @@ def parse():
                         "so that a counter run can calibrate FETCH_SIZE / WRITE_SIZE")
     p.add_argument("--no-drift", action="store_true",
                    help="skip the deep-stack bf16 drift report (batch row 0 against the oracle)")
+    p.add_argument("--traffic-summary", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                   help="print the attention's HBM traffic summary from two rocprofv3 --pmc "
+                        "runs (FETCH_SIZE, WRITE_SIZE) of bench.py --calib-copy")
+    p.add_argument("--trace-summary", metavar="STATS_CSV",
+                   help="print the per-kernel table of a rocprofv3 --kernel-trace --stats run")
     p.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                    help="no GPU work: summarise rocprofv3 --pmc counter CSVs (per kernel: "
                         "MFMA busy fraction, bf16 MFMA FLOPs, HBM bytes) and exit")
@@ -683,10 +688,114 @@ def pmc_summary(paths):
         print(f"{name[:58]:58s} {grid:>9s} {n:4d}  " + "  ".join(parts))
 
 
+def _pmc_per_dispatch(path, counter):
+    """{(kernel name, grid size): [counter value per dispatch]} of a --pmc CSV."""
+    import collections
+    import csv
+    out = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            out[(r["Kernel_Name"], r["Grid_Size"])].append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(workload, fetch_csv, write_csv):
+    """HBM bytes per attention launch (attn_mfma_kernel, plus attn_part_merge_kernel
+    when the plan splits keys) from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the 256 MiB device copy that
+    --calib-copy adds to the run."""
+    fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    copy_kib = float(64 << 20) * 4 / 1024
+    mean = lambda v: sum(v) / len(v)
+
+    def calib(tab):
+        for (name, grid), v in tab.items():
+            if "copyBuffer" in name and int(grid) * 2048 == 64 << 22:  # 256 MiB / 2 KiB per item
+                return mean(v)
+        cand = [mean(v) for (name, _), v in tab.items() if "copyBuffer" in name]
+        return max(cand)
+    cf, cw = calib(fetch), calib(write)
+    fs, wsc = copy_kib / cf, copy_kib / cw
+
+    def kern(tab, key):
+        hits = [(n, g, v) for (n, g), v in tab.items() if key in n]
+        if not hits:
+            return 0, 0.0
+        n, g, v = max(hits, key=lambda t: len(t[2]))
+        return len(v), mean(v)
+    na_f, af = kern(fetch, "attn_mfma_kernel")
+    na_w, aw = kern(write, "attn_mfma_kernel")
+    nm_f, mf = kern(fetch, "attn_part_merge_kernel")
+    nm_w, mw = kern(write, "attn_part_merge_kernel")
+    hbm = (af * fs + aw * wsc + mf * fs + mw * wsc) * 1024
+    from relative_position_memory_amd import inputs as I
+    w = I.workload(workload)
+    src = os.path.relpath(ATTN_SRC, ROOT)
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    R = "$R"
+    cmd = (f"python3 {R}/bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline "
+           f"--main-only --attn-reps 3 --calib-copy")
+    lines = [
+        f"# HBM traffic of the attention ({w.name}: B {w.B}, H {w.H}, d {w.d}, L {w.L}, "
+        f"M {w.M}, {w.dtype}) per launch",
+        "# counter pass 1 (run from /tmp with TMPDIR=/tmp, repo root $R):",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/pmc_fetch_{workload} "
+        f"-o run -- {cmd}",
+        "# counter pass 2:",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/pmc_write_{workload} "
+        f"-o run -- {cmd}",
+        "# summary: python3 bench.py --traffic-summary " + workload +
+        f" gpurun_out/pmc_fetch_{workload}/run_counter_collection.csv"
+        f" gpurun_out/pmc_write_{workload}/run_counter_collection.csv",
+        "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch.  Calibration: a plain device copy of",
+        "# 256 MiB (reads 262144 KiB, writes 262144 KiB) in the same runs.",
+        f"copy_fetch_kib: {cf:.1f}",
+        f"copy_write_kib: {cw:.1f}",
+        f"fetch_scale: {fs:.4f}",
+        f"write_scale: {wsc:.4f}",
+        f"attn_dispatches: {na_f} (fetch run), {na_w} (write run)",
+        f"attn_fetch_kib_raw: {af:.1f}",
+        f"attn_write_kib_raw: {aw:.1f}",
+        f"merge_dispatches: {nm_f} (fetch run), {nm_w} (write run)",
+        f"merge_fetch_kib_raw: {mf:.1f}",
+        f"merge_write_kib_raw: {mw:.1f}",
+        f"hbm_bytes_per_dispatch: {hbm:.0f}",
+        f"algorithmic_bytes_per_dispatch: {attn_bytes(w)}  # q, out, k, v, r once each",
+        f"traffic_over_algorithmic: {hbm / attn_bytes(w):.3f}",
+        f"kernel_source: {src}",
+        f"kernel_source_sha256: {sha}",
+        "# other kernels of the same runs (scaled KiB per dispatch: fetch, write)",
+    ]
+    for (name, grid), v in sorted(fetch.items(), key=lambda kv: -mean(kv[1]))[:10]:
+        wv = write.get((name, grid))
+        lines.append(f"#   {name[:60]:60s} grid {grid:>9s}: {mean(v) * fs:12.1f} "
+                     f"{(mean(wv) * wsc if wv else float('nan')):12.1f}")
+    print("\n".join(lines), flush=True)
+
+
+def trace_summary(path, top=14):
+    """Per-kernel table of rocprofv3's kernel stats CSV: calls, mean, min, max, share."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    print(f"{'kernel':78s} {'calls':>6s} {'mean_us':>9s} {'min_us':>8s} {'max_us':>8s} "
+          f"{'share':>6s}")
+    for r in rows[:top]:
+        print(f"{r['Name'][:78]:78s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+              f"{float(r['MinNs']) / 1e3:8.2f} {float(r['MaxNs']) / 1e3:8.2f} "
+              f"{float(r['Percentage']):5.1f}%")
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -589,85 +589,96 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   }
 }
 
-// Merge of the parts of a split query tile: one workgroup per (query tile,
-// group) whose 256 threads take the writing lanes' places (wave w, lane (g4,
-// n16) holds query 32 w + 16 gm + n16, columns 16 db + 4 g4 .. + 3), so every
-// load covers whole lines:
+// Merge of the parts of a split query tile: one wave per (query tile, group,
+// 16-query block wq = 2 w + gm), whose lanes take the writing lanes' places
+// (lane (g4, n16) of writing wave w holds query 32 w + 16 gm + n16, columns
+// 16 db + 4 g4 .. + 3), so every load covers whole lines:
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// The references and sums of all parts and the outputs of the first 8 parts
+// are loaded at once (one round trip for up to 8 parts, two for up to 16).
 // The part that holds key 0 has a finite reference for every query.
-__global__ __launch_bounds__(256) void attn_part_merge_kernel(AttnArgs a) {
-  const int qt = blockIdx.x, g = blockIdx.y;
+__global__ __launch_bounds__(64) void attn_part_merge_kernel(AttnArgs a) {
+  const int qt = blockIdx.x >> 3, wq = blockIdx.x & 7, g = blockIdx.y;
   const int np = a.plan.nparts[qt];
   if (np <= 1) return;
+  const int wave = wq >> 1, gm = wq & 1;
   const int64_t groups = a.B * a.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int g4 = lane >> 4, n16 = lane & 15;
   const int d = (int)a.d, L = (int)a.L;
   const int64_t b = g / a.H, hd = g % a.H;
   const int64_t blk0 = (int64_t)a.plan.slot0[qt] * groups + g;
-#pragma unroll 1
-  for (int gm = 0; gm < 2; ++gm) {
-    const int i = qt * BQ + wave * BQW + 16 * gm + n16;
-    if (i >= L) continue;
-    const int moff = ((wave * 2 + gm) * 16 + n16) * 2;
-    // references and sums of every part (at most 16), one round trip
-    float2 ml[16];
+  const int i = qt * BQ + wave * BQW + 16 * gm + n16;
+  if (qt * BQ + wave * BQW + 16 * gm >= L) return;  // no query of this block
+  const int moff = (wq * 16 + n16) * 2;
+  auto acc_ptr = [&](int p) {
+    return a.part_acc + (blk0 + (int64_t)p * groups) * (BQ * DP) + (wq * 4 * 2 * 64 + lane) * 2;
+  };
+  float2 ml[16];
 #pragma unroll
-    for (int p = 0; p < 16; ++p)
-      ml[p] = p < np ? *(const float2*)(a.part_ml + (blk0 + p * groups) * (BQ * 2) + moff)
-                     : make_float2(-INFINITY, 0.f);
-    float M = -INFINITY;
+  for (int p = 0; p < 16; ++p)
+    ml[p] = p < np ? *(const float2*)(a.part_ml + (blk0 + p * groups) * (BQ * 2) + moff)
+                   : make_float2(-INFINITY, 0.f);
+  float2 av[8][4][2];
 #pragma unroll
-    for (int p = 0; p < 16; ++p) M = fmaxf(M, ml[p].x);
-    float wgt[16], den = 0.f;
+  for (int j = 0; j < 8; ++j) {
+    const float* pa = acc_ptr(j < np ? j : 0);
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      wgt[p] = p < np ? __builtin_amdgcn_exp2f(ml[p].x - M) : 0.f;
-      den += wgt[p] * ml[p].y;
-    }
-    float o[4][4] = {};
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int p0 = 0; p0 < 16; p0 += 8) {
+      for (int pr = 0; pr < 2; ++pr) av[j][db][pr] = *(const float2*)(pa + (db * 2 + pr) * 128);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) M = fmaxf(M, ml[p].x);
+  float wgt[16], den = 0.f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    wgt[p] = p < np ? __builtin_amdgcn_exp2f(ml[p].x - M) : 0.f;
+    den += wgt[p] * ml[p].y;
+  }
+  float o[4][4] = {};
+#pragma unroll
+  for (int p0 = 0; p0 < 16; p0 += 8) {
+    if (p0 > 0) {
       if (p0 >= np) break;
-      float2 av[8][4][2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int p = p0 + j;
-        const float* pa = a.part_acc + (blk0 + (int64_t)p * groups) * (BQ * DP);
+        const float* pa = acc_ptr(p0 + j < np ? p0 + j : 0);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr)
-            av[j][db][pr] = p < np ? *(const float2*)(pa + ((((wave * 2 + gm) * 4 + db) * 2 + pr) * 64 + lane) * 2)
-                                   : make_float2(0.f, 0.f);
+            av[j][db][pr] = *(const float2*)(pa + (db * 2 + pr) * 128);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            o[db][2 * pr] += wgt[p0 + j] * av[j][db][pr].x;
-            o[db][2 * pr + 1] += wgt[p0 + j] * av[j][db][pr].y;
-          }
     }
-    const float inv = 1.f / den;
-    if (a.lse && g4 == 0) a.lse[(int64_t)g * L + i] = M + __log2f(den);
-    uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
-    const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
-                     ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int c = 16 * db + 4 * g4;
-      if (vec) {
-        if (c < d)
-          *(uint2*)(orow + c) = make_uint2(pack2(o[db][0] * inv, o[db][1] * inv),
-                                           pack2(o[db][2] * inv, o[db][3] * inv));
-      } else {
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (c + e < d) orow[c + e] = bf16_bits(o[db][e] * inv);
-      }
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          o[db][2 * pr] += wgt[p0 + j] * av[j][db][pr].x;
+          o[db][2 * pr + 1] += wgt[p0 + j] * av[j][db][pr].y;
+        }
+  }
+  if (i >= L) return;
+  const float inv = 1.f / den;
+  if (a.lse && g4 == 0) a.lse[(int64_t)g * L + i] = M + __log2f(den);
+  uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
+  const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
+                   ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int c = 16 * db + 4 * g4;
+    if (vec) {
+      if (c < d)
+        *(uint2*)(orow + c) = make_uint2(pack2(o[db][0] * inv, o[db][1] * inv),
+                                         pack2(o[db][2] * inv, o[db][3] * inv));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c + e < d) orow[c + e] = bf16_bits(o[db][e] * inv);
     }
   }
 }
@@ -904,8 +915,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
                        groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.slots == 0) return e;
-  hipLaunchKernelGGL(attn_part_merge_kernel, dim3((unsigned)nqt, (unsigned)groups), dim3(256), 0,
-                     s, a);
+  hipLaunchKernelGGL(attn_part_merge_kernel, dim3((unsigned)nqt * 8, (unsigned)groups), dim3(64),
+                     0, s, a);
   return hipGetLastError();
 }
 
