@@ -216,8 +216,34 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
     }
     __syncthreads();
   } else if (EPI == EPI_STAGE_F32) {
+    // y[m][n] = acc + bias + resid[m][n].  The residual values of every row this
+    // thread stores are loaded before the staging (a load after a store to y
+    // would wait for it: the two may alias as far as the compiler knows).  Four
+    // columns per thread: one 8-byte load and one 16-byte store when N % 4 == 0
+    // and the tensors are aligned, else element by element.
     constexpr int EP = C::BN + 4;  // row pitch (fp32)
+    constexpr int CPR = C::BN / 4;
+    constexpr int STEP = C::NT / CPR, RPT = C::BM / STEP;  // rows per pass, per thread
     float* es = (float*)smem;
+    const int c = tid % CPR, row0 = tid / CPR;
+    const int n = n0 + 4 * c;
+    const int64_t N = g.N;
+    const bool vec = N % 4 == 0 && (uintptr_t)g.e.y % 16 == 0 && (uintptr_t)g.e.resid % 8 == 0;
+    const uint16_t* res = (const uint16_t*)g.e.resid;
+    uint16_t rv[RPT][4];
+#pragma unroll
+    for (int x = 0; x < RPT; ++x) {
+      const int64_t m = (int64_t)m0 + row0 + STEP * x < g.M ? (int64_t)m0 + row0 + STEP * x : g.M - 1;
+      if (vec) {
+        const int64_t nc = n < N ? n : N - 4;
+        const uint2 w = *(const uint2*)(res + m * N + nc);
+        rv[x][0] = (uint16_t)(w.x & 0xffffu); rv[x][1] = (uint16_t)(w.x >> 16);
+        rv[x][2] = (uint16_t)(w.y & 0xffffu); rv[x][3] = (uint16_t)(w.y >> 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[x][e] = res[m * N + (n + e < N ? n + e : N - 1)];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::TI; ++i)
 #pragma unroll
@@ -229,49 +255,63 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
                                                 acc[j][i][4 * e + 2], acc[j][i][4 * e + 3]);
       }
     __syncthreads();
-    constexpr int CPR = C::BN / 4;
-    const int c = tid % CPR;
-    const int n = n0 + 4 * c;
-    for (int row = tid / CPR; row < C::BM; row += C::NT / CPR) {
+#pragma unroll
+    for (int x = 0; x < RPT; ++x) {
+      const int row = row0 + STEP * x;
       const int64_t m = (int64_t)m0 + row;
-      if (m >= g.M || n >= g.N) continue;
-      const uint2 rr = *(const uint2*)((const uint16_t*)g.e.resid + m * g.N + n);
+      if (m >= g.M || n >= N) continue;
       const float4 a4 = *(const float4*)(es + row * EP + 4 * c);
-      float4 o;
-      o.x = epi_value<uint16_t>(g.e, n, a4.x) + bf16_to_f32((uint16_t)(rr.x & 0xffffu));
-      o.y = epi_value<uint16_t>(g.e, n + 1, a4.y) + bf16_to_f32((uint16_t)(rr.x >> 16));
-      o.z = epi_value<uint16_t>(g.e, n + 2, a4.z) + bf16_to_f32((uint16_t)(rr.y & 0xffffu));
-      o.w = epi_value<uint16_t>(g.e, n + 3, a4.w) + bf16_to_f32((uint16_t)(rr.y >> 16));
-      *(float4*)(g.e.y + m * g.N + n) = o;
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = epi_value<uint16_t>(g.e, n + e, av[e]) + bf16_to_f32(rv[x][e]);
+      float* yr = g.e.y + m * N + n;
+      if (vec) {
+        *(float4*)yr = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) yr[e] = o[e];
+      }
     }
     __syncthreads();
   } else {
     // element by element (any layout): each wave passes one 32-row block at a
     // time through its own LDS slice, then its lanes walk the block row-major
     // (consecutive lanes take consecutive columns).
-    constexpr int WC = 32 * C::TJ, EPW = WC + 1;
+    // (the residual values of a block are loaded before its stores: see above)
+    constexpr int WC = 32 * C::TJ, EPW = WC + 1, PER = 32 * WC / 64;
     float* ws = (float*)smem + (wm * C::WN + wn) * 32 * EPW;
     const int lane = tid & 63;
     const bool heads = g.e.mode == EPI_HEADS;
 #pragma unroll
     for (int i = 0; i < C::TI; ++i) {
+      const int64_t mb = (int64_t)m0 + wm * 32 * C::TI + 32 * i;
+      const int64_t nb = (int64_t)n0 + wn * WC;
+      uint16_t rv[PER];
+      if (!heads) {
+#pragma unroll
+        for (int x = 0; x < PER; ++x) {
+          const int idx = lane + 64 * x, r = idx / WC, c = idx - r * WC;
+          const int64_t m = mb + r < g.M ? mb + r : g.M - 1, n = nb + c < g.N ? nb + c : g.N - 1;
+          rv[x] = ((const uint16_t*)g.e.resid)[m * g.N + n];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < C::TJ; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) ws[li * EPW + 32 * j + 16 * lh + e] = acc[j][i][e];
       __syncthreads();
-      const int64_t mb = (int64_t)m0 + wm * 32 * C::TI + 32 * i;
-      const int64_t nb = (int64_t)n0 + wn * WC;
-#pragma unroll 2
-      for (int idx = lane; idx < 32 * WC; idx += 64) {
-        const int r = idx / WC, c = idx - r * WC;
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const int idx = lane + 64 * x, r = idx / WC, c = idx - r * WC;
         const int64_t m = mb + r, n = nb + c;
         if (m >= g.M || n >= g.N) continue;
         const float v = epi_value<uint16_t>(g.e, n, ws[r * EPW + c]);
         if (heads) {
           heads_store<uint16_t>(g, m, n, v);
         } else {
-          g.e.y[m * g.N + n] = v + bf16_to_f32(((const uint16_t*)g.e.resid)[m * g.N + n]);
+          g.e.y[m * g.N + n] = v + bf16_to_f32(rv[x]);
         }
       }
       __syncthreads();
@@ -553,9 +593,8 @@ int epi_kind(const GemmArgs& g) {
                     (uintptr_t)g.e.dst0 % 16 == 0 && (uintptr_t)g.e.dst1 % 16 == 0;
     return ok ? EPI_STAGE_BF16 : EPI_SCALAR;
   }
-  const bool ok = C::ESMEM_F32 <= 160 * 1024 / C::OCC && g.N % 4 == 0 &&
-                  (uintptr_t)g.e.y % 16 == 0 && (uintptr_t)g.e.resid % 8 == 0;
-  return ok ? EPI_STAGE_F32 : EPI_SCALAR;
+  // (any N and alignment: the fp32 epilogue falls back to single elements)
+  return C::ESMEM_F32 <= 160 * 1024 / C::OCC ? EPI_STAGE_F32 : EPI_SCALAR;
 }
 
 // Operand loads: LDS-direct (K % 32 == 0, 16-byte rows), register-staged 16-byte

@@ -48,6 +48,43 @@ __global__ __launch_bounds__(256) void layer_norm_kernel(const float* __restrict
     Elt<T>::store(o + c, (x[c] - mean) * inv * Elt<T>::load(gamma + c) + Elt<T>::load(beta + c));
 }
 
+// The same LayerNorm for any D <= 64 NE: lane l keeps elements l + 64 k of its
+// row (and of gamma and beta) in registers, all loaded before the reductions.
+template <typename T, int NE>
+__global__ __launch_bounds__(256) void layer_norm_reg_kernel(const float* __restrict__ y,
+                                                             const T* __restrict__ gamma,
+                                                             const T* __restrict__ beta,
+                                                             float eps, int64_t rows, int D,
+                                                             T* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* x = y + row * D;
+  float v[NE], ga[NE], be[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int c = lane + 64 * k, cc = c < D ? c : D - 1;
+    v[k] = c < D ? x[cc] : 0.f;
+    ga[k] = Elt<T>::load(gamma + cc);
+    be[k] = Elt<T>::load(beta + cc);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NE; ++k) s += v[k];
+  const float mean = wave_sum(s) / (float)D;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    v[k] = lane + 64 * k < D ? v[k] - mean : 0.f;
+    q += v[k] * v[k];
+  }
+  const float inv = rsqrtf(wave_sum(q) / (float)D + eps);
+  T* o = out + row * D;
+#pragma unroll
+  for (int k = 0; k < NE; ++k)
+    if (lane + 64 * k < D) Elt<T>::store(o + lane + 64 * k, v[k] * inv * ga[k] + be[k]);
+}
+
 // Four consecutive elements as floats / from floats (16-byte aligned fp32,
 // 8-byte aligned bf16).
 __device__ inline float4 load4(const float* p) { return *(const float4*)p; }
@@ -150,6 +187,22 @@ hipError_t launch_layer_norm(int dtype, const float* y, const void* gamma, const
     TXL_LN_VEC(1) TXL_LN_VEC(2) TXL_LN_VEC(3) TXL_LN_VEC(4)
     TXL_LN_VEC(5) TXL_LN_VEC(6) TXL_LN_VEC(7) TXL_LN_VEC(8)
 #undef TXL_LN_VEC
+  }
+  if (D <= 1024) {
+#define TXL_LN_REG(NE)                                                                        \
+  if (D <= 64 * NE) {                                                                         \
+    if (dtype == 0)                                                                           \
+      hipLaunchKernelGGL((layer_norm_reg_kernel<float, NE>), dim3(blocks), dim3(256), 0, s, y, \
+                         (const float*)gamma, (const float*)beta, eps, rows, (int)D,          \
+                         (float*)out);                                                        \
+    else                                                                                      \
+      hipLaunchKernelGGL((layer_norm_reg_kernel<uint16_t, NE>), dim3(blocks), dim3(256), 0,   \
+                         s, y, (const uint16_t*)gamma, (const uint16_t*)beta, eps, rows,       \
+                         (int)D, (uint16_t*)out);                                             \
+    return hipGetLastError();                                                                 \
+  }
+    TXL_LN_REG(2) TXL_LN_REG(4) TXL_LN_REG(8) TXL_LN_REG(16)
+#undef TXL_LN_REG
   }
   if (dtype == 0)
     hipLaunchKernelGGL(layer_norm_kernel<float>, dim3(blocks), dim3(256), 0, s, y,
