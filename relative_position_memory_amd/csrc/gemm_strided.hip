@@ -147,14 +147,61 @@ constexpr int tile_elems() {
   return R * (KS + 8) > KS * (R + 8) ? R * (KS + 8) : KS * (R + 8);
 }
 
+// A staged 8-element piece as loaded: fp32 keeps its two 16-byte loads (eight
+// floats), bf16 its one; it is rounded to bf16 only when stored to LDS, so the
+// wait for the loads falls after the products issued in between.
+template <typename T> struct Raw;
+template <> struct Raw<float> {
+  float4 a, b;
+  __device__ uint4 packed() const {
+    return make_uint4(pack_bf16_pair(a.x, a.y), pack_bf16_pair(a.z, a.w),
+                      pack_bf16_pair(b.x, b.y), pack_bf16_pair(b.z, b.w));
+  }
+  __device__ void load(const void* p, int64_t off) {
+    a = *(const float4*)((const float*)p + off);
+    b = *(const float4*)((const float*)p + off + 4);
+  }
+  __device__ void set(const float* v) {
+    a = make_float4(v[0], v[1], v[2], v[3]);
+    b = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+template <> struct Raw<uint16_t> {
+  uint4 a;
+  __device__ uint4 packed() const { return a; }
+  __device__ void load(const void* p, int64_t off) { a = *(const uint4*)((const uint16_t*)p + off); }
+  __device__ void set(const float* v) {
+    a = make_uint4(pack_bf16_pair(v[0], v[1]), pack_bf16_pair(v[2], v[3]),
+                   pack_bf16_pair(v[4], v[5]), pack_bf16_pair(v[6], v[7]));
+  }
+};
+
 // This thread's pieces of the R x KS block of X(row, k) = p[base + row sr + k sk]
-// (rows r0.., k k0..; zero outside Rmax rows and kend), 8 bf16 each.  Piece
+// (rows r0.., k k0..; zero outside Rmax rows and kend), 8 elements each.  Piece
 // q = tid + 256 x: rows-contiguous: k q / (R / 8), rows 8 (q % (R / 8)) ..;
 // else row q / (KS / 8), k 8 (q % (KS / 8)) ..
+// When the whole block is inside and the layout allows 16-byte loads (a
+// condition uniform over the workgroup) every piece is one unconditional load,
+// so all of them are in flight together; otherwise each piece is checked, and
+// loaded element by element where it crosses an edge.
 template <typename T, int R>
 __device__ inline void stage_load(const void* p, int64_t base, int64_t sr, int64_t sk, int64_t Rmax,
                                   int64_t r0, int64_t k0, int64_t kend, int flags, int tid,
-                                  uint4 (&w)[R * KS / 2048]) {
+                                  Raw<T> (&w)[R * KS / 2048]) {
+  if ((flags & ST_VEC) && r0 + R <= Rmax && k0 + KS <= kend) {
+#pragma unroll
+    for (int x = 0; x < R * KS / 2048; ++x) {
+      const int q = tid + 256 * x;
+      if (flags & ST_ROWS) {
+        const int64_t k = k0 + q / (R / 8), r = r0 + 8 * (q % (R / 8));
+        w[x].load(p, base + r + k * sk);
+      } else {
+        const int64_t r = r0 + q / (KS / 8), k = k0 + 8 * (q % (KS / 8));
+        w[x].load(p, base + r * sr + k);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int x = 0; x < R * KS / 2048; ++x) {
     const int q = tid + 256 * x;
@@ -178,20 +225,20 @@ __device__ inline void stage_load(const void* p, int64_t base, int64_t sr, int64
           v[e] = (r < Rmax && k + e < kend) ? ld<T>(p, base + r * sr + (k + e) * sk) : 0.f;
       }
     }
-    w[x] = make_uint4(pack_bf16_pair(v[0], v[1]), pack_bf16_pair(v[2], v[3]),
-                      pack_bf16_pair(v[4], v[5]), pack_bf16_pair(v[6], v[7]));
+    w[x].set(v);
   }
 }
 
-template <int R>
-__device__ inline void stage_store(uint16_t* Xs, int flags, int tid, const uint4 (&w)[R * KS / 2048]) {
+template <typename T, int R>
+__device__ inline void stage_store(uint16_t* Xs, int flags, int tid, const Raw<T> (&w)[R * KS / 2048]) {
 #pragma unroll
   for (int x = 0; x < R * KS / 2048; ++x) {
     const int q = tid + 256 * x;
+    const uint4 pk = w[x].packed();
     if (flags & ST_ROWS)
-      *(uint4*)(Xs + (q / (R / 8)) * (R + 8) + 8 * (q % (R / 8))) = w[x];
+      *(uint4*)(Xs + (q / (R / 8)) * (R + 8) + 8 * (q % (R / 8))) = pk;
     else
-      *(uint4*)(Xs + (q / (KS / 8)) * (KS + 8) + 8 * (q % (KS / 8))) = w[x];
+      *(uint4*)(Xs + (q / (KS / 8)) * (KS + 8) + 8 * (q % (KS / 8))) = pk;
   }
 }
 
@@ -217,9 +264,12 @@ __device__ inline bf16x8 frag(const uint16_t* Xs, int flags, int rb, int s, int 
 
 // Output tile RM x RN; wave (wm, wn) of the 2 x 2 waves owns (RM / 32) x (RN / 32)
 // blocks of 16 x 16 at rows RM / 2 wm + 16 x, columns RN / 2 wn + 16 y.
-template <typename TA, typename TB, int RM, int RN>
-__global__ __launch_bounds__(256, RM == 64 ? 2 : 1) void gemm_strided_mfma_kernel(StridedGemm g, int ksplit, int fa,
-                                                                int fb) {
+// AR, BR: the ST_ROWS bit of A's and B's staging flags, fixed per instantiation
+// (fa, fb supply the ST_VEC bit), so a kernel carries only its layouts' code.
+template <typename TA, typename TB, int RM, int RN, int AR, int BR>
+__global__ __launch_bounds__(256, RM == 64 ? 2 : 1) void gemm_strided_mfma_kernel(StridedGemm g, int ksplit, int fa_in,
+                                                                int fb_in) {
+  const int fa = (AR ? ST_ROWS : 0) | (fa_in & ST_VEC), fb = (BR ? ST_ROWS : 0) | (fb_in & ST_VEC);
   constexpr int XM = RM / 32, XN = RN / 32;
   __shared__ __align__(16) uint16_t As[tile_elems<RM>()];
   __shared__ __align__(16) uint16_t Bs[tile_elems<RN>()];
@@ -234,7 +284,8 @@ __global__ __launch_bounds__(256, RM == 64 ? 2 : 1) void gemm_strided_mfma_kerne
   const int64_t abase = zq * g.A.s1 + zr * g.A.s2;
   const int64_t bbase = zq * g.B.s1 + zr * g.B.s2;
   // A is staged as X(row m, k), B as X(row n, k)
-  uint4 wa[RM * KS / 2048], wb[RN * KS / 2048];
+  Raw<TA> wa[RM * KS / 2048];
+  Raw<TB> wb[RN * KS / 2048];
   if (kbeg < kend) {
     stage_load<TA, RM>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, kbeg, kend, fa, tid, wa);
     stage_load<TB, RN>(g.B.p, bbase, g.B.sj, g.B.si, g.N, n0, kbeg, kend, fb, tid, wb);
@@ -247,8 +298,8 @@ __global__ __launch_bounds__(256, RM == 64 ? 2 : 1) void gemm_strided_mfma_kerne
     for (int y = 0; y < XN; ++y) acc[x][y] = {0.f, 0.f, 0.f, 0.f};
   for (int64_t k0 = kbeg; k0 < kend; k0 += KS) {
     __syncthreads();  // the previous step's fragment reads are done
-    stage_store<RM>(As, fa, tid, wa);
-    stage_store<RN>(Bs, fb, tid, wb);
+    stage_store<TA, RM>(As, fa, tid, wa);
+    stage_store<TB, RN>(Bs, fb, tid, wb);
     __syncthreads();
     if (k0 + KS < kend) {
       stage_load<TA, RM>(g.A.p, abase, g.A.si, g.A.sj, g.M, m0, k0 + KS, kend, fa, tid, wa);
@@ -319,20 +370,29 @@ int stage_flags(const StridedOperand& o, int64_t sr, int64_t sk, int dtype) {
   return 0;  // neither axis contiguous: element loads
 }
 
+template <int RM, int RN, int AR, int BR>
+void launch_mfma_layout(const StridedGemm& g, dim3 grid, int k, int fa, int fb, hipStream_t s) {
+  if (g.a_dtype == 0 && g.b_dtype == 0)
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, float, RM, RN, AR, BR>), grid, dim3(256), 0,
+                       s, g, k, fa, fb);
+  else if (g.a_dtype == 0 && g.b_dtype == 1)
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, uint16_t, RM, RN, AR, BR>), grid, dim3(256),
+                       0, s, g, k, fa, fb);
+  else if (g.a_dtype == 1 && g.b_dtype == 0)
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, float, RM, RN, AR, BR>), grid, dim3(256),
+                       0, s, g, k, fa, fb);
+  else
+    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, uint16_t, RM, RN, AR, BR>), grid,
+                       dim3(256), 0, s, g, k, fa, fb);
+}
+
 template <int RM, int RN>
 void launch_mfma_variant(const StridedGemm& g, dim3 grid, int k, int fa, int fb, hipStream_t s) {
-  if (g.a_dtype == 0 && g.b_dtype == 0)
-    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, float, RM, RN>), grid, dim3(256), 0, s, g, k,
-                       fa, fb);
-  else if (g.a_dtype == 0 && g.b_dtype == 1)
-    hipLaunchKernelGGL((gemm_strided_mfma_kernel<float, uint16_t, RM, RN>), grid, dim3(256), 0, s, g,
-                       k, fa, fb);
-  else if (g.a_dtype == 1 && g.b_dtype == 0)
-    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, float, RM, RN>), grid, dim3(256), 0, s, g,
-                       k, fa, fb);
-  else
-    hipLaunchKernelGGL((gemm_strided_mfma_kernel<uint16_t, uint16_t, RM, RN>), grid, dim3(256), 0, s,
-                       g, k, fa, fb);
+  const bool ar = fa & ST_ROWS, br = fb & ST_ROWS;
+  if (ar && br) launch_mfma_layout<RM, RN, 1, 1>(g, grid, k, fa, fb, s);
+  else if (ar) launch_mfma_layout<RM, RN, 1, 0>(g, grid, k, fa, fb, s);
+  else if (br) launch_mfma_layout<RM, RN, 0, 1>(g, grid, k, fa, fb, s);
+  else launch_mfma_layout<RM, RN, 0, 0>(g, grid, k, fa, fb, s);
 }
 
 hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s) {
