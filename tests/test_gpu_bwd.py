@@ -136,6 +136,8 @@ GRAD_NAMES = [("dh", "dh"), ("dW_q", "dW_q"), ("dW_kE", "dW_kE"), ("dW_v", "dW_v
     ("bf16", "charlm", {"B": 2, "L": 64, "M": 64, "D": 128, "H": 2, "d": 64}, 0, 0),  # empty memory
     # 128-wide product tiles with a ragged half tile, K split across workgroups
     ("bf16", "charlm", {"B": 2, "L": 96, "M": 160, "D": 192, "H": 3, "d": 64}, 160, 37),
+    # d_model above 512: the backward reuses the forward's fp32 LayerNorm input y
+    ("bf16", "charlm", {"B": 2, "L": 48, "M": 64, "D": 640, "H": 8, "d": 64}, 40, 30),
 ])
 def test_layer_step_bwd_matches_oracle(dtype, name, over, mem_len, start):
     from tests.test_gpu_parity import _layer_setup
@@ -165,6 +167,7 @@ def test_layer_step_bwd_matches_oracle(dtype, name, over, mem_len, start):
     ("fp32", "tiny", {"B": 2, "L": 37, "M": 50, "d": 12, "H": 3, "D": 40}, 45, 31),
     ("bf16", "charlm", {"B": 2, "L": 96, "M": 160, "D": 192, "H": 3, "d": 64}, 160, 37),
     ("bf16", "charlm", {"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
+    ("bf16", "charlm", {"B": 2, "L": 48, "M": 64, "D": 640, "H": 8, "d": 64}, 40, 30),
 ])
 def test_layer_step_bwd_saved_matches_recompute(dtype, name, over, mem_len, start):
     """txl_layer_step_save + txl_layer_step_bwd_saved: the forward output equals
