@@ -739,15 +739,15 @@ def traffic_summary(workload, fetch_csv, write_csv):
     lines = [
         f"# HBM traffic of the attention ({w.name}: B {w.B}, H {w.H}, d {w.d}, L {w.L}, "
         f"M {w.M}, {w.dtype}) per launch",
-        "# counter pass 1 (run from /tmp with TMPDIR=/tmp, repo root $R):",
-        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/pmc_fetch_{workload} "
+        "# counter pass 1 (run from /tmp with TMPDIR=/tmp, repo root $R, output folder $OUT):",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch_{workload} "
         f"-o run -- {cmd}",
         "# counter pass 2:",
-        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/pmc_write_{workload} "
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write_{workload} "
         f"-o run -- {cmd}",
         "# summary: python3 bench.py --traffic-summary " + workload +
-        f" gpurun_out/pmc_fetch_{workload}/run_counter_collection.csv"
-        f" gpurun_out/pmc_write_{workload}/run_counter_collection.csv",
+        f" $OUT/pmc_fetch_{workload}/run_counter_collection.csv"
+        f" $OUT/pmc_write_{workload}/run_counter_collection.csv",
         "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch.  Calibration: a plain device copy of",
         "# 256 MiB (reads 262144 KiB, writes 262144 KiB) in the same runs.",
         f"copy_fetch_kib: {cf:.1f}",
