@@ -38,6 +38,14 @@ __device__ inline T* heads_dst(const GemmArgs& g, int64_t m, int64_t n) {
   return base + b * e.sb + head * e.sh + ring_t(e, t) * e.st + c;
 }
 
+// Residual element i of an EPI_RESID_F32 output: 0 without one, else fp32 or
+// the input dtype T (Epilogue::resid_f32).
+template <typename T>
+__device__ inline float resid_at(const Epilogue& e, int64_t i) {
+  if (e.resid == nullptr) return 0.f;
+  return e.resid_f32 ? ((const float*)e.resid)[i] : Elt<T>::load((const T*)e.resid + i);
+}
+
 // acc + bias[n], then the activation (EPI_HEADS) -- see Epilogue::bias.
 template <typename T>
 __device__ inline float epi_value(const Epilogue& e, int64_t n, float acc) {
@@ -68,8 +76,7 @@ __device__ inline void epilogue_store(const GemmArgs& g, int64_t m, int64_t n, f
   if (g.e.mode == EPI_HEADS) {
     heads_store<T>(g, m, n, acc);
   } else {
-    const T* res = (const T*)g.e.resid + m * g.N + n;
-    g.e.y[m * g.N + n] = acc + Elt<T>::load(res);
+    g.e.y[m * g.N + n] = acc + resid_at<T>(g.e, m * g.N + n);
   }
 }
 

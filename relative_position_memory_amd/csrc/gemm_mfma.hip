@@ -43,6 +43,7 @@ struct GemmBatch {
   int ntm[MAXP], ntn[MAXP];
   int block_end[MAXP];  // inclusive prefix sums of the problems' tile counts
   int n;
+  int ksplit;           // K splits per tile (a launch_gemm_splitk problem), >= 1
 };
 
 __device__ inline uint4 keep_if(uint4 v, bool keep) {
@@ -158,7 +159,7 @@ __device__ inline void zero_acc(f32x16 (&acc)[C::TJ][C::TI]) {
 template <class C, int EPI>
 __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
                                 const f32x16 (&acc)[C::TJ][C::TI], int tid, int wm, int wn,
-                                int li, int lh) {
+                                int li, int lh, int split = -1) {
   if (EPI == EPI_STAGE_BF16) {
     constexpr int EP = C::BN + 8;  // row pitch (bf16): 16-byte aligned, conflict-free
     uint16_t* es = (uint16_t*)smem;
@@ -216,11 +217,14 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
     }
     __syncthreads();
   } else if (EPI == EPI_STAGE_F32) {
-    // y[m][n] = acc + bias + resid[m][n].  The residual values of every row this
-    // thread stores are loaded before the staging (a load after a store to y
-    // would wait for it: the two may alias as far as the compiler knows).  Four
-    // columns per thread: one 8-byte load and one 16-byte store when N % 4 == 0
-    // and the tensors are aligned, else element by element.
+    // y[m][n] = acc + bias + resid[m][n] (no residual when resid is NULL; fp32
+    // residual when resid_f32).  In a K-split launch split s stores its partial
+    // sum to y + s M N, with neither bias nor residual.  A bf16
+    // residual is loaded before the staging (a load after a store to y would wait
+    // for it: the two may alias as far as the compiler knows); an fp32 residual,
+    // twice the registers, after it, when the accumulators are dead, all rows of
+    // this thread before the first store.  Four columns per thread: 16-byte
+    // stores when N % 4 == 0 and the tensors are aligned, else element by element.
     constexpr int EP = C::BN + 4;  // row pitch (fp32)
     constexpr int CPR = C::BN / 4;
     constexpr int STEP = C::NT / CPR, RPT = C::BM / STEP;  // rows per pass, per thread
@@ -228,11 +232,17 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
     const int c = tid % CPR, row0 = tid / CPR;
     const int n = n0 + 4 * c;
     const int64_t N = g.N;
-    const bool vec = N % 4 == 0 && (uintptr_t)g.e.y % 16 == 0 && (uintptr_t)g.e.resid % 8 == 0;
-    const uint16_t* res = (const uint16_t*)g.e.resid;
-    uint16_t rv[RPT][4];
+    const bool plain = split >= 0;  // partial of a split launch
+    float* y = g.e.y + (plain ? (int64_t)split * g.M * N : 0);
+    const bool rf32 = g.e.resid_f32 != 0;
+    const void* resv = plain ? nullptr : g.e.resid;
+    const bool vec = N % 4 == 0 && (uintptr_t)g.e.y % 16 == 0 &&
+                     (uintptr_t)resv % (rf32 ? 16 : 8) == 0;
+    const uint16_t* res = (const uint16_t*)resv;
+    uint16_t rv[RPT][4] = {};
 #pragma unroll
     for (int x = 0; x < RPT; ++x) {
+      if (res == nullptr || rf32) break;
       const int64_t m = (int64_t)m0 + row0 + STEP * x < g.M ? (int64_t)m0 + row0 + STEP * x : g.M - 1;
       if (vec) {
         const int64_t nc = n < N ? n : N - 4;
@@ -255,17 +265,36 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
                                                 acc[j][i][4 * e + 2], acc[j][i][4 * e + 3]);
       }
     __syncthreads();
+    float4 fr[RPT];
+#pragma unroll
+    for (int x = 0; x < RPT; ++x) {
+      fr[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (resv == nullptr || !rf32) continue;
+      const float* rf = (const float*)resv;
+      const int64_t m = (int64_t)m0 + row0 + STEP * x < g.M ? (int64_t)m0 + row0 + STEP * x : g.M - 1;
+      if (vec) {
+        fr[x] = *(const float4*)(rf + m * N + (n < N ? n : N - 4));
+      } else {
+        fr[x].x = rf[m * N + (n < N ? n : N - 1)];
+        fr[x].y = rf[m * N + (n + 1 < N ? n + 1 : N - 1)];
+        fr[x].z = rf[m * N + (n + 2 < N ? n + 2 : N - 1)];
+        fr[x].w = rf[m * N + (n + 3 < N ? n + 3 : N - 1)];
+      }
+    }
 #pragma unroll
     for (int x = 0; x < RPT; ++x) {
       const int row = row0 + STEP * x;
       const int64_t m = (int64_t)m0 + row;
       if (m >= g.M || n >= N) continue;
       const float4 a4 = *(const float4*)(es + row * EP + 4 * c);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-      float o[4];
+      float o[4] = {a4.x, a4.y, a4.z, a4.w};
+      if (!plain) {
+        const float r4[4] = {fr[x].x, fr[x].y, fr[x].z, fr[x].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = epi_value<uint16_t>(g.e, n + e, av[e]) + bf16_to_f32(rv[x][e]);
-      float* yr = g.e.y + m * N + n;
+        for (int e = 0; e < 4; ++e)
+          o[e] = epi_value<uint16_t>(g.e, n + e, o[e]) + (rf32 ? r4[e] : bf16_to_f32(rv[x][e]));
+      }
+      float* yr = y + m * N + n;
       if (vec) {
         *(float4*)yr = make_float4(o[0], o[1], o[2], o[3]);
       } else {
@@ -288,13 +317,25 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
     for (int i = 0; i < C::TI; ++i) {
       const int64_t mb = (int64_t)m0 + wm * 32 * C::TI + 32 * i;
       const int64_t nb = (int64_t)n0 + wn * WC;
-      uint16_t rv[PER];
-      if (!heads) {
+      // (the residual's form is decided once, so each loop's loads are unconditional)
+      float rv[PER];
 #pragma unroll
-        for (int x = 0; x < PER; ++x) {
-          const int idx = lane + 64 * x, r = idx / WC, c = idx - r * WC;
-          const int64_t m = mb + r < g.M ? mb + r : g.M - 1, n = nb + c < g.N ? nb + c : g.N - 1;
-          rv[x] = ((const uint16_t*)g.e.resid)[m * g.N + n];
+      for (int x = 0; x < PER; ++x) rv[x] = 0.f;
+      if (!heads && g.e.resid != nullptr) {
+        if (g.e.resid_f32) {
+#pragma unroll
+          for (int x = 0; x < PER; ++x) {
+            const int idx = lane + 64 * x, r = idx / WC, c = idx - r * WC;
+            const int64_t m = mb + r < g.M ? mb + r : g.M - 1, n = nb + c < g.N ? nb + c : g.N - 1;
+            rv[x] = ((const float*)g.e.resid)[m * g.N + n];
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < PER; ++x) {
+            const int idx = lane + 64 * x, r = idx / WC, c = idx - r * WC;
+            const int64_t m = mb + r < g.M ? mb + r : g.M - 1, n = nb + c < g.N ? nb + c : g.N - 1;
+            rv[x] = bf16_to_f32(((const uint16_t*)g.e.resid)[m * g.N + n]);
+          }
         }
       }
 #pragma unroll
@@ -311,7 +352,7 @@ __device__ inline void epilogue(const GemmArgs& g, int m0, int n0, char* smem,
         if (heads) {
           heads_store<uint16_t>(g, m, n, v);
         } else {
-          g.e.y[m * g.N + n] = v + bf16_to_f32(rv[x]);
+          g.e.y[m * g.N + n] = v + rv[x];
         }
       }
       __syncthreads();
@@ -345,8 +386,11 @@ __device__ inline void wait_stages(int later) {
 // in-flight LDS-direct loads (each wave waits for its own loads first).
 __device__ inline void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // The same after this wave's own LDS reads have completed.
+// (the LDS wait goes through the builtin so that the compiler's own wait
+// tracking knows these reads are complete and does not wait again after it)
 __device__ inline void lds_read_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  asm volatile("s_barrier" ::: "memory");
 }
 
 template <class C, int EPI>
@@ -364,11 +408,18 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_dma_kernel(GemmBatch bt) {
 #pragma unroll
   for (int j = 0; j < C::TJ; ++j) wrow_f[j] = wn * 32 * C::TJ + 32 * j + wli;
 
-  for (int tile = blockIdx.x; tile < bt.block_end[bt.n - 1]; tile += gridDim.x) {
-    const TileId tl = tile_id<C>(bt, tile);
+  const int ks = bt.ksplit > 1 ? bt.ksplit : 1;
+  for (int tile = blockIdx.x; tile < bt.block_end[bt.n - 1] * ks; tile += gridDim.x) {
+    const int split = tile % ks;
+    const TileId tl = tile_id<C>(bt, tile / ks);
     if (!tl.valid) continue;
     const GemmArgs& g = bt.g[tl.p];
     const int m0 = tl.m0, n0 = tl.n0;
+    // this split's 32-deep K steps kt0 .. kt0 + nk - 1 (at least
+    // floor(steps / ksplit) >= 1)
+    const int nk_all = (int)(g.K / C::DBK);
+    const int kt0 = split * nk_all / ks;
+    const int nk = (split + 1) * nk_all / ks - kt0;
 
     // This lane's source rows: load q of the wave covers stage rows 16 q' + lane/4
     // (q' = wave * Q + q), 16-byte slot lane % 4, i.e. chunk slot ^ swz(row).
@@ -378,15 +429,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_dma_kernel(GemmBatch bt) {
     for (int q = 0; q < C::QA; ++q) {
       const int r = 16 * (wave * C::QA + q) + (lane >> 2);
       const int m = m0 + r < g.M ? m0 + r : (int)g.M - 1;  // rows past M: never stored
-      asrc[q] = gather_row32(g.a, m) + 8 * ((lane & 3) ^ swz(r));
+      asrc[q] = gather_row32(g.a, m) + 8 * ((lane & 3) ^ swz(r)) + kt0 * C::DBK;
     }
 #pragma unroll
     for (int q = 0; q < C::QW; ++q) {
       const int r = 16 * (wave * C::QW + q) + (lane >> 2);
       const int n = n0 + r < g.N ? n0 + r : (int)g.N - 1;  // columns past N: never stored
-      wsrc[q] = (const uint16_t*)weight_row(g.w, n, 2) + 8 * ((lane & 3) ^ swz(r));
+      wsrc[q] = (const uint16_t*)weight_row(g.w, n, 2) + 8 * ((lane & 3) ^ swz(r)) + kt0 * C::DBK;
     }
-    const int nk = (int)(g.K / C::DBK);
     auto issue = [&](int kt) {
       uint16_t* st = ring + (kt % C::NS) * C::STAGE;
 #pragma unroll
@@ -439,21 +489,33 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_dma_kernel(GemmBatch bt) {
     lds_barrier();
     if (C::NS - 1 < nk) issue(C::NS - 1);
     bf16x8 wf0[C::TJ], af0[C::TI], wf1[C::TJ], af1[C::TI];
+    // Within each half step: one MFMA, then the next half's fragment reads, then
+    // the other MFMAs (the reads then have all but one MFMA of the half to land).
+    // The last step is peeled off so that the products after the barrier are
+    // reached only through its LDS wait and start without waiting again.
+    auto pin = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, C::TI + C::TJ, 0);      // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, C::TI * C::TJ - 1, 0);  // MFMA
+    };
     frags(0, 0, wf0, af0);
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt + 1 < nk; ++kt) {
       frags(kt, 1, wf1, af1);
       mfmas(wf0, af0);
-      if (kt + 1 < nk) {
-        const int later = nk - 2 - kt < C::NS - 2 ? nk - 2 - kt : C::NS - 2;
-        wait_stages<PER_STAGE>(later);
-        lds_read_barrier();
-        if (kt + C::NS < nk) issue(kt + C::NS);
-        frags(kt + 1, 0, wf0, af0);
-      }
+      pin();
+      const int later = nk - 2 - kt < C::NS - 2 ? nk - 2 - kt : C::NS - 2;
+      wait_stages<PER_STAGE>(later);
+      lds_read_barrier();
+      if (kt + C::NS < nk) issue(kt + C::NS);
+      frags(kt + 1, 0, wf0, af0);
       mfmas(wf1, af1);
+      pin();
     }
+    frags(nk - 1, 1, wf1, af1);
+    mfmas(wf0, af0);
+    mfmas(wf1, af1);
     __syncthreads();  // all fragment reads done before the epilogue reuses LDS
-    epilogue<C, EPI>(g, m0, n0, smem_raw, acc, tid, wm, wn, li, lh);
+    epilogue<C, EPI>(g, m0, n0, smem_raw, acc, tid, wm, wn, li, lh, ks > 1 ? split : -1);
   }
 }
 
@@ -627,7 +689,11 @@ hipError_t launch_cfg(const GemmBatch& bt, int total, int num_cus, hipStream_t s
 template <class C, int LOAD>
 hipError_t launch_epi(const GemmBatch& bt, int epi, int total, int num_cus, hipStream_t s) {
   if (epi == EPI_STAGE_BF16) return launch_cfg<C, EPI_STAGE_BF16, LOAD>(bt, total, num_cus, s);
-  if (epi == EPI_STAGE_F32) return launch_cfg<C, EPI_STAGE_F32, LOAD>(bt, total, num_cus, s);
+  // (the fp32 staging fits only the tiles whose ESMEM_F32 fits in LDS: no other
+  // instance is built)
+  if constexpr (C::ESMEM_F32 <= 160 * 1024 / C::OCC)
+    if (epi == EPI_STAGE_F32) return launch_cfg<C, EPI_STAGE_F32, LOAD>(bt, total, num_cus, s);
+  if (epi == EPI_STAGE_F32) return hipErrorInvalidValue;
   return launch_cfg<C, EPI_SCALAR, LOAD>(bt, total, num_cus, s);
 }
 
@@ -641,7 +707,7 @@ bool wide_rows(const GemmArgs& g) {
 bool dma_ok(const GemmArgs& g) { return g.K % 32 == 0 && wide_rows(g); }
 
 template <class C>
-hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s) {
+hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s, int ksplit = 1) {
   GemmBatch bt{};
   int64_t total = 0;
   int epi = -1;
@@ -659,6 +725,14 @@ hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s) {
     wide = wide && wide_rows(gs[p]);
   }
   bt.n = n;
+  bt.ksplit = 1;
+  if (ksplit > 1) {
+    if (n != 1 || !dma || epi != EPI_STAGE_F32 || gs[0].e.mode != EPI_RESID_F32)
+      return hipErrorInvalidValue;
+    bt.ksplit = ksplit;
+    total *= ksplit;
+    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  }
   if (total == 0) return hipSuccess;
   if (dma) return launch_epi<C, LOAD_DMA>(bt, epi, (int)total, num_cus, s);
   if (wide) return launch_epi<C, LOAD_REG>(bt, epi, (int)total, num_cus, s);
@@ -776,7 +850,7 @@ __device__ inline void gemv_store(const GemmArgs& g, int m, int n, float acc) {
   acc = epi_value<uint16_t>(e, n, acc);
   if (e.mode != EPI_HEADS) {
     const int64_t i = (int64_t)m * g.N + n;
-    e.y[i] = acc + Elt<uint16_t>::load((const uint16_t*)e.resid + i);
+    e.y[i] = acc + resid_at<uint16_t>(e, i);
     return;
   }
   const int per = (int)(g.a.mem_len + g.a.cur_rows), HD = (int)e.HD, d = (int)e.d;
@@ -1140,6 +1214,21 @@ bool gemm_mfma_supported(const GemmArgs& g) {
     if (span > 0x7fffffffLL) return false;
   }
   return true;
+}
+
+hipError_t launch_gemm_splitk(const GemmArgs& g, int ksplit, hipStream_t s, int num_cus) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (ksplit < 1 || g.e.mode != EPI_RESID_F32 || !dma_ok(g) || !gemm_mfma_supported(g) ||
+      g.K / 32 < ksplit || epi_kind<Small>(g) != EPI_STAGE_F32)
+    return hipErrorInvalidValue;
+  if (g.M * g.N * ksplit > ((int64_t)1 << 40)) return hipErrorInvalidValue;
+  if (ksplit == 1) {
+    GemmArgs g1 = g;
+    g1.e.resid = nullptr;
+    g1.e.bias = nullptr;
+    return launch_tiles<Small>(&g1, 1, num_cus, s);
+  }
+  return launch_tiles<Small>(&g, 1, num_cus, s, ksplit);
 }
 
 hipError_t launch_gemm_mfma_multi(const GemmArgs* gs, int n, hipStream_t s, int num_cus) {

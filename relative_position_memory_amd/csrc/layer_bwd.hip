@@ -5,10 +5,16 @@
 // LayerNorm backward, the copies and the gather of [memory ; h_in].
 #include "txl_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace txl {
 namespace {
+
+// two floats -> bf16 pair (low half = lo), round to nearest even
+__device__ inline uint32_t pack2_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
 
 template <typename E>
 __device__ inline float ldE(const void* p, int64_t off) {
@@ -135,6 +141,155 @@ unsigned grid_for(int64_t n) {
   return (unsigned)(g < 4096 ? (g > 0 ? g : 1) : 4096);
 }
 
+// Transposing pack to bf16: dst[r][k] = bf16(src[r + k * sk]) for r < R, k < K,
+// and 0 for K <= k < Kp (row pitch Kp): a 64 x 64 block per workgroup passes
+// through LDS, read along r (contiguous in src) and written along k.  Every
+// load is issued (indexes past the ends are clamped, their values zeroed).
+// One 64 x 64 tile of destination rows r0.., columns c0.. of a pack job per
+// block: dst[r][c] = source element (r, c) converted to bf16 for c < C, zero for
+// C <= c < Cpad.  A transposed job reads element (r, c) at src[c sk + r] and
+// passes the tile through LDS; a rows job reads src[(r / rpb) sb + (r % rpb) ld
+// + c] directly.  Jobs marked vec (every row and pitch 16-byte aligned, R, C
+// and Cpad multiples of 8) move 16 bytes per access, both in and out; the
+// others go element by element.  Out-of-range addresses are clamped and their
+// values replaced, so every load of a tile is issued unconditionally.
+__device__ inline float pk_ld(const void* p, int64_t i, int dtype) {
+  return dtype ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
+  __shared__ float t[64][65];
+  int jn = 0;
+  while (jn + 1 < jobs.n && (int64_t)blockIdx.x >= jobs.j[jn].tile_end) ++jn;
+  const PackJob& J = jobs.j[jn];
+  const int64_t tile = (int64_t)blockIdx.x - (jn ? jobs.j[jn - 1].tile_end : 0);
+  const int64_t ntc = (J.Cpad + 63) / 64;
+  const int64_t r0 = (tile / ntc) * 64, c0 = (tile % ntc) * 64;
+  const int tid = threadIdx.x;
+  if (J.vec) {
+    if (J.trans) {
+      // source rows are c: 64 of them, 64 r each, into t[c - c0][r - r0]
+      if (J.dtype == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cl = tid / 16 + 16 * i, rl = 4 * (tid % 16);
+          const int64_t c = c0 + cl, r = r0 + rl;
+          const bool ok = c < J.C && r < J.R;
+          const float4 v = *(const float4*)((const float*)J.src +
+                                            (ok ? c : 0) * J.sk + (ok ? r : 0));
+          t[cl][rl] = ok ? v.x : 0.f; t[cl][rl + 1] = ok ? v.y : 0.f;
+          t[cl][rl + 2] = ok ? v.z : 0.f; t[cl][rl + 3] = ok ? v.w : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int cl = tid / 8 + 32 * i, rl = 8 * (tid % 8);
+          const int64_t c = c0 + cl, r = r0 + rl;
+          const bool ok = c < J.C && r < J.R;
+          const uint4 v = *(const uint4*)((const uint16_t*)J.src +
+                                          (ok ? c : 0) * J.sk + (ok ? r : 0));
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            t[cl][rl + 2 * e] = ok ? bf16_to_f32((uint16_t)(w[e] & 0xffffu)) : 0.f;
+            t[cl][rl + 2 * e + 1] = ok ? bf16_to_f32((uint16_t)(w[e] >> 16)) : 0.f;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rl = tid / 8 + 32 * i, cl = 8 * (tid % 8);
+        const int64_t r = r0 + rl, c = c0 + cl;
+        if (r >= J.R || c >= J.Cpad) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack2_bf16(t[cl + 2 * e][rl], t[cl + 2 * e + 1][rl]);
+        *(uint4*)(J.dst + r * J.ldd + c) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rl = tid / 8 + 32 * i, cl = 8 * (tid % 8);
+        const int64_t r = r0 + rl, c = c0 + cl;
+        if (r >= J.R || c >= J.Cpad) continue;
+        const bool ok = c < J.C;
+        const int64_t off = (r / J.rpb) * J.sb + (r % J.rpb) * J.ld + (ok ? c : 0);
+        uint4 o;
+        if (J.dtype == 0) {
+          const float4 a = *(const float4*)((const float*)J.src + off);
+          const float4 b = *(const float4*)((const float*)J.src + off + 4);
+          o = make_uint4(pack2_bf16(a.x, a.y), pack2_bf16(a.z, a.w), pack2_bf16(b.x, b.y),
+                         pack2_bf16(b.z, b.w));
+        } else {
+          o = *(const uint4*)((const uint16_t*)J.src + off);
+        }
+        if (!ok) o = make_uint4(0u, 0u, 0u, 0u);
+        *(uint4*)(J.dst + r * J.ldd + c) = o;
+      }
+    }
+    return;
+  }
+  // element by element
+  if (J.trans) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int cl = tid / 64 + 4 * i, rl = tid % 64;
+      const int64_t c = c0 + cl, r = r0 + rl;
+      const bool ok = c < J.C && r < J.R;
+      const float v = pk_ld(J.src, (ok ? c : 0) * J.sk + (ok ? r : 0), J.dtype);
+      t[cl][rl] = ok ? v : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rl = tid / 64 + 4 * i, cl = tid % 64;
+      const int64_t r = r0 + rl, c = c0 + cl;
+      if (r < J.R && c < J.Cpad) J.dst[r * J.ldd + c] = f32_to_bf16(t[cl][rl]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rl = tid / 64 + 4 * i, cl = tid % 64;
+      const int64_t r = r0 + rl, c = c0 + cl;
+      if (r >= J.R || c >= J.Cpad) continue;
+      const bool ok = c < J.C;
+      const float v = pk_ld(J.src, (r / J.rpb) * J.sb + (r % J.rpb) * J.ld + (ok ? c : 0), J.dtype);
+      J.dst[r * J.ldd + c] = ok ? f32_to_bf16(v) : (uint16_t)0;
+    }
+  }
+}
+
+// dst[i] = sum over s < parts of src[s n + i], four elements per thread.
+template <bool VEC>
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ src, int parts,
+                                                           int64_t n, float* __restrict__ dst) {
+  const int64_t q = (n + 3) / 4;
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < q;
+       it += (int64_t)gridDim.x * 256) {
+    const int64_t i = 4 * it;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (VEC) {
+      float4 v[16];
+#pragma unroll
+      for (int p = 0; p < 16; ++p)
+        if (p < parts) v[p] = *(const float4*)(src + p * n + i);
+#pragma unroll
+      for (int p = 0; p < 16; ++p)
+        if (p < parts) {
+          acc.x += v[p].x; acc.y += v[p].y; acc.z += v[p].z; acc.w += v[p].w;
+        }
+      *(float4*)(dst + i) = acc;
+    } else {
+      for (int e = 0; e < 4 && i + e < n; ++e) {
+        float a = 0.f;
+        for (int p = 0; p < parts; ++p) a += src[p * n + i + e];
+        dst[i + e] = a;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_zero_many(float* const* p, const int64_t* count, int n, hipStream_t s) {
@@ -204,6 +359,67 @@ hipError_t launch_gather_ctx(int dtype, const void* ring, int64_t cap, int64_t s
   else
     hipLaunchKernelGGL((gather_ctx_kernel<float, 1>), dim3(grid_for(n)), dim3(256), 0, s, ring,
                        cap, start, len, h, B, L, D, ctx);
+  return hipGetLastError();
+}
+
+PackJob pack_rows(const void* src, int dtype, int64_t R, int64_t C, int64_t Cpad, int64_t rpb,
+                  int64_t sb, int64_t ld, uint16_t* dst, int64_t ldd) {
+  PackJob j{};
+  j.src = src; j.dtype = dtype; j.trans = 0;
+  j.R = R; j.C = C; j.Cpad = Cpad; j.rpb = rpb; j.sb = sb; j.ld = ld;
+  j.dst = dst; j.ldd = ldd;
+  return j;
+}
+
+PackJob pack_trans(const void* src, int dtype, int64_t R, int64_t C, int64_t Cpad, int64_t sk,
+                   uint16_t* dst, int64_t ldd) {
+  PackJob j{};
+  j.src = src; j.dtype = dtype; j.trans = 1;
+  j.R = R; j.C = C; j.Cpad = Cpad; j.rpb = 1; j.sk = sk;
+  j.dst = dst; j.ldd = ldd;
+  return j;
+}
+
+hipError_t launch_pack(const PackJob* js, int n, hipStream_t s) {
+  for (int base = 0; base < n; base += PJ_MAX) {
+    PackJobs b{};
+    int64_t tiles = 0;
+    for (int x = 0; x < PJ_MAX && base + x < n; ++x) {
+      PackJob j = js[base + x];
+      if (j.R < 0 || j.C < 0 || j.Cpad < j.C || j.ldd < j.Cpad || j.rpb < 1 ||
+          (j.dtype != 0 && j.dtype != 1) || (j.C > 0 && j.R > 0 && !j.src))
+        return hipErrorInvalidValue;
+      const int64_t es = j.dtype ? 2 : 4, al = 16 / es;  // elements per 16 bytes
+      const uintptr_t src = (uintptr_t)j.src, dst = (uintptr_t)j.dst;
+      bool vec = j.Cpad % 8 == 0 && j.ldd % 8 == 0 && dst % 16 == 0 && src % 16 == 0;
+      if (j.trans)
+        vec = vec && j.R % 8 == 0 && j.sk % al == 0;
+      else
+        vec = vec && j.C % 8 == 0 && j.ld % al == 0 && j.sb % al == 0;
+      j.vec = vec ? 1 : 0;
+      tiles += ((j.R + 63) / 64) * ((j.Cpad + 63) / 64);
+      if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+      j.tile_end = tiles;
+      b.j[x] = j;
+      b.n = x + 1;
+    }
+    if (tiles == 0) continue;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)tiles), dim3(256), 0, s, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_sum_partials(const float* src, int parts, int64_t n, float* dst, hipStream_t s) {
+  if (parts < 1 || parts > 16 || n < 0) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  const bool vec = n % 4 == 0 && (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0;
+  const unsigned grid = (unsigned)std::min<int64_t>(((n + 3) / 4 + 255) / 256, 65536);
+  if (vec)
+    hipLaunchKernelGGL(sum_partials_kernel<true>, dim3(grid), dim3(256), 0, s, src, parts, n, dst);
+  else
+    hipLaunchKernelGGL(sum_partials_kernel<false>, dim3(grid), dim3(256), 0, s, src, parts, n, dst);
   return hipGetLastError();
 }
 

@@ -827,8 +827,19 @@ int txl_rel_attn_bwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
 // ---- layer step backward --------------------------------------------------------------
 namespace {
 
+// K splits of a weight-gradient product dW [M][N] summed over K rows: about one
+// workgroup of 128 x 128 outputs per CU of a 256-CU chip, each split at least 8
+// steps of 32 (a fixed rule, so the workspace does not depend on the device).
+int wg_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int64_t ks = (256 + tiles - 1) / tiles;
+  ks = std::min<int64_t>(ks, std::min<int64_t>(K / 32 / 8, 16));
+  return ks > 1 ? (int)ks : 1;
+}
+
 struct BwdWs {
-  size_t fwd, hout, y, dy, mean, rstd, da, dq, dk, dv, dr, ctx, lse, attn, total;
+  size_t fwd, hout, y, dy, mean, rstd, da, dq, dk, dv, dr, ctx, lse, attn, dyb, wot, cat, wcat,
+      pko, pkq, pkkv, pkr, part, total;
 };
 
 BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
@@ -855,8 +866,66 @@ BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
   w.ctx = take((size_t)(B * T * D * es));
   w.lse = take((size_t)(B * dm.n_head * L) * 4);
   w.attn = take(txl::attn_bwd_scratch_bytes(B, dm.n_head, L, cap));
+  // bf16 layers: the input-gradient products' operands as bf16 rows along K (K
+  // rounded up to 32, zero-padded): dy and W_o^T for da; [dq | dk | dv] of the
+  // current rows and [W_q^T | W_kE^T | W_v^T] for dh
+  const bool mc = dtype == TXL_BF16;
+  const int64_t Kd = round_up(D, 32), Kc = round_up(3 * HD, 32);
+  w.dyb = take(mc ? (size_t)(B * L * Kd) * 2 : 0);
+  w.wot = take(mc ? (size_t)(HD * Kd) * 2 : 0);
+  w.cat = take(mc ? (size_t)(B * L * Kc) * 2 : 0);
+  w.wcat = take(mc ? (size_t)(D * Kc) * 2 : 0);
+  // and the weight-gradient products' operands transposed to rows along the
+  // summed rows (B L, B T or T, rounded up to 32): [dy^T ; a^T], [dq^T ; h_in^T],
+  // [dk^T ; dv^T ; ctx^T], [dr^T ; R^T], then the K-split partial sums
+  const int64_t Kbl = round_up(B * L, 32), Kbt = round_up(B * T, 32), Kt = round_up(T, 32);
+  w.pko = take(mc ? (size_t)((D + HD) * Kbl) * 2 : 0);
+  w.pkq = take(mc ? (size_t)((HD + D) * Kbl) * 2 : 0);
+  w.pkkv = take(mc ? (size_t)((2 * HD + D) * Kbt) * 2 : 0);
+  w.pkr = take(mc ? (size_t)((HD + D) * Kt) * 2 : 0);
+  size_t part = 0;
+  if (mc) {
+    const int64_t shapes[5][3] = {{D, HD, Kbl}, {HD, D, Kbl}, {HD, D, Kbt}, {HD, D, Kbt}, {HD, D, Kt}};
+    for (const auto& sh : shapes) {
+      const int ks = wg_splits(sh[0], sh[1], sh[2]);
+      if (ks > 1) part = std::max(part, (size_t)(ks * sh[0] * sh[1]) * 4);
+    }
+  }
+  w.part = take(part);
   w.total = off;
   return w;
+}
+
+// y[m][n] = sum_k A[m][k] W[n][k] (+ resid[m][n], fp32) on the bf16 matrix cores:
+// A [M][K] and W [N][K] dense bf16 rows (K a multiple of 32 takes the LDS-direct
+// pipeline), y fp32 [M][N].
+hipError_t mm_bf16(hipStream_t st, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                   const uint16_t* W, float* y, const float* resid) {
+  txl::GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.a = {nullptr, 1, 0, 0, A, M, K};
+  g.w = {W, W, N, K, 0, 0};
+  g.e.mode = txl::EPI_RESID_F32;
+  g.e.y = y;
+  g.e.resid = resid;
+  g.e.resid_f32 = 1;
+  return txl::launch_gemm_mfma_multi(&g, 1, st, num_cus());
+}
+
+// dW [M][N] = A W^T for a weight gradient: A [M][K] and W [N][K] bf16 rows (the
+// transposed operands), split along K by wg_splits into part, then summed.
+hipError_t wg_bf16(hipStream_t st, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                   const uint16_t* W, float* dW, float* part) {
+  const int ks = wg_splits(M, N, K);
+  txl::GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.a = {nullptr, 1, 0, 0, A, M, K};
+  g.w = {W, W, N, K, 0, 0};
+  g.e.mode = txl::EPI_RESID_F32;
+  g.e.y = ks > 1 ? part : dW;
+  hipError_t e = txl::launch_gemm_splitk(g, ks, st, num_cus());
+  if (e == hipSuccess && ks > 1) e = txl::launch_sum_partials(part, ks, M * N, dW, st);
+  return e;
 }
 
 // C = alpha A B (+ C), A (m, k) at a + m*am + k*ak, B (k, n) at b + k*bk + n*bn, C row-major
@@ -1062,9 +1131,11 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
   // every output that is summed into (atomically or by accumulating products),
   // cleared in one launch
   {
+    // (bf16 layers store the weight gradients and da whole)
+    const int64_t wz = dt == 1 ? 0 : HD * D;
     float* zp[] = {g->dgamma, g->dbeta, g->du, g->dv_bias, dr, g->dW_o, g->dW_q, g->dW_kE,
                    g->dW_v, g->dW_kR, da};
-    const int64_t zn[] = {D, D, HD, HD, T * HD, D * HD, HD * D, HD * D, HD * D, HD * D, BL * HD};
+    const int64_t zn[] = {D, D, HD, HD, T * HD, wz, wz, wz, wz, wz, dt == 1 ? 0 : BL * HD};
     TXL_TRY(txl::launch_zero_many(zp, zn, 11, st), "clear");
   }
   // y = a W_o^T + h_in (the LayerNorm input), then the LayerNorm backward
@@ -1075,9 +1146,28 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
   TXL_TRY(txl::launch_ln_bwd(dt, y, w->ln_gamma, dh_out, BL, D, dm.ln_eps, dy,
                              (float*)(base + bw.mean), (float*)(base + bw.rstd), g->dgamma,
                              g->dbeta, st, true), "layernorm backward");
-  // dW_o = dy^T a, da = dy W_o
-  TXL_TRY(sgemm(st, D, HD, BL, dy, 0, 1, D, a, dt, HD, 1, g->dW_o, HD, true), "dW_o");
-  TXL_TRY(sgemm(st, BL, HD, D, dy, 0, D, 1, w->W_o, dt, HD, 1, da, HD, true), "da");
+  // dW_o = dy^T a, da = dy W_o.  bf16 layers: both on the matrix cores, from dy
+  // as bf16 rows, W_o^T, dy^T and a^T packed in one launch
+  const int64_t Kd = round_up(D, 32), Kc = round_up(3 * HD, 32);
+  const int64_t Kbl = round_up(BL, 32), Kbt = round_up(B * T, 32), Kt = round_up(T, 32);
+  float* part = (float*)(base + bw.part);
+  if (dt == 1) {
+    uint16_t* dyb = (uint16_t*)(base + bw.dyb);
+    uint16_t* wot = (uint16_t*)(base + bw.wot);
+    uint16_t* ao = (uint16_t*)(base + bw.pko);
+    uint16_t* wo = ao + D * Kbl;
+    const txl::PackJob jobs[] = {
+        txl::pack_rows(dy, 0, BL, D, Kd, BL, 0, D, dyb, Kd),
+        txl::pack_trans(w->W_o, 1, HD, D, Kd, HD, wot, Kd),
+        txl::pack_trans(dy, 0, D, BL, Kbl, D, ao, Kbl),
+        txl::pack_trans(a, 1, HD, BL, Kbl, HD, wo, Kbl)};
+    TXL_TRY(txl::launch_pack(jobs, 4, st), "operand packs");
+    TXL_TRY(mm_bf16(st, BL, HD, Kd, dyb, wot, da, nullptr), "da");
+    TXL_TRY(wg_bf16(st, D, HD, Kbl, ao, wo, g->dW_o, part), "dW_o");
+  } else {
+    TXL_TRY(sgemm(st, D, HD, BL, dy, 0, 1, D, a, dt, HD, 1, g->dW_o, HD, true), "dW_o");
+    TXL_TRY(sgemm(st, BL, HD, D, dy, 0, D, 1, w->W_o, dt, HD, 1, da, HD, true), "da");
+  }
   // attention backward on the forward's head-major q, k, v, r
   txl::AttnBwdArgs ab{};
   ab.B = B; ab.H = H; ab.L = L; ab.mem_len = len; ab.d = d;
@@ -1097,17 +1187,51 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
   // projection weights: dW_q = dq^T h_in, dW_kE = dk^T ctx, dW_v = dv^T ctx, dW_kR = dr^T R
   TXL_TRY(txl::launch_gather_ctx(dt, mem->data, mem->capacity, mem->start, len, h_in, B, L, D, ctx,
                                  st), "context gather");
-  TXL_TRY(sgemm(st, HD, D, BL, dq, 0, 1, HD, h_in, dt, D, 1, g->dW_q, D, true), "dW_q");
-  TXL_TRY(sgemm(st, HD, D, B * T, dk, 0, 1, HD, ctx, dt, D, 1, g->dW_kE, D, true), "dW_kE");
-  TXL_TRY(sgemm(st, HD, D, B * T, dv, 0, 1, HD, ctx, dt, D, 1, g->dW_v, D, true), "dW_v");
-  TXL_TRY(sgemm(st, HD, D, T, dr, 0, 1, HD, R, dt, D, 1, g->dW_kR, D, true), "dW_kR");
   // dh = dy + dq W_q + (dk W_kE + dv W_v) on the current rows (the memory's gradient is stopped)
-  TXL_TRY(txl::launch_to_f32(0, dy, g->dh, BL * D, st), "copy");
-  TXL_TRY(sgemm(st, BL, D, HD, dq, 0, HD, 1, w->W_q, dt, D, 1, g->dh, D, true), "dh q");
-  TXL_TRY(sgemm(st, L, D, HD, dk + len * HD, 0, HD, 1, w->W_kE, dt, D, 1, g->dh, D, true, B,
-                T * HD, 0, L * D), "dh k");
-  TXL_TRY(sgemm(st, L, D, HD, dv + len * HD, 0, HD, 1, w->W_v, dt, D, 1, g->dh, D, true, B,
-                T * HD, 0, L * D), "dh v");
+  if (dt == 1) {
+    // one launch packs the four weight gradients' operands and dh's: one product
+    // over K = 3 HD, [dq | dk | dv] (bf16 rows) times [W_q^T | W_kE^T | W_v^T]
+    uint16_t* cat = (uint16_t*)(base + bw.cat);
+    uint16_t* wcat = (uint16_t*)(base + bw.wcat);
+    uint16_t* aq = (uint16_t*)(base + bw.pkq);
+    uint16_t* wq = aq + HD * Kbl;
+    uint16_t* ak = (uint16_t*)(base + bw.pkkv);
+    uint16_t* av = ak + HD * Kbt;
+    uint16_t* wc = av + HD * Kbt;
+    uint16_t* ar = (uint16_t*)(base + bw.pkr);
+    uint16_t* wr = ar + HD * Kt;
+    const txl::PackJob jobs[] = {
+        txl::pack_trans(dq, 0, HD, BL, Kbl, HD, aq, Kbl),
+        txl::pack_trans(h_in, 1, D, BL, Kbl, D, wq, Kbl),
+        txl::pack_trans(dk, 0, HD, B * T, Kbt, HD, ak, Kbt),
+        txl::pack_trans(dv, 0, HD, B * T, Kbt, HD, av, Kbt),
+        txl::pack_trans(ctx, 1, D, B * T, Kbt, D, wc, Kbt),
+        txl::pack_trans(dr, 0, HD, T, Kt, HD, ar, Kt),
+        txl::pack_trans(R, 1, D, T, Kt, D, wr, Kt),
+        txl::pack_rows(dq, 0, BL, HD, HD, BL, 0, HD, cat, Kc),
+        txl::pack_rows(dk + len * HD, 0, BL, HD, HD, L, T * HD, HD, cat + HD, Kc),
+        txl::pack_rows(dv + len * HD, 0, BL, HD, Kc - 2 * HD, L, T * HD, HD, cat + 2 * HD, Kc),
+        txl::pack_trans(w->W_q, 1, D, HD, HD, D, wcat, Kc),
+        txl::pack_trans(w->W_kE, 1, D, HD, HD, D, wcat + HD, Kc),
+        txl::pack_trans(w->W_v, 1, D, HD, Kc - 2 * HD, D, wcat + 2 * HD, Kc)};
+    TXL_TRY(txl::launch_pack(jobs, 13, st), "operand packs");
+    TXL_TRY(wg_bf16(st, HD, D, Kbl, aq, wq, g->dW_q, part), "dW_q");
+    TXL_TRY(wg_bf16(st, HD, D, Kbt, ak, wc, g->dW_kE, part), "dW_kE");
+    TXL_TRY(wg_bf16(st, HD, D, Kbt, av, wc, g->dW_v, part), "dW_v");
+    TXL_TRY(wg_bf16(st, HD, D, Kt, ar, wr, g->dW_kR, part), "dW_kR");
+    TXL_TRY(mm_bf16(st, BL, D, Kc, cat, wcat, g->dh, dy), "dh");
+  } else {
+    TXL_TRY(sgemm(st, HD, D, BL, dq, 0, 1, HD, h_in, dt, D, 1, g->dW_q, D, true), "dW_q");
+    TXL_TRY(sgemm(st, HD, D, B * T, dk, 0, 1, HD, ctx, dt, D, 1, g->dW_kE, D, true), "dW_kE");
+    TXL_TRY(sgemm(st, HD, D, B * T, dv, 0, 1, HD, ctx, dt, D, 1, g->dW_v, D, true), "dW_v");
+    TXL_TRY(sgemm(st, HD, D, T, dr, 0, 1, HD, R, dt, D, 1, g->dW_kR, D, true), "dW_kR");
+    TXL_TRY(txl::launch_to_f32(0, dy, g->dh, BL * D, st), "copy");
+    TXL_TRY(sgemm(st, BL, D, HD, dq, 0, HD, 1, w->W_q, dt, D, 1, g->dh, D, true), "dh q");
+    TXL_TRY(sgemm(st, L, D, HD, dk + len * HD, 0, HD, 1, w->W_kE, dt, D, 1, g->dh, D, true, B,
+                  T * HD, 0, L * D), "dh k");
+    TXL_TRY(sgemm(st, L, D, HD, dv + len * HD, 0, HD, 1, w->W_v, dt, D, 1, g->dh, D, true, B,
+                  T * HD, 0, L * D), "dh v");
+  }
 #undef TXL_TRY
   return TXL_OK;
 }

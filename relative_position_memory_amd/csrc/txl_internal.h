@@ -185,6 +185,30 @@ hipError_t launch_zero_many(float* const* p, const int64_t* count, int n, hipStr
 hipError_t launch_ln_bwd(int dtype, const float* y, const void* gamma, const void* dh_out,
                          int64_t M, int64_t D, float eps, float* dy, float* mean, float* rstd,
                          float* dgamma, float* dbeta, hipStream_t s, bool zeroed = false);
+// Conversion of fp32 or bf16 operands into bf16 rows along K for the matrix
+// cores, several independent jobs per launch.  Job output: dst[r][c] (row pitch
+// ldd) = element (r, c) of the source for r < R, c < C, zero for C <= c < Cpad.
+// pack_rows: element (r, c) at src[(r / rpb) sb + (r % rpb) ld + c] (rows of
+// several batches); pack_trans: at src[c sk + r] (a transpose).  dtype 0 = fp32
+// source, 1 = bf16.  tile_end and vec are filled in by launch_pack.
+struct PackJob {
+  const void* src;
+  int64_t R, C, Cpad, rpb, sb, ld, sk;
+  uint16_t* dst;
+  int64_t ldd;
+  int dtype, trans, vec;
+  int64_t tile_end;
+};
+constexpr int PJ_MAX = 16;
+struct PackJobs {
+  PackJob j[PJ_MAX];
+  int n;
+};
+PackJob pack_rows(const void* src, int dtype, int64_t R, int64_t C, int64_t Cpad, int64_t rpb,
+                  int64_t sb, int64_t ld, uint16_t* dst, int64_t ldd);
+PackJob pack_trans(const void* src, int dtype, int64_t R, int64_t C, int64_t Cpad, int64_t sk,
+                   uint16_t* dst, int64_t ldd);
+hipError_t launch_pack(const PackJob* jobs, int n, hipStream_t s);
 // ctx [B][len + L][D] = [ring rows (oldest first) ; h]
 hipError_t launch_gather_ctx(int dtype, const void* ring, int64_t cap, int64_t start, int64_t len,
                              const void* h, int64_t B, int64_t L, int64_t D, void* ctx,
@@ -233,7 +257,8 @@ struct Epilogue {
   // EPI_HEADS: column n -> tensor (n / HD), head (n % HD) / d, element (n % HD) % d,
   //   written to dst[n / HD] + b*sb + head*sh + t*st + elem, (b, t) as in RowGather.
   void* dst0; void* dst1; int64_t HD, d, sb, sh, st;
-  // EPI_RESID_F32: y[m][n] = acc + resid[m][n]  (y fp32 [M][N], resid dtype [M][N]).
+  // EPI_RESID_F32: y[m][n] = acc + resid[m][n]  (y fp32 [M][N], resid [M][N] of
+  // the input dtype, or fp32 when resid_f32 below; no residual when resid is NULL).
   float* y; const void* resid;
   // EPI_HEADS into a ring: when t_mod > 0, row t is stored at (t_off + t) % t_mod
   // (0 <= t_off < t_mod, t < t_mod).
@@ -248,6 +273,8 @@ struct Epilogue {
   // EPI_HEADS with head-padded columns: elements d_valid .. d-1 of every head
   // row are stored as zeros (0 = every element is valid).
   int64_t d_valid;
+  // EPI_RESID_F32: the residual is fp32 (else the input dtype).
+  int resid_f32;
 };
 enum ActMode { ACT_NONE = 0, ACT_RELU = 1 };
 
@@ -263,6 +290,15 @@ struct GemmArgs {
   WeightPair w;
   Epilogue e;
 };
+// K-split partial products on the bf16 matrix cores, for outputs whose tiles
+// alone leave the GPU short of work: y[s][m][n] = sum over K slice s of
+// A[m][k] W[n][k] for s < ksplit (fp32, y + s M N; g.e.mode EPI_RESID_F32, its
+// bias and residual unused).  A and W dense bf16 rows (16-byte aligned, pitches
+// multiples of 8), K a multiple of 32 with K / 32 >= ksplit.  The caller sums
+// the partials (launch_sum_partials).
+hipError_t launch_gemm_splitk(const GemmArgs& g, int ksplit, hipStream_t s, int num_cus);
+// dst[i] = sum_{s < parts} src[s n + i] for i < n (fp32).
+hipError_t launch_sum_partials(const float* src, int parts, int64_t n, float* dst, hipStream_t s);
 
 hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
 
