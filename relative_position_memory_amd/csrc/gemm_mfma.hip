@@ -123,7 +123,9 @@ struct TileId {
 // runs on XCD w % 8, the grid is a multiple of 8 and every problem's tile
 // range starts at a multiple of 8, so tile n is always computed on XCD n % 8);
 // the column tiles of one row tile run consecutively on the same XCD, whose L2
-// then serves the A tile to all of them.
+// then serves the A tile to all of them.  That covers the row tiles of whole
+// groups of 8; the last ntm % 8 row tiles follow in plain row-major order, and
+// only the problem's tile count is padded to a multiple of 8 (tile_slots).
 template <class C>
 __device__ inline TileId tile_id(const GemmBatch& bt, int tile) {
   TileId t;
@@ -131,12 +133,26 @@ __device__ inline TileId tile_id(const GemmBatch& bt, int tile) {
   while (t.p + 1 < bt.n && tile >= bt.block_end[t.p]) ++t.p;
   const int ntm = bt.ntm[t.p], ntn = bt.ntn[t.p];
   const int bid = tile - (t.p ? bt.block_end[t.p - 1] : 0);
-  const int xcd = bid % NXCD, k_on = bid / NXCD;
-  const int tm = (k_on / ntn) * NXCD + xcd;
+  const int main_rows = ntm / NXCD * NXCD;
+  int tm, tn;
+  if (bid < main_rows * ntn) {
+    const int xcd = bid % NXCD, k_on = bid / NXCD;
+    tm = (k_on / ntn) * NXCD + xcd;
+    tn = k_on % ntn;
+  } else {
+    const int r = bid - main_rows * ntn;
+    tm = main_rows + r / ntn;
+    tn = r % ntn;
+  }
   t.valid = tm < ntm;
   t.m0 = tm * C::BM;
-  t.n0 = (k_on % ntn) * C::BN;
+  t.n0 = tn * C::BN;
   return t;
+}
+
+// Grid slots of one problem in tile_id's order: its tiles, padded to a multiple of 8.
+inline int64_t tile_slots(int64_t ntm, int64_t ntn) {
+  return (ntm * ntn + NXCD - 1) / NXCD * NXCD;
 }
 
 template <class C>
@@ -716,7 +732,7 @@ hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s, i
     bt.g[p] = gs[p];
     bt.ntm[p] = (int)((gs[p].M + C::BM - 1) / C::BM);
     bt.ntn[p] = (int)((gs[p].N + C::BN - 1) / C::BN);
-    total += (int64_t)NXCD * ((bt.ntm[p] + NXCD - 1) / NXCD) * bt.ntn[p];
+    total += tile_slots(bt.ntm[p], bt.ntn[p]);
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     bt.block_end[p] = (int)total;
     const int k = epi_kind<C>(gs[p]);
