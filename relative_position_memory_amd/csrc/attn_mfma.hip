@@ -364,42 +364,50 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
       for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
         for (int s = 0; s < 2; ++s) kf[kbk][s] = lds_b128(Kt + kbk * 16 * DP + koff[s]);
-#pragma unroll
-      for (int gm = 0; gm < 2; ++gm) {
-        // ---- position term: W^T[gm] block bw = union block bw + 1 - gm ------------------
-        f32x4 wv[5];
+      // ---- position terms of both groups; group 1's products run while group 0's
+      //      shifted stores and reads go through LDS --------------------------------------
+      f32x4 wv[2][5];
+      auto pos = [&](int gm) {
 #pragma unroll
         for (int bw = 0; bw < 5; ++bw) {
           const int u = bw + 1 - gm;
           f32x4 w = {-s_off[gm], -s_off[gm], -s_off[gm], -s_off[gm]};
           w = mfma(rf[u][0], qp[gm][0], w);
-          wv[bw] = mfma(rf[u][1], qp[gm][1], w);
+          wv[gm][bw] = mfma(rf[u][1], qp[gm][1], w);
         }
-        // The diagonal shift happens at the store: value (bw, e) is window row
-        // 16 bw + 4 g4 + e of query n16 and goes to key 16 bw + 4 g4 + e - 15 + n16
-        // (keys 0..63 only).  Blocks 0 and 4 hold keys jj and jj + 64 for the same
-        // (lane, e), and exactly one of the two is in range, so they share one
-        // unconditional store.  The buffer is reused by the next group: LDS
-        // operations of one wave complete in order, so this group's stores follow
-        // the previous group's reads.
+      };
+      auto store_w = [&](int gm) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int jj = 4 * g4 + e - 15 + n16;  // key of block 0, in -15 .. 15
-          wbuf[sp_slot(jj & (BK - 1))] = jj >= 0 ? wv[0][e] : wv[4][e];
+          wbuf[sp_slot(jj & (BK - 1))] = jj >= 0 ? wv[gm][0][e] : wv[gm][4][e];
         }
 #pragma unroll
         for (int bw = 1; bw < 4; ++bw)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wbuf[sp_slot(16 * bw + 4 * g4 + e - 15 + n16)] = wv[bw][e];
-        // ---- content term on top of the gathered position term ------------------------
+          for (int e = 0; e < 4; ++e) wbuf[sp_slot(16 * bw + 4 * g4 + e - 15 + n16)] = wv[gm][bw][e];
+      };
+      f32x4 cw[2][4];
+      auto read_w = [&](int gm) {
+#pragma unroll
+        for (int kbk = 0; kbk < 4; ++kbk)
+          cw[gm][kbk] = *(const f32x4*)(wbuf + n16 * 64 + (((4 * kbk + g4 + sprot) & 15) << 2));
+      };
+      pos(0);
+      store_w(0);
+      pos(1);
+      read_w(0);
+      store_w(1);  // (after group 0's reads: one wave's LDS operations complete in order)
+      read_w(1);
+#pragma unroll
+      for (int gm = 0; gm < 2; ++gm)
 #pragma unroll
         for (int kbk = 0; kbk < 4; ++kbk) {
-          f32x4 c = *(const f32x4*)(wbuf + n16 * 64 + (((4 * kbk + g4 + sprot) & 15) << 2));
+          f32x4 c = cw[gm][kbk];
           c = mfma(kf[kbk][0], qc[gm][0], c);
           c = mfma(kf[kbk][1], qc[gm][1], c);
           sc[gm][kbk] = c;
         }
-      }
     }
     // the next tile's union blocks sit one ring block lower
 #pragma unroll
