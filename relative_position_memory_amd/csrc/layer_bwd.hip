@@ -82,6 +82,145 @@ __global__ __launch_bounds__(256) void ln_bwd_rows_kernel(const float* y, const 
 }
 
 // dgamma[c] += sum over a chunk of rows of dh_out yhat, dbeta[c] += sum of dh_out
+// LayerNorm backward with the row in registers, for D = 256 NJ: one wave per row,
+// lane l holding columns 256 j + 4 l .. + 3 (16-byte loads), the four row sums
+// as DPP wave reductions, the next row of the wave loaded before this one is
+// reduced.  dy fp32 (and, when dyb is set, as bf16 rows of pitch ldyb).  Each
+// workgroup adds its rows' dgamma and dbeta terms over its four waves and writes
+// them to part[block][0 / 1][D]; ln_part_sum_kernel adds the blocks.
+template <typename E, int NJ>
+__global__ __launch_bounds__(256) void ln_bwd_fused_kernel(const float* __restrict__ y,
+                                                           const void* __restrict__ gamma,
+                                                           const void* __restrict__ dh_out,
+                                                           int M, float eps, float* __restrict__ dy,
+                                                           uint16_t* __restrict__ dyb, int64_t ldyb,
+                                                           float* __restrict__ part) {
+  __shared__ float red[4][2][256 * NJ];
+  constexpr int D = 256 * NJ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float gm[NJ][4], dg[NJ][4], db[NJ][4];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gm[j][e] = ldE<E>(gamma, 256 * j + 4 * lane + e);
+      dg[j][e] = 0.f;
+      db[j][e] = 0.f;
+    }
+  auto load = [&](int m, float (&yv)[NJ][4], float (&hv)[NJ][4]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t o = (int64_t)m * D + 256 * j + 4 * lane;
+      const float4 a = *(const float4*)(y + o);
+      yv[j][0] = a.x; yv[j][1] = a.y; yv[j][2] = a.z; yv[j][3] = a.w;
+      if constexpr (std::is_same<E, float>::value) {
+        const float4 b = *(const float4*)((const float*)dh_out + o);
+        hv[j][0] = b.x; hv[j][1] = b.y; hv[j][2] = b.z; hv[j][3] = b.w;
+      } else {
+        const uint2 b = *(const uint2*)((const uint16_t*)dh_out + o);
+        hv[j][0] = bf16_to_f32((uint16_t)(b.x & 0xffffu)); hv[j][1] = bf16_to_f32((uint16_t)(b.x >> 16));
+        hv[j][2] = bf16_to_f32((uint16_t)(b.y & 0xffffu)); hv[j][3] = bf16_to_f32((uint16_t)(b.y >> 16));
+      }
+    }
+  };
+  const int stride = gridDim.x * 4;
+  int m = blockIdx.x * 4 + wave;
+  float yv[NJ][4], hv[NJ][4], yn[NJ][4], hn[NJ][4];
+  load(m < M ? m : M - 1, yv, hv);
+  for (; m < M; m += stride) {
+    const int mn = m + stride < M ? m + stride : m;
+    load(mn, yn, hn);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += yv[j][e];
+    const float mu = wave_allsum(s) / (float)D;
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v += (yv[j][e] - mu) * (yv[j][e] - mu);
+    const float rstd = rsqrtf(wave_allsum(v) / (float)D + eps);
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float yh = (yv[j][e] - mu) * rstd;
+        const float g = hv[j][e] * gm[j][e];
+        s1 += g;
+        s2 += g * yh;
+        dg[j][e] += hv[j][e] * yh;
+        db[j][e] += hv[j][e];
+        yv[j][e] = yh;  // (y hat from here on)
+      }
+    const float m1 = wave_allsum(s1) / (float)D, m2 = wave_allsum(s2) / (float)D;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (hv[j][e] * gm[j][e] - m1 - yv[j][e] * m2) * rstd;
+      const int64_t c = 256 * j + 4 * lane;
+      *(float4*)(dy + (int64_t)m * D + c) = make_float4(o[0], o[1], o[2], o[3]);
+      if (dyb)
+        *(uint2*)(dyb + (int64_t)m * ldyb + c) = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        yv[j][e] = yn[j][e];
+        hv[j][e] = hn[j][e];
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      red[wave][0][256 * j + 4 * lane + e] = dg[j][e];
+      red[wave][1][256 * j + 4 * lane + e] = db[j][e];
+    }
+  __syncthreads();
+  for (int c = tid; c < 2 * D; c += 256) {
+    const int w2 = c / D, cc = c - w2 * D;
+    part[(int64_t)blockIdx.x * 2 * D + c] = red[0][w2][cc] + red[1][w2][cc] + red[2][w2][cc] +
+                                            red[3][w2][cc];
+  }
+}
+
+// dgamma[c] = sum_b part[b][0][c], dbeta[c] = sum_b part[b][1][c]: a workgroup
+// takes 16 of the 2 D columns; thread (g, c) adds blocks 16 g' .. of its group g
+// (all 16 loads issued at once, indexes clamped), then the 16 groups add in LDS.
+__global__ __launch_bounds__(256) void ln_part_sum_kernel(const float* __restrict__ part, int blocks,
+                                                          int D, float* __restrict__ dgamma,
+                                                          float* __restrict__ dbeta) {
+  __shared__ float red[16][17];
+  const int tid = threadIdx.x, cl = tid & 15, pg = tid >> 4;
+  const int c0 = blockIdx.x * 16 + cl;
+  const int c = c0 < 2 * D ? c0 : 2 * D - 1;
+  const int per = (blocks + 15) / 16;  // <= 16 (blocks <= LN_BWD_BLOCKS)
+  float v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int b = pg * per + k;
+    const int bb = b < blocks ? b : blocks - 1;
+    v[k] = part[(int64_t)bb * 2 * D + c];
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) a += (k < per && pg * per + k < blocks) ? v[k] : 0.f;
+  red[pg][cl] = a;
+  __syncthreads();
+  if (pg == 0 && c0 < 2 * D) {
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) t += red[g][cl];
+    if (c0 < D) dgamma[c0] = t;
+    else dbeta[c0 - D] = t;
+  }
+}
+
 template <typename E>
 __global__ __launch_bounds__(256) void ln_bwd_cols_kernel(const float* y, const float* mean,
                                                           const float* rstd, const void* dh_out,
@@ -313,6 +452,47 @@ hipError_t launch_to_f32(int dtype, const void* src, float* dst, int64_t n, hipS
     hipLaunchKernelGGL(to_f32_kernel<uint16_t>, dim3(grid_for(n)), dim3(256), 0, s, src, dst, n);
   else
     hipLaunchKernelGGL(to_f32_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+bool ln_bwd_fused_ok(int64_t M, int64_t D) {
+  return D % 256 == 0 && D >= 256 && D <= 1024 && M >= 1 && M * D < 0x7fffffffLL;
+}
+
+size_t ln_bwd_part_bytes(int64_t M, int64_t D) {
+  const int64_t blocks = std::min<int64_t>((M + 3) / 4, LN_BWD_BLOCKS);
+  return (size_t)(blocks * 2 * D) * sizeof(float);
+}
+
+hipError_t launch_ln_bwd_fused(int dtype, const float* y, const void* gamma, const void* dh_out,
+                               int64_t M, int64_t D, float eps, float* dy, uint16_t* dyb,
+                               int64_t ldyb, float* part, float* dgamma, float* dbeta,
+                               hipStream_t s) {
+  if (!ln_bwd_fused_ok(M, D) || !part || (dyb && (ldyb < D || ldyb % 4 || (uintptr_t)dyb % 8)) ||
+      (uintptr_t)y % 16 || (uintptr_t)dy % 16 || (uintptr_t)dh_out % 16)
+    return hipErrorInvalidValue;
+  const int blocks = (int)std::min<int64_t>((M + 3) / 4, LN_BWD_BLOCKS);
+  const int nj = (int)(D / 256);
+  auto go = [&](auto tag, auto njc) {
+    using E = decltype(tag);
+    constexpr int NJ = decltype(njc)::value;
+    hipLaunchKernelGGL((ln_bwd_fused_kernel<E, NJ>), dim3((unsigned)blocks), dim3(256), 0, s, y,
+                       gamma, dh_out, (int)M, eps, dy, dyb, ldyb, part);
+  };
+  if (dtype == 1) {
+    if (nj == 1) go(uint16_t{}, std::integral_constant<int, 1>{});
+    else if (nj == 2) go(uint16_t{}, std::integral_constant<int, 2>{});
+    else if (nj == 3) go(uint16_t{}, std::integral_constant<int, 3>{});
+    else go(uint16_t{}, std::integral_constant<int, 4>{});
+  } else {
+    if (nj == 1) go(float{}, std::integral_constant<int, 1>{});
+    else if (nj == 2) go(float{}, std::integral_constant<int, 2>{});
+    else if (nj == 3) go(float{}, std::integral_constant<int, 3>{});
+    else go(float{}, std::integral_constant<int, 4>{});
+  }
+  static_assert(LN_BWD_BLOCKS <= 256, "ln_part_sum_kernel adds at most 16 x 16 blocks");
+  hipLaunchKernelGGL(ln_part_sum_kernel, dim3((unsigned)((2 * D + 15) / 16)), dim3(256), 0, s,
+                     part, blocks, (int)D, dgamma, dbeta);
   return hipGetLastError();
 }
 

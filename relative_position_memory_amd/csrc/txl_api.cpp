@@ -839,7 +839,7 @@ int wg_splits(int64_t M, int64_t N, int64_t K) {
 
 struct BwdWs {
   size_t fwd, hout, y, dy, mean, rstd, da, dq, dk, dv, dr, ctx, lse, attn, dyb, wot, cat, wcat,
-      pko, pkq, pkkv, pkr, part, total;
+      pko, pkq, pkkv, pkr, part, lnpart, total;
 };
 
 BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
@@ -892,6 +892,8 @@ BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
     }
   }
   w.part = take(part);
+  // per-workgroup dgamma / dbeta sums of the fused LayerNorm backward
+  w.lnpart = take(txl::ln_bwd_fused_ok(B * L, D) ? txl::ln_bwd_part_bytes(B * L, D) : 0);
   w.total = off;
   return w;
 }
@@ -1143,25 +1145,32 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
     TXL_TRY(txl::launch_to_f32(dt, h_in, y, BL * D, st), "copy");
     TXL_TRY(sgemm(st, BL, D, HD, a, dt, HD, 1, w->W_o, dt, 1, HD, y, D, true), "y");
   }
-  TXL_TRY(txl::launch_ln_bwd(dt, y, w->ln_gamma, dh_out, BL, D, dm.ln_eps, dy,
-                             (float*)(base + bw.mean), (float*)(base + bw.rstd), g->dgamma,
-                             g->dbeta, st, true), "layernorm backward");
-  // dW_o = dy^T a, da = dy W_o.  bf16 layers: both on the matrix cores, from dy
-  // as bf16 rows, W_o^T, dy^T and a^T packed in one launch
   const int64_t Kd = round_up(D, 32), Kc = round_up(3 * HD, 32);
   const int64_t Kbl = round_up(BL, 32), Kbt = round_up(B * T, 32), Kt = round_up(T, 32);
+  uint16_t* dyb = (uint16_t*)(base + bw.dyb);
+  // (D a multiple of 256: one wave per row, which also writes dy's bf16 rows)
+  const bool ln_fused = txl::ln_bwd_fused_ok(BL, D);
+  if (ln_fused)
+    TXL_TRY(txl::launch_ln_bwd_fused(dt, y, w->ln_gamma, dh_out, BL, D, dm.ln_eps, dy,
+                                     dt == 1 ? dyb : nullptr, Kd, (float*)(base + bw.lnpart),
+                                     g->dgamma, g->dbeta, st), "layernorm backward");
+  else
+    TXL_TRY(txl::launch_ln_bwd(dt, y, w->ln_gamma, dh_out, BL, D, dm.ln_eps, dy,
+                               (float*)(base + bw.mean), (float*)(base + bw.rstd), g->dgamma,
+                               g->dbeta, st, true), "layernorm backward");
+  // dW_o = dy^T a, da = dy W_o.  bf16 layers: both on the matrix cores, from dy
+  // as bf16 rows, W_o^T, dy^T and a^T packed in one launch
   float* part = (float*)(base + bw.part);
   if (dt == 1) {
-    uint16_t* dyb = (uint16_t*)(base + bw.dyb);
     uint16_t* wot = (uint16_t*)(base + bw.wot);
     uint16_t* ao = (uint16_t*)(base + bw.pko);
     uint16_t* wo = ao + D * Kbl;
     const txl::PackJob jobs[] = {
-        txl::pack_rows(dy, 0, BL, D, Kd, BL, 0, D, dyb, Kd),
         txl::pack_trans(w->W_o, 1, HD, D, Kd, HD, wot, Kd),
         txl::pack_trans(dy, 0, D, BL, Kbl, D, ao, Kbl),
-        txl::pack_trans(a, 1, HD, BL, Kbl, HD, wo, Kbl)};
-    TXL_TRY(txl::launch_pack(jobs, 4, st), "operand packs");
+        txl::pack_trans(a, 1, HD, BL, Kbl, HD, wo, Kbl),
+        txl::pack_rows(dy, 0, BL, D, Kd, BL, 0, D, dyb, Kd)};
+    TXL_TRY(txl::launch_pack(jobs, ln_fused ? 3 : 4, st), "operand packs");
     TXL_TRY(mm_bf16(st, BL, HD, Kd, dyb, wot, da, nullptr), "da");
     TXL_TRY(wg_bf16(st, D, HD, Kbl, ao, wo, g->dW_o, part), "dW_o");
   } else {

@@ -185,6 +185,17 @@ hipError_t launch_zero_many(float* const* p, const int64_t* count, int n, hipStr
 hipError_t launch_ln_bwd(int dtype, const float* y, const void* gamma, const void* dh_out,
                          int64_t M, int64_t D, float eps, float* dy, float* mean, float* rstd,
                          float* dgamma, float* dbeta, hipStream_t s, bool zeroed = false);
+// LayerNorm backward with dgamma / dbeta summed per workgroup (no atomics) for
+// D = 256, 512, 768 or 1024 (ln_bwd_fused_ok): dy fp32 [M][D], and also as bf16
+// rows of pitch ldyb when dyb is set; part is scratch of ln_bwd_part_bytes(M, D).
+// dgamma and dbeta are written (not added to).
+constexpr int LN_BWD_BLOCKS = 256;
+bool ln_bwd_fused_ok(int64_t M, int64_t D);
+size_t ln_bwd_part_bytes(int64_t M, int64_t D);
+hipError_t launch_ln_bwd_fused(int dtype, const float* y, const void* gamma, const void* dh_out,
+                               int64_t M, int64_t D, float eps, float* dy, uint16_t* dyb,
+                               int64_t ldyb, float* part, float* dgamma, float* dbeta,
+                               hipStream_t s);
 // Conversion of fp32 or bf16 operands into bf16 rows along K for the matrix
 // cores, several independent jobs per launch.  Job output: dst[r][c] (row pitch
 // ldd) = element (r, c) of the source for r < R, c < C, zero for C <= c < Cpad.

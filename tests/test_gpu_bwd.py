@@ -138,6 +138,12 @@ GRAD_NAMES = [("dh", "dh"), ("dW_q", "dW_q"), ("dW_kE", "dW_kE"), ("dW_v", "dW_v
     ("bf16", "charlm", {"B": 2, "L": 96, "M": 160, "D": 192, "H": 3, "d": 64}, 160, 37),
     # d_model above 512: the backward reuses the forward's fp32 LayerNorm input y
     ("bf16", "charlm", {"B": 2, "L": 48, "M": 64, "D": 640, "H": 8, "d": 64}, 40, 30),
+    # d_model a multiple of 256: the one-wave-per-row LayerNorm backward; 1,050 rows
+    # (more than one row per wave, a partial last workgroup), 66 rows in fp32, and
+    # four 256-column chunks per lane at d_model 1024
+    ("bf16", "charlm", {"B": 3, "L": 350, "M": 50, "D": 256, "H": 4, "d": 64}, 50, 7),
+    ("fp32", "tiny", {"B": 2, "L": 33, "M": 40, "D": 256, "H": 4, "d": 64}, 40, 5),
+    ("bf16", "charlm", {"B": 1, "L": 40, "M": 24, "D": 1024, "H": 16, "d": 64}, 24, 3),
 ])
 def test_layer_step_bwd_matches_oracle(dtype, name, over, mem_len, start):
     from tests.test_gpu_parity import _layer_setup
