@@ -33,7 +33,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int NXCD = 8;
-constexpr int MAXP = 4;
+constexpr int MAXP = 8;
 #ifndef TXL_GEMV
 #define TXL_GEMV 1
 #endif
@@ -41,9 +41,9 @@ constexpr int MAXP = 4;
 struct GemmBatch {
   GemmArgs g[MAXP];
   int ntm[MAXP], ntn[MAXP];
-  int block_end[MAXP];  // inclusive prefix sums of the problems' tile counts
+  int block_end[MAXP];  // inclusive prefix sums of the problems' tile counts (x ks)
+  int ks[MAXP];         // K splits of each output tile, >= 1 (> 1: fp32 partials)
   int n;
-  int ksplit;           // K splits per tile (a launch_gemm_splitk problem), >= 1
 };
 
 __device__ inline uint4 keep_if(uint4 v, bool keep) {
@@ -127,12 +127,15 @@ struct TileId {
 // groups of 8; the last ntm % 8 row tiles follow in plain row-major order, and
 // only the problem's tile count is padded to a multiple of 8 (tile_slots).
 template <class C>
-__device__ inline TileId tile_id(const GemmBatch& bt, int tile) {
+__device__ inline TileId tile_id(const GemmBatch& bt, int tile, int& split) {
   TileId t;
   t.p = 0;
   while (t.p + 1 < bt.n && tile >= bt.block_end[t.p]) ++t.p;
   const int ntm = bt.ntm[t.p], ntn = bt.ntn[t.p];
-  const int bid = tile - (t.p ? bt.block_end[t.p - 1] : 0);
+  // the K splits of one output tile are consecutive slots
+  const int local = tile - (t.p ? bt.block_end[t.p - 1] : 0), ks = bt.ks[t.p];
+  split = local % ks;
+  const int bid = local / ks;
   const int main_rows = ntm / NXCD * NXCD;
   int tm, tn;
   if (bid < main_rows * ntn) {
@@ -150,7 +153,8 @@ __device__ inline TileId tile_id(const GemmBatch& bt, int tile) {
   return t;
 }
 
-// Grid slots of one problem in tile_id's order: its tiles, padded to a multiple of 8.
+// Grid slots of one problem in tile_id's order: its tiles, padded to a multiple of 8
+// (times the problem's K splits).
 inline int64_t tile_slots(int64_t ntm, int64_t ntn) {
   return (ntm * ntn + NXCD - 1) / NXCD * NXCD;
 }
@@ -424,12 +428,12 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_dma_kernel(GemmBatch bt) {
 #pragma unroll
   for (int j = 0; j < C::TJ; ++j) wrow_f[j] = wn * 32 * C::TJ + 32 * j + wli;
 
-  const int ks = bt.ksplit > 1 ? bt.ksplit : 1;
-  for (int tile = blockIdx.x; tile < bt.block_end[bt.n - 1] * ks; tile += gridDim.x) {
-    const int split = tile % ks;
-    const TileId tl = tile_id<C>(bt, tile / ks);
+  for (int tile = blockIdx.x; tile < bt.block_end[bt.n - 1]; tile += gridDim.x) {
+    int split;
+    const TileId tl = tile_id<C>(bt, tile, split);
     if (!tl.valid) continue;
     const GemmArgs& g = bt.g[tl.p];
+    const int ks = bt.ks[tl.p];
     const int m0 = tl.m0, n0 = tl.n0;
     // this split's 32-deep K steps kt0 .. kt0 + nk - 1 (at least
     // floor(steps / ksplit) >= 1)
@@ -594,7 +598,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_reg_kernel(GemmBatch bt) {
   const int wli = wrow_perm(li);
 
   for (int tile = blockIdx.x; tile < bt.block_end[bt.n - 1]; tile += gridDim.x) {
-    const TileId tl = tile_id<C>(bt, tile);
+    int split;  // (always 0: the register-staged pipeline takes no K splits)
+    const TileId tl = tile_id<C>(bt, tile, split);
     if (!tl.valid) continue;
     const GemmArgs& g = bt.g[tl.p];
     const int m0 = tl.m0, n0 = tl.n0;
@@ -723,16 +728,19 @@ bool wide_rows(const GemmArgs& g) {
 bool dma_ok(const GemmArgs& g) { return g.K % 32 == 0 && wide_rows(g); }
 
 template <class C>
-hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s, int ksplit = 1) {
+hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s,
+                        const int* ksplit = nullptr) {
   GemmBatch bt{};
   int64_t total = 0;
   int epi = -1;
-  bool dma = true, wide = true;
+  bool dma = true, wide = true, split = false;
   for (int p = 0; p < n; ++p) {
     bt.g[p] = gs[p];
     bt.ntm[p] = (int)((gs[p].M + C::BM - 1) / C::BM);
     bt.ntn[p] = (int)((gs[p].N + C::BN - 1) / C::BN);
-    total += tile_slots(bt.ntm[p], bt.ntn[p]);
+    bt.ks[p] = ksplit && ksplit[p] > 1 ? ksplit[p] : 1;
+    split = split || bt.ks[p] > 1;
+    total += tile_slots(bt.ntm[p], bt.ntn[p]) * bt.ks[p];
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     bt.block_end[p] = (int)total;
     const int k = epi_kind<C>(gs[p]);
@@ -741,14 +749,11 @@ hipError_t launch_tiles(const GemmArgs* gs, int n, int num_cus, hipStream_t s, i
     wide = wide && wide_rows(gs[p]);
   }
   bt.n = n;
-  bt.ksplit = 1;
-  if (ksplit > 1) {
-    if (n != 1 || !dma || epi != EPI_STAGE_F32 || gs[0].e.mode != EPI_RESID_F32)
+  // K splits write fp32 partial tiles: the LDS-direct pipeline, staged fp32 epilogue
+  if (split && (!dma || epi != EPI_STAGE_F32)) return hipErrorInvalidValue;
+  for (int p = 0; p < n; ++p)
+    if (bt.ks[p] > 1 && (gs[p].e.mode != EPI_RESID_F32 || gs[p].K / 32 < bt.ks[p]))
       return hipErrorInvalidValue;
-    bt.ksplit = ksplit;
-    total *= ksplit;
-    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-  }
   if (total == 0) return hipSuccess;
   if (dma) return launch_epi<C, LOAD_DMA>(bt, epi, (int)total, num_cus, s);
   if (wide) return launch_epi<C, LOAD_REG>(bt, epi, (int)total, num_cus, s);
@@ -1232,19 +1237,36 @@ bool gemm_mfma_supported(const GemmArgs& g) {
   return true;
 }
 
+hipError_t launch_gemm_batch(const GemmArgs* gs, const int* ksplit, int n, hipStream_t s,
+                             int num_cus) {
+  if (n < 1 || n > MAXP || !ksplit) return hipErrorInvalidValue;
+  GemmArgs gv[MAXP];
+  int nv = 0, kv[MAXP];
+  for (int p = 0; p < n; ++p) {
+    if (ksplit[p] < 1 || gs[p].e.mode != EPI_RESID_F32 || !dma_ok(gs[p]) ||
+        !gemm_mfma_supported(gs[p]) || gs[p].K / 32 < ksplit[p] ||
+        epi_kind<Small>(gs[p]) != EPI_STAGE_F32)
+      return hipErrorInvalidValue;
+    if (gs[p].M * gs[p].N * ksplit[p] > ((int64_t)1 << 40)) return hipErrorInvalidValue;
+    if (gs[p].M == 0 || gs[p].N == 0) continue;
+    gv[nv] = gs[p];
+    if (ksplit[p] > 1) {  // partials carry neither bias nor residual
+      gv[nv].e.resid = nullptr;
+      gv[nv].e.bias = nullptr;
+    }
+    kv[nv++] = ksplit[p];
+  }
+  if (nv == 0) return hipSuccess;
+  return launch_tiles<Small>(gv, nv, num_cus, s, kv);
+}
+
 hipError_t launch_gemm_splitk(const GemmArgs& g, int ksplit, hipStream_t s, int num_cus) {
-  if (g.M == 0 || g.N == 0) return hipSuccess;
-  if (ksplit < 1 || g.e.mode != EPI_RESID_F32 || !dma_ok(g) || !gemm_mfma_supported(g) ||
-      g.K / 32 < ksplit || epi_kind<Small>(g) != EPI_STAGE_F32)
-    return hipErrorInvalidValue;
-  if (g.M * g.N * ksplit > ((int64_t)1 << 40)) return hipErrorInvalidValue;
-  if (ksplit == 1) {
-    GemmArgs g1 = g;
+  GemmArgs g1 = g;
+  if (ksplit == 1) {  // one split: y = the product itself
     g1.e.resid = nullptr;
     g1.e.bias = nullptr;
-    return launch_tiles<Small>(&g1, 1, num_cus, s);
   }
-  return launch_tiles<Small>(&g, 1, num_cus, s, ksplit);
+  return launch_gemm_batch(&g1, &ksplit, 1, s, num_cus);
 }
 
 hipError_t launch_gemm_mfma_multi(const GemmArgs* gs, int n, hipStream_t s, int num_cus) {

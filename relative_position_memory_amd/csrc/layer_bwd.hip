@@ -399,31 +399,45 @@ __global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
   }
 }
 
-// dst[i] = sum over s < parts of src[s n + i], four elements per thread.
-template <bool VEC>
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ src, int parts,
-                                                           int64_t n, float* __restrict__ dst) {
-  const int64_t q = (n + 3) / 4;
-  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < q;
+// dst[i] = sum over s < parts of src[s n + i] for each job, four elements per
+// thread (16-byte loads when the job's n and pointers allow), every part's load
+// issued before the first add (indexes of parts past the job's clamped, their
+// values dropped).
+constexpr int SJ_MAX = 8;
+struct SumJobsK {
+  const float* src[SJ_MAX];
+  float* dst[SJ_MAX];
+  int64_t n[SJ_MAX];
+  int64_t item_end[SJ_MAX];  // inclusive prefix sums of (n + 3) / 4
+  int parts[SJ_MAX], vec[SJ_MAX];
+  int nj;
+};
+
+__global__ __launch_bounds__(256) void sum_partials_kernel(SumJobsK J) {
+  const int64_t items = J.item_end[J.nj - 1];
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items;
        it += (int64_t)gridDim.x * 256) {
-    const int64_t i = 4 * it;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (VEC) {
+    int j = 0;
+    while (j + 1 < J.nj && it >= J.item_end[j]) ++j;
+    const int64_t i = 4 * (it - (j ? J.item_end[j - 1] : 0)), n = J.n[j];
+    const float* src = J.src[j];
+    const int parts = J.parts[j];
+    if (J.vec[j]) {
       float4 v[16];
 #pragma unroll
-      for (int p = 0; p < 16; ++p)
-        if (p < parts) v[p] = *(const float4*)(src + p * n + i);
+      for (int p = 0; p < 16; ++p) v[p] = *(const float4*)(src + (p < parts ? p : parts - 1) * n + i);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int p = 0; p < 16; ++p)
         if (p < parts) {
           acc.x += v[p].x; acc.y += v[p].y; acc.z += v[p].z; acc.w += v[p].w;
         }
-      *(float4*)(dst + i) = acc;
+      *(float4*)(J.dst[j] + i) = acc;
     } else {
       for (int e = 0; e < 4 && i + e < n; ++e) {
         float a = 0.f;
         for (int p = 0; p < parts; ++p) a += src[p * n + i + e];
-        dst[i + e] = a;
+        J.dst[j][i + e] = a;
       }
     }
   }
@@ -591,16 +605,34 @@ hipError_t launch_pack(const PackJob* js, int n, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_sum_partials(const float* src, int parts, int64_t n, float* dst, hipStream_t s) {
-  if (parts < 1 || parts > 16 || n < 0) return hipErrorInvalidValue;
-  if (n == 0) return hipSuccess;
-  const bool vec = n % 4 == 0 && (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0;
-  const unsigned grid = (unsigned)std::min<int64_t>(((n + 3) / 4 + 255) / 256, 65536);
-  if (vec)
-    hipLaunchKernelGGL(sum_partials_kernel<true>, dim3(grid), dim3(256), 0, s, src, parts, n, dst);
-  else
-    hipLaunchKernelGGL(sum_partials_kernel<false>, dim3(grid), dim3(256), 0, s, src, parts, n, dst);
+hipError_t launch_sum_partials_multi(const SumJob* jobs, int n, hipStream_t s) {
+  if (n < 1 || n > SJ_MAX) return hipErrorInvalidValue;
+  SumJobsK J{};
+  int64_t items = 0;
+  int nj = 0;
+  for (int x = 0; x < n; ++x) {
+    const SumJob& b = jobs[x];
+    if (b.parts < 1 || b.parts > 16 || b.n < 0 || (b.n > 0 && (!b.src || !b.dst)))
+      return hipErrorInvalidValue;
+    if (b.n == 0) continue;
+    J.src[nj] = b.src;
+    J.dst[nj] = b.dst;
+    J.n[nj] = b.n;
+    J.parts[nj] = b.parts;
+    J.vec[nj] = b.n % 4 == 0 && (uintptr_t)b.src % 16 == 0 && (uintptr_t)b.dst % 16 == 0;
+    items += (b.n + 3) / 4;
+    J.item_end[nj++] = items;
+  }
+  if (nj == 0) return hipSuccess;
+  J.nj = nj;
+  const unsigned grid = (unsigned)std::min<int64_t>((items + 255) / 256, 65536);
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(grid), dim3(256), 0, s, J);
   return hipGetLastError();
+}
+
+hipError_t launch_sum_partials(const float* src, int parts, int64_t n, float* dst, hipStream_t s) {
+  const SumJob j = {src, parts, n, dst};
+  return launch_sum_partials_multi(&j, 1, s);
 }
 
 }  // namespace txl

@@ -837,6 +837,21 @@ int wg_splits(int64_t M, int64_t N, int64_t K) {
   return ks > 1 ? (int)ks : 1;
 }
 
+// The five weight-gradient products dW [M][N] over K summed rows (K rounded up
+// to 32): dW_o, dW_q, dW_kE, dW_v, dW_kR.
+void wg_shapes(const txl_layer_dims& dm, int64_t cap, int64_t (&sh)[5][3]) {
+  const int64_t B = dm.B, L = dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head, T = cap + L;
+  const int64_t Kbl = round_up(B * L, 32), Kbt = round_up(B * T, 32), Kt = round_up(T, 32);
+  const int64_t v[5][3] = {{D, HD, Kbl}, {HD, D, Kbl}, {HD, D, Kbt}, {HD, D, Kbt}, {HD, D, Kt}};
+  for (int i = 0; i < 5; ++i)
+    for (int j = 0; j < 3; ++j) sh[i][j] = v[i][j];
+}
+// fp32 partials of one weight gradient (0 when it is not split)
+int64_t wg_part_floats(int64_t M, int64_t N, int64_t K) {
+  const int ks = wg_splits(M, N, K);
+  return ks > 1 ? ks * M * N : 0;
+}
+
 struct BwdWs {
   size_t fwd, hout, y, dy, mean, rstd, da, dq, dk, dv, dr, ctx, lse, attn, dyb, wot, cat, wcat,
       pko, pkq, pkkv, pkr, part, lnpart, total;
@@ -883,13 +898,13 @@ BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
   w.pkq = take(mc ? (size_t)((HD + D) * Kbl) * 2 : 0);
   w.pkkv = take(mc ? (size_t)((2 * HD + D) * Kbt) * 2 : 0);
   w.pkr = take(mc ? (size_t)((HD + D) * Kt) * 2 : 0);
+  // (a region per split weight gradient, taken in the backward's order; all are
+  // summed by one launch at the end)
   size_t part = 0;
   if (mc) {
-    const int64_t shapes[5][3] = {{D, HD, Kbl}, {HD, D, Kbl}, {HD, D, Kbt}, {HD, D, Kbt}, {HD, D, Kt}};
-    for (const auto& sh : shapes) {
-      const int ks = wg_splits(sh[0], sh[1], sh[2]);
-      if (ks > 1) part = std::max(part, (size_t)(ks * sh[0] * sh[1]) * 4);
-    }
+    int64_t sh[5][3];
+    wg_shapes(dm, cap, sh);
+    for (const auto& x : sh) part += wg_part_floats(x[0], x[1], x[2]) * 4;
   }
   w.part = take(part);
   // per-workgroup dgamma / dbeta sums of the fused LayerNorm backward
@@ -898,11 +913,10 @@ BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
   return w;
 }
 
-// y[m][n] = sum_k A[m][k] W[n][k] (+ resid[m][n], fp32) on the bf16 matrix cores:
-// A [M][K] and W [N][K] dense bf16 rows (K a multiple of 32 takes the LDS-direct
-// pipeline), y fp32 [M][N].
-hipError_t mm_bf16(hipStream_t st, int64_t M, int64_t N, int64_t K, const uint16_t* A,
-                   const uint16_t* W, float* y, const float* resid) {
+// Arguments of y = A W^T on the matrix cores: A [M][K] and W [N][K] bf16 rows,
+// y fp32 [M][N] (+ an fp32 residual when resid is set).
+txl::GemmArgs mm_args(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* W,
+                      float* y, const float* resid) {
   txl::GemmArgs g{};
   g.M = M; g.N = N; g.K = K;
   g.a = {nullptr, 1, 0, 0, A, M, K};
@@ -911,23 +925,21 @@ hipError_t mm_bf16(hipStream_t st, int64_t M, int64_t N, int64_t K, const uint16
   g.e.y = y;
   g.e.resid = resid;
   g.e.resid_f32 = 1;
-  return txl::launch_gemm_mfma_multi(&g, 1, st, num_cus());
+  return g;
 }
 
-// dW [M][N] = A W^T for a weight gradient: A [M][K] and W [N][K] bf16 rows (the
-// transposed operands), split along K by wg_splits into part, then summed.
-hipError_t wg_bf16(hipStream_t st, int64_t M, int64_t N, int64_t K, const uint16_t* A,
-                   const uint16_t* W, float* dW, float* part) {
-  const int ks = wg_splits(M, N, K);
-  txl::GemmArgs g{};
-  g.M = M; g.N = N; g.K = K;
-  g.a = {nullptr, 1, 0, 0, A, M, K};
-  g.w = {W, W, N, K, 0, 0};
-  g.e.mode = txl::EPI_RESID_F32;
-  g.e.y = ks > 1 ? part : dW;
-  hipError_t e = txl::launch_gemm_splitk(g, ks, st, num_cus());
-  if (e == hipSuccess && ks > 1) e = txl::launch_sum_partials(part, ks, M * N, dW, st);
-  return e;
+// A weight gradient dW [M][N] = A W^T from the transposed operands A [M][K] and
+// W [N][K]: appended to a GEMM batch (into its partial region when split, whose
+// sum goes to sums) and the partial region advanced.
+void wg_add(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* W, float* dW,
+            float*& part, txl::GemmArgs* gs, int* ks, int& n, txl::SumJob* sums, int& nsum) {
+  const int k = wg_splits(M, N, K);
+  gs[n] = mm_args(M, N, K, A, W, k > 1 ? part : dW, nullptr);
+  ks[n++] = k;
+  if (k > 1) {
+    sums[nsum++] = {part, k, M * N, dW};
+    part += k * M * N;
+  }
 }
 
 // C = alpha A B (+ C), A (m, k) at a + m*am + k*ak, B (k, n) at b + k*bk + n*bn, C row-major
@@ -1160,7 +1172,9 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
                                g->dbeta, st, true), "layernorm backward");
   // dW_o = dy^T a, da = dy W_o.  bf16 layers: both on the matrix cores, from dy
   // as bf16 rows, W_o^T, dy^T and a^T packed in one launch
-  float* part = (float*)(base + bw.part);
+  float* part_next = (float*)(base + bw.part);
+  txl::SumJob sums[5];
+  int nsum = 0;
   if (dt == 1) {
     uint16_t* wot = (uint16_t*)(base + bw.wot);
     uint16_t* ao = (uint16_t*)(base + bw.pko);
@@ -1171,8 +1185,13 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
         txl::pack_trans(a, 1, HD, BL, Kbl, HD, wo, Kbl),
         txl::pack_rows(dy, 0, BL, D, Kd, BL, 0, D, dyb, Kd)};
     TXL_TRY(txl::launch_pack(jobs, ln_fused ? 3 : 4, st), "operand packs");
-    TXL_TRY(mm_bf16(st, BL, HD, Kd, dyb, wot, da, nullptr), "da");
-    TXL_TRY(wg_bf16(st, D, HD, Kbl, ao, wo, g->dW_o, part), "dW_o");
+    // da and dW_o in one grid (dW_o's partials are summed with the others at the end)
+    txl::GemmArgs gs[2];
+    int ks[2], n = 0;
+    gs[n] = mm_args(BL, HD, Kd, dyb, wot, da, nullptr);
+    ks[n++] = 1;
+    wg_add(D, HD, Kbl, ao, wo, g->dW_o, part_next, gs, ks, n, sums, nsum);
+    TXL_TRY(txl::launch_gemm_batch(gs, ks, n, st, num_cus()), "da, dW_o");
   } else {
     TXL_TRY(sgemm(st, D, HD, BL, dy, 0, 1, D, a, dt, HD, 1, g->dW_o, HD, true), "dW_o");
     TXL_TRY(sgemm(st, BL, HD, D, dy, 0, D, 1, w->W_o, dt, HD, 1, da, HD, true), "da");
@@ -1224,11 +1243,18 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
         txl::pack_trans(w->W_kE, 1, D, HD, HD, D, wcat + HD, Kc),
         txl::pack_trans(w->W_v, 1, D, HD, Kc - 2 * HD, D, wcat + 2 * HD, Kc)};
     TXL_TRY(txl::launch_pack(jobs, 13, st), "operand packs");
-    TXL_TRY(wg_bf16(st, HD, D, Kbl, aq, wq, g->dW_q, part), "dW_q");
-    TXL_TRY(wg_bf16(st, HD, D, Kbt, ak, wc, g->dW_kE, part), "dW_kE");
-    TXL_TRY(wg_bf16(st, HD, D, Kbt, av, wc, g->dW_v, part), "dW_v");
-    TXL_TRY(wg_bf16(st, HD, D, Kt, ar, wr, g->dW_kR, part), "dW_kR");
-    TXL_TRY(mm_bf16(st, BL, D, Kc, cat, wcat, g->dh, dy), "dh");
+    // dh (its tiles the longest: first) and the four weight gradients in one grid,
+    // then every split weight gradient's partials summed in one launch
+    txl::GemmArgs gs[5];
+    int ks[5], n = 0;
+    gs[n] = mm_args(BL, D, Kc, cat, wcat, g->dh, dy);
+    ks[n++] = 1;
+    wg_add(HD, D, Kbt, ak, wc, g->dW_kE, part_next, gs, ks, n, sums, nsum);
+    wg_add(HD, D, Kbt, av, wc, g->dW_v, part_next, gs, ks, n, sums, nsum);
+    wg_add(HD, D, Kbl, aq, wq, g->dW_q, part_next, gs, ks, n, sums, nsum);
+    wg_add(HD, D, Kt, ar, wr, g->dW_kR, part_next, gs, ks, n, sums, nsum);
+    TXL_TRY(txl::launch_gemm_batch(gs, ks, n, st, num_cus()), "dh and weight gradients");
+    if (nsum) TXL_TRY(txl::launch_sum_partials_multi(sums, nsum, st), "weight-gradient sums");
   } else {
     TXL_TRY(sgemm(st, HD, D, BL, dq, 0, 1, HD, h_in, dt, D, 1, g->dW_q, D, true), "dW_q");
     TXL_TRY(sgemm(st, HD, D, B * T, dk, 0, 1, HD, ctx, dt, D, 1, g->dW_kE, D, true), "dW_kE");

@@ -308,8 +308,20 @@ struct GemmArgs {
 // multiples of 8), K a multiple of 32 with K / 32 >= ksplit.  The caller sums
 // the partials (launch_sum_partials).
 hipError_t launch_gemm_splitk(const GemmArgs& g, int ksplit, hipStream_t s, int num_cus);
+// Up to 8 such problems in one grid (128 x 128 tiles), problem p split ksplit[p]
+// ways (1: y = the product, with bias and residual; more: partials as above).
+hipError_t launch_gemm_batch(const GemmArgs* gs, const int* ksplit, int n, hipStream_t s,
+                             int num_cus);
 // dst[i] = sum_{s < parts} src[s n + i] for i < n (fp32).
 hipError_t launch_sum_partials(const float* src, int parts, int64_t n, float* dst, hipStream_t s);
+// The same for up to 8 independent (src, parts, n, dst) sums in one launch.
+struct SumJob {
+  const float* src;
+  int parts;
+  int64_t n;
+  float* dst;
+};
+hipError_t launch_sum_partials_multi(const SumJob* jobs, int n, hipStream_t s);
 
 hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
 
