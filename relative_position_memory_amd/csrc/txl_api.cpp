@@ -827,28 +827,33 @@ int txl_rel_attn_bwd(void* stream, int dtype, int64_t B, int64_t H, int64_t L, i
 // ---- layer step backward --------------------------------------------------------------
 namespace {
 
-// K splits of a weight-gradient product dW [M][N] summed over K rows: about one
-// workgroup of 128 x 128 outputs per CU of a 256-CU chip, each split at least 8
-// steps of 32 (a fixed rule, so the workspace does not depend on the device).
-int wg_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  int64_t ks = (256 + tiles - 1) / tiles;
-  ks = std::min<int64_t>(ks, std::min<int64_t>(K / 32 / 8, 16));
+// K splits of a weight-gradient product summed over K rows that shares a grid
+// with an unsplit product of depth Kref (da for dW_o, dh for the others): enough
+// that no split is deeper than that product's tiles, at most 16 and at least 32
+// rows deep.  (Splits exist only to balance that grid; each costs its partial's
+// write and read.)  A fixed rule of the dims, so the workspace does not depend
+// on the device.
+int wg_splits(int64_t K, int64_t Kref) {
+  int64_t ks = (K + Kref - 1) / std::max<int64_t>(Kref, 32);
+  ks = std::min<int64_t>(ks, std::min<int64_t>(K / 32, 16));
   return ks > 1 ? (int)ks : 1;
 }
 
 // The five weight-gradient products dW [M][N] over K summed rows (K rounded up
-// to 32): dW_o, dW_q, dW_kE, dW_v, dW_kR.
-void wg_shapes(const txl_layer_dims& dm, int64_t cap, int64_t (&sh)[5][3]) {
+// to 32), each with the depth Kref of the unsplit product of its grid: dW_o
+// (with da: K = d_model), dW_q, dW_kE, dW_v, dW_kR (with dh: K = 3 HD).
+void wg_shapes(const txl_layer_dims& dm, int64_t cap, int64_t (&sh)[5][4]) {
   const int64_t B = dm.B, L = dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head, T = cap + L;
   const int64_t Kbl = round_up(B * L, 32), Kbt = round_up(B * T, 32), Kt = round_up(T, 32);
-  const int64_t v[5][3] = {{D, HD, Kbl}, {HD, D, Kbl}, {HD, D, Kbt}, {HD, D, Kbt}, {HD, D, Kt}};
+  const int64_t Kd = round_up(D, 32), Kc = round_up(3 * HD, 32);
+  const int64_t v[5][4] = {{D, HD, Kbl, Kd}, {HD, D, Kbl, Kc}, {HD, D, Kbt, Kc},
+                           {HD, D, Kbt, Kc}, {HD, D, Kt, Kc}};
   for (int i = 0; i < 5; ++i)
-    for (int j = 0; j < 3; ++j) sh[i][j] = v[i][j];
+    for (int j = 0; j < 4; ++j) sh[i][j] = v[i][j];
 }
 // fp32 partials of one weight gradient (0 when it is not split)
-int64_t wg_part_floats(int64_t M, int64_t N, int64_t K) {
-  const int ks = wg_splits(M, N, K);
+int64_t wg_part_floats(int64_t M, int64_t N, int64_t K, int64_t Kref) {
+  const int ks = wg_splits(K, Kref);
   return ks > 1 ? ks * M * N : 0;
 }
 
@@ -902,9 +907,9 @@ BwdWs bwd_ws_layout(const txl_layer_dims& dm, int64_t cap, int dtype) {
   // summed by one launch at the end)
   size_t part = 0;
   if (mc) {
-    int64_t sh[5][3];
+    int64_t sh[5][4];
     wg_shapes(dm, cap, sh);
-    for (const auto& x : sh) part += wg_part_floats(x[0], x[1], x[2]) * 4;
+    for (const auto& x : sh) part += wg_part_floats(x[0], x[1], x[2], x[3]) * 4;
   }
   w.part = take(part);
   // per-workgroup dgamma / dbeta sums of the fused LayerNorm backward
@@ -931,9 +936,10 @@ txl::GemmArgs mm_args(int64_t M, int64_t N, int64_t K, const uint16_t* A, const 
 // A weight gradient dW [M][N] = A W^T from the transposed operands A [M][K] and
 // W [N][K]: appended to a GEMM batch (into its partial region when split, whose
 // sum goes to sums) and the partial region advanced.
-void wg_add(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* W, float* dW,
-            float*& part, txl::GemmArgs* gs, int* ks, int& n, txl::SumJob* sums, int& nsum) {
-  const int k = wg_splits(M, N, K);
+void wg_add(int64_t M, int64_t N, int64_t K, int64_t Kref, const uint16_t* A, const uint16_t* W,
+            float* dW, float*& part, txl::GemmArgs* gs, int* ks, int& n, txl::SumJob* sums,
+            int& nsum) {
+  const int k = wg_splits(K, Kref);
   gs[n] = mm_args(M, N, K, A, W, k > 1 ? part : dW, nullptr);
   ks[n++] = k;
   if (k > 1) {
@@ -1190,7 +1196,7 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
     int ks[2], n = 0;
     gs[n] = mm_args(BL, HD, Kd, dyb, wot, da, nullptr);
     ks[n++] = 1;
-    wg_add(D, HD, Kbl, ao, wo, g->dW_o, part_next, gs, ks, n, sums, nsum);
+    wg_add(D, HD, Kbl, Kd, ao, wo, g->dW_o, part_next, gs, ks, n, sums, nsum);
     TXL_TRY(txl::launch_gemm_batch(gs, ks, n, st, num_cus()), "da, dW_o");
   } else {
     TXL_TRY(sgemm(st, D, HD, BL, dy, 0, 1, D, a, dt, HD, 1, g->dW_o, HD, true), "dW_o");
@@ -1249,10 +1255,10 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
     int ks[5], n = 0;
     gs[n] = mm_args(BL, D, Kc, cat, wcat, g->dh, dy);
     ks[n++] = 1;
-    wg_add(HD, D, Kbt, ak, wc, g->dW_kE, part_next, gs, ks, n, sums, nsum);
-    wg_add(HD, D, Kbt, av, wc, g->dW_v, part_next, gs, ks, n, sums, nsum);
-    wg_add(HD, D, Kbl, aq, wq, g->dW_q, part_next, gs, ks, n, sums, nsum);
-    wg_add(HD, D, Kt, ar, wr, g->dW_kR, part_next, gs, ks, n, sums, nsum);
+    wg_add(HD, D, Kbt, Kc, ak, wc, g->dW_kE, part_next, gs, ks, n, sums, nsum);
+    wg_add(HD, D, Kbt, Kc, av, wc, g->dW_v, part_next, gs, ks, n, sums, nsum);
+    wg_add(HD, D, Kbl, Kc, aq, wq, g->dW_q, part_next, gs, ks, n, sums, nsum);
+    wg_add(HD, D, Kt, Kc, ar, wr, g->dW_kR, part_next, gs, ks, n, sums, nsum);
     TXL_TRY(txl::launch_gemm_batch(gs, ks, n, st, num_cus()), "dh and weight gradients");
     if (nsum) TXL_TRY(txl::launch_sum_partials_multi(sums, nsum, st), "weight-gradient sums");
   } else {

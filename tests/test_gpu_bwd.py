@@ -134,8 +134,11 @@ GRAD_NAMES = [("dh", "dh"), ("dW_q", "dW_q"), ("dW_kE", "dW_kE"), ("dW_v", "dW_v
     ("bf16", "charlm", {"B": 2, "L": 64, "M": 64, "D": 128, "H": 2, "d": 64}, 64, 0),
     ("bf16", "charlm", {"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
     ("bf16", "charlm", {"B": 2, "L": 64, "M": 64, "D": 128, "H": 2, "d": 64}, 0, 0),  # empty memory
-    # 128-wide product tiles with a ragged half tile, K split across workgroups
+    # 128-wide product tiles with a ragged half tile
     ("bf16", "charlm", {"B": 2, "L": 96, "M": 160, "D": 192, "H": 3, "d": 64}, 160, 37),
+    # weight gradients split along their summed rows (dW_o over B L = 200 > d_model;
+    # dW_kE and dW_v over B T = 1,000 > 3 HD), partials summed after the grid
+    ("bf16", "charlm", {"B": 2, "L": 100, "M": 400, "D": 192, "H": 3, "d": 64}, 400, 123),
     # d_model above 512: the backward reuses the forward's fp32 LayerNorm input y
     ("bf16", "charlm", {"B": 2, "L": 48, "M": 64, "D": 640, "H": 8, "d": 64}, 40, 30),
     # d_model a multiple of 256: the one-wave-per-row LayerNorm backward; 1,050 rows
