@@ -430,23 +430,34 @@ __global__ __launch_bounds__(256) void attn_bwd_dr_mfma_kernel(AttnBwdArgs a, in
       // unit u: distances / columns 4 (u % 16) .. + 3 of queries 2 (u / 16), + 1
       const int u = tid + 256 * x;
       const int f4 = 4 * (u & 15), ii = 2 * (u >> 4);
+      // every load issued unconditionally (indexes clamped into the tensors, the
+      // values of pairs outside the block dropped afterwards): a per-lane test
+      // around each load made every load wait for the one before it
       float v[2][4], w[2][4];
+      uint16_t raw[2][4];
+      float4 qf[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = i0 + ii + r, ic = i < L ? i : L - 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = p0 + f4 + e, j = len + ic - p;
+          const int jc = j < 0 ? 0 : (j < T ? j : T - 1);
+          raw[r][e] = ((const uint16_t*)a.dS)[(z * L + ic) * T + jc];
+        }
+        qf[r] = *(const float4*)(a.qp + (z * L + ic) * DP + f4);
+      }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int i = i0 + ii + r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int p = p0 + f4 + e, j = len + i - p;
-          v[r][e] = (i < L && p < T && j >= 0)
-                        ? bf16_to_f32(((const uint16_t*)a.dS)[(z * L + i) * T + j])
-                        : 0.f;
+          v[r][e] = (i < L && p < T && j >= 0) ? bf16_to_f32(raw[r][e]) : 0.f;
         }
-        if (i < L) {
-          const float4 f = *(const float4*)(a.qp + (z * L + i) * DP + f4);
-          w[r][0] = f.x; w[r][1] = f.y; w[r][2] = f.z; w[r][3] = f.w;
-        } else {
-          w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0.f;
-        }
+        const bool iok = i < L;
+        w[r][0] = iok ? qf[r].x : 0.f; w[r][1] = iok ? qf[r].y : 0.f;
+        w[r][2] = iok ? qf[r].z : 0.f; w[r][3] = iok ? qf[r].w : 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
