@@ -295,6 +295,19 @@ unsigned grid_for(int64_t n) {
 __device__ inline float pk_ld(const void* p, int64_t i, int dtype) {
   return dtype ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
+// first byte of source row c of a transposed job (0 <= c < C)
+__device__ inline const char* pk_row(const PackJob& J, int64_t c) {
+  const int64_t es = J.dtype ? 2 : 4;
+  if (!J.gather) return (const char*)J.src + c * J.sk * es;
+  // (32-bit: launch_pack checks that the context's rows fit)
+  const uint32_t cc = (uint32_t)c, per = (uint32_t)J.per, b = cc / per, t = cc - b * per;
+  if (t < (uint32_t)J.len) {
+    uint32_t slot = (uint32_t)J.start + t;
+    slot = slot >= (uint32_t)J.cap ? slot - (uint32_t)J.cap : slot;
+    return (const char*)J.src + ((int64_t)b * J.cap + slot) * J.sk * es;
+  }
+  return (const char*)J.h + ((int64_t)b * J.h_rows + (t - (uint32_t)J.len)) * J.sk * es;
+}
 
 __global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
   __shared__ float t[64][65];
@@ -314,8 +327,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
           const int cl = tid / 16 + 16 * i, rl = 4 * (tid % 16);
           const int64_t c = c0 + cl, r = r0 + rl;
           const bool ok = c < J.C && r < J.R;
-          const float4 v = *(const float4*)((const float*)J.src +
-                                            (ok ? c : 0) * J.sk + (ok ? r : 0));
+          const float4 v = *(const float4*)((const float*)pk_row(J, ok ? c : 0) + (ok ? r : 0));
           t[cl][rl] = ok ? v.x : 0.f; t[cl][rl + 1] = ok ? v.y : 0.f;
           t[cl][rl + 2] = ok ? v.z : 0.f; t[cl][rl + 3] = ok ? v.w : 0.f;
         }
@@ -325,8 +337,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
           const int cl = tid / 8 + 32 * i, rl = 8 * (tid % 8);
           const int64_t c = c0 + cl, r = r0 + rl;
           const bool ok = c < J.C && r < J.R;
-          const uint4 v = *(const uint4*)((const uint16_t*)J.src +
-                                          (ok ? c : 0) * J.sk + (ok ? r : 0));
+          const uint4 v = *(const uint4*)((const uint16_t*)pk_row(J, ok ? c : 0) + (ok ? r : 0));
           const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -376,7 +387,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
       const int cl = tid / 64 + 4 * i, rl = tid % 64;
       const int64_t c = c0 + cl, r = r0 + rl;
       const bool ok = c < J.C && r < J.R;
-      const float v = pk_ld(J.src, (ok ? c : 0) * J.sk + (ok ? r : 0), J.dtype);
+      const float v = pk_ld(pk_row(J, ok ? c : 0), ok ? r : 0, J.dtype);
       t[cl][rl] = ok ? v : 0.f;
     }
     __syncthreads();
@@ -574,6 +585,20 @@ PackJob pack_trans(const void* src, int dtype, int64_t R, int64_t C, int64_t Cpa
   return j;
 }
 
+PackJob pack_trans_ctx(const void* ring, int64_t cap, int64_t start, int64_t len, const void* h,
+                       int64_t h_rows, int64_t B, int dtype, int64_t R, int64_t Cpad, int64_t sk,
+                       uint16_t* dst, int64_t ldd) {
+  PackJob j = pack_trans(ring, dtype, R, B * (len + h_rows), Cpad, sk, dst, ldd);
+  j.gather = 1;
+  j.h = h;
+  j.per = len + h_rows;
+  j.len = len;
+  j.cap = cap;
+  j.start = start;
+  j.h_rows = h_rows;
+  return j;
+}
+
 hipError_t launch_pack(const PackJob* js, int n, hipStream_t s) {
   for (int base = 0; base < n; base += PJ_MAX) {
     PackJobs b{};
@@ -584,7 +609,11 @@ hipError_t launch_pack(const PackJob* js, int n, hipStream_t s) {
           (j.dtype != 0 && j.dtype != 1) || (j.C > 0 && j.R > 0 && !j.src))
         return hipErrorInvalidValue;
       const int64_t es = j.dtype ? 2 : 4, al = 16 / es;  // elements per 16 bytes
-      const uintptr_t src = (uintptr_t)j.src, dst = (uintptr_t)j.dst;
+      if (j.gather && (!j.trans || j.per < 1 || j.len < 0 || j.len > j.cap || j.start < 0 ||
+                       j.start >= (j.cap > 0 ? j.cap : 1) || (j.per > j.len && !j.h) ||
+                       j.C > 0x7fffffffLL || j.cap > 0x7fffffffLL))
+        return hipErrorInvalidValue;
+      const uintptr_t src = (uintptr_t)j.src | (j.gather ? (uintptr_t)j.h : 0), dst = (uintptr_t)j.dst;
       bool vec = j.Cpad % 8 == 0 && j.ldd % 8 == 0 && dst % 16 == 0 && src % 16 == 0;
       if (j.trans)
         vec = vec && j.R % 8 == 0 && j.sk % al == 0;

@@ -1219,8 +1219,10 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
   txl::attn_bwd_bind(ab, base + bw.attn);
   TXL_TRY(txl::launch_attn_bwd(dt, ab, st), "attention backward");
   // projection weights: dW_q = dq^T h_in, dW_kE = dk^T ctx, dW_v = dv^T ctx, dW_kR = dr^T R
-  TXL_TRY(txl::launch_gather_ctx(dt, mem->data, mem->capacity, mem->start, len, h_in, B, L, D, ctx,
-                                 st), "context gather");
+  // (bf16 layers pack ctx^T straight from the ring and h_in instead)
+  if (dt != 1)
+    TXL_TRY(txl::launch_gather_ctx(dt, mem->data, mem->capacity, mem->start, len, h_in, B, L, D,
+                                   ctx, st), "context gather");
   // dh = dy + dq W_q + (dk W_kE + dv W_v) on the current rows (the memory's gradient is stopped)
   if (dt == 1) {
     // one launch packs the four weight gradients' operands and dh's: one product
@@ -1239,7 +1241,8 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
         txl::pack_trans(h_in, 1, D, BL, Kbl, D, wq, Kbl),
         txl::pack_trans(dk, 0, HD, B * T, Kbt, HD, ak, Kbt),
         txl::pack_trans(dv, 0, HD, B * T, Kbt, HD, av, Kbt),
-        txl::pack_trans(ctx, 1, D, B * T, Kbt, D, wc, Kbt),
+        txl::pack_trans_ctx(mem->data, mem->capacity, mem->start, len, h_in, L, B, 1, D, Kbt, D,
+                            wc, Kbt),
         txl::pack_trans(dr, 0, HD, T, Kt, HD, ar, Kt),
         txl::pack_trans(R, 1, D, T, Kt, D, wr, Kt),
         txl::pack_rows(dq, 0, BL, HD, HD, BL, 0, HD, cat, Kc),

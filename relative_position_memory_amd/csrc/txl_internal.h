@@ -209,6 +209,12 @@ struct PackJob {
   int64_t ldd;
   int dtype, trans, vec;
   int64_t tile_end;
+  // pack_trans_ctx: source row c (pitch sk) of the context [ring ; h] of batch
+  // row b = c / per, position t = c % per: ring row (start + t) mod cap of batch
+  // row b for t < len (src = the ring [B][cap]), else row t - len of h [B][h_rows]
+  int gather;
+  const void* h;
+  int64_t per, len, cap, start, h_rows;
 };
 constexpr int PJ_MAX = 16;
 struct PackJobs {
@@ -219,6 +225,12 @@ PackJob pack_rows(const void* src, int dtype, int64_t R, int64_t C, int64_t Cpad
                   int64_t sb, int64_t ld, uint16_t* dst, int64_t ldd);
 PackJob pack_trans(const void* src, int dtype, int64_t R, int64_t C, int64_t Cpad, int64_t sk,
                    uint16_t* dst, int64_t ldd);
+// pack_trans over the context rows [ring rows (oldest first) ; h] of B batch rows
+// (per = len + h_rows of them each), read where they are: dst[r][c] = context
+// row c, element r.
+PackJob pack_trans_ctx(const void* ring, int64_t cap, int64_t start, int64_t len, const void* h,
+                       int64_t h_rows, int64_t B, int dtype, int64_t R, int64_t Cpad, int64_t sk,
+                       uint16_t* dst, int64_t ldd);
 hipError_t launch_pack(const PackJob* jobs, int n, hipStream_t s);
 // ctx [B][len + L][D] = [ring rows (oldest first) ; h]
 hipError_t launch_gather_ctx(int dtype, const void* ring, int64_t cap, int64_t start, int64_t len,
