@@ -357,6 +357,21 @@ __global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
         for (int e = 0; e < 4; ++e) w[e] = pack2_bf16(t[cl + 2 * e][rl], t[cl + 2 * e + 1][rl]);
         *(uint4*)(J.dst + r * J.ldd + c) = make_uint4(w[0], w[1], w[2], w[3]);
       }
+      if (J.dst2) {  // the same tile in rows form: 8 r of one source row c per thread
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int cl = tid / 8 + 32 * i, rl = 8 * (tid % 8);
+          const int64_t c = c0 + cl, r = r0 + rl;
+          if (c >= J.C || r >= J.R) continue;
+          const int64_t b = c / J.per2, tt = c - b * J.per2;
+          if (tt < J.skip2) continue;
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = pack2_bf16(t[cl][rl + 2 * e], t[cl][rl + 2 * e + 1]);
+          *(uint4*)(J.dst2 + (b * (J.per2 - J.skip2) + tt - J.skip2) * J.ldd2 + r) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -396,6 +411,17 @@ __global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
       const int rl = tid / 64 + 4 * i, cl = tid % 64;
       const int64_t r = r0 + rl, c = c0 + cl;
       if (r < J.R && c < J.Cpad) J.dst[r * J.ldd + c] = f32_to_bf16(t[cl][rl]);
+    }
+    if (J.dst2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int cl = tid / 64 + 4 * i, rl = tid % 64;
+        const int64_t c = c0 + cl, r = r0 + rl;
+        if (c >= J.C || r >= J.R) continue;
+        const int64_t b = c / J.per2, tt = c - b * J.per2;
+        if (tt >= J.skip2)
+          J.dst2[(b * (J.per2 - J.skip2) + tt - J.skip2) * J.ldd2 + r] = f32_to_bf16(t[cl][rl]);
+      }
     }
   } else {
 #pragma unroll
@@ -615,8 +641,11 @@ hipError_t launch_pack(const PackJob* js, int n, hipStream_t s) {
         return hipErrorInvalidValue;
       const uintptr_t src = (uintptr_t)j.src | (j.gather ? (uintptr_t)j.h : 0), dst = (uintptr_t)j.dst;
       bool vec = j.Cpad % 8 == 0 && j.ldd % 8 == 0 && dst % 16 == 0 && src % 16 == 0;
+      if (j.dst2 && (!j.trans || j.per2 < 1 || j.skip2 < 0 || j.skip2 >= j.per2 || j.ldd2 < j.R))
+        return hipErrorInvalidValue;
       if (j.trans)
-        vec = vec && j.R % 8 == 0 && j.sk % al == 0;
+        vec = vec && j.R % 8 == 0 && j.sk % al == 0 &&
+              (!j.dst2 || ((uintptr_t)j.dst2 % 16 == 0 && j.ldd2 % 8 == 0));
       else
         vec = vec && j.C % 8 == 0 && j.ld % al == 0 && j.sb % al == 0;
       j.vec = vec ? 1 : 0;

@@ -1236,7 +1236,10 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
     uint16_t* wc = av + HD * Kbt;
     uint16_t* ar = (uint16_t*)(base + bw.pkr);
     uint16_t* wr = ar + HD * Kt;
-    const txl::PackJob jobs[] = {
+    // dq, dk and dv are read once: their transposes for the weight gradients also
+    // write the current rows into [dq | dk | dv] (dst2); the columns of that
+    // operand past 3 HD are zeros
+    txl::PackJob jobs[] = {
         txl::pack_trans(dq, 0, HD, BL, Kbl, HD, aq, Kbl),
         txl::pack_trans(h_in, 1, D, BL, Kbl, D, wq, Kbl),
         txl::pack_trans(dk, 0, HD, B * T, Kbt, HD, ak, Kbt),
@@ -1245,13 +1248,17 @@ static int layer_bwd_run(void* stream, int dtype, const txl_layer_dims* dims, co
                             wc, Kbt),
         txl::pack_trans(dr, 0, HD, T, Kt, HD, ar, Kt),
         txl::pack_trans(R, 1, D, T, Kt, D, wr, Kt),
-        txl::pack_rows(dq, 0, BL, HD, HD, BL, 0, HD, cat, Kc),
-        txl::pack_rows(dk + len * HD, 0, BL, HD, HD, L, T * HD, HD, cat + HD, Kc),
-        txl::pack_rows(dv + len * HD, 0, BL, HD, Kc - 2 * HD, L, T * HD, HD, cat + 2 * HD, Kc),
         txl::pack_trans(w->W_q, 1, D, HD, HD, D, wcat, Kc),
         txl::pack_trans(w->W_kE, 1, D, HD, HD, D, wcat + HD, Kc),
-        txl::pack_trans(w->W_v, 1, D, HD, Kc - 2 * HD, D, wcat + 2 * HD, Kc)};
-    TXL_TRY(txl::launch_pack(jobs, 13, st), "operand packs");
+        txl::pack_trans(w->W_v, 1, D, HD, Kc - 2 * HD, D, wcat + 2 * HD, Kc),
+        txl::pack_rows(dq, 0, BL, 0, Kc - 3 * HD, BL, 0, HD, cat + 3 * HD, Kc)};
+    auto rows_too = [&](txl::PackJob& j, uint16_t* d2, int64_t per2, int64_t skip2) {
+      j.dst2 = d2; j.ldd2 = Kc; j.per2 = per2; j.skip2 = skip2;
+    };
+    rows_too(jobs[0], cat, L, 0);
+    rows_too(jobs[2], cat + HD, T, len);
+    rows_too(jobs[3], cat + 2 * HD, T, len);
+    TXL_TRY(txl::launch_pack(jobs, Kc > 3 * HD ? 11 : 10, st), "operand packs");
     // dh (its tiles the longest: first) and the four weight gradients in one grid,
     // then every split weight gradient's partials summed in one launch
     txl::GemmArgs gs[5];

@@ -215,6 +215,11 @@ struct PackJob {
   int gather;
   const void* h;
   int64_t per, len, cap, start, h_rows;
+  // transposed jobs: also the rows form, dst2[row2][r] = element (r, c) for the
+  // source rows c with t = c mod per2 >= skip2, row2 = (c / per2) (per2 - skip2)
+  // + t - skip2 (NULL: none)
+  uint16_t* dst2;
+  int64_t ldd2, per2, skip2;
 };
 constexpr int PJ_MAX = 16;
 struct PackJobs {
