@@ -446,9 +446,15 @@ struct SumJobsK {
   float* dst[SJ_MAX];
   int64_t n[SJ_MAX];
   int64_t item_end[SJ_MAX];  // inclusive prefix sums of (n + 3) / 4
-  int parts[SJ_MAX], vec[SJ_MAX];
+  const void* resid[SJ_MAX];  // optional residual added to the sum
+  int parts[SJ_MAX], vec[SJ_MAX], rbf[SJ_MAX];
   int nj;
 };
+
+__device__ inline float sum_resid(const SumJobsK& J, int j, int64_t i) {
+  if (!J.resid[j]) return 0.f;
+  return J.rbf[j] ? bf16_to_f32(((const uint16_t*)J.resid[j])[i]) : ((const float*)J.resid[j])[i];
+}
 
 __global__ __launch_bounds__(256) void sum_partials_kernel(SumJobsK J) {
   const int64_t items = J.item_end[J.nj - 1];
@@ -469,12 +475,16 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(SumJobsK J) {
         if (p < parts) {
           acc.x += v[p].x; acc.y += v[p].y; acc.z += v[p].z; acc.w += v[p].w;
         }
+      if (J.resid[j]) {
+        acc.x += sum_resid(J, j, i); acc.y += sum_resid(J, j, i + 1);
+        acc.z += sum_resid(J, j, i + 2); acc.w += sum_resid(J, j, i + 3);
+      }
       *(float4*)(J.dst[j] + i) = acc;
     } else {
       for (int e = 0; e < 4 && i + e < n; ++e) {
         float a = 0.f;
         for (int p = 0; p < parts; ++p) a += src[p * n + i + e];
-        J.dst[j][i + e] = a;
+        J.dst[j][i + e] = a + sum_resid(J, j, i + e);
       }
     }
   }
@@ -677,6 +687,8 @@ hipError_t launch_sum_partials_multi(const SumJob* jobs, int n, hipStream_t s) {
     J.dst[nj] = b.dst;
     J.n[nj] = b.n;
     J.parts[nj] = b.parts;
+    J.resid[nj] = b.resid;
+    J.rbf[nj] = b.resid_bf16 ? 1 : 0;
     J.vec[nj] = b.n % 4 == 0 && (uintptr_t)b.src % 16 == 0 && (uintptr_t)b.dst % 16 == 0;
     items += (b.n + 3) / 4;
     J.item_end[nj++] = items;
@@ -689,7 +701,7 @@ hipError_t launch_sum_partials_multi(const SumJob* jobs, int n, hipStream_t s) {
 }
 
 hipError_t launch_sum_partials(const float* src, int parts, int64_t n, float* dst, hipStream_t s) {
-  const SumJob j = {src, parts, n, dst};
+  const SumJob j = {src, parts, n, dst, nullptr, 0};
   return launch_sum_partials_multi(&j, 1, s);
 }
 

@@ -58,8 +58,21 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // Workspace layout of txl_layer_step (byte offsets, each 256-aligned).
 struct WsLayout {
   int64_t dp;                      // padded head size of q/k/v/r rows
-  size_t q, k, v, r, a, y, part, total;  // offsets and total bytes
+  size_t q, k, v, r, a, y, part, opart, total;  // offsets and total bytes
 };
+
+// K splits of the unfused output projection y = a W_o^T + h: when its 128 x 128
+// tiles would leave most of a 256-CU chip idle (a few rows, as at a long-memory
+// evaluation segment), about 128 workgroups, each at least two K steps of 32
+// deep (a fixed rule of the dims, so the workspace does not depend on the device).
+int out_splits(const txl_layer_dims& dm) {
+  const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
+  const int64_t tiles = ((BL + 127) / 128) * ((D + 127) / 128);
+  if (tiles >= 64 || HD % 32 != 0) return 1;
+  int64_t ks = (128 + tiles - 1) / tiles;
+  ks = std::min<int64_t>(ks, std::min<int64_t>(HD / 64, 16));
+  return ks > 1 ? (int)ks : 1;
+}
 // part_bytes: room for the attention's key-split partials (0 when it does not split)
 WsLayout ws_layout(const txl_layer_dims& dm, int64_t T, int64_t es, size_t part_bytes = 0) {
   WsLayout w;
@@ -78,6 +91,9 @@ WsLayout ws_layout(const txl_layer_dims& dm, int64_t T, int64_t es, size_t part_
   w.a = take(B * L * H * dm.d_head * es);
   w.y = take(B * L * dm.d_model * 4);
   w.part = take((int64_t)part_bytes);
+  // the output projection's K-split partials (bf16 layers)
+  const int ks = out_splits(dm);
+  w.opart = take(es == 2 && ks > 1 ? ks * B * L * dm.d_model * 4 : 0);
   w.total = off;
   return w;
 }
@@ -218,7 +234,7 @@ bool out_ln_fused(int dtype, const txl_layer_dims& dm, const void* a, const txl_
 }
 
 int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
-               const void* h_in, void* h_out, float* y, hipStream_t st) {
+               const void* h_in, void* h_out, float* y, hipStream_t st, float* opart = nullptr) {
   const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
   // one fused kernel when the rows fit it
   txl::LnArgs ln{BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
@@ -234,7 +250,21 @@ int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_lay
   g.w = {w->W_o, w->W_o, D, HD};
   g.e = {txl::EPI_RESID_F32, nullptr, nullptr, 0, 1, 0, 0, 0, y, h_in};
   int rc;
-  if ((rc = run_gemm(dtype, g, st, "output projection")) != TXL_OK) return rc;
+  const int ks = out_splits(dm);
+  if (opart && ks > 1 && dtype == TXL_BF16 && txl::gemm_mfma_supported(g) && HD % 32 == 0 &&
+      (uintptr_t)a % 16 == 0 && (uintptr_t)w->W_o % 16 == 0) {
+    // few rows: K split into partials, summed with the residual into y
+    txl::GemmArgs gp = g;
+    gp.e.y = opart;
+    gp.e.resid = nullptr;
+    hipError_t e = txl::launch_gemm_splitk(gp, ks, st, num_cus());
+    if (e != hipSuccess) return hip_fail(e, "output projection");
+    const txl::SumJob sj = {opart, ks, BL * D, y, h_in, 1};
+    e = txl::launch_sum_partials_multi(&sj, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "output projection sum");
+  } else if ((rc = run_gemm(dtype, g, st, "output projection")) != TXL_OK) {
+    return rc;
+  }
   const hipError_t e =
       txl::launch_layer_norm(dtype, y, w->ln_gamma, w->ln_beta, dm.ln_eps, BL, D, h_out, st);
   if (e != hipSuccess) return hip_fail(e, "layer norm");
@@ -509,7 +539,7 @@ static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, c
   }
   if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
   if (y_written) *y_written = !out_ln_fused(dtype, dm, a, w, h_in, h_out);
-  return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st);
+  return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st, (float*)(base + ws.opart));
 }
 
 int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,

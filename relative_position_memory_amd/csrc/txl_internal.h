@@ -337,6 +337,8 @@ struct SumJob {
   int parts;
   int64_t n;
   float* dst;
+  const void* resid;  // optional: dst[i] also adds resid[i] (bf16 when resid_bf16, else fp32)
+  int resid_bf16;
 };
 hipError_t launch_sum_partials_multi(const SumJob* jobs, int n, hipStream_t s);
 
