@@ -188,6 +188,66 @@ __global__ __launch_bounds__(256) void ring_copy_flat_kernel(char* __restrict__ 
   for (int u = 0; u < RC_U; ++u) *(int4*)(ring + dst[u]) = v[u];
 }
 
+// Padded row copies (PadJob): a block is 4 waves of PAD_RPW rows of one job.
+// Lane l writes the 16-byte pieces l, l + 64, ... of its wave's rows, each from
+// four 4-byte source words (the source rows are only 4-byte aligned), the loads
+// of all rows issued before their stores; a source index past the width is
+// clamped and its value replaced by zero, so every load is unconditional.  Rows
+// past the job repeat its last row (the same values written twice).  32-bit
+// index arithmetic (the launch checks the sizes).
+constexpr int PAD_RPW = 4;
+struct PadJobsK {
+  PadJob j[PAD_MAX];
+  uint32_t block_end[PAD_MAX];  // inclusive prefix sums of the jobs' blocks
+  int n;
+};
+
+__device__ inline const uint32_t* pad_src_row(const RowGather& a, uint32_t r) {
+  const uint32_t per = (uint32_t)(a.mem_len + a.cur_rows), len = (uint32_t)a.mem_len;
+  const uint32_t b = r / per, t = r - b * per;
+  if (t < len) {
+    uint32_t slot = (uint32_t)a.mem_start + t;
+    if (slot >= (uint32_t)a.mem_cap) slot -= (uint32_t)a.mem_cap;
+    return (const uint32_t*)((const uint16_t*)a.mem + ((int64_t)b * a.mem_cap + slot) * a.lda);
+  }
+  return (const uint32_t*)((const uint16_t*)a.cur + ((int64_t)b * a.cur_rows + (t - len)) * a.lda);
+}
+
+__global__ __launch_bounds__(256) void pad_rows_kernel(PadJobsK J) {
+  int jn = 0;
+  while (jn + 1 < J.n && blockIdx.x >= J.block_end[jn]) ++jn;
+  const PadJob& p = J.j[jn];
+  const uint32_t blk = blockIdx.x - (jn ? J.block_end[jn - 1] : 0u);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint32_t R = (uint32_t)p.R, r0 = (blk * 4 + wave) * PAD_RPW;
+  const uint32_t nq = (uint32_t)(p.Cpad / 8), wsrc = (uint32_t)(p.C / 2);
+  const uint32_t* srow[PAD_RPW];
+  uint4* drow[PAD_RPW];
+#pragma unroll
+  for (int i = 0; i < PAD_RPW; ++i) {
+    const uint32_t r = r0 + i < R ? r0 + i : R - 1;
+    srow[i] = pad_src_row(p.src, r);
+    drow[i] = (uint4*)(p.dst + (int64_t)r * p.Cpad);
+  }
+  for (uint32_t q0 = 0; q0 < nq; q0 += 64) {
+    const uint32_t q = q0 + lane;
+    uint32_t v[PAD_RPW][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = 4 * q + e, ws = w < wsrc ? w : wsrc - 1;
+#pragma unroll
+      for (int i = 0; i < PAD_RPW; ++i) v[i][e] = srow[i][ws];
+    }
+#pragma unroll
+    for (int i = 0; i < PAD_RPW; ++i) {
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = 4 * q + e < wsrc ? v[i][e] : 0u;
+      if (q < nq) drow[i][q] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 __global__ void fill_kernel(float* p, int64_t n, float v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -268,6 +328,35 @@ hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0, c
   else
     hipLaunchKernelGGL(ring_copy_kernel<short>, grid, dim3(256), 0, s, (char*)ring, cap, slot0,
                        (const char*)src, src_rows, row0, rb);
+  return hipGetLastError();
+}
+
+bool pad_job_ok(const PadJob& j) {
+  const RowGather& a = j.src;
+  if (j.R < 0 || j.C < 2 || j.C > j.Cpad || (j.C & 1) || (j.Cpad & 7) || !j.dst) return false;
+  if ((uintptr_t)j.dst % 16 || j.R * j.Cpad >= ((int64_t)1 << 31)) return false;
+  const uintptr_t al = (uintptr_t)a.cur | (a.mem_len ? (uintptr_t)a.mem : 0);
+  if (a.lda < j.C || (a.lda & 1) || al % 4) return false;
+  const int64_t per = a.mem_len + a.cur_rows;
+  if (per <= 0 || a.mem_len < 0 || a.cur_rows < 0 || per >= 0x7fffffff) return false;
+  if (a.mem_len > 0 && (a.mem_cap > 0x7fffffff || a.mem_start < 0 || a.mem_start >= a.mem_cap))
+    return false;
+  return true;
+}
+
+hipError_t launch_pad_rows(const PadJob* jobs, int n, hipStream_t s) {
+  if (n < 0 || n > PAD_MAX) return hipErrorInvalidValue;
+  PadJobsK k{};
+  uint32_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!pad_job_ok(jobs[i])) return hipErrorInvalidValue;
+    if (jobs[i].R == 0) continue;
+    k.j[k.n] = jobs[i];
+    blocks += (uint32_t)((jobs[i].R + 4 * PAD_RPW - 1) / (4 * PAD_RPW));
+    k.block_end[k.n++] = blocks;
+  }
+  if (k.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pad_rows_kernel, dim3(blocks), dim3(256), 0, s, k);
   return hipGetLastError();
 }
 

@@ -59,7 +59,17 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 struct WsLayout {
   int64_t dp;                      // padded head size of q/k/v/r rows
   size_t q, k, v, r, a, y, part, opart, total;  // offsets and total bytes
+  // zero-padded operand copies (pad_k): context rows [B][T][Dp], R rows [T][Dp],
+  // W_q, W_kE, W_v, W_kR [H d][Dp] each; W_o [D][HDp] and a [B L][HDp]
+  int64_t Dp, HDp;
+  size_t xa, xr, xw, xwo, xo;
 };
+
+// bf16 products over rows that are not whole 32-element K steps (d_model or
+// H d not a multiple of 32) run on copies padded with zero columns to the next
+// multiple of 32, which the LDS-direct product takes (its K loop moves whole
+// 32-deep steps of 16-byte pieces).
+int64_t pad_k(int64_t es, int64_t K) { return es == 2 && K % 32 != 0 && K % 2 == 0 ? round_up(K, 32) : 0; }
 
 // K splits of the unfused output projection y = a W_o^T + h: when its 128 x 128
 // tiles would leave most of a 256-CU chip idle (a few rows, as at a long-memory
@@ -90,6 +100,14 @@ WsLayout ws_layout(const txl_layer_dims& dm, int64_t T, int64_t es, size_t part_
   w.r = take(H * T * w.dp * es);
   w.a = take(B * L * H * dm.d_head * es);
   w.y = take(B * L * dm.d_model * 4);
+  const int64_t D = dm.d_model, HD = H * dm.d_head;
+  w.Dp = pad_k(es, D);
+  w.HDp = pad_k(es, HD);
+  w.xa = take(w.Dp ? B * T * w.Dp * es : 0);
+  w.xr = take(w.Dp ? T * w.Dp * es : 0);
+  w.xw = take(w.Dp ? 4 * HD * w.Dp * es : 0);
+  w.xwo = take(w.HDp ? D * w.HDp * es : 0);
+  w.xo = take(w.HDp ? B * L * w.HDp * es : 0);
   w.part = take((int64_t)part_bytes);
   // the output projection's K-split partials (bf16 layers)
   const int ks = out_splits(dm);
@@ -233,8 +251,10 @@ bool out_ln_fused(int dtype, const txl_layer_dims& dm, const void* a, const txl_
   return dtype == TXL_BF16 && BL > 32 && txl::gemm_ln_supported(ln);
 }
 
+// a_pad, wo_pad: a and W_o copied to rows of HDp (zero columns past H d), or NULL.
 int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
-               const void* h_in, void* h_out, float* y, hipStream_t st, float* opart = nullptr) {
+               const void* h_in, void* h_out, float* y, hipStream_t st, float* opart = nullptr,
+               const void* a_pad = nullptr, const void* wo_pad = nullptr, int64_t HDp = 0) {
   const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
   // one fused kernel when the rows fit it
   txl::LnArgs ln{BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
@@ -249,10 +269,15 @@ int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_lay
   g.a = {nullptr, 1, 0, 0, a, BL, HD};
   g.w = {w->W_o, w->W_o, D, HD};
   g.e = {txl::EPI_RESID_F32, nullptr, nullptr, 0, 1, 0, 0, 0, y, h_in};
+  if (a_pad && wo_pad) {  // the zero columns add nothing to the sums
+    g.K = HDp;
+    g.a = {nullptr, 1, 0, 0, a_pad, BL, HDp};
+    g.w = {wo_pad, wo_pad, D, HDp};
+  }
   int rc;
   const int ks = out_splits(dm);
-  if (opart && ks > 1 && dtype == TXL_BF16 && txl::gemm_mfma_supported(g) && HD % 32 == 0 &&
-      (uintptr_t)a % 16 == 0 && (uintptr_t)w->W_o % 16 == 0) {
+  if (opart && ks > 1 && dtype == TXL_BF16 && txl::gemm_mfma_supported(g) && g.K % 32 == 0 &&
+      (uintptr_t)g.a.cur % 16 == 0 && (uintptr_t)g.w.W0 % 16 == 0) {
     // few rows: K split into partials, summed with the residual into y
     txl::GemmArgs gp = g;
     gp.e.y = opart;
@@ -510,6 +535,37 @@ static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, c
   gr.a = {nullptr, 1, 0, 0, R, T, D};
   gr.w = {w->W_kR, w->W_kR, HD, D};
   gr.e = {txl::EPI_HEADS, r, r, HD, d, 0, T * dp, dp, nullptr, nullptr, 0, 0, dp};
+  // d_model not a multiple of 32: the projections read zero-padded copies of the
+  // context rows, R and the weights (one launch), then run K = Dp
+  uint16_t* xw = (uint16_t*)(base + ws.xw);
+  const int64_t Dp = ws.Dp;
+  auto al4 = [](const void* p) { return (uintptr_t)p % 4 == 0; };
+  const bool pin = dtype == TXL_BF16 && Dp > 0 && al4(h_in) && al4(mem->data) && al4(R) &&
+                   al4(w->W_q) && al4(w->W_kE) && al4(w->W_v) && al4(w->W_kR);
+  const bool pout = dtype == TXL_BF16 && ws.HDp > 0 && al4(w->W_o) && al4(a);
+  if (pin || pout) {
+    txl::PadJob pj[7];
+    int np = 0;
+    if (pin) {
+      uint16_t* xa = (uint16_t*)(base + ws.xa);
+      pj[np++] = {{mem->data, mem->capacity, mem->start, len, h_in, L, D}, B * T, D, Dp, xa};
+      pj[np++] = {{nullptr, 1, 0, 0, R, T, D}, T, D, Dp, (uint16_t*)(base + ws.xr)};
+      const void* wsrc[4] = {w->W_q, w->W_kE, w->W_v, w->W_kR};
+      for (int i = 0; i < 4; ++i)
+        pj[np++] = {{nullptr, 1, 0, 0, wsrc[i], HD, D}, HD, D, Dp, xw + i * HD * Dp};
+      gkv.K = gq.K = gr.K = Dp;
+      gkv.a = {nullptr, 1, 0, 0, xa, T, Dp};
+      gq.a = {xa, T, len, L, nullptr, 0, Dp};  // rows len .. T-1 of each batch row
+      gr.a = {nullptr, 1, 0, 0, base + ws.xr, T, Dp};
+      gkv.w = {xw + HD * Dp, xw + 2 * HD * Dp, HD, Dp};
+      gq.w = {xw, xw, HD, Dp};
+      gr.w = {xw + 3 * HD * Dp, xw + 3 * HD * Dp, HD, Dp};
+    }
+    if (pout)
+      pj[np++] = {{nullptr, 1, 0, 0, w->W_o, D, HD}, D, HD, ws.HDp, (uint16_t*)(base + ws.xwo)};
+    const hipError_t e = txl::launch_pad_rows(pj, np, st);
+    if (e != hipSuccess) return hip_fail(e, "padded operand copies");
+  }
   head_padded_cols(gkv, 2, H, d, dp);
   head_padded_cols(gq, 1, H, d, dp);
   head_padded_cols(gr, 1, H, d, dp);
@@ -539,6 +595,15 @@ static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, c
   }
   if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
   if (y_written) *y_written = !out_ln_fused(dtype, dm, a, w, h_in, h_out);
+  if (pout && !out_ln_fused(dtype, dm, a, w, h_in, h_out)) {
+    // H d not a multiple of 32: a copied to rows of HDp for the output projection
+    const txl::PadJob pa = {{nullptr, 1, 0, 0, a, B * L, HD}, B * L, HD, ws.HDp,
+                            (uint16_t*)(base + ws.xo)};
+    const hipError_t e = txl::launch_pad_rows(&pa, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "padded attention output");
+    return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st, (float*)(base + ws.opart),
+                      base + ws.xo, base + ws.xwo, ws.HDp);
+  }
   return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st, (float*)(base + ws.opart));
 }
 

@@ -354,6 +354,19 @@ hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0,
                             int64_t B, int64_t D, hipStream_t s);
 // p[0 .. n) = value
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
+// bf16 rows copied to a wider pitch with zero columns past the source width:
+// dst[r][c] = src row r element c for c < C, 0 for C <= c < Cpad.  Source row r
+// is RowGather's logical row r (the memory ring and the current rows, or one
+// plain matrix).  C and the source pitch even, source rows 4-byte aligned; Cpad
+// a multiple of 8 and dst 16-byte aligned; R * Cpad below 2^31 (pad_job_ok).
+struct PadJob {
+  RowGather src;
+  int64_t R, C, Cpad;
+  uint16_t* dst;
+};
+constexpr int PAD_MAX = 8;
+bool pad_job_ok(const PadJob& j);
+hipError_t launch_pad_rows(const PadJob* jobs, int n, hipStream_t s);
 
 // Static device scratch of txl_rel_attn_fwd_noalloc (static_scratch.hip): its
 // size, and its address on the current device (looked up once per device).

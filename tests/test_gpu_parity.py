@@ -254,6 +254,11 @@ def test_layer_step_fp32(name, over, mem_len, start):
     ({"B": 2, "L": 100, "M": 130, "D": 96, "H": 3, "d": 32}, 130, 77),
     ({"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
     ({"B": 1, "L": 33, "M": 200, "D": 128, "H": 2, "d": 64}, 17, 190),
+    # d_model or H d not a multiple of 32: the products read zero-padded copies
+    # (an empty memory; d_model padded alone; H d padded alone, ring wrapped)
+    ({"B": 2, "L": 70, "M": 60, "D": 82, "H": 2, "d": 41}, 0, 0),
+    ({"B": 2, "L": 45, "M": 40, "D": 200, "H": 2, "d": 64}, 40, 9),
+    ({"B": 2, "L": 40, "M": 75, "D": 256, "H": 5, "d": 20}, 60, 70),
     # d_model above 512: the output projection's fp32 residual epilogue, then the
     # row LayerNorm (d_model 640 through the register kernel, 1024 the vector one)
     ({"B": 2, "L": 48, "M": 64, "D": 640, "H": 8, "d": 64}, 40, 30),
