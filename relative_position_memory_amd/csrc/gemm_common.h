@@ -87,7 +87,8 @@ hipError_t launch_gemm_mfma_multi(const GemmArgs* g, int n, hipStream_t s, int n
 bool gemm_mfma_supported(const GemmArgs& g);
 
 // h_out = LayerNorm(a W^T + bias + resid) * gamma + beta for bf16 rows of width D
-// (D % 64 == 0, D <= 512, K % 32 == 0, 16-byte aligned tensors).
+// (D <= 512 and even, K % 32 == 0; a and W 16-byte aligned; resid, gamma, beta,
+// bias and out 16-byte aligned when D % 64 == 0, else 4-byte aligned).
 struct LnArgs {
   int64_t M, D, K;        // rows, width, inner size
   const void* a;          // [M][K]

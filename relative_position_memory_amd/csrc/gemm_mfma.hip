@@ -1010,8 +1010,13 @@ hipError_t launch_skinny(const GemmArgs* gs, int n, hipStream_t s) {
 // wave w owns output columns 64 w .. 64 w + 63 (2 x 2 blocks of 32 x 32 over the
 // 64 rows), so D <= 512.  K streams through the same LDS-direct ring as above:
 // per 32-deep stage 4 KB of a and D x 64 B of W_o.
+// RAGGED: D not a multiple of 64 (even): the waves cover Dw = D rounded up to 64
+// columns (W_o rows past D repeat row D - 1), the columns past D are left out of
+// the row statistics and the stores, and the residual, gamma, beta, bias and
+// output rows, only 4-byte aligned, move in 4-byte words.
 constexpr int LBM = 64, LNW = 8, LNT = 64 * LNW, LBK = 32, LNS = 4, LDMAX = 512;
 
+template <bool RAGGED>
 __global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
   extern __shared__ __align__(16) char smem_raw[];
   uint16_t* ring = (uint16_t*)smem_raw;
@@ -1019,13 +1024,14 @@ __global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
   const int li = lane & 31, lh = lane >> 5;
   const int D = (int)p.D, K = (int)p.K, M = (int)p.M;
   const int m0 = blockIdx.x * LBM;
-  const int stage = (LBM + D) * LBK;         // bf16 elements per stage
-  const bool active = wave * 64 < D;         // this wave owns columns
+  const int Dw = RAGGED ? (D + 63) / 64 * 64 : D;  // columns the waves cover
+  const int stage = (LBM + Dw) * LBK;        // bf16 elements per stage
+  const bool active = wave * 64 < Dw;        // this wave owns columns
   const int wli = wrow_perm(li);
 
   // DMA sources: a-block loads 0..3 by waves 0..3, W loads q = wave + 8 x
   const int qa = wave < LBM / 16 ? 1 : 0;
-  const int qw = (D / 16 - wave + LNW - 1) / LNW;  // W loads of this wave (<= 4)
+  const int qw = (Dw / 16 - wave + LNW - 1) / LNW;  // W loads of this wave (<= 4)
   const uint16_t* asrc = nullptr;
   if (qa) {
     const int r = 16 * wave + (lane >> 2);
@@ -1115,23 +1121,43 @@ __global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
     for (int j = 0; j < 2; ++j) {
       const int n = wave * 64 + 32 * j + 16 * lh;
       if (!active) continue;
-      const uint4* rp = (const uint4*)((const uint16_t*)p.resid + (int64_t)mc * D + n);
-      const uint4 r0 = rp[0], r1 = rp[1];
-      const uint32_t rw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      uint32_t rw[8];
+      if (RAGGED) {  // 4-byte words, clamped to the row (past D: dropped below)
+        const uint32_t* rp = (const uint32_t*)p.resid + (int64_t)mc * (D / 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rw[e] = rp[n / 2 + e < D / 2 ? n / 2 + e : D / 2 - 1];
+      } else {
+        const uint4* rp = (const uint4*)((const uint16_t*)p.resid + (int64_t)mc * D + n);
+        const uint4 r0 = rp[0], r1 = rp[1];
+        rw[0] = r0.x; rw[1] = r0.y; rw[2] = r0.z; rw[3] = r0.w;
+        rw[4] = r1.x; rw[5] = r1.y; rw[6] = r1.z; rw[7] = r1.w;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         acc[j][i][2 * e] += bf16_to_f32((uint16_t)(rw[e] & 0xffffu));
         acc[j][i][2 * e + 1] += bf16_to_f32((uint16_t)(rw[e] >> 16));
       }
       if (p.bias) {
-        const uint4* bp = (const uint4*)((const uint16_t*)p.bias + n);
-        const uint4 b0 = bp[0], b1 = bp[1];
-        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        uint32_t bw[8];
+        if (RAGGED) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            bw[e] = ((const uint32_t*)p.bias)[n / 2 + e < D / 2 ? n / 2 + e : D / 2 - 1];
+        } else {
+          const uint4* bp = (const uint4*)((const uint16_t*)p.bias + n);
+          const uint4 b0 = bp[0], b1 = bp[1];
+          bw[0] = b0.x; bw[1] = b0.y; bw[2] = b0.z; bw[3] = b0.w;
+          bw[4] = b1.x; bw[5] = b1.y; bw[6] = b1.z; bw[7] = b1.w;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           acc[j][i][2 * e] += bf16_to_f32((uint16_t)(bw[e] & 0xffffu));
           acc[j][i][2 * e + 1] += bf16_to_f32((uint16_t)(bw[e] >> 16));
         }
+      }
+      if (RAGGED) {  // columns past D take no part in the statistics
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][i][e] = n + e < D ? acc[j][i][e] : 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) rs[i] += acc[j][i][e];
@@ -1161,7 +1187,7 @@ __global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float t = acc[j][i][e] - mean[i];
+          const float t = (!RAGGED || wave * 64 + 32 * j + 16 * lh + e < D) ? acc[j][i][e] - mean[i] : 0.f;
           rq[i] += t * t;
         }
   }
@@ -1183,11 +1209,23 @@ __global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = wave * 64 + 32 * j + 16 * lh;
-      const uint4* gp = (const uint4*)((const uint16_t*)p.gamma + n);
-      const uint4* bp = (const uint4*)((const uint16_t*)p.beta + n);
-      const uint4 g0 = gp[0], g1 = gp[1], b0 = bp[0], b1 = bp[1];
-      const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-      const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      uint32_t gw[8], bw[8];
+      if (RAGGED) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = n / 2 + e < D / 2 ? n / 2 + e : D / 2 - 1;
+          gw[e] = ((const uint32_t*)p.gamma)[c];
+          bw[e] = ((const uint32_t*)p.beta)[c];
+        }
+      } else {
+        const uint4* gp = (const uint4*)((const uint16_t*)p.gamma + n);
+        const uint4* bp = (const uint4*)((const uint16_t*)p.beta + n);
+        const uint4 g0 = gp[0], g1 = gp[1], b0 = bp[0], b1 = bp[1];
+        gw[0] = g0.x; gw[1] = g0.y; gw[2] = g0.z; gw[3] = g0.w;
+        gw[4] = g1.x; gw[5] = g1.y; gw[6] = g1.z; gw[7] = g1.w;
+        bw[0] = b0.x; bw[1] = b0.y; bw[2] = b0.z; bw[3] = b0.w;
+        bw[4] = b1.x; bw[5] = b1.y; bw[6] = b1.z; bw[7] = b1.w;
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         uint32_t pk[8];
@@ -1208,6 +1246,13 @@ __global__ __launch_bounds__(LNT, 1) void gemm_ln_kernel(LnArgs p) {
     }
   }
   __syncthreads();
+  if (RAGGED) {
+    // 4-byte words: wave w stores rows w, w + 8, ..., its lanes consecutive words
+    for (int row = wave; row < LBM && m0 + row < M; row += LNW)
+      for (int c = lane; c < D / 2; c += 64)
+        ((uint32_t*)p.out)[(int64_t)(m0 + row) * (D / 2) + c] = *(const uint32_t*)(es + row * EP + 2 * c);
+    return;
+  }
   // 16-byte chunks: D / 8 per row, rows contiguous in h_out
   const int cpr = D / 8;
   for (int q = tid; q < LBM * cpr; q += LNT) {
@@ -1291,29 +1336,37 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s, int num_cus) {
 }
 
 bool gemm_ln_supported(const LnArgs& p) {
-  if (p.D % 64 != 0 || p.D > LDMAX || p.D < 64 || p.K % LBK != 0 || p.K < LBK) return false;
+  // D a multiple of 64, or any even D (the ragged form) up to LDMAX
+  const bool ragged = p.D % 64 != 0;
+  if (p.D > LDMAX || p.D < 2 || p.D % 2 != 0 || p.K % LBK != 0 || p.K < LBK) return false;
   if (p.M < 1 || p.M > 0x7fffffffLL - LBM || p.M * p.K > 0x7fffffffLL || p.M * p.D > 0x7fffffffLL)
     return false;
-  const uintptr_t al = (uintptr_t)p.a | (uintptr_t)p.W | (uintptr_t)p.resid |
-                       (uintptr_t)p.gamma | (uintptr_t)p.beta | (uintptr_t)p.out |
-                       (uintptr_t)p.bias;
-  return al % 16 == 0;
+  const uintptr_t ops = (uintptr_t)p.a | (uintptr_t)p.W;
+  const uintptr_t rows = (uintptr_t)p.resid | (uintptr_t)p.gamma | (uintptr_t)p.beta |
+                         (uintptr_t)p.out | (uintptr_t)p.bias;
+  return ops % 16 == 0 && rows % (ragged ? 4 : 16) == 0;
 }
 
 hipError_t launch_gemm_ln(const LnArgs& p, hipStream_t s) {
-  const size_t ring = (size_t)LNS * (LBM + p.D) * LBK * sizeof(uint16_t);
+  if (!gemm_ln_supported(p)) return hipErrorInvalidValue;
+  const bool ragged = p.D % 64 != 0;
+  const int64_t Dw = (p.D + 63) / 64 * 64;
+  const size_t ring = (size_t)LNS * (LBM + Dw) * LBK * sizeof(uint16_t);
   const size_t epi = (size_t)LBM * (LDMAX + 8) * sizeof(uint16_t) + LNW * 64 * sizeof(float);
   const size_t smem = cmax(ring, epi);
-  static bool attr_set = false;
-  if (!attr_set) {
+  static bool attr_set[2] = {false, false};
+  const void* fn = ragged ? (const void*)gemm_ln_kernel<true> : (const void*)gemm_ln_kernel<false>;
+  if (!attr_set[ragged]) {
     const size_t most = cmax((size_t)LNS * (LBM + LDMAX) * LBK * sizeof(uint16_t), epi);
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_ln_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[ragged] = true;
   }
   const unsigned blocks = (unsigned)((p.M + LBM - 1) / LBM);
-  hipLaunchKernelGGL(gemm_ln_kernel, dim3(blocks), dim3(LNT), smem, s, p);
+  if (ragged)
+    hipLaunchKernelGGL(gemm_ln_kernel<true>, dim3(blocks), dim3(LNT), smem, s, p);
+  else
+    hipLaunchKernelGGL(gemm_ln_kernel<false>, dim3(blocks), dim3(LNT), smem, s, p);
   return hipGetLastError();
 }
 

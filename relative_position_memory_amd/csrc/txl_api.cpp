@@ -243,22 +243,30 @@ void head_padded_cols(txl::GemmArgs& g, int64_t nw, int64_t H, int64_t d, int64_
 // token-major; y: fp32 [B*L][D] scratch for the unfused form.
 // Whether run_out_ln takes the fused kernel (else it writes y = a W_o^T + h_in,
 // fp32, before the LayerNorm).
-bool out_ln_fused(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
-                  const void* h_in, void* h_out) {
+// a_pad, wo_pad: a and W_o copied to rows of HDp (zero columns past H d), or NULL.
+txl::LnArgs out_ln_args(const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
+                        const void* h_in, void* h_out, const void* a_pad, const void* wo_pad,
+                        int64_t HDp) {
   const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
-  txl::LnArgs ln{BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
+  if (a_pad && wo_pad)
+    return {BL, D, HDp, a_pad, wo_pad, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
+  return {BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
+}
+bool out_ln_fused(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
+                  const void* h_in, void* h_out, const void* a_pad = nullptr,
+                  const void* wo_pad = nullptr, int64_t HDp = 0) {
   // (a few rows, as in a decode step, go to the skinny GEMM and the row kernel)
-  return dtype == TXL_BF16 && BL > 32 && txl::gemm_ln_supported(ln);
+  return dtype == TXL_BF16 && dm.B * dm.L > 32 &&
+         txl::gemm_ln_supported(out_ln_args(dm, a, w, h_in, h_out, a_pad, wo_pad, HDp));
 }
 
-// a_pad, wo_pad: a and W_o copied to rows of HDp (zero columns past H d), or NULL.
 int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
                const void* h_in, void* h_out, float* y, hipStream_t st, float* opart = nullptr,
                const void* a_pad = nullptr, const void* wo_pad = nullptr, int64_t HDp = 0) {
   const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
   // one fused kernel when the rows fit it
-  txl::LnArgs ln{BL, D, HD, a, w->W_o, h_in, w->ln_gamma, w->ln_beta, dm.ln_eps, h_out};
-  if (out_ln_fused(dtype, dm, a, w, h_in, h_out)) {
+  const txl::LnArgs ln = out_ln_args(dm, a, w, h_in, h_out, a_pad, wo_pad, HDp);
+  if (out_ln_fused(dtype, dm, a, w, h_in, h_out, a_pad, wo_pad, HDp)) {
     const hipError_t e = txl::launch_gemm_ln(ln, st);
     if (e != hipSuccess) return hip_fail(e, "output projection + LayerNorm");
     return TXL_OK;
@@ -594,17 +602,18 @@ static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, c
     *lse_written = true;
   }
   if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
-  if (y_written) *y_written = !out_ln_fused(dtype, dm, a, w, h_in, h_out);
-  if (pout && !out_ln_fused(dtype, dm, a, w, h_in, h_out)) {
+  if (pout) {
     // H d not a multiple of 32: a copied to rows of HDp for the output projection
     const txl::PadJob pa = {{nullptr, 1, 0, 0, a, B * L, HD}, B * L, HD, ws.HDp,
                             (uint16_t*)(base + ws.xo)};
     const hipError_t e = txl::launch_pad_rows(&pa, 1, st);
     if (e != hipSuccess) return hip_fail(e, "padded attention output");
-    return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st, (float*)(base + ws.opart),
-                      base + ws.xo, base + ws.xwo, ws.HDp);
   }
-  return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st, (float*)(base + ws.opart));
+  const void* a_pad = pout ? base + ws.xo : nullptr;
+  const void* wo_pad = pout ? base + ws.xwo : nullptr;
+  if (y_written) *y_written = !out_ln_fused(dtype, dm, a, w, h_in, h_out, a_pad, wo_pad, ws.HDp);
+  return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st, (float*)(base + ws.opart), a_pad,
+                    wo_pad, ws.HDp);
 }
 
 int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,
