@@ -221,14 +221,19 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(PadJobsK J) {
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const uint32_t R = (uint32_t)p.R, r0 = (blk * 4 + wave) * PAD_RPW;
   const uint32_t nq = (uint32_t)(p.Cpad / 8), wsrc = (uint32_t)(p.C / 2);
-  const uint32_t* srow[PAD_RPW];
   uint4* drow[PAD_RPW];
 #pragma unroll
-  for (int i = 0; i < PAD_RPW; ++i) {
-    const uint32_t r = r0 + i < R ? r0 + i : R - 1;
-    srow[i] = pad_src_row(p.src, r);
-    drow[i] = (uint4*)(p.dst + (int64_t)r * p.Cpad);
+  for (int i = 0; i < PAD_RPW; ++i)
+    drow[i] = (uint4*)(p.dst + (int64_t)(r0 + i < R ? r0 + i : R - 1) * p.Cpad);
+  if (p.src.cur == nullptr && p.src.mem == nullptr) {  // rows of zeros
+    for (uint32_t q = lane; q < nq; q += 64)
+#pragma unroll
+      for (int i = 0; i < PAD_RPW; ++i) drow[i][q] = make_uint4(0u, 0u, 0u, 0u);
+    return;
   }
+  const uint32_t* srow[PAD_RPW];
+#pragma unroll
+  for (int i = 0; i < PAD_RPW; ++i) srow[i] = pad_src_row(p.src, r0 + i < R ? r0 + i : R - 1);
   for (uint32_t q0 = 0; q0 < nq; q0 += 64) {
     const uint32_t q = q0 + lane;
     uint32_t v[PAD_RPW][4];
@@ -333,8 +338,10 @@ hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0, c
 
 bool pad_job_ok(const PadJob& j) {
   const RowGather& a = j.src;
-  if (j.R < 0 || j.C < 2 || j.C > j.Cpad || (j.C & 1) || (j.Cpad & 7) || !j.dst) return false;
+  if (j.R < 0 || j.Cpad < 8 || (j.Cpad & 7) || !j.dst) return false;
   if ((uintptr_t)j.dst % 16 || j.R * j.Cpad >= ((int64_t)1 << 31)) return false;
+  if (a.cur == nullptr && a.mem == nullptr) return true;  // zeros
+  if (j.C < 2 || j.C > j.Cpad || (j.C & 1)) return false;
   const uintptr_t al = (uintptr_t)a.cur | (a.mem_len ? (uintptr_t)a.mem : 0);
   if (a.lda < j.C || (a.lda & 1) || al % 4) return false;
   const int64_t per = a.mem_len + a.cur_rows;

@@ -787,10 +787,38 @@ int txl_layer_step_kv(void* stream, int dtype, const txl_layer_dims* dims, const
 
 // ---- position-wise feed-forward ---------------------------------------------------------
 
+// Workspace of txl_pos_ff: f = relu(x W1^T + b1) [rows][Fp], y fp32 [rows][D]
+// (the unfused second layer), then, when d_model or d_inner is not a multiple of
+// 32 (bf16), the zero-padded operand copies: x [rows][K1], W1 [Fp][K1] (rows past
+// d_inner zero), b1 [Fp], W2 [D][Fp], with K1 = pad_k(d_model) or d_model and
+// Fp = pad_k(d_inner) or d_inner.
+struct FfWs { size_t f, y, xp, w1p, b1p, w2p, total; int64_t K1, Fp; bool pad; };
+FfWs ff_ws_layout(int64_t rows, int64_t D, int64_t Di, int64_t es) {
+  FfWs w{};
+  const int64_t Dp = pad_k(es, D), Dip = pad_k(es, Di);
+  w.K1 = Dp ? Dp : D;
+  w.Fp = Dip ? Dip : Di;
+  w.pad = (Dp > 0 || Dip > 0) && w.K1 % 32 == 0 && w.Fp % 32 == 0;
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up(bytes, 256);
+    return o;
+  };
+  w.f = take(rows * w.Fp * es);
+  w.y = take(rows * D * 4);
+  w.xp = take(w.pad && Dp ? rows * w.K1 * es : 0);
+  w.w1p = take(w.pad ? w.Fp * w.K1 * es : 0);
+  w.b1p = take(w.pad ? w.Fp * es : 0);
+  w.w2p = take(w.pad ? D * w.Fp * es : 0);
+  w.total = off;
+  return w;
+}
+
 size_t txl_pos_ff_workspace_bytes(int64_t rows, int64_t d_model, int64_t d_inner, int dtype) {
   if ((dtype != TXL_FP32 && dtype != TXL_BF16) || rows < 1 || d_model < 1 || d_inner < 1)
     return 0;
-  return (size_t)(round_up(rows * d_inner * elt_size(dtype), 256) + round_up(rows * d_model * 4, 256));
+  return ff_ws_layout(rows, d_model, d_inner, elt_size(dtype)).total;
 }
 
 int txl_pos_ff(void* stream, int dtype, int64_t rows, int64_t d_model, int64_t d_inner,
@@ -825,27 +853,52 @@ int txl_pos_ff(void* stream, int dtype, int64_t rows, int64_t d_model, int64_t d
   if (overlap(so, sws)) return fail(TXL_EINVAL, "out overlaps the workspace");
 
   char* base = (char*)workspace;
-  void* f = base;  // relu(x W1^T + b1), [rows][Di]
-  float* y = (float*)(base + round_up(rows * Di * es, 256));
+  const FfWs fw = ff_ws_layout(rows, D, Di, es);
+  void* f = base + fw.f;  // relu(x W1^T + b1), [rows][Di] (pitch Fp when padded)
+  float* y = (float*)(base + fw.y);
   hipStream_t st = (hipStream_t)stream;
+  // d_model or d_inner not a multiple of 32: both products read zero-padded copies
+  // (one launch; the padded inner columns of f come out as relu(0 + 0) = 0)
+  auto al4 = [](const void* p) { return (uintptr_t)p % 4 == 0; };
+  const bool pad = dtype == TXL_BF16 && fw.pad && al4(x) && al4(W1) && al4(b1) && al4(W2);
+  const int64_t K1 = pad ? fw.K1 : D, Fp = pad ? fw.Fp : Di;
+  const void *xa = x, *w1 = W1, *bb1 = b1, *w2 = W2;
+  if (pad) {
+    txl::PadJob pj[5];
+    int np = 0;
+    if (K1 != D) {
+      xa = base + fw.xp;
+      pj[np++] = {{nullptr, 1, 0, 0, x, rows, D}, rows, D, K1, (uint16_t*)xa};
+    }
+    uint16_t* w1p = (uint16_t*)(base + fw.w1p);
+    pj[np++] = {{nullptr, 1, 0, 0, W1, Di, D}, Di, D, K1, w1p};
+    if (Fp > Di) pj[np++] = {{}, Fp - Di, 0, K1, w1p + Di * K1};
+    pj[np++] = {{nullptr, 1, 0, 0, b1, 1, Di}, 1, Di, Fp, (uint16_t*)(base + fw.b1p)};
+    pj[np++] = {{nullptr, 1, 0, 0, W2, D, Di}, D, Di, Fp, (uint16_t*)(base + fw.w2p)};
+    const hipError_t e = txl::launch_pad_rows(pj, np, st);
+    if (e != hipSuccess) return hip_fail(e, "feed-forward padded operands");
+    w1 = w1p;
+    bb1 = base + fw.b1p;
+    w2 = base + fw.w2p;
+  }
   txl::GemmArgs g1{};
-  g1.M = rows; g1.N = Di; g1.K = D;
-  g1.a = {nullptr, 1, 0, 0, x, rows, D};
-  g1.w = {W1, W1, Di, D};
-  // row-major [rows][Di] as a single "head" of width Di
-  g1.e = {txl::EPI_HEADS, f, f, Di, Di, 0, 0, Di, nullptr, nullptr, 0, 0, 0, b1, txl::ACT_RELU};
+  g1.M = rows; g1.N = Fp; g1.K = K1;
+  g1.a = {nullptr, 1, 0, 0, xa, rows, K1};
+  g1.w = {w1, w1, Fp, K1};
+  // row-major [rows][Fp] as a single "head" of width Fp
+  g1.e = {txl::EPI_HEADS, f, f, Fp, Fp, 0, 0, Fp, nullptr, nullptr, 0, 0, 0, bb1, txl::ACT_RELU};
   int rc = run_gemm(dtype, g1, st, "feed-forward first layer");
   if (rc != TXL_OK) return rc;
-  txl::LnArgs ln{rows, D, Di, f, W2, x, ln_gamma, ln_beta, ln_eps, out, b2};
+  txl::LnArgs ln{rows, D, Fp, f, w2, x, ln_gamma, ln_beta, ln_eps, out, b2};
   if (dtype == TXL_BF16 && rows > 32 && txl::gemm_ln_supported(ln)) {
     const hipError_t e = txl::launch_gemm_ln(ln, st);
     if (e != hipSuccess) return hip_fail(e, "feed-forward second layer + LayerNorm");
     return TXL_OK;
   }
   txl::GemmArgs g2{};
-  g2.M = rows; g2.N = D; g2.K = Di;
-  g2.a = {nullptr, 1, 0, 0, f, rows, Di};
-  g2.w = {W2, W2, D, Di};
+  g2.M = rows; g2.N = D; g2.K = Fp;
+  g2.a = {nullptr, 1, 0, 0, f, rows, Fp};
+  g2.w = {w2, w2, D, Fp};
   g2.e = {txl::EPI_RESID_F32, nullptr, nullptr, 0, 1, 0, 0, 0, y, x, 0, 0, 0, b2, txl::ACT_NONE};
   if ((rc = run_gemm(dtype, g2, st, "feed-forward second layer")) != TXL_OK) return rc;
   const hipError_t e =

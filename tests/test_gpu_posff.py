@@ -33,8 +33,9 @@ def _ff_weights(rng, D, Di, dtype):
 @pytest.mark.parametrize("dtype,rows,D,Di", [
     ("fp32", 37, 40, 72),       # generic kernels
     ("bf16", 300, 512, 2048),   # matrix cores, fused second layer + LayerNorm
-    ("bf16", 77, 96, 200),      # ragged rows, unfused LayerNorm (inner size 200)
+    ("bf16", 77, 96, 200),      # ragged rows; d_inner 200 read as a zero-padded 224
     ("bf16", 150, 96, 256),     # D % 64 != 0: the fused kernel's ragged form, with bias
+    ("bf16", 300, 410, 1640),   # the 10-head word-level model's widths, both padded
     ("bf16", 100, 1024, 4096),  # D > 512: unfused LayerNorm
     ("bf16", 3, 512, 2048),     # a decode step's rows: matrix-vector products
     ("bf16", 1, 1024, 4096),    # one token of the long-memory evaluation shape
