@@ -145,6 +145,60 @@ __global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* __rest
   }
 }
 
+// out = LayerNorm(sum_p parts[p] + resid) * gamma + beta for D = 256 NV with
+// aligned rows: the K-split partial sums of the output projection, the residual
+// and the LayerNorm in one pass, laid out as layer_norm_vec_kernel (one wave per
+// row, NV 4-element chunks per lane).  y, when not NULL, receives the fp32 sum.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void layer_norm_parts_kernel(
+    const float* __restrict__ parts, int nparts, int64_t pstride, const T* __restrict__ resid,
+    const T* __restrict__ gamma, const T* __restrict__ beta, float eps, int64_t rows,
+    T* __restrict__ out, float* __restrict__ y) {
+  constexpr int D = 256 * NV;
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float4 v[NV], ga[NV], be[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int c = 4 * (lane + 64 * k);
+    v[k] = load4(resid + row * D + c);
+    ga[k] = load4(gamma + c);
+    be[k] = load4(beta + c);
+  }
+#pragma unroll 2
+  for (int p = 0; p < nparts; ++p) {
+    const float* src = parts + p * pstride + row * D;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const float4 a = load4(src + 4 * (lane + 64 * k));
+      v[k].x += a.x; v[k].y += a.y; v[k].z += a.z; v[k].w += a.w;
+    }
+  }
+  if (y) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) store4(y + row * D + 4 * (lane + 64 * k), v[k]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+  const float mean = wave_sum(s) / (float)D;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    v[k].x -= mean; v[k].y -= mean; v[k].z -= mean; v[k].w -= mean;
+    q += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
+  }
+  const float inv = rsqrtf(wave_sum(q) / (float)D + eps);
+  T* o = out + row * D;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const float4 r = make_float4(v[k].x * inv * ga[k].x + be[k].x, v[k].y * inv * ga[k].y + be[k].y,
+                                 v[k].z * inv * ga[k].z + be[k].z, v[k].w * inv * ga[k].w + be[k].w);
+    store4(o + 4 * (lane + 64 * k), r);
+  }
+}
+
 // One row of D elements per (t, b), copied with `V`-byte words.
 template <typename V>
 __global__ __launch_bounds__(256) void ring_copy_kernel(char* ring, int64_t cap, int64_t slot0,
@@ -306,6 +360,41 @@ hipError_t launch_layer_norm(int dtype, const float* y, const void* gamma, const
                        (const uint16_t*)gamma, (const uint16_t*)beta, eps, rows, D,
                        (uint16_t*)out);
   return hipGetLastError();
+}
+
+bool layer_norm_parts_ok(int dtype, const float* parts, int64_t pstride, const void* resid,
+                         const void* gamma, const void* beta, int64_t D, const void* out,
+                         const float* y) {
+  const uintptr_t f = (uintptr_t)parts | (uintptr_t)y;
+  const uintptr_t t = (uintptr_t)resid | (uintptr_t)gamma | (uintptr_t)beta | (uintptr_t)out;
+  return D % 256 == 0 && D <= 2048 && pstride % 4 == 0 && f % 16 == 0 &&
+         t % (dtype == 0 ? 16 : 8) == 0;
+}
+
+hipError_t launch_layer_norm_parts(int dtype, const float* parts, int nparts, int64_t pstride,
+                                   const void* resid, const void* gamma, const void* beta,
+                                   float eps, int64_t rows, int64_t D, void* out, float* y,
+                                   hipStream_t s) {
+  if (nparts < 1 || !layer_norm_parts_ok(dtype, parts, pstride, resid, gamma, beta, D, out, y))
+    return hipErrorInvalidValue;
+  if (rows == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+#define TXL_LNP(NV)                                                                            \
+  if (D == 256 * NV) {                                                                         \
+    if (dtype == 0)                                                                            \
+      hipLaunchKernelGGL((layer_norm_parts_kernel<float, NV>), dim3(blocks), dim3(256), 0, s,   \
+                         parts, nparts, pstride, (const float*)resid, (const float*)gamma,     \
+                         (const float*)beta, eps, rows, (float*)out, y);                       \
+    else                                                                                       \
+      hipLaunchKernelGGL((layer_norm_parts_kernel<uint16_t, NV>), dim3(blocks), dim3(256), 0,   \
+                         s, parts, nparts, pstride, (const uint16_t*)resid,                     \
+                         (const uint16_t*)gamma, (const uint16_t*)beta, eps, rows,              \
+                         (uint16_t*)out, y);                                                   \
+    return hipGetLastError();                                                                  \
+  }
+  TXL_LNP(1) TXL_LNP(2) TXL_LNP(3) TXL_LNP(4) TXL_LNP(5) TXL_LNP(6) TXL_LNP(7) TXL_LNP(8)
+#undef TXL_LNP
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0, const void* src,

@@ -74,11 +74,13 @@ int64_t pad_k(int64_t es, int64_t K) { return es == 2 && K % 32 != 0 && K % 2 ==
 // K splits of the unfused output projection y = a W_o^T + h: when its 128 x 128
 // tiles would leave most of a 256-CU chip idle (a few rows, as at a long-memory
 // evaluation segment), about 128 workgroups, each at least two K steps of 32
-// deep (a fixed rule of the dims, so the workspace does not depend on the device).
+// deep; when they would fill less than half of its 512 workgroup slots, two
+// (a fixed rule of the dims, so the workspace does not depend on the device).
 int out_splits(const txl_layer_dims& dm) {
   const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
   const int64_t tiles = ((BL + 127) / 128) * ((D + 127) / 128);
-  if (tiles >= 64 || HD % 32 != 0) return 1;
+  if (HD % 32 != 0) return 1;
+  if (tiles >= 64) return tiles < 256 && HD >= 256 ? 2 : 1;
   int64_t ks = (128 + tiles - 1) / tiles;
   ks = std::min<int64_t>(ks, std::min<int64_t>(HD / 64, 16));
   return ks > 1 ? (int)ks : 1;
@@ -260,9 +262,12 @@ bool out_ln_fused(int dtype, const txl_layer_dims& dm, const void* a, const txl_
          txl::gemm_ln_supported(out_ln_args(dm, a, w, h_in, h_out, a_pad, wo_pad, HDp));
 }
 
+// need_y: y must hold a W_o^T + h_in afterwards (the unfused form writes it anyway
+// unless the LayerNorm sums the K-split partials itself).
 int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_layer_weights* w,
                const void* h_in, void* h_out, float* y, hipStream_t st, float* opart = nullptr,
-               const void* a_pad = nullptr, const void* wo_pad = nullptr, int64_t HDp = 0) {
+               const void* a_pad = nullptr, const void* wo_pad = nullptr, int64_t HDp = 0,
+               bool need_y = true) {
   const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
   // one fused kernel when the rows fit it
   const txl::LnArgs ln = out_ln_args(dm, a, w, h_in, h_out, a_pad, wo_pad, HDp);
@@ -292,6 +297,15 @@ int run_out_ln(int dtype, const txl_layer_dims& dm, const void* a, const txl_lay
     gp.e.resid = nullptr;
     hipError_t e = txl::launch_gemm_splitk(gp, ks, st, num_cus());
     if (e != hipSuccess) return hip_fail(e, "output projection");
+    float* yo = need_y ? y : nullptr;
+    if (txl::layer_norm_parts_ok(dtype, opart, BL * D, h_in, w->ln_gamma, w->ln_beta, D, h_out,
+                                 yo)) {
+      // the partials, the residual and the LayerNorm in one pass
+      e = txl::launch_layer_norm_parts(dtype, opart, ks, BL * D, h_in, w->ln_gamma, w->ln_beta,
+                                       dm.ln_eps, BL, D, h_out, yo, st);
+      if (e != hipSuccess) return hip_fail(e, "output projection sum + layer norm");
+      return TXL_OK;
+    }
     const txl::SumJob sj = {opart, ks, BL * D, y, h_in, 1};
     e = txl::launch_sum_partials_multi(&sj, 1, st);
     if (e != hipSuccess) return hip_fail(e, "output projection sum");
@@ -613,7 +627,7 @@ static int layer_step_run(void* stream, int dtype, const txl_layer_dims* dims, c
   const void* wo_pad = pout ? base + ws.xwo : nullptr;
   if (y_written) *y_written = !out_ln_fused(dtype, dm, a, w, h_in, h_out, a_pad, wo_pad, ws.HDp);
   return run_out_ln(dtype, dm, a, w, h_in, h_out, y, st, (float*)(base + ws.opart), a_pad,
-                    wo_pad, ws.HDp);
+                    wo_pad, ws.HDp, y_written != nullptr);
 }
 
 int txl_layer_step(void* stream, int dtype, const txl_layer_dims* dims, const void* h_in,

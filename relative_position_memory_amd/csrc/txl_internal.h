@@ -348,6 +348,17 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
 // out[m] = LayerNorm(y[m]) * gamma + beta, biased variance over D.
 hipError_t launch_layer_norm(int dtype, const float* y, const void* gamma, const void* beta,
                              float eps, int64_t rows, int64_t D, void* out, hipStream_t s);
+// out[m] = LayerNorm(sum_{p < nparts} parts[p pstride + m D ..] + resid[m]) * gamma
+// + beta (fp32 partials, resid/gamma/beta/out of the dtype), and y[m] = that sum
+// when y is not NULL.  D a multiple of 256 up to 2048, 16-byte aligned fp32
+// rows (layer_norm_parts_ok).
+bool layer_norm_parts_ok(int dtype, const float* parts, int64_t pstride, const void* resid,
+                         const void* gamma, const void* beta, int64_t D, const void* out,
+                         const float* y);
+hipError_t launch_layer_norm_parts(int dtype, const float* parts, int nparts, int64_t pstride,
+                                   const void* resid, const void* gamma, const void* beta,
+                                   float eps, int64_t rows, int64_t D, void* out, float* y,
+                                   hipStream_t s);
 // ring[b][(slot0 + t) % cap] = src[b][row0 + t] for t < n, rows of D elements.
 hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0,
                             const void* src, int64_t src_rows, int64_t row0, int64_t n,

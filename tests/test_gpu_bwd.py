@@ -177,6 +177,8 @@ def test_layer_step_bwd_matches_oracle(dtype, name, over, mem_len, start):
     ("bf16", "charlm", {"B": 2, "L": 96, "M": 160, "D": 192, "H": 3, "d": 64}, 160, 37),
     ("bf16", "charlm", {"B": 3, "L": 50, "M": 50, "D": 82, "H": 2, "d": 41}, 50, 11),
     ("bf16", "charlm", {"B": 2, "L": 48, "M": 64, "D": 640, "H": 8, "d": 64}, 40, 30),
+    # K-split output projection whose LayerNorm also writes the saved y
+    ("bf16", "charlm", {"B": 1, "L": 40, "M": 24, "D": 1024, "H": 16, "d": 64}, 24, 3),
 ])
 def test_layer_step_bwd_saved_matches_recompute(dtype, name, over, mem_len, start):
     """txl_layer_step_save + txl_layer_step_bwd_saved: the forward output equals

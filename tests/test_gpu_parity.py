@@ -263,6 +263,9 @@ def test_layer_step_fp32(name, over, mem_len, start):
     # row LayerNorm (d_model 640 through the register kernel, 1024 the vector one)
     ({"B": 2, "L": 48, "M": 64, "D": 640, "H": 8, "d": 64}, 40, 30),
     ({"B": 1, "L": 128, "M": 96, "D": 1024, "H": 16, "d": 64}, 96, 5),
+    # 64 output tiles of 128 x 128: the output projection's K split in two, its
+    # partials summed by the LayerNorm
+    ({"B": 2, "L": 512, "M": 48, "D": 1024, "H": 16, "d": 64}, 48, 5),
 ])
 def test_layer_step_bf16(over, mem_len, start):
     w = I.workload("charlm", **over)
