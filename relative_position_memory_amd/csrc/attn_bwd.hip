@@ -385,6 +385,11 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s) {
   g.alpha = 1.f; g.accumulate = 0; g.a_dtype = 0; g.b_dtype = (dtype == 1 && !a.dout_f32) ? 1 : 0;
   g.bf16_mfma = dtype == 1 ? 1 : 0;  // bf16 inputs: P and dS enter the products as bf16
   g.a_dtype = dtype == 1 ? 1 : 0;     // and the matrix-core rows kernel stores them so
+  // (matrix-core path: the rows kernel writes P and dS only up to each query
+  // block's last visible key tile; the products read key j of query i only where
+  // j <= mem_len + i)
+  g.causal_on = dtype == 1 ? 1 : 0;
+  g.causal_off = a.mem_len;
   if ((e = launch_gemm_strided(g, s)) != hipSuccess) return e;
   g.A.p = a.dS;  // (bf16 path: P and dS are stored as bf16)
   g.B = {a.qc, H * a.L * DP, a.L * DP, DP, 1};

@@ -2,9 +2,10 @@
 // (Transformer-XL, section 3.3: score with content and position terms and the
 // global biases u and v; Appendix B: key j of query i at distance mem_len+i-j).
 // It replaces the fp32 rows kernel for bf16 inputs and writes the same things:
-// P and dS of every pair (here as bf16 scratch, the precision in which the
-// key-side products take them), dq, and this block's shares of du and dv; the
-// gradients sum in fp32.
+// P and dS (here as bf16 scratch, the precision in which the key-side products
+// take them; only up to each query block's last visible key tile, the products
+// taking the pairs past the diagonal as zero), dq, and this block's shares of du
+// and dv; the gradients sum in fp32.
 //
 // One workgroup = 4 waves = 64 queries of one (batch, head); wave w owns queries
 // 16 w .. 16 w + 15 of the block.  All products are v_mfma_f32_16x16x32_bf16 and
@@ -347,15 +348,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_mfma_kernel(AttnBwdArgs a, in
     }
   }
 
-  // keys past the last visible one: P = dS = 0 (the key-side products read whole rows)
-  for (int e = tid; e < BQ * (T - nkb * BK > 0 ? T - nkb * BK : 0); e += 256) {
-    const int span = T - nkb * BK;
-    const int ii = e / span, j = nkb * BK + e % span, iq = i0 + ii;
-    if (iq < L) {
-      ((uint16_t*)a.P)[((int64_t)z * L + iq) * T + j] = 0;
-      ((uint16_t*)a.dS)[((int64_t)z * L + iq) * T + j] = 0;
-    }
-  }
+  // (keys past the block's last visible key tile are left unwritten: the key-side
+  // products take P and dS as zero past the diagonal, and the position gradient
+  // reads visible pairs only)
   // dq, and this block's shares of du and dv
   if (qok) {
     float* dqrow = a.dq + (((int64_t)b * L + i) * H + h) * d;

@@ -153,6 +153,13 @@ constexpr int tile_elems() {
 template <typename T> struct Raw;
 template <> struct Raw<float> {
   float4 a, b;
+  // elements e with bit e of keep clear become 0
+  __device__ void mask(uint32_t keep) {
+    a.x = keep & 1 ? a.x : 0.f; a.y = keep & 2 ? a.y : 0.f;
+    a.z = keep & 4 ? a.z : 0.f; a.w = keep & 8 ? a.w : 0.f;
+    b.x = keep & 16 ? b.x : 0.f; b.y = keep & 32 ? b.y : 0.f;
+    b.z = keep & 64 ? b.z : 0.f; b.w = keep & 128 ? b.w : 0.f;
+  }
   __device__ uint4 packed() const {
     return make_uint4(pack_bf16_pair(a.x, a.y), pack_bf16_pair(a.z, a.w),
                       pack_bf16_pair(b.x, b.y), pack_bf16_pair(b.z, b.w));
@@ -168,6 +175,10 @@ template <> struct Raw<float> {
 };
 template <> struct Raw<uint16_t> {
   uint4 a;
+  __device__ void mask(uint32_t keep) {
+    auto m2 = [&](int e) { return (keep >> e & 1 ? 0x0000ffffu : 0u) | (keep >> (e + 1) & 1 ? 0xffff0000u : 0u); };
+    a.x &= m2(0); a.y &= m2(2); a.z &= m2(4); a.w &= m2(6);
+  }
   __device__ uint4 packed() const { return a; }
   __device__ void load(const void* p, int64_t off) { a = *(const uint4*)((const uint16_t*)p + off); }
   __device__ void set(const float* v) {
@@ -229,6 +240,28 @@ __device__ inline void stage_load(const void* p, int64_t base, int64_t sr, int64
   }
 }
 
+// Causal mask of this thread's pieces of the block at rows r0, k k0 (see
+// StridedGemm::causal_off): element (row, k) is kept when row <= k + off.
+template <typename T, int R>
+__device__ inline void stage_causal(int flags, int tid, int64_t r0, int64_t k0, int64_t off,
+                                    Raw<T> (&w)[R * KS / 2048]) {
+#pragma unroll
+  for (int x = 0; x < R * KS / 2048; ++x) {
+    const int q = tid + 256 * x;
+    uint32_t keep = 0;
+    if (flags & ST_ROWS) {  // rows r .. r + 7 at one k
+      const int64_t k = k0 + q / (R / 8), r = r0 + 8 * (q % (R / 8));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) keep |= (r + e <= k + off ? 1u : 0u) << e;
+    } else {  // k .. k + 7 of one row
+      const int64_t r = r0 + q / (KS / 8), k = k0 + 8 * (q % (KS / 8));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) keep |= (r <= k + e + off ? 1u : 0u) << e;
+    }
+    w[x].mask(keep);
+  }
+}
+
 template <typename T, int R>
 __device__ inline void stage_store(uint16_t* Xs, int flags, int tid, const Raw<T> (&w)[R * KS / 2048]) {
 #pragma unroll
@@ -267,7 +300,7 @@ __device__ inline bf16x8 frag(const uint16_t* Xs, int flags, int rb, int s, int 
 // AR, BR: the ST_ROWS bit of A's and B's staging flags, fixed per instantiation
 // (fa, fb supply the ST_VEC bit), so a kernel carries only its layouts' code.
 template <typename TA, typename TB, int RM, int RN, int AR, int BR>
-__global__ __launch_bounds__(256, RM == 64 ? 2 : 1) void gemm_strided_mfma_kernel(StridedGemm g, int ksplit, int fa_in,
+__global__ __launch_bounds__(256, RM * RN <= 128 * 64 ? 2 : 1) void gemm_strided_mfma_kernel(StridedGemm g, int ksplit, int fa_in,
                                                                 int fb_in) {
   const int fa = (AR ? ST_ROWS : 0) | (fa_in & ST_VEC), fb = (BR ? ST_ROWS : 0) | (fb_in & ST_VEC);
   constexpr int XM = RM / 32, XN = RN / 32;
@@ -278,8 +311,14 @@ __global__ __launch_bounds__(256, RM == 64 ? 2 : 1) void gemm_strided_mfma_kerne
   const int64_t z = blockIdx.z / ksplit;
   const int split = blockIdx.z % ksplit;
   const int64_t kchunk = ((g.K + ksplit - 1) / ksplit + KS - 1) / KS * KS;
-  const int64_t kbeg = split * kchunk, kend = kbeg + kchunk < g.K ? kbeg + kchunk : g.K;
+  int64_t kbeg = split * kchunk;
+  const int64_t kend = kbeg + kchunk < g.K ? kbeg + kchunk : g.K;
   const int64_t m0 = (int64_t)blockIdx.y * RM, n0 = (int64_t)blockIdx.x * RN;
+  // causal A: the steps before the first k that sees row m0 hold no visible pair
+  if (g.causal_on) {
+    const int64_t kmin = (m0 - g.causal_off) > 0 ? (m0 - g.causal_off) / KS * KS : 0;
+    kbeg = kbeg > kmin ? kbeg : (kmin < kend ? kmin : kend);
+  }
   const int64_t zq = z / g.zdiv, zr = z % g.zdiv;
   const int64_t abase = zq * g.A.s1 + zr * g.A.s2;
   const int64_t bbase = zq * g.B.s1 + zr * g.B.s2;
@@ -298,6 +337,9 @@ __global__ __launch_bounds__(256, RM == 64 ? 2 : 1) void gemm_strided_mfma_kerne
     for (int y = 0; y < XN; ++y) acc[x][y] = {0.f, 0.f, 0.f, 0.f};
   for (int64_t k0 = kbeg; k0 < kend; k0 += KS) {
     __syncthreads();  // the previous step's fragment reads are done
+    // (a step that reaches past the diagonal: pairs not visible are zeroed)
+    if (g.causal_on && m0 + RM - 1 > k0 + g.causal_off)
+      stage_causal<TA, RM>(fa, tid, m0, k0, g.causal_off, wa);
     stage_store<TA, RM>(As, fa, tid, wa);
     stage_store<TB, RN>(Bs, fb, tid, wb);
     __syncthreads();
@@ -398,9 +440,11 @@ void launch_mfma_variant(const StridedGemm& g, dim3 grid, int k, int fa, int fb,
 hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   if (g.zdiv <= 0 || g.batch > 65535) return hipErrorInvalidValue;
-  // matrix cores: 128 x 128 tiles when both output sides reach 128
+  // matrix cores: 128 x 128 tiles when both output sides reach 128, 128 x 64
+  // when only the rows do (the key-major products dk, dv of a head: N = d)
   const bool big = g.bf16_mfma && g.M >= 128 && g.N >= 128;
-  const int64_t tm = big ? 128 : 64, tn = big ? 128 : 64;
+  const bool tall = g.bf16_mfma && !big && g.M >= 128;
+  const int64_t tm = big || tall ? 128 : 64, tn = big ? 128 : 64;
   if ((g.N + tn - 1) / tn > 0x7fffffff || (g.M + tm - 1) / tm > 65535) return hipErrorInvalidValue;
   // Split K when the tiles alone leave the GPU short of workgroups (about one per
   // CU for the matrix-core kernel, four for the fp32 one; measured), each split at
@@ -424,6 +468,8 @@ hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s) {
     const int fb = stage_flags(g.B, g.B.sj, g.B.si, g.b_dtype);
     if (big)
       launch_mfma_variant<128, 128>(g, grid, k, fa, fb, s);
+    else if (tall)
+      launch_mfma_variant<128, 64>(g, grid, k, fa, fb, s);
     else
       launch_mfma_variant<64, 64>(g, grid, k, fa, fb, s);
     return hipGetLastError();

@@ -172,6 +172,11 @@ struct StridedGemm {
   // 1: the products may run on the bf16 matrix cores (operands rounded to bf16
   // as they are staged, fp32 accumulation); 0: fp32 throughout.
   int bf16_mfma;
+  // Causal A (matrix-core path): A(m, k) is taken as 0 wherever m > k + causal_off
+  // (key m is not visible to query k), whatever memory holds there, and K steps
+  // with no visible pair are skipped.
+  int causal_on;
+  int64_t causal_off;
 };
 hipError_t launch_gemm_strided(const StridedGemm& g, hipStream_t s);
 
