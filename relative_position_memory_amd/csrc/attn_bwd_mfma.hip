@@ -414,23 +414,30 @@ __global__ __launch_bounds__(256) void attn_bwd_dr_mfma_kernel(AttnBwdArgs a, in
   f32x4 acc[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) acc[cb] = {0.f, 0.f, 0.f, 0.f};
-  for (int it = split; it < items; it += nsplit) {
+  // items with a pair at these distances, in this split's order
+  auto next_item = [&](int it) {
+    for (; it < items; it += nsplit) {
+      const int i0 = (it % nqb) * 64, ilast = i0 + 63 < L - 1 ? i0 + 63 : L - 1;
+      if (p0 <= len + ilast) break;
+    }
+    return it;
+  };
+  // this thread's gathers of one item: unit u = tid + 256 x covers distances /
+  // columns 4 (u % 16) .. + 3 of queries i0 + 2 (u / 16), + 1.  Every load is
+  // issued unconditionally (indexes clamped into the tensors, the values of
+  // pairs outside the block dropped when staged): a per-lane test around each
+  // load made every load wait for the one before it.
+  struct Gath {
+    uint16_t raw[2][2][4];
+    float4 qf[2][2];
+  };
+  auto gather = [&](int it, Gath& G) {
     const int b = it / nqb, i0 = (it % nqb) * 64;
-    const int ilast = i0 + 63 < L - 1 ? i0 + 63 : L - 1;
-    if (p0 > len + ilast) continue;  // no pair of this block at these distances
     const int64_t z = (int64_t)b * H + h;
-    __syncthreads();  // the previous item's tiles are read
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      // unit u: distances / columns 4 (u % 16) .. + 3 of queries 2 (u / 16), + 1
       const int u = tid + 256 * x;
       const int f4 = 4 * (u & 15), ii = 2 * (u >> 4);
-      // every load issued unconditionally (indexes clamped into the tensors, the
-      // values of pairs outside the block dropped afterwards): a per-lane test
-      // around each load made every load wait for the one before it
-      float v[2][4], w[2][4];
-      uint16_t raw[2][4];
-      float4 qf[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int i = i0 + ii + r, ic = i < L ? i : L - 1;
@@ -438,21 +445,38 @@ __global__ __launch_bounds__(256) void attn_bwd_dr_mfma_kernel(AttnBwdArgs a, in
         for (int e = 0; e < 4; ++e) {
           const int p = p0 + f4 + e, j = len + ic - p;
           const int jc = j < 0 ? 0 : (j < T ? j : T - 1);
-          raw[r][e] = ((const uint16_t*)a.dS)[(z * L + ic) * T + jc];
+          G.raw[x][r][e] = ((const uint16_t*)a.dS)[(z * L + ic) * T + jc];
         }
-        qf[r] = *(const float4*)(a.qp + (z * L + ic) * DP + f4);
+        G.qf[x][r] = *(const float4*)(a.qp + (z * L + ic) * DP + f4);
       }
+    }
+  };
+  // the next item's gathers are in flight while this one is staged and multiplied
+  int it = next_item(split);
+  Gath cur;
+  if (it < items) gather(it, cur);
+  while (it < items) {
+    const int nit = next_item(it + nsplit);
+    Gath nxt;
+    if (nit < items) gather(nit, nxt);
+    const int i0 = (it % nqb) * 64;
+    __syncthreads();  // the previous item's tiles are read
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int u = tid + 256 * x;
+      const int f4 = 4 * (u & 15), ii = 2 * (u >> 4);
+      float v[2][4], w[2][4];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int i = i0 + ii + r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int p = p0 + f4 + e, j = len + i - p;
-          v[r][e] = (i < L && p < T && j >= 0) ? bf16_to_f32(raw[r][e]) : 0.f;
+          v[r][e] = (i < L && p < T && j >= 0) ? bf16_to_f32(cur.raw[x][r][e]) : 0.f;
         }
         const bool iok = i < L;
-        w[r][0] = iok ? qf[r].x : 0.f; w[r][1] = iok ? qf[r].y : 0.f;
-        w[r][2] = iok ? qf[r].z : 0.f; w[r][3] = iok ? qf[r].w : 0.f;
+        w[r][0] = iok ? cur.qf[x][r].x : 0.f; w[r][1] = iok ? cur.qf[x][r].y : 0.f;
+        w[r][2] = iok ? cur.qf[x][r].z : 0.f; w[r][3] = iok ? cur.qf[x][r].w : 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -468,6 +492,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dr_mfma_kernel(AttnBwdArgs a, in
       for (int cb = 0; cb < 4; ++cb)
         acc[cb] = mfma(af, *(const bf16x8*)(QT + (16 * cb + n16) * DGP + 32 * s + 8 * g4), acc[cb]);
     }
+    if (nit < items) cur = nxt;
+    it = nit;
   }
   // lane (g4, n16) of block cb: distance p0 + 16 wave + 4 g4 + e, column 16 cb + n16
 #pragma unroll
