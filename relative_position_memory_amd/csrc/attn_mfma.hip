@@ -605,10 +605,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
 // The references and sums of all parts and the outputs of the first 8 parts
 // are loaded at once (one round trip for up to 8 parts, two for up to 16).
 // The part that holds key 0 has a finite reference for every query.
+template <int MP>
 __global__ __launch_bounds__(64) void attn_part_merge_kernel(AttnArgs a) {
-  const int qt = blockIdx.x >> 3, wq = blockIdx.x & 7, g = blockIdx.y;
-  const int np = a.plan.nparts[qt];
-  if (np <= 1) return;
+  const int qt = a.plan.split_qt[blockIdx.x >> 3], wq = blockIdx.x & 7, g = blockIdx.y;
+  const int np = a.plan.nparts[qt];  // 2 .. MP
   const int wave = wq >> 1, gm = wq & 1;
   const int64_t groups = a.B * a.H;
   const int lane = threadIdx.x;
@@ -622,14 +622,17 @@ __global__ __launch_bounds__(64) void attn_part_merge_kernel(AttnArgs a) {
   auto acc_ptr = [&](int p) {
     return a.part_acc + (blk0 + (int64_t)p * groups) * (BQ * DP) + (wq * 4 * 2 * 64 + lane) * 2;
   };
-  float2 ml[16];
+  // (indexes of parts past np are clamped to part 0 and their values dropped)
+  float2 ml[MP];
 #pragma unroll
-  for (int p = 0; p < 16; ++p)
-    ml[p] = p < np ? *(const float2*)(a.part_ml + (blk0 + p * groups) * (BQ * 2) + moff)
-                   : make_float2(-INFINITY, 0.f);
-  float2 av[8][4][2];
+  for (int p = 0; p < MP; ++p) {
+    const float2 v = *(const float2*)(a.part_ml + (blk0 + (p < np ? p : 0) * groups) * (BQ * 2) + moff);
+    ml[p] = p < np ? v : make_float2(-INFINITY, 0.f);
+  }
+  constexpr int NB = MP < 8 ? MP : 8;  // parts whose outputs are loaded together
+  float2 av[NB][4][2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < NB; ++j) {
     const float* pa = acc_ptr(j < np ? j : 0);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -638,20 +641,20 @@ __global__ __launch_bounds__(64) void attn_part_merge_kernel(AttnArgs a) {
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int p = 0; p < 16; ++p) M = fmaxf(M, ml[p].x);
-  float wgt[16], den = 0.f;
+  for (int p = 0; p < MP; ++p) M = fmaxf(M, ml[p].x);
+  float wgt[MP], den = 0.f;
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
+  for (int p = 0; p < MP; ++p) {
     wgt[p] = p < np ? __builtin_amdgcn_exp2f(ml[p].x - M) : 0.f;
     den += wgt[p] * ml[p].y;
   }
   float o[4][4] = {};
 #pragma unroll
-  for (int p0 = 0; p0 < 16; p0 += 8) {
+  for (int p0 = 0; p0 < MP; p0 += NB) {
     if (p0 > 0) {
       if (p0 >= np) break;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < NB; ++j) {
         const float* pa = acc_ptr(p0 + j < np ? p0 + j : 0);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(64) void attn_part_merge_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -841,10 +844,14 @@ AttnPlan plan_uncached(const AttnArgs& a, int num_cus, size_t budget) {
   struct Cls { int sz, qt, part; };
   std::vector<Cls> cl;
   int slot = 0;
+  p.nsplit_qt = 0;
   for (int t = 0; t < sh.nqt; ++t) {
     p.nparts[t] = (uint8_t)k[t];
     p.slot0[t] = (uint8_t)(k[t] > 1 ? slot : 0);
-    if (k[t] > 1) slot += k[t];
+    if (k[t] > 1) {
+      slot += k[t];
+      p.split_qt[p.nsplit_qt++] = (uint8_t)t;
+    }
     for (int q = 0; q < k[t]; ++q) {
       const int lo = q * sh.n_kt[t] / k[t], hi = (q + 1) * sh.n_kt[t] / k[t];
       cl.push_back({hi - lo, t, q});
@@ -923,8 +930,20 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
                        groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.slots == 0) return e;
-  hipLaunchKernelGGL(attn_part_merge_kernel, dim3((unsigned)nqt * 8, (unsigned)groups), dim3(64),
-                     0, s, a);
+  // one wave per (split query tile, 16-query block, group), the part loop sized
+  // to the most parts any tile has
+  int mp = 2;
+  for (int t = 0; t < a.plan.nsplit_qt; ++t)
+    while (mp < a.plan.nparts[a.plan.split_qt[t]]) mp *= 2;
+  const dim3 mgrid((unsigned)a.plan.nsplit_qt * 8, (unsigned)groups);
+  if (mp <= 2)
+    hipLaunchKernelGGL(attn_part_merge_kernel<2>, mgrid, dim3(64), 0, s, a);
+  else if (mp <= 4)
+    hipLaunchKernelGGL(attn_part_merge_kernel<4>, mgrid, dim3(64), 0, s, a);
+  else if (mp <= 8)
+    hipLaunchKernelGGL(attn_part_merge_kernel<8>, mgrid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_part_merge_kernel<16>, mgrid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

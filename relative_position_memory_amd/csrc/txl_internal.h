@@ -74,6 +74,8 @@ struct AttnPlan {
   uint8_t cls_qt[ATTN_MAXCLS], cls_part[ATTN_MAXCLS];
   uint8_t nparts[ATTN_MAXQT];
   uint8_t slot0[ATTN_MAXQT];       // first partial slot of a split tile's parts
+  uint8_t split_qt[ATTN_MAXQT];    // the split query tiles (nsplit_qt of them)
+  int nsplit_qt;
 };
 
 struct AttnArgs {
