@@ -331,7 +331,9 @@ int run_gemm(int dtype, const txl::GemmArgs& g, hipStream_t st, const char* what
 
 // Workspace of txl_layer_step_kv: q [B][H][L][dp], a [B][L][H*d], y fp32
 // [B][L][D], then the attention's scratch.
-struct KvWs { size_t q, a, y, part, total; int64_t dp; };
+// (with zero-padded copies as in WsLayout: h [B L][Dp], W_q, W_kE, W_v [H d][Dp];
+// W_o [D][HDp] and a [B L][HDp])
+struct KvWs { size_t q, a, y, xh, xw, xwo, xo, part, total; int64_t dp, Dp, HDp; };
 KvWs kv_ws_layout(const txl_layer_dims& dm, int64_t es, size_t part_bytes) {
   KvWs w;
   w.dp = round_up(dm.d_head, 8);
@@ -341,9 +343,16 @@ KvWs kv_ws_layout(const txl_layer_dims& dm, int64_t es, size_t part_bytes) {
     off += (size_t)round_up(bytes, 256);
     return o;
   };
+  const int64_t BL = dm.B * dm.L, D = dm.d_model, HD = dm.n_head * dm.d_head;
   w.q = take(dm.B * dm.n_head * dm.L * w.dp * es);
-  w.a = take(dm.B * dm.L * dm.n_head * dm.d_head * es);
-  w.y = take(dm.B * dm.L * dm.d_model * 4);
+  w.a = take(BL * HD * es);
+  w.y = take(BL * D * 4);
+  w.Dp = pad_k(es, D);
+  w.HDp = pad_k(es, HD);
+  w.xh = take(w.Dp ? BL * w.Dp * es : 0);
+  w.xw = take(w.Dp ? 3 * HD * w.Dp * es : 0);
+  w.xwo = take(w.HDp ? D * w.HDp * es : 0);
+  w.xo = take(w.HDp ? BL * w.HDp * es : 0);
   w.part = take((int64_t)part_bytes);
   w.total = off;
   return w;
@@ -770,6 +779,34 @@ int txl_layer_step_kv(void* stream, int dtype, const txl_layer_dims* dims, const
   gq.a = {nullptr, 1, 0, 0, h_in, L, D};
   gq.w = {w->W_q, w->W_q, HD, D};
   gq.e = {txl::EPI_HEADS, q, q, HD, d, H * L * dp, L * dp, dp, nullptr, nullptr, 0, 0, dp};
+  // d_model or H d not a multiple of 32: zero-padded copies (one launch), as in
+  // txl_layer_step
+  auto al4 = [](const void* p) { return (uintptr_t)p % 4 == 0; };
+  const bool pin = dtype == TXL_BF16 && ws.Dp > 0 && al4(h_in) && al4(w->W_q) && al4(w->W_kE) &&
+                   al4(w->W_v);
+  const bool pout = dtype == TXL_BF16 && ws.HDp > 0 && al4(w->W_o) && al4(a);
+  if (pin || pout) {
+    txl::PadJob pj[5];
+    int np = 0;
+    const int64_t Dp = ws.Dp;
+    if (pin) {
+      uint16_t* xh = (uint16_t*)(base + ws.xh);
+      uint16_t* xw = (uint16_t*)(base + ws.xw);
+      pj[np++] = {{nullptr, 1, 0, 0, h_in, B * L, D}, B * L, D, Dp, xh};
+      const void* wsrc[3] = {w->W_q, w->W_kE, w->W_v};
+      for (int i = 0; i < 3; ++i)
+        pj[np++] = {{nullptr, 1, 0, 0, wsrc[i], HD, D}, HD, D, Dp, xw + i * HD * Dp};
+      gkv.K = gq.K = Dp;
+      gkv.a = {nullptr, 1, 0, 0, xh, L, Dp};
+      gq.a = {nullptr, 1, 0, 0, xh, L, Dp};
+      gkv.w = {xw + HD * Dp, xw + 2 * HD * Dp, HD, Dp};
+      gq.w = {xw, xw, HD, Dp};
+    }
+    if (pout)
+      pj[np++] = {{nullptr, 1, 0, 0, w->W_o, D, HD}, D, HD, ws.HDp, (uint16_t*)(base + ws.xwo)};
+    const hipError_t e = txl::launch_pad_rows(pj, np, st);
+    if (e != hipSuccess) return hip_fail(e, "padded operand copies");
+  }
   head_padded_cols(gkv, 2, H, d, dp);
   head_padded_cols(gq, 1, H, d, dp);
   if (dtype == TXL_BF16 && txl::gemm_mfma_supported(gkv) && txl::gemm_mfma_supported(gq)) {
@@ -791,7 +828,17 @@ int txl_layer_step_kv(void* stream, int dtype, const txl_layer_dims* dims, const
   at.scores = nullptr;
   at.d_load = dp;  // ring, q and r rows hold dp readable columns (padding zeroed)
   if ((rc = run_attn(dtype, at, base + ws.part, ws_bytes - ws.part, st)) != TXL_OK) return rc;
-  if ((rc = run_out_ln(dtype, dm, a, w, h_in, h_out, y, st)) != TXL_OK) return rc;
+  if (pout) {
+    const txl::PadJob pa = {{nullptr, 1, 0, 0, a, B * L, HD}, B * L, HD, ws.HDp,
+                            (uint16_t*)(base + ws.xo)};
+    const hipError_t e = txl::launch_pad_rows(&pa, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "padded attention output");
+    rc = run_out_ln(dtype, dm, a, w, h_in, h_out, y, st, nullptr, base + ws.xo, base + ws.xwo,
+                    ws.HDp, false);
+  } else {
+    rc = run_out_ln(dtype, dm, a, w, h_in, h_out, y, st);
+  }
+  if (rc != TXL_OK) return rc;
   // the memory keeps the newest min(M, len + L) rows: only the ring state moves
   const int64_t new_len = T < M ? T : M;
   kv->start = (kv->start + T - new_len) % C;

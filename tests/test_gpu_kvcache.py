@@ -79,6 +79,8 @@ def test_kv_stream_matches_oracle(name, over, segments, extra):
     ({"B": 2, "L": 1, "M": 100, "D": 128, "H": 2, "d": 64, "R_rows": 101}, 12),
     # the long-memory evaluation model's width: matrix-vector products over K = 1024
     ({"B": 1, "L": 1, "M": 300, "D": 1024, "H": 16, "d": 64, "R_rows": 301}, 6),
+    # widths that are not multiples of 32: the products read zero-padded copies
+    ({"B": 3, "L": 1, "M": 40, "D": 82, "H": 2, "d": 41, "R_rows": 41}, 5),
 ])
 def test_kv_decode_one_token_at_a_time(over, segments):
     """L = 1: a memory of up to M tokens, one new token per step."""
