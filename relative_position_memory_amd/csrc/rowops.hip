@@ -213,12 +213,13 @@ __global__ __launch_bounds__(256) void ring_copy_kernel(char* ring, int64_t cap,
   for (int64_t c = threadIdx.x; c < n; c += blockDim.x) dst[c] = s[c];
 }
 
-// The same copy for 16-byte rows, as one flat list of 16-byte items (row r =
-// b n + t, chunk c of cpr): each thread moves RC_U items, all loaded before any
-// is stored (ring and src never overlap); an item index past the end repeats
-// the last item, whose identical value is then written twice.  32-bit index
-// arithmetic (the caller checks the item count).
+// The same copy as one flat list of V-sized items (16 bytes when the rows allow,
+// else 4; row r = b n + t, chunk c of cpr): each thread moves RC_U items, all
+// loaded before any is stored (ring and src never overlap); an item index past
+// the end repeats the last item, whose identical value is then written twice.
+// 32-bit index arithmetic (the caller checks the item count).
 constexpr int RC_U = 4;
+template <typename V>
 __global__ __launch_bounds__(256) void ring_copy_flat_kernel(char* __restrict__ ring, uint32_t cap,
                                                              uint32_t slot0,
                                                              const char* __restrict__ src,
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(256) void ring_copy_flat_kernel(char* __restrict__ 
                                                              uint32_t n, uint32_t cpr,
                                                              uint32_t total, int64_t rb) {
   const uint32_t i0 = blockIdx.x * (256u * RC_U) + threadIdx.x;
-  int4 v[RC_U];
+  V v[RC_U];
   int64_t dst[RC_U];
 #pragma unroll
   for (int u = 0; u < RC_U; ++u) {
@@ -235,11 +236,11 @@ __global__ __launch_bounds__(256) void ring_copy_flat_kernel(char* __restrict__ 
     const uint32_t row = ic / cpr, c = ic - row * cpr;
     const uint32_t b = row / n, t = row - b * n;
     const uint32_t slot = (slot0 + t) % cap;
-    v[u] = *(const int4*)(src + ((int64_t)b * src_rows + row0 + t) * rb + 16 * (int64_t)c);
-    dst[u] = ((int64_t)b * cap + slot) * rb + 16 * (int64_t)c;
+    v[u] = *(const V*)(src + ((int64_t)b * src_rows + row0 + t) * rb + (int64_t)sizeof(V) * c);
+    dst[u] = ((int64_t)b * cap + slot) * rb + (int64_t)sizeof(V) * c;
   }
 #pragma unroll
-  for (int u = 0; u < RC_U; ++u) *(int4*)(ring + dst[u]) = v[u];
+  for (int u = 0; u < RC_U; ++u) *(V*)(ring + dst[u]) = v[u];
 }
 
 // Padded row copies (PadJob): a block is 4 waves of PAD_RPW rows of one job.
@@ -405,14 +406,21 @@ hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0, c
   const int64_t rb = D * es;
   const uintptr_t al = (uintptr_t)ring | (uintptr_t)src;
   dim3 grid((unsigned)n, (unsigned)B);
-  const int64_t total = n * B * (rb / 16);
+  const bool wide = rb % 16 == 0 && al % 16 == 0;
+  const int64_t isz = wide ? 16 : 4;
+  const int64_t total = n * B * (rb / isz);
   const bool fits = total < 0x7fffffffLL && cap < 0x7fffffffLL && slot0 < cap &&
                     src_rows + row0 < 0x7fffffffLL;
-  if (rb % 16 == 0 && al % 16 == 0 && fits) {
+  if ((wide || (rb % 4 == 0 && al % 4 == 0)) && fits) {
     const unsigned blocks = (unsigned)((total + 256 * RC_U - 1) / (256 * RC_U));
-    hipLaunchKernelGGL(ring_copy_flat_kernel, dim3(blocks), dim3(256), 0, s, (char*)ring,
-                       (uint32_t)cap, (uint32_t)slot0, (const char*)src, (uint32_t)src_rows,
-                       (uint32_t)row0, (uint32_t)n, (uint32_t)(rb / 16), (uint32_t)total, rb);
+    if (wide)
+      hipLaunchKernelGGL(ring_copy_flat_kernel<int4>, dim3(blocks), dim3(256), 0, s, (char*)ring,
+                         (uint32_t)cap, (uint32_t)slot0, (const char*)src, (uint32_t)src_rows,
+                         (uint32_t)row0, (uint32_t)n, (uint32_t)(rb / 16), (uint32_t)total, rb);
+    else
+      hipLaunchKernelGGL(ring_copy_flat_kernel<int>, dim3(blocks), dim3(256), 0, s, (char*)ring,
+                         (uint32_t)cap, (uint32_t)slot0, (const char*)src, (uint32_t)src_rows,
+                         (uint32_t)row0, (uint32_t)n, (uint32_t)(rb / 4), (uint32_t)total, rb);
   } else if (rb % 16 == 0 && al % 16 == 0)
     hipLaunchKernelGGL(ring_copy_kernel<int4>, grid, dim3(64), 0, s, (char*)ring, cap, slot0,
                        (const char*)src, src_rows, row0, rb);
