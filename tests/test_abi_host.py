@@ -211,3 +211,34 @@ def test_noalloc_entry_point_checks_need_no_gpu():
             base(6), L * H * d, H * d, d, None]
     assert lib.txl_rel_attn_fwd_noalloc(*args) == txl.EWORKSPACE
     assert "static scratch" in txl.status_string(txl.EWORKSPACE)
+
+
+def test_workspaces_cover_the_padded_copies_need_no_gpu():
+    """bf16 widths that are not whole 32-element K steps (the word-level model's
+    d_model 410, 10 heads of 41) are read through zero-padded copies that live in
+    the caller's workspace: its size must cover them (pure host arithmetic)."""
+    import torch
+    from relative_position_memory_amd import txl
+    B, L, M, D, H, d = 60, 150, 150, 410, 10, 41
+    Dp, HDp, HD, T = 416, 416, H * d, M + L
+    dims = txl.layer_dims(B, L, D, H, d)
+    n = txl.workspace_bytes(dims, M, torch.bfloat16)
+    dp = 48  # head rows padded to a multiple of 8
+    base = 2 * (B * H * L * dp + 2 * B * H * T * dp + H * T * dp + B * L * HD) + 4 * B * L * D
+    pads = 2 * (B * T * Dp + T * Dp + 4 * HD * Dp + D * HDp + B * L * HDp)
+    assert n >= base + pads
+    # the same model in fp32 takes no copies: its workspace is the plain layout
+    r256 = lambda x: (x + 255) // 256 * 256
+    n32 = txl.workspace_bytes(dims, M, torch.float32)
+    assert n32 == sum(r256(4 * x) for x in (B * H * L * dp, B * H * T * dp, B * H * T * dp,
+                                             H * T * dp, B * L * HD, B * L * D))
+    # cached keys and values: h, W_q, W_kE, W_v and W_o, a padded
+    nk = txl.kv_workspace_bytes(dims, M, torch.bfloat16)
+    assert nk >= 2 * (B * L * Dp + 3 * HD * Dp + D * HDp + B * L * HDp)
+    # feed-forward 410 x 1640: x, W1 (1664 rows), b1, W2 and f at a pitch of 1664
+    rows, Di, Dip = 9000, 1640, 1664
+    nf = txl.pos_ff_workspace_bytes(rows, D, Di, torch.bfloat16)
+    assert nf >= 2 * (rows * Dip + rows * Dp + Dip * Dp + Dip + D * Dip) + 4 * rows * D
+    # widths already whole K steps take no copies
+    assert txl.pos_ff_workspace_bytes(rows, 512, 2048, torch.bfloat16) == \
+        r256(rows * 2048 * 2) + r256(rows * 512 * 4)
