@@ -244,12 +244,13 @@ __global__ __launch_bounds__(256) void ring_copy_flat_kernel(char* __restrict__ 
 }
 
 // Padded row copies (PadJob): a block is 4 waves of PAD_RPW rows of one job.
-// Lane l writes the 16-byte pieces l, l + 64, ... of its wave's rows, each from
-// four 4-byte source words (the source rows are only 4-byte aligned), the loads
-// of all rows issued before their stores; a source index past the width is
-// clamped and its value replaced by zero, so every load is unconditional.  Rows
-// past the job repeat its last row (the same values written twice).  32-bit
-// index arithmetic (the launch checks the sizes).
+// Lane l moves the 4-byte words l, l + 64, l + 128, l + 192 of each of its
+// wave's rows (one 1 KB block of each row at a time), so every load and store
+// instruction covers 256 contiguous bytes, and all of a block's loads (16 per
+// lane) are issued before its stores; a source index past the width is clamped
+// and its value replaced by zero, so every load is unconditional.  Rows past
+// the job repeat its last row (the same values written twice).  32-bit index
+// arithmetic (the launch checks the sizes).
 constexpr int PAD_RPW = 4;
 struct PadJobsK {
   PadJob j[PAD_MAX];
@@ -275,35 +276,35 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(PadJobsK J) {
   const uint32_t blk = blockIdx.x - (jn ? J.block_end[jn - 1] : 0u);
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const uint32_t R = (uint32_t)p.R, r0 = (blk * 4 + wave) * PAD_RPW;
-  const uint32_t nq = (uint32_t)(p.Cpad / 8), wsrc = (uint32_t)(p.C / 2);
-  uint4* drow[PAD_RPW];
+  const uint32_t wdst = (uint32_t)(p.Cpad / 2), wsrc = (uint32_t)(p.C / 2);
+  uint32_t* drow[PAD_RPW];
 #pragma unroll
   for (int i = 0; i < PAD_RPW; ++i)
-    drow[i] = (uint4*)(p.dst + (int64_t)(r0 + i < R ? r0 + i : R - 1) * p.Cpad);
+    drow[i] = (uint32_t*)(p.dst + (int64_t)(r0 + i < R ? r0 + i : R - 1) * p.Cpad);
   if (p.src.cur == nullptr && p.src.mem == nullptr) {  // rows of zeros
-    for (uint32_t q = lane; q < nq; q += 64)
+    for (uint32_t c = lane; c < wdst; c += 64)
 #pragma unroll
-      for (int i = 0; i < PAD_RPW; ++i) drow[i][q] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < PAD_RPW; ++i) drow[i][c] = 0u;
     return;
   }
   const uint32_t* srow[PAD_RPW];
 #pragma unroll
   for (int i = 0; i < PAD_RPW; ++i) srow[i] = pad_src_row(p.src, r0 + i < R ? r0 + i : R - 1);
-  for (uint32_t q0 = 0; q0 < nq; q0 += 64) {
-    const uint32_t q = q0 + lane;
+  for (uint32_t c0 = 0; c0 < wdst; c0 += 256) {
     uint32_t v[PAD_RPW][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = 4 * q + e, ws = w < wsrc ? w : wsrc - 1;
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t c = c0 + lane + 64 * k, cs = c < wsrc ? c : wsrc - 1;
 #pragma unroll
-      for (int i = 0; i < PAD_RPW; ++i) v[i][e] = srow[i][ws];
+      for (int i = 0; i < PAD_RPW; ++i) v[i][k] = srow[i][cs];
     }
 #pragma unroll
-    for (int i = 0; i < PAD_RPW; ++i) {
-      uint32_t o[4];
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t c = c0 + lane + 64 * k;
+      if (c < wdst) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = 4 * q + e < wsrc ? v[i][e] : 0u;
-      if (q < nq) drow[i][q] = make_uint4(o[0], o[1], o[2], o[3]);
+        for (int i = 0; i < PAD_RPW; ++i) drow[i][c] = c < wsrc ? v[i][k] : 0u;
+      }
     }
   }
 }
@@ -435,8 +436,8 @@ hipError_t launch_ring_copy(int dtype, void* ring, int64_t cap, int64_t slot0, c
 
 bool pad_job_ok(const PadJob& j) {
   const RowGather& a = j.src;
-  if (j.R < 0 || j.Cpad < 8 || (j.Cpad & 7) || !j.dst) return false;
-  if ((uintptr_t)j.dst % 16 || j.R * j.Cpad >= ((int64_t)1 << 31)) return false;
+  if (j.R < 0 || j.Cpad < 2 || (j.Cpad & 1) || !j.dst) return false;
+  if ((uintptr_t)j.dst % 4 || j.R * j.Cpad >= ((int64_t)1 << 31)) return false;
   if (a.cur == nullptr && a.mem == nullptr) return true;  // zeros
   if (j.C < 2 || j.C > j.Cpad || (j.C & 1)) return false;
   const uintptr_t al = (uintptr_t)a.cur | (a.mem_len ? (uintptr_t)a.mem : 0);

@@ -375,9 +375,9 @@ hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 // bf16 rows copied to a wider pitch with zero columns past the source width:
 // dst[r][c] = src row r element c for c < C, 0 for C <= c < Cpad.  Source row r
 // is RowGather's logical row r (the memory ring and the current rows, or one
-// plain matrix); src.cur and src.mem both NULL write rows of zeros.  C and the
-// source pitch even, source rows 4-byte aligned; Cpad a multiple of 8 and dst
-// 16-byte aligned; R * Cpad below 2^31 (pad_job_ok).
+// plain matrix); src.cur and src.mem both NULL write rows of zeros.  C, Cpad
+// and the source pitch even, source rows and dst 4-byte aligned; R * Cpad below
+// 2^31 (pad_job_ok).
 struct PadJob {
   RowGather src;
   int64_t R, C, Cpad;
