@@ -69,7 +69,9 @@ struct WsLayout {
 // H d not a multiple of 32) run on copies padded with zero columns to the next
 // multiple of 32, which the LDS-direct product takes (its K loop moves whole
 // 32-deep steps of 16-byte pieces).
-int64_t pad_k(int64_t es, int64_t K) { return es == 2 && K % 32 != 0 && K % 2 == 0 ? round_up(K, 32) : 0; }
+int64_t pad_k(int64_t es, int64_t K) {
+  return es == 2 && K % 32 != 0 && K % 2 == 0 ? round_up(K, 32) : 0;
+}
 
 // K splits of the unfused output projection y = a W_o^T + h: when its 128 x 128
 // tiles would leave most of a 256-CU chip idle (a few rows, as at a long-memory
