@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="charlm", choices=WORKLOAD_NAMES + ("tiny",))
     p.add_argument("--attn-reps", type=int, default=50)
+    p.add_argument("--streams", type=int, default=4,
+                   help="HIP streams the stack's segments go round (txl_stack_fwd); 1 = serial")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--train", action="store_true",
                    help="time a training step (forward + backward, stop-gradient memory) at the "
@@ -833,25 +835,39 @@ def main():
     bufs = [torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(2)]
     stream = torch.cuda.current_stream()
 
-    def step():
-        for s in range(w.n_segments):
-            h = h0[s]
-            for n in range(w.n_layers):
-                out = bufs[n % 2]
-                txl.layer_step(dims, h, rings[n], lws[n], u, vb, R, out, ws, stream=stream)
-                txl.mem_update(rings[n], h, stream=stream)
-                h = out
+    # A step: every segment through every layer with its memory update
+    # (txl_stack_fwd).  Segment s goes to streams[s % n]; layer n of segment s + 1
+    # waits only for layer n of segment s, so consecutive segments overlap one
+    # layer apart, with results bit-identical to the serial order.
+    def make_step(n_streams):
+        streams = [stream] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
+        sws = torch.empty(txl.stack_workspace_bytes(dims, w.M, tdt, n_streams),
+                          dtype=torch.uint8, device="cuda")
+        h_in = h0[:w.n_segments]
+        h_out = torch.empty_like(h_in)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+        def step():
+            txl.stack_fwd(streams, dims, h_in, rings, lws, u, vb, R, h_out, sws)
+        return step
+
+    def timed_ms(step, steps, warmup):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed_ms(make_step(args.streams), args.steps, args.warmup)
+    # the same stack in the serial order on one stream, for comparison
+    ms_serial = ms if args.streams == 1 else timed_ms(make_step(1), max(3, args.steps // 4), 1)
+    # the layer step behind the attention timing below: full memory, q, k, v, r
+    # left in ws
+    txl.layer_step(dims, h0[0], rings[0], lws[0], u, vb, R, bufs[0], ws, stream=stream)
 
     # the attention kernel alone, on the last layer step's q, k, v, r (HIP events, same
     # stream); with the memory full (every ring holds M rows after the first segment)
@@ -933,6 +949,10 @@ def main():
                        "unit": "GB/s", "frac": mu_bytes / (mu_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                        "bound": "hbm", "kernel": "ring_copy_kernel"},
         "step_tflops": step_flops / (ms / 1e3) / 1e12,
+        "schedule": {"entry_point": "txl_stack_fwd", "streams": args.streams,
+                     "serial_ms_per_step": ms_serial,
+                     "note": "segments go round the streams, segment s+1 one layer behind "
+                             "segment s; outputs bit-identical to the one-stream order"},
     }
     if not args.main_only:
         res["pos_ff"] = ff

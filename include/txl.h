@@ -379,6 +379,55 @@ int txl_mem_update(void* stream, int dtype, txl_ring* mem, int64_t B, int64_t d_
                    const void* h_new, int64_t L);
 
 /*
+ * An n_layers stack run over n_segments consecutive segments, forward (the
+ * recurrence of section 3.2 over the N-layer procedure of section 3.3; the
+ * layer is txl_layer_step, the memory update txl_mem_update):
+ *
+ *   for s in 0 .. n_segments-1:
+ *     h = h_in[s]
+ *     for n in 0 .. n_layers-1:
+ *       y = txl_layer_step(h, mem[n], w[n]);  txl_mem_update(mem[n], h);  h = y
+ *     h_out[s] = h
+ *
+ * Layer n of segment s reads two things: the output of layer n-1 of segment s
+ * and ring n as segment s-1 left it.  So layer n of segment s+1 and layer n+1 of
+ * segment s do not depend on each other, and with more than one stream the
+ * segments go round the streams (segment s on streams[s % n_streams]), each
+ * layer step of segment s waiting for the memory update of the same layer in
+ * segment s-1 (an event on the previous segment's stream): segment s+1 runs one
+ * layer behind segment s, and the two overlap.  Every kernel reads and writes
+ * what it would in the serial order above, so the results are bit-identical to
+ * it for any n_streams.
+ *   streams    n_streams (1 .. TXL_STACK_MAX_STREAMS) HIP streams; NULL entries
+ *              are the default stream, repeats are allowed (they serialise).
+ *              Streams 1.. first wait for the work already on streams[0], and
+ *              streams[0] waits for their last work before the call returns, so
+ *              ordering later work after streams[0] covers the whole stack.
+ *   h_in       [n_segments][B][L][d_model] dense, the first layer's inputs.
+ *   mem        n_layers rings (capacity, start and len each their own), updated
+ *              in place, n_segments times each, as txl_mem_update does.
+ *   w          n_layers layer weights;  u_bias, v_bias, R as in txl_layer_step,
+ *              R_rows covering each layer's longest memory + L.
+ *   h_out      [n_segments][B][L][d_model] dense, the last layer's outputs; must
+ *              not overlap h_in, the rings or the workspace.
+ *   workspace  >= txl_stack_workspace_bytes(dims, largest ring capacity, dtype,
+ *              n_streams) bytes, 256-byte aligned: per stream one layer
+ *              workspace and two [B][L][d_model] buffers for the layer outputs.
+ * Every argument is checked before anything is enqueued (a failing call writes
+ * nothing and leaves the rings as they were).  Returns TXL_OK or a txl_status.
+ */
+#define TXL_STACK_MAX_STREAMS 8
+int txl_stack_fwd(void* const* streams, int n_streams, int dtype, const txl_layer_dims* dims,
+                  int64_t n_layers, int64_t n_segments, const void* h_in, txl_ring* mem,
+                  const txl_layer_weights* w, const void* u_bias, const void* v_bias,
+                  const void* R, int64_t R_rows, void* h_out, void* workspace,
+                  size_t ws_bytes);
+
+/* Workspace bytes of txl_stack_fwd (0 for invalid dims, dtype or n_streams). */
+size_t txl_stack_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype,
+                                 int n_streams);
+
+/*
  * ---- Evaluation with cached keys and values ---------------------------------------------
  * At evaluation the weights are fixed, so the projected keys and values of a
  * memory row (section 3.2's cached hidden states, projected by W_kE and W_v as in

@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "../../include/txl.h"
 #include "gemm_common.h"
 #include "txl_internal.h"
@@ -673,6 +676,145 @@ int txl_mem_update(void* stream, int dtype, txl_ring* mem, int64_t B, int64_t d_
   const int64_t new_len = tot < M ? tot : M;
   mem->start = (mem->start + tot - new_len) % M;
   mem->len = new_len;
+  return TXL_OK;
+}
+
+// ---- a stack of layers over several segments ----------------------------------------
+
+size_t txl_stack_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype,
+                                 int n_streams) {
+  if (n_streams < 1 || n_streams > TXL_STACK_MAX_STREAMS) return 0;
+  const size_t lw = txl_layer_workspace_bytes(dims, mem_capacity, dtype);
+  if (lw == 0) return 0;
+  const int64_t hb = round_up(dims->B * dims->L * dims->d_model * elt_size(dtype), 256);
+  return (size_t)n_streams * (size_t)(round_up((int64_t)lw, 256) + 2 * hb);
+}
+
+int txl_stack_fwd(void* const* streams, int n_streams, int dtype, const txl_layer_dims* dims,
+                  int64_t n_layers, int64_t n_segments, const void* h_in, txl_ring* mem,
+                  const txl_layer_weights* w, const void* u_bias, const void* v_bias,
+                  const void* R, int64_t R_rows, void* h_out, void* workspace,
+                  size_t ws_bytes) {
+  g_detail[0] = 0;
+  if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_EUNSUPPORTED, "dtype %d", dtype);
+  int rc = check_dims(dims);
+  if (rc != TXL_OK) return rc;
+  if (!streams) return fail(TXL_EINVAL, "streams is NULL");
+  if (n_streams < 1 || n_streams > TXL_STACK_MAX_STREAMS)
+    return fail(TXL_EINVAL, "n_streams %d not in 1 .. %d", n_streams, TXL_STACK_MAX_STREAMS);
+  if (n_layers < 1 || n_segments < 1)
+    return fail(TXL_EINVAL, "n_layers and n_segments must be >= 1");
+  if (!h_in || !mem || !w || !u_bias || !v_bias || !R || !h_out)
+    return fail(TXL_EINVAL, "NULL pointer");
+  if (!workspace) return fail(TXL_EINVAL, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(TXL_EINVAL, "workspace is not 256-byte aligned");
+  const txl_layer_dims dm = *dims;
+  const int64_t B = dm.B, L = dm.L, D = dm.d_model, es = elt_size(dtype);
+  const int64_t seg = B * L * D * es;  // bytes of one segment's [B][L][D]
+  // every layer's arguments, before anything is enqueued
+  size_t lw = 0;
+  for (int64_t n = 0; n < n_layers; ++n) {
+    const txl_ring& m = mem[n];
+    if (m.capacity < 1 || m.start < 0 || m.start >= m.capacity || m.len < 0 ||
+        m.len > m.capacity || !m.data)
+      return fail(TXL_EINVAL, "ring of layer %lld: state (capacity %lld, start %lld, len %lld)",
+                  (long long)n, (long long)m.capacity, (long long)m.start, (long long)m.len);
+    const txl_layer_weights& wl = w[n];
+    if (!wl.W_q || !wl.W_kE || !wl.W_v || !wl.W_kR || !wl.W_o || !wl.ln_gamma || !wl.ln_beta)
+      return fail(TXL_EINVAL, "NULL weight pointer in layer %lld", (long long)n);
+    // the longest memory this layer reads: len grows by L per segment up to the capacity
+    const int64_t len_max = std::min<int64_t>(m.len + (n_segments - 1) * L, m.capacity);
+    if (R_rows < len_max + L)
+      return fail(TXL_EINVAL, "R_rows %lld < %lld (layer %lld's longest memory + L)",
+                  (long long)R_rows, (long long)(len_max + L), (long long)n);
+    lw = std::max(lw, txl_layer_workspace_bytes(dims, m.capacity, dtype));
+  }
+  if (lw == 0) return fail(TXL_EINVAL, "invalid layer dims");
+  const int64_t hb = round_up(seg, 256);
+  const int64_t per = round_up((int64_t)lw, 256) + 2 * hb;  // one stream's share
+  const size_t need = (size_t)(n_streams * per);
+  if (ws_bytes < need) return fail(TXL_EWORKSPACE, "need %zu bytes, got %zu", need, ws_bytes);
+  const Span sin = {(uintptr_t)h_in, (uintptr_t)h_in + (uintptr_t)(n_segments * seg)};
+  const Span sout = {(uintptr_t)h_out, (uintptr_t)h_out + (uintptr_t)(n_segments * seg)};
+  const Span sws = {(uintptr_t)workspace, (uintptr_t)workspace + ws_bytes};
+  if (overlap(sout, sin)) return fail(TXL_EINVAL, "h_out overlaps h_in");
+  if (overlap(sws, sin) || overlap(sws, sout)) return fail(TXL_EINVAL, "workspace overlaps h_in or h_out");
+  for (int64_t n = 0; n < n_layers; ++n) {
+    const Span sr = {(uintptr_t)mem[n].data,
+                     (uintptr_t)mem[n].data + (uintptr_t)(B * mem[n].capacity * D * es)};
+    if (overlap(sr, sin) || overlap(sr, sout) || overlap(sr, sws))
+      return fail(TXL_EINVAL, "the ring of layer %lld overlaps h_in, h_out or the workspace",
+                  (long long)n);
+    for (int64_t m = 0; m < n; ++m) {
+      const Span so = {(uintptr_t)mem[m].data,
+                       (uintptr_t)mem[m].data + (uintptr_t)(B * mem[m].capacity * D * es)};
+      if (overlap(sr, so))
+        return fail(TXL_EINVAL, "the rings of layers %lld and %lld overlap", (long long)m,
+                    (long long)n);
+    }
+  }
+
+  // Streams that get segments, and the events of the schedule: done[s & 1][n] is
+  // recorded after layer n of segment s has appended its input to ring n; layer
+  // n of segment s + 1 (the next stream) waits for it.  The same slot is recorded
+  // again two segments later, after that wait was enqueued.
+  const int ns = (int)std::min<int64_t>(n_streams, n_segments);
+  struct Events {
+    std::vector<hipEvent_t> v;
+    ~Events() { for (hipEvent_t e : v) (void)hipEventDestroy(e); }  // released when complete
+  } evs;
+  auto make_event = [&](hipEvent_t* e) {
+    const hipError_t x = hipEventCreateWithFlags(e, hipEventDisableTiming);
+    if (x == hipSuccess) evs.v.push_back(*e);
+    return x;
+  };
+  std::vector<hipEvent_t> done;
+  hipEvent_t e_start = nullptr;
+  if (ns > 1) {
+    done.resize(2 * n_layers);
+    for (hipEvent_t& e : done) {
+      const hipError_t x = make_event(&e);
+      if (x != hipSuccess) return hip_fail(x, "event create");
+    }
+    hipError_t x = make_event(&e_start);
+    if (x == hipSuccess) x = hipEventRecord(e_start, (hipStream_t)streams[0]);
+    for (int k = 1; k < ns && x == hipSuccess; ++k)
+      x = hipStreamWaitEvent((hipStream_t)streams[k], e_start, 0);
+    if (x != hipSuccess) return hip_fail(x, "stream start order");
+  }
+  char* base = (char*)workspace;
+  for (int64_t s = 0; s < n_segments; ++s) {
+    const int k = (int)(s % ns);
+    void* st = streams[k];
+    char* wsk = base + k * per;
+    char* buf[2] = {wsk + round_up((int64_t)lw, 256), wsk + round_up((int64_t)lw, 256) + hb};
+    const char* h = (const char*)h_in + s * seg;
+    for (int64_t n = 0; n < n_layers; ++n) {
+      if (ns > 1 && s > 0) {
+        const hipError_t x = hipStreamWaitEvent((hipStream_t)st, done[((s - 1) & 1) * n_layers + n], 0);
+        if (x != hipSuccess) return hip_fail(x, "stream wait");
+      }
+      void* out = n == n_layers - 1 ? (void*)((char*)h_out + s * seg) : (void*)buf[n & 1];
+      rc = layer_step_run(st, dtype, dims, h, &mem[n], &w[n], u_bias, v_bias, R, R_rows, out,
+                          wsk, (size_t)round_up((int64_t)lw, 256), nullptr, nullptr);
+      if (rc != TXL_OK) return rc;
+      rc = txl_mem_update(st, dtype, &mem[n], B, D, h, L);
+      if (rc != TXL_OK) return rc;
+      if (ns > 1) {
+        const hipError_t x = hipEventRecord(done[(s & 1) * n_layers + n], (hipStream_t)st);
+        if (x != hipSuccess) return hip_fail(x, "event record");
+      }
+      h = (const char*)out;
+    }
+  }
+  // stream 0 waits for the others' last work, so that it alone orders what follows
+  for (int k = 1; k < ns; ++k) {
+    hipEvent_t e_end = nullptr;
+    hipError_t x = make_event(&e_end);
+    if (x == hipSuccess) x = hipEventRecord(e_end, (hipStream_t)streams[k]);
+    if (x == hipSuccess) x = hipStreamWaitEvent((hipStream_t)streams[0], e_end, 0);
+    if (x != hipSuccess) return hip_fail(x, "stream end order");
+  }
   return TXL_OK;
 }
 

@@ -255,6 +255,46 @@ def mem_update(ring, h_new, stream=None):
     return ring
 
 
+STACK_MAX_STREAMS = 8
+_lib.txl_stack_workspace_bytes.argtypes = [ctypes.POINTER(LayerDims), _i64, ctypes.c_int,
+                                           ctypes.c_int]
+_lib.txl_stack_workspace_bytes.restype = _sz
+_lib.txl_stack_fwd.argtypes = [ctypes.POINTER(_p), ctypes.c_int, ctypes.c_int,
+                               ctypes.POINTER(LayerDims), _i64, _i64, _p, ctypes.POINTER(Ring),
+                               ctypes.POINTER(LayerWeights), _p, _p, _p, _i64, _p, _p, _sz]
+_lib.txl_stack_fwd.restype = ctypes.c_int
+
+
+def stack_workspace_bytes(dims: LayerDims, mem_capacity: int, dtype: torch.dtype,
+                          n_streams: int) -> int:
+    n = _lib.txl_stack_workspace_bytes(ctypes.byref(dims), int(mem_capacity), dtype_code(dtype),
+                                       int(n_streams))
+    if n == 0:
+        raise ValueError("invalid dims, dtype or stream count")
+    return int(n)
+
+
+def stack_fwd(streams, dims, h_in, rings, lws, u, vb, R, h_out, workspace):
+    """txl_stack_fwd: the layer stack over h_in's segments [S, B, L, D] on the given
+    streams (a list; None entries mean the current stream).  rings (a list of Ring)
+    are advanced in place; lws is a list of LayerWeights."""
+    S = h_in.shape[0]
+    n = len(rings)
+    if len(lws) != n:
+        raise ValueError("one LayerWeights per ring")
+    sa = (_p * len(streams))(*[_stream(st).value for st in streams])
+    ra = (Ring * n)(*rings)
+    wa = (LayerWeights * n)(*lws)
+    rc = _lib.txl_stack_fwd(sa, len(streams), dtype_code(h_in.dtype), ctypes.byref(dims), n, S,
+                            _ptr(h_in), ra, wa, _ptr(u), _ptr(vb), _ptr(R), R.shape[0],
+                            _ptr(h_out), _ptr(workspace),
+                            workspace.numel() * workspace.element_size())
+    for i in range(n):  # the library advanced the copies
+        rings[i].start, rings[i].len = ra[i].start, ra[i].len
+    _check(rc, "txl_stack_fwd")
+    return h_out
+
+
 class WorkspaceMap(ctypes.Structure):
     _fields_ = [("q", _sz), ("k", _sz), ("v", _sz), ("r", _sz), ("a", _sz), ("d_pad", _i64)]
 

@@ -242,3 +242,58 @@ def test_workspaces_cover_the_padded_copies_need_no_gpu():
     # widths already whole K steps take no copies
     assert txl.pos_ff_workspace_bytes(rows, 512, 2048, torch.bfloat16) == \
         r256(rows * 2048 * 2) + r256(rows * 512 * 4)
+
+
+def test_stack_argument_errors_need_no_gpu():
+    """txl_stack_fwd checks every layer's arguments before it enqueues anything."""
+    from relative_position_memory_amd import txl
+    lib = txl._lib
+    dims = txl.layer_dims(2, 16, 64, 2, 32)
+    one = txl.stack_workspace_bytes(dims, 32, torch_bf16(), 1)
+    assert txl._lib.txl_stack_workspace_bytes(ctypes.byref(dims), 32, txl.BF16, 2) == 2 * one
+    assert txl._lib.txl_stack_workspace_bytes(ctypes.byref(dims), 32, txl.BF16, 0) == 0
+    assert txl._lib.txl_stack_workspace_bytes(ctypes.byref(dims), 32, txl.BF16, 9) == 0
+    seg = 2 * 16 * 64 * 2                  # one segment's [B][L][D] bf16
+    ring_bytes = 2 * 32 * 64 * 2
+    base = 0x100000000
+    h_in, h_out, ws = base, base + 0x1000000, base + 0x2000000
+    rdata = [base + 0x3000000 + i * 0x100000 for i in range(3)]
+    fake = ctypes.c_void_p(base + 0x4000000)
+    lw = txl.LayerWeights(*[fake.value] * 7)
+
+    def call(n_streams=2, streams=True, n_layers=3, n_seg=2, rings=None, R_rows=200,
+             ws_ptr=ws, ws_bytes=2 * one):
+        rs = rings or [txl.Ring(rdata[i], 32, 0, 0) for i in range(3)]
+        ra = (txl.Ring * 3)(*rs)
+        wa = (txl.LayerWeights * 3)(lw, lw, lw)
+        sa = (ctypes.c_void_p * 2)(None, None) if streams else None
+        rc = lib.txl_stack_fwd(sa, n_streams, txl.BF16, ctypes.byref(dims), n_layers, n_seg,
+                               h_in, ra, wa, fake, fake, fake, R_rows, h_out, ws_ptr, ws_bytes)
+        return rc, [(r.start, r.len) for r in ra]
+
+    assert call(n_streams=0)[0] == txl.EINVAL
+    assert call(n_streams=9)[0] == txl.EINVAL
+    assert call(streams=False)[0] == txl.EINVAL
+    assert call(n_layers=0)[0] == txl.EINVAL
+    assert call(n_seg=0)[0] == txl.EINVAL
+    assert call(ws_ptr=ws + 8)[0] == txl.EINVAL               # not 256-byte aligned
+    assert call(ws_bytes=2 * one - 1)[0] == txl.EWORKSPACE
+    # R must cover the longest memory a layer reaches (len grows by L per segment up
+    # to M) + L: from empty rings over 2 segments that is 16 + 16 rows
+    assert call(R_rows=31)[0] == txl.EINVAL
+    # bad ring state, and two layers sharing ring memory
+    assert call(rings=[txl.Ring(rdata[0], 32, 32, 0)] * 3)[0] == txl.EINVAL
+    rc, states = call(rings=[txl.Ring(rdata[0], 32, 0, 5), txl.Ring(rdata[0] + ring_bytes // 2, 32, 0, 5),
+                             txl.Ring(rdata[2], 32, 0, 5)])
+    assert rc == txl.EINVAL and states == [(0, 5)] * 3      # rejected, rings untouched
+    # h_out overlapping h_in
+    sa = (ctypes.c_void_p * 1)(None)
+    ra = (txl.Ring * 1)(txl.Ring(rdata[0], 32, 0, 0))
+    wa = (txl.LayerWeights * 1)(lw)
+    assert lib.txl_stack_fwd(sa, 1, txl.BF16, ctypes.byref(dims), 1, 2, h_in, ra, wa, fake, fake,
+                             fake, 200, h_in + seg, ws, one) == txl.EINVAL
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
