@@ -66,7 +66,7 @@ def parse():
     p.add_argument("--traffic-summary", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
                    help="print the attention's HBM traffic summary from two rocprofv3 --pmc "
                         "runs (FETCH_SIZE, WRITE_SIZE) of bench.py --calib-copy")
-    p.add_argument("--trace-summary", metavar="STATS_CSV",
+    p.add_argument("--trace-summary", nargs="+", metavar="CSV",
                    help="print the per-kernel table of a rocprofv3 --kernel-trace --stats run")
     p.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                    help="no GPU work: summarise rocprofv3 --pmc counter CSVs (per kernel: "
@@ -776,8 +776,11 @@ def traffic_summary(workload, fetch_csv, write_csv):
     print("\n".join(lines), flush=True)
 
 
-def trace_summary(path, top=14):
-    """Per-kernel table of rocprofv3's kernel stats CSV: calls, mean, min, max, share."""
+def trace_summary(path, trace=None, top=14):
+    """Per-kernel table of rocprofv3's kernel stats CSV: calls, mean, min, max, share.
+    With the per-dispatch kernel trace CSV as well, a second table splits each
+    kernel's dispatches into those that ran alone on the GPU (no other dispatch
+    overlapping them in time) and those that shared it with another stream's work."""
     import csv
     rows = list(csv.DictReader(open(path)))
     print(f"{'kernel':78s} {'calls':>6s} {'mean_us':>9s} {'min_us':>8s} {'max_us':>8s} "
@@ -786,6 +789,26 @@ def trace_summary(path, top=14):
         print(f"{r['Name'][:78]:78s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
               f"{float(r['MinNs']) / 1e3:8.2f} {float(r['MaxNs']) / 1e3:8.2f} "
               f"{float(r['Percentage']):5.1f}%")
+    if not trace:
+        return
+    ds = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                 for r in csv.DictReader(open(trace))), key=lambda t: t[0])
+    alone = {}
+    end_max = -1
+    for i, (t0, t1, name) in enumerate(ds):
+        nxt = ds[i + 1][0] if i + 1 < len(ds) else None
+        solo = t0 >= end_max and (nxt is None or t1 <= nxt)
+        end_max = max(end_max, t1)
+        alone.setdefault(name, ([], []))[0 if solo else 1].append((t1 - t0) / 1e3)
+    names = [r["Name"] for r in rows[:top]]
+    print()
+    print(f"{'kernel (dispatches alone on the GPU | overlapping another)':78s} {'alone':>6s} "
+          f"{'mean_us':>9s} {'shared':>7s} {'mean_us':>9s}")
+    for n in names:
+        a, b = alone.get(n, ([], []))
+        ma = f"{sum(a) / len(a):9.2f}" if a else f"{'-':>9s}"
+        mb = f"{sum(b) / len(b):9.2f}" if b else f"{'-':>9s}"
+        print(f"{n[:78]:78s} {len(a):6d} {ma} {len(b):7d} {mb}")
 
 
 def main():
@@ -797,7 +820,7 @@ def main():
         traffic_summary(*args.traffic_summary)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary)
+        trace_summary(*args.trace_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
