@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="charlm", choices=WORKLOAD_NAMES + ("tiny",))
     p.add_argument("--attn-reps", type=int, default=50)
+    p.add_argument("--attn-variant", type=int, default=0, choices=(0, 1, 2),
+                   help="attention kernel (txl_attn_variant): 0 by shape, 1 the 64-query "
+                        "kernel, 2 the 128-query kernel with key splits")
     p.add_argument("--streams", type=int, default=4,
                    help="HIP streams the stack's segments go round (txl_stack_fwd); 1 = serial")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -846,6 +849,7 @@ def main():
     x = I.make_inputs(w, seed=0)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     es = 2 if w.dtype == "bf16" else 4
+    txl.attn_variant(args.attn_variant)
     dev = lambda a: torch.from_numpy(a).to(tdt).cuda()
     Ws = [{k: dev(v) for k, v in lw.items()} for lw in x["weights"]]
     lws = [txl.layer_weights(Wl) for Wl in Ws]
@@ -972,6 +976,7 @@ def main():
                        "unit": "GB/s", "frac": mu_bytes / (mu_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                        "bound": "hbm", "kernel": "ring_copy_kernel"},
         "step_tflops": step_flops / (ms / 1e3) / 1e12,
+        "attn_variant": args.attn_variant,
         "schedule": {"entry_point": "txl_stack_fwd", "streams": args.streams,
                      "serial_ms_per_step": ms_serial,
                      "note": "segments go round the streams, segment s+1 one layer behind "

@@ -512,6 +512,23 @@ int txl_pos_ff(void* stream, int dtype, int64_t rows, int64_t d_model, int64_t d
                void* workspace, size_t ws_bytes);
 
 /* Static text for a status, followed by the calling thread's detail of its last error. */
+/*
+ * Which bf16 matrix-core attention kernel txl_rel_attn_fwd and the layer steps
+ * run (process-wide; the result is the same to rounding, the speed differs):
+ *   0  by shape (the default): the 128-query kernel where its tiles fill at
+ *      least two per CU and the last query tile has 16 or more 64-key tiles;
+ *      else the 64-query kernel (three 4-wave workgroups per CU, no key split)
+ *      where the shape has at least two of its 64-query tiles per CU; else the
+ *      128-query kernel with its planned key splits;
+ *   1  the 64-query kernel wherever the matrix-core path applies;
+ *   2  the 128-query kernel with its planned key splits.
+ * For tests and tuning.  Workspace sizes follow the setting in force when they
+ * are asked for; a call whose workspace cannot hold the planned key-split
+ * partials runs with fewer parts.  Returns the previous setting, or TXL_EINVAL.
+ * Not synchronised with calls running on other host threads.
+ */
+int txl_attn_variant(int variant);
+
 const char* txl_status_string(int status);
 
 #ifdef __cplusplus

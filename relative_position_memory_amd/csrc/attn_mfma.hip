@@ -35,6 +35,7 @@
 #include "txl_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <functional>
 #include <mutex>
 #include <vector>
@@ -597,6 +598,352 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   }
 }
 
+// ---- 64-query workgroups -------------------------------------------------------------
+// The same arithmetic with one 16-query group per wave: a workgroup is 4 waves =
+// 64 queries of one (batch, head), 155 registers per lane and 48 KB of LDS, so
+// three workgroups share a CU (12 waves, three per SIMD) where the 128-query
+// kernel fits two; more waves cover each wave's chain of dependent LDS and
+// matrix steps, and the finer query tiles leave a shorter tail (a 512-query
+// segment has 8 tiles of 9 .. 16 key tiles instead of 4 of 10 .. 16).
+// Every buffer is single: K, V, a 2-block r ring and each wave's shifted
+// position term.  Two barriers per key tile order the loads:
+//   top of tile t:  K(t) and the r blocks of tile t have landed; V(t) is issued
+//                   into the V buffer (its last reader was the P.V of tile t - 1)
+//   middle:         V(t) has landed; every wave has read its K and r fragments,
+//                   so K(t + 1) and the r block tile t + 1 adds (into the slot of
+//                   tile t's upper block) are issued
+// Each load has half a tile to land; the other workgroups of the CU run meanwhile.
+constexpr int BQ64 = 64;        // queries per workgroup
+constexpr int RR64 = 2 * BK;    // r ring rows (two 64-distance blocks)
+
+struct __align__(16) Smem64 {
+  uint16_t K[BK * DP];        // key tile, [key][c], swizzled 16-byte chunks
+  uint16_t V[BK * DP];        // value tile
+  uint16_t R[RR64 * DP];      // r ring, row (distance - mem_len) mod 128, swizzled
+  float W[NW][WGF];           // gathered position term of the wave's 16 queries
+};
+
+template <bool LSE>
+__global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, int groups) {
+  extern __shared__ __align__(16) char smem_raw[];
+  Smem64& sm = *(Smem64*)smem_raw;
+
+  // XCD-aware order as in the 128-query kernel: XCD x owns the groups x, x + 8,
+  // ...; each XCD issues all its groups' last query tile (most key tiles) first.
+  const int gpx = (groups + NXCD - 1) / NXCD;
+  const int xcd = blockIdx.x % NXCD, k_on = blockIdx.x / NXCD;
+  const int qt = nqt - 1 - k_on / gpx;
+  const int g = (k_on % gpx) * NXCD + xcd;
+  if (g >= groups) return;
+  const int64_t b = g / a.H, hd = g % a.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, n16 = lane & 15;
+  const int d = (int)a.d;
+  const int L = (int)a.L, len = (int)a.mem_len, T = len + L;
+  const int q0 = qt * BQ64;
+  const int i0w = q0 + wave * 16;
+  const int cl_max = (int)(a.d_load / 8) - 1;
+
+  const int imax_wg = (q0 + BQ64 - 1 < L - 1) ? q0 + BQ64 - 1 : L - 1;
+  const int n_kt = (len + imax_wg) / BK + 1;
+  const bool wave_has_rows = i0w < L;
+  const int imax_w = (i0w + 15 < L - 1) ? i0w + 15 : L - 1;
+  const int kt_w = wave_has_rows ? (len + imax_w) / BK : -1;
+
+  // ---- LDS-direct loads: instruction x (0, 1) of this wave fills tile rows
+  //      16 wave + 8 x .. + 7; lane -> row + lane / 8, slot lane % 8 ------------------
+  const uint16_t* kb = (const uint16_t*)a.k + b * a.kv_sb + hd * a.kv_sh;
+  const uint16_t* vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
+  const uint16_t* rb = (const uint16_t*)a.r + hd * a.r_sh;
+  const int kv_st = (int)a.kv_st, r_sp = (int)a.r_sp;
+  int drow[2], dch[2], dchv[2], ko[2], vo[2], ro[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    drow[x] = 16 * wave + 8 * x + (lane >> 3);
+    const int c = (lane & 7) ^ swz(drow[x]), cv = (lane & 7) ^ swzv(drow[x]);
+    dch[x] = 8 * (c < cl_max ? c : cl_max);
+    dchv[x] = 8 * (cv < cl_max ? cv : cl_max);
+    ko[x] = drow[x] * kv_st + dch[x];
+    vo[x] = drow[x] * kv_st + dchv[x];
+    ro[x] = drow[x] * r_sp + dch[x];
+  }
+  const int kvs = a.kv_cap > 0 ? (int)a.kv_start : 0;
+  const int kvc = a.kv_cap > 0 ? (int)a.kv_cap : 0x7fffffff - BK;
+  auto load_kv = [&](const uint16_t* base, uint16_t* lds, int j0, const int (&off)[2],
+                     const int (&ch)[2]) {
+    int p0 = kvs + j0;
+    p0 = p0 >= kvc ? p0 - kvc : p0;
+    if (j0 + BK <= T && p0 + BK <= kvc) {
+      const uint16_t* tb = base + p0 * kv_st;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) dma16(tb + off[x], lds + (16 * wave + 8 * x) * DP);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;
+        int p = kvs + j;
+        p = p >= kvc ? p - kvc : p;
+        dma16(base + p * kv_st + ch[x], lds + (16 * wave + 8 * x) * DP);
+      }
+    }
+  };
+  // r rows of relative distances e0 .. e0 + 63 (e = distance - mem_len, e0 % 64 == 0)
+  auto load_r = [&](int e0) {
+    uint16_t* dst = sm.R + ((e0 & (RR64 - 1)) + 16 * wave) * DP;
+    const int dist0 = len + e0;
+    if (dist0 >= 0 && dist0 + BK <= T) {
+      const uint16_t* tb = rb + dist0 * r_sp;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) dma16(tb + ro[x], dst + 8 * x * DP);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        int dist = dist0 + drow[x];
+        dist = dist < 0 ? 0 : (dist < T ? dist : T - 1);
+        dma16(rb + dist * r_sp + dch[x], dst + 8 * x * DP);
+      }
+    }
+  };
+
+  // fragment offsets, as in the 128-query kernel
+  int koff[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) koff[s] = n16 * DP + 8 * ((4 * s + g4) ^ swz(n16));
+  int voff[4];
+  {
+    const int vrow = 4 * g4 + (n16 >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int piece = 4 * db + (n16 & 3);
+      voff[db] = vrow * DP + 8 * ((piece >> 1) ^ swzv(vrow)) + 4 * (piece & 1);
+    }
+  }
+  float* const wbuf = sm.W[wave];
+  const int sprot = 4 * n16 + 3 * (n16 >> 2);
+  auto sp_slot = [&](int jj) { return n16 * 64 + ((((jj >> 2) + sprot) & 15) << 2) + (jj & 3); };
+  // r fragments: window block bw (0..4) of the wave's 80 rows, row n16 is relative
+  // distance i0w - j0 + 15 - 16 bw - n16 (key jj = 16 bw + n16' - 15 + query),
+  // stored at ring row (that) mod 128
+  int roff[5];
+
+  // ---- first tile: K, V and the two r blocks of its window ----------------------------
+  {
+    const int j0 = 0;
+    load_kv(kb, sm.K, j0, ko, dch);
+    load_kv(vb, sm.V, j0, vo, dchv);
+    load_r(q0 - j0 - BK);
+    load_r(q0 - j0);
+#pragma unroll
+    for (int bw = 0; bw < 5; ++bw) {
+      const int e = i0w - j0 + 15 - 16 * bw - n16;
+      const int rr = e & (RR64 - 1);
+      roff[bw] = rr * DP + 8 * (g4 ^ swz(rr));
+    }
+  }
+
+  // ---- this lane's queries, pre-scaled: query i0w + n16, k-step s columns 32 s + 8 g4 ..
+  bf16x8 qc[2], qp[2];
+  {
+    const uint16_t* ur = (const uint16_t*)a.u + hd * d;
+    const uint16_t* vr = (const uint16_t*)a.vb + hd * d;
+    const float sl2 = a.scale * LOG2E;
+    const bool uv_vec = (d % 8 == 0) && ((((uintptr_t)a.u) | ((uintptr_t)a.vb)) % 16 == 0);
+    const int i = i0w + n16;
+    const int ic = i < L ? i : L - 1;
+    const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + (int64_t)ic * a.q_st + hd * a.q_sh;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c0 = 32 * s + 8 * g4;
+      const int cc = c0 / 8 < cl_max ? c0 : 8 * cl_max;
+      const uint4 raw = *(const uint4*)(qrow + cc);
+      const uint16_t* rv = (const uint16_t*)&raw;
+      uint16_t uh[8], vh[8];
+      if (uv_vec && c0 < d) {
+        *(uint4*)uh = *(const uint4*)(ur + c0);
+        *(uint4*)vh = *(const uint4*)(vr + c0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uh[e] = c0 + e < d ? ur[c0 + e] : (uint16_t)0;
+          vh[e] = c0 + e < d ? vr[c0 + e] : (uint16_t)0;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool ok = c0 + e < d && i < L;
+        const float x = bf16_to_f32(rv[e]);
+        qc[s][e] = (__bf16)(ok ? (x + bf16_to_f32(uh[e])) * sl2 : 0.f);
+        qp[s][e] = (__bf16)(ok ? (x + bf16_to_f32(vh[e])) * sl2 : 0.f);
+      }
+    }
+  }
+
+  // softmax state (see the 128-query kernel): reference s_off folded into the
+  // position product's accumulator, limit lim, row sums on the matrix core
+  constexpr float TAU = 8.f;
+  float s_off = 0.f, lim = -INFINITY;
+  f32x4 acc[4], acc_l = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  float* srow_base = nullptr;
+  if (a.scores) srow_base = a.scores + ((b * a.H + hd) * a.L) * (int64_t)T;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int j0 = kt * BK;
+    wait_dma();
+    barrier();
+    if (kt > 0) load_kv(vb, sm.V, j0, vo, dchv);
+    const bool work = kt <= kt_w;
+    const int Dw = len + i0w - j0;  // distance of (query i0w, key j0)
+    f32x4 sc[4];
+    if (work) {
+      // ---- position term through the shifted LDS stores, then the content term
+      bf16x8 rf[5][2], kf[4][2];
+#pragma unroll
+      for (int bw = 0; bw < 5; ++bw) {
+        rf[bw][0] = lds_b128(sm.R + roff[bw]);
+        rf[bw][1] = lds_b128(sm.R + (roff[bw] ^ 32));
+      }
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) kf[kbk][s] = lds_b128(sm.K + kbk * 16 * DP + koff[s]);
+      f32x4 wv[5];
+#pragma unroll
+      for (int bw = 0; bw < 5; ++bw) {
+        f32x4 w = {-s_off, -s_off, -s_off, -s_off};
+        w = mfma(rf[bw][0], qp[0], w);
+        wv[bw] = mfma(rf[bw][1], qp[1], w);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = 4 * g4 + e - 15 + n16;  // key of block 0, in -15 .. 15
+        wbuf[sp_slot(jj & (BK - 1))] = jj >= 0 ? wv[0][e] : wv[4][e];
+      }
+#pragma unroll
+      for (int bw = 1; bw < 4; ++bw)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wbuf[sp_slot(16 * bw + 4 * g4 + e - 15 + n16)] = wv[bw][e];
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk) {
+        f32x4 c = *(const f32x4*)(wbuf + n16 * 64 + (((4 * kbk + g4 + sprot) & 15) << 2));
+        c = mfma(kf[kbk][0], qc[0], c);
+        c = mfma(kf[kbk][1], qc[1], c);
+        sc[kbk] = c;
+      }
+    }
+    // middle barrier: V(kt) has landed, K(kt) and this tile's r fragments are read
+    wait_dma();
+    barrier();
+    if (kt + 1 < n_kt) {
+      load_kv(kb, sm.K, j0 + BK, ko, dch);
+      load_r(q0 - j0 - 2 * BK);  // the block tile kt + 1 adds, over tile kt's upper one
+    }
+#pragma unroll
+    for (int bw = 0; bw < 5; ++bw) roff[bw] = (roff[bw] - BK * DP) & (RR64 * DP - 1);
+    if (!work) continue;
+
+    if (j0 + BK - 1 > len + i0w) {
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 16 * kbk + 4 * g4 + e;
+          sc[kbk][e] = (jj - n16 > Dw) ? -INFINITY : sc[kbk][e];
+        }
+    }
+    if (srow_base) {
+      const int i = i0w + n16;
+      if (i < L) {
+        float* srow = srow_base + (int64_t)i * T;
+#pragma unroll
+        for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = j0 + 16 * kbk + 4 * g4 + e;
+            if (j < T) srow[j] = (sc[kbk][e] + s_off) * (1.0f / LOG2E);
+          }
+      }
+    }
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lmax = fmaxf(lmax, sc[kbk][e]);
+    if (__any(lmax > lim)) {
+      const float tmax = max4(lmax);
+      const bool move = tmax > lim;
+      const float delta = move ? tmax : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[kbk][e] -= delta;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc_l[e] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db][e] *= alpha;
+      }
+      s_off += delta;
+      if (move) lim = TAU;
+    }
+    // ---- P = exp2(S - s_off) packed to bf16; O^T += V^T . P^T ---------------------
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8 vf[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        vf[h][db] = lds_tr2(sm.V + 32 * h * DP + voff[db], sm.V + (32 * h + 16) * DP + voff[db]);
+#pragma unroll
+    for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[kbk][e] = __builtin_amdgcn_exp2f(sc[kbk][e]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w0 = pack2(sc[2 * h][0], sc[2 * h][1]);
+      const uint32_t w1 = pack2(sc[2 * h][2], sc[2 * h][3]);
+      const uint32_t w2 = pack2(sc[2 * h + 1][0], sc[2 * h + 1][1]);
+      const uint32_t w3 = pack2(sc[2 * h + 1][2], sc[2 * h + 1][3]);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = mfma(vf[h][db], pb, acc[db]);
+      acc_l = mfma(ones, pb, acc_l);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  // ---- epilogue: out[i][c] = acc / l; lane (g4, n16) of block db holds query
+  //      i0w + n16, columns 16 db + 4 g4 .. + 3 -------------------------------------------
+  if (!wave_has_rows) return;
+  const int i = i0w + n16;
+  if (i >= L) return;
+  const float l_tot = acc_l[0];
+  const float inv = 1.f / l_tot;
+  if constexpr (LSE) {
+    if (g4 == 0) a.lse[(int64_t)g * L + i] = s_off + __log2f(l_tot);
+  }
+  uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
+  const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
+                   ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int c = 16 * db + 4 * g4;
+    if (vec) {
+      if (c < d)
+        *(uint2*)(orow + c) = make_uint2(pack2(acc[db][0] * inv, acc[db][1] * inv),
+                                         pack2(acc[db][2] * inv, acc[db][3] * inv));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c + e < d) orow[c + e] = bf16_bits(acc[db][e] * inv);
+    }
+  }
+}
+
 // Merge of the parts of a split query tile: one wave per (query tile, group,
 // 16-query block wq = 2 w + gm), whose lanes take the writing lanes' places
 // (lane (g4, n16) of writing wave w holds query 32 w + 16 gm + n16, columns
@@ -737,11 +1084,17 @@ double plan_makespan(const PlanShape& sh, const int* k, std::vector<double>& siz
 
 }  // namespace
 
+// Kernel choice (txl_attn_variant): 0 by shape, 1 the 64-query kernel, 2 the
+// 128-query kernel with its planned key splits.
+std::atomic<int> g_variant{0};
+
 AttnPlan plan_uncached(const AttnArgs& a, int num_cus, size_t budget);
 
 // Plans are cached per shape (the search costs far more than a launch).
+int attn_set_variant(int v) { return g_variant.exchange(v); }
+
 AttnPlan attn_mfma_plan(const AttnArgs& a, int num_cus, size_t budget) {
-  struct Entry { int64_t groups, L, mem_len; int cus; size_t budget; AttnPlan plan; };
+  struct Entry { int64_t groups, L, mem_len; int cus; size_t budget; int var; AttnPlan plan; };
   static std::mutex mu;
   static Entry cache[16];
   static int n_cached = 0, next = 0;
@@ -751,13 +1104,13 @@ AttnPlan attn_mfma_plan(const AttnArgs& a, int num_cus, size_t budget) {
     for (int i = 0; i < n_cached; ++i) {
       const Entry& e = cache[i];
       if (e.groups == groups && e.L == a.L && e.mem_len == a.mem_len && e.cus == num_cus &&
-          e.budget == budget)
+          e.budget == budget && e.var == g_variant.load(std::memory_order_relaxed))
         return e.plan;
     }
   }
   const AttnPlan p = plan_uncached(a, num_cus, budget);
   std::lock_guard<std::mutex> lock(mu);
-  cache[next] = {groups, a.L, a.mem_len, num_cus, budget, p};
+  cache[next] = {groups, a.L, a.mem_len, num_cus, budget, g_variant.load(std::memory_order_relaxed), p};
   next = (next + 1) % 16;
   if (n_cached < 16) ++n_cached;
   return p;
@@ -767,6 +1120,22 @@ AttnPlan plan_uncached(const AttnArgs& a, int num_cus, size_t budget) {
   AttnPlan p{};
   const int64_t nqt = (a.L + BQ - 1) / BQ;
   const int64_t groups = a.B * a.H;
+  // By shape.  A long key loop (16 or more key tiles for the last query tile)
+  // with enough 128-query tiles for a full round of two per CU: the 128-query
+  // kernel, whose two query groups per wave share every K, V and r fragment read
+  // (a 512-token segment over a 512-token memory).  Otherwise, with enough
+  // 64-query tiles for two per CU, the 64-query kernel, unsplit: finer tiles
+  // and three workgroups per CU (the word model's 150-token segments, the
+  // 384-token training segments).  Fewer (a long memory over few query rows):
+  // the 128-query kernel, its key axis split as planned below.
+  const int var = g_variant.load(std::memory_order_relaxed);
+  const int64_t n_kt_last = (a.mem_len + a.L - 1) / BK + 1;
+  const bool long_loop = n_kt_last >= 16 && groups * nqt >= 2 * (int64_t)num_cus;
+  if (var == 1 ||
+      (var == 0 && !long_loop && groups * ((a.L + BQ64 - 1) / BQ64) >= 2 * (int64_t)num_cus)) {
+    p.q64 = 1;
+    return p;
+  }
   if (nqt > ATTN_MAXQT || groups <= 0) return p;  // default order, no split
   PlanShape sh{};
   sh.nqt = (int)nqt;
@@ -906,6 +1275,29 @@ bool attn_mfma_supported(const AttnArgs& a) {
 
 hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
   (void)num_cus;
+  if (a.plan.q64) {
+    const int nqt64 = (int)((a.L + BQ64 - 1) / BQ64);
+    const int groups = (int)(a.B * a.H);
+    const int64_t nblocks = (int64_t)nqt64 * NXCD * ((groups + NXCD - 1) / NXCD);
+    const size_t smem = sizeof(Smem64);
+    static bool attr64 = false;
+    if (!attr64) {
+      hipError_t e = hipFuncSetAttribute((const void*)attn_q64_kernel<false>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)attn_q64_kernel<true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (e != hipSuccess) return e;
+      attr64 = true;
+    }
+    if (a.lse)
+      hipLaunchKernelGGL(attn_q64_kernel<true>, dim3((unsigned)nblocks), dim3(256), smem, s, a,
+                         nqt64, groups);
+    else
+      hipLaunchKernelGGL(attn_q64_kernel<false>, dim3((unsigned)nblocks), dim3(256), smem, s, a,
+                         nqt64, groups);
+    return hipGetLastError();
+  }
   const int nqt = (int)((a.L + BQ - 1) / BQ);
   const int groups = (int)(a.B * a.H);
   const int ncls = a.plan.ncls > 0 ? a.plan.ncls : nqt;

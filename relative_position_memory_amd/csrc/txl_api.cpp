@@ -367,6 +367,12 @@ KvWs kv_ws_layout(const txl_layer_dims& dm, int64_t es, size_t part_bytes) {
 
 extern "C" {
 
+int txl_attn_variant(int variant) {
+  g_detail[0] = 0;
+  if (variant < 0 || variant > 2) return fail(TXL_EINVAL, "variant %d not in 0 .. 2", variant);
+  return txl::attn_set_variant(variant);
+}
+
 const char* txl_status_string(int status) {
   const char* s;
   switch (status) {

@@ -76,6 +76,7 @@ struct AttnPlan {
   uint8_t slot0[ATTN_MAXQT];       // first partial slot of a split tile's parts
   uint8_t split_qt[ATTN_MAXQT];    // the split query tiles (nsplit_qt of them)
   int nsplit_qt;
+  int q64;                         // run the 64-query kernel (no split)
 };
 
 struct AttnArgs {
@@ -119,6 +120,8 @@ __host__ __device__ inline int64_t kv_row(const AttnArgs& a, int64_t j) {
 // num_cus CUs whose partials (and counters) fit in budget bytes, and the bytes a
 // plan needs (0 when it splits nothing).
 AttnPlan attn_mfma_plan(const AttnArgs& a, int num_cus, size_t budget);
+// Kernel choice of the bf16 matrix-core attention (txl_attn_variant); returns the old one.
+int attn_set_variant(int v);
 size_t attn_plan_bytes(const AttnArgs& a, const AttnPlan& p);
 // Points a's partial buffers into scratch (256-byte aligned inside it).
 void attn_plan_bind(AttnArgs& a, const AttnPlan& p, void* scratch);

@@ -64,6 +64,19 @@ _lib.txl_status_string.argtypes = [ctypes.c_int]
 _lib.txl_status_string.restype = ctypes.c_char_p
 
 
+_lib.txl_attn_variant.argtypes = [ctypes.c_int]
+_lib.txl_attn_variant.restype = ctypes.c_int
+
+
+def attn_variant(variant: int) -> int:
+    """txl_attn_variant: 0 by shape, 1 the 64-query kernel, 2 the 128-query kernel
+    with key splits; returns the previous setting."""
+    rc = _lib.txl_attn_variant(int(variant))
+    if rc < 0:
+        raise TxlError(rc, "txl_attn_variant")
+    return rc
+
+
 class TxlError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_string(status)}")
