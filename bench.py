@@ -705,8 +705,8 @@ def _pmc_per_dispatch(path, counter):
 
 
 def traffic_summary(workload, fetch_csv, write_csv):
-    """HBM bytes per attention launch (attn_mfma_kernel, plus attn_part_merge_kernel
-    when the plan splits keys) from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    """HBM bytes per attention launch (attn_mfma_kernel or attn_q64_kernel, plus
+    attn_part_merge_kernel when the plan splits keys) from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the 256 MiB device copy that
     --calib-copy adds to the run."""
     fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
@@ -729,8 +729,10 @@ def traffic_summary(workload, fetch_csv, write_csv):
             return 0, 0.0
         n, g, v = max(hits, key=lambda t: len(t[2]))
         return len(v), mean(v)
-    na_f, af = kern(fetch, "attn_mfma_kernel")
-    na_w, aw = kern(write, "attn_mfma_kernel")
+    # the attention kernel the workload runs (the 128- or the 64-query one)
+    akey = max(("attn_mfma_kernel", "attn_q64_kernel"), key=lambda k: kern(fetch, k)[0])
+    na_f, af = kern(fetch, akey)
+    na_w, aw = kern(write, akey)
     nm_f, mf = kern(fetch, "attn_part_merge_kernel")
     nm_w, mw = kern(write, "attn_part_merge_kernel")
     hbm = (af * fs + aw * wsc + mf * fs + mw * wsc) * 1024
@@ -759,6 +761,7 @@ def traffic_summary(workload, fetch_csv, write_csv):
         f"copy_write_kib: {cw:.1f}",
         f"fetch_scale: {fs:.4f}",
         f"write_scale: {wsc:.4f}",
+        f"attn_kernel: {akey}",
         f"attn_dispatches: {na_f} (fetch run), {na_w} (write run)",
         f"attn_fetch_kib_raw: {af:.1f}",
         f"attn_write_kib_raw: {aw:.1f}",
@@ -927,7 +930,7 @@ def main():
         roof = {"bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": attn_gbs / PEAK_HBM_GBS, "mfma_frac": attn_tflops / PEAK_BF16_TFLOPS}
     roof.update({"traffic": read_traffic(w.name),
-                 "kernel": "attn_mfma_kernel" + (" + key-split merge" if nws else ""),
+                 "kernel": txl.attn_kernel(tdt, w.B, w.H, w.L, w.M, dpad),
                  "launch_us": attn_s * 1e6, "flop_per_launch": af, "bytes_per_launch": ab})
 
     # one layer step alone (full memory; projections, attention, output projection +

@@ -529,6 +529,22 @@ int txl_pos_ff(void* stream, int dtype, int64_t rows, int64_t d_model, int64_t d
  */
 int txl_attn_variant(int variant);
 
+/*
+ * Which kernel txl_rel_attn_fwd runs at these sizes, for dense head rows of
+ * d_head elements in an aligned layout (the workspace of txl_layer_step, or
+ * 16-byte aligned rows whose pitches are multiples of 8): one of
+ * txl_attn_kernel_kind under the txl_attn_variant setting in force, or
+ * TXL_EINVAL.
+ */
+typedef enum {
+  TXL_ATTN_VECTOR = 0,       /* vector-unit kernel (fp32, or rows the matrix cores do not take) */
+  TXL_ATTN_ONE_QUERY = 1,    /* single-query kernel with its key-part merge (L = 1)            */
+  TXL_ATTN_Q128 = 2,         /* matrix cores, 128-query workgroups                              */
+  TXL_ATTN_Q128_SPLIT = 3,   /* the same with the key axis split and a merge kernel             */
+  TXL_ATTN_Q64 = 4           /* matrix cores, 64-query workgroups, three per CU                 */
+} txl_attn_kernel_kind;
+int txl_attn_kernel(int dtype, int64_t B, int64_t H, int64_t L, int64_t mem_len, int64_t d_head);
+
 const char* txl_status_string(int status);
 
 #ifdef __cplusplus

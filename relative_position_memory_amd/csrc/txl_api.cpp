@@ -474,6 +474,24 @@ size_t txl_rel_attn_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t L, 
   return attn_plan_bytes(dtype, a);
 }
 
+int txl_attn_kernel(int dtype, int64_t B, int64_t H, int64_t L, int64_t mem_len,
+                    int64_t d_head) {
+  g_detail[0] = 0;
+  if ((dtype != TXL_FP32 && dtype != TXL_BF16) || B < 1 || H < 1 || L < 1 || mem_len < 0 ||
+      d_head < 1 || d_head > 128)
+    return fail(TXL_EINVAL, "invalid sizes or dtype");
+  txl::AttnArgs a{};
+  a.B = B; a.H = H; a.L = L; a.mem_len = mem_len; a.d = d_head; a.d_load = d_head;
+  a.q = a.k = a.v = a.r = (const void*)(uintptr_t)256;
+  a.q_sb = a.q_st = a.q_sh = a.kv_sb = a.kv_st = a.kv_sh = a.r_sp = a.r_sh = 64;
+  if (dtype != TXL_BF16) return TXL_ATTN_VECTOR;
+  if (txl::attn_decode_supported(a)) return TXL_ATTN_ONE_QUERY;
+  if (!txl::attn_mfma_supported(a)) return TXL_ATTN_VECTOR;
+  const txl::AttnPlan p = txl::attn_mfma_plan(a, num_cus(), (size_t)-1);
+  if (p.q64) return TXL_ATTN_Q64;
+  return p.slots > 0 ? TXL_ATTN_Q128_SPLIT : TXL_ATTN_Q128;
+}
+
 size_t txl_layer_workspace_bytes(const txl_layer_dims* dims, int64_t mem_capacity, int dtype) {
   if (check_dims(dims) != TXL_OK || mem_capacity < 0) return 0;
   if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;

@@ -77,6 +77,21 @@ def attn_variant(variant: int) -> int:
     return rc
 
 
+_lib.txl_attn_kernel.argtypes = [ctypes.c_int] + [_i64] * 5
+_lib.txl_attn_kernel.restype = ctypes.c_int
+ATTN_KERNEL_NAMES = {0: "attn_generic (vector unit)", 1: "attn_decode_kernel + merge",
+                     2: "attn_mfma_kernel", 3: "attn_mfma_kernel + key-split merge",
+                     4: "attn_q64_kernel"}
+
+
+def attn_kernel(dtype: torch.dtype, B, H, L, mem_len, d_head) -> str:
+    """txl_attn_kernel: the name of the kernel txl_rel_attn_fwd runs at these sizes."""
+    rc = _lib.txl_attn_kernel(dtype_code(dtype), B, H, L, int(mem_len), d_head)
+    if rc < 0:
+        raise TxlError(rc, "txl_attn_kernel")
+    return ATTN_KERNEL_NAMES[rc]
+
+
 class TxlError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_string(status)}")
