@@ -125,6 +125,158 @@ __device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ---- pieces shared by the 128- and the 64-query kernels -------------------------------
+
+// LDS-direct loads of one (batch, head)'s key, value and r rows.  Instruction x
+// (0, 1) of a wave fills tile rows 16 wave + 8 x .. + 7: lane -> row + lane / 8,
+// 16-byte slot lane % 8 (chunk slot ^ swz, V: ^ swzv); chunks past d_load repeat
+// a real one (times q = 0).  Interior tiles address from a uniform tile base
+// plus the lane's fixed offset; rows past the ends are clamped (they feed masked
+// scores only).  Keys may sit in a ring (row (kv_start + j) % kv_cap); without
+// one the cap is past every key, so the row is j.
+struct TileLoads {
+  const uint16_t *kb, *vb, *rb;
+  int kv_st, r_sp, T, len, kvs, kvc, wave;
+  int drow[2], dch[2], dchv[2], ko[2], vo[2], ro[2];
+
+  __device__ TileLoads(const AttnArgs& a, int64_t b, int64_t hd, int wave_, int lane) {
+    kb = (const uint16_t*)a.k + b * a.kv_sb + hd * a.kv_sh;
+    vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
+    rb = (const uint16_t*)a.r + hd * a.r_sh;
+    kv_st = (int)a.kv_st;
+    r_sp = (int)a.r_sp;
+    len = (int)a.mem_len;
+    T = len + (int)a.L;
+    kvs = a.kv_cap > 0 ? (int)a.kv_start : 0;
+    kvc = a.kv_cap > 0 ? (int)a.kv_cap : 0x7fffffff - BK;
+    wave = wave_;
+    const int cl_max = (int)(a.d_load / 8) - 1;  // last readable 16-byte chunk of a row
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      drow[x] = 16 * wave + 8 * x + (lane >> 3);
+      const int c = (lane & 7) ^ swz(drow[x]), cv = (lane & 7) ^ swzv(drow[x]);
+      dch[x] = 8 * (c < cl_max ? c : cl_max);
+      dchv[x] = 8 * (cv < cl_max ? cv : cl_max);
+      ko[x] = drow[x] * kv_st + dch[x];  // this lane's element offsets within a tile
+      vo[x] = drow[x] * kv_st + dchv[x];
+      ro[x] = drow[x] * r_sp + dch[x];
+    }
+  }
+  __device__ void kv(const uint16_t* base, uint16_t* lds, int j0, const int (&off)[2],
+                     const int (&ch)[2]) const {
+    int p0 = kvs + j0;
+    p0 = p0 >= kvc ? p0 - kvc : p0;
+    if (j0 + BK <= T && p0 + BK <= kvc) {
+      const uint16_t* tb = base + p0 * kv_st;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) dma16(tb + off[x], lds + (16 * wave + 8 * x) * DP);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;
+        int p = kvs + j;
+        p = p >= kvc ? p - kvc : p;
+        dma16(base + p * kv_st + ch[x], lds + (16 * wave + 8 * x) * DP);
+      }
+    }
+  }
+  // keys j0 .. j0 + 63 into a K or a V tile
+  __device__ void k(uint16_t* lds, int j0) const { kv(kb, lds, j0, ko, dch); }
+  __device__ void v(uint16_t* lds, int j0) const { kv(vb, lds, j0, vo, dchv); }
+  // r rows of relative distances e0 .. e0 + 63 (e = distance - mem_len, e0 % 64 ==
+  // 0) into a ring of RING rows indexed by e mod RING
+  template <int RING>
+  __device__ void r(uint16_t* ring, int e0) const {
+    uint16_t* dst = ring + ((e0 & (RING - 1)) + 16 * wave) * DP;
+    const int dist0 = len + e0;
+    if (dist0 >= 0 && dist0 + BK <= T) {
+      const uint16_t* tb = rb + dist0 * r_sp;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) dma16(tb + ro[x], dst + 8 * x * DP);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        int dist = dist0 + drow[x];
+        dist = dist < 0 ? 0 : (dist < T ? dist : T - 1);
+        dma16(rb + dist * r_sp + dch[x], dst + 8 * x * DP);
+      }
+    }
+  }
+};
+
+// K fragment (16x16x32 A operand) of k-step s: row 16 kb + n16, chunk 4 s + g4
+__device__ inline int k_frag(int n16, int g4, int s) { return n16 * DP + 8 * ((4 * s + g4) ^ swz(n16)); }
+// V^T through transposing reads: lane (g4, n16) of a 16-lane group reads key row
+// 4 g4 + n16 / 4 (+ 32 h + 16 kb'), columns 16 db + 4 (n16 % 4) .. + 3
+__device__ inline int v_frag(int n16, int g4, int db) {
+  const int vrow = 4 * g4 + (n16 >> 2);
+  const int piece = 4 * db + (n16 & 3);  // 8-byte piece of the row
+  return vrow * DP + 8 * ((piece >> 1) ^ swzv(vrow)) + 4 * (piece & 1);
+}
+
+// (q_i + u) and (q_i + v) of query i as the B operands of k-steps 0 and 1 (lane
+// (g4, n16): columns 32 s + 8 g4 .. + 7), scaled by scale * log2(e) before they
+// are rounded to bf16; zero past d and for i >= L.
+__device__ inline void query_operands(const AttnArgs& a, int64_t b, int64_t hd, int i, int g4,
+                                      bf16x8 (&qc)[2], bf16x8 (&qp)[2]) {
+  const int d = (int)a.d, L = (int)a.L;
+  const int cl_max = (int)(a.d_load / 8) - 1;
+  const uint16_t* ur = (const uint16_t*)a.u + hd * d;
+  const uint16_t* vr = (const uint16_t*)a.vb + hd * d;
+  const float sl2 = a.scale * LOG2E;
+  const bool uv_vec = (d % 8 == 0) && ((((uintptr_t)a.u) | ((uintptr_t)a.vb)) % 16 == 0);
+  const int ic = i < L ? i : L - 1;
+  const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + (int64_t)ic * a.q_st + hd * a.q_sh;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int c0 = 32 * s + 8 * g4;
+    const int cc = c0 / 8 < cl_max ? c0 : 8 * cl_max;
+    const uint4 raw = *(const uint4*)(qrow + cc);
+    const uint16_t* rv = (const uint16_t*)&raw;
+    uint16_t uh[8], vh[8];
+    if (uv_vec && c0 < d) {
+      *(uint4*)uh = *(const uint4*)(ur + c0);
+      *(uint4*)vh = *(const uint4*)(vr + c0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uh[e] = c0 + e < d ? ur[c0 + e] : (uint16_t)0;
+        vh[e] = c0 + e < d ? vr[c0 + e] : (uint16_t)0;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = c0 + e < d && i < L;
+      const float x = bf16_to_f32(rv[e]);
+      qc[s][e] = (__bf16)(ok ? (x + bf16_to_f32(uh[e])) * sl2 : 0.f);
+      qp[s][e] = (__bf16)(ok ? (x + bf16_to_f32(vh[e])) * sl2 : 0.f);
+    }
+  }
+}
+
+// out[i][c] = acc * inv for query i < L: lane (g4, n16) of block db holds columns
+// 16 db + 4 g4 .. + 3
+__device__ inline void write_out(const AttnArgs& a, int64_t b, int64_t hd, int i, int g4,
+                                 const f32x4 (&acc)[4], float inv) {
+  const int d = (int)a.d;
+  uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
+  const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
+                   ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int c = 16 * db + 4 * g4;
+    if (vec) {
+      if (c < d)
+        *(uint2*)(orow + c) = make_uint2(pack2(acc[db][0] * inv, acc[db][1] * inv),
+                                         pack2(acc[db][2] * inv, acc[db][3] * inv));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c + e < d) orow[c + e] = bf16_bits(acc[db][e] * inv);
+    }
+  }
+}
+
 // LSE: also write each query's log-sum-exp (AttnArgs::lse).  A separate
 // instantiation, so the plain forward's code is untouched by it.
 template <bool LSE>
@@ -150,11 +302,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address math
   const int g4 = lane >> 4, n16 = lane & 15;  // 16x16 MFMA lane coordinates
-  const int d = (int)a.d;
   const int L = (int)a.L, len = (int)a.mem_len, T = len + L;
   const int q0 = qt * BQ;
   const int i0w = q0 + wave * BQW;
-  const int cl_max = (int)(a.d_load / 8) - 1;  // last readable 16-byte chunk of a row
 
   // key tiles of this workgroup: all tiles up to the last query's last key,
   // or this part's share of them
@@ -165,82 +315,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   const int imax_w = (i0w + BQW - 1 < L - 1) ? i0w + BQW - 1 : L - 1;
   const int kt_w = wave_has_rows ? (len + imax_w) / BK : -1;
 
-  // ---- LDS-direct loads: instruction x (0, 1) of this wave fills tile rows
-  //      16 wave + 8 x .. + 7; lane -> row + lane / 8, slot lane % 8 (chunk slot ^ swz)
-  const uint16_t* kb = (const uint16_t*)a.k + b * a.kv_sb + hd * a.kv_sh;
-  const uint16_t* vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
-  const uint16_t* rb = (const uint16_t*)a.r + hd * a.r_sh;
-  const int kv_st = (int)a.kv_st, r_sp = (int)a.r_sp;
-  int drow[2], dch[2], dchv[2], ko[2], vo[2], ro[2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    drow[x] = 16 * wave + 8 * x + (lane >> 3);
-    // chunks past d_load repeat a real one (times q = 0)
-    const int c = (lane & 7) ^ swz(drow[x]), cv = (lane & 7) ^ swzv(drow[x]);
-    dch[x] = 8 * (c < cl_max ? c : cl_max);
-    dchv[x] = 8 * (cv < cl_max ? cv : cl_max);
-    ko[x] = drow[x] * kv_st + dch[x];  // this lane's element offsets within a tile
-    vo[x] = drow[x] * kv_st + dchv[x];
-    ro[x] = drow[x] * r_sp + dch[x];
-  }
-  // Interior tiles address from a uniform tile base plus the lane's fixed offset;
-  // rows past the ends are clamped (they feed masked scores only).
-  // Keys may sit in a ring (row (kv_start + j) % kv_cap); without one the cap is
-  // past every key, so the row is j.
-  const int kvs = a.kv_cap > 0 ? (int)a.kv_start : 0;
-  const int kvc = a.kv_cap > 0 ? (int)a.kv_cap : 0x7fffffff - BK;
-  auto load_kv = [&](const uint16_t* base, uint16_t* lds, int j0, const int (&off)[2],
-                     const int (&ch)[2]) {
-    int p0 = kvs + j0;
-    p0 = p0 >= kvc ? p0 - kvc : p0;
-    if (j0 + BK <= T && p0 + BK <= kvc) {
-      const uint16_t* tb = base + p0 * kv_st;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) dma16(tb + off[x], lds + (16 * wave + 8 * x) * DP);
-    } else {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;
-        int p = kvs + j;
-        p = p >= kvc ? p - kvc : p;
-        dma16(base + p * kv_st + ch[x], lds + (16 * wave + 8 * x) * DP);
-      }
-    }
-  };
-  // r rows of relative distances e0 .. e0 + 63 (e = distance - mem_len, e0 % 64 == 0)
-  auto load_r = [&](int e0) {
-    uint16_t* dst = sm.R + ((e0 & (RRING - 1)) + 16 * wave) * DP;
-    const int dist0 = len + e0;
-    if (dist0 >= 0 && dist0 + BK <= T) {
-      const uint16_t* tb = rb + dist0 * r_sp;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) dma16(tb + ro[x], dst + 8 * x * DP);
-    } else {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        int dist = dist0 + drow[x];
-        dist = dist < 0 ? 0 : (dist < T ? dist : T - 1);
-        dma16(rb + dist * r_sp + dch[x], dst + 8 * x * DP);
-      }
-    }
-  };
+  const TileLoads ld(a, b, hd, wave, lane);
 
   // ---- fragment offsets (elements / floats), fixed for the whole walk -----------------
-  // K (16x16x32 A operand): row 16 kb + n16, chunk 4 s + g4
-  int koff[2];
+  int koff[2], voff[4];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) koff[s] = n16 * DP + 8 * ((4 * s + g4) ^ swz(n16));
-  // V^T through transposing reads: lane (g4, n16) of a 16-lane group reads key row
-  // 4 g4 + n16 / 4 (+ 32 h + 16 kb'), columns 16 dblk + 4 (n16 % 4) .. + 3
-  int voff[4];
-  {
-    const int vrow = 4 * g4 + (n16 >> 2);
+  for (int s = 0; s < 2; ++s) koff[s] = k_frag(n16, g4, s);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int piece = 4 * db + (n16 & 3);  // 8-byte piece of the row
-      voff[db] = vrow * DP + 8 * ((piece >> 1) ^ swzv(vrow)) + 4 * (piece & 1);
-    }
-  }
+  for (int db = 0; db < 4; ++db) voff[db] = v_frag(n16, g4, db);
   // Gathered position term S_p[query n][key jj] of one 16-query group: row n of
   // 64 floats, 16-byte chunk c of it in slot (c + 4 n + 3 (n / 4)) % 16.  Both
   // the 16-byte reads (16 queries at one chunk) and the 4-byte stores (64 lanes,
@@ -259,10 +341,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   //      query loads, so the two global round trips overlap) -----------------------
   if (kt_lo < kt_hi) {
     const int j0 = kt_lo * BK;
-    load_kv(kb, sm.K[kt_lo & 1], j0, ko, dch);
-    load_kv(vb, sm.V[kt_lo & 1], j0, vo, dchv);
+    ld.k(sm.K[kt_lo & 1], j0);
+    ld.v(sm.V[kt_lo & 1], j0);
 #pragma unroll
-    for (int blk = 0; blk < 3; ++blk) load_r(q0 - j0 - BK + BK * blk);
+    for (int blk = 0; blk < 3; ++blk) ld.r<RRING>(sm.R, q0 - j0 - BK + BK * blk);
     // ring offsets of the union blocks for this tile
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
@@ -275,43 +357,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   // ---- this lane's queries, pre-scaled: group gm holds query i0w + 16 gm + n16,
   //      k-step s columns 32 s + 8 g4 .. + 7 ---------------------------------------------
   bf16x8 qc[2][2], qp[2][2];
-  {
-    const uint16_t* ur = (const uint16_t*)a.u + hd * d;
-    const uint16_t* vr = (const uint16_t*)a.vb + hd * d;
-    const float sl2 = a.scale * LOG2E;
-    const bool uv_vec = (d % 8 == 0) && ((((uintptr_t)a.u) | ((uintptr_t)a.vb)) % 16 == 0);
 #pragma unroll
-    for (int gm = 0; gm < 2; ++gm) {
-      const int i = i0w + 16 * gm + n16;
-      const int ic = i < L ? i : L - 1;
-      const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + (int64_t)ic * a.q_st + hd * a.q_sh;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int c0 = 32 * s + 8 * g4;
-        const int cc = c0 / 8 < cl_max ? c0 : 8 * cl_max;
-        const uint4 raw = *(const uint4*)(qrow + cc);
-        const uint16_t* rv = (const uint16_t*)&raw;
-        uint16_t uh[8], vh[8];
-        if (uv_vec && c0 < d) {
-          *(uint4*)uh = *(const uint4*)(ur + c0);
-          *(uint4*)vh = *(const uint4*)(vr + c0);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            uh[e] = c0 + e < d ? ur[c0 + e] : (uint16_t)0;
-            vh[e] = c0 + e < d ? vr[c0 + e] : (uint16_t)0;
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool ok = c0 + e < d && i < L;
-          const float x = bf16_to_f32(rv[e]);
-          qc[gm][s][e] = (__bf16)(ok ? (x + bf16_to_f32(uh[e])) * sl2 : 0.f);
-          qp[gm][s][e] = (__bf16)(ok ? (x + bf16_to_f32(vh[e])) * sl2 : 0.f);
-        }
-      }
-    }
-  }
+  for (int gm = 0; gm < 2; ++gm) query_operands(a, b, hd, i0w + 16 * gm + n16, g4, qc[gm], qp[gm]);
 
   // Softmax state per query: the reference s_off that the position product
   // subtracts from every score through its accumulator's initial value (so the
@@ -344,9 +391,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
     wait_dma();
     barrier();
     if (kt + 1 < kt_hi) {
-      load_kv(kb, sm.K[(kt + 1) & 1], j0 + BK, ko, dch);
-      load_kv(vb, sm.V[(kt + 1) & 1], j0 + BK, vo, dchv);
-      load_r(q0 - j0 - 2 * BK);  // the block the next tile adds
+      ld.k(sm.K[(kt + 1) & 1], j0 + BK);
+      ld.v(sm.V[(kt + 1) & 1], j0 + BK);
+      ld.r<RRING>(sm.R, q0 - j0 - 2 * BK);  // the block the next tile adds
     }
     const uint16_t* Kt = sm.K[kt & 1];
     const uint16_t* Vt = sm.V[kt & 1];
@@ -575,26 +622,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, int nqt, 
   for (int gm = 0; gm < 2; ++gm) {
     const int i = i0w + 16 * gm + n16;
     if (i >= L) continue;
-    const float inv = 1.f / l_tot[gm];
     if constexpr (LSE) {
       if (g4 == 0) a.lse[(int64_t)g * L + i] = s_off[gm] + __log2f(l_tot[gm]);
     }
-    uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
-    const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
-                     ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int c = 16 * db + 4 * g4;
-      if (vec) {
-        if (c < d)
-          *(uint2*)(orow + c) = make_uint2(pack2(acc[gm][db][0] * inv, acc[gm][db][1] * inv),
-                                           pack2(acc[gm][db][2] * inv, acc[gm][db][3] * inv));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (c + e < d) orow[c + e] = bf16_bits(acc[gm][db][e] * inv);
-      }
-    }
+    write_out(a, b, hd, i, g4, acc[gm], 1.f / l_tot[gm]);
   }
 }
 
@@ -639,11 +670,9 @@ __global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, i
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, n16 = lane & 15;
-  const int d = (int)a.d;
   const int L = (int)a.L, len = (int)a.mem_len, T = len + L;
   const int q0 = qt * BQ64;
   const int i0w = q0 + wave * 16;
-  const int cl_max = (int)(a.d_load / 8) - 1;
 
   const int imax_wg = (q0 + BQ64 - 1 < L - 1) ? q0 + BQ64 - 1 : L - 1;
   const int n_kt = (len + imax_wg) / BK + 1;
@@ -651,74 +680,12 @@ __global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, i
   const int imax_w = (i0w + 15 < L - 1) ? i0w + 15 : L - 1;
   const int kt_w = wave_has_rows ? (len + imax_w) / BK : -1;
 
-  // ---- LDS-direct loads: instruction x (0, 1) of this wave fills tile rows
-  //      16 wave + 8 x .. + 7; lane -> row + lane / 8, slot lane % 8 ------------------
-  const uint16_t* kb = (const uint16_t*)a.k + b * a.kv_sb + hd * a.kv_sh;
-  const uint16_t* vb = (const uint16_t*)a.v + b * a.kv_sb + hd * a.kv_sh;
-  const uint16_t* rb = (const uint16_t*)a.r + hd * a.r_sh;
-  const int kv_st = (int)a.kv_st, r_sp = (int)a.r_sp;
-  int drow[2], dch[2], dchv[2], ko[2], vo[2], ro[2];
+  const TileLoads ld(a, b, hd, wave, lane);
+  int koff[2], voff[4];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    drow[x] = 16 * wave + 8 * x + (lane >> 3);
-    const int c = (lane & 7) ^ swz(drow[x]), cv = (lane & 7) ^ swzv(drow[x]);
-    dch[x] = 8 * (c < cl_max ? c : cl_max);
-    dchv[x] = 8 * (cv < cl_max ? cv : cl_max);
-    ko[x] = drow[x] * kv_st + dch[x];
-    vo[x] = drow[x] * kv_st + dchv[x];
-    ro[x] = drow[x] * r_sp + dch[x];
-  }
-  const int kvs = a.kv_cap > 0 ? (int)a.kv_start : 0;
-  const int kvc = a.kv_cap > 0 ? (int)a.kv_cap : 0x7fffffff - BK;
-  auto load_kv = [&](const uint16_t* base, uint16_t* lds, int j0, const int (&off)[2],
-                     const int (&ch)[2]) {
-    int p0 = kvs + j0;
-    p0 = p0 >= kvc ? p0 - kvc : p0;
-    if (j0 + BK <= T && p0 + BK <= kvc) {
-      const uint16_t* tb = base + p0 * kv_st;
+  for (int s = 0; s < 2; ++s) koff[s] = k_frag(n16, g4, s);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) dma16(tb + off[x], lds + (16 * wave + 8 * x) * DP);
-    } else {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int j = j0 + drow[x] < T ? j0 + drow[x] : T - 1;
-        int p = kvs + j;
-        p = p >= kvc ? p - kvc : p;
-        dma16(base + p * kv_st + ch[x], lds + (16 * wave + 8 * x) * DP);
-      }
-    }
-  };
-  // r rows of relative distances e0 .. e0 + 63 (e = distance - mem_len, e0 % 64 == 0)
-  auto load_r = [&](int e0) {
-    uint16_t* dst = sm.R + ((e0 & (RR64 - 1)) + 16 * wave) * DP;
-    const int dist0 = len + e0;
-    if (dist0 >= 0 && dist0 + BK <= T) {
-      const uint16_t* tb = rb + dist0 * r_sp;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) dma16(tb + ro[x], dst + 8 * x * DP);
-    } else {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        int dist = dist0 + drow[x];
-        dist = dist < 0 ? 0 : (dist < T ? dist : T - 1);
-        dma16(rb + dist * r_sp + dch[x], dst + 8 * x * DP);
-      }
-    }
-  };
-
-  // fragment offsets, as in the 128-query kernel
-  int koff[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) koff[s] = n16 * DP + 8 * ((4 * s + g4) ^ swz(n16));
-  int voff[4];
-  {
-    const int vrow = 4 * g4 + (n16 >> 2);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int piece = 4 * db + (n16 & 3);
-      voff[db] = vrow * DP + 8 * ((piece >> 1) ^ swzv(vrow)) + 4 * (piece & 1);
-    }
-  }
+  for (int db = 0; db < 4; ++db) voff[db] = v_frag(n16, g4, db);
   float* const wbuf = sm.W[wave];
   const int sprot = 4 * n16 + 3 * (n16 >> 2);
   auto sp_slot = [&](int jj) { return n16 * 64 + ((((jj >> 2) + sprot) & 15) << 2) + (jj & 3); };
@@ -730,10 +697,10 @@ __global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, i
   // ---- first tile: K, V and the two r blocks of its window ----------------------------
   {
     const int j0 = 0;
-    load_kv(kb, sm.K, j0, ko, dch);
-    load_kv(vb, sm.V, j0, vo, dchv);
-    load_r(q0 - j0 - BK);
-    load_r(q0 - j0);
+    ld.k(sm.K, j0);
+    ld.v(sm.V, j0);
+    ld.r<RR64>(sm.R, q0 - j0 - BK);
+    ld.r<RR64>(sm.R, q0 - j0);
 #pragma unroll
     for (int bw = 0; bw < 5; ++bw) {
       const int e = i0w - j0 + 15 - 16 * bw - n16;
@@ -744,40 +711,7 @@ __global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, i
 
   // ---- this lane's queries, pre-scaled: query i0w + n16, k-step s columns 32 s + 8 g4 ..
   bf16x8 qc[2], qp[2];
-  {
-    const uint16_t* ur = (const uint16_t*)a.u + hd * d;
-    const uint16_t* vr = (const uint16_t*)a.vb + hd * d;
-    const float sl2 = a.scale * LOG2E;
-    const bool uv_vec = (d % 8 == 0) && ((((uintptr_t)a.u) | ((uintptr_t)a.vb)) % 16 == 0);
-    const int i = i0w + n16;
-    const int ic = i < L ? i : L - 1;
-    const uint16_t* qrow = (const uint16_t*)a.q + b * a.q_sb + (int64_t)ic * a.q_st + hd * a.q_sh;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int c0 = 32 * s + 8 * g4;
-      const int cc = c0 / 8 < cl_max ? c0 : 8 * cl_max;
-      const uint4 raw = *(const uint4*)(qrow + cc);
-      const uint16_t* rv = (const uint16_t*)&raw;
-      uint16_t uh[8], vh[8];
-      if (uv_vec && c0 < d) {
-        *(uint4*)uh = *(const uint4*)(ur + c0);
-        *(uint4*)vh = *(const uint4*)(vr + c0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uh[e] = c0 + e < d ? ur[c0 + e] : (uint16_t)0;
-          vh[e] = c0 + e < d ? vr[c0 + e] : (uint16_t)0;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool ok = c0 + e < d && i < L;
-        const float x = bf16_to_f32(rv[e]);
-        qc[s][e] = (__bf16)(ok ? (x + bf16_to_f32(uh[e])) * sl2 : 0.f);
-        qp[s][e] = (__bf16)(ok ? (x + bf16_to_f32(vh[e])) * sl2 : 0.f);
-      }
-    }
-  }
+  query_operands(a, b, hd, i0w + n16, g4, qc, qp);
 
   // softmax state (see the 128-query kernel): reference s_off folded into the
   // position product's accumulator, limit lim, row sums on the matrix core
@@ -794,7 +728,7 @@ __global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, i
     const int j0 = kt * BK;
     wait_dma();
     barrier();
-    if (kt > 0) load_kv(vb, sm.V, j0, vo, dchv);
+    if (kt > 0) ld.v(sm.V, j0);
     const bool work = kt <= kt_w;
     const int Dw = len + i0w - j0;  // distance of (query i0w, key j0)
     f32x4 sc[4];
@@ -838,8 +772,8 @@ __global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, i
     wait_dma();
     barrier();
     if (kt + 1 < n_kt) {
-      load_kv(kb, sm.K, j0 + BK, ko, dch);
-      load_r(q0 - j0 - 2 * BK);  // the block tile kt + 1 adds, over tile kt's upper one
+      ld.k(sm.K, j0 + BK);
+      ld.r<RR64>(sm.R, q0 - j0 - 2 * BK);  // the block tile kt + 1 adds, over tile kt's upper one
     }
 #pragma unroll
     for (int bw = 0; bw < 5; ++bw) roff[bw] = (roff[bw] - BK * DP) & (RR64 * DP - 1);
@@ -922,26 +856,10 @@ __global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, i
   const int i = i0w + n16;
   if (i >= L) return;
   const float l_tot = acc_l[0];
-  const float inv = 1.f / l_tot;
   if constexpr (LSE) {
     if (g4 == 0) a.lse[(int64_t)g * L + i] = s_off + __log2f(l_tot);
   }
-  uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
-  const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
-                   ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int c = 16 * db + 4 * g4;
-    if (vec) {
-      if (c < d)
-        *(uint2*)(orow + c) = make_uint2(pack2(acc[db][0] * inv, acc[db][1] * inv),
-                                         pack2(acc[db][2] * inv, acc[db][3] * inv));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (c + e < d) orow[c + e] = bf16_bits(acc[db][e] * inv);
-    }
-  }
+  write_out(a, b, hd, i, g4, acc, 1.f / l_tot);
 }
 
 // Merge of the parts of a split query tile: one wave per (query tile, group,
@@ -1240,7 +1158,7 @@ AttnPlan plan_uncached(const AttnArgs& a, int num_cus, size_t budget) {
 
 size_t attn_plan_bytes(const AttnArgs& a, const AttnPlan& p) {
   if (p.slots <= 0) return 0;
-  const size_t groups = (size_t)(a.B * a.H), nqt = (size_t)((a.L + BQ - 1) / BQ);
+  const size_t groups = (size_t)(a.B * a.H);
   const size_t rows = (size_t)p.slots * groups * BQ;
   return rows * (DP + 2) * sizeof(float) + 512;
 }
