@@ -333,77 +333,143 @@ def kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def train_runner(w, x, streams):
+    """The training step's work over all segments of workload w, on one stream or
+    two (streams: a list of one or two torch streams).  Per segment: the forward
+    through every layer (txl_layer_step_save), then the backward from the top
+    (txl_layer_step_bwd_saved; the upstream gradient of the top layer is a fixed
+    synthetic tensor, the gradient of each layer's input feeds the layer below).
+    The memory of segment s + 1 at layer n is the last M rows of segment s's
+    memory and input there ([XL] section 3.2).
+
+    With two streams the backward of segment s runs on the second stream while the
+    forward of segment s + 1 runs on the first (stop-gradient memory: the forward
+    of s + 1 needs segment s's hidden states, not its gradients).  Activations,
+    saved states and rings are held twice (segment parity); the forward of segment
+    s waits for the backward of segment s - 2, the last reader of its parity's
+    buffers, and segment s's rings are built at the top of each of its layers
+    (a copy of segment s - 1's ring and txl_mem_update), beside the backward of
+    s - 1, which reads the same data.  Returns (step, grads, outputs)."""
+    import numpy as np
+    import torch
+    from relative_position_memory_amd import txl
+
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(tdt).cuda()
+    Ws = [{k: dev(v) for k, v in lw.items()} for lw in x["weights"]]
+    lws = [txl.layer_weights(Wl) for Wl in Ws]
+    u, vb, R = dev(x["u"]), dev(x["v"]), dev(x["R"])
+    h0 = dev(x["h0"])
+    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
+    N, S = w.n_layers, w.n_segments
+    mem0 = [dev(m) for m in x["mem"]]
+    ring_data = [[m.clone() for m in mem0], [m.clone() for m in mem0]]
+    rings = [[txl.make_ring(dd, 0, w.M) for dd in ring_data[p]] for p in range(2)]
+    bws = torch.empty(txl.layer_bwd_workspace_bytes(dims, w.M, tdt), dtype=torch.uint8,
+                      device="cuda")
+    nsv = txl.layer_saved_bytes(dims, w.M, tdt)
+    sbufs = [[torch.empty(nsv, dtype=torch.uint8, device="cuda") for _ in range(N)]
+             for _ in range(2)]
+    saved = [[None] * N for _ in range(2)]
+    hs = [[torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(N + 1)]
+          for _ in range(2)]
+    rng = np.random.default_rng(1)
+    g_top = dev(rng.standard_normal((w.B, w.L, w.D)).astype(np.float32))
+    g_cur = torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda")
+    outputs = torch.empty((S, w.B, w.L, w.D), dtype=tdt, device="cuda")
+    # lws holds raw pointers into Ws: the weight tensors live as long as the step
+    box = {"grads": None, "weights": Ws}
+    F = streams[0]
+    Bk = streams[1] if len(streams) > 1 else streams[0]
+
+    def step():
+        # a step starts from the initial memories, so that every step does the same work
+        for n in range(N):
+            rings[0][n].start, rings[0][n].len = 0, w.M
+        with torch.cuda.stream(F):
+            for n in range(N):
+                ring_data[0][n].copy_(mem0[n])
+        bwd_done = [None] * S
+        start = torch.cuda.Event()
+        start.record(F)
+        Bk.wait_stream(F) if Bk is not F else None
+        for s in range(S):
+            p, q = s % 2, (s - 1) % 2
+            if s >= 2 and Bk is not F:
+                F.wait_event(bwd_done[s - 2])
+            with torch.cuda.stream(F):
+                hs[p][0].copy_(h0[s])
+                for n in range(N):
+                    if s > 0:  # this segment's memory at layer n
+                        ring_data[p][n].copy_(ring_data[q][n])
+                        rings[p][n].start, rings[p][n].len = rings[q][n].start, rings[q][n].len
+                        txl.mem_update(rings[p][n], hs[q][n], stream=F)
+                    saved[p][n] = txl.layer_step_save(dims, hs[p][n], rings[p][n], lws[n], u,
+                                                      vb, R, hs[p][n + 1], sbufs[p][n], stream=F)
+                outputs[s].copy_(hs[p][N])
+            fwd_done = torch.cuda.Event()
+            fwd_done.record(F)
+            if Bk is not F:
+                Bk.wait_event(fwd_done)
+            with torch.cuda.stream(Bk):
+                g = g_top
+                for n in reversed(range(N)):
+                    box["grads"] = txl.layer_step_bwd(dims, hs[p][n], rings[p][n], lws[n], u, vb,
+                                                      R, g, bws, grads=box["grads"], stream=Bk,
+                                                      saved=saved[p][n])
+                    g_cur.copy_(box["grads"]["dh"])  # the next layer down takes dh in the layers' dtype
+                    g = g_cur
+            ev = torch.cuda.Event()
+            ev.record(Bk)
+            bwd_done[s] = ev
+        if Bk is not F:
+            F.wait_event(bwd_done[S - 1])
+    return step, box, outputs, (dims, hs, rings, lws, u, vb, R, g_top, bws)
+
+
 def train_step(args):
     """Training step with a stop-gradient memory ([XL] section 3.2) at the Large
     train-shape (batch 8, d_model 1024, 16 heads of 64, L = M = 384, 18 layers,
-    4 segments, bf16).  Per segment: the forward through every layer
-    (txl_layer_step_save, keeping each layer's input and what its backward needs),
-    then the backward from the top (txl_layer_step_bwd_saved; the upstream
-    gradient of the top layer is a fixed synthetic tensor, the gradient of each
-    layer's input feeds the layer below), then the memory updates.  The weight
-    gradients are written per layer (no optimizer update is part of the step).
-    value = B * L * segments / step time."""
-    import numpy as np
+    4 segments, bf16): every segment's forward and backward through the stack
+    (train_runner), the backward of a segment beside the next segment's forward on
+    a second stream.  The weight gradients are written per layer (no optimizer
+    update is part of the step).  value = B * L * segments / step time."""
     import torch
     from relative_position_memory_amd import inputs as I
     from relative_position_memory_amd import txl
 
     w = I.workload("large_train")
     x = I.make_inputs(w, seed=0)
-    tdt = torch.bfloat16
-    dev = lambda a: torch.from_numpy(a).to(tdt).cuda()
-    Ws = [{k: dev(v) for k, v in lw.items()} for lw in x["weights"]]
-    lws = [txl.layer_weights(Wl) for Wl in Ws]
-    u, vb, R = dev(x["u"]), dev(x["v"]), dev(x["R"])
-    ring_data = [dev(m) for m in x["mem"]]
-    rings = [txl.make_ring(dd, 0, w.M) for dd in ring_data]
-    h0 = dev(x["h0"])
-    dims = txl.layer_dims(w.B, w.L, w.D, w.H, w.d)
-    bws = torch.empty(txl.layer_bwd_workspace_bytes(dims, w.M, tdt), dtype=torch.uint8,
-                      device="cuda")
-    nsv = txl.layer_saved_bytes(dims, w.M, tdt)
-    sbufs = [torch.empty(nsv, dtype=torch.uint8, device="cuda") for _ in range(w.n_layers)]
-    saved = [None] * w.n_layers
-    hs = [torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(w.n_layers + 1)]
-    rng = np.random.default_rng(1)
-    g_top = dev(rng.standard_normal((w.B, w.L, w.D)).astype(np.float32))
-    g_cur = torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda")
-    grads = None
     stream = torch.cuda.current_stream()
+    streams = [stream, torch.cuda.Stream()] if args.streams > 1 else [stream]
+    step, box, outputs, (dims, hs, rings, lws, u, vb, R, g_top, bws) = train_runner(w, x, streams)
 
-    def step():
-        nonlocal grads
-        for s in range(w.n_segments):
-            hs[0].copy_(h0[s])
-            for n in range(w.n_layers):
-                saved[n] = txl.layer_step_save(dims, hs[n], rings[n], lws[n], u, vb, R,
-                                               hs[n + 1], sbufs[n], stream=stream)
-            g = g_top
-            for n in reversed(range(w.n_layers)):
-                grads = txl.layer_step_bwd(dims, hs[n], rings[n], lws[n], u, vb, R, g, bws,
-                                           grads=grads, stream=stream, saved=saved[n])
-                g_cur.copy_(grads["dh"])  # the next layer down takes dh in the layers' dtype
-                g = g_cur
-            for n in range(w.n_layers):
-                txl.mem_update(rings[n], hs[n], stream=stream)
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
 
-    for _ in range(max(args.warmup, 1)):
-        step()
-    torch.cuda.synchronize()
     steps = max(1, min(args.steps, 3))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = timed(step, steps, max(args.warmup, 1))
+    if len(streams) > 1:
+        step1, _, _, _ = train_runner(w, x, [stream])
+        ms_serial = timed(step1, 1, 1)
+    else:
+        ms_serial = ms
     # one layer's backward alone, with its forward recomputed (txl_layer_step_bwd),
     # HIP events on the same stream
+    grads = box["grads"]
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for _ in range(5):
-        txl.layer_step_bwd(dims, hs[0], rings[0], lws[0], u, vb, R, g_top, bws, grads=grads,
+        txl.layer_step_bwd(dims, hs[0][0], rings[0][0], lws[0], u, vb, R, g_top, bws, grads=grads,
                            stream=stream)
     b1.record(stream)
     torch.cuda.synchronize()
@@ -418,6 +484,8 @@ def train_step(args):
                    "batch": w.B, "d_model": w.D, "n_head": w.H, "d_head": w.d,
                    "segment_len": w.L, "mem_len": w.M, "n_layers": w.n_layers,
                    "n_segments": w.n_segments},
+        "schedule": {"streams": len(streams), "serial_ms_per_step": ms_serial,
+                     "note": "the backward of segment s beside the forward of segment s+1"},
         "layer_bwd_ms": bwd_ms,
         "roofline": {"bound": "mfma", "kernel": "txl_layer_step_bwd (one layer, all kernels)",
                      "achieved": bwd_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
