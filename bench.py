@@ -290,8 +290,10 @@ def pos_ff_time(w, reps, stream):
             "frac": flop / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, steps, warmup, stream):
-    """ms per step of the stack run with txl_layer_step_kv."""
+def kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, steps, warmup, stream, n_streams=1):
+    """ms per step of the stack run with txl_layer_step_kv, on the stack's segment
+    schedule: segment s on stream s % n_streams, layer n of segment s waiting for
+    layer n of segment s - 1 (which appended to the same key/value ring)."""
     import torch
     from relative_position_memory_amd import txl
     tdt = h0.dtype
@@ -299,27 +301,45 @@ def kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, steps, warmup, stream):
     dims_m = txl.layer_dims(w.B, w.M, w.D, w.H, w.d)
     rs = [txl.pos_proj(dims, R, Wl["W_kR"], stream=stream) for Wl in Ws]
     rings = []
-    ws = torch.empty(max(txl.kv_workspace_bytes(dims, w.M, tdt),
-                         txl.kv_workspace_bytes(dims_m, w.M, tdt)), dtype=torch.uint8,
-                     device="cuda")
+    nws = max(txl.kv_workspace_bytes(dims, w.M, tdt), txl.kv_workspace_bytes(dims_m, w.M, tdt))
+    wss = [torch.empty(nws, dtype=torch.uint8, device="cuda") for _ in range(n_streams)]
     for n, Wl in enumerate(Ws):
         kv, kb, vbuf = txl.make_kv_ring(dims, w.M, tdt, capacity=w.M + max(w.L, w.M))
         kv.mem_max = w.M
         m = torch.from_numpy(x["mem"][n]).to(tdt).cuda()
         # prefill: the initial memory rows as one segment over an empty memory
-        txl.layer_step_kv(dims_m, m, kv, Wl, u, vb, rs[n], torch.empty_like(m), ws,
+        txl.layer_step_kv(dims_m, m, kv, Wl, u, vb, rs[n], torch.empty_like(m), wss[0],
                           stream=stream)
         rings.append((kv, kb, vbuf))
-    bufs = [torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(2)]
+    streams = [stream] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
+    bufs = [[torch.empty((w.B, w.L, w.D), dtype=tdt, device="cuda") for _ in range(2)]
+            for _ in range(n_streams)]
 
     def step():
+        done = [[None] * w.n_layers for _ in range(2)]
+        start = torch.cuda.Event()
+        start.record(stream)
+        for st in streams[1:]:
+            st.wait_event(start)
         for s_ in range(w.n_segments):
+            k = s_ % n_streams
+            st = streams[k]
             h = h0[s_]
             for n in range(w.n_layers):
-                out = bufs[n % 2]
-                txl.layer_step_kv(dims, h, rings[n][0], lws[n], u, vb, rs[n], out, ws,
-                                  stream=stream)
+                if n_streams > 1 and s_ > 0:
+                    st.wait_event(done[(s_ - 1) % 2][n])
+                out = bufs[k][n % 2]
+                txl.layer_step_kv(dims, h, rings[n][0], lws[n], u, vb, rs[n], out, wss[k],
+                                  stream=st)
+                if n_streams > 1:
+                    ev = torch.cuda.Event()
+                    ev.record(st)
+                    done[s_ % 2][n] = ev
                 h = out
+        for st in streams[1:]:
+            fin = torch.cuda.Event()
+            fin.record(st)
+            stream.wait_event(fin)
 
     for _ in range(warmup):
         step()
@@ -1014,7 +1034,7 @@ def main():
     # the same stack with cached keys and values (txl_layer_step_kv): each layer's
     # ring is filled from its initial memory first (untimed), then the segments run
     kv_ms = None if args.main_only else kv_stack_ms(w, x, Ws, lws, u, vb, R, h0, args.steps,
-                                                    args.warmup, stream)
+                                                    args.warmup, stream, args.streams)
 
     # the position-wise feed-forward (not part of the step above) at the same rows,
     # d_inner = 4 d_model
@@ -1058,8 +1078,9 @@ def main():
         res["eval_kv_cache"] = {
             "value": tokens / (kv_ms / 1e3), "unit": "query tokens/s", "ms_per_step": kv_ms,
             "note": "same stack and inputs with cached keys/values (txl_layer_step_kv): only "
-                    "the L new rows are projected per segment, r is projected once; outputs "
-                    "equal the step above up to rounding"}
+                    "the L new rows are projected per segment, r is projected once; the same "
+                    "segment schedule over the same streams; outputs equal the step above up "
+                    "to rounding"}
     if args.calib_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -259,6 +259,8 @@ def make_ring(data, start=0, length=0) -> Ring:
 
 
 def layer_weights(W) -> LayerWeights:
+    """LayerWeights of raw device pointers into the tensors of W: they must outlive
+    every call that takes the returned struct (it holds no reference to them)."""
     return LayerWeights(*[W[n].data_ptr() for n in
                           ("W_q", "W_kE", "W_v", "W_kR", "W_o", "gamma", "beta")])
 
