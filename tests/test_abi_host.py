@@ -297,3 +297,31 @@ def test_stack_argument_errors_need_no_gpu():
 def torch_bf16():
     import torch
     return torch.bfloat16
+
+
+def test_attention_kernel_choice_needs_no_gpu():
+    """txl_attn_kernel reports the kernel each workload's attention takes (the
+    rule is one of sizes and CU count; without a device the count is 256, as on
+    an MI355X), and txl_attn_variant forces one and rejects unknown settings."""
+    import torch
+    from relative_position_memory_amd import txl
+    bf = torch.bfloat16
+    assert txl.attn_kernel(bf, 22, 8, 512, 512, 64) == "attn_mfma_kernel"        # Char-LM
+    assert txl.attn_kernel(bf, 60, 10, 150, 150, 48) == "attn_q64_kernel"        # Word-LM rows
+    assert txl.attn_kernel(bf, 8, 16, 384, 384, 64) == "attn_q64_kernel"         # Large-train
+    assert txl.attn_kernel(bf, 1, 16, 128, 1600, 64).startswith("attn_mfma_kernel + key-split")
+    assert txl.attn_kernel(bf, 1, 16, 1, 3799, 64).startswith("attn_decode_kernel")
+    assert txl.attn_kernel(torch.float32, 22, 8, 512, 512, 64).startswith("attn_generic")
+    assert txl.attn_kernel(bf, 2, 2, 64, 64, 41).startswith("attn_generic")      # dense 41-wide rows
+    with pytest.raises(txl.TxlError):
+        txl.attn_kernel(bf, 0, 8, 512, 512, 64)
+    old = txl.attn_variant(1)
+    try:
+        assert txl.attn_kernel(bf, 1, 16, 128, 1600, 64) == "attn_q64_kernel"
+        assert txl.attn_variant(2) == 1
+        assert txl.attn_kernel(bf, 8, 16, 384, 384, 64).startswith("attn_mfma_kernel")
+        with pytest.raises(txl.TxlError):
+            txl.attn_variant(3)
+    finally:
+        txl.attn_variant(old)
+    assert txl.attn_kernel(bf, 8, 16, 384, 384, 64) == "attn_q64_kernel"
