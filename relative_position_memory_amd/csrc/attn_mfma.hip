@@ -863,16 +863,18 @@ __global__ __launch_bounds__(256, 3) void attn_q64_kernel(AttnArgs a, int nqt, i
 }
 
 // Merge of the parts of a split query tile: one wave per (query tile, group,
-// 16-query block wq = 2 w + gm), whose lanes take the writing lanes' places
-// (lane (g4, n16) of writing wave w holds query 32 w + 16 gm + n16, columns
-// 16 db + 4 g4 .. + 3), so every load covers whole lines:
+// 16-query block wq = 2 w + gm, 16-column block db), whose lanes take the
+// writing lanes' places (lane (g4, n16) of writing wave w holds query
+// 32 w + 16 gm + n16, columns 16 db + 4 g4 .. + 3), so every load covers whole
+// lines:
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-// The references and sums of all parts and the outputs of the first 8 parts
-// are loaded at once (one round trip for up to 8 parts, two for up to 16).
-// The part that holds key 0 has a finite reference for every query.
+// The references, sums and outputs of all parts (4 values per lane and part)
+// are loaded at once: one memory round trip for up to 16 parts.  The part that
+// holds key 0 has a finite reference for every query.
 template <int MP>
 __global__ __launch_bounds__(64) void attn_part_merge_kernel(AttnArgs a) {
-  const int qt = a.plan.split_qt[blockIdx.x >> 3], wq = blockIdx.x & 7, g = blockIdx.y;
+  const int qt = a.plan.split_qt[blockIdx.x >> 5], wq = (blockIdx.x >> 2) & 7;
+  const int db = blockIdx.x & 3, g = blockIdx.y;
   const int np = a.plan.nparts[qt];  // 2 .. MP
   const int wave = wq >> 1, gm = wq & 1;
   const int64_t groups = a.B * a.H;
@@ -883,79 +885,46 @@ __global__ __launch_bounds__(64) void attn_part_merge_kernel(AttnArgs a) {
   const int64_t blk0 = (int64_t)a.plan.slot0[qt] * groups + g;
   const int i = qt * BQ + wave * BQW + 16 * gm + n16;
   if (qt * BQ + wave * BQW + 16 * gm >= L) return;  // no query of this block
+  if (16 * db >= d) return;                          // no column of this block
   const int moff = (wq * 16 + n16) * 2;
-  auto acc_ptr = [&](int p) {
-    return a.part_acc + (blk0 + (int64_t)p * groups) * (BQ * DP) + (wq * 4 * 2 * 64 + lane) * 2;
-  };
   // (indexes of parts past np are clamped to part 0 and their values dropped)
-  float2 ml[MP];
+  float2 ml[MP], av[MP][2];
 #pragma unroll
   for (int p = 0; p < MP; ++p) {
-    const float2 v = *(const float2*)(a.part_ml + (blk0 + (p < np ? p : 0) * groups) * (BQ * 2) + moff);
+    const int64_t blk = blk0 + (int64_t)(p < np ? p : 0) * groups;
+    const float2 v = *(const float2*)(a.part_ml + blk * (BQ * 2) + moff);
+    const float* pa = a.part_acc + blk * (BQ * DP) + (wq * 4 * 2 * 64 + lane) * 2;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) av[p][pr] = *(const float2*)(pa + (db * 2 + pr) * 128);
     ml[p] = p < np ? v : make_float2(-INFINITY, 0.f);
-  }
-  constexpr int NB = MP < 8 ? MP : 8;  // parts whose outputs are loaded together
-  float2 av[NB][4][2];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const float* pa = acc_ptr(j < np ? j : 0);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) av[j][db][pr] = *(const float2*)(pa + (db * 2 + pr) * 128);
   }
   float M = -INFINITY;
 #pragma unroll
   for (int p = 0; p < MP; ++p) M = fmaxf(M, ml[p].x);
-  float wgt[MP], den = 0.f;
+  float den = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < MP; ++p) {
-    wgt[p] = p < np ? __builtin_amdgcn_exp2f(ml[p].x - M) : 0.f;
-    den += wgt[p] * ml[p].y;
-  }
-  float o[4][4] = {};
-#pragma unroll
-  for (int p0 = 0; p0 < MP; p0 += NB) {
-    if (p0 > 0) {
-      if (p0 >= np) break;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const float* pa = acc_ptr(p0 + j < np ? p0 + j : 0);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr)
-            av[j][db][pr] = *(const float2*)(pa + (db * 2 + pr) * 128);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          o[db][2 * pr] += wgt[p0 + j] * av[j][db][pr].x;
-          o[db][2 * pr + 1] += wgt[p0 + j] * av[j][db][pr].y;
-        }
+    const float wgt = p < np ? __builtin_amdgcn_exp2f(ml[p].x - M) : 0.f;
+    den += wgt * ml[p].y;
+    o[0] += wgt * av[p][0].x;
+    o[1] += wgt * av[p][0].y;
+    o[2] += wgt * av[p][1].x;
+    o[3] += wgt * av[p][1].y;
   }
   if (i >= L) return;
   const float inv = 1.f / den;
-  if (a.lse && g4 == 0) a.lse[(int64_t)g * L + i] = M + __log2f(den);
+  if (a.lse && db == 0 && g4 == 0) a.lse[(int64_t)g * L + i] = M + __log2f(den);
   uint16_t* orow = (uint16_t*)a.out + b * a.o_sb + (int64_t)i * a.o_st + hd * a.o_sh;
   const bool vec = ((d & 3) == 0) && (((uintptr_t)a.out & 7) == 0) && ((a.o_sb & 3) == 0) &&
                    ((a.o_st & 3) == 0) && ((a.o_sh & 3) == 0);
+  const int c = 16 * db + 4 * g4;
+  if (vec) {
+    if (c < d)
+      *(uint2*)(orow + c) = make_uint2(pack2(o[0] * inv, o[1] * inv), pack2(o[2] * inv, o[3] * inv));
+  } else {
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int c = 16 * db + 4 * g4;
-    if (vec) {
-      if (c < d)
-        *(uint2*)(orow + c) = make_uint2(pack2(o[db][0] * inv, o[db][1] * inv),
-                                         pack2(o[db][2] * inv, o[db][3] * inv));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (c + e < d) orow[c + e] = bf16_bits(o[db][e] * inv);
-    }
+    for (int e = 0; e < 4; ++e)
+      if (c + e < d) orow[c + e] = bf16_bits(o[e] * inv);
   }
 }
 
@@ -1240,12 +1209,12 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int num_cus, hipStream_t s) {
                        groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.slots == 0) return e;
-  // one wave per (split query tile, 16-query block, group), the part loop sized
-  // to the most parts any tile has
+  // one wave per (split query tile, 16-query block, 16-column block, group), the
+  // part loop sized to the most parts any tile has
   int mp = 2;
   for (int t = 0; t < a.plan.nsplit_qt; ++t)
     while (mp < a.plan.nparts[a.plan.split_qt[t]]) mp *= 2;
-  const dim3 mgrid((unsigned)a.plan.nsplit_qt * 8, (unsigned)groups);
+  const dim3 mgrid((unsigned)a.plan.nsplit_qt * 32, (unsigned)groups);
   if (mp <= 2)
     hipLaunchKernelGGL(attn_part_merge_kernel<2>, mgrid, dim3(64), 0, s, a);
   else if (mp <= 4)
